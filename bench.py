@@ -1,0 +1,284 @@
+"""Benchmark of the HYPIC linear-layer hot path on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input:
+  main workload  GDN, H=32, d_k=d_v=128, bf16 k/v, fp32 records: one 32768-token
+                 request split into 16 segments of 2048 tokens; build all 512
+                 (segment, head) records, then compose the 16-segment chain to
+                 the request's final state.
+Secondary lines (same JSON object, key "secondary"):
+  compose_pool   4096-slot GDN pool (H=32, d=128, fp32 records), 64 requests each
+                 composing 32 seeded slot ids -> compositions/s
+  scalar/diag    RetNet-style scalar and GLA-style diagonal builds, H=16, d=128,
+                 bf16, 8 x 2048 tokens, plus their 8-segment chains
+
+Inputs are resident in HBM before the timed region starts.  Kernel durations
+come from HIP events recorded on the stream the kernels are launched on.
+The cpu_baseline leg times the fp64 oracle on a bounded sample on the host.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import hybrid_prefill_amd as hp  # noqa: E402
+import synth  # noqa: E402
+
+METRIC = "segment-build tokens/s + segment compositions/s at GDN H=32,d=128; % MFMA/HBM peak"
+PEAK_HBM = 8.0e12            # B/s, MI355X published
+PEAK_BF16 = 2.5e15           # FLOP/s dense bf16 MFMA
+PEAK_FP32 = 157.3e12         # FLOP/s fp32 (matrix and vector, published)
+CHUNK = 64
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- algorithmic counts
+
+def gdn_build_flops_per_token_head(dk, dv, c=CHUNK):
+    """Gram (strict lower triangle) + triangular solves on the right-hand sides of
+    the P and S columns + the inter-chunk carry (Z = K X and the rank-c update, for
+    P and S)."""
+    return (c - 1) * dk + (c - 1) * (dk + dv) + 4 * dk * (dk + dv)
+
+
+def gdn_build_bytes(N, H, dk, dv, nseg, kv_bytes=2):
+    tokens = N * H * (kv_bytes * (dk + dv) + 4 + 4)          # k, v, beta, log alpha
+    records = nseg * H * 4 * (dk * dk + dk * dv + 1)          # P, S, ell
+    return tokens + records
+
+
+def sd_build_bytes(family, N, H, dk, dv, nseg, kv_bytes=2):
+    gates = 4 * dk if family == hp.DIAGONAL else 0            # per-token gates (diagonal); scalar: per head
+    tokens = N * H * (kv_bytes * (dk + dv) + gates)
+    ell = dk if family == hp.DIAGONAL else 1
+    return tokens + nseg * H * 4 * (dk * dv + ell)
+
+
+def compose_bytes(chain_lengths, H, dk, dv, family=hp.GDN):
+    """Per (request, head): every record's S and ell, the P of every record but
+    the first (the first acts on a zero state), and the output S."""
+    ell = dk if family == hp.DIAGONAL else 1
+    per_P = dk * dk if family == hp.GDN else 0
+    total = 0
+    for m in chain_lengths:
+        if m == 0:
+            total += H * 4 * dk * dv
+            continue
+        total += H * 4 * (m * (dk * dv + ell) + (m - 1) * per_P + dk * dv)
+    return total
+
+
+# ----------------------------------------------------------------------------- timing helpers
+
+class KernelTimer:
+    """Accumulates HIP-event durations of launches on the current stream."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def time(self, name, fn):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+        return out
+
+    def mean_ms(self, name):
+        torch.cuda.synchronize()
+        ts = [s.elapsed_time(e) for s, e in self.pairs.get(name, [])]
+        return float(np.mean(ts)) if ts else float("nan")
+
+    def reset(self):
+        self.pairs = {}
+
+
+def roofline(bound, achieved, peak, unit, traffic=None):
+    return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "traffic": traffic}
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def gdn_workload(H=32, dk=128, dv=128, nseg=16, seg_len=2048, seed=301):
+    st = synth.gdn_stream([seg_len] * nseg, H, dk, dv, torch.bfloat16, seed, 0.1, "cuda")
+    pool = hp.Pool.allocate(hp.GDN, nseg, H, dk, dv, device="cuda")
+    return dict(st=st, pool=pool, offs=torch.as_tensor(st.seg_offsets).cuda(),
+                slots=torch.arange(nseg, dtype=torch.int32, device="cuda"),
+                chain_offs=torch.tensor([0, nseg], dtype=torch.int64, device="cuda"),
+                out_S=torch.empty((1, H, dk, dv), device="cuda"),
+                err=torch.zeros(1, dtype=torch.int32, device="cuda"),
+                H=H, dk=dk, dv=dv, nseg=nseg, seg_len=seg_len, N=nseg * seg_len)
+
+
+def gdn_step(w, timer):
+    st, pool = w["st"], w["pool"]
+    timer.time("build", lambda: hp.build_segment(hp.GDN, st.k, st.v, st.log_alpha, w["offs"], pool,
+                                                 w["slots"], beta=st.beta, err_flag=w["err"]))
+    timer.time("compose", lambda: hp.compose_chain(pool, w["chain_offs"], w["slots"], out_S=w["out_S"],
+                                                   err_flag=w["err"]))
+
+
+def bench_main(args):
+    w = gdn_workload()
+    timer = KernelTimer()
+    for _ in range(args.warmup):
+        gdn_step(w, timer)
+    torch.cuda.synchronize()
+    timer.reset()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        gdn_step(w, timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(w["err"].item()) == 0
+    ms_step = wall * 1e3 / args.steps
+    b_ms, c_ms = timer.mean_ms("build"), timer.mean_ms("compose")
+    N, H, dk, dv, nseg = w["N"], w["H"], w["dk"], w["dv"], w["nseg"]
+    flops = gdn_build_flops_per_token_head(dk, dv) * N * H
+    bbytes = gdn_build_bytes(N, H, dk, dv, nseg)
+    cbytes = compose_bytes([nseg], H, dk, dv)
+    log(f"main: {ms_step:.3f} ms/step wall; build {b_ms:.3f} ms, compose {c_ms:.3f} ms; "
+        f"build {flops / (b_ms * 1e-3) / 1e12:.1f} TFLOP/s, {bbytes / (b_ms * 1e-3) / 1e9:.0f} GB/s")
+    kern = {
+        "gdn_build": {"ms": b_ms, "algorithmic_flop": flops, "algorithmic_bytes": bbytes,
+                      "tflops": flops / (b_ms * 1e-3) / 1e12, "gbps": bbytes / (b_ms * 1e-3) / 1e9,
+                      "tokens_per_s": N / (b_ms * 1e-3)},
+        "gdn_compose_chain16": {"ms": c_ms, "algorithmic_bytes": cbytes, "gbps": cbytes / (c_ms * 1e-3) / 1e9,
+                                "compositions_per_s": nseg / (c_ms * 1e-3)},
+    }
+    del w
+    torch.cuda.empty_cache()
+    return ms_step, N, kern, flops, b_ms
+
+
+def bench_compose_pool(args, slots=4096, H=32, d=128, R=64, m=32, seg_len=64, seed=401):
+    """Pool of GDN records (filled untimed by the build), R requests x m slot ids."""
+    st = synth.gdn_stream([seg_len] * slots, H, d, d, torch.bfloat16, seed, 0.01, "cuda")
+    pool = hp.Pool.allocate(hp.GDN, slots, H, d, d, device="cuda")
+    hp.build_segment(hp.GDN, st.k, st.v, st.log_alpha, torch.as_tensor(st.seg_offsets).cuda(), pool,
+                     torch.arange(slots, dtype=torch.int32, device="cuda"), beta=st.beta)
+    del st
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ids = torch.as_tensor(rng.integers(0, slots, size=R * m).astype(np.int32)).cuda()
+    offs = torch.arange(0, R * m + 1, m, dtype=torch.int64, device="cuda")
+    out = torch.empty((R, H, d, d), device="cuda")
+    timer = KernelTimer()
+    for _ in range(args.warmup):
+        hp.compose_chain(pool, offs, ids, out_S=out)
+    torch.cuda.synchronize()
+    for _ in range(max(3, args.steps // 2)):
+        timer.time("compose", lambda: hp.compose_chain(pool, offs, ids, out_S=out))
+    ms = timer.mean_ms("compose")
+    nbytes = compose_bytes([m] * R, H, d, d)
+    comps = R * m
+    log(f"compose_pool: {ms:.3f} ms, {comps / (ms * 1e-3):.3e} compositions/s, {nbytes / (ms * 1e-3) / 1e9:.0f} GB/s")
+    del pool
+    torch.cuda.empty_cache()
+    return {"workload": f"gdn_compose_pool{slots}_h{H}_d{d}_{R}x{m}", "metric": "compositions/s",
+            "value": comps / (ms * 1e-3), "unit": "compositions/s", "ms": ms,
+            "roofline": roofline("hbm", nbytes / (ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s")}
+
+
+def bench_sd(args, H=16, d=128, nseg=8, seg_len=2048, seed=201):
+    out = []
+    N = nseg * seg_len
+    k = synth.keys(N, H, d, torch.bfloat16, seed * 10 + 1, "cuda")
+    v = synth.values(N, H, d, torch.bfloat16, seed * 10 + 2, "cuda")
+    offs = torch.as_tensor(synth.even_offsets(nseg, seg_len)).cuda()
+    slots = torch.arange(nseg, dtype=torch.int32, device="cuda")
+    chain = torch.tensor([0, nseg], dtype=torch.int64, device="cuda")
+    for fam, name in ((hp.SCALAR, "scalar"), (hp.DIAGONAL, "diagonal")):
+        la = (synth.scalar_log_gamma(H, seed * 10 + 4, device="cuda") if fam == hp.SCALAR
+              else synth.diagonal_log_gates(N, H, d, seed * 10 + 4, device="cuda"))
+        pool = hp.Pool.allocate(fam, nseg, H, d, d, device="cuda")
+        timer = KernelTimer()
+        for _ in range(args.warmup):
+            hp.build_segment(fam, k, v, la, offs, pool, slots)
+        torch.cuda.synchronize()
+        for _ in range(max(3, args.steps)):
+            timer.time("build", lambda: hp.build_segment(fam, k, v, la, offs, pool, slots))
+            timer.time("compose", lambda: hp.compose_chain(pool, chain, slots))
+        b_ms, c_ms = timer.mean_ms("build"), timer.mean_ms("compose")
+        nb = sd_build_bytes(fam, N, H, d, d, nseg)
+        log(f"{name}: build {b_ms:.3f} ms ({nb / (b_ms * 1e-3) / 1e9:.0f} GB/s), compose {c_ms:.3f} ms")
+        out.append({"workload": f"{name}_build_h{H}_d{d}_{nseg}x{seg_len}", "metric": "tokens/s",
+                    "value": N / (b_ms * 1e-3), "unit": "tokens/s", "ms": b_ms, "compose_ms": c_ms,
+                    "roofline": roofline("hbm", nb / (b_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s")})
+    return out
+
+
+def cpu_baseline(seg_len=2048, H=32, d=128, nseg_sample=1, seed=301):
+    """fp64 oracle on the host: build of nseg_sample segments x all heads of the main workload."""
+    import oracle
+    st = synth.gdn_stream([seg_len] * nseg_sample, H, d, d, torch.bfloat16, seed, 0.1, "cpu")
+    k, v = st.k.double().numpy(), st.v.double().numpy()
+    b, la = st.beta.double().numpy(), st.log_alpha.double().numpy()
+    t0 = time.perf_counter()
+    oracle.build_segments(oracle.GDN, k, v, la, st.seg_offsets, beta=b)
+    dt = time.perf_counter() - t0
+    toks = seg_len * nseg_sample
+    return {"value": toks / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"GDN build of {nseg_sample} x {seg_len}-token segment(s) x {H} heads, d={d}, "
+                      f"fp64 token-by-token recurrence ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", choices=["all", "main"], default="all")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 (the path shards by "
+              "(segment, head) with no collective, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    hp.lib()
+    torch.cuda.synchronize()
+    ms_step, N, kern, flops, b_ms = bench_main(args)
+    secondary = []
+    if args.only == "all":
+        secondary.append(bench_compose_pool(args))
+        secondary.extend(bench_sd(args))
+    cpu = None if args.no_cpu else cpu_baseline()
+    line = {
+        "metric": METRIC,
+        "value": N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "gdn_build_compose_h32_d128_bf16_16x2048",
+                   "heads": 32, "d_k": 128, "d_v": 128, "segments": 16, "segment_tokens": 2048,
+                   "kv_dtype": "bf16", "record_dtype": "fp32", "parallelism": "none (1 GPU)"},
+        "roofline": roofline("alu", flops / (b_ms * 1e-3) / 1e12, PEAK_FP32 / 1e12, "TFLOP/s"),
+        "cpu_baseline": cpu,
+        "kernels": kern,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,249 @@
+"""Python binding of libhypic (ctypes): argument marshalling only.
+
+Every step of the hot path runs in the HIP kernels of ``libhypic.so``; this
+module only turns torch tensors into device pointers, strides and the current
+HIP stream, and allocates outputs the caller did not pass.  The names follow
+the C ABI in ``include/hypic.h``:
+
+* :func:`build_segment`  -- records ``(ell, P, S)`` of segments into pool slots
+* :func:`compose_chain`  -- fold pool records along request chains
+* :func:`conv_warmup`    -- short-conv outputs at segment starts with the
+  previous segment's tail as conv state
+
+There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+SCALAR, DIAGONAL, GDN = 0, 1, 2
+F32, BF16 = 0, 1
+EFLAG_SLOT_OUT_OF_RANGE = 0x1
+EFLAG_BAD_OFFSETS = 0x2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhypic.so")
+_lib = None
+
+
+class HypicError(RuntimeError):
+    pass
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [("family", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("num_slots", ctypes.c_int64),
+                ("log_scale", ctypes.c_void_p), ("P", ctypes.c_void_p), ("S", ctypes.c_void_p)]
+
+
+class _Segments(ctypes.Structure):
+    _fields_ = [("family", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("num_segments", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("num_tokens", ctypes.c_int64),
+                ("seg_offsets", ctypes.c_void_p),
+                ("k", ctypes.c_void_p), ("k_stride_t", ctypes.c_int64), ("k_stride_h", ctypes.c_int64),
+                ("v", ctypes.c_void_p), ("v_stride_t", ctypes.c_int64), ("v_stride_h", ctypes.c_int64),
+                ("beta", ctypes.c_void_p), ("beta_stride_t", ctypes.c_int64), ("beta_stride_h", ctypes.c_int64),
+                ("log_alpha", ctypes.c_void_p), ("la_stride_t", ctypes.c_int64), ("la_stride_h", ctypes.c_int64)]
+
+
+EXPORTED = ("hypic_build_segment", "hypic_compose_chain", "hypic_conv_warmup",
+            "hypic_status_string", "hypic_abi_version")
+
+
+def lib():
+    """Load libhypic.so (built in-tree by ``hybrid_prefill_amd._build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise HypicError(f"{LIB_PATH} is missing: build it with `python -m hybrid_prefill_amd._build` "
+                         "(or __graft_entry__.build()); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.hypic_build_segment.argtypes = [ctypes.POINTER(_Segments), ctypes.POINTER(_Pool), vp, vp, vp]
+    L.hypic_build_segment.restype = i32
+    L.hypic_compose_chain.argtypes = [ctypes.POINTER(_Pool), i32, vp, vp, i64, vp, vp, vp, vp, vp, vp]
+    L.hypic_compose_chain.restype = i32
+    L.hypic_conv_warmup.argtypes = [i32, i32, i32, i32, vp, i64, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp]
+    L.hypic_conv_warmup.restype = i32
+    L.hypic_status_string.argtypes = [i32]
+    L.hypic_status_string.restype = ctypes.c_char_p
+    L.hypic_abi_version.restype = i32
+    _lib = L
+    return L
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        msg = lib().hypic_status_string(rc).decode()
+        raise HypicError(f"{what}: {msg} (status {rc})")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise HypicError(f"unsupported dtype {t.dtype} (fp32 or bf16)")
+
+
+def _device_check(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise HypicError("every tensor must be on the GPU")
+
+
+@dataclass
+class Pool:
+    """Caller-owned segment pool: per (slot, head) record (log_scale, P, S), fp32."""
+    family: int
+    num_heads: int
+    d_k: int
+    d_v: int
+    log_scale: torch.Tensor          # [slots,H] or [slots,H,d_k] (diagonal)
+    S: torch.Tensor                  # [slots,H,d_k,d_v]
+    P: Optional[torch.Tensor] = None  # [slots,H,d_k,d_k] (GDN)
+
+    @property
+    def num_slots(self) -> int:
+        return self.S.shape[0]
+
+    @staticmethod
+    def allocate(family: int, num_slots: int, num_heads: int, d_k: int, d_v: int, device="cuda",
+                 fill: Optional[float] = None) -> "Pool":
+        ls_shape = (num_slots, num_heads, d_k) if family == DIAGONAL else (num_slots, num_heads)
+        mk = (lambda s: torch.full(s, fill, dtype=torch.float32, device=device)) if fill is not None \
+            else (lambda s: torch.empty(s, dtype=torch.float32, device=device))
+        P = mk((num_slots, num_heads, d_k, d_k)) if family == GDN else None
+        return Pool(family, num_heads, d_k, d_v, mk(ls_shape), mk((num_slots, num_heads, d_k, d_v)), P)
+
+    def _c(self) -> _Pool:
+        for t in (self.log_scale, self.S, self.P):
+            if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+                raise HypicError("pool tensors must be contiguous fp32")
+        _device_check(self.log_scale, self.S, self.P)
+        return _Pool(self.family, self.num_heads, self.d_k, self.d_v, self.num_slots,
+                     _ptr(self.log_scale), _ptr(self.P), _ptr(self.S))
+
+
+def build_segment(family: int, k: torch.Tensor, v: torch.Tensor, log_alpha: Optional[torch.Tensor],
+                  seg_offsets: torch.Tensor, pool: Pool, dst_slots: torch.Tensor,
+                  beta: Optional[torch.Tensor] = None, err_flag: Optional[torch.Tensor] = None,
+                  stream=None) -> None:
+    """hypic_build_segment: records of every segment of a packed stream into pool slots.
+
+    k [N,H,d_k], v [N,H,d_v] (bf16 or fp32, unit channel stride); log_alpha
+    [N,H] (scalar, GDN), [H] broadcast per head (constant decay) or [N,H,d_k]
+    (diagonal), fp32, or None (no decay); beta [N,H] fp32 or None (= 1);
+    seg_offsets device int64 [S+1]; dst_slots device int32 [S].
+    """
+    _device_check(k, v, log_alpha, seg_offsets, dst_slots, beta, err_flag)
+    if k.dtype != v.dtype:
+        raise HypicError("k and v must share a dtype")
+    if k.dim() != 3 or v.dim() != 3 or k.stride(2) != 1 or v.stride(2) != 1:
+        raise HypicError("k, v must be [N,H,d] with unit channel stride")
+    if seg_offsets.dtype != torch.int64 or dst_slots.dtype != torch.int32:
+        raise HypicError("seg_offsets must be int64 and dst_slots int32")
+    N, H, dk = k.shape
+    dv = v.shape[2]
+    la_st = la_sh = 0
+    if log_alpha is not None:
+        if log_alpha.dtype != torch.float32:
+            raise HypicError("log_alpha must be fp32")
+        if family == DIAGONAL:
+            if log_alpha.dim() != 3 or log_alpha.stride(2) != 1:
+                raise HypicError("diagonal log_alpha must be [N,H,d_k] with unit channel stride")
+            la_st, la_sh = log_alpha.stride(0), log_alpha.stride(1)
+        elif log_alpha.dim() == 1:
+            la_st, la_sh = 0, log_alpha.stride(0)
+        else:
+            la_st, la_sh = log_alpha.stride(0), log_alpha.stride(1)
+    b_st = b_sh = 0
+    if beta is not None:
+        if beta.dtype != torch.float32 or beta.dim() != 2:
+            raise HypicError("beta must be fp32 [N,H]")
+        b_st, b_sh = beta.stride(0), beta.stride(1)
+    seg = _Segments(family, H, dk, dv, seg_offsets.numel() - 1, _dtype_code(k), N,
+                    _ptr(seg_offsets),
+                    _ptr(k), k.stride(0), k.stride(1),
+                    _ptr(v), v.stride(0), v.stride(1),
+                    _ptr(beta), b_st, b_sh,
+                    _ptr(log_alpha), la_st, la_sh)
+    cpool = pool._c()
+    rc = lib().hypic_build_segment(ctypes.byref(seg), ctypes.byref(cpool), _ptr(dst_slots),
+                                   _ptr(err_flag), _stream(stream))
+    _check(rc, "hypic_build_segment")
+
+
+def compose_chain(pool: Pool, chain_offsets: torch.Tensor, chain_slots: torch.Tensor,
+                  init_S: Optional[torch.Tensor] = None, out_S: Optional[torch.Tensor] = None,
+                  out_log_scale: Optional[torch.Tensor] = None, out_P: Optional[torch.Tensor] = None,
+                  err_flag: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """hypic_compose_chain: S <- T_i S + S_i along each chain; returns out_S [R,H,d_k,d_v]."""
+    _device_check(chain_offsets, chain_slots, init_S, out_S, out_log_scale, out_P, err_flag)
+    if chain_offsets.dtype != torch.int64 or chain_slots.dtype != torch.int32:
+        raise HypicError("chain_offsets must be int64 and chain_slots int32")
+    R = chain_offsets.numel() - 1
+    if out_S is None:
+        out_S = torch.empty((R, pool.num_heads, pool.d_k, pool.d_v), dtype=torch.float32,
+                            device=pool.S.device)
+    for t in (init_S, out_S, out_log_scale, out_P):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise HypicError("state tensors must be contiguous fp32")
+    cpool = pool._c()
+    rc = lib().hypic_compose_chain(ctypes.byref(cpool), R, _ptr(chain_offsets), _ptr(chain_slots),
+                                   chain_slots.numel(), _ptr(init_S), _ptr(out_S), _ptr(out_log_scale),
+                                   _ptr(out_P), _ptr(err_flag), _stream(stream))
+    _check(rc, "hypic_compose_chain")
+    return out_S
+
+
+def conv_warmup(tails: torch.Tensor, heads: torch.Tensor, weight: torch.Tensor,
+                bias: Optional[torch.Tensor] = None, activation: int = 0,
+                tail_index: Optional[torch.Tensor] = None, head_index: Optional[torch.Tensor] = None,
+                num_boundaries: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                err_flag: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """hypic_conv_warmup: tails/heads [rows,K-1,C] raw inputs, weight [C,K]; returns out [B,K-1,C] fp32."""
+    _device_check(tails, heads, weight, bias, tail_index, head_index, out, err_flag)
+    if tails.dtype != heads.dtype or not tails.is_contiguous() or not heads.is_contiguous():
+        raise HypicError("tails and heads must be contiguous and share a dtype")
+    C, K = weight.shape
+    if weight.dtype != torch.float32 or not weight.is_contiguous():
+        raise HypicError("weight must be contiguous fp32 [C,K]")
+    if tails.shape[1:] != (K - 1, C) or heads.shape[1:] != (K - 1, C):
+        raise HypicError("tails/heads must be [rows, K-1, C]")
+    for ix in (tail_index, head_index):
+        if ix is not None and ix.dtype != torch.int32:
+            raise HypicError("indices must be int32")
+    if num_boundaries is None:
+        num_boundaries = tail_index.numel() if tail_index is not None else (
+            head_index.numel() if head_index is not None else tails.shape[0])
+    if out is None:
+        out = torch.empty((num_boundaries, K - 1, C), dtype=torch.float32, device=weight.device)
+    rc = lib().hypic_conv_warmup(num_boundaries, C, K, _dtype_code(tails),
+                                 _ptr(tails), tails.shape[0], _ptr(tail_index),
+                                 _ptr(heads), heads.shape[0], _ptr(head_index),
+                                 _ptr(weight), _ptr(bias), int(activation), _ptr(out), _ptr(err_flag),
+                                 _stream(stream))
+    _check(rc, "hypic_conv_warmup")
+    return out

@@ -1,0 +1,210 @@
+// Composition of pool records along request chains, fp32 LDS-tiled kernel.
+//
+// What it computes (besthub article "Cut First-Token Latency by 3.25x ...",
+// paragraph 4: reuse composes T_C2*S(C1)+S(C2); podcast companion page,
+// "Composition law, step by step"): for every request r and head h, over the
+// chain's slots in prompt order
+//     S <- e^{ell_i} (P_i S) + S_i           (GDN; T_i = e^{ell_i} P_i)
+//     S <- e^{ell_i} S + S_i                 (scalar)
+//     S <- diag(e^{ell_i}) S + S_i           (diagonal)
+// and optionally the composed operator ell <- ell + ell_i, P <- P_i P.
+//
+// GDN work split: one workgroup per (request, head, 64-column slab of S, or
+// of P when the composed P is asked for).  The slab stays in LDS across the
+// chain; P_i streams through LDS in 32-column blocks.  Scalar and diagonal
+// families: one workgroup per (request, head), the state in registers.
+#include "hypic_internal.h"
+
+namespace hypic {
+namespace {
+
+constexpr int NT = 256;
+constexpr int NSL = 64;
+constexpr int KB = 32;
+
+// Check a request's chain; returns 0 ok, 1 slot out of range, 2 bad offsets.
+__device__ int check_chain(const ComposeArgs &a, int r, int64_t &c_lo, int64_t &c_hi, int *sh_bad) {
+    if (threadIdx.x == 0) {
+        const int64_t lo = a.chain_offsets[r], hi = a.chain_offsets[r + 1];
+        *sh_bad = (lo < 0 || hi < lo || hi > a.num_chain_slots) ? 2 : 0;
+    }
+    __syncthreads();
+    c_lo = a.chain_offsets[r];
+    c_hi = a.chain_offsets[r + 1];
+    if (*sh_bad) return *sh_bad;
+    __syncthreads();
+    for (int64_t c = c_lo + threadIdx.x; c < c_hi; c += blockDim.x) {
+        const int32_t s = a.chain_slots[c];
+        if (s < 0 || s >= a.num_slots) *sh_bad = 1;   // benign race: every writer stores 1
+    }
+    __syncthreads();
+    return *sh_bad;
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void compose_dense_ref_kernel(ComposeArgs a, int nslab_S) {
+    __shared__ float St[DK][NSL + 1];
+    __shared__ float Pt[DK][KB + 1];
+    __shared__ int sh_bad;
+
+    const int tid = threadIdx.x;
+    const int nslab = nslab_S + (a.out_P ? DK / NSL : 0);
+    const int slab = blockIdx.x % nslab;
+    const int unit = blockIdx.x / nslab;
+    const int h = unit % a.H;
+    const int r = unit / a.H;
+    const bool isP = slab >= nslab_S;
+    const int c0 = (isP ? slab - nslab_S : slab) * NSL;
+    const int ldo = isP ? DK : DV;      // row length of the output matrix
+    float *out = isP ? a.out_P + ((int64_t)r * a.H + h) * DK * DK : a.out_S + ((int64_t)r * a.H + h) * DK * DV;
+
+    int64_t lo, hi;
+    const int bad = check_chain(a, r, lo, hi, &sh_bad);
+    if (bad) {
+        if (tid == 0 && slab == 0)
+            raise_flag(a.err_flag, bad == 1 ? HYPIC_EFLAG_SLOT_OUT_OF_RANGE : HYPIC_EFLAG_BAD_OFFSETS);
+        const float nanv = __int_as_float(0x7fc00000);
+        for (int e = tid; e < DK * NSL; e += NT) out[(int64_t)(e / NSL) * ldo + c0 + e % NSL] = nanv;
+        if (slab == 0 && a.out_ell && tid == 0) a.out_ell[(int64_t)r * a.H + h] = nanv;
+        return;
+    }
+
+    for (int e = tid; e < DK * NSL; e += NT) {
+        const int i = e / NSL, c = e % NSL;
+        float x;
+        if (isP) x = (i == c0 + c) ? 1.0f : 0.0f;
+        else x = a.init_S ? a.init_S[((int64_t)r * a.H + h) * DK * DV + (int64_t)i * DV + c0 + c] : 0.0f;
+        St[i][c] = x;
+    }
+    double ell = 0.0;
+    const int tr = tid / 16, tc = tid % 16;
+    constexpr int RP = DK / 16;
+
+    for (int64_t ci = lo; ci < hi; ++ci) {
+        const int64_t rec = (int64_t)a.chain_slots[ci] * a.H + h;
+        const float *Pi = a.pool_P + rec * DK * DK;
+        const float le = a.pool_ell[rec];
+        ell += (double)le;
+        const float sc = isP ? 1.0f : expf(le);
+        float acc[RP][4];
+#pragma unroll
+        for (int p = 0; p < RP; ++p)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[p][q] = 0.f;
+        for (int kb = 0; kb < DK; kb += KB) {
+            __syncthreads();
+            for (int e = tid; e < DK * KB; e += NT) {
+                const int i = e / KB, k = e % KB;
+                Pt[i][k] = Pi[(int64_t)i * DK + kb + k];
+            }
+            __syncthreads();
+            for (int k = 0; k < KB; ++k) {
+                float pv[RP], sv[4];
+#pragma unroll
+                for (int p = 0; p < RP; ++p) pv[p] = Pt[tr + 16 * p][k];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sv[q] = St[kb + k][tc + 16 * q];
+#pragma unroll
+                for (int p = 0; p < RP; ++p)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[p][q] += pv[p] * sv[q];
+            }
+        }
+        __syncthreads();   // everyone is done reading the old slab
+        const float *Si = a.pool_S + rec * DK * DV;
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+            const int i = tr + 16 * p;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = tc + 16 * q;
+                St[i][c] = isP ? acc[p][q] : sc * acc[p][q] + Si[(int64_t)i * DV + c0 + c];
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < DK * NSL; e += NT) {
+        const int i = e / NSL, c = e % NSL;
+        out[(int64_t)i * ldo + c0 + c] = St[i][c];
+    }
+    if (slab == 0 && a.out_ell && tid == 0) a.out_ell[(int64_t)r * a.H + h] = (float)ell;
+}
+
+// Scalar / diagonal: elementwise, one workgroup per (request, head).
+template <int FAM, int DK, int DV>
+__global__ __launch_bounds__(NT) void compose_sd_kernel(ComposeArgs a) {
+    constexpr int PER = DK * DV / NT;
+    __shared__ int sh_bad;
+    const int tid = threadIdx.x;
+    const int h = blockIdx.x % a.H;
+    const int r = blockIdx.x / a.H;
+    const int64_t orec = (int64_t)r * a.H + h;
+    float *out = a.out_S + orec * DK * DV;
+    int64_t lo, hi;
+    const int bad = check_chain(a, r, lo, hi, &sh_bad);
+    if (bad) {
+        if (tid == 0) raise_flag(a.err_flag, bad == 1 ? HYPIC_EFLAG_SLOT_OUT_OF_RANGE : HYPIC_EFLAG_BAD_OFFSETS);
+        const float nanv = __int_as_float(0x7fc00000);
+        for (int e = tid; e < DK * DV; e += NT) out[e] = nanv;
+        if (a.out_ell) {
+            if (FAM == HYPIC_DIAGONAL) { if (tid < DK) a.out_ell[orec * DK + tid] = nanv; }
+            else if (tid == 0) a.out_ell[orec] = nanv;
+        }
+        return;
+    }
+    float s[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) s[q] = a.init_S ? a.init_S[orec * DK * DV + tid + q * NT] : 0.0f;
+    double ell = 0.0;   // thread i < DK keeps channel i (diagonal), thread 0 the scalar
+    for (int64_t ci = lo; ci < hi; ++ci) {
+        const int64_t rec = (int64_t)a.chain_slots[ci] * a.H + h;
+        const float *Si = a.pool_S + rec * DK * DV;
+        if (FAM == HYPIC_DIAGONAL) {
+            const float *le = a.pool_ell + rec * DK;
+            if (tid < DK) ell += (double)le[tid];
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                const int e = tid + q * NT;
+                s[q] = expf(le[e / DV]) * s[q] + Si[e];
+            }
+        } else {
+            const float le = a.pool_ell[rec];
+            ell += (double)le;
+            const float sc = expf(le);
+#pragma unroll
+            for (int q = 0; q < PER; ++q) s[q] = sc * s[q] + Si[tid + q * NT];
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) out[tid + q * NT] = s[q];
+    if (a.out_ell) {
+        if (FAM == HYPIC_DIAGONAL) { if (tid < DK) a.out_ell[orec * DK + tid] = (float)ell; }
+        else if (tid == 0) a.out_ell[orec] = (float)ell;
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_dims(const ComposeArgs &a, hipStream_t stream) {
+    const int64_t units = (int64_t)a.num_requests * a.H;
+    if (a.family == HYPIC_GDN) {
+        const int nslab_S = DV / NSL;
+        const int nslab = nslab_S + (a.out_P ? DK / NSL : 0);
+        hipLaunchKernelGGL((compose_dense_ref_kernel<DK, DV>), dim3((unsigned)(units * nslab)), dim3(NT), 0, stream, a, nslab_S);
+    } else if (a.family == HYPIC_SCALAR) {
+        hipLaunchKernelGGL((compose_sd_kernel<HYPIC_SCALAR, DK, DV>), dim3((unsigned)units), dim3(NT), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((compose_sd_kernel<HYPIC_DIAGONAL, DK, DV>), dim3((unsigned)units), dim3(NT), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_compose_ref(const ComposeArgs &a, hipStream_t stream) {
+    if (a.dk == 64 && a.dv == 64) return launch_dims<64, 64>(a, stream);
+    if (a.dk == 64 && a.dv == 128) return launch_dims<64, 128>(a, stream);
+    if (a.dk == 128 && a.dv == 64) return launch_dims<128, 64>(a, stream);
+    return launch_dims<128, 128>(a, stream);
+}
+
+}  // namespace hypic

@@ -1,0 +1,65 @@
+// Internal declarations shared by the HIP translation units of libhypic.
+// Not part of the public ABI (include/hypic.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hypic.h"
+
+namespace hypic {
+
+// Kernel-side view of one build call (all device pointers).
+struct BuildArgs {
+    int32_t family, H, dk, dv, num_segments, kv_dtype;
+    int64_t num_tokens;
+    const int64_t *seg_offsets;
+    const void *k;  int64_t k_st, k_sh;
+    const void *v;  int64_t v_st, v_sh;
+    const float *beta; int64_t b_st, b_sh;
+    const float *log_alpha; int64_t la_st, la_sh;
+    const int32_t *dst_slots;
+    int64_t num_slots;
+    float *pool_ell, *pool_P, *pool_S;
+    uint32_t *err_flag;
+};
+
+struct ComposeArgs {
+    int32_t family, H, dk, dv, num_requests;
+    int64_t num_slots, num_chain_slots;
+    const float *pool_ell, *pool_P, *pool_S;
+    const int64_t *chain_offsets;
+    const int32_t *chain_slots;
+    const float *init_S;
+    float *out_S, *out_ell, *out_P;
+    uint32_t *err_flag;
+};
+
+struct ConvArgs {
+    int32_t num_boundaries, channels, ksize, x_dtype, activation;
+    const void *tails; int64_t num_tails; const int32_t *tail_index;
+    const void *heads; int64_t num_heads; const int32_t *head_index;
+    const float *weight, *bias;
+    float *out;
+    uint32_t *err_flag;
+};
+
+hipError_t launch_build(const BuildArgs &a, hipStream_t stream);
+hipError_t launch_compose(const ComposeArgs &a, hipStream_t stream);
+hipError_t launch_conv_warmup(const ConvArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_f32(const T *p);
+template <> __device__ __forceinline__ float load_f32<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
+
+__device__ __forceinline__ void raise_flag(uint32_t *flag, uint32_t bits) {
+    if (flag) atomicOr(flag, bits);
+}
+
+}  // namespace hypic

@@ -1,0 +1,204 @@
+/*
+ * hypic.h -- C ABI of the HYPIC linear-layer hot path on one MI355X (gfx950).
+ *
+ * What the library computes (the pages never print equations; this is the
+ * reading the library implements):
+ *
+ *   Per head a state S in R^{d_k x d_v} follows the gated linear recurrence
+ *       S_t = A_t S_{t-1} + beta_t k_t v_t^T ,      S_0 = 0
+ *   with the transition family
+ *       HYPIC_SCALAR    A_t = alpha_t I               (RetNet / Mamba2 style decay)
+ *       HYPIC_DIAGONAL  A_t = diag(alpha_t)           (GLA style gates on the key channels)
+ *       HYPIC_GDN       A_t = alpha_t (I - beta_t k_t k_t^T)   (gated delta rule; DeltaNet = alpha 1)
+ *   For a segment C of n tokens its record is the cumulative transition operator
+ *   T_C = A_n ... A_1 and the zero-initial terminal state S(C|0) = S_n, so that
+ *   a start state S_0 maps to T_C S_0 + S(C|0).  Segments are then composed in
+ *   prompt order, S = T_C2 S(C1) + S(C2), which equals the recurrence run over
+ *   the concatenation.
+ *
+ *   Sources: "HYPIC: Cache Acceleration for Hybrid Attention Models"
+ *   (agihunt.info), "Core Approach" (cache T_C beside the zero-initial terminal
+ *   state; constant-time combination on reuse); "Cut First-Token Latency by
+ *   3.25x: Introducing HYPIC ..." (besthub.dev), paragraph 4 (store the pair at
+ *   first prefill, compose T_C2*S(C1)+S(C2); the family list; the convolution
+ *   state warm-up patch); "Hypic: Position-Independent KV Caching for
+ *   Hybrid-Attention LLM Serving" (podcast companion page), "The transition
+ *   operator: compose, don't add" and "Family comparison: scalar -> diagonal ->
+ *   dense"; its reference 7 (Gated Delta Networks) for the GDN transition.
+ *
+ * Stored record (exact factorisation, not an approximation).  The scalar gate
+ * commutes with everything, so T_C = e^{ell} P with ell = sum_t log alpha_t
+ * and P = prod_{t=n..1} (I - beta_t k_t k_t^T).  A pool record per head is
+ *       log_scale  ell         1 float (d_k floats for HYPIC_DIAGONAL)
+ *       P          d_k x d_k   fp32, row-major (HYPIC_GDN only; P = I otherwise)
+ *       S          d_k x d_v   fp32, row-major
+ * Keeping ell apart keeps T_C inside fp32 range: e^{ell} of a 2048-token
+ * segment is far below the smallest fp32 normal at typical decay rates.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is DEVICE memory owned by the caller; the library
+ *     never allocates, frees or retains a pointer past the call.  Descriptor
+ *     structs are host memory read only during the call.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream).  No host synchronisation happens inside.
+ *   - The return code reports synchronous argument validation and launch
+ *     errors only; on any error nothing is launched.  Validation happens
+ *     before any HIP call.
+ *   - Data-dependent errors (slot ids, offsets) are OR-ed into the device word
+ *     *err_flag (HYPIC_EFLAG_*), when err_flag is not NULL; the output they
+ *     concern is filled with NaN (when it exists) and every other output is
+ *     computed normally.  The caller clears *err_flag.
+ *   - Inputs are never written; outputs are overwritten in full; inputs and
+ *     outputs must not alias.  There is no global mutable state: concurrent
+ *     calls on different streams are safe when their outputs do not overlap.
+ *   - Supported head sizes: d_k, d_v in {64, 128}.
+ */
+#ifndef HYPIC_H
+#define HYPIC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HYPIC_ABI_VERSION 1
+
+typedef enum {
+    HYPIC_OK = 0,
+    HYPIC_ERR_INVALID_ARG = 1,   /* NULL required pointer, negative size, family/shape mismatch */
+    HYPIC_ERR_UNSUPPORTED = 2,   /* d_k or d_v not in {64,128}, unknown dtype, family or activation */
+    HYPIC_ERR_HIP = 3            /* the kernel launch failed (hipGetLastError) */
+} hypic_status;
+
+typedef enum { HYPIC_SCALAR = 0, HYPIC_DIAGONAL = 1, HYPIC_GDN = 2 } hypic_family;
+typedef enum { HYPIC_F32 = 0, HYPIC_BF16 = 1 } hypic_dtype;
+
+#define HYPIC_EFLAG_SLOT_OUT_OF_RANGE 0x1u   /* a slot id outside [0, num_slots) */
+#define HYPIC_EFLAG_BAD_OFFSETS       0x2u   /* decreasing offsets, or an offset outside [0, num_tokens] */
+
+/*
+ * Segment pool: caller-owned device memory holding one record per (slot, head).
+ *   log_scale  [num_slots][H] fp32, or [num_slots][H][d_k] for HYPIC_DIAGONAL
+ *   P          [num_slots][H][d_k][d_k] fp32, HYPIC_GDN only (must be NULL otherwise)
+ *   S          [num_slots][H][d_k][d_v] fp32
+ * All three are dense and row-major.
+ */
+typedef struct hypic_pool {
+    int32_t family;       /* hypic_family */
+    int32_t num_heads;    /* H */
+    int32_t d_k, d_v;
+    int64_t num_slots;
+    float *log_scale;
+    float *P;
+    float *S;
+} hypic_pool;
+
+/*
+ * A packed stream of segments (device pointers; strides in ELEMENTS, the
+ * innermost channel stride is 1).
+ *   token t, head h:  k[t*k_stride_t + h*k_stride_h + i]   i < d_k   (kv_dtype)
+ *                     v[t*v_stride_t + h*v_stride_h + j]   j < d_v   (kv_dtype)
+ *                     beta[t*beta_stride_t + h*beta_stride_h]        (fp32; NULL means beta = 1)
+ *                     log_alpha[t*la_stride_t + h*la_stride_h (+ i for HYPIC_DIAGONAL)]
+ *                                                          (fp32, log of the decay; NULL means 0)
+ *   la_stride_t = 0 gives a per-head constant decay (RetNet).
+ *   Segment s is tokens [seg_offsets[s], seg_offsets[s+1]) (device int64,
+ *   num_segments+1 entries, non-decreasing, inside [0, num_tokens]).
+ *   A segment may be empty (identity record) and needs no particular length.
+ */
+typedef struct hypic_segments {
+    int32_t family;       /* hypic_family; must equal the pool's */
+    int32_t num_heads;
+    int32_t d_k, d_v;
+    int32_t num_segments;
+    int32_t kv_dtype;     /* hypic_dtype of k and v */
+    int64_t num_tokens;   /* rows of the packed stream, bound for the offsets */
+    const int64_t *seg_offsets;
+    const void *k;          int64_t k_stride_t, k_stride_h;
+    const void *v;          int64_t v_stride_t, v_stride_h;
+    const float *beta;      int64_t beta_stride_t, beta_stride_h;
+    const float *log_alpha; int64_t la_stride_t, la_stride_h;
+} hypic_segments;
+
+/*
+ * hypic_build_segment -- build the record (ell, P, S) of every segment and head
+ * of `in` and write it to pool slot dst_slots[s] (device int32, one per
+ * segment; distinct).  Source: besthub article, paragraph 4 (the pair
+ * (T_C, S(C|0)) is stored during the first prefill); agihunt summary, "Core
+ * Approach" (the segment-cumulative transition operator T_C).
+ *
+ * Error behaviour: a dst slot outside [0, num_slots) sets
+ * HYPIC_EFLAG_SLOT_OUT_OF_RANGE and writes nothing for that segment; bad
+ * offsets set HYPIC_EFLAG_BAD_OFFSETS and fill the segment's record with NaN.
+ * NaN or Inf inputs propagate into the affected record.
+ */
+hypic_status hypic_build_segment(const hypic_segments *in, const hypic_pool *pool,
+                                 const int32_t *dst_slots, uint32_t *err_flag, void *stream);
+
+/*
+ * hypic_compose_chain -- for every request r and head h, fold the pool records
+ * chain_slots[chain_offsets[r] .. chain_offsets[r+1]) in prompt order:
+ *       S <- T_i S + S_i = e^{ell_i} (P_i S) + S_i
+ * starting from init_S[r][h] (NULL = zero).  Source: besthub article,
+ * paragraph 4 (reuse composes T_C2*S(C1)+S(C2) in constant time); podcast
+ * page, "Composition law, step by step".
+ *
+ *   chain_offsets  device int64 [num_requests+1], non-decreasing from 0
+ *   chain_slots    device int32, slot ids; repeats allowed; an empty chain
+ *                  yields init_S (or 0)
+ *   init_S         [R][H][d_k][d_v] fp32 or NULL
+ *   out_S          [R][H][d_k][d_v] fp32 (required)
+ *   out_log_scale  [R][H] ([R][H][d_k] diagonal) fp32 or NULL: sum of ell_i
+ *   out_P          [R][H][d_k][d_k] fp32 or NULL (GDN only): P_m ... P_1
+ *   (out_log_scale, out_P, out_S) is itself a record of the concatenated chain.
+ *
+ * Error behaviour: a slot id outside [0, num_slots) sets
+ * HYPIC_EFLAG_SLOT_OUT_OF_RANGE, bad chain offsets set HYPIC_EFLAG_BAD_OFFSETS;
+ * in both cases that request's outputs are filled with NaN.
+ */
+hypic_status hypic_compose_chain(const hypic_pool *pool, int32_t num_requests,
+                                 const int64_t *chain_offsets, const int32_t *chain_slots,
+                                 int64_t num_chain_slots,
+                                 const float *init_S, float *out_S, float *out_log_scale,
+                                 float *out_P, uint32_t *err_flag, void *stream);
+
+/*
+ * hypic_conv_warmup -- convolution state warm-up at segment boundaries
+ * (besthub article, paragraph 4).  A causal depthwise conv of kernel size K
+ * runs before the recurrence in conv variants; a segment prefilled on its own
+ * saw a zero history for its first K-1 tokens.  At boundary b the warm-up
+ * recomputes those outputs with the previous segment's last K-1 raw inputs as
+ * the conv state:
+ *       x_bar = [tail_b (K-1 rows) ; head_b (K-1 rows)]
+ *       out[b][t][c] = act( bias[c] + sum_{j<K} w[c][j] * x_bar[t+j][c] ),  t < K-1
+ * (w[c][K-1] multiplies the current token).  act: 0 identity, 1 SiLU.
+ *
+ *   tails       [num_tails][K-1][C] raw inputs (x_dtype), rows in stream order
+ *   tail_index  device int32 [B] or NULL (boundary b uses tails[b])
+ *   heads       [num_heads][K-1][C] raw inputs (x_dtype)
+ *   head_index  device int32 [B] or NULL (boundary b uses heads[b])
+ *   weight      [C][K] fp32;  bias [C] fp32 or NULL
+ *   out         [B][K-1][C] fp32
+ *   2 <= K <= 8.
+ * Error behaviour: an index outside its table sets
+ * HYPIC_EFLAG_SLOT_OUT_OF_RANGE and fills that boundary's output with NaN.
+ */
+hypic_status hypic_conv_warmup(int32_t num_boundaries, int32_t channels, int32_t kernel_size,
+                               int32_t x_dtype,
+                               const void *tails, int64_t num_tails, const int32_t *tail_index,
+                               const void *heads, int64_t num_heads, const int32_t *head_index,
+                               const float *weight, const float *bias, int32_t activation,
+                               float *out, uint32_t *err_flag, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *hypic_status_string(int32_t status);
+
+/* HYPIC_ABI_VERSION of the built library. */
+int32_t hypic_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYPIC_H */

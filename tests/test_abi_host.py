@@ -1,0 +1,152 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute call).
+
+* libhypic.so loads and exports every function include/hypic.h declares;
+* synchronous argument validation rejects bad calls before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hybrid_prefill_amd as hp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hypic.h")
+
+INVALID, UNSUPPORTED = 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(hypic_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(hp.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return hp.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(hp.EXPORTED) <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in hypic.h but not exported"
+
+
+def test_version_and_status_strings(L):
+    assert L.hypic_abi_version() == 1
+    assert L.hypic_status_string(0) == b"ok"
+    assert L.hypic_status_string(1) == b"invalid argument"
+    assert L.hypic_status_string(2) == b"unsupported configuration"
+    assert L.hypic_status_string(3) == b"HIP launch error"
+    assert L.hypic_status_string(99) == b"unknown status"
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def pool(family=hp.GDN, H=2, dk=64, dv=64, slots=4, P=True):
+    return hp._Pool(family, H, dk, dv, slots, FAKE, FAKE if P else None, FAKE)
+
+
+def segs(family=hp.GDN, H=2, dk=64, dv=64, nseg=1, dtype=hp.BF16, N=10, **kw):
+    s = hp._Segments(family, H, dk, dv, nseg, dtype, N, FAKE, FAKE, 64 * H, 64, FAKE, 64 * H, 64,
+                     None, 0, 0, FAKE, H, 1)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def build(L, s, p, slots=FAKE):
+    return L.hypic_build_segment(ctypes.byref(s) if s is not None else None,
+                                 ctypes.byref(p) if p is not None else None, slots, None, None)
+
+
+def test_build_validation(L):
+    assert build(L, None, pool()) == INVALID
+    assert build(L, segs(), None) == INVALID
+    assert build(L, segs(dk=96), pool(dk=96)) == UNSUPPORTED
+    assert build(L, segs(dv=32), pool(dv=32)) == UNSUPPORTED
+    assert build(L, segs(family=7), pool()) == UNSUPPORTED
+    assert build(L, segs(dtype=5), pool()) == UNSUPPORTED
+    assert build(L, segs(family=hp.SCALAR), pool()) == INVALID          # family mismatch
+    assert build(L, segs(H=3), pool()) == INVALID                       # head count mismatch
+    assert build(L, segs(), pool(P=False)) == INVALID                   # GDN pool needs P
+    assert build(L, segs(family=hp.SCALAR), pool(family=hp.SCALAR)) == INVALID  # P given for scalar
+    assert build(L, segs(nseg=-1), pool()) == INVALID
+    assert build(L, segs(N=-5), pool()) == INVALID
+    assert build(L, segs(seg_offsets=None), pool()) == INVALID
+    assert build(L, segs(), pool(), slots=None) == INVALID
+    assert build(L, segs(k=None), pool()) == INVALID
+    assert build(L, segs(k_stride_t=-1), pool()) == INVALID
+    # nothing to do is not an error and launches nothing
+    assert build(L, segs(nseg=0), pool()) == 0
+
+
+def test_compose_validation(L):
+    p = pool()
+    c = L.hypic_compose_chain
+    assert c(None, 1, FAKE, FAKE, 1, None, FAKE, None, None, None, None) == INVALID
+    assert c(ctypes.byref(p), -1, FAKE, FAKE, 1, None, FAKE, None, None, None, None) == INVALID
+    assert c(ctypes.byref(p), 1, None, FAKE, 1, None, FAKE, None, None, None, None) == INVALID
+    assert c(ctypes.byref(p), 1, FAKE, FAKE, 1, None, None, None, None, None, None) == INVALID
+    assert c(ctypes.byref(p), 1, FAKE, None, 3, None, FAKE, None, None, None, None) == INVALID
+    assert c(ctypes.byref(p), 1, FAKE, FAKE, -2, None, FAKE, None, None, None, None) == INVALID
+    ps = pool(family=hp.SCALAR, P=False)
+    assert c(ctypes.byref(ps), 1, FAKE, FAKE, 1, None, FAKE, None, FAKE, None, None) == INVALID  # out_P for scalar
+    pbad = pool(dk=32)
+    assert c(ctypes.byref(pbad), 1, FAKE, FAKE, 1, None, FAKE, None, None, None, None) == UNSUPPORTED
+    assert c(ctypes.byref(p), 0, None, None, 0, None, None, None, None, None, None) == 0
+
+
+def test_conv_validation(L):
+    c = L.hypic_conv_warmup
+    ok = dict(B=2, C=8, K=4, dt=hp.BF16, tails=FAKE, nt=2, ti=None, heads=FAKE, nh=2, hi=None,
+              w=FAKE, b=None, act=0, out=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return c(a["B"], a["C"], a["K"], a["dt"], a["tails"], a["nt"], a["ti"], a["heads"], a["nh"],
+                 a["hi"], a["w"], a["b"], a["act"], a["out"], None, None)
+
+    assert call(K=1) == UNSUPPORTED
+    assert call(K=9) == UNSUPPORTED
+    assert call(dt=3) == UNSUPPORTED
+    assert call(act=2) == UNSUPPORTED
+    assert call(C=0) == INVALID
+    assert call(B=-1) == INVALID
+    assert call(tails=None) == INVALID
+    assert call(w=None) == INVALID
+    assert call(out=None) == INVALID
+    assert call(nt=1) == INVALID        # fewer tails than boundaries and no index
+    assert call(B=0) == 0
+
+
+def test_ctypes_layout_matches_header(tmp_path):
+    """The binding's ctypes structs have the C header's field offsets and sizes."""
+    import subprocess
+    src = tmp_path / "layout.c"
+    fields = {"hypic_pool": [f for f, _ in hp._Pool._fields_],
+              "hypic_segments": [f for f, _ in hp._Segments._fields_]}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "hypic.h"', "int main(void) {"]
+    for T, fs in fields.items():
+        for f in fs:
+            lines.append(f'printf("{T} {f} %zu\\n", offsetof({T}, {f}));')
+        lines.append(f'printf("{T} __size %zu\\n", sizeof({T}));')
+    lines.append("return 0; }")
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    types = {"hypic_pool": hp._Pool, "hypic_segments": hp._Segments}
+    n = 0
+    for line in filter(None, out):
+        T, f, off = line.split()
+        want = ctypes.sizeof(types[T]) if f == "__size" else getattr(types[T], f).offset
+        assert want == int(off), (T, f, want, off)
+        n += 1
+    assert n == sum(len(v) + 1 for v in fields.values())

@@ -1,0 +1,303 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: relative Frobenius error <= 1e-4 for fp32 inputs and <= 2e-2 for
+bf16 inputs, per (segment or request, head); pool indexing bit-exact.
+Every input is seeded and synthetic (module ``synth``).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import hybrid_prefill_amd as hp
+import oracle
+import synth
+from oracle import rel_fro
+from parity_util import (TOL, dev_i32, dev_i64, full_log_alpha, np64, oracle_unit, record_errors,
+                         say)
+
+pytestmark = pytest.mark.gpu
+CANARY = 12345.0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hp.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------- inputs
+
+def make_inputs(family, lens, H, dk, dv, dtype, seed, variant="as_given"):
+    """Seeded stream for one family; variant 'weak' weakens the decay so the prefix matters."""
+    offs = synth.offsets_from_lengths(lens)
+    N = int(offs[-1])
+    k = synth.keys(N, H, dk, dtype, seed * 10 + 1, "cuda")
+    v = synth.values(N, H, dv, dtype, seed * 10 + 2, "cuda")
+    beta = None
+    if family == hp.GDN:
+        beta = synth.write_gate(N, H, seed * 10 + 3, "cuda")
+        scale = {"as_given": 0.1, "weak": 0.001, "none": 0.0}[variant]
+        la = synth.gdn_log_decay(N, H, seed * 10 + 4, scale, "cuda")
+    elif family == hp.SCALAR:
+        lo, hi = (0.9, 0.999) if variant == "as_given" else (0.9995, 0.99995)
+        la = synth.scalar_log_gamma(H, seed * 10 + 4, lo, hi, "cuda")
+    else:
+        div = 16.0 if variant == "as_given" else 1600.0
+        la = synth.diagonal_log_gates(N, H, dk, seed * 10 + 4, div, "cuda")
+    return dict(k=k, v=v, beta=beta, la=la, offs=offs, N=N)
+
+
+def host_inputs(family, inp, H):
+    return (np64(inp["k"]), np64(inp["v"]), full_log_alpha(family, inp["la"], inp["N"], H),
+            None if inp["beta"] is None else np64(inp["beta"]))
+
+
+def gpu_build(family, inp, H, dk, dv, slots, num_slots, err=None):
+    pool = hp.Pool.allocate(family, num_slots, H, dk, dv, device="cuda", fill=CANARY)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda") if err is None else err
+    hp.build_segment(family, inp["k"], inp["v"], inp["la"], dev_i64(inp["offs"]), pool, dev_i32(slots),
+                     beta=inp["beta"], err_flag=err)
+    return pool, err
+
+
+# ----------------------------------------------------------------------------- core check
+
+def check_build_compose(family, lens, H, dk, dv, dtype, seed, variant="as_given", units=None,
+                        seq_heads=None, label=""):
+    """Build every segment into permuted slots, compose the whole chain, compare with the oracle.
+
+    units: (segment, head) pairs whose records are checked (default all);
+    seq_heads: heads whose composed state is checked against the sequential
+    recurrence over the concatenation (default all).
+    """
+    tol = TOL[dtype]
+    nseg = len(lens)
+    num_slots = nseg + 3
+    slots = np.random.default_rng(seed).permutation(num_slots)[:nseg].astype(np.int32)
+    inp = make_inputs(family, lens, H, dk, dv, dtype, seed, variant)
+    say(f"[{label}] family={family} H={H} dk={dk} dv={dv} {dtype} lens={lens[:6]}{'...' if nseg > 6 else ''}")
+    pool, err = gpu_build(family, inp, H, dk, dv, slots, num_slots)
+    out_ell = torch.empty((1, H, dk) if family == hp.DIAGONAL else (1, H), device="cuda")
+    out_P = torch.empty((1, H, dk, dk), device="cuda") if family == hp.GDN else None
+    out_S = hp.compose_chain(pool, dev_i64([0, nseg]), dev_i32(slots), out_log_scale=out_ell,
+                             out_P=out_P, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    k, v, la, b = host_inputs(family, inp, H)
+    offs = inp["offs"]
+    # canary slots untouched, bit for bit
+    unused = sorted(set(range(num_slots)) - set(slots.tolist()))
+    assert torch.all(pool.S[unused] == CANARY)
+    assert torch.all(pool.log_scale[unused] == CANARY)
+    if units is None:
+        units = [(s, h) for s in range(nseg) for h in range(H)]
+    worst = [0.0, 0.0, 0.0]
+    for s, h in units:
+        ell_r, P_r, S_r = oracle_unit(family, k, v, la, b, int(offs[s]), int(offs[s + 1]), h)
+        sl = int(slots[s])
+        e = record_errors(family, np64(pool.log_scale[sl, h]),
+                          None if pool.P is None else np64(pool.P[sl, h]), np64(pool.S[sl, h]),
+                          ell_r, P_r, S_r)
+        worst = [max(a, c) for a, c in zip(worst, e)]
+    say(f"   records: max err S {worst[0]:.2e}  T {worst[1]:.2e}  ell {worst[2]:.2e}  (tol {tol:g})")
+    assert worst[0] <= tol and worst[1] <= tol and worst[2] <= tol
+    heads = range(H) if seq_heads is None else seq_heads
+    worst_seq = 0.0
+    naive = 0.0
+    for h in heads:
+        ell_q, P_q, S_q = oracle_unit(family, k, v, la, b, 0, inp["N"], h)
+        worst_seq = max(worst_seq, rel_fro(np64(out_S[0, h]), S_q))
+        e = record_errors(family, np64(out_ell[0, h]), None if out_P is None else np64(out_P[0, h]),
+                          np64(out_S[0, h]), ell_q, P_q, S_q)
+        worst_seq = max(worst_seq, e[1], e[2])
+        naive = max(naive, rel_fro(np64(pool.S[slots, h]).sum(axis=0), S_q))
+    say(f"   composed vs sequential: max err {worst_seq:.2e}; naive end-state sum err {naive:.2e}")
+    assert worst_seq <= tol
+    return naive
+
+
+# ----------------------------------------------------------------------------- configs
+
+def test_gdn_fp32_two_segments_of_256():
+    """GDN, 1 head, d_k=d_v=64, fp32, 2 x 256 tokens: build both, compose, vs sequential."""
+    check_build_compose(hp.GDN, [256, 256], 1, 64, 64, torch.float32, 101, label="gdn-1x64-fp32")
+
+
+@pytest.mark.parametrize("variant", ["weak", "none"])
+def test_gdn_fp32_two_segments_sensitivity(variant):
+    """Same shapes with weak (or no) decay: the prefix matters, naive addition must fail."""
+    naive = check_build_compose(hp.GDN, [256, 256], 1, 64, 64, torch.float32, 101, variant,
+                                label=f"gdn-1x64-fp32-{variant}")
+    assert naive > 1e-4
+
+
+@pytest.mark.parametrize("family", [hp.SCALAR, hp.DIAGONAL])
+@pytest.mark.parametrize("variant", ["as_given", "weak"])
+def test_scalar_diagonal_16_heads_8x2048(family, variant):
+    """Scalar and diagonal families, H=16, d=128, bf16, 8 segments x 2048 tokens, chain of 8."""
+    naive = check_build_compose(family, [2048] * 8, 16, 128, 128, torch.bfloat16, 201, variant,
+                                label=f"sd-{family}-{variant}")
+    if variant == "weak":
+        assert naive > 2e-2
+
+
+@pytest.mark.parametrize("variant", ["as_given", "none"])
+def test_gdn_32_heads_16x2048(variant):
+    """GDN H=32, d=128, bf16, one 32768-token request in 16 x 2048 segments (sampled)."""
+    units = [(0, 0), (5, 17), (9, 3), (15, 31), (15, 0), (7, 12)]
+    check_build_compose(hp.GDN, [2048] * 16, 32, 128, 128, torch.bfloat16, 301, variant, units=units,
+                        seq_heads=[0, 21], label=f"gdn-32x128-{variant}")
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+EDGE_LENS = [0, 1, 63, 64, 65, 127, 129, 200]
+
+
+@pytest.mark.parametrize("family", [hp.GDN, hp.SCALAR, hp.DIAGONAL])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_edge_lengths(family, dtype, dims):
+    dk, dv = dims
+    variant = "none" if family == hp.GDN else "weak"
+    check_build_compose(family, EDGE_LENS, 2, dk, dv, dtype, 401 + family, variant,
+                        label=f"edge-{family}-{dk}x{dv}")
+
+
+def test_special_gdn_inputs():
+    """beta = 0 (nothing written), log alpha = 0 (DeltaNet), a repeated key with beta = 1."""
+    H, d, n = 2, 64, 130
+    inp = make_inputs(hp.GDN, [n], H, d, d, torch.float32, 501)
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    pool, err = gpu_build(hp.GDN, inp, H, d, d, [0], 1)
+    torch.cuda.synchronize()
+    assert torch.all(pool.S == 0) and int(err.item()) == 0
+    eye = torch.eye(d, device="cuda").expand(1, H, d, d)
+    assert torch.equal(pool.P, eye)
+    ref = np64(inp["la"]).sum(axis=0)
+    assert np.max(np.abs(np64(pool.log_scale[0]) - ref)) < 1e-4
+    # repeated key, beta = 1, no decay: the last value overwrites
+    inp = make_inputs(hp.GDN, [n], H, d, d, torch.float32, 502, "none")
+    inp["k"][:] = inp["k"][0:1]
+    inp["beta"] = torch.ones_like(inp["beta"])
+    pool, err = gpu_build(hp.GDN, inp, H, d, d, [0], 1)
+    torch.cuda.synchronize()
+    for h in range(H):
+        ref = np.outer(np64(inp["k"][0, h]), np64(inp["v"][n - 1, h]))
+        assert rel_fro(np64(pool.S[0, h]), ref) < 1e-4
+
+
+# ----------------------------------------------------------------------------- pool indexing / errors
+
+def _gdn_pool(num_slots=6, H=2, d=64, seed=601):
+    lens = [70] * num_slots
+    inp = make_inputs(hp.GDN, lens, H, d, d, torch.float32, seed, "weak")
+    pool, err = gpu_build(hp.GDN, inp, H, d, d, list(range(num_slots)), num_slots)
+    torch.cuda.synchronize()
+    return pool
+
+
+def test_compose_indexing_bit_exact():
+    pool = _gdn_pool()
+    # chains of length 1 from a zero start return the slot's S bit for bit; repeats are fine
+    chains = [[3], [0], [5], [3]]
+    offs = np.concatenate([[0], np.cumsum([len(c) for c in chains])])
+    out = hp.compose_chain(pool, dev_i64(offs), dev_i32(sum(chains, [])))
+    torch.cuda.synchronize()
+    for r, c in enumerate(chains):
+        assert torch.equal(out[r], pool.S[c[0]])
+    # a record with ell = -inf forgets everything before it: output == its S exactly
+    pool.log_scale[4] = -math.inf
+    out = hp.compose_chain(pool, dev_i64([0, 3]), dev_i32([1, 2, 4]))
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], pool.S[4])
+    # empty chain: the init state comes back unchanged
+    init = torch.randn((2, 2, 64, 64), device="cuda")
+    out = hp.compose_chain(pool, dev_i64([0, 0, 1]), dev_i32([2]), init_S=init)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], init[0])
+
+
+def test_compose_out_of_range_slot_flags_and_isolates():
+    pool = _gdn_pool()
+    chains = [[0, 1, 2], [1, 9, 2], [3, 4]]          # slot 9 is outside the 6-slot pool
+    offs = dev_i64(np.concatenate([[0], np.cumsum([len(c) for c in chains])]))
+    flat = dev_i32(sum(chains, []))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ell = torch.empty((3, 2), device="cuda")
+    out = hp.compose_chain(pool, offs, flat, out_log_scale=ell, err_flag=err)
+    clean = hp.compose_chain(pool, dev_i64([0, 3, 5]), dev_i32([0, 1, 2, 3, 4]))
+    torch.cuda.synchronize()
+    assert int(err.item()) == hp.EFLAG_SLOT_OUT_OF_RANGE
+    assert torch.all(torch.isnan(out[1])) and torch.all(torch.isnan(ell[1]))
+    assert torch.equal(out[0], clean[0]) and torch.equal(out[2], clean[1])
+    # decreasing offsets: flag 2, NaN for that request only
+    err.zero_()
+    out = hp.compose_chain(pool, dev_i64([0, 2, 1, 3]), dev_i32([0, 1, 2]), err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & hp.EFLAG_BAD_OFFSETS
+    assert torch.all(torch.isnan(out[1])) and not torch.any(torch.isnan(out[0]))
+
+
+def test_build_error_flags():
+    H, d = 2, 64
+    inp = make_inputs(hp.GDN, [40, 50], H, d, d, torch.float32, 701)
+    pool = hp.Pool.allocate(hp.GDN, 3, H, d, d, device="cuda", fill=CANARY)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hp.build_segment(hp.GDN, inp["k"], inp["v"], inp["la"], dev_i64(inp["offs"]), pool, dev_i32([1, 7]),
+                     beta=inp["beta"], err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == hp.EFLAG_SLOT_OUT_OF_RANGE
+    assert torch.all(pool.S[[0, 2]] == CANARY) and not torch.any(pool.S[1] == CANARY)
+    # offsets beyond the stream: flag 2, NaN record in the (valid) slot
+    err.zero_()
+    hp.build_segment(hp.GDN, inp["k"], inp["v"], inp["la"], dev_i64([0, 40, 95]), pool, dev_i32([0, 2]),
+                     beta=inp["beta"], err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == hp.EFLAG_BAD_OFFSETS
+    assert torch.all(torch.isnan(pool.S[2])) and torch.all(torch.isnan(pool.P[2]))
+    assert not torch.any(torch.isnan(pool.S[0]))
+
+
+# ----------------------------------------------------------------------------- conv warm-up
+
+@pytest.mark.parametrize("K,C,dtype,act,bias", [(4, 4096, torch.bfloat16, 0, False),
+                                                (4, 4096, torch.bfloat16, 1, True),
+                                                (2, 96, torch.float32, 1, True),
+                                                (8, 200, torch.float32, 0, True)])
+def test_conv_warmup_equals_sequential_conv(K, C, dtype, act, bias):
+    rng = np.random.default_rng(800 + K)
+    lens = rng.integers(K, 40, size=12)
+    offs = synth.offsets_from_lengths(lens)
+    N = int(offs[-1])
+    x = synth.conv_stream(N, C, dtype, 801, "cuda")
+    w = synth.conv_weights(C, K, 802, "cuda")
+    bvec = torch.randn(C, device="cuda") if bias else None
+    # per segment: its first and last K-1 raw tokens, as a cache would keep them
+    heads = torch.stack([x[offs[s]:offs[s] + K - 1] for s in range(len(lens))]).contiguous()
+    tails = torch.stack([x[offs[s + 1] - (K - 1):offs[s + 1]] for s in range(len(lens))]).contiguous()
+    B = len(lens) - 1
+    out = hp.conv_warmup(tails, heads, w, bvec, act, tail_index=dev_i32(np.arange(B)),
+                         head_index=dev_i32(np.arange(1, B + 1)))
+    torch.cuda.synchronize()
+    y = oracle.causal_conv(np64(x), np64(w), None if bvec is None else np64(bvec), act)
+    worst = max(rel_fro(np64(out[b]), y[offs[b + 1]:offs[b + 1] + K - 1]) for b in range(B))
+    say(f"   conv warm-up K={K} C={C} {dtype} act={act}: max err {worst:.2e}")
+    assert worst <= 1e-4
+
+
+def test_conv_warmup_bad_index():
+    K, C = 4, 64
+    x = synth.conv_stream(12, C, torch.bfloat16, 810, "cuda").reshape(4, 3, C)
+    w = synth.conv_weights(C, K, 811, "cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = hp.conv_warmup(x, x, w, tail_index=dev_i32([0, 5, 1]), head_index=dev_i32([1, 2, 3]),
+                         err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == hp.EFLAG_SLOT_OUT_OF_RANGE
+    assert torch.all(torch.isnan(out[1])) and not torch.any(torch.isnan(out[[0, 2]]))
