@@ -53,11 +53,9 @@ struct __align__(16) Smem {
         struct { float A0[CH * AFL]; float A1[CH * AFL]; } a;   // A0 -> T0, A -> T (fp32, in place)
         struct { u16 W0n[CH * KML]; u16 Wsn[CH * KML]; } w;     // -W0, -Ws  [token][channel]
     } m;
-    union {
-        struct { u16 T0b[CH * TFL]; u16 Tgb[CH * TFL]; u16 Tb[CH * TFL]; } t;  // T0 diag(b), T diag(b e^g), T diag(b)
-        float scratch[4 * 256];                                                // 16x16 merge temporaries
-    } f;
-    float g[CH], eg[CH], egr[CH], beta[CH];
+    struct { u16 T0b[CH * TFL]; u16 Tgb[CH * TFL]; u16 Tb[CH * TFL]; } t;  // T0 diag(b), T diag(b e^g), T diag(b)
+    float scratch[2][512];                                                  // 16x16 merge temporaries
+    float g[CH], eg[CH], egr[CH], beta[CH], la[CH];
     float eG;
     int64_t t0, n;
     int32_t slot, state;
@@ -96,6 +94,14 @@ __device__ __forceinline__ u16 f2bf(float x) { return __builtin_bit_cast(u16, (_
 __device__ __forceinline__ u16 u4_elem(const uint4 &q, int e) {
     const uint32_t w = e < 2 ? q.x : e < 4 ? q.y : e < 6 ? q.z : q.w;
     return (u16)(w >> (16 * (e & 1)));
+}
+
+// Order this wave's LDS writes before its later LDS reads (the lanes of a wave
+// run in lockstep, so no workgroup barrier is needed when only this wave reads).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 // Row of the 32x32 accumulator element held in register r by lane half h.
@@ -146,16 +152,25 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             st[mb][r] = (!isS && 32 * mb + acc_row(r, h) == col0 + l32) ? 1.0f : 0.0f;
-    double ell = 0.0;   // thread 0
+    double ell = 0.0;   // thread 256 (wave 4, lane 0)
+    for (int e = th; e < 3 * CH * CH; e += NT) {
+        const int t = (e >> 6) & 63, s = e & 63;
+        if ((s >> 4) > (t >> 4)) {
+            u16 *dst = (e >> 12) == 0 ? sm.t.T0b : (e >> 12) == 1 ? sm.t.Tgb : sm.t.Tb;
+            dst[t * TFL + s] = 0;
+        }
+    }
 
     const u16 *kp = static_cast<const u16 *>(a.k);
     const u16 *vp = static_cast<const u16 *>(a.v);
-    // per thread: token row lt, 16 channels starting at lc (two 16-byte pieces)
-    const int lt = th >> 3, lc = 16 * (th & 7);
+    // per thread: token row lt = th / 8, 16 channels from lc = 16 (th % 8) (two 16-byte pieces)
     uint4 kreg[2], vreg[2];
     float breg = 0.f, lareg = 0.f;
 
     auto fetch = [&](int64_t base) {
+        int thf = th;
+        asm volatile("" : "+v"(thf));
+        const int lt = thf >> 3, lc = 16 * (thf & 7);
         const int64_t rem = n - base;
         const int cl = rem < CH ? (int)rem : CH;
         const int64_t t = t0 + base + lt;
@@ -177,6 +192,13 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
     if (n > 0) fetch(0);
 
     for (int64_t base = 0; base < n; base += CH) {
+        // Lane indices re-derived from an opaque copy each chunk: otherwise the
+        // compiler hoists every lane-dependent LDS address out of the loop and
+        // runs out of registers holding them.
+        int thv = th;
+        asm volatile("" : "+v"(thv));
+        const int l = thv & 63, h = l >> 5, l32 = l & 31;
+        const int lt = thv >> 3, lc = 16 * (thv & 7);
         // ---------------- 1. stage keys (Km, Kt) and gates
         *reinterpret_cast<uint4 *>(&sm.x.Km[lt * KML + lc]) = kreg[0];
         *reinterpret_cast<uint4 *>(&sm.x.Km[lt * KML + lc + 8]) = kreg[1];
@@ -185,30 +207,33 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
             sm.Kt[(lc + e) * KTL + lt] = u4_elem(kreg[0], e);
             sm.Kt[(lc + 8 + e) * KTL + lt] = u4_elem(kreg[1], e);
         }
+        if (th < CH) { sm.la[th] = lareg; sm.beta[th] = breg; }
         const uint4 vkeep0 = vreg[0], vkeep1 = vreg[1];
-        const float bcur = breg, lacur = lareg;
         if (base + CH < n) fetch(base + CH);     // next chunk's loads fly during this chunk
         __syncthreads();                                                   // B1
 
-        // ---------------- 2. gate scan (wave 0) | Gram blocks (waves 1-3)
+        // ---------------- 2. decay prefix (wave 0) | Gram blocks (waves 1-3)
         f32x16 gacc;
         const int gmb = (w >= 2) ? 1 : 0, gnb = (w == 3) ? 1 : 0;
         if (w == 0) {
-            float gv = lacur;
+            // lane t: g_t = sum_{s<=t} log alpha_s (inclusive scan), G = g_63
+            float gv = sm.la[l];
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
                 const float y = __shfl_up(gv, o);
                 if (l >= o) gv += y;
             }
-            const float G = __shfl(gv, 63);
+            const float gt = __shfl(gv, 63);
             sm.g[l] = gv;
             sm.eg[l] = __expf(gv);
-            sm.egr[l] = __expf(G - gv);
-            sm.beta[l] = bcur;
-            double sd = (double)lacur;
+            sm.egr[l] = __expf(gt - gv);
+            if (l == 63) sm.eG = __expf(gt);
+        } else if (w == 4) {
+            // the segment total of log alpha in fp64 (thread 256 keeps it)
+            double gd = (double)sm.la[l];
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) sd += __shfl_xor(sd, o);
-            if (l == 0) { ell += sd; sm.eG = __expf(G); }
+            for (int o = 32; o >= 1; o >>= 1) gd += __shfl_xor(gd, o);
+            ell += gd;
         } else if (w <= 3) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) gacc[r] = 0.f;
@@ -242,9 +267,23 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         }
         __syncthreads();                                                   // B3
 
-        // ---------------- 4. 16x16 diagonal blocks of T0 (wave 0) and T (wave 4)
-        if (w == 0 || w == 4) {
-            float *M = w == 0 ? sm.m.a.A0 : sm.m.a.A1;
+        // ---------------- 4. UT transform: T0 = (I+A0)^-1, T = (I+A)^-1 in 16x16 blocks,
+        //                     writing the bf16 column-scaled forms as blocks become final
+        // emit: write the bf16 column-scaled forms of a final T entry (t, s)
+        //   matrix 0: T0 diag(beta) -> T0b;  matrix 1: T diag(beta) -> Tb, T diag(beta e^g) -> Tgb
+#define HYPIC_EMIT(MAT_, ROW_, COL_, VAL_, SB_, SG_)                          \
+    do {                                                                     \
+        if ((MAT_) == 0) {                                                   \
+            sm.t.T0b[(ROW_) * TFL + (COL_)] = f2bf((VAL_) * (SB_));          \
+        } else {                                                             \
+            sm.t.Tb[(ROW_) * TFL + (COL_)] = f2bf((VAL_) * (SB_));           \
+            sm.t.Tgb[(ROW_) * TFL + (COL_)] = f2bf((VAL_) * (SG_));          \
+        }                                                                    \
+    } while (0)
+        // (a) 16x16 diagonal blocks by forward substitution: wave 0 -> T0, wave 1 -> T
+        if (w <= 1) {
+            const int mat = w;
+            float *M = mat == 0 ? sm.m.a.A0 : sm.m.a.A1;
             const int R = 16 * (l >> 4), j = l & 15;
             float x[16];
 #pragma unroll
@@ -254,13 +293,16 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 for (int s = 0; s < i; ++s) acc += M[(R + i) * AFL + R + s] * x[s];
                 x[i] = (i == j) ? 1.0f : (i < j ? 0.0f : -acc);
             }
+            const float sb = sm.beta[R + j], sg = sb * sm.eg[R + j];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) M[(R + i) * AFL + R + j] = x[i];
+            for (int i = 0; i < 16; ++i) {
+                M[(R + i) * AFL + R + j] = x[i];
+                HYPIC_EMIT(mat, R + i, R + j, x[i], sb, sg);
+            }
         }
         __syncthreads();                                                   // B4
 
-        // ---------------- 5. 16 -> 32 merge: T_{q1,q0} = -T_{q1,q1} A_{q1,q0} T_{q0,q0}
-        //                     tasks (matrix, half) on waves 0-3, 4 rows x 1 column per lane
+        // (b) 16 -> 32: T_10 = -T_11 A_10 T_00, tasks (matrix, half) on waves 0-3
         const int mrow = 4 * (l >> 4), mcol = l & 15;
         if (w < 4) {
             const float *M = (w >> 1) ? sm.m.a.A1 : sm.m.a.A0;
@@ -273,29 +315,33 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 float acc = 0.f;
 #pragma unroll
                 for (int k = 0; k < 16; ++k) acc += M[(R1 + mrow + r) * AFL + R0 + k] * tl[k];
-                sm.f.scratch[w * 256 + (mrow + r) * 16 + mcol] = acc;
+                sm.scratch[w >> 1][256 * (w & 1) + (mrow + r) * 16 + mcol] = acc;
             }
         }
         __syncthreads();                                                   // B5
         if (w < 4) {
-            float *M = (w >> 1) ? sm.m.a.A1 : sm.m.a.A0;
+            const int mat = w >> 1;
+            float *M = mat ? sm.m.a.A1 : sm.m.a.A0;
             const int R0 = 32 * (w & 1), R1 = R0 + 16;
             float tc[16];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) tc[k] = sm.f.scratch[w * 256 + k * 16 + mcol];
+            for (int k = 0; k < 16; ++k) tc[k] = sm.scratch[mat][256 * (w & 1) + k * 16 + mcol];
+            const float sb = sm.beta[R0 + mcol], sg = sb * sm.eg[R0 + mcol];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float acc = 0.f;
 #pragma unroll
                 for (int k = 0; k < 16; ++k) acc += M[(R1 + mrow + r) * AFL + R1 + k] * tc[k];
                 M[(R1 + mrow + r) * AFL + R0 + mcol] = -acc;
+                HYPIC_EMIT(mat, R1 + mrow + r, R0 + mcol, -acc, sb, sg);
             }
         }
         __syncthreads();                                                   // B6
 
-        // ---------------- 6. 32 -> 64 merge: T_21 = -T_22 A_21 T_11 (bf16 MFMA), waves 0 and 4
-        if (w == 0 || w == 4) {
-            float *M = w == 0 ? sm.m.a.A0 : sm.m.a.A1;
+        // (c) 32 -> 64: T_21 = -T_22 A_21 T_11 on bf16 MFMA, waves 0 and 1
+        if (w <= 1) {
+            const int mat = w;
+            const float *M = mat == 0 ? sm.m.a.A0 : sm.m.a.A1;
             f32x16 tmp;
 #pragma unroll
             for (int r = 0; r < 16; ++r) tmp[r] = 0.f;
@@ -317,25 +363,16 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 const bf16x8 fa = pack8(ar[0], ar[1], ar[2], ar[3], ar[8], ar[9], ar[10], ar[11]);
                 o = mfma(fa, acc_to_b(tmp, half), o);
             }
+            const float sb = sm.beta[l32], sg = sb * sm.eg[l32];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) M[(32 + acc_row(r, h)) * AFL + l32] = -o[r];
+            for (int r = 0; r < 16; ++r) HYPIC_EMIT(mat, 32 + acc_row(r, h), l32, -o[r], sb, sg);
         }
+#undef HYPIC_EMIT
         __syncthreads();                                                   // B7
 
-        // ---------------- 7. scaled bf16 forms: T0 diag(b), T diag(b e^g), T diag(b)
-        for (int e = th; e < 3 * CH * CH; e += NT) {
-            const int which = e >> 12, t = (e >> 6) & 63, s = e & 63;
-            const float *M = which == 0 ? sm.m.a.A0 : sm.m.a.A1;
-            float val = s <= t ? M[t * AFL + s] : 0.0f;
-            val *= which == 1 ? sm.beta[s] * sm.eg[s] : sm.beta[s];
-            u16 *dst = which == 0 ? sm.f.t.T0b : which == 1 ? sm.f.t.Tgb : sm.f.t.Tb;
-            dst[t * TFL + s] = f2bf(val);
-        }
-        __syncthreads();                                                   // B8
-
-        // ---------------- 8. -W0, -Ws (all waves, 2 tiles each) and U (S waves, own columns)
+        // ---------------- 5. -W0, -Ws (all waves, 2 tiles each) and U (S waves, own columns)
         {
-            const u16 *TF = (w >> 2) ? sm.f.t.Tgb : sm.f.t.T0b;
+            const u16 *TF = (w >> 2) ? sm.t.Tgb : sm.t.T0b;
             u16 *Wd = (w >> 2) ? sm.m.w.Wsn : sm.m.w.W0n;
             const int mb = (w >> 1) & 1;
 #pragma unroll
@@ -363,14 +400,14 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     if (ks >= 2 && mb == 0) break;
-                    acc[mb] = mfma(lds8(&sm.f.t.Tb[(32 * mb + l32) * TFL + 16 * ks + 8 * h]),
+                    acc[mb] = mfma(lds8(&sm.t.Tb[(32 * mb + l32) * TFL + 16 * ks + 8 * h]),
                                    lds8(&sm.x.Vt[(col0 + l32) * KTL + 16 * ks + 8 * h]), acc[mb]);
                 }
             }
         }
-        __syncthreads();                                                   // B9
+        __syncthreads();                                                   // B8
 
-        // ---------------- 9. carry: Y = (U) - W . state ; state += K^T diag(.) Y
+        // ---------------- 6. carry: Y = (U) - W . state ; state += K^T diag(.) Y
         {
             const u16 *Wn = isS ? sm.m.w.Wsn : sm.m.w.W0n;
 #pragma unroll
@@ -403,7 +440,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 }
             }
         }
-        __syncthreads();                                                   // B10
+        __syncthreads();                                                   // B9
     }
 
     // ---------------- record
@@ -416,7 +453,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             dst[(int64_t)(32 * mb + acc_row(r, h)) * D + col0 + l32] = bad ? nanv : st[mb][r];
-    if (th == 0) a.pool_ell[rec] = bad ? nanv : (float)ell;
+    if (th == 256) a.pool_ell[rec] = bad ? nanv : (float)ell;
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
