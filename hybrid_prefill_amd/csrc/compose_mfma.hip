@@ -19,7 +19,9 @@
 // tiles (rows 0-127).  P_i is staged once per step through LDS as bf16 hi/lo
 // fragments laid out in MFMA operand order (one 16-byte read per lane, no bank
 // conflicts); the B operand comes from the state's accumulator registers.  The
-// next record's P is prefetched into registers while the current product runs.
+// next record is prefetched while the current product runs: P into registers
+// (coalesced 16-byte loads), S straight from HBM into LDS (global_load_lds),
+// read back from LDS in accumulator order.
 #include "hypic_internal.h"
 
 namespace hypic {
@@ -34,7 +36,12 @@ typedef uint16_t u16;
 constexpr int D = 128;
 constexpr int NT = 256;
 constexpr int NFRAG = 4 * 8;          // (row block mb, k-step kb) fragments of P
-constexpr int FRAG_U32 = 64 * 4;      // one fragment: 64 lanes x 8 bf16
+// One fragment holds 64 lanes x 8 bf16 (4 dwords per lane).  Lane half h is
+// placed 132 dwords after half 0 and fragments 264 dwords apart, so that the
+// 8-byte staging writes of 16 consecutive threads (4 k-steps x 4 pieces) hit
+// 16 distinct bank pairs, and the 16-byte operand reads stay conflict-free.
+constexpr int FRAG_U32 = 264;
+__device__ __forceinline__ int lane_slot(int li, int hh) { return 4 * li + 132 * hh; }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -70,9 +77,10 @@ __device__ __forceinline__ void acc_to_b2(const f32x16 &c, int half, bf16x8 &bh,
 // k-step kb, in the order that pairs with acc_to_b2 (k-step kb covers the
 // 16 columns 16*kb .. 16*kb+15; lane half h takes columns 4h..4h+3 and
 // 8+4h..8+4h+3 of them, as elements 0-3 and 4-7).
-struct PStage {
+struct __align__(16) PStage {
     uint32_t hi[NFRAG * FRAG_U32];
     uint32_t lo[NFRAG * FRAG_U32];
+    float s[D * D];                   // S_i, row-major, loaded straight from HBM into LDS
 };
 
 template <bool MODE_P>
@@ -140,14 +148,29 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
 
     // ---- P staging: thread th loads float4 pieces q = th + 256*u (u < 16) of P, row q/32,
     //      columns 4*(q%32) .. +3
+    // both P_c and S_c are fetched as coalesced 16-byte pieces q = th + 256 u
+    // P_c: coalesced 16-byte pieces q = th + 256 u into registers, split to bf16 hi/lo
+    // fragments in LDS at the top of the step.  S_c: HBM -> LDS directly (no
+    // registers), wave w's instruction u moving pieces (16 w + u) * 64 + lane.
     float4 pre[16];
-    auto fetchP = [&](int64_t cc) {
-        const int64_t rec = (int64_t)a.chain_slots[cc] * a.H + head;
-        const float4 *src = reinterpret_cast<const float4 *>(a.pool_P + rec * D * D);
-#pragma unroll
-        for (int u = 0; u < 16; ++u) pre[u] = src[th + NT * u];
-    };
-    if (c < c_hi) fetchP(c);
+#define HYPIC_FETCH_P(CC)                                                                        \
+    do {                                                                                         \
+        const int64_t frec = (int64_t)a.chain_slots[(CC)] * a.H + head;                          \
+        const float4 *fsrc = reinterpret_cast<const float4 *>(a.pool_P + frec * D * D);          \
+        _Pragma("unroll") for (int u = 0; u < 16; ++u) pre[u] = fsrc[th + NT * u];               \
+    } while (0)
+#define HYPIC_FETCH_S(CC)                                                                        \
+    do {                                                                                         \
+        const int64_t frec = (int64_t)a.chain_slots[(CC)] * a.H + head;                          \
+        const float4 *fss = reinterpret_cast<const float4 *>(a.pool_S + frec * D * D);           \
+        _Pragma("unroll") for (int u = 0; u < 16; ++u)                                           \
+            __builtin_amdgcn_global_load_lds(fss + (16 * w + u) * 64 + l,                       \
+                                             &ps.s[(16 * w + u) * 256], 16, 0, 0);               \
+    } while (0)
+    if (c < c_hi) {
+        HYPIC_FETCH_P(c);
+        if (!MODE_P) HYPIC_FETCH_S(c);
+    }
 
     for (; c < c_hi; ++c) {
         const int64_t rec = (int64_t)a.chain_slots[c] * a.H + head;
@@ -164,25 +187,33 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
             split(pre[u].y, hi[1], lo[1]);
             split(pre[u].z, hi[2], lo[2]);
             split(pre[u].w, hi[3], lo[3]);
-            const int slot = (mb * 8 + kb) * FRAG_U32 + (li + 32 * hh) * 4 + (e0 >> 1);
+            const int slot = (mb * 8 + kb) * FRAG_U32 + lane_slot(li, hh) + (e0 >> 1);
             *reinterpret_cast<u32x2 *>(&ps.hi[slot]) =
                 u32x2{(uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16)};
             *reinterpret_cast<u32x2 *>(&ps.lo[slot]) =
                 u32x2{(uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)};
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this wave's S_c pieces have landed
         __syncthreads();
-        if (c + 1 < c_hi) fetchP(c + 1);     // next record's P flies during this product
-        // this record's S columns (addend), loaded now, consumed after the product
         float sadd[4][16];
         if (!MODE_P) {
-            const float *src = a.pool_S + rec * D * D;
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-                for (int q = 0; q < 16; ++q) sadd[mb][q] = src[(32 * mb + acc_row(q, h)) * D + col0 + l32];
+                for (int q = 0; q < 16; ++q) sadd[mb][q] = ps.s[(32 * mb + acc_row(q, h)) * D + col0 + l32];
+            __syncthreads();                                   // S_c read by all before S_{c+1} lands
+        }
+        if (c + 1 < c_hi) {                                    // the next record flies during this product
+            HYPIC_FETCH_P(c + 1);
+            if (!MODE_P) HYPIC_FETCH_S(c + 1);
         }
         const float le = a.pool_ell[rec];
         // acc = P_c * state, hi.hi + hi.lo + lo.hi
+        // the state's B fragments (hi, lo) for all 8 k-steps, once per step; the
+        // state itself is not needed again until the combine overwrites it
+        bf16x8 bh[8], bl[8];
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) acc_to_b2(st[kb >> 1], kb & 1, bh[kb], bl[kb]);
         f32x16 acc[4];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
@@ -190,17 +221,19 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
             for (int q = 0; q < 16; ++q) acc[mb][q] = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
-            bf16x8 bh, bl;
-            acc_to_b2(st[kb >> 1], kb & 1, bh, bl);
+            bf16x8 ah[4], al[4];
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
-                const int f = (mb * 8 + kb) * FRAG_U32 + l * 4;
-                const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&ps.hi[f]));
-                const bf16x8 al = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&ps.lo[f]));
-                acc[mb] = mfma(ah, bh, acc[mb]);
-                acc[mb] = mfma(ah, bl, acc[mb]);
-                acc[mb] = mfma(al, bh, acc[mb]);
+                const int f = (mb * 8 + kb) * FRAG_U32 + lane_slot(l32, h);
+                ah[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&ps.hi[f]));
+                al[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&ps.lo[f]));
             }
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma(ah[mb], bh[kb], acc[mb]);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma(ah[mb], bl[kb], acc[mb]);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma(al[mb], bh[kb], acc[mb]);
         }
         if (MODE_P) {
 #pragma unroll
@@ -215,7 +248,8 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
         ell += (double)le;
         __syncthreads();     // everyone is done with this P before the next is staged
     }
-
+#undef HYPIC_FETCH_P
+#undef HYPIC_FETCH_S
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
