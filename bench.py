@@ -195,24 +195,30 @@ def bench_compose_pool(args, slots=4096, H=32, d=128, R=64, m=32, seg_len=64, se
             "roofline": roofline("hbm", nbytes / (ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s")}
 
 
-def bench_sd(args, H=16, d=128, nseg=8, seg_len=2048, seed=201):
+def bench_sd(args, H=16, d=128, nseg=8, seg_len=2048, seed=201, copies=3):
+    """Scalar and diagonal builds + their 8-segment chains.  The inputs are
+    rotated over `copies` seeded copies so that the timed working set exceeds
+    the 256 MB Infinity Cache (one copy of k, v and the gates would fit)."""
     out = []
     N = nseg * seg_len
-    k = synth.keys(N, H, d, torch.bfloat16, seed * 10 + 1, "cuda")
-    v = synth.values(N, H, d, torch.bfloat16, seed * 10 + 2, "cuda")
+    ks = [synth.keys(N, H, d, torch.bfloat16, seed * 10 + 1 + 100 * c, "cuda") for c in range(copies)]
+    vs = [synth.values(N, H, d, torch.bfloat16, seed * 10 + 2 + 100 * c, "cuda") for c in range(copies)]
     offs = torch.as_tensor(synth.even_offsets(nseg, seg_len)).cuda()
     slots = torch.arange(nseg, dtype=torch.int32, device="cuda")
     chain = torch.tensor([0, nseg], dtype=torch.int64, device="cuda")
     for fam, name in ((hp.SCALAR, "scalar"), (hp.DIAGONAL, "diagonal")):
-        la = (synth.scalar_log_gamma(H, seed * 10 + 4, device="cuda") if fam == hp.SCALAR
-              else synth.diagonal_log_gates(N, H, d, seed * 10 + 4, device="cuda"))
+        las = ([synth.scalar_log_gamma(H, seed * 10 + 4 + 100 * c, device="cuda") for c in range(copies)]
+               if fam == hp.SCALAR else
+               [synth.diagonal_log_gates(N, H, d, seed * 10 + 4 + 100 * c, device="cuda") for c in range(copies)])
         pool = hp.Pool.allocate(fam, nseg, H, d, d, device="cuda")
         timer = KernelTimer()
-        for _ in range(args.warmup):
-            hp.build_segment(fam, k, v, la, offs, pool, slots)
+        for i in range(args.warmup):
+            c = i % copies
+            hp.build_segment(fam, ks[c], vs[c], las[c], offs, pool, slots)
         torch.cuda.synchronize()
-        for _ in range(max(3, args.steps)):
-            timer.time("build", lambda: hp.build_segment(fam, k, v, la, offs, pool, slots))
+        for i in range(max(3, args.steps)):
+            c = i % copies
+            timer.time("build", lambda: hp.build_segment(fam, ks[c], vs[c], las[c], offs, pool, slots))
             timer.time("compose", lambda: hp.compose_chain(pool, chain, slots))
         b_ms, c_ms = timer.mean_ms("build"), timer.mean_ms("compose")
         nb = sd_build_bytes(fam, N, H, d, d, nseg)
@@ -220,6 +226,7 @@ def bench_sd(args, H=16, d=128, nseg=8, seg_len=2048, seed=201):
         out.append({"workload": f"{name}_build_h{H}_d{d}_{nseg}x{seg_len}", "metric": "tokens/s",
                     "value": N / (b_ms * 1e-3), "unit": "tokens/s", "ms": b_ms, "compose_ms": c_ms,
                     "roofline": roofline("hbm", nb / (b_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s")})
+        del las, pool
     return out
 
 

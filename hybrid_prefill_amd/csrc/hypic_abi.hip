@@ -8,6 +8,7 @@
 namespace hypic {
 hipError_t launch_build_ref(const BuildArgs &a, hipStream_t stream);
 hipError_t launch_build_mfma(const BuildArgs &a, hipStream_t stream, bool *taken);
+hipError_t launch_build_sd_mfma(const BuildArgs &a, hipStream_t stream, bool *taken);
 hipError_t launch_compose_ref(const ComposeArgs &a, hipStream_t stream);
 hipError_t launch_compose_mfma(const ComposeArgs &a, hipStream_t stream, bool *taken);
 }  // namespace hypic
@@ -80,6 +81,7 @@ hypic_status hypic_build_segment(const hypic_segments *in, const hypic_pool *poo
     hipStream_t st = static_cast<hipStream_t>(stream);
     bool taken = false;
     hipError_t e = launch_build_mfma(a, st, &taken);
+    if (!taken) e = launch_build_sd_mfma(a, st, &taken);
     if (!taken) e = launch_build_ref(a, st);
     return e == hipSuccess ? HYPIC_OK : HYPIC_ERR_HIP;
 }
