@@ -42,11 +42,11 @@ constexpr int NT = 256;
 constexpr int KML = 136;   // row length (bf16) of the token-major k / v tiles
 constexpr int GL = 132;    // row length (fp32) of the token-major gate tile (diagonal)
 
-template <int FAM>
+template <int FAM, int NJB>
 struct __align__(16) SdSmem {
     u16 Km[CH * KML];
-    u16 Vm[CH * KML];
-    uint32_t vx[4 * 4 * 64 * 4];            // V^T B fragments: [j block][k-step][lane] x 16 B
+    u16 Vm[CH * (32 * NJB + 8)];            // this workgroup's value columns, token-major
+    uint32_t vx[NJB * 4 * 64 * 4];          // V^T B fragments: [j block][k-step][lane] x 16 B
     float gate[FAM == HYPIC_DIAGONAL ? CH * GL : 1];
     float la[CH], beta[CH], wsc[CH];        // per-token log decay, write gate, scalar-family scale
     float gd[D];                            // diagonal: per-channel chunk decay G_i
@@ -72,15 +72,27 @@ __device__ __forceinline__ bf16x8 lds8(const u16 *p) {
 }
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-template <int FAM>
-__global__ __launch_bounds__(NT, 1) void sd_build_mfma_kernel(BuildArgs a) {
-    __shared__ SdSmem<FAM> sm;
+// NSPLIT workgroups share one (segment, head): workgroup q keeps the value
+// columns [128 q / NSPLIT, 128 (q+1) / NSPLIT).  They all read the keys (and
+// gates); block ids are laid out so the NSPLIT workgroups of a unit land on the
+// same XCD (consecutive block ids go to consecutive XCDs), where the repeated
+// key reads hit that XCD's L2 instead of HBM.
+template <int FAM, int NSPLIT>
+__global__ __launch_bounds__(NT, FAM == HYPIC_DIAGONAL ? 1 : 2) void sd_build_mfma_kernel(BuildArgs a) {
+    constexpr int NJB = 4 / NSPLIT;          // 32-column value blocks per workgroup
+    constexpr int VML = 32 * NJB + 8;
+    __shared__ SdSmem<FAM, NJB> sm;
     constexpr bool DIAG = FAM == HYPIC_DIAGONAL;
 
     const int th = threadIdx.x;
     const int w = th >> 6, l = th & 63, h = l >> 5, l32 = l & 31;
-    const int head = blockIdx.x % a.H;
-    const int seg = blockIdx.x / a.H;
+    const int b = blockIdx.x;
+    const int q = (b >> 3) % NSPLIT;
+    const int unit = (b / (8 * NSPLIT)) * 8 + (b & 7);
+    const int head = unit % a.H;
+    const int seg = unit / a.H;
+    const int jc0 = 32 * NJB * q;            // first value column of this workgroup
+    if (seg >= a.num_segments) return;       // grid padding
 
     if (th == 0) {
         const int64_t o0 = a.seg_offsets[seg], o1 = a.seg_offsets[seg + 1];
@@ -88,8 +100,8 @@ __global__ __launch_bounds__(NT, 1) void sd_build_mfma_kernel(BuildArgs a) {
         int st = 0;
         if (slot < 0 || slot >= a.num_slots) st = 1;
         else if (o0 < 0 || o1 < o0 || o1 > a.num_tokens) st = 2;
-        if (st == 1) raise_flag(a.err_flag, HYPIC_EFLAG_SLOT_OUT_OF_RANGE);
-        if (st == 2) raise_flag(a.err_flag, HYPIC_EFLAG_BAD_OFFSETS);
+        if (st == 1 && q == 0) raise_flag(a.err_flag, HYPIC_EFLAG_SLOT_OUT_OF_RANGE);
+        if (st == 2 && q == 0) raise_flag(a.err_flag, HYPIC_EFLAG_BAD_OFFSETS);
         sm.t0 = o0; sm.n = o1 - o0; sm.slot = slot; sm.state = st;
     }
     __syncthreads();
@@ -99,9 +111,9 @@ __global__ __launch_bounds__(NT, 1) void sd_build_mfma_kernel(BuildArgs a) {
     const int64_t n = state == 2 ? 0 : sm.n;
     const int64_t slot = sm.slot;
 
-    f32x16 st[4];
+    f32x16 st[NJB];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
+    for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[jb][r] = 0.f;
     double ell = 0.0;   // scalar: thread 0; diagonal: lanes of half 0 keep channel 32w + l32
@@ -116,7 +128,7 @@ __global__ __launch_bounds__(NT, 1) void sd_build_mfma_kernel(BuildArgs a) {
     const u16 *kp = static_cast<const u16 *>(a.k);
     const u16 *vp = static_cast<const u16 *>(a.v);
     // per thread: 16-byte pieces p = th + 256 u (u < 4) of the 64 x 128 chunk: row p/16, channels 8 (p%16)
-    uint4 kr[4], vr[4];
+    uint4 kr[4], vr[NJB];
     float4 gr[8];
     float br = 0.f, lr = 0.f;
 
@@ -126,14 +138,15 @@ __global__ __launch_bounds__(NT, 1) void sd_build_mfma_kernel(BuildArgs a) {
         const int cl_ = rem_ < CH ? (int)rem_ : CH;                                                    \
         _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                                \
             const int p = th + NT * u, t = p >> 4, c8 = 8 * (p & 15);                                  \
-            if (t < cl_) {                                                                             \
-                const int64_t tt = t0 + (BASE) + t;                                                    \
-                kr[u] = *reinterpret_cast<const uint4 *>(kp + tt * a.k_st + head * a.k_sh + c8);       \
-                vr[u] = *reinterpret_cast<const uint4 *>(vp + tt * a.v_st + head * a.v_sh + c8);       \
-            } else {                                                                                   \
-                kr[u] = make_uint4(0, 0, 0, 0);                                                        \
-                vr[u] = make_uint4(0, 0, 0, 0);                                                        \
-            }                                                                                          \
+            kr[u] = t < cl_ ? *reinterpret_cast<const uint4 *>(kp + (t0 + (BASE) + t) * a.k_st +       \
+                                                                head * a.k_sh + c8)                    \
+                            : make_uint4(0, 0, 0, 0);                                                  \
+        }                                                                                              \
+        _Pragma("unroll") for (int u = 0; u < NJB; ++u) {                                              \
+            const int p = th + NT * u, t = p / (4 * NJB), c8 = 8 * (p % (4 * NJB));                    \
+            vr[u] = t < cl_ ? *reinterpret_cast<const uint4 *>(vp + (t0 + (BASE) + t) * a.v_st +       \
+                                                                head * a.v_sh + jc0 + c8)              \
+                            : make_uint4(0, 0, 0, 0);                                                  \
         }                                                                                              \
         if (DIAG) {                                                                                    \
             _Pragma("unroll") for (int u = 0; u < 8; ++u) {                                            \
@@ -159,7 +172,11 @@ __global__ __launch_bounds__(NT, 1) void sd_build_mfma_kernel(BuildArgs a) {
         for (int u = 0; u < 4; ++u) {
             const int p = th + NT * u, t = p >> 4, c8 = 8 * (p & 15);
             *reinterpret_cast<uint4 *>(&sm.Km[t * KML + c8]) = kr[u];
-            *reinterpret_cast<uint4 *>(&sm.Vm[t * KML + c8]) = vr[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NJB; ++u) {
+            const int p = th + NT * u, t = p / (4 * NJB), c8 = 8 * (p % (4 * NJB));
+            *reinterpret_cast<uint4 *>(&sm.Vm[t * VML + c8]) = vr[u];
         }
         if (DIAG) {
 #pragma unroll
@@ -197,9 +214,9 @@ __global__ __launch_bounds__(NT, 1) void sd_build_mfma_kernel(BuildArgs a) {
             for (int r = 0; r < 16; ++r) { dk[tb][r] = 0.f; dv[tb][r] = 0.f; }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const int off = (32 * tb + l32) * KML + 32 * w + 16 * ks + 8 * h;
-                dk[tb] = mfma(lds8(&sm.Km[off]), eye[ks], dk[tb]);
-                dv[tb] = mfma(lds8(&sm.Vm[off]), eye[ks], dv[tb]);
+                dk[tb] = mfma(lds8(&sm.Km[(32 * tb + l32) * KML + 32 * w + 16 * ks + 8 * h]), eye[ks], dk[tb]);
+                if (w < NJB)
+                    dv[tb] = mfma(lds8(&sm.Vm[(32 * tb + l32) * VML + 32 * w + 16 * ks + 8 * h]), eye[ks], dv[tb]);
             }
         }
         // ---- per-channel gates (diagonal): lane (l32, h) runs the cumulative sum of channel
@@ -244,7 +261,7 @@ __global__ __launch_bounds__(NT, 1) void sd_build_mfma_kernel(BuildArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             ka[ks] = __builtin_bit_cast(bf16x8, pack8u(dk[ks >> 1], ks & 1));
-            *reinterpret_cast<u32x4 *>(&sm.vx[((w * 4 + ks) * 64 + l) * 4]) = pack8u(dv[ks >> 1], ks & 1);
+            if (w < NJB) *reinterpret_cast<u32x4 *>(&sm.vx[((w * 4 + ks) * 64 + l) * 4]) = pack8u(dv[ks >> 1], ks & 1);
         }
         // decay of the carried state
         if (DIAG) {
@@ -252,19 +269,19 @@ __global__ __launch_bounds__(NT, 1) void sd_build_mfma_kernel(BuildArgs a) {
             for (int r = 0; r < 16; ++r) {
                 const float f = __expf(sm.gd[32 * w + acc_row(r, h)]);
 #pragma unroll
-                for (int jb = 0; jb < 4; ++jb) st[jb][r] *= f;
+                for (int jb = 0; jb < NJB; ++jb) st[jb][r] *= f;
             }
         } else {
             const float f = sm.eG;
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb)
+            for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) st[jb][r] *= f;
         }
         __syncthreads();
-        // ---- S[own rows][:] += K^T V over the chunk's 64 tokens
+        // ---- S[own rows][own columns] += K^T V over the chunk's 64 tokens
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
+        for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const bf16x8 vb =
@@ -281,10 +298,11 @@ __global__ __launch_bounds__(NT, 1) void sd_build_mfma_kernel(BuildArgs a) {
     const int64_t rec = slot * a.H + head;
     float *dst = a.pool_S + rec * D * D;
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
+    for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            dst[(int64_t)(32 * w + acc_row(r, h)) * D + 32 * jb + l32] = bad ? nanv : st[jb][r];
+            dst[(int64_t)(32 * w + acc_row(r, h)) * D + jc0 + 32 * jb + l32] = bad ? nanv : st[jb][r];
+    if (q != 0) return;
     if (DIAG) {
         if (h == 0) a.pool_ell[rec * D + 32 * w + l32] = bad ? nanv : (float)ell;
     } else if (th == 0) {
@@ -307,11 +325,25 @@ hipError_t launch_build_sd_mfma(const BuildArgs &a, hipStream_t stream, bool *ta
         (!aligned16(a.log_alpha) || (a.la_st % 4) || (a.la_sh % 4)))
         return hipSuccess;
     *taken = true;
-    const dim3 grid((unsigned)((int64_t)a.num_segments * a.H));
-    if (a.family == HYPIC_SCALAR)
-        hipLaunchKernelGGL(sd_build_mfma_kernel<HYPIC_SCALAR>, grid, dim3(NT), 0, stream, a);
-    else
-        hipLaunchKernelGGL(sd_build_mfma_kernel<HYPIC_DIAGONAL>, grid, dim3(NT), 0, stream, a);
+    // split the value columns over more workgroups while the units alone leave CUs idle;
+    // the grid is padded to a multiple of 8 units (padding blocks exit at once)
+    const int64_t units = (int64_t)a.num_segments * a.H;
+    // (the diagonal family re-reads its per-channel gates in every split and needs
+    // one workgroup per CU for registers, so it is not split)
+    const int nsplit = (a.family == HYPIC_DIAGONAL || units >= 1024) ? 1 : units >= 512 ? 2 : 4;
+    const int64_t padded = (units + 7) / 8 * 8;
+    const dim3 grid((unsigned)(padded * nsplit));
+#define HYPIC_SD_LAUNCH(FAM_, NS_) hipLaunchKernelGGL((sd_build_mfma_kernel<FAM_, NS_>), grid, dim3(NT), 0, stream, a)
+    if (a.family == HYPIC_SCALAR) {
+        if (nsplit == 1) HYPIC_SD_LAUNCH(HYPIC_SCALAR, 1);
+        else if (nsplit == 2) HYPIC_SD_LAUNCH(HYPIC_SCALAR, 2);
+        else HYPIC_SD_LAUNCH(HYPIC_SCALAR, 4);
+    } else {
+        if (nsplit == 1) HYPIC_SD_LAUNCH(HYPIC_DIAGONAL, 1);
+        else if (nsplit == 2) HYPIC_SD_LAUNCH(HYPIC_DIAGONAL, 2);
+        else HYPIC_SD_LAUNCH(HYPIC_DIAGONAL, 4);
+    }
+#undef HYPIC_SD_LAUNCH
     return hipGetLastError();
 }
 
