@@ -10,6 +10,8 @@ Secondary lines (same JSON object, key "secondary"):
                  composing 32 seeded slot ids -> compositions/s
   scalar/diag    RetNet-style scalar and GLA-style diagonal builds, H=16, d=128,
                  bf16, 8 x 2048 tokens, plus their 8-segment chains
+  rag mix        128 requests of 24-96 cached/cold GDN segments (128-1024 tokens),
+                 cold builds + conv warm-up (4096 channels, kernel 4) + all chains
 
 Inputs are resident in HBM before the timed region starts.  Kernel durations
 come from HIP events recorded on the stream the kernels are launched on.
@@ -230,6 +232,80 @@ def bench_sd(args, H=16, d=128, nseg=8, seg_len=2048, seed=201, copies=3):
     return out
 
 
+def conv_bytes(B, C, K, x_bytes=2):
+    return B * (2 * (K - 1) * C * x_bytes + (K - 1) * C * 4) + C * K * 4
+
+
+def bench_rag(args, R=128, pool_slots=4096, H=32, d=128, C=4096, K=4, seed=501):
+    """RAG-shaped step: 128 requests of 24-96 segments (128-1024 tokens), 70 %
+    cache hits from a 4096-slot pool built untimed, 30 % cold segments built in
+    the step, conv warm-up at every boundary, all chains composed."""
+    from hybrid_prefill_amd import rag
+    plan = synth.rag_plan(R, pool_slots, seed)
+    n_cold = len(plan.cold_lengths)
+    pool = hp.Pool.allocate(hp.GDN, pool_slots + n_cold, H, d, d, device="cuda")
+    for b0 in range(0, pool_slots, 256):                      # untimed pool fill, in batches
+        lens = plan.pool_lengths[b0:b0 + 256]
+        st = synth.gdn_stream(lens, H, d, d, torch.bfloat16, seed * 1000 + b0, 0.1, "cuda")
+        hp.build_segment(hp.GDN, st.k, st.v, st.log_alpha, torch.as_tensor(st.seg_offsets).cuda(), pool,
+                         torch.arange(b0, b0 + len(lens), dtype=torch.int32, device="cuda"), beta=st.beta)
+        del st
+    chains, cold_len, j = [], {}, 0
+    for r in range(R):
+        ch = []
+        for pos in range(plan.chain_lengths[r]):
+            if plan.is_cached[r][pos]:
+                ch.append(int(plan.cached_slot[r][pos]))
+            else:
+                cold_len[pool_slots + j] = int(plan.cold_lengths[j])
+                ch.append(pool_slots + j)
+                j += 1
+        chains.append(np.asarray(ch, dtype=np.int32))
+    step = rag.plan_step(chains, cold_len)
+    sorted_lens = sorted(cold_len.values(), reverse=True)
+    cold = synth.gdn_stream(sorted_lens, H, d, d, torch.bfloat16, seed * 1000 + 999, 0.1, "cuda")
+    tails = synth.conv_stream((pool_slots + n_cold) * (K - 1), C, torch.bfloat16, seed + 7, "cuda").view(-1, K - 1, C)
+    heads = synth.conv_stream((pool_slots + n_cold) * (K - 1), C, torch.bfloat16, seed + 8, "cuda").view(-1, K - 1, C)
+    wconv = synth.conv_weights(C, K, seed + 9, "cuda")
+    out_S = torch.empty((R, H, d, d), device="cuda")
+    conv_out = torch.empty((step.tail_index.numel(), K - 1, C), device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    timer = KernelTimer()
+    args_ = (step, pool, cold.k, cold.v, cold.beta, cold.log_alpha, tails, heads, wconv, out_S, conv_out)
+    for _ in range(max(1, args.warmup)):
+        rag.prefill_step(*args_, err_flag=err)
+    torch.cuda.synchronize()
+    n = max(3, args.steps // 4)
+    t0 = time.perf_counter()
+    for _ in range(n):
+        rag.prefill_step(*args_, err_flag=err, timer=timer)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    assert int(err.item()) == 0 and bool(torch.isfinite(out_S).all())
+    b_ms, c_ms, v_ms = timer.mean_ms("build"), timer.mean_ms("compose"), timer.mean_ms("conv")
+    ncold_tok = step.n_cold_tokens
+    bflops = gdn_build_flops_per_token_head(d, d) * ncold_tok * H
+    bbytes = gdn_build_bytes(ncold_tok, H, d, d, n_cold)
+    cbytes = compose_bytes([len(c) for c in chains], H, d, d)
+    vbytes = conv_bytes(step.tail_index.numel(), C, K)
+    prompt_tokens = int(sum(plan.pool_lengths[s] if s < pool_slots else cold_len[s] for c in chains for s in c))
+    log(f"rag: {ms:.3f} ms/step; build {b_ms:.3f} ms ({bflops / (b_ms * 1e-3) / 1e12:.0f} TFLOP/s), conv {v_ms:.3f} ms "
+        f"({vbytes / (v_ms * 1e-3) / 1e9:.0f} GB/s), compose {c_ms:.3f} ms ({cbytes / (c_ms * 1e-3) / 1e9:.0f} GB/s)")
+    del pool, cold
+    torch.cuda.empty_cache()
+    return {"workload": f"rag_mix_{R}req_pool{pool_slots}_h{H}_d{d}_conv{C}x{K}", "metric": "prompt tokens/s",
+            "value": prompt_tokens / (ms * 1e-3), "unit": "tokens/s", "ms": ms,
+            "prompt_tokens": prompt_tokens, "cold_tokens": ncold_tok, "cold_segments": n_cold,
+            "compositions": step.n_compositions, "boundaries": int(step.tail_index.numel()),
+            "kernels": {
+                "gdn_build": {"ms": b_ms, "roofline": roofline("mfma", bflops / (b_ms * 1e-3) / 1e12, PEAK_BF16 / 1e12,
+                                                                "TFLOP/s")},
+                "conv_warmup": {"ms": v_ms, "roofline": roofline("hbm", vbytes / (v_ms * 1e-3) / 1e9, PEAK_HBM / 1e9,
+                                                                 "GB/s")},
+                "compose": {"ms": c_ms, "compositions_per_s": step.n_compositions / (c_ms * 1e-3),
+                            "roofline": roofline("hbm", cbytes / (c_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s")}}}
+
+
 def cpu_baseline(seg_len=2048, H=32, d=128, nseg_sample=1, seed=301):
     """fp64 oracle on the host: build of nseg_sample segments x all heads of the main workload."""
     import oracle
@@ -267,6 +343,7 @@ def main():
     if args.only == "all":
         secondary.append(bench_compose_pool(args))
         secondary.extend(bench_sd(args))
+        secondary.append(bench_rag(args))
     cpu = None if args.no_cpu else cpu_baseline()
     line = {
         "metric": METRIC,
