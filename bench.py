@@ -41,6 +41,9 @@ PEAK_HBM = 8.0e12            # B/s, MI355X published
 PEAK_BF16 = 2.5e15           # FLOP/s dense bf16 MFMA
 PEAK_FP32 = 157.3e12         # FLOP/s fp32 (matrix and vector, published)
 CHUNK = 64
+# HBM bytes per launch of the GDN build kernel, from rocprofv3 FETCH_SIZE + WRITE_SIZE
+# (scaled by the copy-kernel calibration); None until measured for the current kernel.
+TRAFFIC_GDN_BUILD = None
 
 
 def log(msg):
@@ -306,8 +309,9 @@ def bench_rag(args, R=128, pool_slots=4096, H=32, d=128, C=4096, K=4, seed=501):
                             "roofline": roofline("hbm", cbytes / (c_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s")}}}
 
 
-def cpu_baseline(seg_len=2048, H=32, d=128, nseg_sample=1, seed=301):
-    """fp64 oracle on the host: build of nseg_sample segments x all heads of the main workload."""
+def cpu_baseline(seg_len=2048, H=32, d=128, nseg_sample=8, seed=301):
+    """fp64 oracle on the host: build of nseg_sample of the main workload's 16
+    segments, all heads (the first nseg_sample segments' tokens, same seed)."""
     import oracle
     st = synth.gdn_stream([seg_len] * nseg_sample, H, d, d, torch.bfloat16, seed, 0.1, "cpu")
     k, v = st.k.double().numpy(), st.v.double().numpy()
@@ -328,6 +332,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", choices=["all", "main"], default="all")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one untimed 1 GiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 (the path shards by "
@@ -338,7 +344,14 @@ def main():
         sys.exit(2)
     hp.lib()
     torch.cuda.synchronize()
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     ms_step, N, kern, flops, b_ms = bench_main(args)
+    traffic = TRAFFIC_GDN_BUILD
     secondary = []
     if args.only == "all":
         secondary.append(bench_compose_pool(args))
@@ -352,11 +365,11 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "gdn_build_compose_h32_d128_bf16_16x2048",
                    "heads": 32, "d_k": 128, "d_v": 128, "segments": 16, "segment_tokens": 2048,
                    "kv_dtype": "bf16", "record_dtype": "fp32", "parallelism": "none (1 GPU)"},
-        "roofline": roofline("alu", flops / (b_ms * 1e-3) / 1e12, PEAK_FP32 / 1e12, "TFLOP/s"),
+        "roofline": roofline("mfma", flops / (b_ms * 1e-3) / 1e12, PEAK_BF16 / 1e12, "TFLOP/s", traffic),
         "cpu_baseline": cpu,
         "kernels": kern,
         "secondary": secondary,
