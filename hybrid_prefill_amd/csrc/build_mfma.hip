@@ -8,22 +8,28 @@
 //
 // Chunked WY/UT form, chunk = 64 tokens, g = in-chunk cumulative log decay,
 // G = chunk total (the plain-arithmetic statement is in build_ref.hip):
-//   M    = K K^T                                  Gram, MFMA
-//   A0   = strictlower(beta_t M),  A = A0 . e^{g_t - g_s}
-//   T0   = (I + A0)^{-1},  T = (I + A)^{-1}       16x16 diagonal blocks by
-//                                                  substitution, then block merges
-//   W0   = T0 diag(beta) K,  Ws = T diag(beta e^g) K,  U = T diag(beta) V   (MFMA)
-//   P   <- P - K^T (W0 P)                                              (MFMA)
-//   S   <- e^G S + K^T diag(e^{G-g}) (U - Ws S)                        (MFMA)
-// The P update uses the ungated system (no decay factor can overflow it).
+//   A0 = strictlower(beta_t k_t.k_s),   A = A0 . e^{g_t - g_s}
+//   P columns X:  Y = (I + A0)^{-1} (beta . (K X));                X <- X - K^T Y
+//   S columns X:  Y = (I + A )^{-1} (beta . (V - e^g . (K X)));    X <- e^G X + K^T (e^{G-g} . Y)
+// The P update uses the ungated system, so no decay factor can overflow it.
+//
+// The triangular systems are solved on each wave's own columns instead of
+// forming the 64x64 inverse.  With 32-row blocks,
+//     Y_1 = T_11 R_1,   Y_2 = T_22 (R_2 - A_21 Y_1),   T_ii = (I + A_ii)^{-1},
+// so the shared work is the two 32x32 diagonal inverses of each system (16x16
+// diagonal blocks by forward substitution, one 16 -> 32 merge in fp32); the
+// rest is six MFMAs per wave.
 //
 // Work split: one 512-thread workgroup (8 waves) per (segment, head).  Wave w
-// owns 32 columns of [P | S] (waves 0-3: P, waves 4-7: S) as 4 fp32 32x32
-// accumulator tiles that stay in registers for the whole segment.  The
-// B operand of the carry products is built from those registers: the 32x32
-// accumulator layout and the B-operand layout of v_mfma_f32_32x32x16_bf16
-// both put one column per lane, so only the order of the contraction index
-// differs, and the A operand is read from LDS in that same order.
+// owns 32 columns of [P | S] (waves 0-3: P, waves 4-7: S) as four fp32 32x32
+// accumulator tiles that stay in registers for the whole segment.  The 32x32
+// accumulator layout and the B-operand layout of v_mfma_f32_32x32x16_bf16 both
+// put one column per lane, so an accumulator tile becomes the B operand of the
+// next product after a bf16 pack; only the order of the contraction index
+// changes, and the A operand is read in that same order.  The same fact moves
+// token-major tiles into the accumulator layout: X . I on the MFMA returns X
+// with one column per lane, which gives K^T for the update's A operand and V
+// in the layout of K X.
 #include "hypic_internal.h"
 
 namespace hypic {
@@ -38,23 +44,17 @@ typedef uint16_t u16;
 constexpr int CH = 64;     // tokens per chunk
 constexpr int D = 128;     // d_k = d_v
 constexpr int NT = 512;    // 8 waves
-constexpr int KTL = 72;    // row length (bf16) of the [channel][token] tiles Kt, Vt
-constexpr int KML = 136;   // row length (bf16) of the [token][channel] tiles Km, W0n, Wsn
-constexpr int AFL = 68;    // row length (fp32) of A0/T0, A/T
-constexpr int TFL = 72;    // row length (bf16) of the scaled T tiles
+constexpr int KTL = 72;    // row length (bf16) of Kt [channel][token]
+constexpr int KML = 136;   // row length (bf16) of Km, Vm [token][channel]
+constexpr int AFL = 68;    // row length (fp32) of A0 and A
 
 struct __align__(16) Smem {
-    u16 Kt[D * KTL];                                   // keys, [channel][token]
-    union {
-        u16 Km[CH * KML];                              // keys, [token][channel] (Gram only)
-        u16 Vt[D * KTL];                               // values, [channel][token]
-    } x;
-    union {
-        struct { float A0[CH * AFL]; float A1[CH * AFL]; } a;   // A0 -> T0, A -> T (fp32, in place)
-        struct { u16 W0n[CH * KML]; u16 Wsn[CH * KML]; } w;     // -W0, -Ws  [token][channel]
-    } m;
-    struct { u16 T0b[CH * TFL]; u16 Tgb[CH * TFL]; u16 Tb[CH * TFL]; } t;  // T0 diag(b), T diag(b e^g), T diag(b)
-    float scratch[2][512];                                                  // 16x16 merge temporaries
+    u16 Kt[D * KTL];           // keys, channel-major: A operand of the update
+    u16 Km[CH * KML];          // keys, token-major: Gram, K X, turn-around
+    u16 Vm[CH * KML];          // values, token-major
+    float A0[CH * AFL];        // A0; its 32x32 diagonal blocks become T0_11, T0_22
+    float A1[CH * AFL];        // A;  its 32x32 diagonal blocks become T_11,  T_22
+    float scratch[2][512];     // 16 -> 32 merge temporaries
     float g[CH], eg[CH], egr[CH], beta[CH], la[CH];
     float eG;
     int64_t t0, n;
@@ -89,40 +89,42 @@ __device__ __forceinline__ bf16x8 lds4x2(const u16 *p0, const u16 *p1) {
     return __builtin_bit_cast(bf16x8, u);
 }
 
-__device__ __forceinline__ u16 f2bf(float x) { return __builtin_bit_cast(u16, (__bf16)x); }
-
-__device__ __forceinline__ u16 u4_elem(const uint4 &q, int e) {
-    const uint32_t w = e < 2 ? q.x : e < 4 ? q.y : e < 6 ? q.z : q.w;
-    return (u16)(w >> (16 * (e & 1)));
-}
-
-// Order this wave's LDS writes before its later LDS reads (the lanes of a wave
-// run in lockstep, so no workgroup barrier is needed when only this wave reads).
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
 // Row of the 32x32 accumulator element held in register r by lane half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// B operand (k-step kb of a 32-row block) from accumulator registers: element e
-// of the fragment is accumulator row 8*(2*(kb&1) + e/4) + 4h + (e&3).
+// B operand (k-step `half` of a 32-row block) from accumulator registers: element e
+// of the fragment is accumulator row 16 half + 4h + e for e < 4, 16 half + 8 + 4h + e - 4 after.
 __device__ __forceinline__ bf16x8 acc_to_b(const f32x16 &c, int half) {
     const int o = 8 * half;
     return pack8(c[o + 0], c[o + 1], c[o + 2], c[o + 3], c[o + 4], c[o + 5], c[o + 6], c[o + 7]);
 }
 
 // Column offset inside a 32-wide block for the A operand that matches acc_to_b:
-// elements 0-3 at 16*half + 4h, elements 4-7 at 16*half + 8 + 4h.
+// elements 0-3 at 16 half + 4h, elements 4-7 at 16 half + 8 + 4h.
 __device__ __forceinline__ int perm_col(int half, int h) { return 16 * half + 4 * h; }
+
+// A operand in acc_to_b order from an fp32 matrix in LDS: row `row`, the
+// 32-wide column block starting at c0, times sgn.
+__device__ __forceinline__ bf16x8 a_from_f32(const float *M, int row, int c0, int half, int h, float sgn) {
+    const float *p = M + row * AFL + c0 + perm_col(half, h);
+    const float4 x = *reinterpret_cast<const float4 *>(p);
+    const float4 y = *reinterpret_cast<const float4 *>(p + 8);
+    return pack8(sgn * x.x, sgn * x.y, sgn * x.z, sgn * x.w, sgn * y.x, sgn * y.y, sgn * y.z, sgn * y.w);
+}
+
+// B operand of the identity for k-step ks: column l32, rows 16 ks + 8h + e.
+__device__ __forceinline__ bf16x8 eye_b(int ks, int h, int l32) {
+    bf16x8 e8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) e8[e] = (__bf16)((16 * ks + 8 * h + e == l32) ? 1.0f : 0.0f);
+    return e8;
+}
 
 __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
     __shared__ Smem sm;
 
     const int th = threadIdx.x;
-    const int w = th >> 6, l = th & 63, h = l >> 5, l32 = l & 31;
+    const int w = th >> 6;
     const int head = blockIdx.x % a.H;
     const int seg = blockIdx.x / a.H;
     const bool isS = w >= 4;
@@ -147,23 +149,19 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 
     // state slab: P = I, S = 0
     f32x16 st[4];
+    {
+        const int h = (th & 63) >> 5, l32 = th & 31;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            st[mb][r] = (!isS && 32 * mb + acc_row(r, h) == col0 + l32) ? 1.0f : 0.0f;
-    double ell = 0.0;   // thread 256 (wave 4, lane 0)
-    for (int e = th; e < 3 * CH * CH; e += NT) {
-        const int t = (e >> 6) & 63, s = e & 63;
-        if ((s >> 4) > (t >> 4)) {
-            u16 *dst = (e >> 12) == 0 ? sm.t.T0b : (e >> 12) == 1 ? sm.t.Tgb : sm.t.Tb;
-            dst[t * TFL + s] = 0;
-        }
+            for (int r = 0; r < 16; ++r)
+                st[mb][r] = (!isS && 32 * mb + acc_row(r, h) == col0 + l32) ? 1.0f : 0.0f;
     }
+    double ell = 0.0;   // thread 256 (wave 4, lane 0)
 
     const u16 *kp = static_cast<const u16 *>(a.k);
     const u16 *vp = static_cast<const u16 *>(a.v);
-    // per thread: token row lt = th / 8, 16 channels from lc = 16 (th % 8) (two 16-byte pieces)
+    // per thread: token row th / 8, 16 channels from 16 (th % 8): two 16-byte pieces of k and of v
     uint4 kreg[2], vreg[2];
     float breg = 0.f, lareg = 0.f;
 
@@ -199,20 +197,18 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         asm volatile("" : "+v"(thv));
         const int l = thv & 63, h = l >> 5, l32 = l & 31;
         const int lt = thv >> 3, lc = 16 * (thv & 7);
-        // ---------------- 1. stage keys (Km, Kt) and gates
-        *reinterpret_cast<uint4 *>(&sm.x.Km[lt * KML + lc]) = kreg[0];
-        *reinterpret_cast<uint4 *>(&sm.x.Km[lt * KML + lc + 8]) = kreg[1];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sm.Kt[(lc + e) * KTL + lt] = u4_elem(kreg[0], e);
-            sm.Kt[(lc + 8 + e) * KTL + lt] = u4_elem(kreg[1], e);
-        }
-        if (th < CH) { sm.la[th] = lareg; sm.beta[th] = breg; }
-        const uint4 vkeep0 = vreg[0], vkeep1 = vreg[1];
+
+        // ---------------- 1. stage keys, values (token-major) and gates
+        *reinterpret_cast<uint4 *>(&sm.Km[lt * KML + lc]) = kreg[0];
+        *reinterpret_cast<uint4 *>(&sm.Km[lt * KML + lc + 8]) = kreg[1];
+        *reinterpret_cast<uint4 *>(&sm.Vm[lt * KML + lc]) = vreg[0];
+        *reinterpret_cast<uint4 *>(&sm.Vm[lt * KML + lc + 8]) = vreg[1];
+        if (thv < CH) { sm.la[thv] = lareg; sm.beta[thv] = breg; }
         if (base + CH < n) fetch(base + CH);     // next chunk's loads fly during this chunk
         __syncthreads();                                                   // B1
 
-        // ---------------- 2. decay prefix (wave 0) | Gram blocks (waves 1-3)
+        // ---------------- 2. decay prefix (wave 0) | ell (wave 4) | Gram blocks (waves 1-3)
+        //                     | K^T by turn-around (all) | Z = K X on own columns (all)
         f32x16 gacc;
         const int gmb = (w >= 2) ? 1 : 0, gnb = (w == 3) ? 1 : 0;
         if (w == 0) {
@@ -229,7 +225,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
             sm.egr[l] = __expf(gt - gv);
             if (l == 63) sm.eG = __expf(gt);
         } else if (w == 4) {
-            // the segment total of log alpha in fp64 (thread 256 keeps it)
+            // the chunk total of log alpha in fp64, accumulated by thread 256
             double gd = (double)sm.la[l];
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) gd += __shfl_xor(gd, o);
@@ -239,14 +235,43 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
             for (int r = 0; r < 16; ++r) gacc[r] = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) {
-                const bf16x8 fa = lds8(&sm.x.Km[(32 * gmb + l32) * KML + 16 * kb + 8 * h]);
-                const bf16x8 fb = gmb == gnb ? fa : lds8(&sm.x.Km[(32 * gnb + l32) * KML + 16 * kb + 8 * h]);
+                const bf16x8 fa = lds8(&sm.Km[(32 * gmb + l32) * KML + 16 * kb + 8 * h]);
+                const bf16x8 fb = gmb == gnb ? fa : lds8(&sm.Km[(32 * gnb + l32) * KML + 16 * kb + 8 * h]);
                 gacc = mfma(fa, fb, gacc);
+            }
+        }
+        {
+            // wave w writes K^T of the 32x32 block (tokens 32 tb.., channels 32 ib..)
+            const int tb = w >> 2, ib = w & 3;
+            f32x16 kk;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) kk[r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                kk = mfma(lds8(&sm.Km[(32 * tb + l32) * KML + 32 * ib + 16 * ks + 8 * h]), eye_b(ks, h, l32), kk);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x2 v2 = {pack2(kk[4 * q], kk[4 * q + 1]), pack2(kk[4 * q + 2], kk[4 * q + 3])};
+                *reinterpret_cast<u32x2 *>(&sm.Kt[(32 * ib + l32) * KTL + 32 * tb + 8 * q + 4 * h]) = v2;
+            }
+        }
+        f32x16 z[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[mb][r] = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+            const bf16x8 sb = acc_to_b(st[kb >> 1], kb & 1);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const u16 *row = &sm.Km[(32 * mb + l32) * KML + 32 * (kb >> 1) + perm_col(kb & 1, h)];
+                z[mb] = mfma(lds4x2(row, row + 8), sb, z[mb]);
             }
         }
         __syncthreads();                                                   // B2
 
-        // ---------------- 3. A0, A (waves 1-3) ; values to LDS (all)
+        // ---------------- 3. A0, A (waves 1-3) | right-hand sides R on own columns (all)
         if (w >= 1 && w <= 3) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -256,34 +281,32 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     a0 = sm.beta[t] * gacc[r];
                     a1 = a0 * __expf(sm.g[t] - sm.g[s]);
                 }
-                sm.m.a.A0[t * AFL + s] = a0;
-                sm.m.a.A1[t * AFL + s] = a1;
+                sm.A0[t * AFL + s] = a0;
+                sm.A1[t * AFL + s] = a1;
             }
         }
+        if (isS) {
+            // R = beta (V - e^g Z): scale, then add V turned around on the MFMA
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sm.x.Vt[(lc + e) * KTL + lt] = u4_elem(vkeep0, e);
-            sm.x.Vt[(lc + 8 + e) * KTL + lt] = u4_elem(vkeep1, e);
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) z[mb][r] *= -sm.eg[32 * mb + acc_row(r, h)];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    z[mb] = mfma(lds8(&sm.Vm[(32 * mb + l32) * KML + col0 + 16 * ks + 8 * h]), eye_b(ks, h, l32),
+                                 z[mb]);
         }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[mb][r] *= sm.beta[32 * mb + acc_row(r, h)];
         __syncthreads();                                                   // B3
 
-        // ---------------- 4. UT transform: T0 = (I+A0)^-1, T = (I+A)^-1 in 16x16 blocks,
-        //                     writing the bf16 column-scaled forms as blocks become final
-        // emit: write the bf16 column-scaled forms of a final T entry (t, s)
-        //   matrix 0: T0 diag(beta) -> T0b;  matrix 1: T diag(beta) -> Tb, T diag(beta e^g) -> Tgb
-#define HYPIC_EMIT(MAT_, ROW_, COL_, VAL_, SB_, SG_)                          \
-    do {                                                                     \
-        if ((MAT_) == 0) {                                                   \
-            sm.t.T0b[(ROW_) * TFL + (COL_)] = f2bf((VAL_) * (SB_));          \
-        } else {                                                             \
-            sm.t.Tb[(ROW_) * TFL + (COL_)] = f2bf((VAL_) * (SB_));           \
-            sm.t.Tgb[(ROW_) * TFL + (COL_)] = f2bf((VAL_) * (SG_));          \
-        }                                                                    \
-    } while (0)
-        // (a) 16x16 diagonal blocks by forward substitution: wave 0 -> T0, wave 1 -> T
+        // ---------------- 4. 16x16 diagonal blocks by forward substitution: wave 0 -> T0, wave 1 -> T
         if (w <= 1) {
-            const int mat = w;
-            float *M = mat == 0 ? sm.m.a.A0 : sm.m.a.A1;
+            float *M = w == 0 ? sm.A0 : sm.A1;
             const int R = 16 * (l >> 4), j = l & 15;
             float x[16];
 #pragma unroll
@@ -293,19 +316,16 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 for (int s = 0; s < i; ++s) acc += M[(R + i) * AFL + R + s] * x[s];
                 x[i] = (i == j) ? 1.0f : (i < j ? 0.0f : -acc);
             }
-            const float sb = sm.beta[R + j], sg = sb * sm.eg[R + j];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                M[(R + i) * AFL + R + j] = x[i];
-                HYPIC_EMIT(mat, R + i, R + j, x[i], sb, sg);
-            }
+            for (int i = 0; i < 16; ++i) M[(R + i) * AFL + R + j] = x[i];
         }
         __syncthreads();                                                   // B4
 
-        // (b) 16 -> 32: T_10 = -T_11 A_10 T_00, tasks (matrix, half) on waves 0-3
+        // ---------------- 5. 16 -> 32: T_10 = -T_11 A_10 T_00 in each 32x32 diagonal block of
+        //                     both systems, one (system, block) per wave 0-3
         const int mrow = 4 * (l >> 4), mcol = l & 15;
         if (w < 4) {
-            const float *M = (w >> 1) ? sm.m.a.A1 : sm.m.a.A0;
+            const float *M = (w >> 1) ? sm.A1 : sm.A0;
             const int R0 = 32 * (w & 1), R1 = R0 + 16;
             float tl[16];
 #pragma unroll
@@ -321,118 +341,56 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         __syncthreads();                                                   // B5
         if (w < 4) {
             const int mat = w >> 1;
-            float *M = mat ? sm.m.a.A1 : sm.m.a.A0;
+            float *M = mat ? sm.A1 : sm.A0;
             const int R0 = 32 * (w & 1), R1 = R0 + 16;
             float tc[16];
 #pragma unroll
             for (int k = 0; k < 16; ++k) tc[k] = sm.scratch[mat][256 * (w & 1) + k * 16 + mcol];
-            const float sb = sm.beta[R0 + mcol], sg = sb * sm.eg[R0 + mcol];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float acc = 0.f;
 #pragma unroll
                 for (int k = 0; k < 16; ++k) acc += M[(R1 + mrow + r) * AFL + R1 + k] * tc[k];
                 M[(R1 + mrow + r) * AFL + R0 + mcol] = -acc;
-                HYPIC_EMIT(mat, R1 + mrow + r, R0 + mcol, -acc, sb, sg);
             }
         }
         __syncthreads();                                                   // B6
 
-        // (c) 32 -> 64: T_21 = -T_22 A_21 T_11 on bf16 MFMA, waves 0 and 1
-        if (w <= 1) {
-            const int mat = w;
-            const float *M = mat == 0 ? sm.m.a.A0 : sm.m.a.A1;
-            f32x16 tmp;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) tmp[r] = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const float *ar = &M[(32 + l32) * AFL + 16 * kb + 8 * h];
-                const bf16x8 fa = pack8(ar[0], ar[1], ar[2], ar[3], ar[4], ar[5], ar[6], ar[7]);
-                const float *bc = &M[(16 * kb + 8 * h) * AFL + l32];
-                const bf16x8 fb = pack8(bc[0], bc[AFL], bc[2 * AFL], bc[3 * AFL], bc[4 * AFL], bc[5 * AFL],
-                                        bc[6 * AFL], bc[7 * AFL]);
-                tmp = mfma(fa, fb, tmp);
-            }
-            f32x16 o;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[r] = 0.f;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const float *ar = &M[(32 + l32) * AFL + 32 + perm_col(half, h)];
-                const bf16x8 fa = pack8(ar[0], ar[1], ar[2], ar[3], ar[8], ar[9], ar[10], ar[11]);
-                o = mfma(fa, acc_to_b(tmp, half), o);
-            }
-            const float sb = sm.beta[l32], sg = sb * sm.eg[l32];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) HYPIC_EMIT(mat, 32 + acc_row(r, h), l32, -o[r], sb, sg);
-        }
-#undef HYPIC_EMIT
-        __syncthreads();                                                   // B7
-
-        // ---------------- 5. -W0, -Ws (all waves, 2 tiles each) and U (S waves, own columns)
+        // ---------------- 6. solve on own columns, then the carry update
         {
-            const u16 *TF = (w >> 2) ? sm.t.Tgb : sm.t.T0b;
-            u16 *Wd = (w >> 2) ? sm.m.w.Wsn : sm.m.w.W0n;
-            const int mb = (w >> 1) & 1;
+            const float *M = isS ? sm.A1 : sm.A0;      // T_11, T_22 and the untouched A_21
+            f32x16 y0, y2;
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int nb = 2 * (w & 1) + q;
-                f32x16 c;
+            for (int r = 0; r < 16; ++r) { y0[r] = 0.f; y2[r] = 0.f; }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) c[r] = 0.f;
+            for (int half = 0; half < 2; ++half)                                       // Y_1 = T_11 R_1
+                y0 = mfma(a_from_f32(M, l32, 0, half, h, 1.0f), acc_to_b(z[0], half), y0);
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    if (ks >= 2 && mb == 0) break;     // T is lower triangular
-                    c = mfma(lds8(&TF[(32 * mb + l32) * TFL + 16 * ks + 8 * h]),
-                             lds8(&sm.Kt[(32 * nb + l32) * KTL + 16 * ks + 8 * h]), c);
-                }
+            for (int half = 0; half < 2; ++half)                                       // R_2 - A_21 Y_1
+                z[1] = mfma(a_from_f32(M, 32 + l32, 0, half, h, -1.0f), acc_to_b(y0, half), z[1]);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) Wd[(32 * mb + acc_row(r, h)) * KML + 32 * nb + l32] = f2bf(-c[r]);
-            }
-        }
-        f32x16 acc[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+            for (int half = 0; half < 2; ++half)                                       // Y_2 = T_22 (..)
+                y2 = mfma(a_from_f32(M, 32 + l32, 32, half, h, 1.0f), acc_to_b(z[1], half), y2);
             if (isS) {
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    if (ks >= 2 && mb == 0) break;
-                    acc[mb] = mfma(lds8(&sm.t.Tb[(32 * mb + l32) * TFL + 16 * ks + 8 * h]),
-                                   lds8(&sm.x.Vt[(col0 + l32) * KTL + 16 * ks + 8 * h]), acc[mb]);
-                }
-            }
-        }
-        __syncthreads();                                                   // B8
-
-        // ---------------- 6. carry: Y = (U) - W . state ; state += K^T diag(.) Y
-        {
-            const u16 *Wn = isS ? sm.m.w.Wsn : sm.m.w.W0n;
-#pragma unroll
-            for (int kb = 0; kb < 8; ++kb) {
-                const bf16x8 sb = acc_to_b(st[kb >> 1], kb & 1);
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    const u16 *row = &Wn[(32 * mb + l32) * KML + 32 * (kb >> 1) + perm_col(kb & 1, h)];
-                    acc[mb] = mfma(lds4x2(row, row + 8), sb, acc[mb]);
-                }
-            }
-            if (isS) {
+                // S: e^G X + K^T (e^{G-g} . Y)
                 const float eG = sm.eG;
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[mb][r] *= sm.egr[32 * mb + acc_row(r, h)];
+                for (int r = 0; r < 16; ++r) {
+                    y0[r] *= sm.egr[acc_row(r, h)];
+                    y2[r] *= sm.egr[32 + acc_row(r, h)];
+                }
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) st[mb][r] *= eG;
+            } else {
+                // P: X - K^T Y
+#pragma unroll
+                for (int r = 0; r < 16; ++r) { y0[r] = -y0[r]; y2[r] = -y2[r]; }
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const bf16x8 yb = acc_to_b(acc[s >> 1], s & 1);
+                const bf16x8 yb = acc_to_b(s < 2 ? y0 : y2, s & 1);
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb) {
                     const u16 *row = &sm.Kt[(32 * mb + l32) * KTL + 32 * (s >> 1) + perm_col(s & 1, h)];
@@ -440,10 +398,11 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 }
             }
         }
-        __syncthreads();                                                   // B9
+        __syncthreads();                                                   // B7
     }
 
     // ---------------- record
+    const int h = (th & 63) >> 5, l32 = th & 31;
     const float nanv = __int_as_float(0x7fc00000);
     const bool bad = state == 2;
     const int64_t rec = slot * a.H + head;
