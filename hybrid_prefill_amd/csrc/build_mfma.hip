@@ -47,13 +47,18 @@ constexpr int NT = 512;    // 8 waves
 constexpr int KTL = 72;    // row length (bf16) of Kt [channel][token]
 constexpr int KML = 136;   // row length (bf16) of Km, Vm [token][channel]
 constexpr int AFL = 68;    // row length (fp32) of A0 and A
+constexpr int TBL = 72;    // row length (bf16) of the bf16 copies of T0 and T
 
+// Kt (tokens), Km (channels) and TB (columns) are stored with the index
+// swizzle below, so that every MFMA A operand in acc_to_b order is one
+// 16-byte LDS read.
 struct __align__(16) Smem {
     u16 Kt[D * KTL];           // keys, channel-major: A operand of the update
     u16 Km[CH * KML];          // keys, token-major: Gram, K X, turn-around
-    u16 Vm[CH * KML];          // values, token-major
+    u16 Vm[CH * KML];          // values, token-major, plain order
     float A0[CH * AFL];        // A0; its 32x32 diagonal blocks become T0_11, T0_22
     float A1[CH * AFL];        // A;  its 32x32 diagonal blocks become T_11,  T_22
+    u16 TB[2][CH * TBL];       // bf16 [T_11 0; -A_21 T_22] of both systems (the solve's A operands)
     float scratch[2][512];     // 16 -> 32 merge temporaries
     float g[CH], eg[CH], egr[CH], beta[CH], la[CH];
     float eG;
@@ -81,14 +86,6 @@ __device__ __forceinline__ bf16x8 lds8(const u16 *p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
 }
 
-// 4 + 4 bf16 from two 8-byte aligned LDS addresses
-__device__ __forceinline__ bf16x8 lds4x2(const u16 *p0, const u16 *p1) {
-    const u32x2 a = *reinterpret_cast<const u32x2 *>(p0);
-    const u32x2 b = *reinterpret_cast<const u32x2 *>(p1);
-    u32x4 u = {a.x, a.y, b.x, b.y};
-    return __builtin_bit_cast(bf16x8, u);
-}
-
 // Row of the 32x32 accumulator element held in register r by lane half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
@@ -99,26 +96,31 @@ __device__ __forceinline__ bf16x8 acc_to_b(const f32x16 &c, int half) {
     return pack8(c[o + 0], c[o + 1], c[o + 2], c[o + 3], c[o + 4], c[o + 5], c[o + 6], c[o + 7]);
 }
 
-// Column offset inside a 32-wide block for the A operand that matches acc_to_b:
-// elements 0-3 at 16 half + 4h, elements 4-7 at 16 half + 8 + 4h.
-__device__ __forceinline__ int perm_col(int half, int h) { return 16 * half + 4 * h; }
+// Storage position of index c: bits 2 and 3 swapped (an involution inside each
+// group of 16).  The eight indices that lane half h contributes in acc_to_b
+// order, 16 half + 4h + 0..3 and 16 half + 8 + 4h + 0..3, then sit at
+// 16 half + 8h + 0..7.
+__device__ __forceinline__ int swz(int c) { return (c & ~12) | ((c & 4) << 1) | ((c & 8) >> 1); }
 
-// A operand in acc_to_b order from an fp32 matrix in LDS: row `row`, the
-// 32-wide column block starting at c0, times sgn.
-__device__ __forceinline__ bf16x8 a_from_f32(const float *M, int row, int c0, int half, int h, float sgn) {
-    const float *p = M + row * AFL + c0 + perm_col(half, h);
-    const float4 x = *reinterpret_cast<const float4 *>(p);
-    const float4 y = *reinterpret_cast<const float4 *>(p + 8);
-    return pack8(sgn * x.x, sgn * x.y, sgn * x.z, sgn * x.w, sgn * y.x, sgn * y.y, sgn * y.z, sgn * y.w);
-}
-
-// B operand of the identity for k-step ks: column l32, rows 16 ks + 8h + e.
-__device__ __forceinline__ bf16x8 eye_b(int ks, int h, int l32) {
+// B operand of the identity for k-step ks: column l32; row 16 ks + 8h + e of the
+// operand holds index c of the block, with c = swz(16 ks + 8h + e) when the A
+// operand is stored swizzled, else c = 16 ks + 8h + e.
+__device__ __forceinline__ bf16x8 eye_b(int ks, int h, int l32, bool swizzled) {
     bf16x8 e8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) e8[e] = (__bf16)((16 * ks + 8 * h + e == l32) ? 1.0f : 0.0f);
+    for (int e = 0; e < 8; ++e) {
+        const int p = 16 * ks + 8 * h + e;
+        e8[e] = (__bf16)(((swizzled ? swz(p) : p) == l32) ? 1.0f : 0.0f);
+    }
     return e8;
 }
+
+// 4 per-row values of accumulator rows 32 mb + 8 q + 4h + 0..3 (registers 4q..4q+3)
+__device__ __forceinline__ float4 rows4(const float *v, int mb, int q, int h) {
+    return *reinterpret_cast<const float4 *>(v + 32 * mb + 8 * q + 4 * h);
+}
+
+__device__ __forceinline__ u16 f2bf(float x) { return __builtin_bit_cast(u16, (__bf16)x); }
 
 __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
     __shared__ Smem sm;
@@ -158,6 +160,11 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 st[mb][r] = (!isS && 32 * mb + acc_row(r, h) == col0 + l32) ? 1.0f : 0.0f;
     }
     double ell = 0.0;   // thread 256 (wave 4, lane 0)
+    // upper-right 16x16 blocks of T_11 and T_22 (zero, never written again)
+    for (int e = th; e < 2 * 2 * 16 * 16; e += NT) {
+        const int m = e >> 9, b = (e >> 8) & 1, i = (e >> 4) & 15, j = e & 15;
+        sm.TB[m][(32 * b + i) * TBL + 32 * b + 16 + j] = 0;
+    }
 
     const u16 *kp = static_cast<const u16 *>(a.k);
     const u16 *vp = static_cast<const u16 *>(a.v);
@@ -199,8 +206,9 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         const int lt = thv >> 3, lc = 16 * (thv & 7);
 
         // ---------------- 1. stage keys, values (token-major) and gates
-        *reinterpret_cast<uint4 *>(&sm.Km[lt * KML + lc]) = kreg[0];
-        *reinterpret_cast<uint4 *>(&sm.Km[lt * KML + lc + 8]) = kreg[1];
+        *reinterpret_cast<uint4 *>(&sm.Km[lt * KML + lc]) = make_uint4(kreg[0].x, kreg[0].y, kreg[1].x, kreg[1].y);
+        *reinterpret_cast<uint4 *>(&sm.Km[lt * KML + lc + 8]) =
+            make_uint4(kreg[0].z, kreg[0].w, kreg[1].z, kreg[1].w);
         *reinterpret_cast<uint4 *>(&sm.Vm[lt * KML + lc]) = vreg[0];
         *reinterpret_cast<uint4 *>(&sm.Vm[lt * KML + lc + 8]) = vreg[1];
         if (thv < CH) { sm.la[thv] = lareg; sm.beta[thv] = breg; }
@@ -248,11 +256,14 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
             for (int r = 0; r < 16; ++r) kk[r] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                kk = mfma(lds8(&sm.Km[(32 * tb + l32) * KML + 32 * ib + 16 * ks + 8 * h]), eye_b(ks, h, l32), kk);
+                kk = mfma(lds8(&sm.Km[(32 * tb + l32) * KML + 32 * ib + 16 * ks + 8 * h]), eye_b(ks, h, l32, true),
+                          kk);
+            // registers 4q..4q+3: tokens 8q + 4h + 0..3 of the block, stored at their swizzled positions
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const u32x2 v2 = {pack2(kk[4 * q], kk[4 * q + 1]), pack2(kk[4 * q + 2], kk[4 * q + 3])};
-                *reinterpret_cast<u32x2 *>(&sm.Kt[(32 * ib + l32) * KTL + 32 * tb + 8 * q + 4 * h]) = v2;
+                *reinterpret_cast<u32x2 *>(
+                    &sm.Kt[(32 * ib + l32) * KTL + 32 * tb + 16 * (q >> 1) + 8 * h + 4 * (q & 1)]) = v2;
             }
         }
         f32x16 z[2];
@@ -265,24 +276,34 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
             const bf16x8 sb = acc_to_b(st[kb >> 1], kb & 1);
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
-                const u16 *row = &sm.Km[(32 * mb + l32) * KML + 32 * (kb >> 1) + perm_col(kb & 1, h)];
-                z[mb] = mfma(lds4x2(row, row + 8), sb, z[mb]);
+                z[mb] = mfma(lds8(&sm.Km[(32 * mb + l32) * KML + 16 * kb + 8 * h]), sb, z[mb]);
             }
         }
         __syncthreads();                                                   // B2
 
         // ---------------- 3. A0, A (waves 1-3) | right-hand sides R on own columns (all)
         if (w >= 1 && w <= 3) {
+            const int s = 32 * gnb + l32;
+            const float gs = sm.g[s];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = 32 * gmb + acc_row(r, h), s = 32 * gnb + l32;
-                float a0 = 0.f, a1 = 0.f;
-                if (s < t) {
-                    a0 = sm.beta[t] * gacc[r];
-                    a1 = a0 * __expf(sm.g[t] - sm.g[s]);
+            for (int q = 0; q < 4; ++q) {
+                const float4 b4 = rows4(sm.beta, gmb, q, h), g4 = rows4(sm.g, gmb, q, h);
+                const float bq[4] = {b4.x, b4.y, b4.z, b4.w}, gq[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 32 * gmb + 8 * q + 4 * h + e;
+                    float a0 = 0.f, a1 = 0.f;
+                    if (s < t) {
+                        a0 = bq[e] * gacc[4 * q + e];
+                        a1 = a0 * __expf(gq[e] - gs);
+                    }
+                    sm.A0[t * AFL + s] = a0;
+                    sm.A1[t * AFL + s] = a1;
+                    if (w == 2) {          // block (1,0): A_21, negated, into the bf16 copies
+                        sm.TB[0][t * TBL + swz(s)] = f2bf(-a0);
+                        sm.TB[1][t * TBL + swz(s)] = f2bf(-a1);
+                    }
                 }
-                sm.A0[t * AFL + s] = a0;
-                sm.A1[t * AFL + s] = a1;
             }
         }
         if (isS) {
@@ -290,18 +311,26 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) z[mb][r] *= -sm.eg[32 * mb + acc_row(r, h)];
+                for (int q = 0; q < 4; ++q) {
+                    const float4 e4 = rows4(sm.eg, mb, q, h);
+                    z[mb][4 * q] *= -e4.x; z[mb][4 * q + 1] *= -e4.y;
+                    z[mb][4 * q + 2] *= -e4.z; z[mb][4 * q + 3] *= -e4.w;
+                }
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    z[mb] = mfma(lds8(&sm.Vm[(32 * mb + l32) * KML + col0 + 16 * ks + 8 * h]), eye_b(ks, h, l32),
-                                 z[mb]);
+                    z[mb] = mfma(lds8(&sm.Vm[(32 * mb + l32) * KML + col0 + 16 * ks + 8 * h]),
+                                 eye_b(ks, h, l32, false), z[mb]);
         }
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) z[mb][r] *= sm.beta[32 * mb + acc_row(r, h)];
+            for (int q = 0; q < 4; ++q) {
+                const float4 b4 = rows4(sm.beta, mb, q, h);
+                z[mb][4 * q] *= b4.x; z[mb][4 * q + 1] *= b4.y;
+                z[mb][4 * q + 2] *= b4.z; z[mb][4 * q + 3] *= b4.w;
+            }
         __syncthreads();                                                   // B3
 
         // ---------------- 4. 16x16 diagonal blocks by forward substitution: wave 0 -> T0, wave 1 -> T
@@ -317,7 +346,10 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 x[i] = (i == j) ? 1.0f : (i < j ? 0.0f : -acc);
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) M[(R + i) * AFL + R + j] = x[i];
+            for (int i = 0; i < 16; ++i) {
+                M[(R + i) * AFL + R + j] = x[i];
+                sm.TB[w][(R + i) * TBL + R + swz(j)] = f2bf(x[i]);
+            }
         }
         __syncthreads();                                                   // B4
 
@@ -352,32 +384,34 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 #pragma unroll
                 for (int k = 0; k < 16; ++k) acc += M[(R1 + mrow + r) * AFL + R1 + k] * tc[k];
                 M[(R1 + mrow + r) * AFL + R0 + mcol] = -acc;
+                sm.TB[mat][(R1 + mrow + r) * TBL + R0 + swz(mcol)] = f2bf(-acc);
             }
         }
         __syncthreads();                                                   // B6
 
         // ---------------- 6. solve on own columns, then the carry update
         {
-            const float *M = isS ? sm.A1 : sm.A0;      // T_11, T_22 and the untouched A_21
+            const u16 *M = sm.TB[isS ? 1 : 0];
             f32x16 y0, y2;
 #pragma unroll
             for (int r = 0; r < 16; ++r) { y0[r] = 0.f; y2[r] = 0.f; }
 #pragma unroll
             for (int half = 0; half < 2; ++half)                                       // Y_1 = T_11 R_1
-                y0 = mfma(a_from_f32(M, l32, 0, half, h, 1.0f), acc_to_b(z[0], half), y0);
+                y0 = mfma(lds8(&M[l32 * TBL + 16 * half + 8 * h]), acc_to_b(z[0], half), y0);
 #pragma unroll
             for (int half = 0; half < 2; ++half)                                       // R_2 - A_21 Y_1
-                z[1] = mfma(a_from_f32(M, 32 + l32, 0, half, h, -1.0f), acc_to_b(y0, half), z[1]);
+                z[1] = mfma(lds8(&M[(32 + l32) * TBL + 16 * half + 8 * h]), acc_to_b(y0, half), z[1]);
 #pragma unroll
             for (int half = 0; half < 2; ++half)                                       // Y_2 = T_22 (..)
-                y2 = mfma(a_from_f32(M, 32 + l32, 32, half, h, 1.0f), acc_to_b(z[1], half), y2);
+                y2 = mfma(lds8(&M[(32 + l32) * TBL + 32 + 16 * half + 8 * h]), acc_to_b(z[1], half), y2);
             if (isS) {
                 // S: e^G X + K^T (e^{G-g} . Y)
                 const float eG = sm.eG;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    y0[r] *= sm.egr[acc_row(r, h)];
-                    y2[r] *= sm.egr[32 + acc_row(r, h)];
+                for (int q = 0; q < 4; ++q) {
+                    const float4 e0 = rows4(sm.egr, 0, q, h), e1 = rows4(sm.egr, 1, q, h);
+                    y0[4 * q] *= e0.x; y0[4 * q + 1] *= e0.y; y0[4 * q + 2] *= e0.z; y0[4 * q + 3] *= e0.w;
+                    y2[4 * q] *= e1.x; y2[4 * q + 1] *= e1.y; y2[4 * q + 2] *= e1.z; y2[4 * q + 3] *= e1.w;
                 }
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb)
@@ -393,8 +427,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 const bf16x8 yb = acc_to_b(s < 2 ? y0 : y2, s & 1);
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb) {
-                    const u16 *row = &sm.Kt[(32 * mb + l32) * KTL + 32 * (s >> 1) + perm_col(s & 1, h)];
-                    st[mb] = mfma(lds4x2(row, row + 8), yb, st[mb]);
+                    st[mb] = mfma(lds8(&sm.Kt[(32 * mb + l32) * KTL + 16 * s + 8 * h]), yb, st[mb]);
                 }
             }
         }
