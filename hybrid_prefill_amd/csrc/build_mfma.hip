@@ -24,7 +24,8 @@
 //  * Prep waves 4-7 build the next chunk's factors meanwhile: the decay
 //    prefix, the Gram matrix and A0, A; the inverses of the 32x32 diagonal
 //    blocks (16x16 forward substitution, one 16 -> 32 merge on the MFMA);
-//    T_22 A_21; K^T; and they stage keys and values in LDS.
+//    T_22 A_21; and they stage keys and values in LDS.  K^T is turned around by
+//    the state waves in phase b.
 // Two workgroup barriers per chunk: in phase a the state waves finish chunk
 // c - 1 (solve, update) while the prep waves compute A of chunk c; in phase b
 // the state waves form W of chunk c while the prep waves invert.
@@ -45,7 +46,11 @@ namespace hypic {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -68,8 +73,10 @@ struct __align__(16) Smem {
     float Af[2][2][32 * AFL];  // per system: diagonal blocks A_11, A_22, inverted in place
     u16 A21t[2][32 * TBL];     // per system: A_21 transposed [s][t]
     float pv[4][2][CH];        // per prep wave: g, beta of the chunk being prepared
-    float eg[2][CH], egr[2][CH];
-    float eG[2];
+    float egs[2][CH];          // -e^{g_t} sigma_c: the K X factor of W (S columns)
+    float egrs[2][CH];         // e^{G - g_t} / sigma_{c+1}: the update factor (S columns)
+    float rs[2];               // sigma_c e^G when the scale is folded back into the state, else 1
+    float sig_fin;             // sigma after the last chunk
     int64_t t0, n;
     int32_t slot, state;
 };
@@ -84,19 +91,18 @@ __device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
 
 __device__ __forceinline__ u16 f2bf(float x) { return __builtin_bit_cast(u16, (__bf16)x); }
 
+// fp32 -> bf16 (round to nearest even), two values per v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
                                         float a7) {
-    u32x4 u = {pack2(a0, a1), pack2(a2, a3), pack2(a4, a5), pack2(a6, a7)};
-    return __builtin_bit_cast(bf16x8, u);
+    return __builtin_convertvector((f32x8){a0, a1, a2, a3, a4, a5, a6, a7}, bf16x8);
 }
 
 __device__ __forceinline__ s16x4 pack4(float a0, float a1, float a2, float a3) {
-    u32x2 u = {pack2(a0, a1), pack2(a2, a3)};
-    return __builtin_bit_cast(s16x4, u);
+    return __builtin_bit_cast(s16x4, __builtin_convertvector((f32x4){a0, a1, a2, a3}, bf16x4));
 }
 
 // 8 consecutive bf16 from LDS (16-byte aligned)
@@ -112,25 +118,42 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele inside each row
+// of 16 lanes (DPP row shifts, zero fill), then the row totals via the row
+// broadcasts of lane 15 (to rows 1, 3) and lane 31 (to rows 2, 3).
+#define HYPIC_DPP_ADD(X, CTRL, ROWMASK) \
+    X += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(X), CTRL, ROWMASK, 0xf, true))
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    HYPIC_DPP_ADD(x, 0x111, 0xf);    // row_shr:1
+    HYPIC_DPP_ADD(x, 0x112, 0xf);    // row_shr:2
+    HYPIC_DPP_ADD(x, 0x114, 0xf);    // row_shr:4
+    HYPIC_DPP_ADD(x, 0x118, 0xf);    // row_shr:8
+    HYPIC_DPP_ADD(x, 0x142, 0xa);    // row_bcast:15
+    HYPIC_DPP_ADD(x, 0x143, 0xc);    // row_bcast:31
+    return x;
+}
+#undef HYPIC_DPP_ADD
+
 // Row of the 32x32 accumulator element held in register r by lane half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// B operand (k-step `half` of a 32-row block) from accumulator registers, times sgn.
-__device__ __forceinline__ bf16x8 acc_to_b(const f32x16 &c, int half, float sgn = 1.0f) {
+// B operand (k-step `half` of a 32-row block) from accumulator registers.
+__device__ __forceinline__ bf16x8 acc_to_b(const f32x16 &c, int half) {
     const int o = 8 * half;
-    return pack8(sgn * c[o + 0], sgn * c[o + 1], sgn * c[o + 2], sgn * c[o + 3], sgn * c[o + 4], sgn * c[o + 5],
-                 sgn * c[o + 6], sgn * c[o + 7]);
+    return pack8(c[o + 0], c[o + 1], c[o + 2], c[o + 3], c[o + 4], c[o + 5], c[o + 6], c[o + 7]);
 }
 
 // Bits 2 and 3 swapped (an involution).
 __device__ __forceinline__ int swz(int c) { return (c & ~12) | ((c & 4) << 1) | ((c & 8) >> 1); }
 
-// B operand of the identity for k-step ks (column l32, rows 16 ks + 8h + e).
+// B operand of the identity for k-step ks (column l32, rows 16 ks + 8h + e): at most
+// one element is 1.0 (bf16 0x3f80), element d = l32 - 16 ks - 8h when 0 <= d < 8.
 __device__ __forceinline__ bf16x8 eye_b(int ks, int h, int l32) {
-    bf16x8 e8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) e8[e] = (__bf16)((16 * ks + 8 * h + e == l32) ? 1.0f : 0.0f);
-    return e8;
+    const int d = l32 - 16 * ks - 8 * h;
+    const uint32_t one = (unsigned)d < 8u ? 0x3f80u << (16 * (d & 1)) : 0u;
+    const int wd = d >> 1;
+    const u32x4 u = {wd == 0 ? one : 0u, wd == 1 ? one : 0u, wd == 2 ? one : 0u, wd == 3 ? one : 0u};
+    return __builtin_bit_cast(bf16x8, u);
 }
 
 // Per-token values for registers 4q..4q+3 of a swizzled accumulator tile whose
@@ -216,13 +239,20 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 #pragma unroll
                     for (int cb = 0; cb < 2; ++cb) y2[cb] = mfma(m21, acc_to_b(y1[cb], half), y2[cb]);
                 }
-                float ysgn = -1.0f;
                 if (isS) {
-                    ysgn = 1.0f;
-                    const float eG = sm.eG[b];
+                    const float rsc = sm.rs[b];
+                    if (rsc != 1.0f) {
+                        // the pending decay sigma_c e^G is folded into the state (rare)
+#pragma unroll
+                        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) st[cb][mb][r] *= rsc;
+                    }
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const float4 e0 = tok4(sm.egr[b], 0, q, h), e1 = tok4(sm.egr[b], 1, q, h);
+                        const float4 e0 = tok4(sm.egrs[b], 0, q, h), e1 = tok4(sm.egrs[b], 1, q, h);
 #pragma unroll
                         for (int cb = 0; cb < 2; ++cb) {
                             y1[cb][4 * q] *= e0.x; y1[cb][4 * q + 1] *= e0.y;
@@ -231,19 +261,14 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                             y2[cb][4 * q + 2] *= e1.z; y2[cb][4 * q + 3] *= e1.w;
                         }
                     }
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-                        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) st[cb][mb][r] *= eG;
                 }
-                // X += K^T (+-Y): A operand = Kt rows (channels) swz(32 mb + lane)
+                // X += K^T Y (the P factors are stored negated): A operand = Kt rows (channels)
+                // swz(32 mb + lane)
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     bf16x8 yb[2];
 #pragma unroll
-                    for (int cb = 0; cb < 2; ++cb) yb[cb] = acc_to_b(s < 2 ? y1[cb] : y2[cb], s & 1, ysgn);
+                    for (int cb = 0; cb < 2; ++cb) yb[cb] = acc_to_b(s < 2 ? y1[cb] : y2[cb], s & 1);
 #pragma unroll
                     for (int mb = 0; mb < 4; ++mb) {
                         const bf16x8 kt = lds8(&sm.Kt[swz(32 * mb + l32) * KTL + 16 * s + 8 * h]);
@@ -256,13 +281,22 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
             // ---- phase b: W of chunk i
             if (i < nc) {
                 const int b = (int)(i & 1);
+                // K^T of chunk i for the next update: blocks (tokens 32 tb, channels 32 ib),
+                // two per state wave, turned around on the MFMA
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int idx = 2 * w + u, tb = idx >> 2, ib = idx & 3;
+                    f32x16 kk;
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        kk = mfma(lds8(&sm.Km[b][(32 * tb + l32) * KML + 32 * ib + 16 * ks + 8 * h]), eye_b(ks, h, l32),
+                                  ks == 0 ? f32x16{} : kk);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<u32x2 *>(&sm.Kt[(32 * ib + l32) * KTL + 32 * tb + 8 * q + 4 * h]) =
+                            u32x2{pack2(kk[4 * q], kk[4 * q + 1]), pack2(kk[4 * q + 2], kk[4 * q + 3])};
+                }
                 f32x16 z[2][2];                   // [column block][token block], rows swizzled
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-                    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) z[cb][mb][r] = 0.f;
                 // K X: A operand = Km rows (tokens) swz(32 mb + lane), B = state rows in swizzled order
 #pragma unroll
                 for (int kb = 0; kb < 8; ++kb) {
@@ -273,7 +307,8 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     for (int mb = 0; mb < 2; ++mb) {
                         const bf16x8 km = lds8(&sm.Km[b][swz(32 * mb + l32) * KML + 16 * kb + 8 * h]);
 #pragma unroll
-                        for (int cb = 0; cb < 2; ++cb) z[cb][mb] = mfma(km, sb[cb], z[cb][mb]);
+                        for (int cb = 0; cb < 2; ++cb)
+                            z[cb][mb] = mfma(km, sb[cb], kb == 0 ? f32x16{} : z[cb][mb]);
                     }
                 }
                 if (isS) {
@@ -282,11 +317,11 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const float4 e4 = tok4(sm.eg[b], mb, q, h);
+                            const float4 e4 = tok4(sm.egs[b], mb, q, h);
 #pragma unroll
                             for (int cb = 0; cb < 2; ++cb) {
-                                z[cb][mb][4 * q] *= -e4.x; z[cb][mb][4 * q + 1] *= -e4.y;
-                                z[cb][mb][4 * q + 2] *= -e4.z; z[cb][mb][4 * q + 3] *= -e4.w;
+                                z[cb][mb][4 * q] *= e4.x; z[cb][mb][4 * q + 1] *= e4.y;
+                                z[cb][mb][4 * q + 2] *= e4.z; z[cb][mb][4 * q + 3] *= e4.w;
                             }
                         }
 #pragma unroll
@@ -311,8 +346,9 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
             }
             __syncthreads();                                        // b -> next a
         }
-        // ---- record: physical row p of a tile holds channel swz(p)
+        // ---- record: physical row p of a tile holds channel swz(p); S = sigma X
         const int h = (th & 63) >> 5, l32 = th & 31;
+        const float sfin = isS ? sm.sig_fin : 1.0f;
         float *dst = isS ? a.pool_S + rec * D * D : a.pool_P + rec * D * D;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
@@ -321,7 +357,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     dst[(int64_t)swz(32 * mb + acc_row(r, h)) * D + cbase + 32 * cb + l32] =
-                        bad ? nanv : st[cb][mb][r];
+                        bad ? nanv : st[cb][mb][r] * sfin;
     } else {
         // =============================== prep waves ===============================
         const int pw = w - 4;
@@ -331,29 +367,35 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         uint4 kr0, kr1, kr2, kr3, vr0, vr1, vr2, vr3;
         float lar = 0.f, br = 0.f;
         double ell = 0.0;     // thread 256 (prep wave 0, lane 0)
+        // S = sigma X for the S columns: the decay e^G of each chunk is carried in
+        // sigma (prep wave 0 keeps it) and folded into X only when sigma would drop
+        // below 2^-60, so the state waves do not rescale X every chunk.
+        float sig = 1.0f;
+        if (th == 256) sm.sig_fin = 1.0f;
 
-        // keys and values of the chunk at BASE: piece q of this thread is token
-        // (pt + 256 q) / 16, channels 8 ((pt + 256 q) % 16) .. +7; la, beta: token = lane
+        // Keys and values of the chunk at BASE: piece q of this thread is token
+        // (pt + 256 q) / 16 = pt / 16 + 16 q, channels 8 (pt % 16) .. +7; la, beta:
+        // token = lane.  Per-thread pointers at token 0 of the segment; a chunk and a
+        // piece only add a wave-uniform offset.
+        const int ptok = pt >> 4, pl = pt & 63;
+        const u16 *kq = kp + (t0 + ptok) * a.k_st + head * a.k_sh + 8 * (pt & 15);
+        const u16 *vq = vp + (t0 + ptok) * a.v_st + head * a.v_sh + 8 * (pt & 15);
+        const float *bq = a.beta ? a.beta + (t0 + pl) * a.b_st + head * a.b_sh : nullptr;
+        const float *lq = a.log_alpha ? a.log_alpha + (t0 + pl) * a.la_st + head * a.la_sh : nullptr;
 #define HYPIC_FETCH(BASE)                                                                            \
     do {                                                                                             \
-        int thf_ = pt;                                                                               \
-        asm volatile("" : "+v"(thf_));                                                               \
         const int64_t base_ = (BASE), rem_ = n - base_;                                              \
         const int cl_ = rem_ < CH ? (int)rem_ : CH;                                                  \
         HYPIC_FETCH_Q(0, kr0, vr0); HYPIC_FETCH_Q(1, kr1, vr1);                                      \
         HYPIC_FETCH_Q(2, kr2, vr2); HYPIC_FETCH_Q(3, kr3, vr3);                                      \
-        const int l_ = thf_ & 63;                                                                    \
-        const int64_t tt_ = t0 + base_ + l_;                                                         \
-        br = l_ < cl_ ? (a.beta ? a.beta[tt_ * a.b_st + head * a.b_sh] : 1.0f) : 0.0f;              \
-        lar = (l_ < cl_ && a.log_alpha) ? a.log_alpha[tt_ * a.la_st + head * a.la_sh] : 0.0f;        \
+        br = pl < cl_ ? (bq ? bq[base_ * a.b_st] : 1.0f) : 0.0f;                                     \
+        lar = (pl < cl_ && lq) ? lq[base_ * a.la_st] : 0.0f;                                         \
     } while (0)
 #define HYPIC_FETCH_Q(Q, KR, VR)                                                                     \
     do {                                                                                             \
-        const int pc_ = thf_ + 256 * (Q), tok_ = pc_ >> 4, col_ = 8 * (pc_ & 15);                    \
-        if (tok_ < cl_) {                                                                            \
-            const int64_t t_ = t0 + base_ + tok_;                                                    \
-            KR = *reinterpret_cast<const uint4 *>(kp + t_ * a.k_st + head * a.k_sh + col_);          \
-            VR = *reinterpret_cast<const uint4 *>(vp + t_ * a.v_st + head * a.v_sh + col_);          \
+        if (ptok + 16 * (Q) < cl_) {                                                                 \
+            KR = *reinterpret_cast<const uint4 *>(kq + (base_ + 16 * (Q)) * a.k_st);                 \
+            VR = *reinterpret_cast<const uint4 *>(vq + (base_ + 16 * (Q)) * a.v_st);                 \
         } else {                                                                                     \
             KR = VR = make_uint4(0, 0, 0, 0);                                                        \
         }                                                                                            \
@@ -384,19 +426,21 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 HYPIC_STAGE(sm.Vm, vr0, vr1, vr2, vr3);
                 const float la_i = lar, b_i = br;
                 if (i + 1 < nc) HYPIC_FETCH((i + 1) * CH);     // next chunk's loads fly during this one
-                float gv = la_i;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const float y = __shfl_up(gv, o);
-                    if (l >= o) gv += y;
-                }
+                const float gv = wave_prefix_sum(la_i);
                 sm.pv[pw][0][l] = gv;
                 sm.pv[pw][1][l] = b_i;
                 if (pw == 0) {
-                    const float gt = __shfl(gv, 63);
-                    sm.eg[b][l] = __expf(gv);
-                    sm.egr[b][l] = __expf(gt - gv);
-                    if (l == 63) sm.eG[b] = __expf(gt);
+                    const float gt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 63));
+                    const float sp = sig * __expf(gt);
+                    const bool fold = sp < 0x1p-60f;
+                    const float inv = fold ? 1.0f : 1.0f / sp;
+                    sm.egs[b][l] = -__expf(gv) * sig;
+                    sm.egrs[b][l] = __expf(gt - gv) * inv;
+                    if (l == 63) {
+                        sm.rs[b] = fold ? sp : 1.0f;
+                        sm.sig_fin = fold ? 1.0f : sp;
+                    }
+                    sig = fold ? 1.0f : sp;
                     double gd = (double)la_i;
 #pragma unroll
                     for (int o = 32; o >= 1; o >>= 1) gd += __shfl_xor(gd, o);
@@ -426,11 +470,10 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                         float a0[4], a1[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            a0[e] = 0.f; a1[e] = 0.f;
-                            if (s < t4 + e) {
-                                a0[e] = bb[e] * gacc[4 * q + e];
-                                a1[e] = a0[e] * __expf(ggv[e] - gs);
-                            }
+                            const bool low = s < t4 + e;
+                            const float v0 = bb[e] * gacc[4 * q + e];
+                            a0[e] = low ? v0 : 0.f;
+                            a1[e] = low ? v0 * __expf(ggv[e] - gs) : 0.f;
                         }
                         if (pw == 2) {
                             // A_21 transposed: row s, tokens t4 - 32 .. +3
@@ -458,21 +501,31 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 //     lanes 16-31 rows 16-31; lane = column
                 if (l < 32) {
                     const int R = 16 * (l >> 4), j = l & 15;
-                    float x[16];
+                    // the strictly lower rows of this 16x16 block, loaded up front (36 x 16 bytes)
+                    float4 mr[36];
 #pragma unroll
-                    for (int ii = 0; ii < 16; ++ii) {
-                        float acc = 0.f;
+                    for (int ii = 1, c = 0; ii < 16; ++ii)
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            if (4 * q < ii) {
-                                const float4 m = *reinterpret_cast<const float4 *>(&M[(R + ii) * AFL + R + 4 * q]);
-                                acc += m.x * x[4 * q];
-                                if (4 * q + 1 < ii) acc += m.y * x[4 * q + 1];
-                                if (4 * q + 2 < ii) acc += m.z * x[4 * q + 2];
-                                if (4 * q + 3 < ii) acc += m.w * x[4 * q + 3];
-                            }
+                        for (int q = 0; 4 * q < ii; ++q, ++c)
+                            mr[c] = *reinterpret_cast<const float4 *>(&M[(R + ii) * AFL + R + 4 * q]);
+                    // right-looking: once x_s is final, every later row takes its term at once,
+                    // so the dependent chain is one FMA per step
+                    float x[16], acc[16];
+#pragma unroll
+                    for (int ii = 0; ii < 16; ++ii) acc[ii] = 0.f;
+#pragma unroll
+                    for (int sc = 0; sc < 16; ++sc) {
+                        x[sc] = (sc == j) ? 1.0f : (sc < j ? 0.0f : -acc[sc]);
+#pragma unroll
+                        for (int ii = sc + 1; ii < 16; ++ii) {
+                            // M[ii][sc] sits in row ii's float4 number sc / 4
+                            int c = 0;
+#pragma unroll
+                            for (int i2 = 1; i2 < ii; ++i2) c += (i2 + 3) / 4;
+                            const float4 m = mr[c + sc / 4];
+                            const float mv = (sc & 3) == 0 ? m.x : (sc & 3) == 1 ? m.y : (sc & 3) == 2 ? m.z : m.w;
+                            acc[ii] += mv * x[sc];
                         }
-                        x[ii] = (ii == j) ? 1.0f : (ii < j ? 0.0f : -acc);
                     }
 #pragma unroll
                     for (int ii = 0; ii < 16; ++ii) M[(R + ii) * AFL + R + j] = x[ii];
@@ -499,12 +552,19 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 wave_lds_sync();
                 // (3) T diag(beta) of this block, bf16; lane = column, 16 rows per lane half
                 {
-                    const float bc = sm.pv[pw][1][32 * blk + l32];
-                    u16 *dst = sm.TB[sys][blk];
+                    // lane: row l / 2, columns 16 (l % 2) .. +15
+                    const int row = l >> 1, c0 = 16 * (l & 1);
+                    const float sg = sys == 0 ? -1.0f : 1.0f;     // P factors negated
+                    u16 *dst = &sm.TB[sys][blk][row * TBL + c0];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = 16 * h + r;
-                        dst[row * TBL + l32] = f2bf(M[row * AFL + l32] * bc);
+                    for (int u = 0; u < 2; ++u) {
+                        const float4 m0 = *reinterpret_cast<const float4 *>(&M[row * AFL + c0 + 8 * u]);
+                        const float4 m1 = *reinterpret_cast<const float4 *>(&M[row * AFL + c0 + 8 * u + 4]);
+                        const float4 b0 = *reinterpret_cast<const float4 *>(&sm.pv[pw][1][32 * blk + c0 + 8 * u]);
+                        const float4 b1 = *reinterpret_cast<const float4 *>(&sm.pv[pw][1][32 * blk + c0 + 8 * u + 4]);
+                        *reinterpret_cast<bf16x8 *>(dst + 8 * u) =
+                            pack8(sg * m0.x * b0.x, sg * m0.y * b0.y, sg * m0.z * b0.z, sg * m0.w * b0.w,
+                                  sg * m1.x * b1.x, sg * m1.y * b1.y, sg * m1.z * b1.z, sg * m1.w * b1.w);
                     }
                 }
                 // (4) -(T_22 A_21): prep waves 1 and 3 (block 1 of each system)
@@ -523,23 +583,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) sm.TB[sys][2][acc_row(r, h) * TBL + l32] = f2bf(-m21[r]);
                 }
-                // (5) K^T: blocks (tokens 32 tb, channels 32 ib), two per prep wave
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int idx = 2 * pw + u, tb = idx >> 2, ib = idx & 3;
-                    f32x16 kk;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) kk[r] = 0.f;
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        kk = mfma(lds8(&sm.Km[b][(32 * tb + l32) * KML + 32 * ib + 16 * ks + 8 * h]), eye_b(ks, h, l32),
-                                  kk);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<u32x2 *>(&sm.Kt[(32 * ib + l32) * KTL + 32 * tb + 8 * q + 4 * h]) =
-                            u32x2{pack2(kk[4 * q], kk[4 * q + 1]), pack2(kk[4 * q + 2], kk[4 * q + 3])};
-                }
-                // (6) keys of chunk i + 1 into the other buffer
+                // (5) keys of chunk i + 1 into the other buffer
                 if (i + 1 < nc) HYPIC_STAGE(sm.Km[b ^ 1], kr0, kr1, kr2, kr3);
             }
             __syncthreads();                                        // b -> next a
