@@ -24,8 +24,8 @@
 //  * Prep waves 4-7 build the next chunk's factors meanwhile: the decay
 //    prefix, the Gram matrix and A0, A; the inverses of the 32x32 diagonal
 //    blocks (16x16 forward substitution, one 16 -> 32 merge on the MFMA);
-//    T_22 A_21; and they stage keys and values in LDS.  K^T is turned around by
-//    the state waves in phase b.
+//    T_22 A_21; prep wave 0 also loads keys and values into LDS.  K^T is turned
+//    around by the state waves in phase b.
 // Two workgroup barriers per chunk: in phase a the state waves finish chunk
 // c - 1 (solve, update) while the prep waves compute A of chunk c; in phase b
 // the state waves form W of chunk c while the prep waves invert.
@@ -60,14 +60,14 @@ typedef uint16_t u16;
 constexpr int CH = 64;     // tokens per chunk
 constexpr int D = 128;     // d_k = d_v
 constexpr int NT = 512;    // 4 state waves + 4 prep waves
-constexpr int KML = 136;   // row length (bf16) of Km, Vm [token][channel]
+constexpr int KML = 128;   // row length (bf16) of Km, Vm [token][channel], granules swizzled (kmo)
 constexpr int KTL = 72;    // row length (bf16) of Kt [channel][token]
 constexpr int AFL = 36;    // row length (fp32) of the 32x32 diagonal blocks in Af
 constexpr int TBL = 40;    // row length (bf16) of the 32x32 factor tiles
 
 struct __align__(16) Smem {
     u16 Km[2][CH * KML];       // keys, token-major, double-buffered by chunk parity
-    u16 Vm[CH * KML];          // values, token-major
+    u16 Vm[2][CH * KML];       // values, token-major, double-buffered by chunk parity
     u16 Kt[D * KTL];           // keys, channel-major
     u16 TB[2][3][32 * TBL];    // per system: T_11 diag(beta_1), T_22 diag(beta_2), -(T_22 A_21)
     float Af[2][2][32 * AFL];  // per system: diagonal blocks A_11, A_22, inverted in place
@@ -80,6 +80,11 @@ struct __align__(16) Smem {
     int64_t t0, n;
     int32_t slot, state;
 };
+
+// Km, Vm: 16-byte granule g of row t sits in slot g ^ (t % 16) of the row, so the 16
+// rows one MFMA operand read touches hit 16 different slots (no bank conflicts)
+// without padding, which lets global_load_lds fill the rows directly.
+__device__ __forceinline__ int kmo(int t, int g) { return t * KML + ((g ^ (t & 15)) << 3); }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -160,6 +165,157 @@ __device__ __forceinline__ bf16x8 eye_b(int ks, int h, int l32) {
 // physical rows 32 mb + 8q + 4h + 0..3 hold tokens 32 mb + 16 (q/2) + 8h + 4 (q%2) + 0..3.
 __device__ __forceinline__ float4 tok4(const float *v, int mb, int q, int h) {
     return *reinterpret_cast<const float4 *>(v + 32 * mb + 16 * (q >> 1) + 8 * h + 4 * (q & 1));
+}
+
+// Prep wave pw, phase b: the factors of 32x32 diagonal block `blk` of system `sys`
+// (0: A0, for P; 1: A, for S) from its A block in Af: the inverse T by 16x16
+// forward substitution and one merge, T diag(beta) into TB (negated for P), and
+// for blk 1 also -(T_22 A_21).
+__device__ __forceinline__ void prep_invert(Smem &sm, int sys, int blk, int pw, int l) {
+    const int h = l >> 5, l32 = l & 31;
+    float *M = sm.Af[sys][blk];
+    // (1) 16x16 diagonal blocks by forward substitution: lanes 0-15 rows 0-15,
+    //     lanes 16-31 rows 16-31; lane = column
+    if (l < 32) {
+        const int R = 16 * (l >> 4), j = l & 15;
+        // the strictly lower rows of this 16x16 block, loaded up front (36 x 16 bytes)
+        float4 mr[36];
+#pragma unroll
+        for (int ii = 1, c = 0; ii < 16; ++ii)
+#pragma unroll
+            for (int q = 0; 4 * q < ii; ++q, ++c)
+                mr[c] = *reinterpret_cast<const float4 *>(&M[(R + ii) * AFL + R + 4 * q]);
+        // right-looking: once x_s is final, every later row takes its term at once,
+        // so the dependent chain is one FMA per step
+        float x[16], acc[16];
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) acc[ii] = 0.f;
+#pragma unroll
+        for (int sc = 0; sc < 16; ++sc) {
+            x[sc] = (sc == j) ? 1.0f : (sc < j ? 0.0f : -acc[sc]);
+#pragma unroll
+            for (int ii = sc + 1; ii < 16; ++ii) {
+                // M[ii][sc] sits in row ii's float4 number sc / 4
+                int c = 0;
+#pragma unroll
+                for (int i2 = 1; i2 < ii; ++i2) c += (i2 + 3) / 4;
+                const float4 m = mr[c + sc / 4];
+                const float mv = (sc & 3) == 0 ? m.x : (sc & 3) == 1 ? m.y : (sc & 3) == 2 ? m.z : m.w;
+                acc[ii] += mv * x[sc];
+            }
+        }
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) M[(R + ii) * AFL + R + j] = x[ii];
+    }
+    wave_lds_sync();
+    // (2) T_10 = -T_11 (A_10 T_00) on the 16x16x16 MFMA (lane: column l%16,
+    //     contraction / rows 4 (l/16) + 0..3)
+    {
+        const int c16 = l & 15, k4 = 4 * (l >> 4);
+        const float4 a10 = *reinterpret_cast<const float4 *>(&M[(16 + c16) * AFL + k4]);
+        const s16x4 fa = pack4(a10.x, a10.y, a10.z, a10.w);
+        const s16x4 fb = pack4(M[(k4 + 0) * AFL + c16], M[(k4 + 1) * AFL + c16], M[(k4 + 2) * AFL + c16],
+                               M[(k4 + 3) * AFL + c16]);
+        f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+        tmp = mfma16(fa, fb, tmp);
+        const float4 t11 = *reinterpret_cast<const float4 *>(&M[(16 + c16) * AFL + 16 + k4]);
+        const s16x4 fa2 = pack4(-t11.x, -t11.y, -t11.z, -t11.w);
+        const s16x4 fb2 = pack4(tmp[0], tmp[1], tmp[2], tmp[3]);
+        f32x4 t10 = {0.f, 0.f, 0.f, 0.f};
+        t10 = mfma16(fa2, fb2, t10);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) M[(16 + k4 + r) * AFL + c16] = t10[r];
+    }
+    wave_lds_sync();
+    // (3) T diag(beta) of this block, bf16; lane = column, 16 rows per lane half
+    {
+        // lane: row l / 2, columns 16 (l % 2) .. +15
+        const int row = l >> 1, c0 = 16 * (l & 1);
+        const float sg = sys == 0 ? -1.0f : 1.0f;     // P factors negated
+        u16 *dst = &sm.TB[sys][blk][row * TBL + c0];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const float4 m0 = *reinterpret_cast<const float4 *>(&M[row * AFL + c0 + 8 * u]);
+            const float4 m1 = *reinterpret_cast<const float4 *>(&M[row * AFL + c0 + 8 * u + 4]);
+            const float4 b0 = *reinterpret_cast<const float4 *>(&sm.pv[pw][1][32 * blk + c0 + 8 * u]);
+            const float4 b1 = *reinterpret_cast<const float4 *>(&sm.pv[pw][1][32 * blk + c0 + 8 * u + 4]);
+            *reinterpret_cast<bf16x8 *>(dst + 8 * u) =
+                pack8(sg * m0.x * b0.x, sg * m0.y * b0.y, sg * m0.z * b0.z, sg * m0.w * b0.w,
+                      sg * m1.x * b1.x, sg * m1.y * b1.y, sg * m1.z * b1.z, sg * m1.w * b1.w);
+        }
+    }
+    // (4) -(T_22 A_21): prep waves 1 and 3 (block 1 of each system)
+    if (blk == 1) {
+        f32x16 m21;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m21[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const float *p = &M[l32 * AFL + 16 * ks + 8 * h];
+            const float4 x0 = *reinterpret_cast<const float4 *>(p);
+            const float4 x1 = *reinterpret_cast<const float4 *>(p + 4);
+            m21 = mfma(pack8(x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w),
+                       lds8(&sm.A21t[sys][l32 * TBL + 16 * ks + 8 * h]), m21);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.TB[sys][2][acc_row(r, h) * TBL + l32] = f2bf(-m21[r]);
+    }
+
+}
+
+// Prep wave pw = 1..3, phase a: Gram block (0,0), (1,0) or (1,1) of the chunk in
+// Km[b] on the MFMA, then A0 = beta_t k_t.k_s and A = A0 e^{g_t - g_s} below the
+// diagonal: diagonal blocks into Af (fp32), block (1,0) transposed into A21t (bf16).
+// pv[pw] holds this wave's g and beta.
+__device__ __forceinline__ void prep_gram(Smem &sm, int b, int pw, int l) {
+    const int h = l >> 5, l32 = l & 31;
+    // Gram block (gmb, gnb): (0,0) for prep wave 1, (1,0) for 2, (1,1) for 3
+    const int gmb = pw >= 2 ? 1 : 0, gnb = pw == 3 ? 1 : 0;
+    const int s = 32 * gnb + l32;
+    const float gs = sm.pv[pw][0][s];
+    float4 bqv[4], gqv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        bqv[q] = *reinterpret_cast<const float4 *>(&sm.pv[pw][1][32 * gmb + 8 * q + 4 * h]);
+        gqv[q] = *reinterpret_cast<const float4 *>(&sm.pv[pw][0][32 * gmb + 8 * q + 4 * h]);
+    }
+    f32x16 ga0, ga1;     // even and odd k-steps: two shorter dependent chains
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        const bf16x8 fa = lds8(&sm.Km[b][kmo(32 * gmb + l32, 2 * kb + h)]);
+        const bf16x8 fb =
+            gmb == gnb ? fa : lds8(&sm.Km[b][kmo(32 * gnb + l32, 2 * kb + h)]);
+        if (kb & 1) ga1 = mfma(fa, fb, kb == 1 ? f32x16{} : ga1);
+        else ga0 = mfma(fa, fb, kb == 0 ? f32x16{} : ga0);
+    }
+    const f32x16 gacc = ga0 + ga1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int t4 = 32 * gmb + 8 * q + 4 * h;
+        const float4 bq4 = bqv[q], gq4 = gqv[q];
+        const float bb[4] = {bq4.x, bq4.y, bq4.z, bq4.w}, ggv[4] = {gq4.x, gq4.y, gq4.z, gq4.w};
+        float a0[4], a1[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool low = s < t4 + e;
+            const float v0 = bb[e] * gacc[4 * q + e];
+            a0[e] = low ? v0 : 0.f;
+            a1[e] = low ? v0 * __expf(ggv[e] - gs) : 0.f;
+        }
+        if (pw == 2) {
+            // A_21 transposed: row s, tokens t4 - 32 .. +3
+            const int o = l32 * TBL + t4 - 32;
+            *reinterpret_cast<u32x2 *>(&sm.A21t[0][o]) = u32x2{pack2(a0[0], a0[1]), pack2(a0[2], a0[3])};
+            *reinterpret_cast<u32x2 *>(&sm.A21t[1][o]) = u32x2{pack2(a1[0], a1[1]), pack2(a1[2], a1[3])};
+        } else {
+            float *A0 = sm.Af[0][gmb], *A1 = sm.Af[1][gmb];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                A0[(t4 - 32 * gmb + e) * AFL + l32] = a0[e];
+                A1[(t4 - 32 * gmb + e) * AFL + l32] = a1[e];
+            }
+        }
+    }
 }
 
 __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
@@ -289,7 +445,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     f32x16 kk;
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks)
-                        kk = mfma(lds8(&sm.Km[b][(32 * tb + l32) * KML + 32 * ib + 16 * ks + 8 * h]), eye_b(ks, h, l32),
+                        kk = mfma(lds8(&sm.Km[b][kmo(32 * tb + l32, 4 * ib + 2 * ks + h)]), eye_b(ks, h, l32),
                                   ks == 0 ? f32x16{} : kk);
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
@@ -305,7 +461,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     for (int cb = 0; cb < 2; ++cb) sb[cb] = acc_to_b(st[cb][kb >> 1], kb & 1);
 #pragma unroll
                     for (int mb = 0; mb < 2; ++mb) {
-                        const bf16x8 km = lds8(&sm.Km[b][swz(32 * mb + l32) * KML + 16 * kb + 8 * h]);
+                        const bf16x8 km = lds8(&sm.Km[b][kmo(swz(32 * mb + l32), 2 * kb + h)]);
 #pragma unroll
                         for (int cb = 0; cb < 2; ++cb)
                             z[cb][mb] = mfma(km, sb[cb], kb == 0 ? f32x16{} : z[cb][mb]);
@@ -332,7 +488,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 #pragma unroll
                             for (int cb = 0; cb < 2; ++cb)
                                 z[cb][mb] = mfma(
-                                    lds8(&sm.Vm[swz(32 * mb + l32) * KML + cbase + 32 * cb + 16 * ks + 8 * h]), eye,
+                                    lds8(&sm.Vm[b][kmo(swz(32 * mb + l32), (cbase + 32 * cb) / 8 + 2 * ks + h)]), eye,
                                     z[cb][mb]);
                     }
                 }
@@ -361,75 +517,88 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
     } else {
         // =============================== prep waves ===============================
         const int pw = w - 4;
-        const int pt = th - 256;
-        const u16 *kp = static_cast<const u16 *>(a.k);
-        const u16 *vp = static_cast<const u16 *>(a.v);
-        uint4 kr0, kr1, kr2, kr3, vr0, vr1, vr2, vr3;
-        float lar = 0.f, br = 0.f;
-        double ell = 0.0;     // thread 256 (prep wave 0, lane 0)
-        // S = sigma X for the S columns: the decay e^G of each chunk is carried in
-        // sigma (prep wave 0 keeps it) and folded into X only when sigma would drop
-        // below 2^-60, so the state waves do not rescale X every chunk.
-        float sig = 1.0f;
-        if (th == 256) sm.sig_fin = 1.0f;
-
-        // Keys and values of the chunk at BASE: piece q of this thread is token
-        // (pt + 256 q) / 16 = pt / 16 + 16 q, channels 8 (pt % 16) .. +7; la, beta:
-        // token = lane.  Per-thread pointers at token 0 of the segment; a chunk and a
-        // piece only add a wave-uniform offset.
-        const int ptok = pt >> 4, pl = pt & 63;
-        const u16 *kq = kp + (t0 + ptok) * a.k_st + head * a.k_sh + 8 * (pt & 15);
-        const u16 *vq = vp + (t0 + ptok) * a.v_st + head * a.v_sh + 8 * (pt & 15);
+        const int pl = th & 63;
+        // every prep wave loads la and beta of a chunk itself (lane = token)
         const float *bq = a.beta ? a.beta + (t0 + pl) * a.b_st + head * a.b_sh : nullptr;
         const float *lq = a.log_alpha ? a.log_alpha + (t0 + pl) * a.la_st + head * a.la_sh : nullptr;
-#define HYPIC_FETCH(BASE)                                                                            \
+        float lar = 0.f, br = 0.f;
+#define HYPIC_FETCH_G(BASE)                                                                          \
     do {                                                                                             \
         const int64_t base_ = (BASE), rem_ = n - base_;                                              \
         const int cl_ = rem_ < CH ? (int)rem_ : CH;                                                  \
-        HYPIC_FETCH_Q(0, kr0, vr0); HYPIC_FETCH_Q(1, kr1, vr1);                                      \
-        HYPIC_FETCH_Q(2, kr2, vr2); HYPIC_FETCH_Q(3, kr3, vr3);                                      \
         br = pl < cl_ ? (bq ? bq[base_ * a.b_st] : 1.0f) : 0.0f;                                     \
         lar = (pl < cl_ && lq) ? lq[base_ * a.la_st] : 0.0f;                                         \
     } while (0)
-#define HYPIC_FETCH_Q(Q, KR, VR)                                                                     \
+        if (nc > 0) HYPIC_FETCH_G(0);
+        if (pw == 0) {
+            // ---- prep wave 0: loads keys and values, the decay factors, ell; inverts
+            //      block 0 of the P system.
+            // Keys and values go straight from HBM into Km/Vm (global_load_lds): the
+            // instruction for rows 4u .. 4u + 3 lands lane l's 16 bytes in row 4u + l / 16,
+            // slot l % 16, so the lane loads the granule that kmo puts there.  Rows past
+            // the segment repeat its last row (finite values; their beta is zero).
+            const u16 *kh = static_cast<const u16 *>(a.k) + t0 * a.k_st + head * a.k_sh;
+            const u16 *vh = static_cast<const u16 *>(a.v) + t0 * a.v_st + head * a.v_sh;
+            // full chunks (the common case): element offsets of this lane's sixteen
+            // pieces, relative to the chunk's first row, fixed for the whole segment
+            const bool small_st = (int64_t)CH * (a.k_st > a.v_st ? a.k_st : a.v_st) < (1LL << 30);
+            uint32_t ko[16], vo[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int t = 4 * u + (pl >> 4), g = (pl & 15) ^ (t & 15);
+                ko[u] = small_st ? (uint32_t)(t * a.k_st + 8 * g) : 0u;
+                vo[u] = small_st ? (uint32_t)(t * a.v_st + 8 * g) : 0u;
+            }
+#define HYPIC_LOAD_KV(BASE, BUF)                                                                     \
     do {                                                                                             \
-        if (ptok + 16 * (Q) < cl_) {                                                                 \
-            KR = *reinterpret_cast<const uint4 *>(kq + (base_ + 16 * (Q)) * a.k_st);                 \
-            VR = *reinterpret_cast<const uint4 *>(vq + (base_ + 16 * (Q)) * a.v_st);                 \
+        const int64_t base_ = (BASE), rem_ = n - base_;                                              \
+        const u16 *kc_ = kh + base_ * a.k_st, *vc_ = vh + base_ * a.v_st;                            \
+        if (rem_ >= CH && small_st) {                                                                \
+            _Pragma("unroll") for (int u_ = 0; u_ < 16; ++u_) {                                      \
+                __builtin_amdgcn_global_load_lds(kc_ + ko[u_], &sm.Km[BUF][4 * u_ * KML], 16, 0, 0);  \
+                __builtin_amdgcn_global_load_lds(vc_ + vo[u_], &sm.Vm[BUF][4 * u_ * KML], 16, 0, 0);  \
+            }                                                                                        \
         } else {                                                                                     \
-            KR = VR = make_uint4(0, 0, 0, 0);                                                        \
+            const int cl_ = rem_ < CH ? (int)rem_ : CH;                                              \
+            int l_ = pl;                                                                             \
+            asm volatile("" : "+v"(l_));                                                             \
+            const int r_ = l_ >> 4, p_ = l_ & 15;                                                    \
+            _Pragma("unroll") for (int u_ = 0; u_ < 16; ++u_) {                                      \
+                const int t_ = 4 * u_ + r_, ts_ = t_ < cl_ ? t_ : cl_ - 1;                           \
+                const int g_ = p_ ^ (t_ & 15);                                                       \
+                __builtin_amdgcn_global_load_lds(kc_ + ts_ * a.k_st + 8 * g_,                        \
+                                                 &sm.Km[BUF][4 * u_ * KML], 16, 0, 0);               \
+                __builtin_amdgcn_global_load_lds(vc_ + ts_ * a.v_st + 8 * g_,                        \
+                                                 &sm.Vm[BUF][4 * u_ * KML], 16, 0, 0);               \
+            }                                                                                        \
         }                                                                                            \
     } while (0)
-#define HYPIC_STAGE(DST, R0, R1, R2, R3)                                                             \
-    do {                                                                                             \
-        int thf_ = pt;                                                                               \
-        asm volatile("" : "+v"(thf_));                                                               \
-        const int tok_ = thf_ >> 4, col_ = 8 * (thf_ & 15);                                          \
-        *reinterpret_cast<uint4 *>(&(DST)[tok_ * KML + col_]) = R0;                                  \
-        *reinterpret_cast<uint4 *>(&(DST)[(tok_ + 16) * KML + col_]) = R1;                           \
-        *reinterpret_cast<uint4 *>(&(DST)[(tok_ + 32) * KML + col_]) = R2;                           \
-        *reinterpret_cast<uint4 *>(&(DST)[(tok_ + 48) * KML + col_]) = R3;                           \
-    } while (0)
-
-        if (nc > 0) {
-            HYPIC_FETCH(0);
-            HYPIC_STAGE(sm.Km[0], kr0, kr1, kr2, kr3);
-        }
-        __syncthreads();                                            // prologue: chunk 0 staged
-        for (int64_t i = 0; i <= nc; ++i) {
-            int thv = th;
-            asm volatile("" : "+v"(thv));
-            const int l = thv & 63, h = l >> 5, l32 = l & 31;
-            // ---- phase a: decay prefix, Gram, A0 and A of chunk i
-            if (i < nc) {
-                const int b = (int)(i & 1);
-                HYPIC_STAGE(sm.Vm, vr0, vr1, vr2, vr3);
-                const float la_i = lar, b_i = br;
-                if (i + 1 < nc) HYPIC_FETCH((i + 1) * CH);     // next chunk's loads fly during this one
-                const float gv = wave_prefix_sum(la_i);
-                sm.pv[pw][0][l] = gv;
-                sm.pv[pw][1][l] = b_i;
-                if (pw == 0) {
+            double ell = 0.0;     // this lane's tokens; summed over the wave at the end
+            // S = sigma X for the S columns: the decay e^G of each chunk is carried in
+            // sigma and folded into X only when sigma would drop below 2^-60, so the
+            // state waves do not rescale X every chunk.
+            float sig = 1.0f;
+            if (pl == 0) sm.sig_fin = 1.0f;
+            if (nc > 0) {
+                HYPIC_LOAD_KV(0, 0);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            __syncthreads();                                        // prologue: chunk 0 staged
+            for (int64_t i = 0; i <= nc; ++i) {
+                int thv = th;
+                asm volatile("" : "+v"(thv));
+                const int l = thv & 63;
+                // ---- phase a: decay factors of chunk i; keys and values of chunk i + 1 start
+                if (i < nc) {
+                    const int b = (int)(i & 1);
+                    const float la_i = lar, b_i = br;
+                    if (i + 1 < nc) {
+                        HYPIC_FETCH_G((i + 1) * CH);
+                        HYPIC_LOAD_KV((i + 1) * CH, b ^ 1);     // lands during this chunk
+                    }
+                    const float gv = wave_prefix_sum(la_i);
+                    sm.pv[0][0][l] = gv;
+                    sm.pv[0][1][l] = b_i;
                     const float gt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 63));
                     const float sp = sig * __expf(gt);
                     const bool fold = sp < 0x1p-60f;
@@ -441,157 +610,41 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                         sm.sig_fin = fold ? 1.0f : sp;
                     }
                     sig = fold ? 1.0f : sp;
-                    double gd = (double)la_i;
+                    ell += (double)la_i;
+                }
+                __syncthreads();                                    // a -> b
+                // ---- phase b: keys and values of chunk i + 1 into the other buffers;
+                //      factors of block 0 of the P system
+                if (i < nc) prep_invert(sm, 0, 0, 0, l);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // chunk i + 1 has landed
+                __syncthreads();                                    // b -> next a
+            }
 #pragma unroll
-                    for (int o = 32; o >= 1; o >>= 1) gd += __shfl_xor(gd, o);
-                    ell += gd;
-                } else {
+            for (int o = 32; o >= 1; o >>= 1) ell += __shfl_xor(ell, o);
+            if (th == 256) a.pool_ell[rec] = bad ? nanv : (float)ell;
+#undef HYPIC_LOAD_KV
+        } else {
+            // ---- prep waves 1-3: Gram block and A in phase a; one factor block in phase b
+            __syncthreads();                                        // prologue: chunk 0 staged
+            for (int64_t i = 0; i <= nc; ++i) {
+                int thv = th;
+                asm volatile("" : "+v"(thv));
+                const int l = thv & 63;
+                if (i < nc) {
+                    const int b = (int)(i & 1);
+                    const float la_i = lar, b_i = br;
+                    if (i + 1 < nc) HYPIC_FETCH_G((i + 1) * CH);
+                    sm.pv[pw][0][l] = wave_prefix_sum(la_i);
+                    sm.pv[pw][1][l] = b_i;
                     wave_lds_sync();
-                    // Gram block (gmb, gnb): (0,0) for prep wave 1, (1,0) for 2, (1,1) for 3
-                    const int gmb = pw >= 2 ? 1 : 0, gnb = pw == 3 ? 1 : 0;
-                    f32x16 gacc;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) gacc[r] = 0.f;
-#pragma unroll
-                    for (int kb = 0; kb < 8; ++kb) {
-                        const bf16x8 fa = lds8(&sm.Km[b][(32 * gmb + l32) * KML + 16 * kb + 8 * h]);
-                        const bf16x8 fb =
-                            gmb == gnb ? fa : lds8(&sm.Km[b][(32 * gnb + l32) * KML + 16 * kb + 8 * h]);
-                        gacc = mfma(fa, fb, gacc);
-                    }
-                    const int s = 32 * gnb + l32;
-                    const float gs = sm.pv[pw][0][s];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int t4 = 32 * gmb + 8 * q + 4 * h;
-                        const float4 bq = *reinterpret_cast<const float4 *>(&sm.pv[pw][1][t4]);
-                        const float4 gq = *reinterpret_cast<const float4 *>(&sm.pv[pw][0][t4]);
-                        const float bb[4] = {bq.x, bq.y, bq.z, bq.w}, ggv[4] = {gq.x, gq.y, gq.z, gq.w};
-                        float a0[4], a1[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const bool low = s < t4 + e;
-                            const float v0 = bb[e] * gacc[4 * q + e];
-                            a0[e] = low ? v0 : 0.f;
-                            a1[e] = low ? v0 * __expf(ggv[e] - gs) : 0.f;
-                        }
-                        if (pw == 2) {
-                            // A_21 transposed: row s, tokens t4 - 32 .. +3
-                            const int o = l32 * TBL + t4 - 32;
-                            *reinterpret_cast<u32x2 *>(&sm.A21t[0][o]) = u32x2{pack2(a0[0], a0[1]), pack2(a0[2], a0[3])};
-                            *reinterpret_cast<u32x2 *>(&sm.A21t[1][o]) = u32x2{pack2(a1[0], a1[1]), pack2(a1[2], a1[3])};
-                        } else {
-                            float *A0 = sm.Af[0][gmb], *A1 = sm.Af[1][gmb];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                A0[(t4 - 32 * gmb + e) * AFL + l32] = a0[e];
-                                A1[(t4 - 32 * gmb + e) * AFL + l32] = a1[e];
-                            }
-                        }
-                    }
+                    prep_gram(sm, b, pw, l);
                 }
+                __syncthreads();                                    // a -> b
+                if (i < nc) prep_invert(sm, pw >> 1, pw & 1, pw, l);
+                __syncthreads();                                    // b -> next a
             }
-            __syncthreads();                                        // a -> b
-            // ---- phase b: factors of chunk i, K^T, keys of chunk i + 1
-            if (i < nc) {
-                const int b = (int)(i & 1);
-                const int sys = pw >> 1, blk = pw & 1;
-                float *M = sm.Af[sys][blk];
-                // (1) 16x16 diagonal blocks by forward substitution: lanes 0-15 rows 0-15,
-                //     lanes 16-31 rows 16-31; lane = column
-                if (l < 32) {
-                    const int R = 16 * (l >> 4), j = l & 15;
-                    // the strictly lower rows of this 16x16 block, loaded up front (36 x 16 bytes)
-                    float4 mr[36];
-#pragma unroll
-                    for (int ii = 1, c = 0; ii < 16; ++ii)
-#pragma unroll
-                        for (int q = 0; 4 * q < ii; ++q, ++c)
-                            mr[c] = *reinterpret_cast<const float4 *>(&M[(R + ii) * AFL + R + 4 * q]);
-                    // right-looking: once x_s is final, every later row takes its term at once,
-                    // so the dependent chain is one FMA per step
-                    float x[16], acc[16];
-#pragma unroll
-                    for (int ii = 0; ii < 16; ++ii) acc[ii] = 0.f;
-#pragma unroll
-                    for (int sc = 0; sc < 16; ++sc) {
-                        x[sc] = (sc == j) ? 1.0f : (sc < j ? 0.0f : -acc[sc]);
-#pragma unroll
-                        for (int ii = sc + 1; ii < 16; ++ii) {
-                            // M[ii][sc] sits in row ii's float4 number sc / 4
-                            int c = 0;
-#pragma unroll
-                            for (int i2 = 1; i2 < ii; ++i2) c += (i2 + 3) / 4;
-                            const float4 m = mr[c + sc / 4];
-                            const float mv = (sc & 3) == 0 ? m.x : (sc & 3) == 1 ? m.y : (sc & 3) == 2 ? m.z : m.w;
-                            acc[ii] += mv * x[sc];
-                        }
-                    }
-#pragma unroll
-                    for (int ii = 0; ii < 16; ++ii) M[(R + ii) * AFL + R + j] = x[ii];
-                }
-                wave_lds_sync();
-                // (2) T_10 = -T_11 (A_10 T_00) on the 16x16x16 MFMA (lane: column l%16,
-                //     contraction / rows 4 (l/16) + 0..3)
-                {
-                    const int c16 = l & 15, k4 = 4 * (l >> 4);
-                    const float4 a10 = *reinterpret_cast<const float4 *>(&M[(16 + c16) * AFL + k4]);
-                    const s16x4 fa = pack4(a10.x, a10.y, a10.z, a10.w);
-                    const s16x4 fb = pack4(M[(k4 + 0) * AFL + c16], M[(k4 + 1) * AFL + c16], M[(k4 + 2) * AFL + c16],
-                                           M[(k4 + 3) * AFL + c16]);
-                    f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
-                    tmp = mfma16(fa, fb, tmp);
-                    const float4 t11 = *reinterpret_cast<const float4 *>(&M[(16 + c16) * AFL + 16 + k4]);
-                    const s16x4 fa2 = pack4(-t11.x, -t11.y, -t11.z, -t11.w);
-                    const s16x4 fb2 = pack4(tmp[0], tmp[1], tmp[2], tmp[3]);
-                    f32x4 t10 = {0.f, 0.f, 0.f, 0.f};
-                    t10 = mfma16(fa2, fb2, t10);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) M[(16 + k4 + r) * AFL + c16] = t10[r];
-                }
-                wave_lds_sync();
-                // (3) T diag(beta) of this block, bf16; lane = column, 16 rows per lane half
-                {
-                    // lane: row l / 2, columns 16 (l % 2) .. +15
-                    const int row = l >> 1, c0 = 16 * (l & 1);
-                    const float sg = sys == 0 ? -1.0f : 1.0f;     // P factors negated
-                    u16 *dst = &sm.TB[sys][blk][row * TBL + c0];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const float4 m0 = *reinterpret_cast<const float4 *>(&M[row * AFL + c0 + 8 * u]);
-                        const float4 m1 = *reinterpret_cast<const float4 *>(&M[row * AFL + c0 + 8 * u + 4]);
-                        const float4 b0 = *reinterpret_cast<const float4 *>(&sm.pv[pw][1][32 * blk + c0 + 8 * u]);
-                        const float4 b1 = *reinterpret_cast<const float4 *>(&sm.pv[pw][1][32 * blk + c0 + 8 * u + 4]);
-                        *reinterpret_cast<bf16x8 *>(dst + 8 * u) =
-                            pack8(sg * m0.x * b0.x, sg * m0.y * b0.y, sg * m0.z * b0.z, sg * m0.w * b0.w,
-                                  sg * m1.x * b1.x, sg * m1.y * b1.y, sg * m1.z * b1.z, sg * m1.w * b1.w);
-                    }
-                }
-                // (4) -(T_22 A_21): prep waves 1 and 3 (block 1 of each system)
-                if (blk == 1) {
-                    f32x16 m21;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) m21[r] = 0.f;
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        const float *p = &M[l32 * AFL + 16 * ks + 8 * h];
-                        const float4 x0 = *reinterpret_cast<const float4 *>(p);
-                        const float4 x1 = *reinterpret_cast<const float4 *>(p + 4);
-                        m21 = mfma(pack8(x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w),
-                                   lds8(&sm.A21t[sys][l32 * TBL + 16 * ks + 8 * h]), m21);
-                    }
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sm.TB[sys][2][acc_row(r, h) * TBL + l32] = f2bf(-m21[r]);
-                }
-                // (5) keys of chunk i + 1 into the other buffer
-                if (i + 1 < nc) HYPIC_STAGE(sm.Km[b ^ 1], kr0, kr1, kr2, kr3);
-            }
-            __syncthreads();                                        // b -> next a
         }
-#undef HYPIC_FETCH
-#undef HYPIC_FETCH_Q
-#undef HYPIC_STAGE
-        if (th == 256) a.pool_ell[rec] = bad ? nanv : (float)ell;
+#undef HYPIC_FETCH_G
     }
 }
 
