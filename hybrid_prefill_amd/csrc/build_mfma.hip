@@ -17,9 +17,9 @@
 // so each system needs three 32x32 factors per chunk.
 //
 // Work split: one 512-thread workgroup per (segment, head), two roles.
-//  * State waves 0-3 each own 64 columns of [P | S] (waves 0, 1: P; 2, 3: S)
+//  * State waves 0-3 each own 32 columns of P and the same 32 columns of S
 //    as eight fp32 32x32 accumulator tiles that stay in registers for the
-//    whole segment.  Per chunk: W = K X (and V - e^g . W for S), the two-step
+//    whole segment (so the four waves do identical work).  Per chunk: W = K X (and V - e^g . W for S), the two-step
 //    solve against the factors, and the update.
 //  * Prep waves 4-7 build the next chunk's factors meanwhile: the decay
 //    prefix, the Gram matrix and A0, A; the inverses of the 32x32 diagonal
@@ -244,23 +244,23 @@ __device__ __forceinline__ void prep_invert(Smem &sm, int sys, int blk, int pw, 
                       sg * m1.x * b1.x, sg * m1.y * b1.y, sg * m1.z * b1.z, sg * m1.w * b1.w);
         }
     }
-    // (4) -(T_22 A_21): prep waves 1 and 3 (block 1 of each system)
+    // (4) -(T_22 A_21) (prep waves 1 and 3): computed transposed, so lane j holds row j
+    //     of the product and writes four consecutive columns per store
     if (blk == 1) {
-        f32x16 m21;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) m21[r] = 0.f;
+        f32x16 mt;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const float *p = &M[l32 * AFL + 16 * ks + 8 * h];
             const float4 x0 = *reinterpret_cast<const float4 *>(p);
             const float4 x1 = *reinterpret_cast<const float4 *>(p + 4);
-            m21 = mfma(pack8(x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w),
-                       lds8(&sm.A21t[sys][l32 * TBL + 16 * ks + 8 * h]), m21);
+            mt = mfma(lds8(&sm.A21t[sys][l32 * TBL + 16 * ks + 8 * h]),
+                      pack8(x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w), ks == 0 ? f32x16{} : mt);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sm.TB[sys][2][acc_row(r, h) * TBL + l32] = f2bf(-m21[r]);
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<u32x2 *>(&sm.TB[sys][2][l32 * TBL + 8 * q + 4 * h]) =
+                u32x2{pack2(-mt[4 * q], -mt[4 * q + 1]), pack2(-mt[4 * q + 2], -mt[4 * q + 3])};
     }
-
 }
 
 // Prep wave pw = 1..3, phase a: Gram block (0,0), (1,0) or (1,1) of the chunk in
@@ -349,8 +349,8 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 
     if (w < 4) {
         // =============================== state waves ===============================
-        const bool isS = w >= 2;
-        const int cbase = 64 * (w & 1);           // first column of this wave (within P or S)
+        // column block 0: P columns 32w .. 32w + 31; column block 1: the same S columns
+        const int col = 32 * w;
         f32x16 st[2][4];                          // [column block][row block], rows swizzled
         bf16x8 wb[2][2][2];                       // W of the chunk in flight as B operands [cb][tb][half]
         {
@@ -361,8 +361,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        st[cb][mb][r] =
-                            (!isS && swz(32 * mb + acc_row(r, h)) == cbase + 32 * cb + l32) ? 1.0f : 0.0f;
+                        st[cb][mb][r] = (cb == 0 && swz(32 * mb + acc_row(r, h)) == col + l32) ? 1.0f : 0.0f;
         }
         __syncthreads();                                            // prologue: chunk 0 staged
         for (int64_t i = 0; i <= nc; ++i) {
@@ -372,50 +371,36 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
             // ---- phase a: solve and update of chunk i - 1
             if (i >= 1) {
                 const int b = (int)((i - 1) & 1);
-                const int sys = isS ? 1 : 0;
                 const int rr = swz(l32) * TBL + 8 * h;
-                f32x16 y1[2], y2[2];
+                f32x16 y1[2], y2[2];     // [column block = system]
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) { y1[cb][r] = 0.f; y2[cb][r] = 0.f; }
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const bf16x8 t11 = lds8(&sm.TB[sys][0][rr + 16 * half]);
-                    const bf16x8 t22 = lds8(&sm.TB[sys][1][rr + 16 * half]);
+                for (int half = 0; half < 2; ++half)
 #pragma unroll
                     for (int cb = 0; cb < 2; ++cb) {
-                        y1[cb] = mfma(t11, wb[cb][0][half], y1[cb]);
-                        y2[cb] = mfma(t22, wb[cb][1][half], y2[cb]);
+                        y1[cb] = mfma(lds8(&sm.TB[cb][0][rr + 16 * half]), wb[cb][0][half], half == 0 ? f32x16{} : y1[cb]);
+                        y2[cb] = mfma(lds8(&sm.TB[cb][1][rr + 16 * half]), wb[cb][1][half], half == 0 ? f32x16{} : y2[cb]);
                     }
-                }
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const bf16x8 m21 = lds8(&sm.TB[sys][2][rr + 16 * half]);
+                for (int half = 0; half < 2; ++half)
 #pragma unroll
-                    for (int cb = 0; cb < 2; ++cb) y2[cb] = mfma(m21, acc_to_b(y1[cb], half), y2[cb]);
-                }
-                if (isS) {
+                    for (int cb = 0; cb < 2; ++cb)
+                        y2[cb] = mfma(lds8(&sm.TB[cb][2][rr + 16 * half]), acc_to_b(y1[cb], half), y2[cb]);
+                {
                     const float rsc = sm.rs[b];
                     if (rsc != 1.0f) {
-                        // the pending decay sigma_c e^G is folded into the state (rare)
+                        // the pending decay sigma_c e^G is folded into the S state (rare)
 #pragma unroll
-                        for (int cb = 0; cb < 2; ++cb)
+                        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-                            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                                for (int r = 0; r < 16; ++r) st[cb][mb][r] *= rsc;
+                            for (int r = 0; r < 16; ++r) st[1][mb][r] *= rsc;
                     }
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const float4 e0 = tok4(sm.egrs[b], 0, q, h), e1 = tok4(sm.egrs[b], 1, q, h);
-#pragma unroll
-                        for (int cb = 0; cb < 2; ++cb) {
-                            y1[cb][4 * q] *= e0.x; y1[cb][4 * q + 1] *= e0.y;
-                            y1[cb][4 * q + 2] *= e0.z; y1[cb][4 * q + 3] *= e0.w;
-                            y2[cb][4 * q] *= e1.x; y2[cb][4 * q + 1] *= e1.y;
-                            y2[cb][4 * q + 2] *= e1.z; y2[cb][4 * q + 3] *= e1.w;
-                        }
+                        y1[1][4 * q] *= e0.x; y1[1][4 * q + 1] *= e0.y;
+                        y1[1][4 * q + 2] *= e0.z; y1[1][4 * q + 3] *= e0.w;
+                        y2[1][4 * q] *= e1.x; y2[1][4 * q + 1] *= e1.y;
+                        y2[1][4 * q + 2] *= e1.z; y2[1][4 * q + 3] *= e1.w;
                     }
                 }
                 // X += K^T Y (the P factors are stored negated): A operand = Kt rows (channels)
@@ -467,29 +452,22 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                             z[cb][mb] = mfma(km, sb[cb], kb == 0 ? f32x16{} : z[cb][mb]);
                     }
                 }
-                if (isS) {
-                    // W = V - e^g . (K X): scale, then add V turned around on the MFMA
+                {
+                    // S block: W = V - e^g . (K X): scale, then add V turned around on the MFMA
 #pragma unroll
                     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const float4 e4 = tok4(sm.egs[b], mb, q, h);
-#pragma unroll
-                            for (int cb = 0; cb < 2; ++cb) {
-                                z[cb][mb][4 * q] *= e4.x; z[cb][mb][4 * q + 1] *= e4.y;
-                                z[cb][mb][4 * q + 2] *= e4.z; z[cb][mb][4 * q + 3] *= e4.w;
-                            }
+                            z[1][mb][4 * q] *= e4.x; z[1][mb][4 * q + 1] *= e4.y;
+                            z[1][mb][4 * q + 2] *= e4.z; z[1][mb][4 * q + 3] *= e4.w;
                         }
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
                         const bf16x8 eye = eye_b(ks, h, l32);
 #pragma unroll
                         for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                            for (int cb = 0; cb < 2; ++cb)
-                                z[cb][mb] = mfma(
-                                    lds8(&sm.Vm[b][kmo(swz(32 * mb + l32), (cbase + 32 * cb) / 8 + 2 * ks + h)]), eye,
-                                    z[cb][mb]);
+                            z[1][mb] = mfma(lds8(&sm.Vm[b][kmo(swz(32 * mb + l32), 4 * w + 2 * ks + h)]), eye, z[1][mb]);
                     }
                 }
                 // kept across the barrier as bf16 B operands: half the registers of W
@@ -504,16 +482,17 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         }
         // ---- record: physical row p of a tile holds channel swz(p); S = sigma X
         const int h = (th & 63) >> 5, l32 = th & 31;
-        const float sfin = isS ? sm.sig_fin : 1.0f;
-        float *dst = isS ? a.pool_S + rec * D * D : a.pool_P + rec * D * D;
+        const float sfin = sm.sig_fin;
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+        for (int cb = 0; cb < 2; ++cb) {
+            float *dst = (cb == 0 ? a.pool_P : a.pool_S) + rec * D * D;
+            const float sc = cb == 0 ? 1.0f : sfin;
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    dst[(int64_t)swz(32 * mb + acc_row(r, h)) * D + cbase + 32 * cb + l32] =
-                        bad ? nanv : st[cb][mb][r] * sfin;
+                    dst[(int64_t)swz(32 * mb + acc_row(r, h)) * D + col + l32] = bad ? nanv : st[cb][mb][r] * sc;
+        }
     } else {
         // =============================== prep waves ===============================
         const int pw = w - 4;
