@@ -282,9 +282,9 @@ __device__ __forceinline__ void prep_gram(Smem &sm, int b, int pw, int l) {
     f32x16 ga0, ga1;     // even and odd k-steps: two shorter dependent chains
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
+        // both operands read unconditionally: no branch between the loads, so they batch
         const bf16x8 fa = lds8(&sm.Km[b][kmo(32 * gmb + l32, 2 * kb + h)]);
-        const bf16x8 fb =
-            gmb == gnb ? fa : lds8(&sm.Km[b][kmo(32 * gnb + l32, 2 * kb + h)]);
+        const bf16x8 fb = lds8(&sm.Km[b][kmo(32 * gnb + l32, 2 * kb + h)]);
         if (kb & 1) ga1 = mfma(fa, fb, kb == 1 ? f32x16{} : ga1);
         else ga0 = mfma(fa, fb, kb == 0 ? f32x16{} : ga0);
     }
