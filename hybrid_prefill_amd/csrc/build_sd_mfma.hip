@@ -13,25 +13,30 @@
 //     S <- e^{G} S + K^T diag(beta e^{G-g}) V            (scalar)
 //     S <- diag(e^{G}) S + (e^{G-g} . K)^T diag(beta) V  (diagonal, per key channel)
 // i.e. one 128 x 128 x 64 contraction per chunk.  The arithmetic intensity is
-// 64 FLOP/B (scalar) and 32 FLOP/B (diagonal), so the build is bound by HBM;
-// the contraction runs on bf16 MFMA so that the VALU is free for the scale
-// factors.
+// 64 FLOP/B (scalar) and 32 FLOP/B (diagonal, whose fp32 gates double the
+// bytes), so the build is bound by HBM; the contraction runs on bf16 MFMA so
+// that the VALU is free for the scale factors.
 //
-// Work split: one 256-thread workgroup per (segment, head); wave w keeps rows
-// [32w, 32w+32) of S, all 128 columns, as four fp32 32x32 accumulator tiles.
-// The contraction runs over tokens, but k and v arrive token-major, so both
-// are turned around on the MFMA itself: X . I (identity) returns X's columns in
-// the accumulator layout, which is the A layout of K^T and the B layout of
-// V^T with the same token order.  Wave w turns around its own 32 key channels
-// (A operands it keeps) and 32 value channels (B operands, shared with the
-// other waves through LDS).  The next chunk's k, v (and gates) are loaded into
-// registers while the current chunk is reduced.
+// Work split: NSPLIT 256-thread workgroups per (segment, head), workgroup q
+// keeping value columns [128 q / NSPLIT, 128 (q + 1) / NSPLIT); wave w keeps rows
+// [32w, 32w + 32) of S as fp32 32x32 accumulator tiles.  Keys and values arrive
+// token-major and are turned around on the MFMA itself: X . I returns X's
+// columns in the accumulator layout, which is the A layout of K^T and the B
+// layout of V^T with the same token order.  Every wave turns around what it
+// needs (its own 32 key channels, all of the workgroup's value columns), so
+// the waves share nothing but the staged tiles.
+//
+// Streaming: keys, values and gates go from HBM straight into LDS
+// (global_load_lds), NBUF chunks deep; one workgroup barrier per chunk.  Tail
+// rows past the segment repeat its last row and are masked at use (beta and
+// log alpha of those tokens read as 0).
 #include "hypic_internal.h"
 
 namespace hypic {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
@@ -39,53 +44,101 @@ typedef uint16_t u16;
 constexpr int CH = 64;
 constexpr int D = 128;
 constexpr int NT = 256;
-constexpr int KML = 136;   // row length (bf16) of the token-major k / v tiles
-constexpr int GL = 132;    // row length (fp32) of the token-major gate tile (diagonal)
-
-template <int FAM, int NJB>
-struct __align__(16) SdSmem {
-    u16 Km[CH * KML];
-    u16 Vm[CH * (32 * NJB + 8)];            // this workgroup's value columns, token-major
-    uint32_t vx[NJB * 4 * 64 * 4];          // V^T B fragments: [j block][k-step][lane] x 16 B
-    float gate[FAM == HYPIC_DIAGONAL ? CH * GL : 1];
-    float la[CH], beta[CH], wsc[CH];        // per-token log decay, write gate, scalar-family scale
-    float gd[D];                            // diagonal: per-channel chunk decay G_i
-    float eG;
-    int64_t t0, n;
-    int32_t slot, state;
-};
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-    const __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(u16, x) | ((uint32_t)__builtin_bit_cast(u16, y) << 16);
-}
-__device__ __forceinline__ u32x4 pack8u(const f32x16 &c, int half) {
+__device__ __forceinline__ bf16x8 pack8(const f32x16 &c, int half) {
     const int o = 8 * half;
-    return u32x4{pack2(c[o], c[o + 1]), pack2(c[o + 2], c[o + 3]), pack2(c[o + 4], c[o + 5]),
-                 pack2(c[o + 6], c[o + 7])};
+    return __builtin_convertvector((f32x8){c[o], c[o + 1], c[o + 2], c[o + 3], c[o + 4], c[o + 5], c[o + 6], c[o + 7]},
+                                   bf16x8);
 }
 __device__ __forceinline__ bf16x8 lds8(const u16 *p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
 }
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// NSPLIT workgroups share one (segment, head): workgroup q keeps the value
-// columns [128 q / NSPLIT, 128 (q+1) / NSPLIT).  They all read the keys (and
-// gates); block ids are laid out so the NSPLIT workgroups of a unit land on the
-// same XCD (consecutive block ids go to consecutive XCDs), where the repeated
-// key reads hit that XCD's L2 instead of HBM.
+// global_load_lds through non-template helpers: called directly from the kernel
+// template, the builtin's LDS-pointer argument keeps the host pass from emitting
+// the launch stubs.  Lane i of the wave lands its bytes at dst + size * i.
+__device__ __forceinline__ void gll16(const void *src, void *dst) {
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+__device__ __forceinline__ void gll4(const void *src, void *dst) { __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0); }
+
+// B operand of the identity for k-step ks (column l32, rows 16 ks + 8h + e).
+__device__ __forceinline__ bf16x8 eye_b(int ks, int h, int l32) {
+    const int d = l32 - 16 * ks - 8 * h;
+    const uint32_t one = (unsigned)d < 8u ? 0x3f80u << (16 * (d & 1)) : 0u;
+    const int wd = d >> 1;
+    const u32x4 u = {wd == 0 ? one : 0u, wd == 1 ? one : 0u, wd == 2 ? one : 0u, wd == 3 ? one : 0u};
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+#define HYPIC_DPP_ADD(X, CTRL, ROWMASK) \
+    X += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(X), CTRL, ROWMASK, 0xf, true))
+// inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then row broadcasts)
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    HYPIC_DPP_ADD(x, 0x111, 0xf);
+    HYPIC_DPP_ADD(x, 0x112, 0xf);
+    HYPIC_DPP_ADD(x, 0x114, 0xf);
+    HYPIC_DPP_ADD(x, 0x118, 0xf);
+    HYPIC_DPP_ADD(x, 0x142, 0xa);
+    HYPIC_DPP_ADD(x, 0x143, 0xc);
+    return x;
+}
+#undef HYPIC_DPP_ADD
+
+// One staged chunk.  Row r of Km holds 16 granules of 8 channels; granule g sits in
+// slot g ^ (r % 16).  Vm rows hold the workgroup's 32 NJB value columns (4 NJB
+// granules); granule g sits in slot g ^ ((r >> SH) % (4 NJB)), SH = 2, 1, 0 for
+// NJB = 1, 2, 4.  Either way the 16 rows one operand read touches hit distinct
+// bank groups, and global_load_lds can fill whole rows.
+template <bool DIAG, int NJB>
+struct __align__(16) SdBuf {
+    u16 Km[CH * D];
+    u16 Vm[CH * 32 * NJB];
+    float gate[DIAG ? CH * D : CH];      // diagonal: [token][channel]; scalar: [token]
+    float beta[CH];
+    float dummy[CH];                     // target of the loads that keep per-wave load counts equal
+};
+
+template <bool DIAG, int NJB, int NBUF>
+struct __align__(16) SdSmem {
+    SdBuf<DIAG, NJB> buf[NBUF];
+    float wsc[4][CH];                    // per wave: scalar beta e^{G-g}; diagonal beta
+    float gd[4][DIAG ? 32 : 1];          // diagonal, per wave: chunk decay G_i of its channels
+    float tot[4][2][32][DIAG ? 8 : 1];   // diagonal, per wave: token-group sums of each lane half
+    int64_t t0, n;
+    int32_t slot, state;
+};
+
+__device__ __forceinline__ int kmo(int r, int g) { return r * D + ((g ^ (r & 15)) << 3); }
+template <int NJB>
+__device__ __forceinline__ int vmo(int r, int g) {
+    constexpr int SH = NJB == 1 ? 2 : NJB == 2 ? 1 : 0;
+    return r * 32 * NJB + ((g ^ ((r >> SH) & (4 * NJB - 1))) << 3);
+}
+
 template <int FAM, int NSPLIT>
-__global__ __launch_bounds__(NT, FAM == HYPIC_DIAGONAL ? 1 : 2) void sd_build_mfma_kernel(BuildArgs a) {
-    constexpr int NJB = 4 / NSPLIT;          // 32-column value blocks per workgroup
-    constexpr int VML = 32 * NJB + 8;
-    __shared__ SdSmem<FAM, NJB> sm;
+__global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) void sd_build_mfma_kernel(BuildArgs a) {
     constexpr bool DIAG = FAM == HYPIC_DIAGONAL;
+    constexpr int NJB = 4 / NSPLIT;                    // 32-column value blocks per workgroup
+    constexpr int NBUF = DIAG ? 2 : 3;                 // chunks staged (DIAG: fp32 gates are big)
+    constexpr int DIST = NBUF - 1;                     // prefetch distance in chunks
+    // global_load_lds instructions per wave per chunk: keys, values, gates, beta (+dummy)
+    constexpr int LPW = 4 + NJB + (DIAG ? 8 : 1) + 1;
+    __shared__ SdSmem<DIAG, NJB, NBUF> sm;
 
     const int th = threadIdx.x;
-    const int w = th >> 6, l = th & 63, h = l >> 5, l32 = l & 31;
+    const int w = __builtin_amdgcn_readfirstlane(th >> 6);
+    const int l = th & 63, h = l >> 5, l32 = l & 31;
     const int b = blockIdx.x;
     const int q = (b >> 3) % NSPLIT;
     const int unit = (b / (8 * NSPLIT)) * 8 + (b & 7);
@@ -110,188 +163,228 @@ __global__ __launch_bounds__(NT, FAM == HYPIC_DIAGONAL ? 1 : 2) void sd_build_mf
     const int64_t t0 = sm.t0;
     const int64_t n = state == 2 ? 0 : sm.n;
     const int64_t slot = sm.slot;
+    const int64_t nc = (n + CH - 1) / CH;
+
+    const u16 *kh = static_cast<const u16 *>(a.k) + t0 * a.k_st + head * a.k_sh;
+    const u16 *vh = static_cast<const u16 *>(a.v) + t0 * a.v_st + head * a.v_sh + jc0;
+    const float *gh = a.log_alpha ? a.log_alpha + t0 * a.la_st + head * a.la_sh : nullptr;
+    const float *bh = a.beta ? a.beta + t0 * a.b_st + head * a.b_sh : nullptr;
+
+    // Issue this wave's share of chunk C's loads into buffer C % NBUF.  Every wave
+    // issues exactly LPW instructions (so vmcnt can count chunks).  Full chunks use
+    // per-lane element offsets fixed for the segment; the tail chunk clamps rows.
+    constexpr int GR = 4 * NJB, RPI = 64 / GR, VSH = NJB == 1 ? 2 : NJB == 2 ? 1 : 0;
+    int64_t mst = a.k_st > a.v_st ? a.k_st : a.v_st;
+    if (a.la_st > mst) mst = a.la_st;
+    if (a.b_st > mst) mst = a.b_st;
+    const bool small_st = (int64_t)CH * mst < (1LL << 30);
+    uint32_t ko[4], vo[NJB], go[DIAG ? 8 : 1], to_b, to_l;
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * (4 * w + j) + (l >> 4);
+            ko[j] = small_st ? (uint32_t)(r * a.k_st + 8 * ((l & 15) ^ (r & 15))) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < NJB; ++j) {
+            const int r = RPI * (NJB * w + j) + l / GR;
+            vo[j] = small_st ? (uint32_t)(r * a.v_st + 8 * ((l % GR) ^ ((r >> VSH) & (GR - 1)))) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < (DIAG ? 8 : 1); ++j) {
+            const int r = 2 * (8 * w + j) + (l >> 5);
+            go[j] = small_st ? (uint32_t)(r * a.la_st + 4 * (l & 31)) : 0u;
+        }
+        to_b = small_st ? (uint32_t)(l * a.b_st) : 0u;
+        to_l = small_st ? (uint32_t)(l * a.la_st) : 0u;
+    }
+#define HYPIC_SD_ISSUE(C)                                                                            \
+    do {                                                                                             \
+        const int bi_ = (int)((C) % NBUF);                                                           \
+        const int64_t base_ = (C) * CH, rem_ = n - base_;                                            \
+        if (rem_ >= CH && small_st) {                                                                \
+            const u16 *kc_ = kh + base_ * a.k_st, *vc_ = vh + base_ * a.v_st;                        \
+            _Pragma("unroll") for (int j = 0; j < 4; ++j)                                            \
+                gll16(kc_ + ko[j], &sm.buf[bi_].Km[4 * (4 * w + j) * D]);                            \
+            _Pragma("unroll") for (int j = 0; j < NJB; ++j)                                          \
+                gll16(vc_ + vo[j], &sm.buf[bi_].Vm[RPI * (NJB * w + j) * 32 * NJB]);                 \
+            if (DIAG) {                                                                              \
+                _Pragma("unroll") for (int j = 0; j < 8; ++j)                                        \
+                    gll16(gh ? gh + base_ * a.la_st + go[j] : (const float *)a.k,                    \
+                          &sm.buf[bi_].gate[2 * (8 * w + j) * D]);                                   \
+            }                                                                                        \
+            if (w == 0 && bh) gll4(bh + base_ * a.b_st + to_b, sm.buf[bi_].beta);                    \
+            else if (!DIAG && w == 1 && gh) gll4(gh + base_ * a.la_st + to_l, sm.buf[bi_].gate);     \
+            else gll4(a.k, sm.buf[bi_].dummy);                                                       \
+        } else {                                                                                     \
+            const int cl_ = rem_ < CH ? (int)rem_ : CH;                                              \
+            int ll = l;                                                                              \
+            asm volatile("" : "+v"(ll));                                                             \
+            /* keys: instruction u covers rows 4u .. 4u + 3 (lane: row 4u + ll / 16, slot ll % 16) */ \
+            _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                          \
+                const int u = 4 * w + j, r = 4 * u + (ll >> 4), rs = r < cl_ ? r : cl_ - 1;         \
+                const int g = (ll & 15) ^ (r & 15);                                                  \
+                gll16(kh + (base_ + rs) * a.k_st + 8 * g, &sm.buf[bi_].Km[4 * u * D]);               \
+            }                                                                                        \
+            /* values: GR granules per row, RPI rows per instruction */                              \
+            _Pragma("unroll") for (int j = 0; j < NJB; ++j) {                                        \
+                const int u = NJB * w + j, r = RPI * u + ll / GR, rs = r < cl_ ? r : cl_ - 1;        \
+                const int g = (ll % GR) ^ ((r >> VSH) & (GR - 1));                                   \
+                gll16(vh + (base_ + rs) * a.v_st + 8 * g, &sm.buf[bi_].Vm[RPI * u * 32 * NJB]);      \
+            }                                                                                        \
+            if (DIAG) {                                                                              \
+                /* gates: 2 rows (512 bytes each) per instruction, 8 per wave */                     \
+                _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                      \
+                    const int u = 8 * w + j, r = 2 * u + (ll >> 5), rs = r < cl_ ? r : cl_ - 1;      \
+                    gll16(gh ? gh + (base_ + rs) * a.la_st + 4 * (ll & 31) : (const float *)a.k,     \
+                          &sm.buf[bi_].gate[2 * u * D]);                                             \
+                }                                                                                    \
+            }                                                                                        \
+            /* one dword per lane: wave 0 beta, wave 1 (scalar) log alpha, the rest a dummy */       \
+            const int rs = ll < cl_ ? ll : cl_ - 1;                                                  \
+            if (w == 0 && bh) gll4(bh + (base_ + rs) * a.b_st, sm.buf[bi_].beta);                    \
+            else if (!DIAG && w == 1 && gh) gll4(gh + (base_ + rs) * a.la_st, sm.buf[bi_].gate);     \
+            else gll4(a.k, sm.buf[bi_].dummy);                                                       \
+        }                                                                                            \
+    } while (0)
 
     f32x16 st[NJB];
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[jb][r] = 0.f;
-    double ell = 0.0;   // scalar: thread 0; diagonal: lanes of half 0 keep channel 32w + l32
+    double ell = 0.0;   // scalar: wave 0, one token per lane; diagonal: this lane's tokens of channel 32w + l32
+    const bf16x8 eye0 = eye_b(0, h, l32), eye1 = eye_b(1, h, l32);
 
-    // identity B fragments: B[k][n] = 1 if 16 ks + 8h + e == n
-    bf16x8 eye[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) eye[ks][e] = (__bf16)((16 * ks + 8 * h + e == l32) ? 1.0f : 0.0f);
+    for (int64_t c = 0; c < DIST && c < nc; ++c) HYPIC_SD_ISSUE(c);
 
-    const u16 *kp = static_cast<const u16 *>(a.k);
-    const u16 *vp = static_cast<const u16 *>(a.v);
-    // per thread: 16-byte pieces p = th + 256 u (u < 4) of the 64 x 128 chunk: row p/16, channels 8 (p%16)
-    uint4 kr[4], vr[NJB];
-    float4 gr[8];
-    float br = 0.f, lr = 0.f;
+    for (int64_t c = 0; c < nc; ++c) {
+        // this wave's loads of chunk c have landed once at most the later chunks' remain
+        if (c + 1 < nc && DIST > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();                              // chunk c visible; chunk c - 1's buffer free
+        if (c + DIST < nc) HYPIC_SD_ISSUE(c + DIST);
 
-#define HYPIC_SD_FETCH(BASE)                                                                           \
-    do {                                                                                               \
-        const int64_t rem_ = n - (BASE);                                                               \
-        const int cl_ = rem_ < CH ? (int)rem_ : CH;                                                    \
-        _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                                \
-            const int p = th + NT * u, t = p >> 4, c8 = 8 * (p & 15);                                  \
-            kr[u] = t < cl_ ? *reinterpret_cast<const uint4 *>(kp + (t0 + (BASE) + t) * a.k_st +       \
-                                                                head * a.k_sh + c8)                    \
-                            : make_uint4(0, 0, 0, 0);                                                  \
-        }                                                                                              \
-        _Pragma("unroll") for (int u = 0; u < NJB; ++u) {                                              \
-            const int p = th + NT * u, t = p / (4 * NJB), c8 = 8 * (p % (4 * NJB));                    \
-            vr[u] = t < cl_ ? *reinterpret_cast<const uint4 *>(vp + (t0 + (BASE) + t) * a.v_st +       \
-                                                                head * a.v_sh + jc0 + c8)              \
-                            : make_uint4(0, 0, 0, 0);                                                  \
-        }                                                                                              \
-        if (DIAG) {                                                                                    \
-            _Pragma("unroll") for (int u = 0; u < 8; ++u) {                                            \
-                const int p = th + NT * u, t = p >> 5, c4 = 4 * (p & 31);                              \
-                gr[u] = (t < cl_ && a.log_alpha)                                                       \
-                            ? *reinterpret_cast<const float4 *>(                                      \
-                                  a.log_alpha + (t0 + (BASE) + t) * a.la_st + head * a.la_sh + c4)     \
-                            : make_float4(0.f, 0.f, 0.f, 0.f);                                         \
-            }                                                                                          \
-        }                                                                                              \
-        if (th < CH) {                                                                                 \
-            const int64_t tt = t0 + (BASE) + th;                                                       \
-            br = th < cl_ ? (a.beta ? a.beta[tt * a.b_st + head * a.b_sh] : 1.0f) : 0.0f;              \
-            lr = (!DIAG && th < cl_ && a.log_alpha) ? a.log_alpha[tt * a.la_st + head * a.la_sh] : 0.f; \
-        }                                                                                              \
-    } while (0)
+        const SdBuf<DIAG, NJB> &B = sm.buf[c % NBUF];
+        const int64_t rem = n - c * CH;
+        const int cl = rem < CH ? (int)rem : CH;
+        int thv = th;
+        asm volatile("" : "+v"(thv));
+        const int lv = thv & 63, hv = lv >> 5, lv32 = lv & 31;
 
-    if (n > 0) HYPIC_SD_FETCH(0);
-
-    for (int64_t base = 0; base < n; base += CH) {
-        // ---- stage the chunk (token-major) and the per-token gates
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int p = th + NT * u, t = p >> 4, c8 = 8 * (p & 15);
-            *reinterpret_cast<uint4 *>(&sm.Km[t * KML + c8]) = kr[u];
-        }
-#pragma unroll
-        for (int u = 0; u < NJB; ++u) {
-            const int p = th + NT * u, t = p / (4 * NJB), c8 = 8 * (p % (4 * NJB));
-            *reinterpret_cast<uint4 *>(&sm.Vm[t * VML + c8]) = vr[u];
-        }
-        if (DIAG) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int p = th + NT * u, t = p >> 5, c4 = 4 * (p & 31);
-                *reinterpret_cast<float4 *>(&sm.gate[t * GL + c4]) = gr[u];
-            }
-        }
-        if (th < CH) { sm.beta[th] = br; sm.la[th] = lr; }
-        if (base + CH < n) HYPIC_SD_FETCH(base + CH);    // next chunk flies while this one is reduced
-        __syncthreads();
-
-        // ---- scale factors
+        // ---- per-token factors (lane = token), masked past the segment
+        const float bt = lv < cl ? (a.beta ? B.beta[lv] : 1.0f) : 0.0f;
+        float kfac[2][16];                            // diagonal: e^{G_i - g_{t,i}} per key element
+        float eGv = 0.f;                              // scalar: e^G
         if (!DIAG) {
-            if (w == 0) {
-                float gv = sm.la[l];
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const float y = __shfl_up(gv, o);
-                    if (l >= o) gv += y;
-                }
-                const float G = __shfl(gv, 63);
-                sm.wsc[l] = sm.beta[l] * __expf(G - gv);
-                double sd = (double)sm.la[l];
-#pragma unroll
-                for (int o = 32; o >= 1; o >>= 1) sd += __shfl_xor(sd, o);
-                if (l == 0) { ell += sd; sm.eG = __expf(G); }
-            }
-        }
-        // ---- turn this wave's 32 key channels and 32 value channels around: X . I
-        f32x16 dk[2], dv[2];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) { dk[tb][r] = 0.f; dv[tb][r] = 0.f; }
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                dk[tb] = mfma(lds8(&sm.Km[(32 * tb + l32) * KML + 32 * w + 16 * ks + 8 * h]), eye[ks], dk[tb]);
-                if (w < NJB)
-                    dv[tb] = mfma(lds8(&sm.Vm[(32 * tb + l32) * VML + 32 * w + 16 * ks + 8 * h]), eye[ks], dv[tb]);
-            }
-        }
-        // ---- per-channel gates (diagonal): lane (l32, h) runs the cumulative sum of channel
-        //      i = 32w + l32 and keeps e^{G_i - g_{t,i}} at the 32 token positions it holds
-        float ksc[2][16];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ksc[tb][r] = 0.f;
-        if (DIAG) {
-            const int i = 32 * w + l32;
-            float run = 0.f;
-            double dsum = 0.0;
-#pragma unroll
-            for (int t = 0; t < CH; ++t) {
-                const float x = sm.gate[t * GL + i];
-                run += x;
-                dsum += (double)x;
-                // token t sits in lane half (t >> 2) & 1, tile t >> 5, register index below
-                const int rr = ((t & 31) >> 3) * 4 + (t & 3);
-                if (((t >> 2) & 1) == h) ksc[t >> 5][rr] = run;
-            }
-            const float G = run;
+            const float lat = (lv < cl && a.log_alpha) ? B.gate[lv] : 0.0f;
+            const float gv = wave_prefix_sum(lat);
+            const float G = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 63));
+            sm.wsc[w][lv] = bt * __expf(G - gv);
+            eGv = __expf(G);
+            if (w == 0) ell += (double)lat;
+        } else {
+            sm.wsc[w][lv] = bt;
+            // channel i = 32w + lv32; this lane's tokens 32 tb + 8 qq + 4 hv + e, in groups of 4
+            const int i = 32 * w + lv32;
+            float x[2][4][4], gs[2][4];
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) ksc[tb][r] = __expf(G - ksc[tb][r]);
-            if (h == 0) { sm.gd[i] = G; ell += dsum; }
+                for (int qq = 0; qq < 4; ++qq) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 32 * tb + 8 * qq + 4 * hv + e;
+                        const float v = (t < cl && a.log_alpha) ? B.gate[t * D + i] : 0.0f;
+                        ell += (double)v;
+                        s += v;
+                        x[tb][qq][e] = s;            // inclusive prefix inside the group
+                    }
+                    gs[tb][qq] = s;
+                    sm.tot[w][hv][lv32][4 * tb + qq] = s;
+                }
+            wave_lds_sync();
+            // offsets: every group before this one in token order (other half's groups interleave)
+            float run = 0.f, G = 0.f;
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const float other = sm.tot[w][hv ^ 1][lv32][4 * tb + qq];
+                    const float g0 = hv == 0 ? gs[tb][qq] : other, g1 = hv == 0 ? other : gs[tb][qq];
+                    const float off = run + (hv == 0 ? 0.f : g0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[tb][qq][e] += off;
+                    run += g0 + g1;
+                }
+            G = run;
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) kfac[tb][4 * qq + e] = __expf(G - x[tb][qq][e]);
+            if (hv == 0) sm.gd[w][lv32] = G;
         }
-        __syncthreads();   // wsc / eG / gd visible; the k, v tiles may be overwritten after the next barrier
-        // ---- scale: scalar: beta e^{G-g} on the value side; diagonal: beta on values, e^{G-g} on keys
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = 32 * tb + acc_row(r, h);
-                dv[tb][r] *= DIAG ? sm.beta[t] : sm.wsc[t];
-                if (DIAG) dk[tb][r] *= ksc[tb][r];
-            }
-        // A operands (K^T, own rows) stay in registers; B operands (V^T, own 32 value channels) go to LDS
-        bf16x8 ka[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            ka[ks] = __builtin_bit_cast(bf16x8, pack8u(dk[ks >> 1], ks & 1));
-            if (w < NJB) *reinterpret_cast<u32x4 *>(&sm.vx[((w * 4 + ks) * 64 + l) * 4]) = pack8u(dv[ks >> 1], ks & 1);
-        }
-        // decay of the carried state
+        wave_lds_sync();
+
+        // ---- decay of the carried state
         if (DIAG) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float f = __expf(sm.gd[32 * w + acc_row(r, h)]);
+            for (int qq = 0; qq < 4; ++qq) {
+                const float4 g4 = *reinterpret_cast<const float4 *>(&sm.gd[w][8 * qq + 4 * hv]);
+                const float f[4] = {__expf(g4.x), __expf(g4.y), __expf(g4.z), __expf(g4.w)};
 #pragma unroll
-                for (int jb = 0; jb < NJB; ++jb) st[jb][r] *= f;
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int jb = 0; jb < NJB; ++jb) st[jb][4 * qq + e] *= f[e];
             }
         } else {
-            const float f = sm.eG;
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) st[jb][r] *= f;
+                for (int r = 0; r < 16; ++r) st[jb][r] *= eGv;
         }
-        __syncthreads();
-        // ---- S[own rows][own columns] += K^T V over the chunk's 64 tokens
-#pragma unroll
-        for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 vb =
-                    __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&sm.vx[((jb * 4 + ks) * 64 + l) * 4]));
-                st[jb] = mfma(ka[ks], vb, st[jb]);
-            }
-        __syncthreads();   // vx and the tiles are free for the next chunk
-    }
-#undef HYPIC_SD_FETCH
 
+        // ---- K^T of this wave's 32 key channels (A operands), scaled per element for DIAG
+        bf16x8 ka[4];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            f32x16 dk;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                dk = mfma(lds8(&B.Km[kmo(32 * tb + lv32, 4 * w + 2 * ks + hv)]), ks == 0 ? eye0 : eye1,
+                          ks == 0 ? f32x16{} : dk);
+            if (DIAG) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dk[r] *= kfac[tb][r];
+            }
+            ka[2 * tb] = pack8(dk, 0);
+            ka[2 * tb + 1] = pack8(dk, 1);
+        }
+        // ---- per value block: V^T (B operands) scaled per token, then S += K^T V
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                f32x16 dv;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    dv = mfma(lds8(&B.Vm[vmo<NJB>(32 * tb + lv32, 4 * jb + 2 * ks + hv)]), ks == 0 ? eye0 : eye1,
+                              ks == 0 ? f32x16{} : dv);
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const float4 s4 = *reinterpret_cast<const float4 *>(&sm.wsc[w][32 * tb + 8 * qq + 4 * hv]);
+                    dv[4 * qq] *= s4.x; dv[4 * qq + 1] *= s4.y; dv[4 * qq + 2] *= s4.z; dv[4 * qq + 3] *= s4.w;
+                }
+#pragma unroll
+                for (int half = 0; half < 2; ++half) st[jb] = mfma(ka[2 * tb + half], pack8(dv, half), st[jb]);
+            }
+        }
+    }
+
+#undef HYPIC_SD_ISSUE
     // ---- record
     const float nanv = __int_as_float(0x7fc00000);
     const bool bad = state == 2;
@@ -304,9 +397,12 @@ __global__ __launch_bounds__(NT, FAM == HYPIC_DIAGONAL ? 1 : 2) void sd_build_mf
             dst[(int64_t)(32 * w + acc_row(r, h)) * D + jc0 + 32 * jb + l32] = bad ? nanv : st[jb][r];
     if (q != 0) return;
     if (DIAG) {
+        ell += __shfl_xor(ell, 32);        // the two lane halves hold the two token halves
         if (h == 0) a.pool_ell[rec * D + 32 * w + l32] = bad ? nanv : (float)ell;
-    } else if (th == 0) {
-        a.pool_ell[rec] = bad ? nanv : (float)ell;
+    } else if (w == 0) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ell += __shfl_xor(ell, o);
+        if (l == 0) a.pool_ell[rec] = bad ? nanv : (float)ell;
     }
 }
 
@@ -328,9 +424,10 @@ hipError_t launch_build_sd_mfma(const BuildArgs &a, hipStream_t stream, bool *ta
     // split the value columns over more workgroups while the units alone leave CUs idle;
     // the grid is padded to a multiple of 8 units (padding blocks exit at once)
     const int64_t units = (int64_t)a.num_segments * a.H;
-    // (the diagonal family re-reads its per-channel gates in every split and needs
-    // one workgroup per CU for registers, so it is not split)
-    const int nsplit = (a.family == HYPIC_DIAGONAL || units >= 1024) ? 1 : units >= 512 ? 2 : 4;
+    // (the diagonal family redoes its per-channel gate work in every split, so it
+    // stops at two)
+    const bool diag = a.family == HYPIC_DIAGONAL;
+    const int nsplit = units >= 1024 ? 1 : units >= 512 ? 2 : diag ? 2 : 4;
     const int64_t padded = (units + 7) / 8 * 8;
     const dim3 grid((unsigned)(padded * nsplit));
 #define HYPIC_SD_LAUNCH(FAM_, NS_) hipLaunchKernelGGL((sd_build_mfma_kernel<FAM_, NS_>), grid, dim3(NT), 0, stream, a)
