@@ -43,7 +43,10 @@ PEAK_FP32 = 157.3e12         # FLOP/s fp32 (matrix and vector, published)
 CHUNK = 64
 # HBM bytes per launch of the GDN build kernel, from rocprofv3 FETCH_SIZE + WRITE_SIZE
 # (scaled by the copy-kernel calibration); None until measured for the current kernel.
-TRAFFIC_GDN_BUILD = None
+# HBM bytes per launch of the GDN build on the main workload (rocprofv3 FETCH_SIZE and
+# WRITE_SIZE, each scaled by what the counter reads for a copy of known size: read
+# 606.9 MB + write 69.2 MB); None whenever the kernel changed since the counters were taken
+TRAFFIC_GDN_BUILD = 676.2e6
 
 
 def log(msg):
@@ -309,7 +312,7 @@ def bench_rag(args, R=128, pool_slots=4096, H=32, d=128, C=4096, K=4, seed=501):
                             "roofline": roofline("hbm", cbytes / (c_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s")}}}
 
 
-def cpu_baseline(seg_len=2048, H=32, d=128, nseg_sample=8, seed=301):
+def cpu_baseline(seg_len=2048, H=32, d=128, nseg_sample=16, seed=301):
     """fp64 oracle on the host: build of nseg_sample of the main workload's 16
     segments, all heads (the first nseg_sample segments' tokens, same seed)."""
     import oracle
@@ -322,7 +325,7 @@ def cpu_baseline(seg_len=2048, H=32, d=128, nseg_sample=8, seed=301):
     toks = seg_len * nseg_sample
     return {"value": toks / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"GDN build of {nseg_sample} x {seg_len}-token segment(s) x {H} heads, d={d}, "
-                      f"fp64 token-by-token recurrence ({dt:.1f} s)"}
+                      f"fp64 token-by-token recurrence ({dt:.1f} s wall on {oracle.num_threads()} threads)"}
 
 
 def main():
