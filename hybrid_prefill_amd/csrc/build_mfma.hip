@@ -23,7 +23,8 @@
 //    solve against the factors, and the update.
 //  * Prep waves 4-7 build the next chunk's factors meanwhile: the decay
 //    prefix, the Gram matrix and A0, A; the inverses of the 32x32 diagonal
-//    blocks (16x16 forward substitution, one 16 -> 32 merge on the MFMA);
+//    blocks (4x4 forward substitution and fp32 merges up to 16, one 16 -> 32
+//    merge on the MFMA);
 //    T_22 A_21; prep wave 0 also loads keys and values into LDS.  K^T is turned
 //    around by the state waves in phase b.
 // Two workgroup barriers per chunk: in phase a the state waves finish chunk
@@ -73,6 +74,7 @@ struct __align__(16) Smem {
     float Af[2][2][32 * AFL];  // per system: diagonal blocks A_11, A_22, inverted in place
     u16 A21t[2][32 * TBL];     // per system: A_21 transposed [s][t]
     float pv[4][2][CH];        // per prep wave: g, beta of the chunk being prepared
+    float inv_tmp[4][128];     // per prep wave: products inside the blocked inversion
     float egs[2][CH];          // -e^{g_t} sigma_c: the K X factor of W (S columns)
     float egrs[2][CH];         // e^{G - g_t} / sigma_{c+1}: the update factor (S columns)
     float rs[2];               // sigma_c e^G when the scale is folded back into the state, else 1
@@ -174,38 +176,68 @@ __device__ __forceinline__ float4 tok4(const float *v, int mb, int q, int h) {
 __device__ __forceinline__ void prep_invert(Smem &sm, int sys, int blk, int pw, int l) {
     const int h = l >> 5, l32 = l & 31;
     float *M = sm.Af[sys][blk];
-    // (1) 16x16 diagonal blocks by forward substitution: lanes 0-15 rows 0-15,
-    //     lanes 16-31 rows 16-31; lane = column
+    // (1) the two 16x16 diagonal inverses, blocked: 4x4 diagonal blocks by forward
+    //     substitution, then the merges 4 -> 8 and 8 -> 16, each
+    //     T_10 = -T_11 (A_10 T_00) in two data-parallel fp32 steps through LDS, all
+    //     inside this wave (no workgroup barrier)
+    float *tmp = sm.inv_tmp[pw];
     if (l < 32) {
-        const int R = 16 * (l >> 4), j = l & 15;
-        // the strictly lower rows of this 16x16 block, loaded up front (36 x 16 bytes)
-        float4 mr[36];
+        // level 0: 4x4 block o = 16 (l / 16) + 4 ((l / 4) % 4), column j = l % 4
+        const int o = 16 * (l >> 4) + 4 * ((l >> 2) & 3), j = l & 3;
+        const float n10 = M[(o + 1) * AFL + o];
+        const float n20 = M[(o + 2) * AFL + o], n21 = M[(o + 2) * AFL + o + 1];
+        const float n30 = M[(o + 3) * AFL + o], n31 = M[(o + 3) * AFL + o + 1], n32 = M[(o + 3) * AFL + o + 2];
+        const float x0 = j == 0 ? 1.f : 0.f;
+        const float x1 = (j == 1 ? 1.f : 0.f) - n10 * x0;
+        const float x2 = (j == 2 ? 1.f : 0.f) - n20 * x0 - n21 * x1;
+        const float x3 = (j == 3 ? 1.f : 0.f) - n30 * x0 - n31 * x1 - n32 * x2;
+        M[o * AFL + o + j] = x0;
+        M[(o + 1) * AFL + o + j] = x1;
+        M[(o + 2) * AFL + o + j] = x2;
+        M[(o + 3) * AFL + o + j] = x3;
+    }
+    wave_lds_sync();
+    {
+        // level 1 (4 -> 8): merge m = l / 16 at o = 16 (m / 2) + 8 (m % 2); output (i, j) of
+        // the 4x4 block T_10 at rows o + 4 + i, columns o + j
+        const int m = l >> 4, o = 16 * (m >> 1) + 8 * (m & 1), i = (l >> 2) & 3, j = l & 3;
+        const float4 n = *reinterpret_cast<const float4 *>(&M[(o + 4 + i) * AFL + o]);
+        const float t = n.x * M[o * AFL + o + j] + n.y * M[(o + 1) * AFL + o + j] + n.z * M[(o + 2) * AFL + o + j] +
+                        n.w * M[(o + 3) * AFL + o + j];
+        tmp[16 * m + 4 * i + j] = t;
+        wave_lds_sync();
+        const float4 t11 = *reinterpret_cast<const float4 *>(&M[(o + 4 + i) * AFL + o + 4]);
+        M[(o + 4 + i) * AFL + o + j] = -(t11.x * tmp[16 * m + j] + t11.y * tmp[16 * m + 4 + j] +
+                                         t11.z * tmp[16 * m + 8 + j] + t11.w * tmp[16 * m + 12 + j]);
+    }
+    wave_lds_sync();
+    {
+        // level 2 (8 -> 16): merge m = l / 32 at R = 16 m; lane outputs (i, j), (i, j + 1)
+        // of the 8x8 block T_10 at rows R + 8 + i, columns R + j
+        const int m = l >> 5, R = 16 * m, i = (l & 31) >> 2, j = 2 * (l & 3);
+        const float4 na = *reinterpret_cast<const float4 *>(&M[(R + 8 + i) * AFL + R]);
+        const float4 nb = *reinterpret_cast<const float4 *>(&M[(R + 8 + i) * AFL + R + 4]);
+        const float nv[8] = {na.x, na.y, na.z, na.w, nb.x, nb.y, nb.z, nb.w};
+        float t0 = 0.f, t1 = 0.f;
 #pragma unroll
-        for (int ii = 1, c = 0; ii < 16; ++ii)
-#pragma unroll
-            for (int q = 0; 4 * q < ii; ++q, ++c)
-                mr[c] = *reinterpret_cast<const float4 *>(&M[(R + ii) * AFL + R + 4 * q]);
-        // right-looking: once x_s is final, every later row takes its term at once,
-        // so the dependent chain is one FMA per step
-        float x[16], acc[16];
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) acc[ii] = 0.f;
-#pragma unroll
-        for (int sc = 0; sc < 16; ++sc) {
-            x[sc] = (sc == j) ? 1.0f : (sc < j ? 0.0f : -acc[sc]);
-#pragma unroll
-            for (int ii = sc + 1; ii < 16; ++ii) {
-                // M[ii][sc] sits in row ii's float4 number sc / 4
-                int c = 0;
-#pragma unroll
-                for (int i2 = 1; i2 < ii; ++i2) c += (i2 + 3) / 4;
-                const float4 m = mr[c + sc / 4];
-                const float mv = (sc & 3) == 0 ? m.x : (sc & 3) == 1 ? m.y : (sc & 3) == 2 ? m.z : m.w;
-                acc[ii] += mv * x[sc];
-            }
+        for (int k = 0; k < 8; ++k) {
+            const float2 tk = *reinterpret_cast<const float2 *>(&M[(R + k) * AFL + R + j]);
+            t0 += nv[k] * tk.x;
+            t1 += nv[k] * tk.y;
         }
+        *reinterpret_cast<float2 *>(&tmp[64 * m + 8 * i + j]) = make_float2(t0, t1);
+        wave_lds_sync();
+        const float4 ta = *reinterpret_cast<const float4 *>(&M[(R + 8 + i) * AFL + R + 8]);
+        const float4 tb = *reinterpret_cast<const float4 *>(&M[(R + 8 + i) * AFL + R + 12]);
+        const float tv[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+        float u0 = 0.f, u1 = 0.f;
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) M[(R + ii) * AFL + R + j] = x[ii];
+        for (int k = 0; k < 8; ++k) {
+            const float2 c = *reinterpret_cast<const float2 *>(&tmp[64 * m + 8 * k + j]);
+            u0 += tv[k] * c.x;
+            u1 += tv[k] * c.y;
+        }
+        *reinterpret_cast<float2 *>(&M[(R + 8 + i) * AFL + R + j]) = make_float2(-u0, -u1);
     }
     wave_lds_sync();
     // (2) T_10 = -T_11 (A_10 T_00) on the 16x16x16 MFMA (lane: column l%16,
