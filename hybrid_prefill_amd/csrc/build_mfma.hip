@@ -12,21 +12,23 @@
 //   P columns X:  Y = (I + A0)^{-1} (beta . (K X));                X <- X - K^T Y
 //   S columns X:  Y = (I + A )^{-1} (beta . (V - e^g . (K X)));    X <- e^G X + K^T (e^{G-g} . Y)
 // The P update uses the ungated system, so no decay factor can overflow it.
-// With 32-token blocks and T_ii = (I + A_ii)^{-1}, writing R = beta . W,
-//     Y_1 = (T_11 diag beta_1) W_1,    Y_2 = (T_22 diag beta_2) W_2 - (T_22 A_21) Y_1,
-// so each system needs three 32x32 factors per chunk.
+// With 32-token blocks, T_ii = (I + A_ii)^{-1} and A = diag(beta) H (H: the
+// block of k_t.k_s, with e^{g_t - g_s} for S, without beta),
+//     Y_1 = (T_11 diag beta_1) W_1,    Y_2 = (T_22 diag beta_2) (W_2 - H_21 Y_1),
+// so each system needs two 32x32 inverse factors and H_21 per chunk.
 //
 // Work split: one 512-thread workgroup per (segment, head), two roles.
 //  * State waves 0-3 each own 32 columns of P and the same 32 columns of S
 //    as eight fp32 32x32 accumulator tiles that stay in registers for the
-//    whole segment (so the four waves do identical work).  Per chunk: W = K X (and V - e^g . W for S), the two-step
-//    solve against the factors, and the update.
+//    whole segment (so the four waves do identical work).  Per chunk: W = K X
+//    (and V - e^g . W for S), the block solve against the factors (three
+//    dependent products), and the update.
 //  * Prep waves 4-7 build the next chunk's factors meanwhile: the decay
-//    prefix, the Gram matrix and A0, A; the inverses of the 32x32 diagonal
-//    blocks (4x4 forward substitution and fp32 merges up to 16, one 16 -> 32
-//    merge on the MFMA);
-//    T_22 A_21; prep wave 0 also loads keys and values into LDS.  K^T is turned
-//    around by the state waves in phase b.
+//    prefix, the Gram blocks (A11, A22 in fp32, H_21 in bf16); the inverses
+//    of the 32x32 diagonal blocks (4x4 forward substitution and fp32 merges
+//    up to 16, one 16 -> 32 merge on the MFMA), written as T diag(beta) in
+//    bf16 by each level as it finishes; prep wave 0 also loads keys and
+//    values into LDS.  K^T is turned around by the state waves in phase b.
 // Two workgroup barriers per chunk: in phase a the state waves finish chunk
 // c - 1 (solve, update) while the prep waves compute A of chunk c; in phase b
 // the state waves form W of chunk c while the prep waves invert.
@@ -70,9 +72,9 @@ struct __align__(16) Smem {
     u16 Km[2][CH * KML];       // keys, token-major, double-buffered by chunk parity
     u16 Vm[2][CH * KML];       // values, token-major, double-buffered by chunk parity
     u16 Kt[D * KTL];           // keys, channel-major
-    u16 TB[2][3][32 * TBL];    // per system: T_11 diag(beta_1), T_22 diag(beta_2), -(T_22 A_21)
+    u16 TB[2][2][32 * TBL];    // per system: T_11 diag(beta_1), T_22 diag(beta_2) (negated for P)
+    u16 H21[2][2][32 * TBL];   // [chunk parity][system]: H_21 (P), -H_21 (S), row t, column s
     float Af[2][2][32 * AFL];  // per system: diagonal blocks A_11, A_22, inverted in place
-    u16 A21t[2][32 * TBL];     // per system: A_21 transposed [s][t]
     float pv[4][2][CH];        // per prep wave: g, beta of the chunk being prepared
     float inv_tmp[4][128];     // per prep wave: products inside the blocked inversion
     float egs[2][CH];          // -e^{g_t} sigma_c: the K X factor of W (S columns)
@@ -169,24 +171,28 @@ __device__ __forceinline__ float4 tok4(const float *v, int mb, int q, int h) {
     return *reinterpret_cast<const float4 *>(v + 32 * mb + 16 * (q >> 1) + 8 * h + 4 * (q & 1));
 }
 
-// Prep wave pw, phase b: the factors of 32x32 diagonal block `blk` of system `sys`
-// (0: A0, for P; 1: A, for S) from its A block in Af: the inverse T by 16x16
-// forward substitution and one merge, T diag(beta) into TB (negated for P), and
-// for blk 1 also -(T_22 A_21).
+// Prep wave pw, phase b: the inverse factor of 32x32 diagonal block `blk` of
+// system `sys` (0: A0, for P; 1: A, for S) from its A block in Af.  The fp32
+// inverse T is built in place in Af (4x4 forward substitution, merges to 8 and
+// 16 in fp32, the merge to 32 on the MFMA); each level also writes its part of
+// T diag(beta) into TB in bf16 (negated for P).  TB's upper triangle is zeroed
+// once per segment and never written here.
 __device__ __forceinline__ void prep_invert(Smem &sm, int sys, int blk, int pw, int l) {
-    const int h = l >> 5, l32 = l & 31;
     float *M = sm.Af[sys][blk];
-    // (1) the two 16x16 diagonal inverses, blocked: 4x4 diagonal blocks by forward
-    //     substitution, then the merges 4 -> 8 and 8 -> 16, each
-    //     T_10 = -T_11 (A_10 T_00) in two data-parallel fp32 steps through LDS, all
-    //     inside this wave (no workgroup barrier)
     float *tmp = sm.inv_tmp[pw];
+    u16 *TBp = sm.TB[sys][blk];
+    const float *bet = &sm.pv[pw][1][32 * blk];
+    const float sg = sys == 0 ? -1.0f : 1.0f;     // P factors negated
+    // (1) the two 16x16 diagonal inverses: each merge is T_10 = -T_11 (A_10 T_00)
+    //     in two data-parallel fp32 steps through LDS, inside this wave (no
+    //     workgroup barrier)
     if (l < 32) {
         // level 0: 4x4 block o = 16 (l / 16) + 4 ((l / 4) % 4), column j = l % 4
         const int o = 16 * (l >> 4) + 4 * ((l >> 2) & 3), j = l & 3;
         const float n10 = M[(o + 1) * AFL + o];
         const float n20 = M[(o + 2) * AFL + o], n21 = M[(o + 2) * AFL + o + 1];
         const float n30 = M[(o + 3) * AFL + o], n31 = M[(o + 3) * AFL + o + 1], n32 = M[(o + 3) * AFL + o + 2];
+        const float bc = sg * bet[o + j];
         const float x0 = j == 0 ? 1.f : 0.f;
         const float x1 = (j == 1 ? 1.f : 0.f) - n10 * x0;
         const float x2 = (j == 2 ? 1.f : 0.f) - n20 * x0 - n21 * x1;
@@ -195,6 +201,10 @@ __device__ __forceinline__ void prep_invert(Smem &sm, int sys, int blk, int pw, 
         M[(o + 1) * AFL + o + j] = x1;
         M[(o + 2) * AFL + o + j] = x2;
         M[(o + 3) * AFL + o + j] = x3;
+        TBp[o * TBL + o + j] = f2bf(x0 * bc);
+        TBp[(o + 1) * TBL + o + j] = f2bf(x1 * bc);
+        TBp[(o + 2) * TBL + o + j] = f2bf(x2 * bc);
+        TBp[(o + 3) * TBL + o + j] = f2bf(x3 * bc);
     }
     wave_lds_sync();
     {
@@ -207,8 +217,10 @@ __device__ __forceinline__ void prep_invert(Smem &sm, int sys, int blk, int pw, 
         tmp[16 * m + 4 * i + j] = t;
         wave_lds_sync();
         const float4 t11 = *reinterpret_cast<const float4 *>(&M[(o + 4 + i) * AFL + o + 4]);
-        M[(o + 4 + i) * AFL + o + j] = -(t11.x * tmp[16 * m + j] + t11.y * tmp[16 * m + 4 + j] +
-                                         t11.z * tmp[16 * m + 8 + j] + t11.w * tmp[16 * m + 12 + j]);
+        const float x = -(t11.x * tmp[16 * m + j] + t11.y * tmp[16 * m + 4 + j] + t11.z * tmp[16 * m + 8 + j] +
+                          t11.w * tmp[16 * m + 12 + j]);
+        M[(o + 4 + i) * AFL + o + j] = x;
+        TBp[(o + 4 + i) * TBL + o + j] = f2bf(x * sg * bet[o + j]);
     }
     wave_lds_sync();
     {
@@ -238,114 +250,84 @@ __device__ __forceinline__ void prep_invert(Smem &sm, int sys, int blk, int pw, 
             u1 += tv[k] * c.y;
         }
         *reinterpret_cast<float2 *>(&M[(R + 8 + i) * AFL + R + j]) = make_float2(-u0, -u1);
+        const float2 bj = *reinterpret_cast<const float2 *>(&bet[R + j]);
+        *reinterpret_cast<uint32_t *>(&TBp[(R + 8 + i) * TBL + R + j]) =
+            pack2(-u0 * sg * bj.x, -u1 * sg * bj.y);
     }
     wave_lds_sync();
     // (2) T_10 = -T_11 (A_10 T_00) on the 16x16x16 MFMA (lane: column l%16,
-    //     contraction / rows 4 (l/16) + 0..3)
+    //     contraction / rows 4 (l/16) + 0..3); only the bf16 TB copy is needed after it
     {
         const int c16 = l & 15, k4 = 4 * (l >> 4);
         const float4 a10 = *reinterpret_cast<const float4 *>(&M[(16 + c16) * AFL + k4]);
         const s16x4 fa = pack4(a10.x, a10.y, a10.z, a10.w);
         const s16x4 fb = pack4(M[(k4 + 0) * AFL + c16], M[(k4 + 1) * AFL + c16], M[(k4 + 2) * AFL + c16],
                                M[(k4 + 3) * AFL + c16]);
-        f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
-        tmp = mfma16(fa, fb, tmp);
+        f32x4 tmp4 = {0.f, 0.f, 0.f, 0.f};
+        tmp4 = mfma16(fa, fb, tmp4);
         const float4 t11 = *reinterpret_cast<const float4 *>(&M[(16 + c16) * AFL + 16 + k4]);
         const s16x4 fa2 = pack4(-t11.x, -t11.y, -t11.z, -t11.w);
-        const s16x4 fb2 = pack4(tmp[0], tmp[1], tmp[2], tmp[3]);
+        const s16x4 fb2 = pack4(tmp4[0], tmp4[1], tmp4[2], tmp4[3]);
         f32x4 t10 = {0.f, 0.f, 0.f, 0.f};
         t10 = mfma16(fa2, fb2, t10);
+        const float bc = sg * bet[c16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) M[(16 + k4 + r) * AFL + c16] = t10[r];
-    }
-    wave_lds_sync();
-    // (3) T diag(beta) of this block, bf16; lane = column, 16 rows per lane half
-    {
-        // lane: row l / 2, columns 16 (l % 2) .. +15
-        const int row = l >> 1, c0 = 16 * (l & 1);
-        const float sg = sys == 0 ? -1.0f : 1.0f;     // P factors negated
-        u16 *dst = &sm.TB[sys][blk][row * TBL + c0];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const float4 m0 = *reinterpret_cast<const float4 *>(&M[row * AFL + c0 + 8 * u]);
-            const float4 m1 = *reinterpret_cast<const float4 *>(&M[row * AFL + c0 + 8 * u + 4]);
-            const float4 b0 = *reinterpret_cast<const float4 *>(&sm.pv[pw][1][32 * blk + c0 + 8 * u]);
-            const float4 b1 = *reinterpret_cast<const float4 *>(&sm.pv[pw][1][32 * blk + c0 + 8 * u + 4]);
-            *reinterpret_cast<bf16x8 *>(dst + 8 * u) =
-                pack8(sg * m0.x * b0.x, sg * m0.y * b0.y, sg * m0.z * b0.z, sg * m0.w * b0.w,
-                      sg * m1.x * b1.x, sg * m1.y * b1.y, sg * m1.z * b1.z, sg * m1.w * b1.w);
-        }
-    }
-    // (4) -(T_22 A_21) (prep waves 1 and 3): computed transposed, so lane j holds row j
-    //     of the product and writes four consecutive columns per store
-    if (blk == 1) {
-        f32x16 mt;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const float *p = &M[l32 * AFL + 16 * ks + 8 * h];
-            const float4 x0 = *reinterpret_cast<const float4 *>(p);
-            const float4 x1 = *reinterpret_cast<const float4 *>(p + 4);
-            mt = mfma(lds8(&sm.A21t[sys][l32 * TBL + 16 * ks + 8 * h]),
-                      pack8(x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w), ks == 0 ? f32x16{} : mt);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<u32x2 *>(&sm.TB[sys][2][l32 * TBL + 8 * q + 4 * h]) =
-                u32x2{pack2(-mt[4 * q], -mt[4 * q + 1]), pack2(-mt[4 * q + 2], -mt[4 * q + 3])};
+        for (int r = 0; r < 4; ++r) TBp[(16 + k4 + r) * TBL + c16] = f2bf(t10[r] * bc);
     }
 }
 
-// Prep wave pw = 1..3, phase a: Gram block (0,0), (1,0) or (1,1) of the chunk in
-// Km[b] on the MFMA, then A0 = beta_t k_t.k_s and A = A0 e^{g_t - g_s} below the
-// diagonal: diagonal blocks into Af (fp32), block (1,0) transposed into A21t (bf16).
-// pv[pw] holds this wave's g and beta.
+// Prep wave pw = 1..3, phase a: Gram block of the chunk in Km[b] on the MFMA with
+// the A operand from token block am and the B operand from token block bn, so
+// lane l32 holds row t = 32 bn + l32 and registers hold columns s (k_t.k_s is
+// symmetric, so the diagonal blocks read either way):
+//   prep wave 1: (0,0) -> A0_11, A_11 into Af (fp32), below the diagonal
+//   prep wave 2: (0,1) -> H_21 into H21[b] (bf16): k_t.k_s for P, -k_t.k_s e^{g_t - g_s} for S
+//   prep wave 3: (1,1) -> A0_22, A_22 into Af (fp32), below the diagonal
+// with A0 = beta_t k_t.k_s and A = A0 e^{g_t - g_s}.  pv[pw] holds this wave's g, beta.
 __device__ __forceinline__ void prep_gram(Smem &sm, int b, int pw, int l) {
     const int h = l >> 5, l32 = l & 31;
-    // Gram block (gmb, gnb): (0,0) for prep wave 1, (1,0) for 2, (1,1) for 3
-    const int gmb = pw >= 2 ? 1 : 0, gnb = pw == 3 ? 1 : 0;
-    const int s = 32 * gnb + l32;
-    const float gs = sm.pv[pw][0][s];
-    float4 bqv[4], gqv[4];
+    const int am = pw == 3 ? 1 : 0, bn = pw == 1 ? 0 : 1;
+    const int t = 32 * bn + l32;
+    const float gt = sm.pv[pw][0][t], bt = sm.pv[pw][1][t];
+    float4 gqv[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        bqv[q] = *reinterpret_cast<const float4 *>(&sm.pv[pw][1][32 * gmb + 8 * q + 4 * h]);
-        gqv[q] = *reinterpret_cast<const float4 *>(&sm.pv[pw][0][32 * gmb + 8 * q + 4 * h]);
-    }
+    for (int q = 0; q < 4; ++q) gqv[q] = *reinterpret_cast<const float4 *>(&sm.pv[pw][0][32 * am + 8 * q + 4 * h]);
     f32x16 ga0, ga1;     // even and odd k-steps: two shorter dependent chains
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
         // both operands read unconditionally: no branch between the loads, so they batch
-        const bf16x8 fa = lds8(&sm.Km[b][kmo(32 * gmb + l32, 2 * kb + h)]);
-        const bf16x8 fb = lds8(&sm.Km[b][kmo(32 * gnb + l32, 2 * kb + h)]);
+        const bf16x8 fa = lds8(&sm.Km[b][kmo(32 * am + l32, 2 * kb + h)]);
+        const bf16x8 fb = lds8(&sm.Km[b][kmo(32 * bn + l32, 2 * kb + h)]);
         if (kb & 1) ga1 = mfma(fa, fb, kb == 1 ? f32x16{} : ga1);
         else ga0 = mfma(fa, fb, kb == 0 ? f32x16{} : ga0);
     }
     const f32x16 gacc = ga0 + ga1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int t4 = 32 * gmb + 8 * q + 4 * h;
-        const float4 bq4 = bqv[q], gq4 = gqv[q];
-        const float bb[4] = {bq4.x, bq4.y, bq4.z, bq4.w}, ggv[4] = {gq4.x, gq4.y, gq4.z, gq4.w};
+        const int s4 = 8 * q + 4 * h;     // column within the block
+        const float4 gq4 = gqv[q];
+        const float ggv[4] = {gq4.x, gq4.y, gq4.z, gq4.w};
         float a0[4], a1[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bool low = s < t4 + e;
-            const float v0 = bb[e] * gacc[4 * q + e];
-            a0[e] = low ? v0 : 0.f;
-            a1[e] = low ? v0 * __expf(ggv[e] - gs) : 0.f;
-        }
         if (pw == 2) {
-            // A_21 transposed: row s, tokens t4 - 32 .. +3
-            const int o = l32 * TBL + t4 - 32;
-            *reinterpret_cast<u32x2 *>(&sm.A21t[0][o]) = u32x2{pack2(a0[0], a0[1]), pack2(a0[2], a0[3])};
-            *reinterpret_cast<u32x2 *>(&sm.A21t[1][o]) = u32x2{pack2(a1[0], a1[1]), pack2(a1[2], a1[3])};
-        } else {
-            float *A0 = sm.Af[0][gmb], *A1 = sm.Af[1][gmb];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                A0[(t4 - 32 * gmb + e) * AFL + l32] = a0[e];
-                A1[(t4 - 32 * gmb + e) * AFL + l32] = a1[e];
+                a0[e] = gacc[4 * q + e];
+                a1[e] = -a0[e] * __expf(gt - ggv[e]);
             }
+            const int o = l32 * TBL + s4;
+            *reinterpret_cast<u32x2 *>(&sm.H21[b][0][o]) = u32x2{pack2(a0[0], a0[1]), pack2(a0[2], a0[3])};
+            *reinterpret_cast<u32x2 *>(&sm.H21[b][1][o]) = u32x2{pack2(a1[0], a1[1]), pack2(a1[2], a1[3])};
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool low = s4 + e < l32;
+                const float v0 = bt * gacc[4 * q + e];
+                a0[e] = low ? v0 : 0.f;
+                a1[e] = low ? v0 * __expf(gt - ggv[e]) : 0.f;
+            }
+            const int o = l32 * AFL + s4;
+            *reinterpret_cast<float4 *>(&sm.Af[0][am][o]) = make_float4(a0[0], a0[1], a0[2], a0[3]);
+            *reinterpret_cast<float4 *>(&sm.Af[1][am][o]) = make_float4(a1[0], a1[1], a1[2], a1[3]);
         }
     }
 }
@@ -368,6 +350,8 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         if (st == 2) raise_flag(a.err_flag, HYPIC_EFLAG_BAD_OFFSETS);
         sm.t0 = o0; sm.n = o1 - o0; sm.slot = slot; sm.state = st;
     }
+    // the upper triangles of the T diag(beta) tiles stay zero for the whole segment
+    for (int e = th; e < (int)(sizeof(sm.TB) / 16); e += NT) reinterpret_cast<u32x4 *>(&sm.TB[0][0][0])[e] = u32x4{};
     __syncthreads();
     const int state = sm.state;
     if (state == 1) return;
@@ -408,15 +392,28 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 #pragma unroll
                 for (int half = 0; half < 2; ++half)
 #pragma unroll
-                    for (int cb = 0; cb < 2; ++cb) {
+                    for (int cb = 0; cb < 2; ++cb)
                         y1[cb] = mfma(lds8(&sm.TB[cb][0][rr + 16 * half]), wb[cb][0][half], half == 0 ? f32x16{} : y1[cb]);
-                        y2[cb] = mfma(lds8(&sm.TB[cb][1][rr + 16 * half]), wb[cb][1][half], half == 0 ? f32x16{} : y2[cb]);
-                    }
+                // W_2 - H_21 Y_1 (H21 carries the sign that makes this a sum for both
+                // systems; P's factors and Y are negated), accumulated onto W_2 itself: a
+                // B operand pack holds the registers of its accumulator in order
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    const f32x8 w0 = __builtin_convertvector(wb[cb][1][0], f32x8);
+                    const f32x8 w1 = __builtin_convertvector(wb[cb][1][1], f32x8);
+                    y2[cb] = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+                }
 #pragma unroll
                 for (int half = 0; half < 2; ++half)
 #pragma unroll
                     for (int cb = 0; cb < 2; ++cb)
-                        y2[cb] = mfma(lds8(&sm.TB[cb][2][rr + 16 * half]), acc_to_b(y1[cb], half), y2[cb]);
+                        y2[cb] = mfma(lds8(&sm.H21[b][cb][rr + 16 * half]), acc_to_b(y1[cb], half), y2[cb]);
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    const bf16x8 u0 = acc_to_b(y2[cb], 0), u1 = acc_to_b(y2[cb], 1);
+                    y2[cb] = mfma(lds8(&sm.TB[cb][1][rr]), u0, f32x16{});
+                    y2[cb] = mfma(lds8(&sm.TB[cb][1][rr + 16]), u1, y2[cb]);
+                }
                 {
                     const float rsc = sm.rs[b];
                     if (rsc != 1.0f) {
