@@ -524,6 +524,9 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         }
     } else {
         // =============================== prep waves ===============================
+        // Their work is a chain of short dependent steps that shares each SIMD with a
+        // state wave's long MFMA stream: issue priority keeps the chain moving.
+        __builtin_amdgcn_s_setprio(3);
         const int pw = w - 4;
         const int pl = th & 63;
         // every prep wave loads la and beta of a chunk itself (lane = token)
