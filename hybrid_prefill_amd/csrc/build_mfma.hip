@@ -292,14 +292,18 @@ __device__ __forceinline__ void prep_gram(Smem &sm, int b, int pw, int l) {
     float4 gqv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) gqv[q] = *reinterpret_cast<const float4 *>(&sm.pv[pw][0][32 * am + 8 * q + 4 * h]);
+    // every operand read is issued before the first product, so the reads overlap
+    bf16x8 fa[8], fb[8];
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        fa[kb] = lds8(&sm.Km[b][kmo(32 * am + l32, 2 * kb + h)]);
+        fb[kb] = lds8(&sm.Km[b][kmo(32 * bn + l32, 2 * kb + h)]);
+    }
     f32x16 ga0, ga1;     // even and odd k-steps: two shorter dependent chains
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-        // both operands read unconditionally: no branch between the loads, so they batch
-        const bf16x8 fa = lds8(&sm.Km[b][kmo(32 * am + l32, 2 * kb + h)]);
-        const bf16x8 fb = lds8(&sm.Km[b][kmo(32 * bn + l32, 2 * kb + h)]);
-        if (kb & 1) ga1 = mfma(fa, fb, kb == 1 ? f32x16{} : ga1);
-        else ga0 = mfma(fa, fb, kb == 0 ? f32x16{} : ga0);
+        if (kb & 1) ga1 = mfma(fa[kb], fb[kb], kb == 1 ? f32x16{} : ga1);
+        else ga0 = mfma(fa[kb], fb[kb], kb == 0 ? f32x16{} : ga0);
     }
     const f32x16 gacc = ga0 + ga1;
 #pragma unroll
@@ -388,32 +392,6 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
             if (i >= 1) {
                 const int b = (int)((i - 1) & 1);
                 const int rr = swz(l32) * TBL + 8 * h;
-                f32x16 y1[2], y2[2];     // [column block = system]
-#pragma unroll
-                for (int half = 0; half < 2; ++half)
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb)
-                        y1[cb] = mfma(lds8(&sm.TB[cb][0][rr + 16 * half]), wb[cb][0][half], half == 0 ? f32x16{} : y1[cb]);
-                // W_2 - H_21 Y_1 (H21 carries the sign that makes this a sum for both
-                // systems; P's factors and Y are negated), accumulated onto W_2 itself: a
-                // B operand pack holds the registers of its accumulator in order
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    const f32x8 w0 = __builtin_convertvector(wb[cb][1][0], f32x8);
-                    const f32x8 w1 = __builtin_convertvector(wb[cb][1][1], f32x8);
-                    y2[cb] = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-                }
-#pragma unroll
-                for (int half = 0; half < 2; ++half)
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb)
-                        y2[cb] = mfma(lds8(&sm.H21[b][cb][rr + 16 * half]), acc_to_b(y1[cb], half), y2[cb]);
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    const bf16x8 u0 = acc_to_b(y2[cb], 0), u1 = acc_to_b(y2[cb], 1);
-                    y2[cb] = mfma(lds8(&sm.TB[cb][1][rr]), u0, f32x16{});
-                    y2[cb] = mfma(lds8(&sm.TB[cb][1][rr + 16]), u1, y2[cb]);
-                }
                 {
                     const float rsc = sm.rs[b];
                     if (rsc != 1.0f) {
@@ -423,28 +401,89 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 #pragma unroll
                             for (int r = 0; r < 16; ++r) st[1][mb][r] *= rsc;
                     }
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float4 e0 = tok4(sm.egrs[b], 0, q, h), e1 = tok4(sm.egrs[b], 1, q, h);
-                        y1[1][4 * q] *= e0.x; y1[1][4 * q + 1] *= e0.y;
-                        y1[1][4 * q + 2] *= e0.z; y1[1][4 * q + 3] *= e0.w;
-                        y2[1][4 * q] *= e1.x; y2[1][4 * q + 1] *= e1.y;
-                        y2[1][4 * q + 2] *= e1.z; y2[1][4 * q + 3] *= e1.w;
-                    }
                 }
-                // X += K^T Y (the P factors are stored negated): A operand = Kt rows (channels)
-                // swz(32 mb + lane)
+                // factor operands [system][k-step]: T_11 diag b_1 and H_21 read up front
+                bf16x8 f0[2][2], fh[2][2], f1[2][2];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    bf16x8 yb[2];
+                for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-                    for (int cb = 0; cb < 2; ++cb) yb[cb] = acc_to_b(s < 2 ? y1[cb] : y2[cb], s & 1);
-#pragma unroll
-                    for (int mb = 0; mb < 4; ++mb) {
-                        const bf16x8 kt = lds8(&sm.Kt[swz(32 * mb + l32) * KTL + 16 * s + 8 * h]);
-#pragma unroll
-                        for (int cb = 0; cb < 2; ++cb) st[cb][mb] = mfma(kt, yb[cb], st[cb][mb]);
+                    for (int half = 0; half < 2; ++half) {
+                        f0[cb][half] = lds8(&sm.TB[cb][0][rr + 16 * half]);
+                        fh[cb][half] = lds8(&sm.H21[b][cb][rr + 16 * half]);
                     }
+                f32x16 y1[2], y2[2];     // [column block = system]
+                bf16x8 yb[4][2];         // B operands of the update, [k-step][system]
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    y1[cb] = mfma(f0[cb][0], wb[cb][0][0], f32x16{});
+                    y1[cb] = mfma(f0[cb][1], wb[cb][0][1], y1[cb]);
+                }
+                // W_2 - H_21 Y_1 (H21 carries the sign that makes this a sum for both
+                // systems; P's factors and Y are negated), accumulated onto W_2 itself: a
+                // B operand pack holds the registers of its accumulator in order
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    const f32x8 w0 = __builtin_convertvector(wb[cb][1][0], f32x8);
+                    const f32x8 w1 = __builtin_convertvector(wb[cb][1][1], f32x8);
+                    y2[cb] = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+                    yb[0][cb] = acc_to_b(y1[cb], 0);
+                    yb[1][cb] = acc_to_b(y1[cb], 1);
+                    y2[cb] = mfma(fh[cb][0], yb[0][cb], y2[cb]);
+                    y2[cb] = mfma(fh[cb][1], yb[1][cb], y2[cb]);
+                }
+                // S: Y_1 times e^{G - g} / sigma for the update
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 e0 = tok4(sm.egrs[b], 0, q, h);
+                    y1[1][4 * q] *= e0.x; y1[1][4 * q + 1] *= e0.y;
+                    y1[1][4 * q + 2] *= e0.z; y1[1][4 * q + 3] *= e0.w;
+                }
+                yb[0][1] = acc_to_b(y1[1], 0);
+                yb[1][1] = acc_to_b(y1[1], 1);
+                // T_22 diag b_2, read while the first half of the update runs
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) f1[cb][half] = lds8(&sm.TB[cb][1][rr + 16 * half]);
+                // X += K^T Y (the P factors are stored negated): A operand = Kt rows (channels)
+                // swz(32 mb + lane); token steps 0, 1 need only Y_1, so they overlap the
+                // Y_2 chain below
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    bf16x8 kt[4];
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb) kt[mb] = lds8(&sm.Kt[swz(32 * mb + l32) * KTL + 16 * s2 + 8 * h]);
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                        for (int cb = 0; cb < 2; ++cb) st[cb][mb] = mfma(kt[mb], yb[s2][cb], st[cb][mb]);
+                }
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    const bf16x8 u0 = acc_to_b(y2[cb], 0), u1 = acc_to_b(y2[cb], 1);
+                    y2[cb] = mfma(f1[cb][0], u0, f32x16{});
+                    y2[cb] = mfma(f1[cb][1], u1, y2[cb]);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 e1 = tok4(sm.egrs[b], 1, q, h);
+                    y2[1][4 * q] *= e1.x; y2[1][4 * q + 1] *= e1.y;
+                    y2[1][4 * q + 2] *= e1.z; y2[1][4 * q + 3] *= e1.w;
+                }
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    yb[2][cb] = acc_to_b(y2[cb], 0);
+                    yb[3][cb] = acc_to_b(y2[cb], 1);
+                }
+#pragma unroll
+                for (int s2 = 2; s2 < 4; ++s2) {
+                    bf16x8 kt[4];
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb) kt[mb] = lds8(&sm.Kt[swz(32 * mb + l32) * KTL + 16 * s2 + 8 * h]);
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                        for (int cb = 0; cb < 2; ++cb) st[cb][mb] = mfma(kt[mb], yb[s2][cb], st[cb][mb]);
                 }
             }
             __syncthreads();                                        // a -> b
@@ -603,10 +642,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 if (i < nc) {
                     const int b = (int)(i & 1);
                     const float la_i = lar, b_i = br;
-                    if (i + 1 < nc) {
-                        HYPIC_FETCH_G((i + 1) * CH);
-                        HYPIC_LOAD_KV((i + 1) * CH, b ^ 1);     // lands during this chunk
-                    }
+                    if (i + 1 < nc) HYPIC_LOAD_KV((i + 1) * CH, b ^ 1);     // lands during this chunk
                     const float gv = wave_prefix_sum(la_i);
                     sm.pv[0][0][l] = gv;
                     sm.pv[0][1][l] = b_i;
@@ -624,8 +660,10 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     ell += (double)la_i;
                 }
                 __syncthreads();                                    // a -> b
-                // ---- phase b: keys and values of chunk i + 1 into the other buffers;
-                //      factors of block 0 of the P system
+                // ---- phase b: keys and values of chunk i + 1 land in the other buffers;
+                //      gates of chunk i + 1 (read in phase b, so that their wait falls at
+                //      its end); factors of block 0 of the P system
+                if (i + 1 < nc) HYPIC_FETCH_G((i + 1) * CH);
                 if (i < nc) prep_invert(sm, 0, 0, 0, l);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // chunk i + 1 has landed
                 __syncthreads();                                    // b -> next a
@@ -644,13 +682,13 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 if (i < nc) {
                     const int b = (int)(i & 1);
                     const float la_i = lar, b_i = br;
-                    if (i + 1 < nc) HYPIC_FETCH_G((i + 1) * CH);
                     sm.pv[pw][0][l] = wave_prefix_sum(la_i);
                     sm.pv[pw][1][l] = b_i;
                     wave_lds_sync();
                     prep_gram(sm, b, pw, l);
                 }
                 __syncthreads();                                    // a -> b
+                if (i + 1 < nc) HYPIC_FETCH_G((i + 1) * CH);        // gates of chunk i + 1
                 if (i < nc) prep_invert(sm, pw >> 1, pw & 1, pw, l);
                 __syncthreads();                                    // b -> next a
             }
