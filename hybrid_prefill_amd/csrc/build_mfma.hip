@@ -74,7 +74,7 @@ struct __align__(16) Smem {
     u16 Kt[D * KTL];           // keys, channel-major
     u16 TB[2][2][32 * TBL];    // per system: T_11 diag(beta_1), T_22 diag(beta_2) (negated for P)
     u16 H21[2][2][32 * TBL];   // [chunk parity][system]: H_21 (P), -H_21 (S), row t, column s
-    float Af[2][2][32 * AFL];  // per system: diagonal blocks A_11, A_22, inverted in place
+    float Af[2][32 * AFL];     // diagonal blocks of A0 (P system), inverted in place
     float pv[4][2][CH];        // per prep wave: g, beta of the chunk being prepared
     float inv_tmp[4][128];     // per prep wave: products inside the blocked inversion
     float egs[2][CH];          // -e^{g_t} sigma_c: the K X factor of W (S columns)
@@ -171,18 +171,27 @@ __device__ __forceinline__ float4 tok4(const float *v, int mb, int q, int h) {
     return *reinterpret_cast<const float4 *>(v + 32 * mb + 16 * (q >> 1) + 8 * h + 4 * (q & 1));
 }
 
-// Prep wave pw, phase b: the inverse factor of 32x32 diagonal block `blk` of
-// system `sys` (0: A0, for P; 1: A, for S) from its A block in Af.  The fp32
-// inverse T is built in place in Af (4x4 forward substitution, merges to 8 and
-// 16 in fp32, the merge to 32 on the MFMA); each level also writes its part of
-// T diag(beta) into TB in bf16 (negated for P).  TB's upper triangle is zeroed
-// once per segment and never written here.
-__device__ __forceinline__ void prep_invert(Smem &sm, int sys, int blk, int pw, int l) {
-    float *M = sm.Af[sys][blk];
+// Prep wave pw (1 or 3), phase b: the inverse factors of 32x32 diagonal block
+// `blk` for both systems from A0_blk in Af.  With D = diag(e^g), A = D A0 D^{-1},
+// so (I + A)^{-1} = D (I + A0)^{-1} D^{-1}: one fp32 inversion T0 of I + A0_blk
+// serves both, entry (r, c) of the S inverse being T0[r][c] e^{g_r - g_c}.
+// T0 is built in place in Af (4x4 forward substitution, merges to 8 and 16 in
+// fp32, the merge to 32 on the MFMA); each level writes its part of
+// -T0 diag(beta) (P) and D T0 D^{-1} diag(beta) (S) into TB in bf16.  TB's upper
+// triangles are zeroed once per segment and never written here.
+__device__ __forceinline__ void prep_invert(Smem &sm, int blk, int pw, int l) {
+    float *M = sm.Af[blk];
     float *tmp = sm.inv_tmp[pw];
-    u16 *TBp = sm.TB[sys][blk];
+    u16 *TP = sm.TB[0][blk], *TS = sm.TB[1][blk];
     const float *bet = &sm.pv[pw][1][32 * blk];
-    const float sg = sys == 0 ? -1.0f : 1.0f;     // P factors negated
+    const float *gg = &sm.pv[pw][0][32 * blk];
+    // both factors of T0 entry x at (r, c), r >= c
+#define HYPIC_PUT(R, C, X)                                                                \
+    do {                                                                                  \
+        const float bx_ = (X) * bet[C];                                                   \
+        TP[(R) * TBL + (C)] = f2bf(-bx_);                                                 \
+        TS[(R) * TBL + (C)] = f2bf(bx_ * __expf(gg[R] - gg[C]));                          \
+    } while (0)
     // (1) the two 16x16 diagonal inverses: each merge is T_10 = -T_11 (A_10 T_00)
     //     in two data-parallel fp32 steps through LDS, inside this wave (no
     //     workgroup barrier)
@@ -192,7 +201,6 @@ __device__ __forceinline__ void prep_invert(Smem &sm, int sys, int blk, int pw, 
         const float n10 = M[(o + 1) * AFL + o];
         const float n20 = M[(o + 2) * AFL + o], n21 = M[(o + 2) * AFL + o + 1];
         const float n30 = M[(o + 3) * AFL + o], n31 = M[(o + 3) * AFL + o + 1], n32 = M[(o + 3) * AFL + o + 2];
-        const float bc = sg * bet[o + j];
         const float x0 = j == 0 ? 1.f : 0.f;
         const float x1 = (j == 1 ? 1.f : 0.f) - n10 * x0;
         const float x2 = (j == 2 ? 1.f : 0.f) - n20 * x0 - n21 * x1;
@@ -201,10 +209,10 @@ __device__ __forceinline__ void prep_invert(Smem &sm, int sys, int blk, int pw, 
         M[(o + 1) * AFL + o + j] = x1;
         M[(o + 2) * AFL + o + j] = x2;
         M[(o + 3) * AFL + o + j] = x3;
-        TBp[o * TBL + o + j] = f2bf(x0 * bc);
-        TBp[(o + 1) * TBL + o + j] = f2bf(x1 * bc);
-        TBp[(o + 2) * TBL + o + j] = f2bf(x2 * bc);
-        TBp[(o + 3) * TBL + o + j] = f2bf(x3 * bc);
+        const float xs[4] = {x0, x1, x2, x3};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (r >= j) HYPIC_PUT(o + r, o + j, xs[r]);
     }
     wave_lds_sync();
     {
@@ -220,7 +228,7 @@ __device__ __forceinline__ void prep_invert(Smem &sm, int sys, int blk, int pw, 
         const float x = -(t11.x * tmp[16 * m + j] + t11.y * tmp[16 * m + 4 + j] + t11.z * tmp[16 * m + 8 + j] +
                           t11.w * tmp[16 * m + 12 + j]);
         M[(o + 4 + i) * AFL + o + j] = x;
-        TBp[(o + 4 + i) * TBL + o + j] = f2bf(x * sg * bet[o + j]);
+        HYPIC_PUT(o + 4 + i, o + j, x);
     }
     wave_lds_sync();
     {
@@ -250,13 +258,12 @@ __device__ __forceinline__ void prep_invert(Smem &sm, int sys, int blk, int pw, 
             u1 += tv[k] * c.y;
         }
         *reinterpret_cast<float2 *>(&M[(R + 8 + i) * AFL + R + j]) = make_float2(-u0, -u1);
-        const float2 bj = *reinterpret_cast<const float2 *>(&bet[R + j]);
-        *reinterpret_cast<uint32_t *>(&TBp[(R + 8 + i) * TBL + R + j]) =
-            pack2(-u0 * sg * bj.x, -u1 * sg * bj.y);
+        HYPIC_PUT(R + 8 + i, R + j, -u0);
+        HYPIC_PUT(R + 8 + i, R + j + 1, -u1);
     }
     wave_lds_sync();
     // (2) T_10 = -T_11 (A_10 T_00) on the 16x16x16 MFMA (lane: column l%16,
-    //     contraction / rows 4 (l/16) + 0..3); only the bf16 TB copy is needed after it
+    //     contraction / rows 4 (l/16) + 0..3); only the bf16 factors are needed after it
     {
         const int c16 = l & 15, k4 = 4 * (l >> 4);
         const float4 a10 = *reinterpret_cast<const float4 *>(&M[(16 + c16) * AFL + k4]);
@@ -270,20 +277,20 @@ __device__ __forceinline__ void prep_invert(Smem &sm, int sys, int blk, int pw, 
         const s16x4 fb2 = pack4(tmp4[0], tmp4[1], tmp4[2], tmp4[3]);
         f32x4 t10 = {0.f, 0.f, 0.f, 0.f};
         t10 = mfma16(fa2, fb2, t10);
-        const float bc = sg * bet[c16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) TBp[(16 + k4 + r) * TBL + c16] = f2bf(t10[r] * bc);
+        for (int r = 0; r < 4; ++r) HYPIC_PUT(16 + k4 + r, c16, t10[r]);
     }
+#undef HYPIC_PUT
 }
 
 // Prep wave pw = 1..3, phase a: Gram block of the chunk in Km[b] on the MFMA with
 // the A operand from token block am and the B operand from token block bn, so
 // lane l32 holds row t = 32 bn + l32 and registers hold columns s (k_t.k_s is
 // symmetric, so the diagonal blocks read either way):
-//   prep wave 1: (0,0) -> A0_11, A_11 into Af (fp32), below the diagonal
+//   prep wave 1: (0,0) -> A0_11 into Af (fp32), below the diagonal
 //   prep wave 2: (0,1) -> H_21 into H21[b] (bf16): k_t.k_s for P, -k_t.k_s e^{g_t - g_s} for S
-//   prep wave 3: (1,1) -> A0_22, A_22 into Af (fp32), below the diagonal
-// with A0 = beta_t k_t.k_s and A = A0 e^{g_t - g_s}.  pv[pw] holds this wave's g, beta.
+//   prep wave 3: (1,1) -> A0_22 into Af (fp32), below the diagonal
+// with A0 = beta_t k_t.k_s.  pv[pw] holds this wave's g, beta.
 __device__ __forceinline__ void prep_gram(Smem &sm, int b, int pw, int l) {
     const int h = l >> 5, l32 = l & 31;
     const int am = pw == 3 ? 1 : 0, bn = pw == 1 ? 0 : 1;
@@ -311,8 +318,9 @@ __device__ __forceinline__ void prep_gram(Smem &sm, int b, int pw, int l) {
         const int s4 = 8 * q + 4 * h;     // column within the block
         const float4 gq4 = gqv[q];
         const float ggv[4] = {gq4.x, gq4.y, gq4.z, gq4.w};
-        float a0[4], a1[4];
+        float a0[4];
         if (pw == 2) {
+            float a1[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 a0[e] = gacc[4 * q + e];
@@ -323,15 +331,8 @@ __device__ __forceinline__ void prep_gram(Smem &sm, int b, int pw, int l) {
             *reinterpret_cast<u32x2 *>(&sm.H21[b][1][o]) = u32x2{pack2(a1[0], a1[1]), pack2(a1[2], a1[3])};
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool low = s4 + e < l32;
-                const float v0 = bt * gacc[4 * q + e];
-                a0[e] = low ? v0 : 0.f;
-                a1[e] = low ? v0 * __expf(gt - ggv[e]) : 0.f;
-            }
-            const int o = l32 * AFL + s4;
-            *reinterpret_cast<float4 *>(&sm.Af[0][am][o]) = make_float4(a0[0], a0[1], a0[2], a0[3]);
-            *reinterpret_cast<float4 *>(&sm.Af[1][am][o]) = make_float4(a1[0], a1[1], a1[2], a1[3]);
+            for (int e = 0; e < 4; ++e) a0[e] = s4 + e < l32 ? bt * gacc[4 * q + e] : 0.f;
+            *reinterpret_cast<float4 *>(&sm.Af[am][l32 * AFL + s4]) = make_float4(a0[0], a0[1], a0[2], a0[3]);
         }
     }
 }
@@ -664,7 +665,6 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 //      gates of chunk i + 1 (read in phase b, so that their wait falls at
                 //      its end); factors of block 0 of the P system
                 if (i + 1 < nc) HYPIC_FETCH_G((i + 1) * CH);
-                if (i < nc) prep_invert(sm, 0, 0, 0, l);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // chunk i + 1 has landed
                 __syncthreads();                                    // b -> next a
             }
@@ -689,7 +689,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 }
                 __syncthreads();                                    // a -> b
                 if (i + 1 < nc) HYPIC_FETCH_G((i + 1) * CH);        // gates of chunk i + 1
-                if (i < nc) prep_invert(sm, pw >> 1, pw & 1, pw, l);
+                if (i < nc && pw != 2) prep_invert(sm, pw >> 1, pw, l);
                 __syncthreads();                                    // b -> next a
             }
         }
