@@ -72,7 +72,7 @@ struct __align__(16) Smem {
     u16 Km[2][CH * KML];       // keys, token-major, double-buffered by chunk parity
     u16 Vm[2][CH * KML];       // values, token-major, double-buffered by chunk parity
     u16 Kt[D * KTL];           // keys, channel-major
-    u16 TB[2][2][32 * TBL];    // per system: T_11 diag(beta_1), T_22 diag(beta_2) (negated for P)
+    u16 TB[2][2][2][32 * TBL]; // [chunk parity][system]: T_11 diag(beta_1), T_22 diag(beta_2) (negated for P)
     u16 H21[2][2][32 * TBL];   // [chunk parity][system]: H_21 (P), -H_21 (S), row t, column s
     float Af[2][32 * AFL];     // diagonal blocks of A0 (P system), inverted in place
     float pv[4][2][CH];        // per prep wave: g, beta of the chunk being prepared
@@ -171,53 +171,72 @@ __device__ __forceinline__ float4 tok4(const float *v, int mb, int q, int h) {
     return *reinterpret_cast<const float4 *>(v + 32 * mb + 16 * (q >> 1) + 8 * h + 4 * (q & 1));
 }
 
-// Prep wave pw (1 or 3), phase b: the inverse factors of 32x32 diagonal block
-// `blk` for both systems from A0_blk in Af.  With D = diag(e^g), A = D A0 D^{-1},
-// so (I + A)^{-1} = D (I + A0)^{-1} D^{-1}: one fp32 inversion T0 of I + A0_blk
+// Prep wave pw (1 or 3): the inverse factors of 32x32 diagonal block `blk` for
+// both systems from A0_blk in Af.  With D = diag(e^g), A = D A0 D^{-1}, so
+// (I + A)^{-1} = D (I + A0)^{-1} D^{-1}: one fp32 inversion T0 of I + A0_blk
 // serves both, entry (r, c) of the S inverse being T0[r][c] e^{g_r - g_c}.
-// T0 is built in place in Af (4x4 forward substitution, merges to 8 and 16 in
+// T0 is built in place in Af (4x4 blocks in closed form, merges to 8 and 16 in
 // fp32, the merge to 32 on the MFMA); each level writes its part of
-// -T0 diag(beta) (P) and D T0 D^{-1} diag(beta) (S) into TB in bf16.  TB's upper
-// triangles are zeroed once per segment and never written here.
-__device__ __forceinline__ void prep_invert(Smem &sm, int blk, int pw, int l) {
-    float *M = sm.Af[blk];
-    float *tmp = sm.inv_tmp[pw];
-    u16 *TP = sm.TB[0][blk], *TS = sm.TB[1][blk];
-    const float *bet = &sm.pv[pw][1][32 * blk];
-    const float *gg = &sm.pv[pw][0][32 * blk];
-    // both factors of T0 entry x at (r, c), r >= c
-#define HYPIC_PUT(R, C, X)                                                                \
-    do {                                                                                  \
-        const float bx_ = (X) * bet[C];                                                   \
-        TP[(R) * TBL + (C)] = f2bf(-bx_);                                                 \
-        TS[(R) * TBL + (C)] = f2bf(bx_ * __expf(gg[R] - gg[C]));                          \
-    } while (0)
-    // (1) the two 16x16 diagonal inverses: each merge is T_10 = -T_11 (A_10 T_00)
-    //     in two data-parallel fp32 steps through LDS, inside this wave (no
-    //     workgroup barrier)
+// -T0 diag(beta) (P) and D T0 D^{-1} diag(beta) (S) into TB[par] in bf16.
+// TB's upper triangles are zeroed once per segment and never written here.
+// Part 1 (levels 0 and 1) runs in phase a right after the Gram block, part 2
+// (level 2 and the merge) in phase b; TB is double-buffered by chunk parity, so
+// the writes may land while the state waves read the previous chunk's factors.
+struct InvCtx {
+    float *M, *tmp;
+    u16 *TP, *TS;
+    const float *bet, *gg;
+};
+
+__device__ __forceinline__ InvCtx inv_ctx(Smem &sm, int par, int blk, int pw) {
+    return InvCtx{sm.Af[blk], sm.inv_tmp[pw], sm.TB[par][0][blk], sm.TB[par][1][blk], &sm.pv[pw][1][32 * blk],
+                  &sm.pv[pw][0][32 * blk]};
+}
+
+// both factors of one T0 entry x at (r, c), r > c
+__device__ __forceinline__ void inv_put(const InvCtx &v, int r, int c, float x) {
+    const float bx = x * v.bet[c];
+    v.TP[r * TBL + c] = f2bf(-bx);
+    v.TS[r * TBL + c] = f2bf(bx * __expf(v.gg[r] - v.gg[c]));
+}
+
+// both factors of four consecutive T0 entries of row r, columns c .. c + 3
+// (entries above the diagonal are zero in T0 and written as zero)
+__device__ __forceinline__ void inv_put4(const InvCtx &v, int r, int c, float4 x) {
+    const float4 b4 = *reinterpret_cast<const float4 *>(&v.bet[c]);
+    const float4 g4 = *reinterpret_cast<const float4 *>(&v.gg[c]);
+    const float gr = v.gg[r];
+    const float b0 = x.x * b4.x, b1 = x.y * b4.y, b2 = x.z * b4.z, b3 = x.w * b4.w;
+    const float e0 = r >= c ? __expf(gr - g4.x) : 0.f, e1 = r >= c + 1 ? __expf(gr - g4.y) : 0.f;
+    const float e2 = r >= c + 2 ? __expf(gr - g4.z) : 0.f, e3 = r >= c + 3 ? __expf(gr - g4.w) : 0.f;
+    *reinterpret_cast<u32x2 *>(&v.TP[r * TBL + c]) = u32x2{pack2(-b0, -b1), pack2(-b2, -b3)};
+    *reinterpret_cast<u32x2 *>(&v.TS[r * TBL + c]) = u32x2{pack2(b0 * e0, b1 * e1), pack2(b2 * e2, b3 * e3)};
+}
+
+__device__ __forceinline__ void prep_invert1(const InvCtx &v, int l) {
+    float *M = v.M, *tmp = v.tmp;
     if (l < 32) {
-        // level 0: 4x4 block o = 16 (l / 16) + 4 ((l / 4) % 4), column j = l % 4
-        const int o = 16 * (l >> 4) + 4 * ((l >> 2) & 3), j = l & 3;
+        // level 0: the 4x4 diagonal block o = 16 (l / 16) + 4 ((l / 4) % 4) in closed form;
+        // lane row i = l % 4
+        const int o = 16 * (l >> 4) + 4 * ((l >> 2) & 3), i = l & 3;
         const float n10 = M[(o + 1) * AFL + o];
         const float n20 = M[(o + 2) * AFL + o], n21 = M[(o + 2) * AFL + o + 1];
         const float n30 = M[(o + 3) * AFL + o], n31 = M[(o + 3) * AFL + o + 1], n32 = M[(o + 3) * AFL + o + 2];
-        const float x0 = j == 0 ? 1.f : 0.f;
-        const float x1 = (j == 1 ? 1.f : 0.f) - n10 * x0;
-        const float x2 = (j == 2 ? 1.f : 0.f) - n20 * x0 - n21 * x1;
-        const float x3 = (j == 3 ? 1.f : 0.f) - n30 * x0 - n31 * x1 - n32 * x2;
-        M[o * AFL + o + j] = x0;
-        M[(o + 1) * AFL + o + j] = x1;
-        M[(o + 2) * AFL + o + j] = x2;
-        M[(o + 3) * AFL + o + j] = x3;
-        const float xs[4] = {x0, x1, x2, x3};
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (r >= j) HYPIC_PUT(o + r, o + j, xs[r]);
+        const float t20 = n21 * n10 - n20, t31 = n32 * n21 - n31;
+        const float t30 = -n30 + n31 * n10 - n32 * t20;
+        float4 x;
+        x.x = i == 0 ? 1.f : i == 1 ? -n10 : i == 2 ? t20 : t30;
+        x.y = i == 0 ? 0.f : i == 1 ? 1.f : i == 2 ? -n21 : t31;
+        x.z = i < 2 ? 0.f : i == 2 ? 1.f : -n32;
+        x.w = i == 3 ? 1.f : 0.f;
+        *reinterpret_cast<float4 *>(&M[(o + i) * AFL + o]) = x;
+        inv_put4(v, o + i, o, x);
     }
     wave_lds_sync();
     {
-        // level 1 (4 -> 8): merge m = l / 16 at o = 16 (m / 2) + 8 (m % 2); output (i, j) of
-        // the 4x4 block T_10 at rows o + 4 + i, columns o + j
+        // level 1 (4 -> 8): T_10 = -T_11 (A_10 T_00); merge m = l / 16 at
+        // o = 16 (m / 2) + 8 (m % 2); output (i, j) of the 4x4 block T_10 at rows
+        // o + 4 + i, columns o + j
         const int m = l >> 4, o = 16 * (m >> 1) + 8 * (m & 1), i = (l >> 2) & 3, j = l & 3;
         const float4 n = *reinterpret_cast<const float4 *>(&M[(o + 4 + i) * AFL + o]);
         const float t = n.x * M[o * AFL + o + j] + n.y * M[(o + 1) * AFL + o + j] + n.z * M[(o + 2) * AFL + o + j] +
@@ -228,9 +247,13 @@ __device__ __forceinline__ void prep_invert(Smem &sm, int blk, int pw, int l) {
         const float x = -(t11.x * tmp[16 * m + j] + t11.y * tmp[16 * m + 4 + j] + t11.z * tmp[16 * m + 8 + j] +
                           t11.w * tmp[16 * m + 12 + j]);
         M[(o + 4 + i) * AFL + o + j] = x;
-        HYPIC_PUT(o + 4 + i, o + j, x);
+        inv_put(v, o + 4 + i, o + j, x);
     }
     wave_lds_sync();
+}
+
+__device__ __forceinline__ void prep_invert2(const InvCtx &v, int l) {
+    float *M = v.M, *tmp = v.tmp;
     {
         // level 2 (8 -> 16): merge m = l / 32 at R = 16 m; lane outputs (i, j), (i, j + 1)
         // of the 8x8 block T_10 at rows R + 8 + i, columns R + j
@@ -258,12 +281,18 @@ __device__ __forceinline__ void prep_invert(Smem &sm, int blk, int pw, int l) {
             u1 += tv[k] * c.y;
         }
         *reinterpret_cast<float2 *>(&M[(R + 8 + i) * AFL + R + j]) = make_float2(-u0, -u1);
-        HYPIC_PUT(R + 8 + i, R + j, -u0);
-        HYPIC_PUT(R + 8 + i, R + j + 1, -u1);
+        const int r = R + 8 + i, c = R + j;
+        const float2 b2 = *reinterpret_cast<const float2 *>(&v.bet[c]);
+        const float2 g2 = *reinterpret_cast<const float2 *>(&v.gg[c]);
+        const float gr = v.gg[r];
+        const float b0 = -u0 * b2.x, b1 = -u1 * b2.y;
+        *reinterpret_cast<uint32_t *>(&v.TP[r * TBL + c]) = pack2(-b0, -b1);
+        *reinterpret_cast<uint32_t *>(&v.TS[r * TBL + c]) = pack2(b0 * __expf(gr - g2.x), b1 * __expf(gr - g2.y));
     }
     wave_lds_sync();
-    // (2) T_10 = -T_11 (A_10 T_00) on the 16x16x16 MFMA (lane: column l%16,
-    //     contraction / rows 4 (l/16) + 0..3); only the bf16 factors are needed after it
+    // (2) merge to 32 on the 16x16x16 MFMA: tmp = A_10 T_00 with lane (column l%16,
+    //     rows 4 (l/16) + 0..3); then T_10^T = tmp^T (-T_11^T), the operands swapped so
+    //     that lane (l%16, l/16) holds row 16 + l%16 of T0, columns 4 (l/16) + 0..3
     {
         const int c16 = l & 15, k4 = 4 * (l >> 4);
         const float4 a10 = *reinterpret_cast<const float4 *>(&M[(16 + c16) * AFL + k4]);
@@ -273,14 +302,12 @@ __device__ __forceinline__ void prep_invert(Smem &sm, int blk, int pw, int l) {
         f32x4 tmp4 = {0.f, 0.f, 0.f, 0.f};
         tmp4 = mfma16(fa, fb, tmp4);
         const float4 t11 = *reinterpret_cast<const float4 *>(&M[(16 + c16) * AFL + 16 + k4]);
-        const s16x4 fa2 = pack4(-t11.x, -t11.y, -t11.z, -t11.w);
-        const s16x4 fb2 = pack4(tmp4[0], tmp4[1], tmp4[2], tmp4[3]);
+        const s16x4 nt = pack4(-t11.x, -t11.y, -t11.z, -t11.w);
+        const s16x4 tt = pack4(tmp4[0], tmp4[1], tmp4[2], tmp4[3]);
         f32x4 t10 = {0.f, 0.f, 0.f, 0.f};
-        t10 = mfma16(fa2, fb2, t10);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) HYPIC_PUT(16 + k4 + r, c16, t10[r]);
+        t10 = mfma16(tt, nt, t10);
+        inv_put4(v, 16 + c16, k4, make_float4(t10[0], t10[1], t10[2], t10[3]));
     }
-#undef HYPIC_PUT
 }
 
 // Prep wave pw = 1..3, phase a: Gram block of the chunk in Km[b] on the MFMA with
@@ -356,7 +383,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         sm.t0 = o0; sm.n = o1 - o0; sm.slot = slot; sm.state = st;
     }
     // the upper triangles of the T diag(beta) tiles stay zero for the whole segment
-    for (int e = th; e < (int)(sizeof(sm.TB) / 16); e += NT) reinterpret_cast<u32x4 *>(&sm.TB[0][0][0])[e] = u32x4{};
+    for (int e = th; e < (int)(sizeof(sm.TB) / 16); e += NT) reinterpret_cast<u32x4 *>(&sm.TB[0][0][0][0])[e] = u32x4{};
     __syncthreads();
     const int state = sm.state;
     if (state == 1) return;
@@ -409,7 +436,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
-                        f0[cb][half] = lds8(&sm.TB[cb][0][rr + 16 * half]);
+                        f0[cb][half] = lds8(&sm.TB[b][cb][0][rr + 16 * half]);
                         fh[cb][half] = lds8(&sm.H21[b][cb][rr + 16 * half]);
                     }
                 f32x16 y1[2], y2[2];     // [column block = system]
@@ -445,7 +472,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-                    for (int half = 0; half < 2; ++half) f1[cb][half] = lds8(&sm.TB[cb][1][rr + 16 * half]);
+                    for (int half = 0; half < 2; ++half) f1[cb][half] = lds8(&sm.TB[b][cb][1][rr + 16 * half]);
                 // X += K^T Y (the P factors are stored negated): A operand = Kt rows (channels)
                 // swz(32 mb + lane); token steps 0, 1 need only Y_1, so they overlap the
                 // Y_2 chain below
@@ -686,10 +713,14 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     sm.pv[pw][1][l] = b_i;
                     wave_lds_sync();
                     prep_gram(sm, b, pw, l);
+                    if (pw != 2) {
+                        wave_lds_sync();
+                        prep_invert1(inv_ctx(sm, b, pw >> 1, pw), l);
+                    }
                 }
                 __syncthreads();                                    // a -> b
                 if (i + 1 < nc) HYPIC_FETCH_G((i + 1) * CH);        // gates of chunk i + 1
-                if (i < nc && pw != 2) prep_invert(sm, pw >> 1, pw, l);
+                if (i < nc && pw != 2) prep_invert2(inv_ctx(sm, (int)(i & 1), pw >> 1, pw), l);
                 __syncthreads();                                    // b -> next a
             }
         }
