@@ -56,21 +56,42 @@ __device__ __forceinline__ void split(float x, u16 &hi, u16 &lo) {
     lo = bf_bits(x - bf_val(hi));
 }
 
+// the same split for two values at once, packed bf16 pairs (element 0 in the low half):
+// one v_cvt_pk_bf16_f32 per part and the hi part unpacked with a shift and a mask
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x0, x1}, bf16x2_t));
+    const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x0 - h0, x1 - h1}, bf16x2_t));
+}
+
+// The chain's first CHAIN_LDS slots and their ell values, staged in LDS by the
+// validation pass: the product loop then reads them from LDS instead of waiting on a
+// dependent global load per step (later entries are read from global memory).
+constexpr int CHAIN_LDS = 1024;
+struct ChainStage {
+    int32_t slot[CHAIN_LDS];
+    float ell[CHAIN_LDS];
+};
+__device__ __forceinline__ int32_t chain_slot(const ChainStage &cs, const ComposeArgs &a, int64_t c_lo, int64_t c) {
+    return c - c_lo < CHAIN_LDS ? cs.slot[c - c_lo] : a.chain_slots[c];
+}
+__device__ __forceinline__ float chain_ell(const ChainStage &cs, const ComposeArgs &a, int64_t c_lo, int64_t c,
+                                           int head) {
+    return c - c_lo < CHAIN_LDS ? cs.ell[c - c_lo] : a.pool_ell[(int64_t)a.chain_slots[c] * a.H + head];
+}
+
+
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
 // B operand from accumulator registers 8*half .. 8*half+7, as hi and lo parts
 __device__ __forceinline__ void acc_to_b2(const f32x16 &c, int half, bf16x8 &bh, bf16x8 &bl) {
-    u16 hi[8], lo[8];
+    uint32_t uh[4], ul[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) split(c[8 * half + e], hi[e], lo[e]);
-    u32x4 uh, ul;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        uh[q] = (uint32_t)hi[2 * q] | ((uint32_t)hi[2 * q + 1] << 16);
-        ul[q] = (uint32_t)lo[2 * q] | ((uint32_t)lo[2 * q + 1] << 16);
-    }
-    bh = __builtin_bit_cast(bf16x8, uh);
-    bl = __builtin_bit_cast(bf16x8, ul);
+    for (int q = 0; q < 4; ++q) split2(c[8 * half + 2 * q], c[8 * half + 2 * q + 1], uh[q], ul[q]);
+    bh = __builtin_bit_cast(bf16x8, u32x4{uh[0], uh[1], uh[2], uh[3]});
+    bl = __builtin_bit_cast(bf16x8, u32x4{ul[0], ul[1], ul[2], ul[3]});
 }
 
 // Fragment slot of P element (i, k): A operand of row block mb = i/32 and
@@ -86,6 +107,7 @@ struct __align__(16) PStage {
 template <bool MODE_P>
 __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a) {
     __shared__ PStage ps;
+    __shared__ ChainStage cs;
     __shared__ int sh_bad;
 
     const int th = threadIdx.x;
@@ -107,7 +129,12 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
         __syncthreads();
         for (int64_t c = c_lo + th; c < c_hi; c += NT) {
             const int32_t s = a.chain_slots[c];
-            if (s < 0 || s >= a.num_slots) sh_bad = 1;
+            const bool ok = s >= 0 && s < a.num_slots;
+            if (!ok) sh_bad = 1;
+            if (c - c_lo < CHAIN_LDS) {
+                cs.slot[c - c_lo] = ok ? s : 0;
+                cs.ell[c - c_lo] = ok ? a.pool_ell[(int64_t)s * a.H + head] : 0.f;
+            }
         }
     }
     __syncthreads();
@@ -153,15 +180,17 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
     // fragments in LDS at the top of the step.  S_c: HBM -> LDS directly (no
     // registers), wave w's instruction u moving pieces (16 w + u) * 64 + lane.
     float4 pre[16];
+    float ell_next = 0.f;     // ell of the record in flight
 #define HYPIC_FETCH_P(CC)                                                                        \
     do {                                                                                         \
-        const int64_t frec = (int64_t)a.chain_slots[(CC)] * a.H + head;                          \
+        const int64_t frec = (int64_t)chain_slot(cs, a, c_lo, (CC)) * a.H + head;                     \
+        ell_next = chain_ell(cs, a, c_lo, (CC), head);                                                        \
         const float4 *fsrc = reinterpret_cast<const float4 *>(a.pool_P + frec * D * D);          \
         _Pragma("unroll") for (int u = 0; u < 16; ++u) pre[u] = fsrc[th + NT * u];               \
     } while (0)
 #define HYPIC_FETCH_S(CC)                                                                        \
     do {                                                                                         \
-        const int64_t frec = (int64_t)a.chain_slots[(CC)] * a.H + head;                          \
+        const int64_t frec = (int64_t)chain_slot(cs, a, c_lo, (CC)) * a.H + head;                     \
         const float4 *fss = reinterpret_cast<const float4 *>(a.pool_S + frec * D * D);           \
         _Pragma("unroll") for (int u = 0; u < 16; ++u)                                           \
             __builtin_amdgcn_global_load_lds(fss + (16 * w + u) * 64 + l,                       \
@@ -173,7 +202,7 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
     }
 
     for (; c < c_hi; ++c) {
-        const int64_t rec = (int64_t)a.chain_slots[c] * a.H + head;
+        const float le = ell_next;
         // stage P_c (bf16 hi/lo, fragment order)
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
@@ -182,16 +211,12 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
             const int mb = i >> 5, li = i & 31;
             const int kb = k0 >> 4, c16 = k0 & 15;
             const int hh = (c16 >> 2) & 1, e0 = (c16 >> 3) * 4;
-            u16 hi[4], lo[4];
-            split(pre[u].x, hi[0], lo[0]);
-            split(pre[u].y, hi[1], lo[1]);
-            split(pre[u].z, hi[2], lo[2]);
-            split(pre[u].w, hi[3], lo[3]);
+            uint32_t h01, l01, h23, l23;
+            split2(pre[u].x, pre[u].y, h01, l01);
+            split2(pre[u].z, pre[u].w, h23, l23);
             const int slot = (mb * 8 + kb) * FRAG_U32 + lane_slot(li, hh) + (e0 >> 1);
-            *reinterpret_cast<u32x2 *>(&ps.hi[slot]) =
-                u32x2{(uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16)};
-            *reinterpret_cast<u32x2 *>(&ps.lo[slot]) =
-                u32x2{(uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)};
+            *reinterpret_cast<u32x2 *>(&ps.hi[slot]) = u32x2{h01, h23};
+            *reinterpret_cast<u32x2 *>(&ps.lo[slot]) = u32x2{l01, l23};
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this wave's S_c pieces have landed
         __syncthreads();
@@ -207,7 +232,6 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
             HYPIC_FETCH_P(c + 1);
             if (!MODE_P) HYPIC_FETCH_S(c + 1);
         }
-        const float le = a.pool_ell[rec];
         // acc = P_c * state, hi.hi + hi.lo + lo.hi
         // the state's B fragments (hi, lo) for all 8 k-steps, once per step; the
         // state itself is not needed again until the combine overwrites it
@@ -257,13 +281,213 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
     if (!MODE_P && a.out_ell && th == 0) a.out_ell[orec] = (float)ell;
 }
 
+// Sliced variant for few chains (the chain is sequential, so one workgroup per
+// (request, head) leaves most of the chip idle when there are few of them): the
+// state's columns evolve independently (column j of S only meets column j of S_i),
+// so workgroup (request, head, slice) keeps columns [32 slice, 32 slice + 32) and
+// four of them share a chain.  Wave w owns row block w of the slice (one fp32
+// 32x32 tile) and loads only rows 32w .. 32w + 31 of each P_i, straight into A
+// operand registers (split to bf16 hi/lo there: no LDS staging).  The product needs
+// every row of the slice's state as B operand, so each step the waves publish
+// their tile's hi/lo B fragments in LDS (double-buffered by step parity: one
+// workgroup barrier per step).  The next record is prefetched into registers
+// while the current product runs.
+constexpr int NSL = 4;
+struct __align__(16) XStage {
+    u32x4 f[2][8][2][64];     // [step parity][k-step][hi, lo][lane]
+};
+
+struct __align__(16) PFrag {
+    uint32_t hi[NFRAG * FRAG_U32];
+    uint32_t lo[NFRAG * FRAG_U32];
+};
+
+template <bool MODE_P>
+__global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs a) {
+    __shared__ XStage xs;
+    __shared__ PFrag xp;      // wave w's fragments: row block w of P_c
+    __shared__ ChainStage cs;
+    __shared__ int sh_bad;
+
+    const int th = threadIdx.x;
+    const int w = th >> 6, l = th & 63, h = l >> 5, l32 = l & 31;
+    // the slices of a chain sit 8 blocks apart, so they land on the same XCD (block b
+    // goes to XCD b % 8) and share each P_i through its L2
+    const int bx = blockIdx.x;
+    const int sl = (bx >> 3) % NSL;
+    const int unit = (bx / (8 * NSL)) * 8 + (bx & 7);
+    if (unit >= a.num_requests * a.H) return;   // grid padding
+    const int head = unit % a.H;
+    const int r = unit / a.H;
+    const int64_t orec = (int64_t)r * a.H + head;
+    const int col = 32 * sl + l32;              // this lane's state column
+    float *out = MODE_P ? a.out_P + orec * D * D : a.out_S + orec * D * D;
+
+    // ---- chain validation (same rules as the reference kernel)
+    if (th == 0) {
+        const int64_t lo = a.chain_offsets[r], hi = a.chain_offsets[r + 1];
+        sh_bad = (lo < 0 || hi < lo || hi > a.num_chain_slots) ? 2 : 0;
+    }
+    __syncthreads();
+    const int64_t c_lo = a.chain_offsets[r], c_hi = a.chain_offsets[r + 1];
+    if (sh_bad == 0) {
+        __syncthreads();
+        for (int64_t c = c_lo + th; c < c_hi; c += NT) {
+            const int32_t s = a.chain_slots[c];
+            const bool ok = s >= 0 && s < a.num_slots;
+            if (!ok) sh_bad = 1;
+            if (c - c_lo < CHAIN_LDS) {
+                cs.slot[c - c_lo] = ok ? s : 0;
+                cs.ell[c - c_lo] = ok ? a.pool_ell[(int64_t)s * a.H + head] : 0.f;
+            }
+        }
+    }
+    __syncthreads();
+    const int bad = sh_bad;
+    if (bad) {
+        if (th == 0 && !MODE_P && sl == 0)
+            raise_flag(a.err_flag, bad == 1 ? HYPIC_EFLAG_SLOT_OUT_OF_RANGE : HYPIC_EFLAG_BAD_OFFSETS);
+        const float nanv = __int_as_float(0x7fc00000);
+        for (int e = th; e < 32 * D; e += NT) out[(e >> 5) * D + 32 * sl + (e & 31)] = nanv;
+        if (!MODE_P && a.out_ell && th == 0 && sl == 0) a.out_ell[orec] = nanv;
+        return;
+    }
+
+    // ---- initial tile (rows 32w + acc_row, column col)
+    f32x16 st;
+    int64_t c = c_lo;
+    const bool first_direct = MODE_P || a.init_S == nullptr;
+    double ell = 0.0;
+    if (first_direct && c < c_hi) {
+        const int64_t rec = (int64_t)a.chain_slots[c] * a.H + head;
+        const float *src = MODE_P ? a.pool_P + rec * D * D : a.pool_S + rec * D * D;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) st[q] = src[(32 * w + acc_row(q, h)) * D + col];
+        ell += (double)a.pool_ell[rec];
+        ++c;
+    } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int row = 32 * w + acc_row(q, h);
+            st[q] = MODE_P ? (row == col ? 1.0f : 0.0f)
+                           : (a.init_S ? a.init_S[orec * D * D + (int64_t)row * D + col] : 0.0f);
+        }
+    }
+
+    // ---- records are fetched two steps ahead into two register sets (even and odd
+    //      steps).  P_c: this wave's rows 32w .. 32w + 31 as coalesced 16-byte pieces
+    //      (piece u of lane l: row 32w + 2u + l / 32, columns 4 (l % 32) .. +3), split to
+    //      bf16 hi/lo at the top of the step and written to the wave's own fragment
+    //      area in LDS, whose A operand reads are single 16-byte loads.  S_c: this
+    //      lane's 16 tile positions.  The registers of P_c (S_c) are refilled for step
+    //      c + 2 as soon as the step has staged (added) them.
+    float4 pa[16], pb[16];
+    float sa[16], sb[16];
+    float ea = 0.f, eb = 0.f;     // ell of the record each set holds
+#define HYPIC_PROW(CC) \
+    (a.pool_P + ((int64_t)chain_slot(cs, a, c_lo, (CC)) * a.H + head) * D * D + (int64_t)(32 * w + (l >> 5)) * D + 4 * l32)
+#define HYPIC_PFETCH(PF, PROW)                                                                      \
+    do {                                                                                            \
+        _Pragma("unroll") for (int u = 0; u < 16; ++u)                                              \
+            PF[u] = *reinterpret_cast<const float4 *>((PROW) + 2 * u * D);                          \
+    } while (0)
+#define HYPIC_SFETCH(SV, CC)                                                                        \
+    do {                                                                                            \
+        if (!MODE_P) {                                                                              \
+            const float *ss_ = a.pool_S + ((int64_t)chain_slot(cs, a, c_lo, (CC)) * a.H + head) * D * D + col; \
+            _Pragma("unroll") for (int q = 0; q < 16; ++q) SV[q] = ss_[(32 * w + acc_row(q, h)) * D]; \
+        }                                                                                           \
+    } while (0)
+    // one step: publish the tile, stage P_c (and refetch its registers for step c + 2),
+    // state <- e^{ell_c} P_c state + S_c
+#define HYPIC_STEP(PF, SV, EL, PAR)                                                                 \
+    do {                                                                                            \
+        _Pragma("unroll") for (int half = 0; half < 2; ++half) {                                    \
+            bf16x8 bh_, bl_;                                                                        \
+            acc_to_b2(st, half, bh_, bl_);                                                          \
+            xs.f[PAR][2 * w + half][0][l] = __builtin_bit_cast(u32x4, bh_);                         \
+            xs.f[PAR][2 * w + half][1][l] = __builtin_bit_cast(u32x4, bl_);                         \
+        }                                                                                           \
+        const bool more_ = c + 2 < c_hi;                                                            \
+        const float *pn_ = HYPIC_PROW(more_ ? c + 2 : c);                                           \
+        _Pragma("unroll") for (int u = 0; u < 16; ++u) {                                            \
+            const int li_ = 2 * u + (l >> 5), c0_ = 4 * l32;                                        \
+            const int kb_ = c0_ >> 4, c16_ = c0_ & 15;                                              \
+            const int slot_ = (w * 8 + kb_) * FRAG_U32 + lane_slot(li_, (c16_ >> 2) & 1) + 2 * (c16_ >> 3); \
+            uint32_t h01_, l01_, h23_, l23_;                                                        \
+            split2(PF[u].x, PF[u].y, h01_, l01_);                                                   \
+            split2(PF[u].z, PF[u].w, h23_, l23_);                                                   \
+            *reinterpret_cast<u32x2 *>(&xp.hi[slot_]) = u32x2{h01_, h23_};                          \
+            *reinterpret_cast<u32x2 *>(&xp.lo[slot_]) = u32x2{l01_, l23_};                          \
+            /* unconditional (the last steps reload P_c): no phi copies */                          \
+            PF[u] = *reinterpret_cast<const float4 *>(pn_ + 2 * u * D);                             \
+        }                                                                                           \
+        const float le_ = EL;                                                                       \
+        EL = chain_ell(cs, a, c_lo, more_ ? c + 2 : c, head);          \
+        __syncthreads();                                                                            \
+        f32x16 acc_ = {}, acc1_ = {};                                                               \
+        _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) {                                          \
+            const int f_ = (w * 8 + kb) * FRAG_U32 + lane_slot(l32, h);                             \
+            const bf16x8 ah_ = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&xp.hi[f_])); \
+            const bf16x8 al_ = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&xp.lo[f_])); \
+            const bf16x8 bh_ = __builtin_bit_cast(bf16x8, xs.f[PAR][kb][0][l]);                     \
+            const bf16x8 bl_ = __builtin_bit_cast(bf16x8, xs.f[PAR][kb][1][l]);                     \
+            acc_ = mfma(ah_, bh_, acc_);                                                            \
+            acc1_ = mfma(ah_, bl_, acc1_);                                                          \
+            acc1_ = mfma(al_, bh_, acc1_);                                                          \
+        }                                                                                           \
+        acc_ += acc1_;                                                                              \
+        if (MODE_P) {                                                                               \
+            st = acc_;                                                                              \
+        } else {                                                                                    \
+            const float sc_ = expf(le_);                                                            \
+            _Pragma("unroll") for (int q = 0; q < 16; ++q) st[q] = sc_ * acc_[q] + SV[q];           \
+        }                                                                                           \
+        HYPIC_SFETCH(SV, more_ ? c + 2 : c);                                                        \
+        ell += (double)le_;                                                                         \
+    } while (0)
+    if (c < c_hi) {
+        HYPIC_PFETCH(pa, HYPIC_PROW(c));
+        HYPIC_SFETCH(sa, c);
+        ea = chain_ell(cs, a, c_lo, c, head);
+    }
+    if (c + 1 < c_hi) {
+        HYPIC_PFETCH(pb, HYPIC_PROW(c + 1));
+        HYPIC_SFETCH(sb, c + 1);
+        eb = chain_ell(cs, a, c_lo, c + 1, head);
+    }
+    // even steps use pa/sa and exchange buffer 0, odd steps pb/sb and buffer 1 (the
+    // exchange is double-buffered, so one barrier per step suffices)
+    while (c < c_hi) {
+        HYPIC_STEP(pa, sa, ea, 0);
+        if (++c >= c_hi) break;
+        HYPIC_STEP(pb, sb, eb, 1);
+        ++c;
+    }
+#undef HYPIC_STEP
+#undef HYPIC_PFETCH
+#undef HYPIC_PROW
+#undef HYPIC_SFETCH
+#pragma unroll
+    for (int q = 0; q < 16; ++q) out[(int64_t)(32 * w + acc_row(q, h)) * D + col] = st[q];
+    if (!MODE_P && a.out_ell && th == 0 && sl == 0) a.out_ell[orec] = (float)ell;
+}
+
 }  // namespace
 
 hipError_t launch_compose_mfma(const ComposeArgs &a, hipStream_t stream, bool *taken) {
     *taken = false;
     if (a.family != HYPIC_GDN || a.dk != 128 || a.dv != 128) return hipSuccess;
     *taken = true;
-    const dim3 grid((unsigned)((int64_t)a.num_requests * a.H));
+    const int64_t units = (int64_t)a.num_requests * a.H;
+    if (units <= 512) {
+        // few chains: four workgroups per chain, one per 32-column slice of the state
+        const dim3 grid((unsigned)((units + 7) / 8 * 8 * NSL));
+        hipLaunchKernelGGL(compose_sliced_mfma_kernel<false>, grid, dim3(NT), 0, stream, a);
+        if (a.out_P) hipLaunchKernelGGL(compose_sliced_mfma_kernel<true>, grid, dim3(NT), 0, stream, a);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)units);
     hipLaunchKernelGGL(compose_dense_mfma_kernel<false>, grid, dim3(NT), 0, stream, a);
     if (a.out_P) hipLaunchKernelGGL(compose_dense_mfma_kernel<true>, grid, dim3(NT), 0, stream, a);
     return hipGetLastError();

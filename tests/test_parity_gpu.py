@@ -231,6 +231,50 @@ def test_compose_indexing_bit_exact():
     assert torch.equal(out[0], init[0])
 
 
+@pytest.mark.parametrize("num_req", [1, 16, 17])
+def test_compose_d128_chain_paths(num_req):
+    """d=128 compose on synthetic records, against the oracle: up to 16 x 32 chains run four
+    workgroups per chain (one per 32-column slice of the state), more run one per chain.
+    Chains of length 16, 0 and 1 and random ones, with and without an initial state, and
+    the composed operator."""
+    H, d, nslots = 32, 128, 12
+    rng = np.random.default_rng(900 + num_req)
+    q, _ = np.linalg.qr(rng.standard_normal((nslots, H, d, d)))
+    P = q * rng.uniform(0.9, 1.0, size=(nslots, H, 1, d))     # contractions: chains stay bounded
+    S = rng.standard_normal((nslots, H, d, d))
+    ell = rng.uniform(-0.5, 0.0, size=(nslots, H))
+    pool = hp.Pool.allocate(hp.GDN, nslots, H, d, d, device="cuda", fill=0.0)
+    pool.P.copy_(torch.from_numpy(P).float())
+    pool.S.copy_(torch.from_numpy(S).float())
+    pool.log_scale.copy_(torch.from_numpy(ell).float())
+    lens = [int(x) for x in rng.integers(0, 17, size=num_req)]
+    lens[0] = 16
+    if num_req > 2:
+        lens[1], lens[2] = 0, 1
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    flat = rng.integers(0, nslots, size=int(offs[-1])).astype(np.int32)
+    heads = [0, 13, 31]
+    for with_init in (False, True):
+        init = torch.randn((num_req, H, d, d), device="cuda") if with_init else None
+        out_ell = torch.empty((num_req, H), device="cuda")
+        out_P = torch.empty((num_req, H, d, d), device="cuda")
+        out_S = hp.compose_chain(pool, dev_i64(offs), dev_i32(flat), init_S=init, out_log_scale=out_ell,
+                                 out_P=out_P)
+        torch.cuda.synchronize()
+        say(f"[compose d128] requests={num_req} init={with_init} lens={lens[:8]}")
+        worst = [0.0, 0.0, 0.0]
+        for h in heads:
+            rS, rell, rP = oracle.compose(hp.GDN, np64(pool.log_scale[:, h:h + 1]), np64(pool.P[:, h:h + 1]),
+                                          np64(pool.S[:, h:h + 1]), offs, flat,
+                                          init_S=None if init is None else np64(init[:, h:h + 1]), want_P=True)
+            for r in range(num_req):
+                worst[0] = max(worst[0], rel_fro(np64(out_S[r, h]), rS[r, 0]))
+                worst[1] = max(worst[1], rel_fro(np64(out_P[r, h]), rP[r, 0]))
+                worst[2] = max(worst[2], abs(float(out_ell[r, h]) - float(rell[r, 0])))
+        say(f"   S err {worst[0]:.2e}  P err {worst[1]:.2e}  ell err {worst[2]:.2e}")
+        assert worst[0] <= 1e-4 and worst[1] <= 1e-4 and worst[2] <= 1e-5
+
+
 def test_compose_out_of_range_slot_flags_and_isolates():
     pool = _gdn_pool()
     chains = [[0, 1, 2], [1, 9, 2], [3, 4]]          # slot 9 is outside the 6-slot pool
