@@ -45,8 +45,8 @@ CHUNK = 64
 # (scaled by the copy-kernel calibration); None until measured for the current kernel.
 # HBM bytes per launch of the GDN build on the main workload (rocprofv3 FETCH_SIZE and
 # WRITE_SIZE, each scaled by what the counter reads for a copy of known size: read
-# 606.9 MB + write 69.2 MB); None whenever the kernel changed since the counters were taken
-TRAFFIC_GDN_BUILD = 676.2e6
+# 604.3 MB + write 67.1 MB); None whenever the kernel changed since the counters were taken
+TRAFFIC_GDN_BUILD = 671.5e6
 
 
 def log(msg):
@@ -115,6 +115,27 @@ class KernelTimer:
         self.pairs = {}
 
 
+def kernel_pass(launches, n):
+    """Mean duration of each launch in `launches` (name -> callable, idempotent): one
+    HIP-event pair around n back-to-back launches of it on the current stream, so the
+    per-launch event overhead is spread over n; a short device spin first lets the
+    host run ahead, so host time is never counted as kernel time."""
+    out = []
+    for name, fn in launches:
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(int(5e6))
+        s.record()
+        for _ in range(n):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        out.append(s.elapsed_time(e) / n)
+    return tuple(out)
+
+
 def roofline(bound, achieved, peak, unit, traffic=None):
     return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
             "frac": achieved / peak, "traffic": traffic}
@@ -155,7 +176,15 @@ def bench_main(args):
     wall = time.perf_counter() - t0
     assert int(w["err"].item()) == 0
     ms_step = wall * 1e3 / args.steps
-    b_ms, c_ms = timer.mean_ms("build"), timer.mean_ms("compose")
+    # per-kernel durations: the same steps again with the launch queue filled ahead
+    # (a short device spin first), so that host time between an event and its launch
+    # never shows up as kernel time
+    st_, pool_ = w["st"], w["pool"]
+    b_ms, c_ms = kernel_pass((
+        ("build", lambda: hp.build_segment(hp.GDN, st_.k, st_.v, st_.log_alpha, w["offs"], pool_, w["slots"],
+                                           beta=st_.beta, err_flag=w["err"])),
+        ("compose", lambda: hp.compose_chain(pool_, w["chain_offs"], w["slots"], out_S=w["out_S"],
+                                             err_flag=w["err"]))), args.steps)
     N, H, dk, dv, nseg = w["N"], w["H"], w["dk"], w["dv"], w["nseg"]
     flops = gdn_build_flops_per_token_head(dk, dv) * N * H
     bbytes = gdn_build_bytes(N, H, dk, dv, nseg)
@@ -219,16 +248,18 @@ def bench_sd(args, H=16, d=128, nseg=8, seg_len=2048, seed=201, copies=3):
                if fam == hp.SCALAR else
                [synth.diagonal_log_gates(N, H, d, seed * 10 + 4 + 100 * c, device="cuda") for c in range(copies)])
         pool = hp.Pool.allocate(fam, nseg, H, d, d, device="cuda")
-        timer = KernelTimer()
         for i in range(args.warmup):
             c = i % copies
             hp.build_segment(fam, ks[c], vs[c], las[c], offs, pool, slots)
         torch.cuda.synchronize()
-        for i in range(max(3, args.steps)):
-            c = i % copies
-            timer.time("build", lambda: hp.build_segment(fam, ks[c], vs[c], las[c], offs, pool, slots))
-            timer.time("compose", lambda: hp.compose_chain(pool, chain, slots))
-        b_ms, c_ms = timer.mean_ms("build"), timer.mean_ms("compose")
+        it = [0]
+
+        def build_rot():
+            c = it[0] % copies
+            it[0] += 1
+            hp.build_segment(fam, ks[c], vs[c], las[c], offs, pool, slots)
+        b_ms, c_ms = kernel_pass((("build", build_rot), ("compose", lambda: hp.compose_chain(pool, chain, slots))),
+                                 max(3, args.steps))
         nb = sd_build_bytes(fam, N, H, d, d, nseg)
         log(f"{name}: build {b_ms:.3f} ms ({nb / (b_ms * 1e-3) / 1e9:.0f} GB/s), compose {c_ms:.3f} ms")
         out.append({"workload": f"{name}_build_h{H}_d{d}_{nseg}x{seg_len}", "metric": "tokens/s",
