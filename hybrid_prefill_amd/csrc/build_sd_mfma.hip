@@ -22,9 +22,12 @@
 // [32w, 32w + 32) of S as fp32 32x32 accumulator tiles.  Keys and values arrive
 // token-major and are turned around on the MFMA itself: X . I returns X's
 // columns in the accumulator layout, which is the A layout of K^T and the B
-// layout of V^T with the same token order.  Every wave turns around what it
-// needs (its own 32 key channels, all of the workgroup's value columns), so
-// the waves share nothing but the staged tiles.
+// layout of V^T with the same token order (diagonal family).  The scalar family
+// reads both fragments straight from the token-major tiles with gfx950's
+// transposing LDS read (ds_read_b64_tr_b16) and puts the per-token weights on
+// the K^T fragment, so its chunk is four MFMAs per value block.  Every wave
+// takes what it needs (its own 32 key channels, all of the workgroup's value
+// columns), so the waves share nothing but the staged tiles.
 //
 // Streaming: keys, values and gates go from HBM straight into LDS
 // (global_load_lds), NBUF chunks deep; one workgroup barrier per chunk.  Tail
@@ -40,6 +43,8 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int CH = 64;
 constexpr int D = 128;
@@ -57,6 +62,24 @@ __device__ __forceinline__ bf16x8 lds8(const u16 *p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
 }
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// ds_read_b64_tr_b16: in each 16-lane group, lane 4a + b gives the address of four
+// consecutive b16 of row a of a row-major tile (columns 4b .. 4b + 3 of the group's 16);
+// lane j receives column j of those four rows.  Two reads give the 8-element operand
+// fragment of one lane: 8 consecutive rows of one column.
+__device__ __forceinline__ bf16x8 tr_pair(const u16 *p0, const u16 *p1) {
+    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+    const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// b16 fragment times eight fp32 factors, repacked (rounded to nearest even)
+__device__ __forceinline__ bf16x8 scale8(bf16x8 x, float4 f0, float4 f1) {
+    const f32x8 v = __builtin_convertvector(x, f32x8);
+    const f32x8 s = {v[0] * f0.x, v[1] * f0.y, v[2] * f0.z, v[3] * f0.w, v[4] * f1.x, v[5] * f1.y, v[6] * f1.z,
+                     v[7] * f1.w};
+    return __builtin_convertvector(s, bf16x8);
+}
 
 // global_load_lds through non-template helpers: called directly from the kernel
 // template, the builtin's LDS-pointer argument keeps the host pass from emitting
@@ -255,6 +278,28 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         for (int r = 0; r < 16; ++r) st[jb][r] = 0.f;
     double ell = 0.0;   // scalar: wave 0, one token per lane; diagonal: this lane's tokens of channel 32w + l32
     const bf16x8 eye0 = eye_b(0, h, l32), eye1 = eye_b(1, h, l32);
+    // scalar family: K^T and V^T fragments straight from the token-major tiles with the
+    // transposing read.  Lane l (16-lane group g16 = l / 16, lane j = l % 16 in it, read
+    // row a = j / 4, column piece b = j % 4) addresses token 8 (g16 / 2) + 4r + a of the
+    // k-step's 16 (read r = 0, 1) and channel 32w + 16 (g16 % 2) + 4b (value column
+    // 32 jb + 16 (g16 % 2) + 4b); the swizzle terms do not depend on the k-step, whose
+    // offset is added per read.  Output: lane l's fragment of channel (column) l % 32,
+    // tokens 16 ks + 8h + 0..7.
+    int kofs[2], vofs[2][NJB];
+    {
+        const int g16 = l >> 4, j = l & 15, ra = j >> 2, rb = j & 3;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int t = 8 * (g16 >> 1) + 4 * r + ra;
+            const int ch = 32 * w + 16 * (g16 & 1) + 4 * rb;
+            kofs[r] = kmo(t, ch >> 3) + (ch & 7);
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                const int cv = 32 * jb + 16 * (g16 & 1) + 4 * rb;
+                vofs[r][jb] = vmo<NJB>(t, cv >> 3) + (cv & 7);
+            }
+        }
+    }
 
     for (int64_t c = 0; c < DIST && c < nc; ++c) HYPIC_SD_ISSUE(c);
 
@@ -340,46 +385,58 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
 #pragma unroll
                     for (int jb = 0; jb < NJB; ++jb) st[jb][4 * qq + e] *= f[e];
             }
+            // ---- K^T of this wave's 32 key channels (A operands), scaled per element
+            bf16x8 ka[4];
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                f32x16 dk;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    dk = mfma(lds8(&B.Km[kmo(32 * tb + lv32, 4 * w + 2 * ks + hv)]), ks == 0 ? eye0 : eye1,
+                              ks == 0 ? f32x16{} : dk);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dk[r] *= kfac[tb][r];
+                ka[2 * tb] = pack8(dk, 0);
+                ka[2 * tb + 1] = pack8(dk, 1);
+            }
+            // ---- per value block: V^T (B operands) scaled per token, then S += K^T V
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    f32x16 dv;
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        dv = mfma(lds8(&B.Vm[vmo<NJB>(32 * tb + lv32, 4 * jb + 2 * ks + hv)]), ks == 0 ? eye0 : eye1,
+                                  ks == 0 ? f32x16{} : dv);
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const float4 s4 = *reinterpret_cast<const float4 *>(&sm.wsc[w][32 * tb + 8 * qq + 4 * hv]);
+                        dv[4 * qq] *= s4.x; dv[4 * qq + 1] *= s4.y; dv[4 * qq + 2] *= s4.z; dv[4 * qq + 3] *= s4.w;
+                    }
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) st[jb] = mfma(ka[2 * tb + half], pack8(dv, half), st[jb]);
+                }
+            }
         } else {
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) st[jb][r] *= eGv;
-        }
-
-        // ---- K^T of this wave's 32 key channels (A operands), scaled per element for DIAG
-        bf16x8 ka[4];
+            // ---- S += K^T diag(beta e^{G-g}) V, 16 tokens per k-step; the per-token
+            //      weights go onto the K^T fragment (one scaling serves every value block)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            f32x16 dk;
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 kr = tr_pair(&B.Km[kofs[0] + 16 * ks * D], &B.Km[kofs[1] + 16 * ks * D]);
+                const float4 w0 = *reinterpret_cast<const float4 *>(&sm.wsc[w][16 * ks + 8 * hv]);
+                const float4 w1 = *reinterpret_cast<const float4 *>(&sm.wsc[w][16 * ks + 8 * hv + 4]);
+                const bf16x8 ka = scale8(kr, w0, w1);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                dk = mfma(lds8(&B.Km[kmo(32 * tb + lv32, 4 * w + 2 * ks + hv)]), ks == 0 ? eye0 : eye1,
-                          ks == 0 ? f32x16{} : dk);
-            if (DIAG) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) dk[r] *= kfac[tb][r];
-            }
-            ka[2 * tb] = pack8(dk, 0);
-            ka[2 * tb + 1] = pack8(dk, 1);
-        }
-        // ---- per value block: V^T (B operands) scaled per token, then S += K^T V
-#pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) {
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                f32x16 dv;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    dv = mfma(lds8(&B.Vm[vmo<NJB>(32 * tb + lv32, 4 * jb + 2 * ks + hv)]), ks == 0 ? eye0 : eye1,
-                              ks == 0 ? f32x16{} : dv);
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const float4 s4 = *reinterpret_cast<const float4 *>(&sm.wsc[w][32 * tb + 8 * qq + 4 * hv]);
-                    dv[4 * qq] *= s4.x; dv[4 * qq + 1] *= s4.y; dv[4 * qq + 2] *= s4.z; dv[4 * qq + 3] *= s4.w;
+                for (int jb = 0; jb < NJB; ++jb) {
+                    const bf16x8 vb = tr_pair(&B.Vm[vofs[0][jb] + 16 * ks * 32 * NJB],
+                                              &B.Vm[vofs[1][jb] + 16 * ks * 32 * NJB]);
+                    st[jb] = mfma(ka, vb, st[jb]);
                 }
-#pragma unroll
-                for (int half = 0; half < 2; ++half) st[jb] = mfma(ka[2 * tb + half], pack8(dv, half), st[jb]);
             }
         }
     }
