@@ -179,8 +179,8 @@ __device__ __forceinline__ float4 tok4(const float *v, int mb, int q, int h) {
 // fp32, the merge to 32 on the MFMA); each level writes its part of
 // -T0 diag(beta) (P) and D T0 D^{-1} diag(beta) (S) into TB[par] in bf16.
 // TB's upper triangles are zeroed once per segment and never written here.
-// Part 1 (levels 0 and 1) runs in phase a right after the Gram block, part 2
-// (level 2 and the merge) in phase b; TB is double-buffered by chunk parity, so
+// Part 1 (level 0) runs in phase a right after the Gram block, part 2 (levels 1
+// and 2 and the merge) in phase b; TB is double-buffered by chunk parity, so
 // the writes may land while the state waves read the previous chunk's factors.
 struct InvCtx {
     float *M, *tmp;
@@ -214,7 +214,7 @@ __device__ __forceinline__ void inv_put4(const InvCtx &v, int r, int c, float4 x
 }
 
 __device__ __forceinline__ void prep_invert1(const InvCtx &v, int l) {
-    float *M = v.M, *tmp = v.tmp;
+    float *M = v.M;
     if (l < 32) {
         // level 0: the 4x4 diagonal block o = 16 (l / 16) + 4 ((l / 4) % 4) in closed form;
         // lane row i = l % 4
@@ -233,6 +233,10 @@ __device__ __forceinline__ void prep_invert1(const InvCtx &v, int l) {
         inv_put4(v, o + i, o, x);
     }
     wave_lds_sync();
+}
+
+__device__ __forceinline__ void prep_invert2(const InvCtx &v, int l) {
+    float *M = v.M, *tmp = v.tmp;
     {
         // level 1 (4 -> 8): T_10 = -T_11 (A_10 T_00); merge m = l / 16 at
         // o = 16 (m / 2) + 8 (m % 2); output (i, j) of the 4x4 block T_10 at rows
@@ -250,10 +254,6 @@ __device__ __forceinline__ void prep_invert1(const InvCtx &v, int l) {
         inv_put(v, o + 4 + i, o + j, x);
     }
     wave_lds_sync();
-}
-
-__device__ __forceinline__ void prep_invert2(const InvCtx &v, int l) {
-    float *M = v.M, *tmp = v.tmp;
     {
         // level 2 (8 -> 16): merge m = l / 32 at R = 16 m; lane outputs (i, j), (i, j + 1)
         // of the 8x8 block T_10 at rows R + 8 + i, columns R + j
