@@ -28,7 +28,7 @@
 //    of the 32x32 diagonal blocks (4x4 forward substitution and fp32 merges
 //    up to 16, one 16 -> 32 merge on the MFMA), written as T diag(beta) in
 //    bf16 by each level as it finishes; prep wave 0 also loads keys and
-//    values into LDS.  K^T is turned around by the state waves in phase b.
+//    values into LDS.  Prep waves 4 and 6 turn K^T around for the update in phase b.
 // Two workgroup barriers per chunk: in phase a the state waves finish chunk
 // c - 1 (solve, update) while the prep waves compute A of chunk c; in phase b
 // the state waves form W of chunk c while the prep waves invert.
@@ -118,6 +118,13 @@ __device__ __forceinline__ s16x4 pack4(float a0, float a1, float a2, float a3) {
 __device__ __forceinline__ bf16x8 lds8(const u16 *p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
 }
+
+// Workgroup barrier that orders LDS only: this wave's ds_* operations complete before
+// it arrives, nothing else is waited for.  (A workgroup-scope release fence would also
+// wait for the wave's outstanding global_load_lds, which are consumed one phase later
+// and waited for explicitly then.)  The memory clobber keeps the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void phase_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Order this wave's LDS writes before its later LDS reads (the lanes of a wave
 // run in lockstep, so no workgroup barrier is needed when only this wave reads).
@@ -307,6 +314,26 @@ __device__ __forceinline__ void prep_invert2(const InvCtx &v, int l) {
         f32x4 t10 = {0.f, 0.f, 0.f, 0.f};
         t10 = mfma16(tt, nt, t10);
         inv_put4(v, 16 + c16, k4, make_float4(t10[0], t10[1], t10[2], t10[3]));
+    }
+}
+
+// Phase b, prep waves 0 and 2: K^T of chunk c for the next update, blocks (tokens
+// 32 tb, channels 32 ib) idx = 4 q .. 4 q + 3, turned around on the MFMA (X . I) and
+// stored channel-major.
+__device__ __forceinline__ void prep_kt(Smem &sm, int b, int q, int l) {
+    const int h = l >> 5, l32 = l & 31;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int idx = 4 * q + u, tb = idx >> 2, ib = idx & 3;
+        f32x16 kk;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            kk = mfma(lds8(&sm.Km[b][kmo(32 * tb + l32, 4 * ib + 2 * ks + h)]), eye_b(ks, h, l32),
+                      ks == 0 ? f32x16{} : kk);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<u32x2 *>(&sm.Kt[(32 * ib + l32) * KTL + 32 * tb + 8 * r + 4 * h]) =
+                u32x2{pack2(kk[4 * r], kk[4 * r + 1]), pack2(kk[4 * r + 2], kk[4 * r + 3])};
     }
 }
 
@@ -514,25 +541,10 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                         for (int cb = 0; cb < 2; ++cb) st[cb][mb] = mfma(kt[mb], yb[s2][cb], st[cb][mb]);
                 }
             }
-            __syncthreads();                                        // a -> b
+            phase_barrier();                                        // a -> b
             // ---- phase b: W of chunk i
             if (i < nc) {
                 const int b = (int)(i & 1);
-                // K^T of chunk i for the next update: blocks (tokens 32 tb, channels 32 ib),
-                // two per state wave, turned around on the MFMA
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int idx = 2 * w + u, tb = idx >> 2, ib = idx & 3;
-                    f32x16 kk;
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        kk = mfma(lds8(&sm.Km[b][kmo(32 * tb + l32, 4 * ib + 2 * ks + h)]), eye_b(ks, h, l32),
-                                  ks == 0 ? f32x16{} : kk);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<u32x2 *>(&sm.Kt[(32 * ib + l32) * KTL + 32 * tb + 8 * q + 4 * h]) =
-                            u32x2{pack2(kk[4 * q], kk[4 * q + 1]), pack2(kk[4 * q + 2], kk[4 * q + 3])};
-                }
                 f32x16 z[2][2];                   // [column block][token block], rows swizzled
                 // K X: A operand = Km rows (tokens) swz(32 mb + lane), B = state rows in swizzled order
 #pragma unroll
@@ -687,11 +699,12 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     sig = fold ? 1.0f : sp;
                     ell += (double)la_i;
                 }
-                __syncthreads();                                    // a -> b
+                phase_barrier();                                    // a -> b
                 // ---- phase b: keys and values of chunk i + 1 land in the other buffers;
                 //      gates of chunk i + 1 (read in phase b, so that their wait falls at
                 //      its end); factors of block 0 of the P system
                 if (i + 1 < nc) HYPIC_FETCH_G((i + 1) * CH);
+                if (i < nc) prep_kt(sm, (int)(i & 1), 0, l);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // chunk i + 1 has landed
                 __syncthreads();                                    // b -> next a
             }
@@ -718,9 +731,10 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                         prep_invert1(inv_ctx(sm, b, pw >> 1, pw), l);
                     }
                 }
-                __syncthreads();                                    // a -> b
+                phase_barrier();                                    // a -> b
                 if (i + 1 < nc) HYPIC_FETCH_G((i + 1) * CH);        // gates of chunk i + 1
                 if (i < nc && pw != 2) prep_invert2(inv_ctx(sm, (int)(i & 1), pw >> 1, pw), l);
+                if (i < nc && pw == 2) prep_kt(sm, (int)(i & 1), 1, l);
                 __syncthreads();                                    // b -> next a
             }
         }
