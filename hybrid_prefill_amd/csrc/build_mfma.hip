@@ -119,13 +119,6 @@ __device__ __forceinline__ bf16x8 lds8(const u16 *p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
 }
 
-// Workgroup barrier that orders LDS only: this wave's ds_* operations complete before
-// it arrives, nothing else is waited for.  (A workgroup-scope release fence would also
-// wait for the wave's outstanding global_load_lds, which are consumed one phase later
-// and waited for explicitly then.)  The memory clobber keeps the compiler from moving
-// LDS accesses across it.
-__device__ __forceinline__ void phase_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // Order this wave's LDS writes before its later LDS reads (the lanes of a wave
 // run in lockstep, so no workgroup barrier is needed when only this wave reads).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -541,7 +534,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                         for (int cb = 0; cb < 2; ++cb) st[cb][mb] = mfma(kt[mb], yb[s2][cb], st[cb][mb]);
                 }
             }
-            phase_barrier();                                        // a -> b
+            lds_barrier();                                          // a -> b
             // ---- phase b: W of chunk i
             if (i < nc) {
                 const int b = (int)(i & 1);
@@ -699,7 +692,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     sig = fold ? 1.0f : sp;
                     ell += (double)la_i;
                 }
-                phase_barrier();                                    // a -> b
+                lds_barrier();                                      // a -> b
                 // ---- phase b: keys and values of chunk i + 1 land in the other buffers;
                 //      gates of chunk i + 1 (read in phase b, so that their wait falls at
                 //      its end); factors of block 0 of the P system
@@ -731,7 +724,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                         prep_invert1(inv_ctx(sm, b, pw >> 1, pw), l);
                     }
                 }
-                phase_barrier();                                    // a -> b
+                lds_barrier();                                      // a -> b
                 if (i + 1 < nc) HYPIC_FETCH_G((i + 1) * CH);        // gates of chunk i + 1
                 if (i < nc && pw != 2) prep_invert2(inv_ctx(sm, (int)(i & 1), pw >> 1, pw), l);
                 if (i < nc && pw == 2) prep_kt(sm, (int)(i & 1), 1, l);

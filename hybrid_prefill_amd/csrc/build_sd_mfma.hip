@@ -307,7 +307,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         // this wave's loads of chunk c have landed once at most the later chunks' remain
         if (c + 1 < nc && DIST > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();                              // chunk c visible; chunk c - 1's buffer free
+        lds_barrier();                                // chunk c visible; chunk c - 1's buffer free
         if (c + DIST < nc) HYPIC_SD_ISSUE(c + DIST);
 
         const SdBuf<DIAG, NJB> &B = sm.buf[c % NBUF];

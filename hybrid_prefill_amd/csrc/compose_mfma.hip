@@ -219,14 +219,14 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
             *reinterpret_cast<u32x2 *>(&ps.lo[slot]) = u32x2{l01, l23};
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this wave's S_c pieces have landed
-        __syncthreads();
+        lds_barrier();
         float sadd[4][16];
         if (!MODE_P) {
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
                 for (int q = 0; q < 16; ++q) sadd[mb][q] = ps.s[(32 * mb + acc_row(q, h)) * D + col0 + l32];
-            __syncthreads();                                   // S_c read by all before S_{c+1} lands
+            lds_barrier();                                     // S_c read by all before S_{c+1} lands
         }
         if (c + 1 < c_hi) {                                    // the next record flies during this product
             HYPIC_FETCH_P(c + 1);
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
                 for (int q = 0; q < 16; ++q) st[mb][q] = sc * acc[mb][q] + sadd[mb][q];
         }
         ell += (double)le;
-        __syncthreads();     // everyone is done with this P before the next is staged
+        lds_barrier();       // everyone is done with this P before the next is staged
     }
 #undef HYPIC_FETCH_P
 #undef HYPIC_FETCH_S
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
         }                                                                                           \
         const float le_ = EL;                                                                       \
         EL = chain_ell(cs, a, c_lo, more_ ? c + 2 : c, head);          \
-        __syncthreads();                                                                            \
+        lds_barrier();                                                                              \
         f32x16 acc_ = {}, acc1_ = {};                                                               \
         _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) {                                          \
             const int f_ = (w * 8 + kb) * FRAG_U32 + lane_slot(l32, h);                             \

@@ -62,4 +62,11 @@ __device__ __forceinline__ void raise_flag(uint32_t *flag, uint32_t bits) {
     if (flag) atomicOr(flag, bits);
 }
 
+// Workgroup barrier that orders LDS only: the wave's ds_* operations complete before
+// it arrives; outstanding vector-memory loads (prefetches into registers, and
+// global_load_lds whose data is consumed later and waited for explicitly by vmcnt)
+// keep flying.  __syncthreads's workgroup-scope fence would wait for all of them.
+// The memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace hypic
