@@ -45,7 +45,7 @@ CHUNK = 64
 # (scaled by the copy-kernel calibration); None until measured for the current kernel.
 # HBM bytes per launch of the GDN build on the main workload (rocprofv3 FETCH_SIZE and
 # WRITE_SIZE, each scaled by what the counter reads for a copy of known size: read
-# 604.3 MB + write 67.1 MB); None whenever the kernel changed since the counters were taken
+# 604.4 MB + write 67.1 MB); None whenever the kernel changed since the counters were taken
 TRAFFIC_GDN_BUILD = 671.5e6
 
 
