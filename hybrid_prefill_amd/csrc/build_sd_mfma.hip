@@ -12,7 +12,12 @@
 // cumulative g and chunk total G this is
 //     S <- e^{G} S + K^T diag(beta e^{G-g}) V            (scalar)
 //     S <- diag(e^{G}) S + (e^{G-g} . K)^T diag(beta) V  (diagonal, per key channel)
-// i.e. one 128 x 128 x 64 contraction per chunk.  The arithmetic intensity is
+// i.e. one 128 x 128 x 64 contraction per chunk.  The scalar family needs no
+// per-chunk rescale at all: over a block of up to 2048 tokens with total G_b,
+//     S <- e^{G_b} S + sum_t beta_t e^{G_b - L_t} k_t v_t^T
+// (L_t cumulative from the block start), so the weights of a whole block are
+// computed once, before its chunks, into an LDS table, and each chunk only
+// reads them.  The arithmetic intensity is
 // 64 FLOP/B (scalar) and 32 FLOP/B (diagonal, whose fp32 gates double the
 // bytes), so the build is bound by HBM; the contraction runs on bf16 MFMA so
 // that the VALU is free for the scale factors.
@@ -25,12 +30,14 @@
 // layout of V^T with the same token order (diagonal family).  The scalar family
 // reads both fragments straight from the token-major tiles with gfx950's
 // transposing LDS read (ds_read_b64_tr_b16) and puts the per-token weights on
-// the K^T fragment, so its chunk is four MFMAs per value block.  Every wave
+// the K^T fragment, so its chunk is four MFMAs per value block; every operand
+// read of a chunk is issued before its first product.  Every wave
 // takes what it needs (its own 32 key channels, all of the workgroup's value
 // columns), so the waves share nothing but the staged tiles.
 //
-// Streaming: keys, values and gates go from HBM straight into LDS
-// (global_load_lds), NBUF chunks deep; one workgroup barrier per chunk.  Tail
+// Streaming: keys, values (and the diagonal family's gates and beta) go from
+// HBM straight into LDS (global_load_lds), NBUF chunks deep; one workgroup
+// barrier per chunk.  Tail
 // rows past the segment repeat its last row and are masked at use (beta and
 // log alpha of those tokens read as 0).
 #include "hypic_internal.h"
@@ -81,13 +88,29 @@ __device__ __forceinline__ bf16x8 scale8(bf16x8 x, float4 f0, float4 f1) {
     return __builtin_convertvector(s, bf16x8);
 }
 
-// global_load_lds through non-template helpers: called directly from the kernel
-// template, the builtin's LDS-pointer argument keeps the host pass from emitting
-// the launch stubs.  Lane i of the wave lands its bytes at dst + size * i.
-__device__ __forceinline__ void gll16(const void *src, void *dst) {
-    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+// global_load_lds (lane i of the wave lands its bytes at dst + size * i), issued
+// through inline asm: the compiler then sees no LDS write in flight, so it puts
+// no s_waitcnt vmcnt(0) in front of every LDS read (which would wait for the
+// chunks still being prefetched); the kernel counts its own loads instead (every
+// wave issues the same number per chunk, and loads complete in issue order).
+__device__ __forceinline__ uint32_t lds_off(const void *p) {
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
 }
-__device__ __forceinline__ void gll4(const void *src, void *dst) { __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0); }
+__device__ __forceinline__ void gll16(const void *src, void *dst) {
+    uint32_t keep;     // m0 is the compiler's: restored after the load
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep)
+                 : "v"(src), "s"(lds_off(dst))
+                 : "memory");
+}
+__device__ __forceinline__ void gll4(const void *src, void *dst) {
+    uint32_t keep;     // m0 is the compiler's: restored after the load
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep)
+                 : "v"(src), "s"(lds_off(dst))
+                 : "memory");
+}
 
 // B operand of the identity for k-step ks (column l32, rows 16 ks + 8h + e).
 __device__ __forceinline__ bf16x8 eye_b(int ks, int h, int l32) {
@@ -127,15 +150,21 @@ template <bool DIAG, int NJB>
 struct __align__(16) SdBuf {
     u16 Km[CH * D];
     u16 Vm[CH * 32 * NJB];
-    float gate[DIAG ? CH * D : CH];      // diagonal: [token][channel]; scalar: [token]
-    float beta[CH];
-    float dummy[CH];                     // target of the loads that keep per-wave load counts equal
+    // diagonal family only (the scalar family reads its gates once per table block)
+    float gate[DIAG ? CH * D : 4];       // [token][channel]
+    float beta[DIAG ? CH : 4];
+    float dummy[DIAG ? CH : 4];          // target of the loads that keep per-wave load counts equal
 };
+
+constexpr int TBT = 2048;                // tokens per scalar weight table
 
 template <bool DIAG, int NJB, int NBUF>
 struct __align__(16) SdSmem {
     SdBuf<DIAG, NJB> buf[NBUF];
-    float wsc[4][CH];                    // per wave: scalar beta e^{G-g}; diagonal beta
+    float wsc[4][DIAG ? CH : 1];         // per wave: diagonal beta
+    float wt[DIAG ? 4 : TBT];            // scalar: beta_t e^{G_b - L_t} of the current table block
+    float wtot[4];                       // scalar: per-wave sums while a table is built
+    double ellw[4];                      // scalar: per-wave ell
     float gd[4][DIAG ? 32 : 1];          // diagonal, per wave: chunk decay G_i of its channels
     float tot[4][2][32][DIAG ? 8 : 1];   // diagonal, per wave: token-group sums of each lane half
     int64_t t0, n;
@@ -149,14 +178,29 @@ __device__ __forceinline__ int vmo(int r, int g) {
     return r * 32 * NJB + ((g ^ ((r >> SH) & (4 * NJB - 1))) << 3);
 }
 
+// s_waitcnt vmcnt(k LPW) for a wave-uniform k <= K (the count must be an immediate)
+template <int LPW, int K>
+__device__ __forceinline__ void wait_chunks(int k) {
+    if constexpr (K == 0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+        if (k >= K) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K * LPW) : "memory");
+        else wait_chunks<LPW, K - 1>(k);
+    }
+}
+
 template <int FAM, int NSPLIT>
 __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) void sd_build_mfma_kernel(BuildArgs a) {
     constexpr bool DIAG = FAM == HYPIC_DIAGONAL;
     constexpr int NJB = 4 / NSPLIT;                    // 32-column value blocks per workgroup
-    constexpr int NBUF = DIAG ? 2 : 3;                 // chunks staged (DIAG: fp32 gates are big)
+    // chunks staged: as many as fit beside the other workgroup on the CU (value
+    // split 4: two per CU) or alone (diagonal: the fp32 gates are big)
+    constexpr int NBUF = DIAG ? 2 : NSPLIT == 4 ? 3 : NSPLIT == 2 ? 5 : 4;
     constexpr int DIST = NBUF - 1;                     // prefetch distance in chunks
-    // global_load_lds instructions per wave per chunk: keys, values, gates, beta (+dummy)
-    constexpr int LPW = 4 + NJB + (DIAG ? 8 : 1) + 1;
+    // global_load_lds instructions per wave per chunk: keys, values, and for the
+    // diagonal family its gates and one dword row (beta or a dummy)
+    constexpr int LPW = 4 + NJB + (DIAG ? 9 : 0);
+    constexpr int TBC = TBT / CH;                      // chunks per scalar weight table
     __shared__ SdSmem<DIAG, NJB, NBUF> sm;
 
     const int th = threadIdx.x;
@@ -201,7 +245,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     if (a.la_st > mst) mst = a.la_st;
     if (a.b_st > mst) mst = a.b_st;
     const bool small_st = (int64_t)CH * mst < (1LL << 30);
-    uint32_t ko[4], vo[NJB], go[DIAG ? 8 : 1], to_b, to_l;
+    uint32_t ko[4], vo[NJB], go[DIAG ? 8 : 1], to_b;
     {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -219,7 +263,6 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
             go[j] = small_st ? (uint32_t)(r * a.la_st + 4 * (l & 31)) : 0u;
         }
         to_b = small_st ? (uint32_t)(l * a.b_st) : 0u;
-        to_l = small_st ? (uint32_t)(l * a.la_st) : 0u;
     }
 #define HYPIC_SD_ISSUE(C)                                                                            \
     do {                                                                                             \
@@ -236,9 +279,10 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
                     gll16(gh ? gh + base_ * a.la_st + go[j] : (const float *)a.k,                    \
                           &sm.buf[bi_].gate[2 * (8 * w + j) * D]);                                   \
             }                                                                                        \
-            if (w == 0 && bh) gll4(bh + base_ * a.b_st + to_b, sm.buf[bi_].beta);                    \
-            else if (!DIAG && w == 1 && gh) gll4(gh + base_ * a.la_st + to_l, sm.buf[bi_].gate);     \
-            else gll4(a.k, sm.buf[bi_].dummy);                                                       \
+            if (DIAG) {                                                                              \
+                if (w == 0 && bh) gll4(bh + base_ * a.b_st + to_b, sm.buf[bi_].beta);                \
+                else gll4(a.k, sm.buf[bi_].dummy);                                                   \
+            }                                                                                        \
         } else {                                                                                     \
             const int cl_ = rem_ < CH ? (int)rem_ : CH;                                              \
             int ll = l;                                                                              \
@@ -263,11 +307,12 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
                           &sm.buf[bi_].gate[2 * u * D]);                                             \
                 }                                                                                    \
             }                                                                                        \
-            /* one dword per lane: wave 0 beta, wave 1 (scalar) log alpha, the rest a dummy */       \
-            const int rs = ll < cl_ ? ll : cl_ - 1;                                                  \
-            if (w == 0 && bh) gll4(bh + (base_ + rs) * a.b_st, sm.buf[bi_].beta);                    \
-            else if (!DIAG && w == 1 && gh) gll4(gh + (base_ + rs) * a.la_st, sm.buf[bi_].gate);     \
-            else gll4(a.k, sm.buf[bi_].dummy);                                                       \
+            if (DIAG) {                                                                              \
+                /* one dword per lane: wave 0 beta, the rest a dummy */                              \
+                const int rs = ll < cl_ ? ll : cl_ - 1;                                              \
+                if (w == 0 && bh) gll4(bh + (base_ + rs) * a.b_st, sm.buf[bi_].beta);                \
+                else gll4(a.k, sm.buf[bi_].dummy);                                                   \
+            }                                                                                        \
         }                                                                                            \
     } while (0)
 
@@ -276,7 +321,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[jb][r] = 0.f;
-    double ell = 0.0;   // scalar: wave 0, one token per lane; diagonal: this lane's tokens of channel 32w + l32
+    double ell = 0.0;   // scalar: this thread's table tokens; diagonal: this lane's tokens of channel 32w + l32
     const bf16x8 eye0 = eye_b(0, h, l32), eye1 = eye_b(1, h, l32);
     // scalar family: K^T and V^T fragments straight from the token-major tiles with the
     // transposing read.  Lane l (16-lane group g16 = l / 16, lane j = l % 16 in it, read
@@ -301,14 +346,71 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         }
     }
 
-    for (int64_t c = 0; c < DIST && c < nc; ++c) HYPIC_SD_ISSUE(c);
+    // Scalar family: the weight table of tokens [tb0, min(tb0 + TBT, n)); thread th
+    // takes tokens tb0 + 8 th + 0..7 (inclusive prefix in the thread, then over the
+    // wave with DPP, then over the waves through LDS).  Returns the block's G_b and
+    // adds the thread's log alphas into ell.  Every thread calls it.
+    auto make_table = [&](int64_t tb0) -> float {
+        if constexpr (DIAG) return 0.0f;
+        const int64_t tb1 = tb0 + TBT < n ? tb0 + TBT : n;
+        float la8[8], b8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t t = tb0 + 8 * th + e;
+            const bool ok = t < tb1;
+            la8[e] = (ok && gh) ? gh[t * a.la_st] : 0.0f;
+            b8[e] = ok ? (bh ? bh[t * a.b_st] : 1.0f) : 0.0f;
+        }
+        float run = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ell += (double)la8[e];
+            run += la8[e];
+            la8[e] = run;
+        }
+        const float incl = wave_prefix_sum(run);
+        if (l == 63) sm.wtot[w] = incl;
+        lds_barrier();
+        float woff = 0.0f, G = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float x = sm.wtot[u];
+            woff += u < w ? x : 0.0f;
+            G += x;
+        }
+        const float base = woff + incl - run;         // cumulative before this thread's tokens
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.wt[8 * th + e] = b8[e] * __expf(G - (base + la8[e]));
+        lds_barrier();                                // table visible; wtot free again
+        return G;
+    };
+
+    if (!DIAG) {
+        // chunk 0's loads first, then the first table (its global reads overlap them),
+        // then the rest of the prologue
+        if (nc > 0) HYPIC_SD_ISSUE(0);
+        make_table(0);
+        for (int64_t c = 1; c < DIST && c < nc; ++c) HYPIC_SD_ISSUE(c);
+    } else {
+        for (int64_t c = 0; c < DIST && c < nc; ++c) HYPIC_SD_ISSUE(c);
+    }
 
     for (int64_t c = 0; c < nc; ++c) {
         // this wave's loads of chunk c have landed once at most the later chunks' remain
-        if (c + 1 < nc && DIST > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        {
+            const int64_t later = nc - 1 - c;
+            wait_chunks<LPW, DIST - 1>(later < DIST - 1 ? (int)later : DIST - 1);
+        }
         lds_barrier();                                // chunk c visible; chunk c - 1's buffer free
         if (c + DIST < nc) HYPIC_SD_ISSUE(c + DIST);
+        if (!DIAG && c > 0 && c % TBC == 0) {
+            // a new table block: carry the state into it (every wave is past chunk c - 1)
+            const float eG = __expf(make_table(c * CH));
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) st[jb][r] *= eG;
+        }
 
         const SdBuf<DIAG, NJB> &B = sm.buf[c % NBUF];
         const int64_t rem = n - c * CH;
@@ -317,18 +419,10 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         asm volatile("" : "+v"(thv));
         const int lv = thv & 63, hv = lv >> 5, lv32 = lv & 31;
 
-        // ---- per-token factors (lane = token), masked past the segment
-        const float bt = lv < cl ? (a.beta ? B.beta[lv] : 1.0f) : 0.0f;
         float kfac[2][16];                            // diagonal: e^{G_i - g_{t,i}} per key element
-        float eGv = 0.f;                              // scalar: e^G
-        if (!DIAG) {
-            const float lat = (lv < cl && a.log_alpha) ? B.gate[lv] : 0.0f;
-            const float gv = wave_prefix_sum(lat);
-            const float G = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 63));
-            sm.wsc[w][lv] = bt * __expf(G - gv);
-            eGv = __expf(G);
-            if (w == 0) ell += (double)lat;
-        } else {
+        if (DIAG) {
+            // ---- per-token factors (lane = token), masked past the segment
+            const float bt = lv < cl ? (a.beta ? B.beta[lv] : 1.0f) : 0.0f;
             sm.wsc[w][lv] = bt;
             // channel i = 32w + lv32; this lane's tokens 32 tb + 8 qq + 4 hv + e, in groups of 4
             const int i = 32 * w + lv32;
@@ -371,8 +465,8 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
 #pragma unroll
                     for (int e = 0; e < 4; ++e) kfac[tb][4 * qq + e] = __expf(G - x[tb][qq][e]);
             if (hv == 0) sm.gd[w][lv32] = G;
+            wave_lds_sync();
         }
-        wave_lds_sync();
 
         // ---- decay of the carried state
         if (DIAG) {
@@ -419,24 +513,27 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
                 }
             }
         } else {
-#pragma unroll
-            for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) st[jb][r] *= eGv;
-            // ---- S += K^T diag(beta e^{G-g}) V, 16 tokens per k-step; the per-token
-            //      weights go onto the K^T fragment (one scaling serves every value block)
+            // ---- S += K^T diag(w) V with the table's weights, 16 tokens per k-step; the
+            //      weights go onto the K^T fragment (one scaling serves every value block).
+            //      Every operand read is issued before the first product.
+            const float *wrow = &sm.wt[CH * (int)(c % TBC)];
+            bf16x8 kr[4], vb[4][NJB];
+            float4 w0[4], w1[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 kr = tr_pair(&B.Km[kofs[0] + 16 * ks * D], &B.Km[kofs[1] + 16 * ks * D]);
-                const float4 w0 = *reinterpret_cast<const float4 *>(&sm.wsc[w][16 * ks + 8 * hv]);
-                const float4 w1 = *reinterpret_cast<const float4 *>(&sm.wsc[w][16 * ks + 8 * hv + 4]);
-                const bf16x8 ka = scale8(kr, w0, w1);
+                kr[ks] = tr_pair(&B.Km[kofs[0] + 16 * ks * D], &B.Km[kofs[1] + 16 * ks * D]);
+                w0[ks] = *reinterpret_cast<const float4 *>(&wrow[16 * ks + 8 * hv]);
+                w1[ks] = *reinterpret_cast<const float4 *>(&wrow[16 * ks + 8 * hv + 4]);
 #pragma unroll
-                for (int jb = 0; jb < NJB; ++jb) {
-                    const bf16x8 vb = tr_pair(&B.Vm[vofs[0][jb] + 16 * ks * 32 * NJB],
-                                              &B.Vm[vofs[1][jb] + 16 * ks * 32 * NJB]);
-                    st[jb] = mfma(ka, vb, st[jb]);
-                }
+                for (int jb = 0; jb < NJB; ++jb)
+                    vb[ks][jb] = tr_pair(&B.Vm[vofs[0][jb] + 16 * ks * 32 * NJB],
+                                         &B.Vm[vofs[1][jb] + 16 * ks * 32 * NJB]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 ka = scale8(kr[ks], w0[ks], w1[ks]);
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) st[jb] = mfma(ka, vb[ks][jb], st[jb]);
             }
         }
     }
@@ -456,10 +553,13 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     if (DIAG) {
         ell += __shfl_xor(ell, 32);        // the two lane halves hold the two token halves
         if (h == 0) a.pool_ell[rec * D + 32 * w + l32] = bad ? nanv : (float)ell;
-    } else if (w == 0) {
+    } else {
+        // every thread summed its table tokens
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) ell += __shfl_xor(ell, o);
-        if (l == 0) a.pool_ell[rec] = bad ? nanv : (float)ell;
+        if (l == 0) sm.ellw[w] = ell;
+        lds_barrier();
+        if (th == 0) a.pool_ell[rec] = bad ? nanv : (float)(sm.ellw[0] + sm.ellw[1] + sm.ellw[2] + sm.ellw[3]);
     }
 }
 
@@ -482,9 +582,10 @@ hipError_t launch_build_sd_mfma(const BuildArgs &a, hipStream_t stream, bool *ta
     // the grid is padded to a multiple of 8 units (padding blocks exit at once)
     const int64_t units = (int64_t)a.num_segments * a.H;
     // (the diagonal family redoes its per-channel gate work in every split, so it
-    // stops at two)
+    // stops at two; the scalar family stages all keys in every split, so it splits
+    // only below 256 units)
     const bool diag = a.family == HYPIC_DIAGONAL;
-    const int nsplit = units >= 1024 ? 1 : units >= 512 ? 2 : diag ? 2 : 4;
+    const int nsplit = diag ? (units >= 1024 ? 1 : 2) : (units >= 256 ? 1 : units >= 128 ? 2 : 4);
     const int64_t padded = (units + 7) / 8 * 8;
     const dim3 grid((unsigned)(padded * nsplit));
 #define HYPIC_SD_LAUNCH(FAM_, NS_) hipLaunchKernelGGL((sd_build_mfma_kernel<FAM_, NS_>), grid, dim3(NT), 0, stream, a)

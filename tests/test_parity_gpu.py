@@ -316,6 +316,33 @@ def test_build_error_flags():
     assert not torch.any(torch.isnan(pool.S[0]))
 
 
+def test_scalar_mfma_build_error_flags():
+    """Scalar family, bf16 d=128 (the MFMA build with its weight table, value
+    split 4): an out-of-range slot leaves every other slot's canary alone;
+    bad offsets give a NaN record beside a finite one."""
+    H, d = 2, 128
+    inp = make_inputs(hp.SCALAR, [100, 300], H, d, d, torch.bfloat16, 711)
+    pool = hp.Pool.allocate(hp.SCALAR, 3, H, d, d, device="cuda", fill=CANARY)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hp.build_segment(hp.SCALAR, inp["k"], inp["v"], inp["la"], dev_i64(inp["offs"]), pool, dev_i32([1, 7]),
+                     err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == hp.EFLAG_SLOT_OUT_OF_RANGE
+    assert torch.all(pool.S[[0, 2]] == CANARY) and torch.all(pool.log_scale[[0, 2]] == CANARY)
+    k, v, la, _ = host_inputs(hp.SCALAR, inp, H)
+    for h in range(H):
+        ell_r, P_r, S_r = oracle_unit(hp.SCALAR, k, v, la, None, 0, 100, h)
+        e = record_errors(hp.SCALAR, np64(pool.log_scale[1, h]), None, np64(pool.S[1, h]), ell_r, P_r, S_r)
+        assert max(e) <= TOL[torch.bfloat16], e
+    err.zero_()
+    hp.build_segment(hp.SCALAR, inp["k"], inp["v"], inp["la"], dev_i64([0, 100, 500]), pool, dev_i32([0, 2]),
+                     err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == hp.EFLAG_BAD_OFFSETS
+    assert torch.all(torch.isnan(pool.S[2])) and torch.all(torch.isnan(pool.log_scale[2]))
+    assert not torch.any(torch.isnan(pool.S[0])) and not torch.any(pool.S[0] == CANARY)
+
+
 # ----------------------------------------------------------------------------- conv warm-up
 
 @pytest.mark.parametrize("K,C,dtype,act,bias", [(4, 4096, torch.bfloat16, 0, False),
