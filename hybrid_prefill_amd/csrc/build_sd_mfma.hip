@@ -22,9 +22,10 @@
 // bytes), so the build is bound by HBM; the contraction runs on bf16 MFMA so
 // that the VALU is free for the scale factors.
 //
-// Work split: NSPLIT 256-thread workgroups per (segment, head), workgroup q
-// keeping value columns [128 q / NSPLIT, 128 (q + 1) / NSPLIT); wave w keeps rows
-// [32w, 32w + 32) of S as fp32 32x32 accumulator tiles.  Keys and values arrive
+// Work split: NSPLIT workgroups per (segment, head) of four compute waves and
+// one loading wave, workgroup q keeping value columns [128 q / NSPLIT,
+// 128 (q + 1) / NSPLIT); compute wave w keeps rows [32w, 32w + 32) of S as fp32
+// 32x32 accumulator tiles.  Keys and values arrive
 // token-major and are turned around on the MFMA itself: X . I returns X's
 // columns in the accumulator layout, which is the A layout of K^T and the B
 // layout of V^T with the same token order (diagonal family).  The scalar family
@@ -35,8 +36,9 @@
 // takes what it needs (its own 32 key channels, all of the workgroup's value
 // columns), so the waves share nothing but the staged tiles.
 //
-// Streaming: keys, values (and the diagonal family's gates and beta) go from
-// HBM straight into LDS (global_load_lds), NBUF chunks deep; one workgroup
+// Streaming: a fifth wave only loads: keys, values (and the diagonal family's
+// gates and beta) go from HBM straight into LDS (global_load_lds), NBUF chunks
+// deep, so the four compute waves never stall on the load queue; one workgroup
 // barrier per chunk.  Tail
 // rows past the segment repeat its last row and are masked at use (beta and
 // log alpha of those tokens read as 0).
@@ -55,7 +57,8 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int CH = 64;
 constexpr int D = 128;
-constexpr int NT = 256;
+constexpr int NWC = 4;           // compute waves; wave NWC loads
+constexpr int NT = 64 * (NWC + 1);
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -163,7 +166,7 @@ struct __align__(16) SdSmem {
     SdBuf<DIAG, NJB> buf[NBUF];
     float wsc[4][DIAG ? CH : 1];         // per wave: diagonal beta
     float wt[DIAG ? 4 : TBT];            // scalar: beta_t e^{G_b - L_t} of the current table block
-    float wtot[4];                       // scalar: per-wave sums while a table is built
+    float wtot[NWC];                     // scalar: per-wave sums while a table is built
     double ellw[4];                      // scalar: per-wave ell
     float gd[4][DIAG ? 32 : 1];          // diagonal, per wave: chunk decay G_i of its channels
     float tot[4][2][32][DIAG ? 8 : 1];   // diagonal, per wave: token-group sums of each lane half
@@ -178,13 +181,14 @@ __device__ __forceinline__ int vmo(int r, int g) {
     return r * 32 * NJB + ((g ^ ((r >> SH) & (4 * NJB - 1))) << 3);
 }
 
-// s_waitcnt vmcnt(k LPW) for a wave-uniform k <= K (the count must be an immediate)
+// s_waitcnt vmcnt(k LPW) for a wave-uniform k <= K (the count must be an immediate;
+// the counter's limit of 63 makes the wait at most a little stricter)
 template <int LPW, int K>
 __device__ __forceinline__ void wait_chunks(int k) {
     if constexpr (K == 0) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
-        if (k >= K) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K * LPW) : "memory");
+        if (k >= K) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K * LPW < 63 ? K * LPW : 63) : "memory");
         else wait_chunks<LPW, K - 1>(k);
     }
 }
@@ -197,9 +201,9 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     // split 4: two per CU) or alone (diagonal: the fp32 gates are big)
     constexpr int NBUF = DIAG ? 2 : NSPLIT == 4 ? 3 : NSPLIT == 2 ? 5 : 4;
     constexpr int DIST = NBUF - 1;                     // prefetch distance in chunks
-    // global_load_lds instructions per wave per chunk: keys, values, and for the
-    // diagonal family its gates and one dword row (beta or a dummy)
-    constexpr int LPW = 4 + NJB + (DIAG ? 9 : 0);
+    // global_load_lds instructions of the loading wave per chunk: keys, values, and
+    // for the diagonal family its gates and one dword row (beta or a dummy)
+    constexpr int LPW = 16 + 4 * NJB + (DIAG ? 33 : 0);
     constexpr int TBC = TBT / CH;                      // chunks per scalar weight table
     __shared__ SdSmem<DIAG, NJB, NBUF> sm;
 
@@ -237,84 +241,61 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     const float *gh = a.log_alpha ? a.log_alpha + t0 * a.la_st + head * a.la_sh : nullptr;
     const float *bh = a.beta ? a.beta + t0 * a.b_st + head * a.b_sh : nullptr;
 
-    // Issue this wave's share of chunk C's loads into buffer C % NBUF.  Every wave
-    // issues exactly LPW instructions (so vmcnt can count chunks).  Full chunks use
-    // per-lane element offsets fixed for the segment; the tail chunk clamps rows.
+    // Loading wave: chunk C's loads into buffer C % NBUF, LPW instructions in a fixed
+    // order (so vmcnt can count chunks).  Full chunks use per-lane element offsets
+    // fixed for the segment; the tail chunk clamps rows (finite values; masked at use).
     constexpr int GR = 4 * NJB, RPI = 64 / GR, VSH = NJB == 1 ? 2 : NJB == 2 ? 1 : 0;
     int64_t mst = a.k_st > a.v_st ? a.k_st : a.v_st;
     if (a.la_st > mst) mst = a.la_st;
     if (a.b_st > mst) mst = a.b_st;
     const bool small_st = (int64_t)CH * mst < (1LL << 30);
-    uint32_t ko[4], vo[NJB], go[DIAG ? 8 : 1], to_b;
-    {
+    auto issue = [&](int64_t C, const uint32_t *ko, const uint32_t *vo, const uint32_t *go) {
+        const int bi = (int)(C % NBUF);
+        const int64_t base = C * CH, rem = n - base;
+        SdBuf<DIAG, NJB> &Bf = sm.buf[bi];
+        if (rem >= CH && small_st) {
+            const u16 *kc = kh + base * a.k_st, *vc = vh + base * a.v_st;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 4 * (4 * w + j) + (l >> 4);
-            ko[j] = small_st ? (uint32_t)(r * a.k_st + 8 * ((l & 15) ^ (r & 15))) : 0u;
-        }
+            for (int u = 0; u < 16; ++u) gll16(kc + ko[u], &Bf.Km[4 * u * D]);
 #pragma unroll
-        for (int j = 0; j < NJB; ++j) {
-            const int r = RPI * (NJB * w + j) + l / GR;
-            vo[j] = small_st ? (uint32_t)(r * a.v_st + 8 * ((l % GR) ^ ((r >> VSH) & (GR - 1)))) : 0u;
-        }
+            for (int u = 0; u < GR; ++u) gll16(vc + vo[u], &Bf.Vm[RPI * u * 32 * NJB]);
+            if (DIAG) {
 #pragma unroll
-        for (int j = 0; j < (DIAG ? 8 : 1); ++j) {
-            const int r = 2 * (8 * w + j) + (l >> 5);
-            go[j] = small_st ? (uint32_t)(r * a.la_st + 4 * (l & 31)) : 0u;
+                for (int u = 0; u < 32; ++u)
+                    gll16(gh ? gh + base * a.la_st + go[u] : (const float *)a.k, &Bf.gate[2 * u * D]);
+                if (bh) gll4(bh + base * a.b_st + go[32], Bf.beta);
+                else gll4(a.k, Bf.dummy);
+            }
+        } else {
+            const int cl = rem < CH ? (int)rem : CH;
+            int ll = l;
+            asm volatile("" : "+v"(ll));
+            // keys: instruction u covers rows 4u .. 4u + 3 (lane: row 4u + ll / 16, slot ll % 16)
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int r = 4 * u + (ll >> 4), rs = r < cl ? r : cl - 1;
+                gll16(kh + (base + rs) * a.k_st + 8 * ((ll & 15) ^ (r & 15)), &Bf.Km[4 * u * D]);
+            }
+            // values: GR granules per row, RPI rows per instruction
+#pragma unroll
+            for (int u = 0; u < GR; ++u) {
+                const int r = RPI * u + ll / GR, rs = r < cl ? r : cl - 1;
+                gll16(vh + (base + rs) * a.v_st + 8 * ((ll % GR) ^ ((r >> VSH) & (GR - 1))),
+                      &Bf.Vm[RPI * u * 32 * NJB]);
+            }
+            if (DIAG) {
+                // gates: 2 rows (512 bytes each) per instruction
+#pragma unroll
+                for (int u = 0; u < 32; ++u) {
+                    const int r = 2 * u + (ll >> 5), rs = r < cl ? r : cl - 1;
+                    gll16(gh ? gh + (base + rs) * a.la_st + 4 * (ll & 31) : (const float *)a.k, &Bf.gate[2 * u * D]);
+                }
+                const int rs = ll < cl ? ll : cl - 1;
+                if (bh) gll4(bh + (base + rs) * a.b_st, Bf.beta);
+                else gll4(a.k, Bf.dummy);
+            }
         }
-        to_b = small_st ? (uint32_t)(l * a.b_st) : 0u;
-    }
-#define HYPIC_SD_ISSUE(C)                                                                            \
-    do {                                                                                             \
-        const int bi_ = (int)((C) % NBUF);                                                           \
-        const int64_t base_ = (C) * CH, rem_ = n - base_;                                            \
-        if (rem_ >= CH && small_st) {                                                                \
-            const u16 *kc_ = kh + base_ * a.k_st, *vc_ = vh + base_ * a.v_st;                        \
-            _Pragma("unroll") for (int j = 0; j < 4; ++j)                                            \
-                gll16(kc_ + ko[j], &sm.buf[bi_].Km[4 * (4 * w + j) * D]);                            \
-            _Pragma("unroll") for (int j = 0; j < NJB; ++j)                                          \
-                gll16(vc_ + vo[j], &sm.buf[bi_].Vm[RPI * (NJB * w + j) * 32 * NJB]);                 \
-            if (DIAG) {                                                                              \
-                _Pragma("unroll") for (int j = 0; j < 8; ++j)                                        \
-                    gll16(gh ? gh + base_ * a.la_st + go[j] : (const float *)a.k,                    \
-                          &sm.buf[bi_].gate[2 * (8 * w + j) * D]);                                   \
-            }                                                                                        \
-            if (DIAG) {                                                                              \
-                if (w == 0 && bh) gll4(bh + base_ * a.b_st + to_b, sm.buf[bi_].beta);                \
-                else gll4(a.k, sm.buf[bi_].dummy);                                                   \
-            }                                                                                        \
-        } else {                                                                                     \
-            const int cl_ = rem_ < CH ? (int)rem_ : CH;                                              \
-            int ll = l;                                                                              \
-            asm volatile("" : "+v"(ll));                                                             \
-            /* keys: instruction u covers rows 4u .. 4u + 3 (lane: row 4u + ll / 16, slot ll % 16) */ \
-            _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                          \
-                const int u = 4 * w + j, r = 4 * u + (ll >> 4), rs = r < cl_ ? r : cl_ - 1;         \
-                const int g = (ll & 15) ^ (r & 15);                                                  \
-                gll16(kh + (base_ + rs) * a.k_st + 8 * g, &sm.buf[bi_].Km[4 * u * D]);               \
-            }                                                                                        \
-            /* values: GR granules per row, RPI rows per instruction */                              \
-            _Pragma("unroll") for (int j = 0; j < NJB; ++j) {                                        \
-                const int u = NJB * w + j, r = RPI * u + ll / GR, rs = r < cl_ ? r : cl_ - 1;        \
-                const int g = (ll % GR) ^ ((r >> VSH) & (GR - 1));                                   \
-                gll16(vh + (base_ + rs) * a.v_st + 8 * g, &sm.buf[bi_].Vm[RPI * u * 32 * NJB]);      \
-            }                                                                                        \
-            if (DIAG) {                                                                              \
-                /* gates: 2 rows (512 bytes each) per instruction, 8 per wave */                     \
-                _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                      \
-                    const int u = 8 * w + j, r = 2 * u + (ll >> 5), rs = r < cl_ ? r : cl_ - 1;      \
-                    gll16(gh ? gh + (base_ + rs) * a.la_st + 4 * (ll & 31) : (const float *)a.k,     \
-                          &sm.buf[bi_].gate[2 * u * D]);                                             \
-                }                                                                                    \
-            }                                                                                        \
-            if (DIAG) {                                                                              \
-                /* one dword per lane: wave 0 beta, the rest a dummy */                              \
-                const int rs = ll < cl_ ? ll : cl_ - 1;                                              \
-                if (w == 0 && bh) gll4(bh + (base_ + rs) * a.b_st, sm.buf[bi_].beta);                \
-                else gll4(a.k, sm.buf[bi_].dummy);                                                   \
-            }                                                                                        \
-        }                                                                                            \
-    } while (0)
+    };
 
     f32x16 st[NJB];
 #pragma unroll
@@ -346,10 +327,11 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         }
     }
 
-    // Scalar family: the weight table of tokens [tb0, min(tb0 + TBT, n)); thread th
-    // takes tokens tb0 + 8 th + 0..7 (inclusive prefix in the thread, then over the
-    // wave with DPP, then over the waves through LDS).  Returns the block's G_b and
-    // adds the thread's log alphas into ell.  Every thread calls it.
+    // Scalar family: the weight table of tokens [tb0, min(tb0 + TBT, n)); compute
+    // thread th takes tokens tb0 + 8 th + 0..7 (inclusive prefix in the thread, then
+    // over the wave with DPP, then over the waves through LDS).  Returns the block's
+    // G_b and adds the thread's log alphas into ell.  Every compute wave calls it; the
+    // loading wave passes its two barriers.
     auto make_table = [&](int64_t tb0) -> float {
         if constexpr (DIAG) return 0.0f;
         const int64_t tb1 = tb0 + TBT < n ? tb0 + TBT : n;
@@ -373,7 +355,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         lds_barrier();
         float woff = 0.0f, G = 0.0f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < NWC; ++u) {
             const float x = sm.wtot[u];
             woff += u < w ? x : 0.0f;
             G += x;
@@ -385,24 +367,51 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         return G;
     };
 
-    if (!DIAG) {
-        // chunk 0's loads first, then the first table (its global reads overlap them),
-        // then the rest of the prologue
-        if (nc > 0) HYPIC_SD_ISSUE(0);
-        make_table(0);
-        for (int64_t c = 1; c < DIST && c < nc; ++c) HYPIC_SD_ISSUE(c);
-    } else {
-        for (int64_t c = 0; c < DIST && c < nc; ++c) HYPIC_SD_ISSUE(c);
-    }
-
-    for (int64_t c = 0; c < nc; ++c) {
-        // this wave's loads of chunk c have landed once at most the later chunks' remain
-        {
+    if (w == NWC) {
+        // ================= loading wave: the same barriers as the compute waves
+        uint32_t ko[16], vo[GR], go[DIAG ? 33 : 1];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int r = 4 * u + (l >> 4);
+            ko[u] = small_st ? (uint32_t)(r * a.k_st + 8 * ((l & 15) ^ (r & 15))) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < GR; ++u) {
+            const int r = RPI * u + l / GR;
+            vo[u] = small_st ? (uint32_t)(r * a.v_st + 8 * ((l % GR) ^ ((r >> VSH) & (GR - 1)))) : 0u;
+        }
+        if (DIAG) {
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                const int r = 2 * u + (l >> 5);
+                go[u] = small_st ? (uint32_t)(r * a.la_st + 4 * (l & 31)) : 0u;
+            }
+            go[DIAG ? 32 : 0] = small_st ? (uint32_t)(l * a.b_st) : 0u;
+        }
+        for (int64_t c = 0; c < DIST && c < nc; ++c) issue(c, ko, vo, go);
+        // make_table's two barriers (this wave has no tokens, and no load to wait for)
+        if (!DIAG) {
+            lds_barrier();
+            lds_barrier();
+        }
+        for (int64_t c = 0; c < nc; ++c) {
+            // chunk c has landed once at most the later chunks' loads remain
             const int64_t later = nc - 1 - c;
             wait_chunks<LPW, DIST - 1>(later < DIST - 1 ? (int)later : DIST - 1);
+            lds_barrier();                            // chunk c visible; chunk c - 1's buffer free
+            if (c + DIST < nc) issue(c + DIST, ko, vo, go);
+            if (!DIAG && c > 0 && c % TBC == 0) {
+                lds_barrier();
+                lds_barrier();
+            }
         }
+        return;
+    }
+
+    // ================= compute waves
+    if (!DIAG) make_table(0);
+    for (int64_t c = 0; c < nc; ++c) {
         lds_barrier();                                // chunk c visible; chunk c - 1's buffer free
-        if (c + DIST < nc) HYPIC_SD_ISSUE(c + DIST);
         if (!DIAG && c > 0 && c % TBC == 0) {
             // a new table block: carry the state into it (every wave is past chunk c - 1)
             const float eG = __expf(make_table(c * CH));
@@ -538,7 +547,6 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         }
     }
 
-#undef HYPIC_SD_ISSUE
     // ---- record
     const float nanv = __int_as_float(0x7fc00000);
     const bool bad = state == 2;
@@ -581,11 +589,11 @@ hipError_t launch_build_sd_mfma(const BuildArgs &a, hipStream_t stream, bool *ta
     // split the value columns over more workgroups while the units alone leave CUs idle;
     // the grid is padded to a multiple of 8 units (padding blocks exit at once)
     const int64_t units = (int64_t)a.num_segments * a.H;
-    // (the diagonal family redoes its per-channel gate work in every split, so it
-    // stops at two; the scalar family stages all keys in every split, so it splits
-    // only below 256 units)
+    // (the diagonal family always splits in two: its whole state plus the per-channel
+    // gate work does not fit the registers a wave has beside the loading wave; the
+    // scalar family stages all keys in every split, so it splits only below 256 units)
     const bool diag = a.family == HYPIC_DIAGONAL;
-    const int nsplit = diag ? (units >= 1024 ? 1 : 2) : (units >= 256 ? 1 : units >= 128 ? 2 : 4);
+    const int nsplit = diag ? 2 : (units >= 256 ? 1 : units >= 128 ? 2 : 4);
     const int64_t padded = (units + 7) / 8 * 8;
     const dim3 grid((unsigned)(padded * nsplit));
 #define HYPIC_SD_LAUNCH(FAM_, NS_) hipLaunchKernelGGL((sd_build_mfma_kernel<FAM_, NS_>), grid, dim3(NT), 0, stream, a)
@@ -594,9 +602,7 @@ hipError_t launch_build_sd_mfma(const BuildArgs &a, hipStream_t stream, bool *ta
         else if (nsplit == 2) HYPIC_SD_LAUNCH(HYPIC_SCALAR, 2);
         else HYPIC_SD_LAUNCH(HYPIC_SCALAR, 4);
     } else {
-        if (nsplit == 1) HYPIC_SD_LAUNCH(HYPIC_DIAGONAL, 1);
-        else if (nsplit == 2) HYPIC_SD_LAUNCH(HYPIC_DIAGONAL, 2);
-        else HYPIC_SD_LAUNCH(HYPIC_DIAGONAL, 4);
+        HYPIC_SD_LAUNCH(HYPIC_DIAGONAL, 2);
     }
 #undef HYPIC_SD_LAUNCH
     return hipGetLastError();
