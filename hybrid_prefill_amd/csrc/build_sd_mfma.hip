@@ -23,7 +23,7 @@
 // that the VALU is free for the scale factors.
 //
 // Work split: NSPLIT workgroups per (segment, head) of four compute waves and
-// one loading wave, workgroup q keeping value columns [128 q / NSPLIT,
+// four loading waves, workgroup q keeping value columns [128 q / NSPLIT,
 // 128 (q + 1) / NSPLIT); compute wave w keeps rows [32w, 32w + 32) of S as fp32
 // 32x32 accumulator tiles.  Keys and values arrive
 // token-major and are turned around on the MFMA itself: X . I returns X's
@@ -36,10 +36,11 @@
 // takes what it needs (its own 32 key channels, all of the workgroup's value
 // columns), so the waves share nothing but the staged tiles.
 //
-// Streaming: a fifth wave only loads: keys, values (and the diagonal family's
+// Streaming: four more waves only load: keys, values (and the diagonal family's
 // gates and beta) go from HBM straight into LDS (global_load_lds), NBUF chunks
-// deep, so the four compute waves never stall on the load queue; one workgroup
-// barrier per chunk.  Tail
+// deep, so the compute waves never stall on the load queue (a single wave
+// cannot issue a chunk's loads as fast as the compute waves use it); one
+// workgroup barrier per chunk.  Tail
 // rows past the segment repeat its last row and are masked at use (beta and
 // log alpha of those tokens read as 0).
 #include "hypic_internal.h"
@@ -57,8 +58,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int CH = 64;
 constexpr int D = 128;
-constexpr int NWC = 4;           // compute waves; wave NWC loads
-constexpr int NT = 64 * (NWC + 1);
+constexpr int NWC = 4;           // compute waves
+constexpr int NLW = 4;           // loading waves (one wave alone cannot issue loads fast enough)
+constexpr int NT = 64 * (NWC + NLW);
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -199,12 +201,19 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     constexpr int NJB = 4 / NSPLIT;                    // 32-column value blocks per workgroup
     // chunks staged: as many as fit beside the other workgroup on the CU (value
     // split 4: two per CU) or alone (diagonal: the fp32 gates are big)
-    constexpr int NBUF = DIAG ? 2 : NSPLIT == 4 ? 3 : NSPLIT == 2 ? 5 : 4;
+    constexpr int NBUF = DIAG ? 2 : NSPLIT == 4 ? 3 : NSPLIT == 2 ? 6 : 4;
     constexpr int DIST = NBUF - 1;                     // prefetch distance in chunks
-    // global_load_lds instructions of the loading wave per chunk: keys, values, and
-    // for the diagonal family its gates and one dword row (beta or a dummy)
-    constexpr int LPW = 16 + 4 * NJB + (DIAG ? 33 : 0);
+    // global_load_lds instructions of each loading wave per chunk: its share of the
+    // keys, values, and for the diagonal family gates, plus one dword row (beta or a
+    // dummy)
+    constexpr int NKI = 16 / NLW, NVI = 4 * NJB / NLW, NGI = DIAG ? 32 / NLW : 0;
+    static_assert(16 % NLW == 0 && (4 * NJB) % NLW == 0 && 32 % NLW == 0, "load shares");
+    constexpr int LPW = NKI + NVI + (DIAG ? NGI + 1 : 0);
     constexpr int TBC = TBT / CH;                      // chunks per scalar weight table
+    // with two value blocks per workgroup the scalar compute waves read a chunk's
+    // operands one chunk ahead (two register sets fit beside the state), so at the
+    // top of chunk c the loading waves have waited for chunk c + 1
+    constexpr int AHEAD = (!DIAG && NJB == 2) ? 1 : 0;
     __shared__ SdSmem<DIAG, NJB, NBUF> sm;
 
     const int th = threadIdx.x;
@@ -249,21 +258,21 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     if (a.la_st > mst) mst = a.la_st;
     if (a.b_st > mst) mst = a.b_st;
     const bool small_st = (int64_t)CH * mst < (1LL << 30);
-    auto issue = [&](int64_t C, const uint32_t *ko, const uint32_t *vo, const uint32_t *go) {
+    auto issue = [&](int64_t C, int lw, const uint32_t *ko, const uint32_t *vo, const uint32_t *go) {
         const int bi = (int)(C % NBUF);
         const int64_t base = C * CH, rem = n - base;
         SdBuf<DIAG, NJB> &Bf = sm.buf[bi];
         if (rem >= CH && small_st) {
             const u16 *kc = kh + base * a.k_st, *vc = vh + base * a.v_st;
 #pragma unroll
-            for (int u = 0; u < 16; ++u) gll16(kc + ko[u], &Bf.Km[4 * u * D]);
+            for (int j = 0; j < NKI; ++j) gll16(kc + ko[j], &Bf.Km[4 * (lw + NLW * j) * D]);
 #pragma unroll
-            for (int u = 0; u < GR; ++u) gll16(vc + vo[u], &Bf.Vm[RPI * u * 32 * NJB]);
+            for (int j = 0; j < NVI; ++j) gll16(vc + vo[j], &Bf.Vm[RPI * (lw + NLW * j) * 32 * NJB]);
             if (DIAG) {
 #pragma unroll
-                for (int u = 0; u < 32; ++u)
-                    gll16(gh ? gh + base * a.la_st + go[u] : (const float *)a.k, &Bf.gate[2 * u * D]);
-                if (bh) gll4(bh + base * a.b_st + go[32], Bf.beta);
+                for (int j = 0; j < NGI; ++j)
+                    gll16(gh ? gh + base * a.la_st + go[j] : (const float *)a.k, &Bf.gate[2 * (lw + NLW * j) * D]);
+                if (lw == 0 && bh) gll4(bh + base * a.b_st + go[NGI], Bf.beta);
                 else gll4(a.k, Bf.dummy);
             }
         } else {
@@ -272,26 +281,26 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
             asm volatile("" : "+v"(ll));
             // keys: instruction u covers rows 4u .. 4u + 3 (lane: row 4u + ll / 16, slot ll % 16)
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int r = 4 * u + (ll >> 4), rs = r < cl ? r : cl - 1;
+            for (int j = 0; j < NKI; ++j) {
+                const int u = lw + NLW * j, r = 4 * u + (ll >> 4), rs = r < cl ? r : cl - 1;
                 gll16(kh + (base + rs) * a.k_st + 8 * ((ll & 15) ^ (r & 15)), &Bf.Km[4 * u * D]);
             }
             // values: GR granules per row, RPI rows per instruction
 #pragma unroll
-            for (int u = 0; u < GR; ++u) {
-                const int r = RPI * u + ll / GR, rs = r < cl ? r : cl - 1;
+            for (int j = 0; j < NVI; ++j) {
+                const int u = lw + NLW * j, r = RPI * u + ll / GR, rs = r < cl ? r : cl - 1;
                 gll16(vh + (base + rs) * a.v_st + 8 * ((ll % GR) ^ ((r >> VSH) & (GR - 1))),
                       &Bf.Vm[RPI * u * 32 * NJB]);
             }
             if (DIAG) {
                 // gates: 2 rows (512 bytes each) per instruction
 #pragma unroll
-                for (int u = 0; u < 32; ++u) {
-                    const int r = 2 * u + (ll >> 5), rs = r < cl ? r : cl - 1;
+                for (int j = 0; j < NGI; ++j) {
+                    const int u = lw + NLW * j, r = 2 * u + (ll >> 5), rs = r < cl ? r : cl - 1;
                     gll16(gh ? gh + (base + rs) * a.la_st + 4 * (ll & 31) : (const float *)a.k, &Bf.gate[2 * u * D]);
                 }
                 const int rs = ll < cl ? ll : cl - 1;
-                if (bh) gll4(bh + (base + rs) * a.b_st, Bf.beta);
+                if (lw == 0 && bh) gll4(bh + (base + rs) * a.b_st, Bf.beta);
                 else gll4(a.k, Bf.dummy);
             }
         }
@@ -331,7 +340,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     // thread th takes tokens tb0 + 8 th + 0..7 (inclusive prefix in the thread, then
     // over the wave with DPP, then over the waves through LDS).  Returns the block's
     // G_b and adds the thread's log alphas into ell.  Every compute wave calls it; the
-    // loading wave passes its two barriers.
+    // loading waves pass its two barriers.
     auto make_table = [&](int64_t tb0) -> float {
         if constexpr (DIAG) return 0.0f;
         const int64_t tb1 = tb0 + TBT < n ? tb0 + TBT : n;
@@ -367,39 +376,49 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         return G;
     };
 
-    if (w == NWC) {
-        // ================= loading wave: the same barriers as the compute waves
-        uint32_t ko[16], vo[GR], go[DIAG ? 33 : 1];
+    if (w >= NWC) {
+        // ================= loading waves: the same barriers as the compute waves
+        const int lw = w - NWC;
+        uint32_t ko[NKI], vo[NVI], go[NGI + 1];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int r = 4 * u + (l >> 4);
-            ko[u] = small_st ? (uint32_t)(r * a.k_st + 8 * ((l & 15) ^ (r & 15))) : 0u;
+        for (int j = 0; j < NKI; ++j) {
+            const int r = 4 * (lw + NLW * j) + (l >> 4);
+            ko[j] = small_st ? (uint32_t)(r * a.k_st + 8 * ((l & 15) ^ (r & 15))) : 0u;
         }
 #pragma unroll
-        for (int u = 0; u < GR; ++u) {
-            const int r = RPI * u + l / GR;
-            vo[u] = small_st ? (uint32_t)(r * a.v_st + 8 * ((l % GR) ^ ((r >> VSH) & (GR - 1)))) : 0u;
+        for (int j = 0; j < NVI; ++j) {
+            const int r = RPI * (lw + NLW * j) + l / GR;
+            vo[j] = small_st ? (uint32_t)(r * a.v_st + 8 * ((l % GR) ^ ((r >> VSH) & (GR - 1)))) : 0u;
         }
-        if (DIAG) {
 #pragma unroll
-            for (int u = 0; u < 32; ++u) {
-                const int r = 2 * u + (l >> 5);
-                go[u] = small_st ? (uint32_t)(r * a.la_st + 4 * (l & 31)) : 0u;
-            }
-            go[DIAG ? 32 : 0] = small_st ? (uint32_t)(l * a.b_st) : 0u;
+        for (int j = 0; j < NGI; ++j) {
+            const int r = 2 * (lw + NLW * j) + (l >> 5);
+            go[j] = small_st ? (uint32_t)(r * a.la_st + 4 * (l & 31)) : 0u;
         }
-        for (int64_t c = 0; c < DIST && c < nc; ++c) issue(c, ko, vo, go);
-        // make_table's two barriers (this wave has no tokens, and no load to wait for)
+        go[NGI] = small_st ? (uint32_t)(l * a.b_st) : 0u;
+        for (int64_t c = 0; c < DIST && c < nc; ++c) issue(c, lw, ko, vo, go);
+        // make_table's two barriers (these waves have no tokens, and no load to wait for)
         if (!DIAG) {
             lds_barrier();
             lds_barrier();
+            if (AHEAD) {
+                if (nc > 0) {
+                    // chunk 0 landed: the compute waves read its operands before their loop
+                    const int64_t issued = (DIST - 1 < nc - 1 ? DIST - 1 : nc - 1);
+                    wait_chunks<LPW, DIST - 1>((int)issued);
+                }
+                lds_barrier();
+            }
         }
         for (int64_t c = 0; c < nc; ++c) {
-            // chunk c has landed once at most the later chunks' loads remain
-            const int64_t later = nc - 1 - c;
-            wait_chunks<LPW, DIST - 1>(later < DIST - 1 ? (int)later : DIST - 1);
-            lds_barrier();                            // chunk c visible; chunk c - 1's buffer free
-            if (c + DIST < nc) issue(c + DIST, ko, vo, go);
+            // chunk c + AHEAD has landed once at most the later chunks' loads remain
+            {
+                const int64_t issued = c + DIST - 1 < nc - 1 ? c + DIST - 1 : nc - 1;
+                const int64_t need = c + AHEAD < nc - 1 ? c + AHEAD : nc - 1;
+                wait_chunks<LPW, DIST - 1>((int)(issued - need));
+            }
+            lds_barrier();                            // chunk c + AHEAD visible; chunk c - 1's buffer free
+            if (c + DIST < nc) issue(c + DIST, lw, ko, vo, go);
             if (!DIAG && c > 0 && c % TBC == 0) {
                 lds_barrier();
                 lds_barrier();
@@ -409,17 +428,66 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     }
 
     // ================= compute waves
-    if (!DIAG) make_table(0);
+    if constexpr (!DIAG) {
+        // ---- S += K^T diag(w) V with the table's weights, 16 tokens per k-step; the
+        //      weights go onto the K^T fragment (one scaling serves every value block).
+        //      With AHEAD, a chunk's K^T and V fragments are read during the previous
+        //      chunk's products (two register sets, the loop unrolled by two).
+        struct Ops {
+            bf16x8 kr[4], vb[4][NJB];
+        };
+        auto load_ops = [&](int64_t cc, Ops &o) {
+            const SdBuf<DIAG, NJB> &B = sm.buf[cc % NBUF];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                o.kr[ks] = tr_pair(&B.Km[kofs[0] + 16 * ks * D], &B.Km[kofs[1] + 16 * ks * D]);
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb)
+                    o.vb[ks][jb] = tr_pair(&B.Vm[vofs[0][jb] + 16 * ks * 32 * NJB],
+                                           &B.Vm[vofs[1][jb] + 16 * ks * 32 * NJB]);
+            }
+        };
+        auto step = [&](int64_t cc, Ops &cur, Ops &nxt) {
+            lds_barrier();                            // chunk cc + AHEAD visible; chunk cc - 1's buffer free
+            if (cc > 0 && cc % TBC == 0) {
+                // a new table block: carry the state into it (every wave is past chunk cc - 1)
+                const float eG = __expf(make_table(cc * CH));
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) st[jb][r] *= eG;
+            }
+            if (!AHEAD) load_ops(cc, cur);
+            else if (cc + 1 < nc) load_ops(cc + 1, nxt);
+            const float *wrow = &sm.wt[CH * (int)(cc % TBC)];
+            float4 w0[4], w1[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                w0[ks] = *reinterpret_cast<const float4 *>(&wrow[16 * ks + 8 * h]);
+                w1[ks] = *reinterpret_cast<const float4 *>(&wrow[16 * ks + 8 * h + 4]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 ka = scale8(cur.kr[ks], w0[ks], w1[ks]);
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) st[jb] = mfma(ka, cur.vb[ks][jb], st[jb]);
+            }
+        };
+        make_table(0);
+        Ops oa, ob;
+        if constexpr (AHEAD) {
+            lds_barrier();                            // chunk 0 visible
+            if (nc > 0) load_ops(0, oa);
+            for (int64_t c = 0; c < nc; c += 2) {
+                step(c, oa, ob);
+                if (c + 1 < nc) step(c + 1, ob, oa);
+            }
+        } else {
+            for (int64_t c = 0; c < nc; ++c) step(c, oa, oa);
+        }
+    } else {
     for (int64_t c = 0; c < nc; ++c) {
         lds_barrier();                                // chunk c visible; chunk c - 1's buffer free
-        if (!DIAG && c > 0 && c % TBC == 0) {
-            // a new table block: carry the state into it (every wave is past chunk c - 1)
-            const float eG = __expf(make_table(c * CH));
-#pragma unroll
-            for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) st[jb][r] *= eG;
-        }
 
         const SdBuf<DIAG, NJB> &B = sm.buf[c % NBUF];
         const int64_t rem = n - c * CH;
@@ -521,32 +589,9 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
                     for (int half = 0; half < 2; ++half) st[jb] = mfma(ka[2 * tb + half], pack8(dv, half), st[jb]);
                 }
             }
-        } else {
-            // ---- S += K^T diag(w) V with the table's weights, 16 tokens per k-step; the
-            //      weights go onto the K^T fragment (one scaling serves every value block).
-            //      Every operand read is issued before the first product.
-            const float *wrow = &sm.wt[CH * (int)(c % TBC)];
-            bf16x8 kr[4], vb[4][NJB];
-            float4 w0[4], w1[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                kr[ks] = tr_pair(&B.Km[kofs[0] + 16 * ks * D], &B.Km[kofs[1] + 16 * ks * D]);
-                w0[ks] = *reinterpret_cast<const float4 *>(&wrow[16 * ks + 8 * hv]);
-                w1[ks] = *reinterpret_cast<const float4 *>(&wrow[16 * ks + 8 * hv + 4]);
-#pragma unroll
-                for (int jb = 0; jb < NJB; ++jb)
-                    vb[ks][jb] = tr_pair(&B.Vm[vofs[0][jb] + 16 * ks * 32 * NJB],
-                                         &B.Vm[vofs[1][jb] + 16 * ks * 32 * NJB]);
-            }
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 ka = scale8(kr[ks], w0[ks], w1[ks]);
-#pragma unroll
-                for (int jb = 0; jb < NJB; ++jb) st[jb] = mfma(ka, vb[ks][jb], st[jb]);
-            }
         }
     }
-
+    }
     // ---- record
     const float nanv = __int_as_float(0x7fc00000);
     const bool bad = state == 2;

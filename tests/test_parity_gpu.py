@@ -154,6 +154,14 @@ def test_scalar_diagonal_16_heads_8x2048(family, variant):
         assert naive > 2e-2
 
 
+def test_scalar_mixed_lengths_128_units():
+    """Scalar family, H=16, d=128, bf16, 8 segments of mixed length (empty, one
+    token, partial chunks, odd and even chunk counts): 128 units take the value
+    split whose compute waves read each chunk's operands one chunk ahead."""
+    check_build_compose(hp.SCALAR, [2048, 1, 65, 0, 129, 700, 64, 1000], 16, 128, 128, torch.bfloat16, 211,
+                        "weak", label="scalar-mixed-128-units")
+
+
 @pytest.mark.parametrize("variant", ["as_given", "none"])
 def test_gdn_32_heads_16x2048(variant):
     """GDN H=32, d=128, bf16, one 32768-token request in 16 x 2048 segments (sampled)."""
