@@ -23,18 +23,19 @@
 // that the VALU is free for the scale factors.
 //
 // Work split: NSPLIT workgroups per (segment, head) of four compute waves and
-// four loading waves, workgroup q keeping value columns [128 q / NSPLIT,
-// 128 (q + 1) / NSPLIT); compute wave w keeps rows [32w, 32w + 32) of S as fp32
-// 32x32 accumulator tiles.  Keys and values arrive
-// token-major and are turned around on the MFMA itself: X . I returns X's
-// columns in the accumulator layout, which is the A layout of K^T and the B
-// layout of V^T with the same token order (diagonal family).  The scalar family
-// reads both fragments straight from the token-major tiles with gfx950's
-// transposing LDS read (ds_read_b64_tr_b16) and puts the per-token weights on
-// the K^T fragment, so its chunk is four MFMAs per value block; every operand
-// read of a chunk is issued before its first product.  Every wave
-// takes what it needs (its own 32 key channels, all of the workgroup's value
-// columns), so the waves share nothing but the staged tiles.
+// four loading waves.  Scalar family: workgroup q keeps value columns
+// [128 q / NSPLIT, 128 (q + 1) / NSPLIT) and compute wave w rows [32w, 32w + 32)
+// of S.  Diagonal family (NSPLIT = 2): workgroup q keeps key channels (rows of S)
+// [64 q, 64 q + 64), so it stages only its half of the keys and of the fp32
+// gates, and compute wave w the 32 rows 64 q + 32 (w / 2) + 0..31 by value
+// columns 64 (w % 2) + 0..63.  Every tile is an fp32 32x32 accumulator.  Keys
+// and values arrive token-major; both families read the K^T and V^T operand
+// fragments straight from the token-major tiles with gfx950's transposing LDS
+// read (ds_read_b64_tr_b16) and put the weights on the K^T fragment (scalar:
+// beta_t e^{G_b - L_t} per token; diagonal: beta_t e^{G_i - L_{t,i}} per token
+// and key channel), so a chunk is four MFMAs per value block.  Operand reads are
+// issued before the first product that uses them.  Every wave takes what it
+// needs, so the waves share nothing but the staged tiles.
 //
 // Streaming: four more waves only load: keys, values (and the diagonal family's
 // gates and beta) go from HBM straight into LDS (global_load_lds), NBUF chunks
@@ -117,15 +118,6 @@ __device__ __forceinline__ void gll4(const void *src, void *dst) {
                  : "memory");
 }
 
-// B operand of the identity for k-step ks (column l32, rows 16 ks + 8h + e).
-__device__ __forceinline__ bf16x8 eye_b(int ks, int h, int l32) {
-    const int d = l32 - 16 * ks - 8 * h;
-    const uint32_t one = (unsigned)d < 8u ? 0x3f80u << (16 * (d & 1)) : 0u;
-    const int wd = d >> 1;
-    const u32x4 u = {wd == 0 ? one : 0u, wd == 1 ? one : 0u, wd == 2 ? one : 0u, wd == 3 ? one : 0u};
-    return __builtin_bit_cast(bf16x8, u);
-}
-
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
@@ -151,12 +143,16 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 // granules); granule g sits in slot g ^ ((r >> SH) % (4 NJB)), SH = 2, 1, 0 for
 // NJB = 1, 2, 4.  Either way the 16 rows one operand read touches hit distinct
 // bank groups, and global_load_lds can fill whole rows.
+// Diagonal family: Km holds the workgroup's 64 key channels (8 granules a row,
+// granule g in slot g ^ ((r >> 1) % 8)), Vm all 128 value columns (as the
+// scalar Km).
+constexpr int DKC = 64;                  // diagonal: key channels per workgroup
 template <bool DIAG, int NJB>
 struct __align__(16) SdBuf {
-    u16 Km[CH * D];
-    u16 Vm[CH * 32 * NJB];
+    u16 Km[DIAG ? CH * DKC : CH * D];
+    u16 Vm[DIAG ? CH * D : CH * 32 * NJB];
     // diagonal family only (the scalar family reads its gates once per table block)
-    float gate[DIAG ? CH * D : 4];       // [token][channel]
+    float gate[DIAG ? CH * DKC : 4];     // [token][key channel of the workgroup]
     float beta[DIAG ? CH : 4];
     float dummy[DIAG ? CH : 4];          // target of the loads that keep per-wave load counts equal
 };
@@ -171,12 +167,13 @@ struct __align__(16) SdSmem {
     float wtot[NWC];                     // scalar: per-wave sums while a table is built
     double ellw[4];                      // scalar: per-wave ell
     float gd[4][DIAG ? 32 : 1];          // diagonal, per wave: chunk decay G_i of its channels
-    float tot[4][2][32][DIAG ? 8 : 1];   // diagonal, per wave: token-group sums of each lane half
+    float tot[4][2][32][DIAG ? 4 : 1];   // diagonal, per wave: token-group sums of each lane half
     int64_t t0, n;
     int32_t slot, state;
 };
 
 __device__ __forceinline__ int kmo(int r, int g) { return r * D + ((g ^ (r & 15)) << 3); }
+__device__ __forceinline__ int kmo_half(int r, int g) { return r * DKC + ((g ^ ((r >> 1) & 7)) << 3); }
 template <int NJB>
 __device__ __forceinline__ int vmo(int r, int g) {
     constexpr int SH = NJB == 1 ? 2 : NJB == 2 ? 1 : 0;
@@ -199,15 +196,16 @@ template <int FAM, int NSPLIT>
 __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) void sd_build_mfma_kernel(BuildArgs a) {
     constexpr bool DIAG = FAM == HYPIC_DIAGONAL;
     constexpr int NJB = 4 / NSPLIT;                    // 32-column value blocks per workgroup
+    static_assert(!DIAG || NSPLIT == 2, "the diagonal family splits the key channels in two");
     // chunks staged: as many as fit beside the other workgroup on the CU (value
-    // split 4: two per CU) or alone (diagonal: the fp32 gates are big)
-    constexpr int NBUF = DIAG ? 2 : NSPLIT == 4 ? 3 : NSPLIT == 2 ? 6 : 4;
+    // split 4: two per CU) or alone
+    constexpr int NBUF = DIAG ? 3 : NSPLIT == 4 ? 3 : NSPLIT == 2 ? 6 : 4;
     constexpr int DIST = NBUF - 1;                     // prefetch distance in chunks
     // global_load_lds instructions of each loading wave per chunk: its share of the
     // keys, values, and for the diagonal family gates, plus one dword row (beta or a
     // dummy)
-    constexpr int NKI = 16 / NLW, NVI = 4 * NJB / NLW, NGI = DIAG ? 32 / NLW : 0;
-    static_assert(16 % NLW == 0 && (4 * NJB) % NLW == 0 && 32 % NLW == 0, "load shares");
+    constexpr int NKI = (DIAG ? 8 : 16) / NLW, NVI = (DIAG ? 16 : 4 * NJB) / NLW, NGI = DIAG ? 16 / NLW : 0;
+    static_assert(8 % NLW == 0 && (4 * NJB) % NLW == 0 && 16 % NLW == 0, "load shares");
     constexpr int LPW = NKI + NVI + (DIAG ? NGI + 1 : 0);
     constexpr int TBC = TBT / CH;                      // chunks per scalar weight table
     // with two value blocks per workgroup the scalar compute waves read a chunk's
@@ -224,7 +222,8 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     const int unit = (b / (8 * NSPLIT)) * 8 + (b & 7);
     const int head = unit % a.H;
     const int seg = unit / a.H;
-    const int jc0 = 32 * NJB * q;            // first value column of this workgroup
+    const int jc0 = DIAG ? 0 : 32 * NJB * q;  // first value column of this workgroup
+    const int kc0 = DIAG ? DKC * q : 0;       // first key channel of this workgroup (diagonal)
     if (seg >= a.num_segments) return;       // grid padding
 
     if (th == 0) {
@@ -245,9 +244,9 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     const int64_t slot = sm.slot;
     const int64_t nc = (n + CH - 1) / CH;
 
-    const u16 *kh = static_cast<const u16 *>(a.k) + t0 * a.k_st + head * a.k_sh;
+    const u16 *kh = static_cast<const u16 *>(a.k) + t0 * a.k_st + head * a.k_sh + kc0;
     const u16 *vh = static_cast<const u16 *>(a.v) + t0 * a.v_st + head * a.v_sh + jc0;
-    const float *gh = a.log_alpha ? a.log_alpha + t0 * a.la_st + head * a.la_sh : nullptr;
+    const float *gh = a.log_alpha ? a.log_alpha + t0 * a.la_st + head * a.la_sh + kc0 : nullptr;
     const float *bh = a.beta ? a.beta + t0 * a.b_st + head * a.b_sh : nullptr;
 
     // Loading wave: chunk C's loads into buffer C % NBUF, LPW instructions in a fixed
@@ -258,6 +257,14 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     if (a.la_st > mst) mst = a.la_st;
     if (a.b_st > mst) mst = a.b_st;
     const bool small_st = (int64_t)CH * mst < (1LL << 30);
+    // Row geometry of one global_load_lds (64 lanes x 16 bytes): keys KR rows of KG
+    // granules (scalar: all 128 channels; diagonal: the workgroup's 64), values VR rows
+    // of VG granules (scalar: the workgroup's columns; diagonal: all 128), gates
+    // (diagonal) 4 rows of 64 floats.  kswz / vswz: the LDS slot of granule g of row r.
+    constexpr int KR = DIAG ? 8 : 4, KG = DIAG ? 8 : 16, KW = DIAG ? DKC : D;
+    constexpr int VR = DIAG ? 4 : RPI, VG = DIAG ? 16 : GR, VW = DIAG ? D : 32 * NJB;
+    auto kswz = [](int r, int g) { return DIAG ? g ^ ((r >> 1) & 7) : g ^ (r & 15); };
+    auto vswz = [](int r, int g) { return DIAG ? g ^ (r & 15) : g ^ ((r >> VSH) & (GR - 1)); };
     auto issue = [&](int64_t C, int lw, const uint32_t *ko, const uint32_t *vo, const uint32_t *go) {
         const int bi = (int)(C % NBUF);
         const int64_t base = C * CH, rem = n - base;
@@ -265,13 +272,13 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         if (rem >= CH && small_st) {
             const u16 *kc = kh + base * a.k_st, *vc = vh + base * a.v_st;
 #pragma unroll
-            for (int j = 0; j < NKI; ++j) gll16(kc + ko[j], &Bf.Km[4 * (lw + NLW * j) * D]);
+            for (int j = 0; j < NKI; ++j) gll16(kc + ko[j], &Bf.Km[KR * (lw + NLW * j) * KW]);
 #pragma unroll
-            for (int j = 0; j < NVI; ++j) gll16(vc + vo[j], &Bf.Vm[RPI * (lw + NLW * j) * 32 * NJB]);
+            for (int j = 0; j < NVI; ++j) gll16(vc + vo[j], &Bf.Vm[VR * (lw + NLW * j) * VW]);
             if (DIAG) {
 #pragma unroll
                 for (int j = 0; j < NGI; ++j)
-                    gll16(gh ? gh + base * a.la_st + go[j] : (const float *)a.k, &Bf.gate[2 * (lw + NLW * j) * D]);
+                    gll16(gh ? gh + base * a.la_st + go[j] : (const float *)a.k, &Bf.gate[4 * (lw + NLW * j) * DKC]);
                 if (lw == 0 && bh) gll4(bh + base * a.b_st + go[NGI], Bf.beta);
                 else gll4(a.k, Bf.dummy);
             }
@@ -279,25 +286,22 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
             const int cl = rem < CH ? (int)rem : CH;
             int ll = l;
             asm volatile("" : "+v"(ll));
-            // keys: instruction u covers rows 4u .. 4u + 3 (lane: row 4u + ll / 16, slot ll % 16)
+            // instruction u covers rows KR u .. KR u + KR - 1 (lane: row KR u + ll / KG, slot ll % KG)
 #pragma unroll
             for (int j = 0; j < NKI; ++j) {
-                const int u = lw + NLW * j, r = 4 * u + (ll >> 4), rs = r < cl ? r : cl - 1;
-                gll16(kh + (base + rs) * a.k_st + 8 * ((ll & 15) ^ (r & 15)), &Bf.Km[4 * u * D]);
+                const int u = lw + NLW * j, r = KR * u + ll / KG, rs = r < cl ? r : cl - 1;
+                gll16(kh + (base + rs) * a.k_st + 8 * kswz(r, ll % KG), &Bf.Km[KR * u * KW]);
             }
-            // values: GR granules per row, RPI rows per instruction
 #pragma unroll
             for (int j = 0; j < NVI; ++j) {
-                const int u = lw + NLW * j, r = RPI * u + ll / GR, rs = r < cl ? r : cl - 1;
-                gll16(vh + (base + rs) * a.v_st + 8 * ((ll % GR) ^ ((r >> VSH) & (GR - 1))),
-                      &Bf.Vm[RPI * u * 32 * NJB]);
+                const int u = lw + NLW * j, r = VR * u + ll / VG, rs = r < cl ? r : cl - 1;
+                gll16(vh + (base + rs) * a.v_st + 8 * vswz(r, ll % VG), &Bf.Vm[VR * u * VW]);
             }
             if (DIAG) {
-                // gates: 2 rows (512 bytes each) per instruction
 #pragma unroll
                 for (int j = 0; j < NGI; ++j) {
-                    const int u = lw + NLW * j, r = 2 * u + (ll >> 5), rs = r < cl ? r : cl - 1;
-                    gll16(gh ? gh + (base + rs) * a.la_st + 4 * (ll & 31) : (const float *)a.k, &Bf.gate[2 * u * D]);
+                    const int u = lw + NLW * j, r = 4 * u + (ll >> 4), rs = r < cl ? r : cl - 1;
+                    gll16(gh ? gh + (base + rs) * a.la_st + 4 * (ll & 15) : (const float *)a.k, &Bf.gate[4 * u * DKC]);
                 }
                 const int rs = ll < cl ? ll : cl - 1;
                 if (lw == 0 && bh) gll4(bh + (base + rs) * a.b_st, Bf.beta);
@@ -312,7 +316,6 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[jb][r] = 0.f;
     double ell = 0.0;   // scalar: this thread's table tokens; diagonal: this lane's tokens of channel 32w + l32
-    const bf16x8 eye0 = eye_b(0, h, l32), eye1 = eye_b(1, h, l32);
     // scalar family: K^T and V^T fragments straight from the token-major tiles with the
     // transposing read.  Lane l (16-lane group g16 = l / 16, lane j = l % 16 in it, read
     // row a = j / 4, column piece b = j % 4) addresses token 8 (g16 / 2) + 4r + a of the
@@ -320,6 +323,23 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     // 32 jb + 16 (g16 % 2) + 4b); the swizzle terms do not depend on the k-step, whose
     // offset is added per read.  Output: lane l's fragment of channel (column) l % 32,
     // tokens 16 ks + 8h + 0..7.
+    // diagonal family: the same fragments from its half-width key rows (kmo_half) and
+    // full-width value rows (kmo); wave w: key block w / 2, value blocks 2 (w % 2) + jb
+    int dkofs[2], dvofs[2][NJB];
+    {
+        const int g16 = l >> 4, j = l & 15, ra = j >> 2, rb = j & 3;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int t = 8 * (g16 >> 1) + 4 * r + ra;
+            const int ch = 32 * (w >> 1) + 16 * (g16 & 1) + 4 * rb;
+            dkofs[r] = kmo_half(t, ch >> 3) + (ch & 7);
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                const int cv = 32 * (2 * (w & 1) + jb) + 16 * (g16 & 1) + 4 * rb;
+                dvofs[r][jb] = kmo(t, cv >> 3) + (cv & 7);
+            }
+        }
+    }
     int kofs[2], vofs[2][NJB];
     {
         const int g16 = l >> 4, j = l & 15, ra = j >> 2, rb = j & 3;
@@ -382,18 +402,18 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         uint32_t ko[NKI], vo[NVI], go[NGI + 1];
 #pragma unroll
         for (int j = 0; j < NKI; ++j) {
-            const int r = 4 * (lw + NLW * j) + (l >> 4);
-            ko[j] = small_st ? (uint32_t)(r * a.k_st + 8 * ((l & 15) ^ (r & 15))) : 0u;
+            const int r = KR * (lw + NLW * j) + l / KG;
+            ko[j] = small_st ? (uint32_t)(r * a.k_st + 8 * kswz(r, l % KG)) : 0u;
         }
 #pragma unroll
         for (int j = 0; j < NVI; ++j) {
-            const int r = RPI * (lw + NLW * j) + l / GR;
-            vo[j] = small_st ? (uint32_t)(r * a.v_st + 8 * ((l % GR) ^ ((r >> VSH) & (GR - 1)))) : 0u;
+            const int r = VR * (lw + NLW * j) + l / VG;
+            vo[j] = small_st ? (uint32_t)(r * a.v_st + 8 * vswz(r, l % VG)) : 0u;
         }
 #pragma unroll
         for (int j = 0; j < NGI; ++j) {
-            const int r = 2 * (lw + NLW * j) + (l >> 5);
-            go[j] = small_st ? (uint32_t)(r * a.la_st + 4 * (l & 31)) : 0u;
+            const int r = 4 * (lw + NLW * j) + (l >> 4);
+            go[j] = small_st ? (uint32_t)(r * a.la_st + 4 * (l & 15)) : 0u;
         }
         go[NGI] = small_st ? (uint32_t)(l * a.b_st) : 0u;
         for (int64_t c = 0; c < DIST && c < nc; ++c) issue(c, lw, ko, vo, go);
@@ -496,99 +516,78 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         asm volatile("" : "+v"(thv));
         const int lv = thv & 63, hv = lv >> 5, lv32 = lv & 31;
 
-        float kfac[2][16];                            // diagonal: e^{G_i - g_{t,i}} per key element
-        if (DIAG) {
-            // ---- per-token factors (lane = token), masked past the segment
-            const float bt = lv < cl ? (a.beta ? B.beta[lv] : 1.0f) : 0.0f;
-            sm.wsc[w][lv] = bt;
-            // channel i = 32w + lv32; this lane's tokens 32 tb + 8 qq + 4 hv + e, in groups of 4
-            const int i = 32 * w + lv32;
-            float x[2][4][4], gs[2][4];
+        // ---- per-(token, channel) factors.  Lane (channel i = 32 (w / 2) + lv32 of the
+        //      workgroup's 64, half hv) takes tokens 16 ks + 8 hv + e, e < 8: the tokens of
+        //      its K^T fragment in k-step ks.  Every gate read is issued before the first
+        //      is used (rows past the segment hold finite copies, masked after the read).
+        const int i = 32 * (w >> 1) + lv32;
+        sm.wsc[w][lv] = lv < cl ? (a.beta ? B.beta[lv] : 1.0f) : 0.0f;
+        float x[4][8], gsum[4];
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    float s = 0.f;
+            for (int e = 0; e < 8; ++e) x[ks][e] = B.gate[(16 * ks + 8 * hv + e) * DKC + i];
+        float csum = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 32 * tb + 8 * qq + 4 * hv + e;
-                        const float v = (t < cl && a.log_alpha) ? B.gate[t * D + i] : 0.0f;
-                        ell += (double)v;
-                        s += v;
-                        x[tb][qq][e] = s;            // inclusive prefix inside the group
-                    }
-                    gs[tb][qq] = s;
-                    sm.tot[w][hv][lv32][4 * tb + qq] = s;
-                }
-            wave_lds_sync();
-            // offsets: every group before this one in token order (other half's groups interleave)
-            float run = 0.f, G = 0.f;
+        for (int ks = 0; ks < 4; ++ks) {
+            float s = 0.f;
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const float other = sm.tot[w][hv ^ 1][lv32][4 * tb + qq];
-                    const float g0 = hv == 0 ? gs[tb][qq] : other, g1 = hv == 0 ? other : gs[tb][qq];
-                    const float off = run + (hv == 0 ? 0.f : g0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[tb][qq][e] += off;
-                    run += g0 + g1;
-                }
-            G = run;
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) kfac[tb][4 * qq + e] = __expf(G - x[tb][qq][e]);
-            if (hv == 0) sm.gd[w][lv32] = G;
-            wave_lds_sync();
+            for (int e = 0; e < 8; ++e) {
+                const int t = 16 * ks + 8 * hv + e;
+                s += (t < cl && a.log_alpha) ? x[ks][e] : 0.0f;
+                x[ks][e] = s;                        // inclusive prefix inside the group
+            }
+            gsum[ks] = s;
+            csum += s;
+            sm.tot[w][hv][lv32][ks] = s;
         }
-
-        // ---- decay of the carried state
-        if (DIAG) {
+        ell += (double)csum;
+        wave_lds_sync();
+        // offsets: every group before this one in token order (the halves' groups interleave)
+        float run = 0.f;
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const float4 g4 = *reinterpret_cast<const float4 *>(&sm.gd[w][8 * qq + 4 * hv]);
-                const float f[4] = {__expf(g4.x), __expf(g4.y), __expf(g4.z), __expf(g4.w)};
+        for (int ks = 0; ks < 4; ++ks) {
+            const float other = sm.tot[w][hv ^ 1][lv32][ks];
+            const float g0 = hv == 0 ? gsum[ks] : other, g1 = hv == 0 ? other : gsum[ks];
+            const float off = run + (hv == 0 ? 0.f : g0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
+            for (int e = 0; e < 8; ++e) x[ks][e] += off;
+            run += g0 + g1;
+        }
+        const float G = run;
+        if (hv == 0) sm.gd[w][lv32] = G;
+        wave_lds_sync();
+        // ---- decay of the carried state: row (key channel) r of a tile by e^{G_r}
 #pragma unroll
-                    for (int jb = 0; jb < NJB; ++jb) st[jb][4 * qq + e] *= f[e];
-            }
-            // ---- K^T of this wave's 32 key channels (A operands), scaled per element
-            bf16x8 ka[4];
+        for (int qq = 0; qq < 4; ++qq) {
+            const float4 g4 = *reinterpret_cast<const float4 *>(&sm.gd[w][8 * qq + 4 * hv]);
+            const float f[4] = {__expf(g4.x), __expf(g4.y), __expf(g4.z), __expf(g4.w)};
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                f32x16 dk;
+            for (int e = 0; e < 4; ++e)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    dk = mfma(lds8(&B.Km[kmo(32 * tb + lv32, 4 * w + 2 * ks + hv)]), ks == 0 ? eye0 : eye1,
-                              ks == 0 ? f32x16{} : dk);
+                for (int jb = 0; jb < NJB; ++jb) st[jb][4 * qq + e] *= f[e];
+        }
+        // ---- S += (W . K)^T V, W[t][i] = beta_t e^{G_i - L_{t,i}}: K^T and V^T fragments
+        //      with the transposing read, the weights on the K^T fragment
+        bf16x8 kr[4], vb[4][NJB];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dk[r] *= kfac[tb][r];
-                ka[2 * tb] = pack8(dk, 0);
-                ka[2 * tb + 1] = pack8(dk, 1);
-            }
-            // ---- per value block: V^T (B operands) scaled per token, then S += K^T V
+        for (int ks = 0; ks < 4; ++ks) {
+            kr[ks] = tr_pair(&B.Km[dkofs[0] + 16 * ks * DKC], &B.Km[dkofs[1] + 16 * ks * DKC]);
 #pragma unroll
-            for (int jb = 0; jb < NJB; ++jb) {
+            for (int jb = 0; jb < NJB; ++jb)
+                vb[ks][jb] = tr_pair(&B.Vm[dvofs[0][jb] + 16 * ks * D], &B.Vm[dvofs[1][jb] + 16 * ks * D]);
+        }
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb) {
-                    f32x16 dv;
+        for (int ks = 0; ks < 4; ++ks) {
+            const float4 b0 = *reinterpret_cast<const float4 *>(&sm.wsc[w][16 * ks + 8 * hv]);
+            const float4 b1 = *reinterpret_cast<const float4 *>(&sm.wsc[w][16 * ks + 8 * hv + 4]);
+            const float4 f0 = make_float4(b0.x * __expf(G - x[ks][0]), b0.y * __expf(G - x[ks][1]),
+                                          b0.z * __expf(G - x[ks][2]), b0.w * __expf(G - x[ks][3]));
+            const float4 f1 = make_float4(b1.x * __expf(G - x[ks][4]), b1.y * __expf(G - x[ks][5]),
+                                          b1.z * __expf(G - x[ks][6]), b1.w * __expf(G - x[ks][7]));
+            const bf16x8 ka = scale8(kr[ks], f0, f1);
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        dv = mfma(lds8(&B.Vm[vmo<NJB>(32 * tb + lv32, 4 * jb + 2 * ks + hv)]), ks == 0 ? eye0 : eye1,
-                                  ks == 0 ? f32x16{} : dv);
-#pragma unroll
-                    for (int qq = 0; qq < 4; ++qq) {
-                        const float4 s4 = *reinterpret_cast<const float4 *>(&sm.wsc[w][32 * tb + 8 * qq + 4 * hv]);
-                        dv[4 * qq] *= s4.x; dv[4 * qq + 1] *= s4.y; dv[4 * qq + 2] *= s4.z; dv[4 * qq + 3] *= s4.w;
-                    }
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) st[jb] = mfma(ka[2 * tb + half], pack8(dv, half), st[jb]);
-                }
-            }
+            for (int jb = 0; jb < NJB; ++jb) st[jb] = mfma(ka, vb[ks][jb], st[jb]);
         }
     }
     }
@@ -597,16 +596,20 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     const bool bad = state == 2;
     const int64_t rec = slot * a.H + head;
     float *dst = a.pool_S + rec * D * D;
+    // rows (key channels) and first column of this wave's tiles
+    const int row0 = DIAG ? kc0 + 32 * (w >> 1) : 32 * w;
+    const int col0 = DIAG ? 64 * (w & 1) : jc0;
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            dst[(int64_t)(32 * w + acc_row(r, h)) * D + jc0 + 32 * jb + l32] = bad ? nanv : st[jb][r];
-    if (q != 0) return;
+            dst[(int64_t)(row0 + acc_row(r, h)) * D + col0 + 32 * jb + l32] = bad ? nanv : st[jb][r];
     if (DIAG) {
-        ell += __shfl_xor(ell, 32);        // the two lane halves hold the two token halves
-        if (h == 0) a.pool_ell[rec * D + 32 * w + l32] = bad ? nanv : (float)ell;
+        // the two waves of a key block hold the same sums; the two lane halves the two token halves
+        ell += __shfl_xor(ell, 32);
+        if ((w & 1) == 0 && h == 0) a.pool_ell[rec * D + row0 + l32] = bad ? nanv : (float)ell;
     } else {
+        if (q != 0) return;
         // every thread summed its table tokens
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) ell += __shfl_xor(ell, o);
