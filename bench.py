@@ -17,7 +17,7 @@ Inputs are resident in HBM before the timed region starts.  Kernel durations
 come from HIP events recorded on the stream the kernels are launched on.
 The cpu_baseline leg times the fp64 oracle on a bounded sample on the host.
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|sd|compose] [--no-cpu]
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|sd|compose|rag] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -364,8 +364,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["all", "main", "sd", "compose"], default="all",
-                    help="main: only the headline GDN step; sd / compose: it plus that secondary leg")
+    ap.add_argument("--only", choices=["all", "main", "sd", "compose", "rag"], default="all",
+                    help="main: only the headline GDN step; sd / compose / rag: it plus that secondary leg")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one untimed 1 GiB device copy (reference kernel for HBM byte counters)")
@@ -392,7 +392,7 @@ def main():
         secondary.append(bench_compose_pool(args))
     if args.only in ("all", "sd"):
         secondary.extend(bench_sd(args))
-    if args.only == "all":
+    if args.only in ("all", "rag"):
         secondary.append(bench_rag(args))
     cpu = None if args.no_cpu else cpu_baseline()
     line = {

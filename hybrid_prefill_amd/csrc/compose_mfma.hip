@@ -66,22 +66,40 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t &hi, uint32_
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x0 - h0, x1 - h1}, bf16x2_t));
 }
 
-// The chain's first CHAIN_LDS slots and their ell values, staged in LDS by the
-// validation pass: the product loop then reads them from LDS instead of waiting on a
-// dependent global load per step (later entries are read from global memory).
+// The chain's slots and their ell values, staged in LDS as a ring of CHAIN_LDS
+// entries (entry of chain position c at (c - c_lo) mod CHAIN_LDS): the validation
+// pass fills the first CHAIN_LDS, and at every step c with c - c_lo a positive
+// multiple of CHAIN_LDS / 2 the workgroup refills positions
+// [c + CHAIN_LDS / 2, c + CHAIN_LDS), whose ring entries held positions already
+// consumed.  The product loop then reads a step's slot with an LDS read only: a
+// vector-memory load there (or a generic-pointer load) would make the compiler's
+// wait for its result drain every record prefetch in flight.
 constexpr int CHAIN_LDS = 1024;
 struct ChainStage {
     int32_t slot[CHAIN_LDS];
     float ell[CHAIN_LDS];
 };
-__device__ __forceinline__ int32_t chain_slot(const ChainStage &cs, const ComposeArgs &a, int64_t c_lo, int64_t c) {
-    return c - c_lo < CHAIN_LDS ? cs.slot[c - c_lo] : a.chain_slots[c];
+typedef const __attribute__((address_space(3))) int32_t lds_i32;
+typedef const __attribute__((address_space(3))) float lds_f32;
+__device__ __forceinline__ int32_t chain_slot(const ChainStage &cs, int64_t c_lo, int64_t c) {
+    return ((lds_i32 *)cs.slot)[(c - c_lo) & (CHAIN_LDS - 1)];
 }
-__device__ __forceinline__ float chain_ell(const ChainStage &cs, const ComposeArgs &a, int64_t c_lo, int64_t c,
-                                           int head) {
-    return c - c_lo < CHAIN_LDS ? cs.ell[c - c_lo] : a.pool_ell[(int64_t)a.chain_slots[c] * a.H + head];
+__device__ __forceinline__ float chain_ell(const ChainStage &cs, int64_t c_lo, int64_t c) {
+    return ((lds_f32 *)cs.ell)[(c - c_lo) & (CHAIN_LDS - 1)];
 }
-
+// called by every thread of the workgroup at step c (the condition is uniform); the
+// entries it writes are first read CHAIN_LDS / 2 - 2 steps later, after many barriers
+__device__ __forceinline__ void chain_refill(ChainStage &cs, const ComposeArgs &a, int64_t c_lo, int64_t c_hi,
+                                             int64_t c, int head, int th, int nthreads) {
+    const int64_t d = c - c_lo;
+    if (d < CHAIN_LDS / 2 || (d & (CHAIN_LDS / 2 - 1)) != 0) return;
+    const int64_t j1 = c + CHAIN_LDS < c_hi ? c + CHAIN_LDS : c_hi;
+    for (int64_t j = c + CHAIN_LDS / 2 + th; j < j1; j += nthreads) {
+        const int32_t s = a.chain_slots[j];          // validated in range by the first pass
+        cs.slot[(j - c_lo) & (CHAIN_LDS - 1)] = s;
+        cs.ell[(j - c_lo) & (CHAIN_LDS - 1)] = a.pool_ell[(int64_t)s * a.H + head];
+    }
+}
 
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
@@ -101,12 +119,15 @@ __device__ __forceinline__ void acc_to_b2(const f32x16 &c, int half, bf16x8 &bh,
 struct __align__(16) PStage {
     uint32_t hi[NFRAG * FRAG_U32];
     uint32_t lo[NFRAG * FRAG_U32];
-    float s[D * D];                   // S_i, row-major, loaded straight from HBM into LDS
 };
 
 template <bool MODE_P>
 __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a) {
     __shared__ PStage ps;
+    // S_c, row-major, loaded straight from HBM into LDS; a separate LDS object from the
+    // P fragments, so the compiler sees that staging P does not overlap the S loads
+    // in flight and does not wait for them
+    __shared__ __align__(16) float s_stage[D * D];
     __shared__ ChainStage cs;
     __shared__ int sh_bad;
 
@@ -173,105 +194,101 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
             }
     }
 
-    // ---- P staging: thread th loads float4 pieces q = th + 256*u (u < 16) of P, row q/32,
-    //      columns 4*(q%32) .. +3
-    // both P_c and S_c are fetched as coalesced 16-byte pieces q = th + 256 u
-    // P_c: coalesced 16-byte pieces q = th + 256 u into registers, split to bf16 hi/lo
-    // fragments in LDS at the top of the step.  S_c: HBM -> LDS directly (no
-    // registers), wave w's instruction u moving pieces (16 w + u) * 64 + lane.
-    float4 pre[16];
-    float ell_next = 0.f;     // ell of the record in flight
-#define HYPIC_FETCH_P(CC)                                                                        \
+    // ---- records in flight: P_{c+1} is fetched into registers (coalesced 16-byte
+    //      pieces q = th + 256 u) as soon as P_c has been split to bf16 hi/lo fragments
+    //      in LDS at the top of step c.  S_c goes HBM -> LDS directly (wave w's
+    //      instruction u moves pieces (16 w + u) * 64 + lane), issued at the end of step
+    //      c - 1 and waited for only at the combine of step c.  Per wave the loads issued
+    //      after S_c are exactly the 16 of P_{c+1} (the last step refetches its own P, an
+    //      L2 hit), so the combine waits for vmcnt <= 16.
+    float4 pa[16];
+    float ea = 0.f;               // ell of the record in pa
+#define HYPIC_FETCH_P(PF, EL, CC)                                                                \
     do {                                                                                         \
-        const int64_t frec = (int64_t)chain_slot(cs, a, c_lo, (CC)) * a.H + head;                     \
-        ell_next = chain_ell(cs, a, c_lo, (CC), head);                                                        \
+        const int64_t frec = (int64_t)chain_slot(cs, c_lo, (CC)) * a.H + head;                \
+        EL = chain_ell(cs, c_lo, (CC));                                                 \
         const float4 *fsrc = reinterpret_cast<const float4 *>(a.pool_P + frec * D * D);          \
-        _Pragma("unroll") for (int u = 0; u < 16; ++u) pre[u] = fsrc[th + NT * u];               \
+        _Pragma("unroll") for (int u = 0; u < 16; ++u) PF[u] = fsrc[th + NT * u];                \
     } while (0)
 #define HYPIC_FETCH_S(CC)                                                                        \
     do {                                                                                         \
-        const int64_t frec = (int64_t)chain_slot(cs, a, c_lo, (CC)) * a.H + head;                     \
+        const int64_t frec = (int64_t)chain_slot(cs, c_lo, (CC)) * a.H + head;                \
         const float4 *fss = reinterpret_cast<const float4 *>(a.pool_S + frec * D * D);           \
         _Pragma("unroll") for (int u = 0; u < 16; ++u)                                           \
-            __builtin_amdgcn_global_load_lds(fss + (16 * w + u) * 64 + l,                       \
-                                             &ps.s[(16 * w + u) * 256], 16, 0, 0);               \
+            __builtin_amdgcn_global_load_lds(fss + (16 * w + u) * 64 + l,                        \
+                                             &s_stage[(16 * w + u) * 256], 16, 0, 0);               \
+    } while (0)
+    // one step: stage P_c from PF (then fetch P_{c+1} into PF), acc = P_c state,
+    // state <- e^{ell_c} acc + S_c (S), or state <- acc (P)
+#define HYPIC_STEP(PF, EL)                                                                       \
+    do {                                                                                         \
+        chain_refill(cs, a, c_lo, c_hi, c, head, th, NT);                                        \
+        _Pragma("unroll") for (int u = 0; u < 16; ++u) {                                         \
+            const int q = th + NT * u;                                                           \
+            const int i = q >> 5, k0 = 4 * (q & 31);                                             \
+            const int mb = i >> 5, li = i & 31;                                                  \
+            const int kb = k0 >> 4, c16 = k0 & 15;                                               \
+            const int hh = (c16 >> 2) & 1, e0 = (c16 >> 3) * 4;                                  \
+            uint32_t h01, l01, h23, l23;                                                         \
+            split2(PF[u].x, PF[u].y, h01, l01);                                                  \
+            split2(PF[u].z, PF[u].w, h23, l23);                                                  \
+            const int slot = (mb * 8 + kb) * FRAG_U32 + lane_slot(li, hh) + (e0 >> 1);          \
+            *reinterpret_cast<u32x2 *>(&ps.hi[slot]) = u32x2{h01, h23};                          \
+            *reinterpret_cast<u32x2 *>(&ps.lo[slot]) = u32x2{l01, l23};                          \
+        }                                                                                        \
+        const float le = EL;                                                                     \
+        HYPIC_FETCH_P(PF, EL, c + 1 < c_hi ? c + 1 : c);                                         \
+        lds_barrier();                                   /* fragments visible */                 \
+        bf16x8 bh[8], bl[8];                                                                     \
+        _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) acc_to_b2(st[kb >> 1], kb & 1, bh[kb], bl[kb]); \
+        f32x16 acc[4];                                                                           \
+        _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                         \
+            _Pragma("unroll") for (int q = 0; q < 16; ++q) acc[mb][q] = 0.f;                    \
+        /* A fragments of k-step kb + 1 are read while the products of kb run */               \
+        bf16x8 ah[2][4], al[2][4];                                                               \
+        _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) {                                       \
+            const int f = (mb * 8) * FRAG_U32 + lane_slot(l32, h);                               \
+            ah[0][mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&ps.hi[f])); \
+            al[0][mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&ps.lo[f])); \
+        }                                                                                        \
+        _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) {                                       \
+            const int cb = kb & 1, nb = cb ^ 1;                                                  \
+            if (kb + 1 < 8) {                                                                    \
+                _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) {                               \
+                    const int f = (mb * 8 + kb + 1) * FRAG_U32 + lane_slot(l32, h);              \
+                    ah[nb][mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&ps.hi[f])); \
+                    al[nb][mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&ps.lo[f])); \
+                }                                                                                \
+            }                                                                                    \
+            _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma(ah[cb][mb], bh[kb], acc[mb]); \
+            _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma(ah[cb][mb], bl[kb], acc[mb]); \
+            _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma(al[cb][mb], bh[kb], acc[mb]); \
+        }                                                                                        \
+        if (MODE_P) {                                                                            \
+            _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) st[mb] = acc[mb];                   \
+        } else {                                                                                 \
+            asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   /* this wave's S_c pieces */     \
+            lds_barrier();                               /* everyone's S_c pieces */            \
+            const float sc = expf(le);                                                           \
+            _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                     \
+                _Pragma("unroll") for (int q = 0; q < 16; ++q)                                   \
+                    st[mb][q] = sc * acc[mb][q] + s_stage[(32 * mb + acc_row(q, h)) * D + col0 + l32]; \
+        }                                                                                        \
+        ell += (double)le;                                                                       \
+        lds_barrier();       /* fragments and S_c read by all before they are replaced */       \
+        if (!MODE_P) HYPIC_FETCH_S(c + 1 < c_hi ? c + 1 : c);  /* last step: an L2 hit */       \
     } while (0)
     if (c < c_hi) {
-        HYPIC_FETCH_P(c);
+        HYPIC_FETCH_P(pa, ea, c);
         if (!MODE_P) HYPIC_FETCH_S(c);
+        while (true) {
+            HYPIC_STEP(pa, ea);
+            if (++c >= c_hi) break;
+        }
+        // the last step's S load (a refetch) lands in LDS before the workgroup ends
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-
-    for (; c < c_hi; ++c) {
-        const float le = ell_next;
-        // stage P_c (bf16 hi/lo, fragment order)
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int q = th + NT * u;
-            const int i = q >> 5, k0 = 4 * (q & 31);
-            const int mb = i >> 5, li = i & 31;
-            const int kb = k0 >> 4, c16 = k0 & 15;
-            const int hh = (c16 >> 2) & 1, e0 = (c16 >> 3) * 4;
-            uint32_t h01, l01, h23, l23;
-            split2(pre[u].x, pre[u].y, h01, l01);
-            split2(pre[u].z, pre[u].w, h23, l23);
-            const int slot = (mb * 8 + kb) * FRAG_U32 + lane_slot(li, hh) + (e0 >> 1);
-            *reinterpret_cast<u32x2 *>(&ps.hi[slot]) = u32x2{h01, h23};
-            *reinterpret_cast<u32x2 *>(&ps.lo[slot]) = u32x2{l01, l23};
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this wave's S_c pieces have landed
-        lds_barrier();
-        float sadd[4][16];
-        if (!MODE_P) {
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) sadd[mb][q] = ps.s[(32 * mb + acc_row(q, h)) * D + col0 + l32];
-            lds_barrier();                                     // S_c read by all before S_{c+1} lands
-        }
-        if (c + 1 < c_hi) {                                    // the next record flies during this product
-            HYPIC_FETCH_P(c + 1);
-            if (!MODE_P) HYPIC_FETCH_S(c + 1);
-        }
-        // acc = P_c * state, hi.hi + hi.lo + lo.hi
-        // the state's B fragments (hi, lo) for all 8 k-steps, once per step; the
-        // state itself is not needed again until the combine overwrites it
-        bf16x8 bh[8], bl[8];
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb) acc_to_b2(st[kb >> 1], kb & 1, bh[kb], bl[kb]);
-        f32x16 acc[4];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[mb][q] = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            bf16x8 ah[4], al[4];
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const int f = (mb * 8 + kb) * FRAG_U32 + lane_slot(l32, h);
-                ah[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&ps.hi[f]));
-                al[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&ps.lo[f]));
-            }
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma(ah[mb], bh[kb], acc[mb]);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma(ah[mb], bl[kb], acc[mb]);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma(al[mb], bh[kb], acc[mb]);
-        }
-        if (MODE_P) {
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) st[mb] = acc[mb];
-        } else {
-            const float sc = expf(le);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) st[mb][q] = sc * acc[mb][q] + sadd[mb][q];
-        }
-        ell += (double)le;
-        lds_barrier();       // everyone is done with this P before the next is staged
-    }
+#undef HYPIC_STEP
 #undef HYPIC_FETCH_P
 #undef HYPIC_FETCH_S
 #pragma unroll
@@ -385,7 +402,7 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
     float sa[16], sb[16];
     float ea = 0.f, eb = 0.f;     // ell of the record each set holds
 #define HYPIC_PROW(CC) \
-    (a.pool_P + ((int64_t)chain_slot(cs, a, c_lo, (CC)) * a.H + head) * D * D + (int64_t)(32 * w + (l >> 5)) * D + 4 * l32)
+    (a.pool_P + ((int64_t)chain_slot(cs, c_lo, (CC)) * a.H + head) * D * D + (int64_t)(32 * w + (l >> 5)) * D + 4 * l32)
 #define HYPIC_PFETCH(PF, PROW)                                                                      \
     do {                                                                                            \
         _Pragma("unroll") for (int u = 0; u < 16; ++u)                                              \
@@ -394,7 +411,7 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
 #define HYPIC_SFETCH(SV, CC)                                                                        \
     do {                                                                                            \
         if (!MODE_P) {                                                                              \
-            const float *ss_ = a.pool_S + ((int64_t)chain_slot(cs, a, c_lo, (CC)) * a.H + head) * D * D + col; \
+            const float *ss_ = a.pool_S + ((int64_t)chain_slot(cs, c_lo, (CC)) * a.H + head) * D * D + col; \
             _Pragma("unroll") for (int q = 0; q < 16; ++q) SV[q] = ss_[(32 * w + acc_row(q, h)) * D]; \
         }                                                                                           \
     } while (0)
@@ -402,6 +419,7 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
     // state <- e^{ell_c} P_c state + S_c
 #define HYPIC_STEP(PF, SV, EL, PAR)                                                                 \
     do {                                                                                            \
+        chain_refill(cs, a, c_lo, c_hi, c, head, th, NT);                                           \
         _Pragma("unroll") for (int half = 0; half < 2; ++half) {                                    \
             bf16x8 bh_, bl_;                                                                        \
             acc_to_b2(st, half, bh_, bl_);                                                          \
@@ -423,7 +441,7 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
             PF[u] = *reinterpret_cast<const float4 *>(pn_ + 2 * u * D);                             \
         }                                                                                           \
         const float le_ = EL;                                                                       \
-        EL = chain_ell(cs, a, c_lo, more_ ? c + 2 : c, head);          \
+        EL = chain_ell(cs, c_lo, more_ ? c + 2 : c);          \
         lds_barrier();                                                                              \
         f32x16 acc_ = {}, acc1_ = {};                                                               \
         _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) {                                          \
@@ -449,12 +467,12 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
     if (c < c_hi) {
         HYPIC_PFETCH(pa, HYPIC_PROW(c));
         HYPIC_SFETCH(sa, c);
-        ea = chain_ell(cs, a, c_lo, c, head);
+        ea = chain_ell(cs, c_lo, c);
     }
     if (c + 1 < c_hi) {
         HYPIC_PFETCH(pb, HYPIC_PROW(c + 1));
         HYPIC_SFETCH(sb, c + 1);
-        eb = chain_ell(cs, a, c_lo, c + 1, head);
+        eb = chain_ell(cs, c_lo, c + 1);
     }
     // even steps use pa/sa and exchange buffer 0, odd steps pb/sb and buffer 1 (the
     // exchange is double-buffered, so one barrier per step suffices)

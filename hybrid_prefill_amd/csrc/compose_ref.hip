@@ -12,7 +12,8 @@
 // GDN work split: one workgroup per (request, head, 64-column slab of S, or
 // of P when the composed P is asked for).  The slab stays in LDS across the
 // chain; P_i streams through LDS in 32-column blocks.  Scalar and diagonal
-// families: one workgroup per (request, head), the state in registers.
+// families: 1024 state elements per workgroup, four per thread in registers (or,
+// for unaligned buffers, one workgroup per (request, head)).
 #include "hypic_internal.h"
 
 namespace hypic {
@@ -183,6 +184,76 @@ __global__ __launch_bounds__(NT) void compose_sd_kernel(ComposeArgs a) {
     }
 }
 
+// Scalar / diagonal, wide: the fold is elementwise, so the record is spread over
+// DK DV / 1024 workgroups per (request, head) and each thread keeps four consecutive
+// elements of one row (16-byte loads and stores).  The chain is folded eight steps at
+// a time: the eight slots (wave-uniform), then every step's gate and S_i piece are
+// loaded before the first is used, so one batch costs about two load latencies
+// instead of eight dependent round trips.
+constexpr int WE = 4 * NT;               // elements per workgroup
+constexpr int CB = 8;                    // chain steps per batch
+template <int FAM, int DK, int DV>
+__global__ __launch_bounds__(NT) void compose_sd_wide_kernel(ComposeArgs a) {
+    constexpr int NBLK = DK * DV / WE;
+    __shared__ int sh_bad;
+    const int tid = threadIdx.x;
+    const int blk = blockIdx.x % NBLK;
+    const int unit = blockIdx.x / NBLK;
+    const int h = unit % a.H;
+    const int r = unit / a.H;
+    const int64_t orec = (int64_t)r * a.H + h;
+    const int e0 = blk * WE + 4 * tid;       // first of this thread's four elements
+    const int row = e0 / DV;                 // DV % 4 == 0: the four share a row
+    const bool row_lead = (e0 % DV) == 0;
+    float *out = a.out_S + orec * DK * DV + e0;
+    int64_t lo, hi;
+    const int bad = check_chain(a, r, lo, hi, &sh_bad);
+    if (bad) {
+        if (blk == 0 && tid == 0) raise_flag(a.err_flag, bad == 1 ? HYPIC_EFLAG_SLOT_OUT_OF_RANGE : HYPIC_EFLAG_BAD_OFFSETS);
+        const float nanv = __int_as_float(0x7fc00000);
+        *reinterpret_cast<float4 *>(out) = make_float4(nanv, nanv, nanv, nanv);
+        if (a.out_ell) {
+            if (FAM == HYPIC_DIAGONAL) { if (row_lead) a.out_ell[orec * DK + row] = nanv; }
+            else if (blk == 0 && tid == 0) a.out_ell[orec] = nanv;
+        }
+        return;
+    }
+    float4 s = a.init_S ? *reinterpret_cast<const float4 *>(a.init_S + orec * DK * DV + e0)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    double ell = 0.0;
+    for (int64_t base = lo; base < hi; base += CB) {
+        const int nb = hi - base < CB ? (int)(hi - base) : CB;
+        int64_t rec[CB];
+#pragma unroll
+        for (int k = 0; k < CB; ++k) rec[k] = (int64_t)a.chain_slots[k < nb ? base + k : base] * a.H + h;
+        float4 si[CB];
+        float le[CB];
+#pragma unroll
+        for (int k = 0; k < CB; ++k) {
+            si[k] = *reinterpret_cast<const float4 *>(a.pool_S + rec[k] * DK * DV + e0);
+            le[k] = FAM == HYPIC_DIAGONAL ? a.pool_ell[rec[k] * DK + row] : a.pool_ell[rec[k]];
+        }
+#pragma unroll
+        for (int k = 0; k < CB; ++k) {
+            if (k < nb) {
+                const float sc = expf(le[k]);
+                s.x = sc * s.x + si[k].x;
+                s.y = sc * s.y + si[k].y;
+                s.z = sc * s.z + si[k].z;
+                s.w = sc * s.w + si[k].w;
+                ell += (double)le[k];
+            }
+        }
+    }
+    *reinterpret_cast<float4 *>(out) = s;
+    if (a.out_ell) {
+        if (FAM == HYPIC_DIAGONAL) { if (row_lead) a.out_ell[orec * DK + row] = (float)ell; }
+        else if (blk == 0 && tid == 0) a.out_ell[orec] = (float)ell;
+    }
+}
+
+__host__ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
 template <int DK, int DV>
 hipError_t launch_dims(const ComposeArgs &a, hipStream_t stream) {
     const int64_t units = (int64_t)a.num_requests * a.H;
@@ -190,6 +261,12 @@ hipError_t launch_dims(const ComposeArgs &a, hipStream_t stream) {
         const int nslab_S = DV / NSL;
         const int nslab = nslab_S + (a.out_P ? DK / NSL : 0);
         hipLaunchKernelGGL((compose_dense_ref_kernel<DK, DV>), dim3((unsigned)(units * nslab)), dim3(NT), 0, stream, a, nslab_S);
+    } else if (aligned16(a.pool_S) && aligned16(a.out_S) && (!a.init_S || aligned16(a.init_S))) {
+        const dim3 grid((unsigned)(units * (DK * DV / WE)));
+        if (a.family == HYPIC_SCALAR)
+            hipLaunchKernelGGL((compose_sd_wide_kernel<HYPIC_SCALAR, DK, DV>), grid, dim3(NT), 0, stream, a);
+        else
+            hipLaunchKernelGGL((compose_sd_wide_kernel<HYPIC_DIAGONAL, DK, DV>), grid, dim3(NT), 0, stream, a);
     } else if (a.family == HYPIC_SCALAR) {
         hipLaunchKernelGGL((compose_sd_kernel<HYPIC_SCALAR, DK, DV>), dim3((unsigned)units), dim3(NT), 0, stream, a);
     } else {

@@ -283,6 +283,39 @@ def test_compose_d128_chain_paths(num_req):
         assert worst[0] <= 1e-4 and worst[1] <= 1e-4 and worst[2] <= 1e-5
 
 
+@pytest.mark.parametrize("num_req", [1, 17])
+def test_compose_d128_long_chains(num_req):
+    """d=128 chains longer than the 1024 slot entries the compose kernels keep in LDS
+    (the ring is refilled every 512 steps), on both launch paths (1 request: four
+    workgroups per chain; 17 requests x 32 heads: one per chain)."""
+    H, d, nslots = 32, 128, 40
+    rng = np.random.default_rng(950 + num_req)
+    q, _ = np.linalg.qr(rng.standard_normal((nslots, H, d, d)))
+    P = q * rng.uniform(0.9, 1.0, size=(nslots, H, 1, d))
+    S = rng.standard_normal((nslots, H, d, d))
+    ell = rng.uniform(-0.05, 0.0, size=(nslots, H))
+    pool = hp.Pool.allocate(hp.GDN, nslots, H, d, d, device="cuda", fill=0.0)
+    pool.P.copy_(torch.from_numpy(P).float())
+    pool.S.copy_(torch.from_numpy(S).float())
+    pool.log_scale.copy_(torch.from_numpy(ell).float())
+    lens = [1537] + ([1025] + [int(x) for x in rng.integers(0, 9, size=num_req - 2)] if num_req > 1 else [])
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    flat = rng.integers(0, nslots, size=int(offs[-1])).astype(np.int32)
+    out_ell = torch.empty((num_req, H), device="cuda")
+    say(f"[compose d128 long] requests={num_req} lens={lens[:4]}")
+    out_S = hp.compose_chain(pool, dev_i64(offs), dev_i32(flat), out_log_scale=out_ell)
+    torch.cuda.synchronize()
+    worst = [0.0, 0.0]
+    for h in (0, 31):
+        rS, rell, _ = oracle.compose(hp.GDN, np64(pool.log_scale[:, h:h + 1]), np64(pool.P[:, h:h + 1]),
+                                     np64(pool.S[:, h:h + 1]), offs, flat)
+        for r in range(num_req):
+            worst[0] = max(worst[0], rel_fro(np64(out_S[r, h]), rS[r, 0]))
+            worst[1] = max(worst[1], abs(float(out_ell[r, h]) - float(rell[r, 0])) / max(1.0, abs(float(rell[r, 0]))))
+    say(f"   S err {worst[0]:.2e}  ell rel err {worst[1]:.2e}")
+    assert worst[0] <= 1e-4 and worst[1] <= 1e-5
+
+
 def test_compose_out_of_range_slot_flags_and_isolates():
     pool = _gdn_pool()
     chains = [[0, 1, 2], [1, 9, 2], [3, 4]]          # slot 9 is outside the 6-slot pool
@@ -302,6 +335,46 @@ def test_compose_out_of_range_slot_flags_and_isolates():
     torch.cuda.synchronize()
     assert int(err.item()) & hp.EFLAG_BAD_OFFSETS
     assert torch.all(torch.isnan(out[1])) and not torch.any(torch.isnan(out[0]))
+
+
+@pytest.mark.parametrize("family", [hp.SCALAR, hp.DIAGONAL])
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_compose_scalar_diagonal_chains(family, dims):
+    """Scalar / diagonal compose on synthetic records against the oracle: chain lengths
+    around the kernel's 8-step load batches (0, 1, 7, 8, 9, 17, 20), with and without an
+    initial state; a chain of one returns the slot's S bit for bit; an out-of-range slot
+    flags and NaN-fills only its request."""
+    dk, dv = dims
+    H, nslots = 3, 10
+    rng = np.random.default_rng(970 + 7 * family + dk + dv // 2)
+    pool = hp.Pool.allocate(family, nslots, H, dk, dv, device="cuda", fill=0.0)
+    pool.S.copy_(torch.from_numpy(rng.standard_normal((nslots, H, dk, dv))).float())
+    ell_shape = (nslots, H, dk) if family == hp.DIAGONAL else (nslots, H)
+    pool.log_scale.copy_(torch.from_numpy(rng.uniform(-0.3, 0.0, size=ell_shape)).float())
+    lens = [0, 1, 7, 8, 9, 17, 20]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    flat = rng.integers(0, nslots, size=int(offs[-1])).astype(np.int32)
+    R = len(lens)
+    for with_init in (False, True):
+        init = torch.randn((R, H, dk, dv), device="cuda") if with_init else None
+        out_ell = torch.empty((R, H, dk) if family == hp.DIAGONAL else (R, H), device="cuda")
+        out = hp.compose_chain(pool, dev_i64(offs), dev_i32(flat), init_S=init, out_log_scale=out_ell)
+        torch.cuda.synchronize()
+        rS, rell, _ = oracle.compose(family, np64(pool.log_scale), None, np64(pool.S), offs, flat,
+                                     init_S=None if init is None else np64(init))
+        for r in range(R):
+            for h in range(H):
+                assert rel_fro(np64(out[r, h]), rS[r, h]) <= 1e-5, (r, h)
+        assert np.max(np.abs(np64(out_ell) - rell)) <= 1e-5
+        if not with_init:
+            assert torch.equal(out[1], pool.S[int(flat[offs[1]])])
+            assert torch.all(out[0] == 0)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = hp.compose_chain(pool, dev_i64([0, 2, 4]), dev_i32([1, 2, 3, nslots + 4]), err_flag=err)
+    clean = hp.compose_chain(pool, dev_i64([0, 2]), dev_i32([1, 2]))
+    torch.cuda.synchronize()
+    assert int(err.item()) == hp.EFLAG_SLOT_OUT_OF_RANGE
+    assert torch.all(torch.isnan(out[1])) and torch.equal(out[0], clean[0])
 
 
 def test_build_error_flags():
@@ -356,7 +429,11 @@ def test_scalar_mfma_build_error_flags():
 @pytest.mark.parametrize("K,C,dtype,act,bias", [(4, 4096, torch.bfloat16, 0, False),
                                                 (4, 4096, torch.bfloat16, 1, True),
                                                 (2, 96, torch.float32, 1, True),
-                                                (8, 200, torch.float32, 0, True)])
+                                                (8, 200, torch.float32, 0, True),
+                                                # channel counts off the 16-byte vector width:
+                                                # the one-channel-per-thread kernel
+                                                (3, 100, torch.bfloat16, 0, True),
+                                                (4, 30, torch.float32, 1, False)])
 def test_conv_warmup_equals_sequential_conv(K, C, dtype, act, bias):
     rng = np.random.default_rng(800 + K)
     lens = rng.integers(K, 40, size=12)
@@ -378,8 +455,9 @@ def test_conv_warmup_equals_sequential_conv(K, C, dtype, act, bias):
     assert worst <= 1e-4
 
 
-def test_conv_warmup_bad_index():
-    K, C = 4, 64
+@pytest.mark.parametrize("C", [64, 60])
+def test_conv_warmup_bad_index(C):
+    K = 4
     x = synth.conv_stream(12, C, torch.bfloat16, 810, "cuda").reshape(4, 3, C)
     w = synth.conv_weights(C, K, 811, "cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
