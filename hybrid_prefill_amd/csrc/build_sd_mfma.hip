@@ -34,16 +34,19 @@
 // read (ds_read_b64_tr_b16) and put the weights on the K^T fragment (scalar:
 // beta_t e^{G_b - L_t} per token; diagonal: beta_t e^{G_i - L_{t,i}} per token
 // and key channel), so a chunk is four MFMAs per value block.  Operand reads are
-// issued before the first product that uses them.  Every wave takes what it
-// needs, so the waves share nothing but the staged tiles.
+// issued before the first product that uses them.
 //
-// Streaming: four more waves only load: keys, values (and the diagonal family's
-// gates and beta) go from HBM straight into LDS (global_load_lds), NBUF chunks
-// deep, so the compute waves never stall on the load queue (a single wave
-// cannot issue a chunk's loads as fast as the compute waves use it); one
-// workgroup barrier per chunk.  Tail
-// rows past the segment repeat its last row and are masked at use (beta and
-// log alpha of those tokens read as 0).
+// Streaming: four more waves load: keys, values (and the diagonal family's gates
+// and beta) go from HBM straight into LDS (global_load_lds), NBUF chunks deep, so
+// the compute waves never stall on the load queue (a single wave cannot issue a
+// chunk's loads as fast as the compute waves use it); one workgroup barrier per
+// chunk.  For the diagonal family the loading waves also compute the
+// per-(token, channel) factors and the chunk decay, once per chunk and one chunk
+// ahead, into parity-buffered LDS tiles (the compute waves of a key block would
+// otherwise both compute the same ones); their gates come in a ring of their own,
+// one chunk further ahead than the keys and values.  Tail rows past the segment
+// repeat its last row and are masked at use (beta and log alpha of those tokens
+// read as 0).
 #include "hypic_internal.h"
 
 namespace hypic {
@@ -151,23 +154,37 @@ template <bool DIAG, int NJB>
 struct __align__(16) SdBuf {
     u16 Km[DIAG ? CH * DKC : CH * D];
     u16 Vm[DIAG ? CH * D : CH * 32 * NJB];
-    // diagonal family only (the scalar family reads its gates once per table block)
-    float gate[DIAG ? CH * DKC : 4];     // [token][key channel of the workgroup]
-    float beta[DIAG ? CH : 4];
-    float dummy[DIAG ? CH : 4];          // target of the loads that keep per-wave load counts equal
 };
+// Diagonal family only (the scalar family reads its gates once per table block): a
+// chunk's gates and beta, in a ring of their own (loaded one chunk further ahead than
+// the keys and values).  Loading wave lw's share of the gates is channels
+// 16 lw .. 16 lw + 15 of the workgroup's 64 for all 64 tokens (the channels it computes
+// the factors of), in global_load_lds order: instruction j, lane l holds token
+// 16 j + l / 4, channels 16 lw + 4 (l % 4) .. + 3; every loading wave keeps its own
+// copy of beta.  So a loading wave reads only what it loaded itself.
+struct __align__(16) GateBuf {
+    float gate[CH * DKC];
+    float beta[NLW][CH];
+};
+constexpr int NBG = 3;                   // gate ring depth
+__device__ __forceinline__ int gate_idx(int t, int ci) {   // token t, workgroup key channel ci
+    return ((((ci >> 4) << 2) + (t >> 4)) * 64 + 4 * (t & 15) + ((ci & 15) >> 2)) * 4 + (ci & 3);
+}
+// factor tiles: row = workgroup key channel (64 floats), 16-byte granule g at slot g ^ (row % 16)
+__device__ __forceinline__ int fac_idx(int ci, int g) { return ci * CH + ((g ^ (ci & 15)) << 2); }
 
 constexpr int TBT = 2048;                // tokens per scalar weight table
 
 template <bool DIAG, int NJB, int NBUF>
 struct __align__(16) SdSmem {
     SdBuf<DIAG, NJB> buf[NBUF];
-    float wsc[4][DIAG ? CH : 1];         // per wave: diagonal beta
-    float wt[DIAG ? 4 : TBT];            // scalar: beta_t e^{G_b - L_t} of the current table block
+    GateBuf gbuf[DIAG ? NBG : 0];
+    // (every array read with 16-byte loads starts 16-byte aligned)
+    __align__(16) float fac[DIAG ? 2 : 1][DIAG ? DKC * CH : 4];   // diagonal, by chunk parity: beta_t e^{G_i - L_{t,i}}
+    __align__(16) float eg[DIAG ? 2 : 1][DIAG ? DKC : 4];         // diagonal, by chunk parity: e^{G_i} of the chunk
+    __align__(16) float wt[DIAG ? 4 : TBT];   // scalar: beta_t e^{G_b - L_t} of the current table block
     float wtot[NWC];                     // scalar: per-wave sums while a table is built
     double ellw[4];                      // scalar: per-wave ell
-    float gd[4][DIAG ? 32 : 1];          // diagonal, per wave: chunk decay G_i of its channels
-    float tot[4][2][32][DIAG ? 4 : 1];   // diagonal, per wave: token-group sums of each lane half
     int64_t t0, n;
     int32_t slot, state;
 };
@@ -192,6 +209,19 @@ __device__ __forceinline__ void wait_chunks(int k) {
     }
 }
 
+// s_waitcnt vmcnt(k) for a wave-uniform k (rounded down to an immediate <= K; a
+// smaller count only waits longer)
+template <int K>
+__device__ __forceinline__ void vm_wait(int k) {
+    static_assert(K <= 63, "vmcnt limit");
+    if constexpr (K == 0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+        if (k >= K) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K) : "memory");
+        else vm_wait<K - 1>(k);
+    }
+}
+
 template <int FAM, int NSPLIT>
 __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) void sd_build_mfma_kernel(BuildArgs a) {
     constexpr bool DIAG = FAM == HYPIC_DIAGONAL;
@@ -199,14 +229,15 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     static_assert(!DIAG || NSPLIT == 2, "the diagonal family splits the key channels in two");
     // chunks staged: as many as fit beside the other workgroup on the CU (value
     // split 4: two per CU) or alone
-    constexpr int NBUF = DIAG ? 3 : NSPLIT == 4 ? 3 : NSPLIT == 2 ? 6 : 4;
+    constexpr int NBUF = NSPLIT == 4 || DIAG ? 3 : NSPLIT == 2 ? 6 : 4;
     constexpr int DIST = NBUF - 1;                     // prefetch distance in chunks
     // global_load_lds instructions of each loading wave per chunk: its share of the
     // keys, values, and for the diagonal family gates, plus one dword row (beta or a
     // dummy)
     constexpr int NKI = (DIAG ? 8 : 16) / NLW, NVI = (DIAG ? 16 : 4 * NJB) / NLW, NGI = DIAG ? 16 / NLW : 0;
     static_assert(8 % NLW == 0 && (4 * NJB) % NLW == 0 && 16 % NLW == 0, "load shares");
-    constexpr int LPW = NKI + NVI + (DIAG ? NGI + 1 : 0);
+    constexpr int LPW = NKI + NVI;                     // keys and values (the diagonal gates are counted apart)
+    constexpr int LPG = NGI + 1;                       // diagonal: gates and beta
     constexpr int TBC = TBT / CH;                      // chunks per scalar weight table
     // with two value blocks per workgroup the scalar compute waves read a chunk's
     // operands one chunk ahead (two register sets fit beside the state), so at the
@@ -275,13 +306,6 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
             for (int j = 0; j < NKI; ++j) gll16(kc + ko[j], &Bf.Km[KR * (lw + NLW * j) * KW]);
 #pragma unroll
             for (int j = 0; j < NVI; ++j) gll16(vc + vo[j], &Bf.Vm[VR * (lw + NLW * j) * VW]);
-            if (DIAG) {
-#pragma unroll
-                for (int j = 0; j < NGI; ++j)
-                    gll16(gh ? gh + base * a.la_st + go[j] : (const float *)a.k, &Bf.gate[4 * (lw + NLW * j) * DKC]);
-                if (lw == 0 && bh) gll4(bh + base * a.b_st + go[NGI], Bf.beta);
-                else gll4(a.k, Bf.dummy);
-            }
         } else {
             const int cl = rem < CH ? (int)rem : CH;
             int ll = l;
@@ -297,15 +321,30 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
                 const int u = lw + NLW * j, r = VR * u + ll / VG, rs = r < cl ? r : cl - 1;
                 gll16(vh + (base + rs) * a.v_st + 8 * vswz(r, ll % VG), &Bf.Vm[VR * u * VW]);
             }
-            if (DIAG) {
+        }
+    };
+    // diagonal: chunk C's gates and beta (LPG instructions per loading wave)
+    auto issue_g = [&](int64_t C, int lw, const uint32_t *go) {
+        if constexpr (DIAG) {
+            GateBuf &Gf = sm.gbuf[C % NBG];
+            const int64_t base = C * CH, rem = n - base;
+            if (rem >= CH && small_st) {
+#pragma unroll
+                for (int j = 0; j < NGI; ++j)
+                    gll16(gh ? gh + base * a.la_st + go[j] : (const float *)a.k, &Gf.gate[(4 * lw + j) * 256]);
+                gll4(bh ? bh + base * a.b_st + go[NGI] : (const float *)a.k, Gf.beta[lw]);
+            } else {
+                const int cl = rem < CH ? (int)rem : CH;
+                int ll = l;
+                asm volatile("" : "+v"(ll));
 #pragma unroll
                 for (int j = 0; j < NGI; ++j) {
-                    const int u = lw + NLW * j, r = 4 * u + (ll >> 4), rs = r < cl ? r : cl - 1;
-                    gll16(gh ? gh + (base + rs) * a.la_st + 4 * (ll & 15) : (const float *)a.k, &Bf.gate[4 * u * DKC]);
+                    const int r = 16 * j + (ll >> 2), rs = r < cl ? r : cl - 1;
+                    gll16(gh ? gh + (base + rs) * a.la_st + 4 * (4 * lw + (ll & 3)) : (const float *)a.k,
+                          &Gf.gate[(4 * lw + j) * 256]);
                 }
                 const int rs = ll < cl ? ll : cl - 1;
-                if (lw == 0 && bh) gll4(bh + (base + rs) * a.b_st, Bf.beta);
-                else gll4(a.k, Bf.dummy);
+                gll4(bh ? bh + (base + rs) * a.b_st : (const float *)a.k, Gf.beta[lw]);
             }
         }
     };
@@ -412,11 +451,91 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         }
 #pragma unroll
         for (int j = 0; j < NGI; ++j) {
-            const int r = 4 * (lw + NLW * j) + (l >> 4);
-            go[j] = small_st ? (uint32_t)(r * a.la_st + 4 * (l & 15)) : 0u;
+            const int r = 16 * j + (l >> 2);
+            go[j] = small_st ? (uint32_t)(r * a.la_st + 4 * (4 * lw + (l & 3))) : 0u;
         }
         go[NGI] = small_st ? (uint32_t)(l * a.b_st) : 0u;
-        for (int64_t c = 0; c < DIST && c < nc; ++c) issue(c, lw, ko, vo, go);
+        if (!DIAG)
+            for (int64_t c = 0; c < DIST && c < nc; ++c) issue(c, lw, ko, vo, go);
+        if constexpr (DIAG) {
+            // The loading waves also compute every chunk's per-(token, channel) factors,
+            // one chunk ahead of the compute waves: wave lw takes channels
+            // ci = 16 lw + l % 16 of the workgroup's 64, lane quarter tq = l / 16 the tokens
+            // 16 tq .. 16 tq + 15 (only gates this wave loaded itself, so its own vmcnt
+            // wait is enough).  Per chunk C:
+            //   L_t (inclusive cumulative log decay of the channel), G = L_63,
+            //   fac[ci][t] = beta_t e^{G - L_t},  eg[ci] = e^G,
+            // written to the parity-C tiles before the barrier that starts chunk C.
+            const int cc = l & 15, tq = l >> 4, ci = 16 * lw + cc;
+            double ell_q = 0.0;                           // this lane's quarter of the channel's sum
+            auto factors = [&](int64_t C) {
+                const GateBuf &Bf = sm.gbuf[C % NBG];
+                const int64_t rem = n - C * CH;
+                const int cl = rem < CH ? (int)rem : CH;
+                float x[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) x[j] = Bf.gate[gate_idx(16 * tq + j, ci)];
+                float run = 0.f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    run += (16 * tq + j < cl && a.log_alpha) ? x[j] : 0.0f;
+                    x[j] = run;
+                }
+                ell_q += (double)run;
+                const float q0 = __shfl(run, cc), q1 = __shfl(run, cc + 16), q2 = __shfl(run, cc + 32),
+                            q3 = __shfl(run, cc + 48);
+                const float off = (tq > 0 ? q0 : 0.f) + (tq > 1 ? q1 : 0.f) + (tq > 2 ? q2 : 0.f);
+                const float G = (q0 + q1) + (q2 + q3);
+                const int par = (int)(C & 1);
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    float f[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * tq + 4 * gq + e;
+                        const float b = t < cl ? (a.beta ? Bf.beta[lw][t] : 1.0f) : 0.0f;
+                        f[e] = b * __expf(G - (off + x[4 * gq + e]));
+                    }
+                    *reinterpret_cast<float4 *>(&sm.fac[par][fac_idx(ci, 4 * tq + gq)]) =
+                        make_float4(f[0], f[1], f[2], f[3]);
+                }
+                if (tq == 0) sm.eg[par][ci] = __expf(G);
+            };
+            // Issue order: "step" j >= -3 issues the gates of chunk j + 3, then the keys and
+            // values of chunk j + 2 (those that exist); steps -3 .. -1 run before the loop,
+            // step c after the barrier of chunk c.  So at step c the gates of chunk c + 1
+            // (step c - 2) have two steps to land and the keys and values of chunk c + 1
+            // (step c - 1) one.  A wait names how many of this wave's loads were issued
+            // after the one it waits for.
+            auto nG = [&](int64_t m) { return m < nc ? LPG : 0; };
+            auto nKV = [&](int64_t m) { return m < nc ? LPW : 0; };
+            for (int64_t j = -3; j < 0; ++j) {
+                if (j + 3 < nc) issue_g(j + 3, lw, go);
+                if (j + 2 >= 0 && j + 2 < nc) issue(j + 2, lw, ko, vo, go);
+            }
+            if (nc > 0) {
+                vm_wait<2 * LPG + 3 * LPW>(nG(1) + nKV(0) + nG(2) + nKV(1));   // gates of chunk 0
+                factors(0);
+                vm_wait<2 * LPG + 3 * LPW>(nG(2) + nKV(1));                    // keys, values of chunk 0
+            }
+            for (int64_t c = 0; c < nc; ++c) {
+                lds_barrier();                            // chunk c (and its factors) visible
+                if (c + 3 < nc) issue_g(c + 3, lw, go);
+                if (c + 2 < nc) issue(c + 2, lw, ko, vo, go);
+                if (c + 1 < nc) {
+                    vm_wait<2 * LPG + 3 * LPW>(nKV(c) + nG(c + 2) + nKV(c + 1) + nG(c + 3) + nKV(c + 2));
+                    factors(c + 1);                       // gates of chunk c + 1 landed
+                    vm_wait<2 * LPG + 3 * LPW>(nG(c + 3) + nKV(c + 2));   // keys, values of chunk c + 1
+                }
+            }
+            // record: the channel's ell (sum of the lane quarters)
+            ell_q += __shfl_xor(ell_q, 16);
+            ell_q += __shfl_xor(ell_q, 32);
+            if (tq == 0)
+                a.pool_ell[((int64_t)slot * a.H + head) * D + kc0 + ci] =
+                    state == 2 ? __int_as_float(0x7fc00000) : (float)ell_q;
+            return;
+        }
         // make_table's two barriers (these waves have no tokens, and no load to wait for)
         if (!DIAG) {
             lds_barrier();
@@ -506,86 +625,41 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
             for (int64_t c = 0; c < nc; ++c) step(c, oa, oa);
         }
     } else {
+    // the loading waves computed the chunk's factors: decay, scale, multiply
+    const int i = 32 * (w >> 1) + l32;                // this lane's key channel (of the workgroup's 64)
     for (int64_t c = 0; c < nc; ++c) {
-        lds_barrier();                                // chunk c visible; chunk c - 1's buffer free
-
+        lds_barrier();                                // chunk c and its factors visible; chunk c - 1's buffer free
         const SdBuf<DIAG, NJB> &B = sm.buf[c % NBUF];
-        const int64_t rem = n - c * CH;
-        const int cl = rem < CH ? (int)rem : CH;
-        int thv = th;
-        asm volatile("" : "+v"(thv));
-        const int lv = thv & 63, hv = lv >> 5, lv32 = lv & 31;
-
-        // ---- per-(token, channel) factors.  Lane (channel i = 32 (w / 2) + lv32 of the
-        //      workgroup's 64, half hv) takes tokens 16 ks + 8 hv + e, e < 8: the tokens of
-        //      its K^T fragment in k-step ks.  Every gate read is issued before the first
-        //      is used (rows past the segment hold finite copies, masked after the read).
-        const int i = 32 * (w >> 1) + lv32;
-        sm.wsc[w][lv] = lv < cl ? (a.beta ? B.beta[lv] : 1.0f) : 0.0f;
-        float x[4][8], gsum[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[ks][e] = B.gate[(16 * ks + 8 * hv + e) * DKC + i];
-        float csum = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            float s = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = 16 * ks + 8 * hv + e;
-                s += (t < cl && a.log_alpha) ? x[ks][e] : 0.0f;
-                x[ks][e] = s;                        // inclusive prefix inside the group
-            }
-            gsum[ks] = s;
-            csum += s;
-            sm.tot[w][hv][lv32][ks] = s;
-        }
-        ell += (double)csum;
-        wave_lds_sync();
-        // offsets: every group before this one in token order (the halves' groups interleave)
-        float run = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const float other = sm.tot[w][hv ^ 1][lv32][ks];
-            const float g0 = hv == 0 ? gsum[ks] : other, g1 = hv == 0 ? other : gsum[ks];
-            const float off = run + (hv == 0 ? 0.f : g0);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[ks][e] += off;
-            run += g0 + g1;
-        }
-        const float G = run;
-        if (hv == 0) sm.gd[w][lv32] = G;
-        wave_lds_sync();
-        // ---- decay of the carried state: row (key channel) r of a tile by e^{G_r}
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            const float4 g4 = *reinterpret_cast<const float4 *>(&sm.gd[w][8 * qq + 4 * hv]);
-            const float f[4] = {__expf(g4.x), __expf(g4.y), __expf(g4.z), __expf(g4.w)};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int jb = 0; jb < NJB; ++jb) st[jb][4 * qq + e] *= f[e];
-        }
-        // ---- S += (W . K)^T V, W[t][i] = beta_t e^{G_i - L_{t,i}}: K^T and V^T fragments
-        //      with the transposing read, the weights on the K^T fragment
+        const int par = (int)(c & 1);
+        // ---- operand reads: K^T and V^T fragments (transposing read), the factors of
+        //      this lane's K^T fragment tokens 16 ks + 8 h + 0..7, the rows' chunk decay
         bf16x8 kr[4], vb[4][NJB];
+        float4 f0[4], f1[4], g4[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             kr[ks] = tr_pair(&B.Km[dkofs[0] + 16 * ks * DKC], &B.Km[dkofs[1] + 16 * ks * DKC]);
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb)
                 vb[ks][jb] = tr_pair(&B.Vm[dvofs[0][jb] + 16 * ks * D], &B.Vm[dvofs[1][jb] + 16 * ks * D]);
+            f0[ks] = *reinterpret_cast<const float4 *>(&sm.fac[par][fac_idx(i, 4 * ks + 2 * h)]);
+            f1[ks] = *reinterpret_cast<const float4 *>(&sm.fac[par][fac_idx(i, 4 * ks + 2 * h + 1)]);
         }
 #pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+            g4[qq] = *reinterpret_cast<const float4 *>(&sm.eg[par][32 * (w >> 1) + 8 * qq + 4 * h]);
+        // ---- decay of the carried state: row (key channel) r of a tile by e^{G_r}
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const float f[4] = {g4[qq].x, g4[qq].y, g4[qq].z, g4[qq].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) st[jb][4 * qq + e] *= f[e];
+        }
+        // ---- S += (W . K)^T V, W[t][i] = beta_t e^{G_i - L_{t,i}} on the K^T fragment
+#pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const float4 b0 = *reinterpret_cast<const float4 *>(&sm.wsc[w][16 * ks + 8 * hv]);
-            const float4 b1 = *reinterpret_cast<const float4 *>(&sm.wsc[w][16 * ks + 8 * hv + 4]);
-            const float4 f0 = make_float4(b0.x * __expf(G - x[ks][0]), b0.y * __expf(G - x[ks][1]),
-                                          b0.z * __expf(G - x[ks][2]), b0.w * __expf(G - x[ks][3]));
-            const float4 f1 = make_float4(b1.x * __expf(G - x[ks][4]), b1.y * __expf(G - x[ks][5]),
-                                          b1.z * __expf(G - x[ks][6]), b1.w * __expf(G - x[ks][7]));
-            const bf16x8 ka = scale8(kr[ks], f0, f1);
+            const bf16x8 ka = scale8(kr[ks], f0[ks], f1[ks]);
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb) st[jb] = mfma(ka, vb[ks][jb], st[jb]);
         }
@@ -605,9 +679,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         for (int r = 0; r < 16; ++r)
             dst[(int64_t)(row0 + acc_row(r, h)) * D + col0 + 32 * jb + l32] = bad ? nanv : st[jb][r];
     if (DIAG) {
-        // the two waves of a key block hold the same sums; the two lane halves the two token halves
-        ell += __shfl_xor(ell, 32);
-        if ((w & 1) == 0 && h == 0) a.pool_ell[rec * D + row0 + l32] = bad ? nanv : (float)ell;
+        // (the loading waves wrote the channels' ell)
     } else {
         if (q != 0) return;
         // every thread summed its table tokens
