@@ -343,6 +343,19 @@ def bench_rag(args, R=128, pool_slots=4096, H=32, d=128, C=4096, K=4, seed=501):
                             "roofline": roofline("hbm", cbytes / (c_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s")}}}
 
 
+def hbm_attainable(gib=4):
+    """Context for the HBM fractions: the rate PyTorch's own device copy (read + write)
+    reaches on this GPU over `gib` GiB."""
+    x = torch.empty((gib << 28,), dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    (ms,) = kernel_pass((("copy", lambda: y.copy_(x)),), 5)
+    out = {"copy_gbps": 2 * x.numel() * 4 / (ms * 1e-3) / 1e9}
+    del x, y
+    torch.cuda.empty_cache()
+    log(f"attainable: torch copy {out['copy_gbps']:.0f} GB/s (read + write)")
+    return out
+
+
 def cpu_baseline(seg_len=2048, H=32, d=128, nseg_sample=16, seed=301):
     """fp64 oracle on the host: build of nseg_sample of the main workload's 16
     segments, all heads (the first nseg_sample segments' tokens, same seed)."""
@@ -394,6 +407,7 @@ def main():
         secondary.extend(bench_sd(args))
     if args.only in ("all", "rag"):
         secondary.append(bench_rag(args))
+    attainable = hbm_attainable()
     cpu = None if args.no_cpu else cpu_baseline()
     line = {
         "metric": METRIC,
@@ -410,6 +424,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kern,
         "secondary": secondary,
+        "hbm_attainable": attainable,
     }
     print(json.dumps(line), flush=True)
 
