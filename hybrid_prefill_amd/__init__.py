@@ -54,7 +54,7 @@ class _Segments(ctypes.Structure):
                 ("log_alpha", ctypes.c_void_p), ("la_stride_t", ctypes.c_int64), ("la_stride_h", ctypes.c_int64)]
 
 
-EXPORTED = ("hypic_build_segment", "hypic_compose_chain", "hypic_conv_warmup",
+EXPORTED = ("hypic_build_segment", "hypic_compose_chain", "hypic_conv_warmup", "hypic_conv_kv",
             "hypic_status_string", "hypic_abi_version")
 
 
@@ -74,6 +74,9 @@ def lib():
     L.hypic_compose_chain.restype = i32
     L.hypic_conv_warmup.argtypes = [i32, i32, i32, i32, vp, i64, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp]
     L.hypic_conv_warmup.restype = i32
+    L.hypic_conv_kv.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, vp, i32, i32, i32, vp, vp,
+                                vp, i64, vp, vp, vp, vp, vp, vp]
+    L.hypic_conv_kv.restype = i32
     L.hypic_status_string.argtypes = [i32]
     L.hypic_status_string.restype = ctypes.c_char_p
     L.hypic_abi_version.restype = i32
@@ -247,3 +250,45 @@ def conv_warmup(tails: torch.Tensor, heads: torch.Tensor, weight: torch.Tensor,
                                  _stream(stream))
     _check(rc, "hypic_conv_warmup")
     return out
+
+
+def conv_kv(x: torch.Tensor, window: torch.Tensor, weight: torch.Tensor, num_heads: int, d_k: int, d_v: int,
+            bias: Optional[torch.Tensor] = None, activation: int = 1, normalize_k: bool = True,
+            out_dtype=torch.bfloat16, src_token: Optional[torch.Tensor] = None,
+            beta: Optional[torch.Tensor] = None, log_alpha: Optional[torch.Tensor] = None,
+            err_flag: Optional[torch.Tensor] = None, stream=None):
+    """hypic_conv_kv: x [rows, C] raw inputs, window [T, K] int32 rows (-1 = zero), weight [C, K].
+    Returns (k [T, H, d_k], v [T, H, d_v]) and, with src_token, (beta [T, H], log_alpha [T, H])."""
+    _device_check(x, window, weight, bias, src_token, beta, log_alpha, err_flag)
+    C, K = weight.shape
+    if C != num_heads * (d_k + d_v):
+        raise HypicError("weight must have H (d_k + d_v) channels")
+    if not x.is_contiguous() or x.dim() != 2 or x.shape[1] != C:
+        raise HypicError("x must be contiguous [rows, C]")
+    if weight.dtype != torch.float32 or not weight.is_contiguous():
+        raise HypicError("weight must be contiguous fp32 [C, K]")
+    if window.dtype != torch.int32 or not window.is_contiguous() or window.dim() != 2 or window.shape[1] != K:
+        raise HypicError("window must be contiguous int32 [T, K]")
+    T = window.shape[0]
+    for t_ in (beta, log_alpha):
+        if t_ is not None and (t_.dtype != torch.float32 or not t_.is_contiguous() or t_.shape[-1] != num_heads):
+            raise HypicError("beta / log_alpha must be contiguous fp32 [N, H]")
+    if src_token is not None and (src_token.dtype != torch.int32 or src_token.numel() != T):
+        raise HypicError("src_token must be int32 [T]")
+    dev = weight.device
+    k = torch.empty((T, num_heads, d_k), dtype=out_dtype, device=dev)
+    v = torch.empty((T, num_heads, d_v), dtype=out_dtype, device=dev)
+    b_out = la_out = None
+    n_src = 0
+    if src_token is not None:
+        b_out = torch.empty((T, num_heads), dtype=torch.float32, device=dev)
+        la_out = torch.empty((T, num_heads), dtype=torch.float32, device=dev)
+        n_src = (beta if beta is not None else log_alpha).shape[0] if (beta is not None or log_alpha is not None) \
+            else 2 ** 31 - 1
+    rc = lib().hypic_conv_kv(T, num_heads, d_k, d_v, K, _dtype_code(x), _ptr(x), x.shape[0], _ptr(window),
+                             _ptr(weight), _ptr(bias), int(activation), int(bool(normalize_k)),
+                             F32 if out_dtype == torch.float32 else BF16, _ptr(k), _ptr(v),
+                             _ptr(src_token), n_src, _ptr(beta), _ptr(log_alpha), _ptr(b_out), _ptr(la_out),
+                             _ptr(err_flag), _stream(stream))
+    _check(rc, "hypic_conv_kv")
+    return (k, v) if src_token is None else (k, v, b_out, la_out)

@@ -141,4 +141,33 @@ hypic_status hypic_conv_warmup(int32_t num_boundaries, int32_t channels, int32_t
     return e == hipSuccess ? HYPIC_OK : HYPIC_ERR_HIP;
 }
 
+hypic_status hypic_conv_kv(int32_t num_tokens, int32_t num_heads, int32_t d_k, int32_t d_v, int32_t kernel_size,
+                           int32_t x_dtype, const void *x, int64_t num_rows, const int32_t *window,
+                           const float *weight, const float *bias, int32_t activation, int32_t normalize_k,
+                           int32_t out_dtype, void *k_out, void *v_out,
+                           const int32_t *src_token, int64_t num_src_tokens, const float *beta,
+                           const float *log_alpha, float *beta_out, float *la_out,
+                           uint32_t *err_flag, void *stream) {
+    if (num_tokens < 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0 || num_rows < 0 || num_src_tokens < 0)
+        return HYPIC_ERR_INVALID_ARG;
+    if (kernel_size < 1 || kernel_size > 8 || !dtype_ok(x_dtype) || !dtype_ok(out_dtype))
+        return HYPIC_ERR_UNSUPPORTED;
+    if (activation != 0 && activation != 1) return HYPIC_ERR_UNSUPPORTED;
+    if ((int64_t)num_heads * (d_k + d_v) > 16384) return HYPIC_ERR_UNSUPPORTED;   // LDS row of the conv
+    if (num_tokens == 0) return HYPIC_OK;
+    if (!x || !window || !weight || !k_out || !v_out) return HYPIC_ERR_INVALID_ARG;
+    if (src_token && (!beta_out || !la_out)) return HYPIC_ERR_INVALID_ARG;
+
+    ConvKvArgs a;
+    memset(&a, 0, sizeof(a));
+    a.num_tokens = num_tokens; a.H = num_heads; a.dk = d_k; a.dv = d_v; a.ksize = kernel_size;
+    a.x_dtype = x_dtype; a.activation = activation; a.normalize_k = normalize_k != 0; a.out_dtype = out_dtype;
+    a.x = x; a.num_rows = num_rows; a.window = window; a.weight = weight; a.bias = bias;
+    a.k_out = k_out; a.v_out = v_out;
+    a.src_token = src_token; a.num_src_tokens = num_src_tokens; a.beta = beta; a.log_alpha = log_alpha;
+    a.beta_out = beta_out; a.la_out = la_out; a.err_flag = err_flag;
+    const hipError_t e = launch_conv_kv(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HYPIC_OK : HYPIC_ERR_HIP;
+}
+
 }  // extern "C"

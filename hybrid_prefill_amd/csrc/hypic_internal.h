@@ -44,9 +44,22 @@ struct ConvArgs {
     uint32_t *err_flag;
 };
 
+struct ConvKvArgs {
+    int32_t num_tokens, H, dk, dv, ksize, x_dtype, activation, normalize_k, out_dtype;
+    const void *x; int64_t num_rows;
+    const int32_t *window;
+    const float *weight, *bias;
+    void *k_out, *v_out;
+    const int32_t *src_token; int64_t num_src_tokens;
+    const float *beta, *log_alpha;
+    float *beta_out, *la_out;
+    uint32_t *err_flag;
+};
+
 hipError_t launch_build(const BuildArgs &a, hipStream_t stream);
 hipError_t launch_compose(const ComposeArgs &a, hipStream_t stream);
 hipError_t launch_conv_warmup(const ConvArgs &a, hipStream_t stream);
+hipError_t launch_conv_kv(const ConvKvArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers
 

@@ -191,6 +191,42 @@ hypic_status hypic_conv_warmup(int32_t num_boundaries, int32_t channels, int32_t
                                const float *weight, const float *bias, int32_t activation,
                                float *out, uint32_t *err_flag, void *stream);
 
+/*
+ * hypic_conv_kv -- keys and values of chosen tokens of a conv variant, from raw
+ * inputs (besthub article, paragraph 4: the convolution state warm-up that keeps
+ * reused segments aligned).  In a conv variant a causal depthwise conv of kernel
+ * size K and an activation run over time before the recurrence, and the keys are
+ * L2-normalised per head.  For output token t:
+ *       y[c]    = act( bias[c] + sum_{j<K} w[c][j] * x[window[t][j]][c] ),  C = H (d_k + d_v)
+ *       k[t][h] = y[h d_k .. h d_k + d_k) / sqrt(sum of squares + 1e-6)     (normalize_k != 0)
+ *       v[t][h] = y[H d_k + h d_v .. + d_v)
+ * (w[c][K-1] multiplies window[t][K-1], the token itself).  With the window rows
+ * of a segment's own earlier tokens this is its first prefill; with the previous
+ * segment's last raw inputs in the window it is the warm-up of a reused
+ * segment's first K-1 tokens, whose keys and values then feed a short record
+ * (hypic_build_segment) composed between the two segments' records.
+ *
+ *   x            [num_rows][C] raw inputs (x_dtype), row-major
+ *   window       device int32 [num_tokens][K]: rows of x, -1 = a zero row
+ *   weight       [C][K] fp32;  bias [C] fp32 or NULL;  act: 0 identity, 1 SiLU
+ *   k_out        [num_tokens][H][d_k] (out_dtype);  v_out [num_tokens][H][d_v]
+ *   src_token    device int32 [num_tokens] or NULL: when given, beta_out[t][h] =
+ *                beta[src_token[t]][h] (1 when beta is NULL) and la_out[t][h] =
+ *                log_alpha[src_token[t]][h] (0 when NULL); beta, log_alpha
+ *                [num_src_tokens][H] fp32; beta_out, la_out [num_tokens][H] fp32
+ *   1 <= K <= 8, H (d_k + d_v) <= 16384.
+ * Error behaviour: a window row outside [-1, num_rows) or a src_token outside
+ * [0, num_src_tokens) sets HYPIC_EFLAG_SLOT_OUT_OF_RANGE and fills that token's
+ * outputs with NaN.
+ */
+hypic_status hypic_conv_kv(int32_t num_tokens, int32_t num_heads, int32_t d_k, int32_t d_v, int32_t kernel_size,
+                           int32_t x_dtype, const void *x, int64_t num_rows, const int32_t *window,
+                           const float *weight, const float *bias, int32_t activation, int32_t normalize_k,
+                           int32_t out_dtype, void *k_out, void *v_out,
+                           const int32_t *src_token, int64_t num_src_tokens, const float *beta,
+                           const float *log_alpha, float *beta_out, float *la_out,
+                           uint32_t *err_flag, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *hypic_status_string(int32_t status);
 

@@ -14,6 +14,8 @@ compose, don't add" and "Family comparison"):
   ``T_C = e^ell P``, token by token in fp64.
 * ``compose`` -- ``S <- T_i S + S_i`` over a chain of pool records in prompt order.
 * ``causal_conv`` -- the full causal depthwise short convolution over a raw stream.
+* ``conv_kv`` -- a conv variant's keys and values over a raw stream: the causal
+  conv and activation, the channels split per head, each key L2-normalised.
 
 Every function takes numpy arrays; inputs are upcast to fp64 exactly (bf16 and
 fp32 values are representable in fp64), so the oracle sees the exact bytes the
@@ -170,3 +172,18 @@ def rel_fro(x, ref) -> float:
     num = float(np.linalg.norm((x - ref).ravel()))
     den = float(np.linalg.norm(ref.ravel()))
     return num / den if den > 0 else num
+
+
+def conv_kv(x, w, bias, act: int, H: int, dk: int, dv: int, normalize: bool = True, eps: float = 1e-6):
+    """Keys and values of a conv variant over a raw stream x [n, C] (C = H (dk + dv),
+    zero history at its start): the causal conv and activation of causal_conv, the
+    channels split into keys [n, H, dk] and values [n, H, dv], each head's key
+    divided by sqrt(|k|^2 + eps) (besthub article, paragraph 4: the convolution
+    state the warm-up keeps aligned is this conv's)."""
+    y = causal_conv(x, w, bias, act)
+    n = y.shape[0]
+    k = y[:, :H * dk].reshape(n, H, dk)
+    v = y[:, H * dk:].reshape(n, H, dv).copy()
+    if normalize:
+        k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + eps)
+    return k, v

@@ -150,3 +150,29 @@ def test_ctypes_layout_matches_header(tmp_path):
         assert want == int(off), (T, f, want, off)
         n += 1
     assert n == sum(len(v) + 1 for v in fields.values())
+
+
+def test_conv_kv_validation(L):
+    c = L.hypic_conv_kv
+    ok = dict(T=3, H=2, dk=4, dv=4, K=4, dt=hp.BF16, x=FAKE, rows=10, win=FAKE, w=FAKE, b=None, act=1,
+              norm=1, odt=hp.BF16, k=FAKE, v=FAKE, src=None, nsrc=0, beta=None, la=None, bo=None, lo=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return c(a["T"], a["H"], a["dk"], a["dv"], a["K"], a["dt"], a["x"], a["rows"], a["win"], a["w"], a["b"],
+                 a["act"], a["norm"], a["odt"], a["k"], a["v"], a["src"], a["nsrc"], a["beta"], a["la"],
+                 a["bo"], a["lo"], None, None)
+
+    assert call(K=0) == UNSUPPORTED
+    assert call(K=9) == UNSUPPORTED
+    assert call(dt=5) == UNSUPPORTED
+    assert call(odt=5) == UNSUPPORTED
+    assert call(act=3) == UNSUPPORTED
+    assert call(H=65, dk=128, dv=128) == UNSUPPORTED     # conv row larger than the LDS row (16384)
+    assert call(T=-1) == INVALID
+    assert call(H=0) == INVALID
+    assert call(x=None) == INVALID
+    assert call(win=None) == INVALID
+    assert call(k=None) == INVALID
+    assert call(src=FAKE) == INVALID                     # src_token without beta_out / la_out
+    assert call(T=0) == 0

@@ -1,0 +1,117 @@
+"""GPU parity of conv-coupled exact records (hybrid_prefill_amd.conv_exact):
+suffix records built at first prefill, warmed head records built on reuse, the
+chain head_1, suffix_1, head_2, ... composed -- against the fp64 recurrence over
+each request's concatenated tokens, whose keys and values come from the causal
+conv over the request's whole raw stream (oracle.conv_kv).
+
+Negative control: composing the segments' standalone records (every token's conv
+with the segment's own zero history) misses the warm-up and must exceed the
+tolerance (weak decay, so that earlier tokens still matter).
+"""
+import numpy as np
+import pytest
+import torch
+
+import hybrid_prefill_amd as hp
+from hybrid_prefill_amd import conv_exact as ce
+import oracle
+import synth
+from oracle import rel_fro
+from parity_util import np64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hp.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+LENS = [1, 2, 3, 5, 64, 130, 7, 40, 0, 3]
+CHAINS = [[0, 1, 2, 3], [4, 5, 6, 7], [5, 0, 5], [2], [7, 6, 5, 4, 3, 2, 1, 0], [8, 9, 8, 4], []]
+
+
+def _setup(H, dk, dv, x_dtype, kv_dtype, act, bias, seed, decay):
+    K = 4
+    C = H * (dk + dv)
+    offs = synth.offsets_from_lengths(LENS)
+    N = int(offs[-1])
+    x = synth.conv_stream(N, C, x_dtype, seed, "cuda")
+    w = synth.conv_weights(C, K, seed + 1, "cuda")
+    b = torch.randn(C, device="cuda") * 0.1 if bias else None
+    beta = synth.write_gate(N, H, seed + 2, "cuda")
+    la = synth.gdn_log_decay(N, H, seed + 3, decay, "cuda")
+    return ce.ConvCache(x, offs, beta, la, w, b, act, H, dk, dv, kv_dtype)
+
+
+def _sequential(c, chain, H, dk, dv):
+    """Oracle: the recurrence over the request's concatenated tokens, keys and values
+    from the conv over its whole raw stream."""
+    if not chain:
+        return np.zeros((H, dk, dv))
+    rows = np.concatenate([np.arange(c.offsets[s], c.offsets[s + 1]) for s in chain]).astype(np.int64)
+    x = np64(c.x)[rows]
+    k, v = oracle.conv_kv(x, np64(c.weight), None if c.bias is None else np64(c.bias), c.activation, H, dk, dv)
+    b, la = np64(c.beta)[rows], np64(c.log_alpha)[rows]
+    _, _, S = oracle.build_segments(oracle.GDN, k, v, la, [0, len(rows)], beta=b, want_P=False)
+    return S[0]
+
+
+@pytest.mark.parametrize("cfg", [(2, 64, 64, torch.float32, torch.float32, 1, True, 1e-4),
+                                 (4, 128, 128, torch.bfloat16, torch.bfloat16, 0, False, 2e-2)])
+def test_conv_exact_reuse_equals_sequential(cfg):
+    H, dk, dv, x_dtype, kv_dtype, act, bias, tol = cfg
+    c = _setup(H, dk, dv, x_dtype, kv_dtype, act, bias, 1300 + dk, 0.001)
+    S_seg = len(LENS)
+    n_heads = sum(len(ch) for ch in CHAINS)
+    pool = hp.Pool.allocate(hp.GDN, S_seg + n_heads, H, dk, dv, device="cuda", fill=0.0)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ce.cache_segments(c, pool, np.arange(S_seg), err_flag=err)
+    plan = ce.plan_reuse(c, [np.asarray(ch) for ch in CHAINS], np.arange(S_seg), S_seg)
+    out = ce.reuse(c, plan, pool, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    say(f"[conv exact] H={H} d={dk} {x_dtype} act={act}: chains {CHAINS}")
+    worst = 0.0
+    refs = []
+    for r, ch in enumerate(CHAINS):
+        ref = _sequential(c, ch, H, dk, dv)
+        refs.append(ref)
+        for h in range(H):
+            worst = max(worst, rel_fro(np64(out[r, h]), ref[h]))
+    say(f"   composed (warmed heads + suffixes) vs sequential: max err {worst:.2e}")
+    assert worst <= tol
+
+    # negative control: standalone records (zero conv history at every segment start)
+    pool2 = hp.Pool.allocate(hp.GDN, S_seg, H, dk, dv, device="cuda", fill=0.0)
+    ce.cache_segments(c, pool2, np.arange(S_seg), from_token=0)
+    offs = np.concatenate([[0], np.cumsum([len(ch) for ch in CHAINS])]).astype(np.int64)
+    flat = np.asarray(sum(CHAINS, []), dtype=np.int32)
+    naive = hp.compose_chain(pool2, torch.as_tensor(offs).cuda(), torch.as_tensor(flat).cuda())
+    torch.cuda.synchronize()
+    worst_n = max(rel_fro(np64(naive[r, h]), refs[r][h]) for r in (0, 1, 2, 4, 5) for h in range(H))
+    say(f"   negative control, standalone segment records: max err {worst_n:.2e}")
+    assert worst_n > 10 * tol
+
+
+def test_conv_kv_bad_window_flags_and_nans():
+    H, dk, dv, K = 2, 8, 8, 4
+    C = H * (dk + dv)
+    x = synth.conv_stream(6, C, torch.float32, 1400, "cuda")
+    w = synth.conv_weights(C, K, 1401, "cuda")
+    win = torch.tensor([[-1, -1, 0, 1], [0, 1, 2, 9], [2, 3, 4, 5]], dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    k, v = hp.conv_kv(x, win, w, H, dk, dv, out_dtype=torch.float32, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == hp.EFLAG_SLOT_OUT_OF_RANGE
+    assert torch.all(torch.isnan(k[1])) and torch.all(torch.isnan(v[1]))
+    assert not torch.any(torch.isnan(k[[0, 2]])) and not torch.any(torch.isnan(v[[0, 2]]))
+    # rows 0 and 2 against the oracle's conv of their windows
+    xs = np64(x)
+    for t, rows in ((0, [0, 1]), (2, [2, 3, 4, 5])):
+        kr, vr = oracle.conv_kv(xs[rows], np64(w), None, 1, H, dk, dv)
+        assert rel_fro(np64(k[t]), kr[-1]) < 1e-5 and rel_fro(np64(v[t]), vr[-1]) < 1e-5

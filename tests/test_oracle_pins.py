@@ -420,3 +420,55 @@ def test_conv_warmup_window_identity():
         # a zero tail reproduces the cold conv of the segment
         zero_win = np.concatenate([np.zeros((K - 1, C)), x[a:a + K - 1]])
         np.testing.assert_allclose(oracle.causal_conv(zero_win, w, None, 1)[K - 1:], y_cold[:K - 1], atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- conv variant keys / values
+
+@pytest.mark.parametrize("act", [0, 1])
+def test_conv_kv_brute_force(act):
+    """conv_kv against the definition written out element by element: the causal conv
+    with zero history, the activation, the split into heads, the key L2 norm."""
+    rng = np.random.default_rng(70 + act)
+    n, H, dk, dv, K = 7, 2, 3, 2, 3
+    C = H * (dk + dv)
+    x = rng.standard_normal((n, C))
+    w = rng.uniform(-0.5, 0.5, (C, K))
+    bias = rng.standard_normal(C)
+    k, v = oracle.conv_kv(x, w, bias, act, H, dk, dv)
+    for t in range(n):
+        y = np.zeros(C)
+        for c in range(C):
+            acc = bias[c]
+            for j in range(K):
+                s = t - (K - 1) + j
+                if s >= 0:
+                    acc += w[c, j] * x[s, c]
+            y[c] = acc / (1.0 + math.exp(-acc)) if act == 1 else acc
+        for h in range(H):
+            kk = y[h * dk:(h + 1) * dk]
+            np.testing.assert_allclose(k[t, h], kk / math.sqrt(float(kk @ kk) + 1e-6), atol=1e-13)
+            np.testing.assert_allclose(v[t, h], y[H * dk + h * dv:H * dk + (h + 1) * dv], atol=1e-13)
+    ku, _ = oracle.conv_kv(x, w, bias, act, H, dk, dv, normalize=False)
+    np.testing.assert_allclose(ku, oracle.causal_conv(x, w, bias, act)[:, :H * dk].reshape(n, H, dk), atol=1e-13)
+
+
+def test_conv_kv_suffix_context_free_head_warmed():
+    """The reading the conv-coupled records rest on: in a stream cut into two segments,
+    the second segment's keys and values from its token K-1 on equal those of the
+    segment alone (zero history), and its first K-1 equal the conv over the first
+    segment's last K-1 raw inputs followed by its own; with zero history instead the
+    first K-1 differ."""
+    rng = np.random.default_rng(77)
+    H, dk, dv, K = 2, 4, 3, 4
+    C = H * (dk + dv)
+    n1, n2 = 9, 8
+    x = rng.standard_normal((n1 + n2, C))
+    w = rng.uniform(-0.5, 0.5, (C, K))
+    k, v = oracle.conv_kv(x, w, None, 1, H, dk, dv)
+    k2, v2 = oracle.conv_kv(x[n1:], w, None, 1, H, dk, dv)
+    np.testing.assert_allclose(k[n1 + K - 1:], k2[K - 1:], atol=1e-13)
+    np.testing.assert_allclose(v[n1 + K - 1:], v2[K - 1:], atol=1e-13)
+    kw, vw = oracle.conv_kv(x[n1 - (K - 1):], w, None, 1, H, dk, dv)
+    np.testing.assert_allclose(k[n1:n1 + K - 1], kw[K - 1:2 * (K - 1)], atol=1e-13)
+    np.testing.assert_allclose(v[n1:n1 + K - 1], vw[K - 1:2 * (K - 1)], atol=1e-13)
+    assert np.max(np.abs(k[n1:n1 + K - 1] - k2[:K - 1])) > 1e-2
