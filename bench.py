@@ -12,12 +12,14 @@ Secondary lines (same JSON object, key "secondary"):
                  bf16, 8 x 2048 tokens, plus their 8-segment chains
   rag mix        128 requests of 24-96 cached/cold GDN segments (128-1024 tokens),
                  cold builds + conv warm-up (4096 channels, kernel 4) + all chains
+  conv exact     conv-coupled exact reuse: 32 requests of 24-96 cached segments,
+                 warmed head keys/values, head records, chains of 2m records
 
 Inputs are resident in HBM before the timed region starts.  Kernel durations
 come from HIP events recorded on the stream the kernels are launched on.
 The cpu_baseline leg times the fp64 oracle on a bounded sample on the host.
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|sd|compose|rag] [--no-cpu]
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|sd|compose|rag|convexact] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -343,6 +345,54 @@ def bench_rag(args, R=128, pool_slots=4096, H=32, d=128, C=4096, K=4, seed=501):
                             "roofline": roofline("hbm", cbytes / (c_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s")}}}
 
 
+def bench_conv_exact(args, R=32, pool_segs=512, H=32, d=128, K=4, seed=601):
+    """Conv-coupled exact reuse (conv variant, keys and values from a causal conv over
+    C = H (d_k + d_v) raw channels): R requests of 24-96 cached segments (128-1024
+    tokens) drawn from a pool whose suffix records were built untimed.  Timed: the
+    warmed head keys and values (hypic_conv_kv), the head records (hypic_build_segment)
+    and the chains head_1, suffix_1, ... (hypic_compose_chain); beside it the plain
+    chain of the segments' records for the same requests."""
+    from hybrid_prefill_amd import conv_exact as ce
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = rng.integers(128, 1025, size=pool_segs)
+    offs = synth.offsets_from_lengths(lens)
+    N, C = int(offs[-1]), H * 2 * d
+    c = ce.ConvCache(synth.conv_stream(N, C, torch.bfloat16, seed + 1, "cuda"), offs,
+                     synth.write_gate(N, H, seed + 2, "cuda"), synth.gdn_log_decay(N, H, seed + 3, 0.1, "cuda"),
+                     synth.conv_weights(C, K, seed + 4, "cuda"), None, 1, H, d, d, torch.bfloat16)
+    chains = [rng.integers(0, pool_segs, size=int(m)).astype(np.int32) for m in rng.integers(24, 97, size=R)]
+    npos = sum(len(ch) for ch in chains)
+    pool = hp.Pool.allocate(hp.GDN, pool_segs + npos, H, d, d, device="cuda")
+    ce.cache_segments(c, pool, np.arange(pool_segs))                 # first prefill, untimed
+    plan = ce.plan_reuse(c, chains, np.arange(pool_segs), pool_segs)
+    out = torch.empty((R, H, d, d), device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plain_offs = torch.as_tensor(np.concatenate([[0], np.cumsum([len(ch) for ch in chains])]).astype(np.int64)).cuda()
+    plain_ids = torch.as_tensor(np.concatenate(chains)).cuda()
+    for _ in range(max(1, args.warmup)):
+        ce.reuse(c, plan, pool, out_S=out, err_flag=err)
+    torch.cuda.synchronize()
+    timer = KernelTimer()
+    n = max(3, args.steps // 4)
+    t0 = time.perf_counter()
+    for _ in range(n):
+        ce.reuse(c, plan, pool, out_S=out, err_flag=err, timer=timer)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    assert int(err.item()) == 0 and bool(torch.isfinite(out).all())
+    (plain_ms,) = kernel_pass((("plain", lambda: hp.compose_chain(pool, plain_offs, plain_ids, out_S=out)),), n)
+    prompt_tokens = int(sum(int(lens[s]) for ch in chains for s in ch))
+    parts = {k_: timer.mean_ms(k_) for k_ in ("conv_kv", "head_build", "compose")}
+    log(f"conv exact: {ms:.3f} ms/step (conv_kv {parts['conv_kv']:.3f}, head records {parts['head_build']:.3f}, "
+        f"compose of {2 * npos} records {parts['compose']:.3f} ms); plain chain of {npos} records {plain_ms:.3f} ms")
+    del pool, c
+    torch.cuda.empty_cache()
+    return {"workload": f"conv_exact_reuse_{R}req_pool{pool_segs}_h{H}_d{d}_conv{C}x{K}",
+            "metric": "prompt tokens/s", "value": prompt_tokens / (ms * 1e-3), "unit": "tokens/s", "ms": ms,
+            "head_tokens": int(plan.head_src.numel()), "records_composed": 2 * npos,
+            "kernels_ms": parts, "plain_chain_ms": plain_ms}
+
+
 def hbm_attainable(gib=4):
     """Context for the HBM fractions: the rate PyTorch's own device copy (read + write)
     reaches on this GPU over `gib` GiB."""
@@ -377,8 +427,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["all", "main", "sd", "compose", "rag"], default="all",
-                    help="main: only the headline GDN step; sd / compose / rag: it plus that secondary leg")
+    ap.add_argument("--only", choices=["all", "main", "sd", "compose", "rag", "convexact"], default="all",
+                    help="main: only the headline GDN step; sd / compose / rag / convexact: it plus that secondary leg")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one untimed 1 GiB device copy (reference kernel for HBM byte counters)")
@@ -407,6 +457,8 @@ def main():
         secondary.extend(bench_sd(args))
     if args.only in ("all", "rag"):
         secondary.append(bench_rag(args))
+    if args.only in ("all", "convexact"):
+        secondary.append(bench_conv_exact(args))
     attainable = hbm_attainable()
     cpu = None if args.no_cpu else cpu_baseline()
     line = {
