@@ -349,9 +349,10 @@ def bench_conv_exact(args, R=32, pool_segs=512, H=32, d=128, K=4, seed=601):
     """Conv-coupled exact reuse (conv variant, keys and values from a causal conv over
     C = H (d_k + d_v) raw channels): R requests of 24-96 cached segments (128-1024
     tokens) drawn from a pool whose suffix records were built untimed.  Timed: the
-    warmed head keys and values (hypic_conv_kv), the head records (hypic_build_segment)
-    and the chains head_1, suffix_1, ... (hypic_compose_chain); beside it the plain
-    chain of the segments' records for the same requests."""
+    warmed head keys and values (hypic_conv_kv) and the chains of suffix records with
+    the head tokens applied inside the compose (hypic_compose_chain_heads); beside it
+    the plain chain of the same records, and the unfused form (a record per head,
+    chains of 2m records)."""
     from hybrid_prefill_amd import conv_exact as ce
     rng = np.random.Generator(np.random.PCG64(seed))
     lens = rng.integers(128, 1025, size=pool_segs)
@@ -382,15 +383,23 @@ def bench_conv_exact(args, R=32, pool_segs=512, H=32, d=128, K=4, seed=601):
     assert int(err.item()) == 0 and bool(torch.isfinite(out).all())
     (plain_ms,) = kernel_pass((("plain", lambda: hp.compose_chain(pool, plain_offs, plain_ids, out_S=out)),), n)
     prompt_tokens = int(sum(int(lens[s]) for ch in chains for s in ch))
-    parts = {k_: timer.mean_ms(k_) for k_ in ("conv_kv", "head_build", "compose")}
-    log(f"conv exact: {ms:.3f} ms/step (conv_kv {parts['conv_kv']:.3f}, head records {parts['head_build']:.3f}, "
-        f"compose of {2 * npos} records {parts['compose']:.3f} ms); plain chain of {npos} records {plain_ms:.3f} ms")
+    parts = {k_: timer.mean_ms(k_) for k_ in ("conv_kv", "compose")}
+    # the unfused form for comparison: a record per head, chains of 2m records
+    timer2 = KernelTimer()
+    for _ in range(n):
+        ce.reuse(c, plan, pool, out_S=out, err_flag=err, timer=timer2, fused=False)
+    torch.cuda.synchronize()
+    unfused = {k_: timer2.mean_ms(k_) for k_ in ("conv_kv", "head_build", "compose")}
+    log(f"conv exact: {ms:.3f} ms/step (conv_kv {parts['conv_kv']:.3f}, compose with head tokens "
+        f"{parts['compose']:.3f} ms); plain chain {plain_ms:.3f} ms; with head records instead: conv_kv "
+        f"{unfused['conv_kv']:.3f}, head records {unfused['head_build']:.3f}, compose of {2 * npos} records "
+        f"{unfused['compose']:.3f} ms")
     del pool, c
     torch.cuda.empty_cache()
     return {"workload": f"conv_exact_reuse_{R}req_pool{pool_segs}_h{H}_d{d}_conv{C}x{K}",
             "metric": "prompt tokens/s", "value": prompt_tokens / (ms * 1e-3), "unit": "tokens/s", "ms": ms,
-            "head_tokens": int(plan.head_src.numel()), "records_composed": 2 * npos,
-            "kernels_ms": parts, "plain_chain_ms": plain_ms}
+            "head_tokens": int(plan.head_src.numel()), "records_composed": npos,
+            "kernels_ms": parts, "plain_chain_ms": plain_ms, "head_records_path_ms": unfused}
 
 
 def hbm_attainable(gib=4):

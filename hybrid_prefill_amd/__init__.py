@@ -7,8 +7,12 @@ the C ABI in ``include/hypic.h``:
 
 * :func:`build_segment`  -- records ``(ell, P, S)`` of segments into pool slots
 * :func:`compose_chain`  -- fold pool records along request chains
+* :func:`compose_chain_heads` -- the same with a few tokens applied to the state
+  before each record (the warmed first tokens of reused conv-variant segments)
 * :func:`conv_warmup`    -- short-conv outputs at segment starts with the
   previous segment's tail as conv state
+* :func:`conv_kv`        -- keys and values of chosen tokens of a conv variant
+  (causal conv over given window rows, activation, per-head key L2 norm)
 
 There is no fallback: if the library is missing, every call raises.
 """
@@ -54,8 +58,8 @@ class _Segments(ctypes.Structure):
                 ("log_alpha", ctypes.c_void_p), ("la_stride_t", ctypes.c_int64), ("la_stride_h", ctypes.c_int64)]
 
 
-EXPORTED = ("hypic_build_segment", "hypic_compose_chain", "hypic_conv_warmup", "hypic_conv_kv",
-            "hypic_status_string", "hypic_abi_version")
+EXPORTED = ("hypic_build_segment", "hypic_compose_chain", "hypic_compose_chain_heads", "hypic_conv_warmup",
+            "hypic_conv_kv", "hypic_status_string", "hypic_abi_version")
 
 
 def lib():
@@ -77,6 +81,9 @@ def lib():
     L.hypic_conv_kv.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, vp, i32, i32, i32, vp, vp,
                                 vp, i64, vp, vp, vp, vp, vp, vp]
     L.hypic_conv_kv.restype = i32
+    L.hypic_compose_chain_heads.argtypes = [ctypes.POINTER(_Pool), i32, vp, vp, i64, vp, i64, vp, vp, vp, vp,
+                                            vp, vp, vp, vp, vp]
+    L.hypic_compose_chain_heads.restype = i32
     L.hypic_status_string.argtypes = [i32]
     L.hypic_status_string.restype = ctypes.c_char_p
     L.hypic_abi_version.restype = i32
@@ -218,6 +225,42 @@ def compose_chain(pool: Pool, chain_offsets: torch.Tensor, chain_slots: torch.Te
                                    chain_slots.numel(), _ptr(init_S), _ptr(out_S), _ptr(out_log_scale),
                                    _ptr(out_P), _ptr(err_flag), _stream(stream))
     _check(rc, "hypic_compose_chain")
+    return out_S
+
+
+def compose_chain_heads(pool: Pool, chain_offsets: torch.Tensor, chain_slots: torch.Tensor,
+                        head_offsets: torch.Tensor, head_k: torch.Tensor, head_v: torch.Tensor,
+                        head_beta: torch.Tensor, head_log_alpha: torch.Tensor,
+                        init_S: Optional[torch.Tensor] = None, out_S: Optional[torch.Tensor] = None,
+                        out_log_scale: Optional[torch.Tensor] = None, err_flag: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """hypic_compose_chain_heads: each chain entry applies its head tokens, then folds its
+    record; head_k [T,H,d_k], head_v [T,H,d_v], head_beta / head_log_alpha [T,H] fp32."""
+    _device_check(chain_offsets, chain_slots, head_offsets, head_k, head_v, head_beta, head_log_alpha,
+                  init_S, out_S, out_log_scale, err_flag)
+    if chain_offsets.dtype != torch.int64 or chain_slots.dtype != torch.int32 or head_offsets.dtype != torch.int64:
+        raise HypicError("chain_offsets / head_offsets must be int64 and chain_slots int32")
+    if head_offsets.numel() != chain_slots.numel() + 1:
+        raise HypicError("head_offsets needs one entry per chain slot plus one")
+    T = head_k.shape[0]
+    for t_ in (head_k, head_v, head_beta, head_log_alpha):
+        if t_.dtype != torch.float32 or not t_.is_contiguous() or t_.shape[0] != T:
+            raise HypicError("head tensors must be contiguous fp32 with one row per head token")
+    R = chain_offsets.numel() - 1
+    if out_S is None:
+        out_S = torch.empty((R, pool.num_heads, pool.d_k, pool.d_v), dtype=torch.float32, device=pool.S.device)
+    for t_ in (init_S, out_S, out_log_scale):
+        if t_ is not None and (t_.dtype != torch.float32 or not t_.is_contiguous()):
+            raise HypicError("state tensors must be contiguous fp32")
+    cpool = pool._c()
+    none = T == 0
+    rc = lib().hypic_compose_chain_heads(ctypes.byref(cpool), R, _ptr(chain_offsets), _ptr(chain_slots),
+                                         chain_slots.numel(), _ptr(head_offsets), T,
+                                         None if none else _ptr(head_k), None if none else _ptr(head_v),
+                                         None if none else _ptr(head_beta), None if none else _ptr(head_log_alpha),
+                                         _ptr(init_S), _ptr(out_S), _ptr(out_log_scale), _ptr(err_flag),
+                                         _stream(stream))
+    _check(rc, "hypic_compose_chain_heads")
     return out_S
 
 

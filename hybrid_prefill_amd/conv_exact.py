@@ -12,12 +12,15 @@ across the boundary); from token K-1 on they depend on the segment alone.  So:
   exact in any context -- into pool slot s;
 * reuse (``reuse``): for every chain position, the segment's first min(n, K-1)
   tokens are recomputed with the conv warmed by the raw inputs that precede them
-  in this request, built into a short head record, and the request's state is
-  the composition  head_1, suffix_1, head_2, suffix_2, ...,  which equals the
-  recurrence over the concatenated request.
+  in this request; the request's state is the chain  head_1, suffix_1, head_2,
+  suffix_2, ...,  which equals the recurrence over the concatenated request.
+  Where the fused compose takes the pool (GDN, d_k = d_v = 128), the head tokens
+  are applied to the running state inside the compose (hypic_compose_chain_heads:
+  a few hundred bytes per entry); elsewhere each head becomes a short record
+  (hypic_build_segment) composed before its suffix.
 
 Every step runs in libhypic's kernels (hypic_conv_kv, hypic_build_segment,
-hypic_compose_chain); this module only lays out index tables (which raw rows a
+hypic_compose_chain, hypic_compose_chain_heads); this module only lays out index tables (which raw rows a
 token's conv window reads, which tokens form which record) and launches.  The raw
 inputs stay in one stream [rows, C] with per-segment row ranges; a cache that keeps
 only each segment's first and last K-1 raw rows would index those instead.
@@ -30,7 +33,7 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-from . import GDN, Pool, build_segment, compose_chain, conv_kv
+from . import GDN, Pool, build_segment, compose_chain, compose_chain_heads, conv_kv
 
 
 @dataclass
@@ -96,6 +99,8 @@ class ReusePlan:
     head_slots: torch.Tensor      # int32 [B]
     chain_offsets: torch.Tensor   # int64 [R+1]
     chain_slots: torch.Tensor     # int32: head_1, suffix_1, head_2, suffix_2, ...
+    suffix_offsets: torch.Tensor  # int64 [R+1]: the chains of suffix slots alone (fused compose)
+    suffix_slots: torch.Tensor    # int32: suffix_1, suffix_2, ... (entry j's head tokens: head_offsets[j..j+1])
 
 
 def plan_reuse(c: ConvCache, chains: List[np.ndarray], suffix_slot: np.ndarray, head_slot_base: int,
@@ -104,7 +109,7 @@ def plan_reuse(c: ConvCache, chains: List[np.ndarray], suffix_slot: np.ndarray, 
     segment s's suffix record sits in pool slot suffix_slot[s]; head records go to
     consecutive slots from head_slot_base (one per chain position)."""
     K = c.K
-    wins, srcs, hl, cs, co = [], [], [], [], [0]
+    wins, srcs, hl, cs, co, ss, so = [], [], [], [], [0], [], [0]
     j = 0
     for ch in chains:
         ch = [int(s) for s in ch]
@@ -119,9 +124,11 @@ def plan_reuse(c: ConvCache, chains: List[np.ndarray], suffix_slot: np.ndarray, 
             srcs.append(rows_of_pos[pos].astype(np.int32))
             hl.append(h)
             cs += [head_slot_base + j, int(suffix_slot[s])]
+            ss.append(int(suffix_slot[s]))
             j += 1
             p0 += n
         co.append(len(cs))
+        so.append(len(ss))
     T = int(sum(hl))
     win = np.concatenate(wins) if wins else np.zeros((0, K), np.int32)
     src = np.concatenate(srcs) if srcs else np.zeros(0, np.int32)
@@ -131,16 +138,31 @@ def plan_reuse(c: ConvCache, chains: List[np.ndarray], suffix_slot: np.ndarray, 
     t = lambda a, dt: torch.as_tensor(np.asarray(a, dtype=dt), device=device)
     return ReusePlan(t(win, np.int32), t(src, np.int32), t(hoffs, np.int64),
                      t(np.arange(head_slot_base, head_slot_base + len(hl)), np.int32),
-                     t(co, np.int64), t(cs, np.int32))
+                     t(co, np.int64), t(cs, np.int32), t(so, np.int64), t(ss, np.int32))
+
+
+def fused_supported(pool: Pool) -> bool:
+    return pool.family == GDN and pool.d_k == 128 and pool.d_v == 128
 
 
 def reuse(c: ConvCache, plan: ReusePlan, pool: Pool, out_S: Optional[torch.Tensor] = None,
-          err_flag: Optional[torch.Tensor] = None, timer=None) -> torch.Tensor:
-    """One reuse step on the current stream: warmed head keys and values, head records,
-    then every request's chain composed.  Returns out_S [R, H, d_k, d_v]."""
+          err_flag: Optional[torch.Tensor] = None, timer=None, fused: Optional[bool] = None) -> torch.Tensor:
+    """One reuse step on the current stream: warmed head keys and values, then every
+    request's chain composed (fused: head tokens applied inside the compose; else head
+    records first).  Returns out_S [R, H, d_k, d_v]."""
     def run(name, fn):
         return timer.time(name, fn) if timer is not None else fn()
 
+    if fused is None:
+        fused = fused_supported(pool)
+    if fused:
+        k, v, b, la = run("conv_kv", lambda: conv_kv(
+            c.x, plan.head_window, c.weight, c.num_heads, c.d_k, c.d_v, bias=c.bias, activation=c.activation,
+            out_dtype=torch.float32, src_token=plan.head_src, beta=c.beta, log_alpha=c.log_alpha,
+            err_flag=err_flag))
+        return run("compose", lambda: compose_chain_heads(pool, plan.suffix_offsets, plan.suffix_slots,
+                                                          plan.head_offsets, k, v, b, la, out_S=out_S,
+                                                          err_flag=err_flag))
     k, v, b, la = run("conv_kv", lambda: conv_kv(
         c.x, plan.head_window, c.weight, c.num_heads, c.d_k, c.d_v, bias=c.bias, activation=c.activation,
         out_dtype=c.kv_dtype, src_token=plan.head_src, beta=c.beta, log_alpha=c.log_alpha, err_flag=err_flag))

@@ -22,6 +22,8 @@
 // next record is prefetched while the current product runs: P into registers
 // (coalesced 16-byte loads), S straight from HBM into LDS (global_load_lds),
 // read back from LDS in accumulator order.
+#include <type_traits>
+
 #include "hypic_internal.h"
 
 namespace hypic {
@@ -79,6 +81,24 @@ struct ChainStage {
     int32_t slot[CHAIN_LDS];
     float ell[CHAIN_LDS];
 };
+// with head tokens: per chain entry, (first head token << 4) | count (count <= MAXH)
+constexpr int MAXH = 8;
+struct HeadStage {
+    int32_t info[CHAIN_LDS];
+    float k[MAXH][D], v[MAXH][D];     // the current entry's head tokens (this head's channels)
+    float beta[MAXH], la[MAXH];
+};
+struct NoHeadStage { int32_t info[1]; };     // (chains without head tokens)
+__device__ __forceinline__ int32_t head_info(const HeadStage &hs, int64_t c_lo, int64_t c) {
+    return ((const __attribute__((address_space(3))) int32_t *)hs.info)[(c - c_lo) & (CHAIN_LDS - 1)];
+}
+// 0 when the entry's head tokens are well formed, else 2 (bad offsets)
+__device__ __forceinline__ int head_entry(const ComposeArgs &a, int64_t c, int32_t &info) {
+    const int64_t h0 = a.head_offsets[c], h1 = a.head_offsets[c + 1];
+    if (h0 < 0 || h1 < h0 || h1 > a.num_head_tokens || h1 - h0 > MAXH) { info = 0; return 2; }
+    info = (int32_t)((h0 << 4) | (h1 - h0));
+    return 0;
+}
 typedef const __attribute__((address_space(3))) int32_t lds_i32;
 typedef const __attribute__((address_space(3))) float lds_f32;
 __device__ __forceinline__ int32_t chain_slot(const ChainStage &cs, int64_t c_lo, int64_t c) {
@@ -90,7 +110,7 @@ __device__ __forceinline__ float chain_ell(const ChainStage &cs, int64_t c_lo, i
 // called by every thread of the workgroup at step c (the condition is uniform); the
 // entries it writes are first read CHAIN_LDS / 2 - 2 steps later, after many barriers
 __device__ __forceinline__ void chain_refill(ChainStage &cs, const ComposeArgs &a, int64_t c_lo, int64_t c_hi,
-                                             int64_t c, int head, int th, int nthreads) {
+                                             int64_t c, int head, int th, int nthreads, HeadStage *hs = nullptr) {
     const int64_t d = c - c_lo;
     if (d < CHAIN_LDS / 2 || (d & (CHAIN_LDS / 2 - 1)) != 0) return;
     const int64_t j1 = c + CHAIN_LDS < c_hi ? c + CHAIN_LDS : c_hi;
@@ -98,6 +118,11 @@ __device__ __forceinline__ void chain_refill(ChainStage &cs, const ComposeArgs &
         const int32_t s = a.chain_slots[j];          // validated in range by the first pass
         cs.slot[(j - c_lo) & (CHAIN_LDS - 1)] = s;
         cs.ell[(j - c_lo) & (CHAIN_LDS - 1)] = a.pool_ell[(int64_t)s * a.H + head];
+        if (hs) {
+            int32_t info;
+            head_entry(a, j, info);                  // validated by the first pass
+            hs->info[(j - c_lo) & (CHAIN_LDS - 1)] = info;
+        }
     }
 }
 
@@ -121,9 +146,11 @@ struct __align__(16) PStage {
     uint32_t lo[NFRAG * FRAG_U32];
 };
 
-template <bool MODE_P>
+template <bool MODE_P, bool HEADS>
 __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a) {
+    static_assert(!(MODE_P && HEADS), "head tokens act on the state only");
     __shared__ PStage ps;
+    __shared__ typename std::conditional<HEADS, HeadStage, NoHeadStage>::type hst[1];
     // S_c, row-major, loaded straight from HBM into LDS; a separate LDS object from the
     // P fragments, so the compiler sees that staging P does not overlap the S loads
     // in flight and does not wait for them
@@ -152,9 +179,14 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
             const int32_t s = a.chain_slots[c];
             const bool ok = s >= 0 && s < a.num_slots;
             if (!ok) sh_bad = 1;
+            int32_t info = 0;
+            if constexpr (HEADS) {
+                if (head_entry(a, c, info)) sh_bad = 2;
+            }
             if (c - c_lo < CHAIN_LDS) {
                 cs.slot[c - c_lo] = ok ? s : 0;
                 cs.ell[c - c_lo] = ok ? a.pool_ell[(int64_t)s * a.H + head] : 0.f;
+                if constexpr (HEADS) hst[0].info[c - c_lo] = info;
             }
         }
     }
@@ -172,7 +204,8 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
     // ---- initial state; the first record from a zero (S) or identity (P) start is taken as is
     f32x16 st[4];
     int64_t c = c_lo;
-    const bool first_direct = MODE_P || a.init_S == nullptr;
+    // (with head tokens the first record meets the state its head tokens made)
+    const bool first_direct = !HEADS && (MODE_P || a.init_S == nullptr);
     double ell = 0.0;
     if (first_direct && c < c_hi) {
         const int64_t rec = (int64_t)a.chain_slots[c] * a.H + head;
@@ -193,6 +226,69 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
                                    : (a.init_S ? a.init_S[orec * D * D + (int64_t)row * D + col0 + l32] : 0.0f);
             }
     }
+
+    // ---- head tokens of chain entry c (HEADS): fetched into registers with S_c (thread
+    //      th takes channel th of [k | v] of each token, threads 0..MAXH-1 also its beta
+    //      and log alpha; every load unconditional, the token index clamped into the
+    //      stream), written to LDS at the top of step c and applied to the state before
+    //      the product: per token S <- alpha (S - beta k (k^T S)) + beta k v^T.
+    float hreg[MAXH], hb = 0.f, hl = 0.f;
+    int32_t hinfo = 0;
+#define HYPIC_FETCH_H(CC)                                                                        \
+    do {                                                                                         \
+        if constexpr (HEADS) {                                                                   \
+            hinfo = head_info(hst[0], c_lo, (CC));                                               \
+            const int64_t t0_ = hinfo >> 4;                                                      \
+            const int n_ = hinfo & 15;                                                           \
+            _Pragma("unroll") for (int j = 0; j < MAXH; ++j) {                                   \
+                int64_t t_ = t0_ + (j < n_ ? j : 0);                                             \
+                t_ = t_ < a.num_head_tokens ? t_ : a.num_head_tokens - 1;                        \
+                hreg[j] = th < D ? a.head_k[(t_ * a.H + head) * D + th]                          \
+                                 : a.head_v[(t_ * a.H + head) * D + th - D];                     \
+            }                                                                                    \
+            int64_t tb_ = t0_ + (th < n_ ? th : 0);                                              \
+            tb_ = tb_ < a.num_head_tokens ? tb_ : a.num_head_tokens - 1;                         \
+            hb = a.head_beta[tb_ * a.H + head];                                                  \
+            hl = a.head_la[tb_ * a.H + head];                                                    \
+        }                                                                                        \
+    } while (0)
+#define HYPIC_STAGE_H()                                                                          \
+    do {                                                                                         \
+        if constexpr (HEADS) {                                                                   \
+            _Pragma("unroll") for (int j = 0; j < MAXH; ++j) {                                   \
+                if (th < D) hst[0].k[j][th] = hreg[j];                                           \
+                else hst[0].v[j][th - D] = hreg[j];                                              \
+            }                                                                                    \
+            if (th < MAXH) { hst[0].beta[th] = hb; hst[0].la[th] = hl; }                         \
+        }                                                                                        \
+    } while (0)
+#define HYPIC_APPLY_H()                                                                          \
+    do {                                                                                         \
+        if constexpr (HEADS) {                                                                   \
+            const int n_ = hinfo & 15;                                                           \
+            for (int j = 0; j < n_; ++j) {                                                       \
+                float kr_[4][16];                                                                \
+                _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                 \
+                    _Pragma("unroll") for (int qq = 0; qq < 4; ++qq) {                           \
+                        const float4 k4 = *reinterpret_cast<const float4 *>(                     \
+                            &hst[0].k[j][32 * mb + 8 * qq + 4 * h]);                             \
+                        kr_[mb][4 * qq] = k4.x; kr_[mb][4 * qq + 1] = k4.y;                      \
+                        kr_[mb][4 * qq + 2] = k4.z; kr_[mb][4 * qq + 3] = k4.w;                  \
+                    }                                                                            \
+                float u_ = 0.f;                                                                  \
+                _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                 \
+                    _Pragma("unroll") for (int q = 0; q < 16; ++q) u_ += kr_[mb][q] * st[mb][q]; \
+                u_ += __shfl_xor(u_, 32);                /* the other half's rows */             \
+                const float be_ = hst[0].beta[j], la_ = hst[0].la[j];                            \
+                const float al_ = expf(la_);                                                     \
+                const float bu_ = be_ * u_, bv_ = be_ * hst[0].v[j][col0 + l32];                 \
+                _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                 \
+                    _Pragma("unroll") for (int q = 0; q < 16; ++q)                               \
+                        st[mb][q] = al_ * (st[mb][q] - kr_[mb][q] * bu_) + kr_[mb][q] * bv_;     \
+                ell += (double)la_;                                                              \
+            }                                                                                    \
+        }                                                                                        \
+    } while (0)
 
     // ---- records in flight: P_{c+1} is fetched into registers (coalesced 16-byte
     //      pieces q = th + 256 u) as soon as P_c has been split to bf16 hi/lo fragments
@@ -222,7 +318,8 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
     // state <- e^{ell_c} acc + S_c (S), or state <- acc (P)
 #define HYPIC_STEP(PF, EL)                                                                       \
     do {                                                                                         \
-        chain_refill(cs, a, c_lo, c_hi, c, head, th, NT);                                        \
+        if constexpr (HEADS) chain_refill(cs, a, c_lo, c_hi, c, head, th, NT, &hst[0]);          \
+        else chain_refill(cs, a, c_lo, c_hi, c, head, th, NT);                                   \
         _Pragma("unroll") for (int u = 0; u < 16; ++u) {                                         \
             const int q = th + NT * u;                                                           \
             const int i = q >> 5, k0 = 4 * (q & 31);                                             \
@@ -238,7 +335,9 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
         }                                                                                        \
         const float le = EL;                                                                     \
         HYPIC_FETCH_P(PF, EL, c + 1 < c_hi ? c + 1 : c);                                         \
-        lds_barrier();                                   /* fragments visible */                 \
+        HYPIC_STAGE_H();                                                                         \
+        lds_barrier();                                   /* fragments (and head tokens) visible */ \
+        HYPIC_APPLY_H();                                                                         \
         bf16x8 bh[8], bl[8];                                                                     \
         _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) acc_to_b2(st[kb >> 1], kb & 1, bh[kb], bl[kb]); \
         f32x16 acc[4];                                                                           \
@@ -276,10 +375,14 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
         }                                                                                        \
         ell += (double)le;                                                                       \
         lds_barrier();       /* fragments and S_c read by all before they are replaced */       \
+        /* head tokens before S, so that the compiler's wait for them at the top of the   */ \
+        /* next step does not also wait for S (loads complete in issue order)             */ \
+        HYPIC_FETCH_H(c + 1 < c_hi ? c + 1 : c);                                                 \
         if (!MODE_P) HYPIC_FETCH_S(c + 1 < c_hi ? c + 1 : c);  /* last step: an L2 hit */       \
     } while (0)
     if (c < c_hi) {
         HYPIC_FETCH_P(pa, ea, c);
+        HYPIC_FETCH_H(c);
         if (!MODE_P) HYPIC_FETCH_S(c);
         while (true) {
             HYPIC_STEP(pa, ea);
@@ -291,6 +394,9 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
 #undef HYPIC_STEP
 #undef HYPIC_FETCH_P
 #undef HYPIC_FETCH_S
+#undef HYPIC_FETCH_H
+#undef HYPIC_STAGE_H
+#undef HYPIC_APPLY_H
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -506,8 +612,16 @@ hipError_t launch_compose_mfma(const ComposeArgs &a, hipStream_t stream, bool *t
         return hipGetLastError();
     }
     const dim3 grid((unsigned)units);
-    hipLaunchKernelGGL(compose_dense_mfma_kernel<false>, grid, dim3(NT), 0, stream, a);
-    if (a.out_P) hipLaunchKernelGGL(compose_dense_mfma_kernel<true>, grid, dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((compose_dense_mfma_kernel<false, false>), grid, dim3(NT), 0, stream, a);
+    if (a.out_P) hipLaunchKernelGGL((compose_dense_mfma_kernel<true, false>), grid, dim3(NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+// Chains with head tokens (GDN, d_k = d_v = 128, no composed operator): one workgroup
+// per (request, head) whatever the count.
+hipError_t launch_compose_heads_mfma(const ComposeArgs &a, hipStream_t stream) {
+    const int64_t units = (int64_t)a.num_requests * a.H;
+    hipLaunchKernelGGL((compose_dense_mfma_kernel<false, true>), dim3((unsigned)units), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@ hipError_t launch_build_mfma(const BuildArgs &a, hipStream_t stream, bool *taken
 hipError_t launch_build_sd_mfma(const BuildArgs &a, hipStream_t stream, bool *taken);
 hipError_t launch_compose_ref(const ComposeArgs &a, hipStream_t stream);
 hipError_t launch_compose_mfma(const ComposeArgs &a, hipStream_t stream, bool *taken);
+hipError_t launch_compose_heads_mfma(const ComposeArgs &a, hipStream_t stream);
 }  // namespace hypic
 
 using namespace hypic;
@@ -113,6 +114,43 @@ hypic_status hypic_compose_chain(const hypic_pool *pool, int32_t num_requests,
     bool taken = false;
     hipError_t e = launch_compose_mfma(a, st, &taken);
     if (!taken) e = launch_compose_ref(a, st);
+    return e == hipSuccess ? HYPIC_OK : HYPIC_ERR_HIP;
+}
+
+hypic_status hypic_compose_chain_heads(const hypic_pool *pool, int32_t num_requests,
+                                       const int64_t *chain_offsets, const int32_t *chain_slots,
+                                       int64_t num_chain_slots, const int64_t *head_offsets,
+                                       int64_t num_head_tokens, const float *head_k, const float *head_v,
+                                       const float *head_beta, const float *head_log_alpha,
+                                       const float *init_S, float *out_S, float *out_log_scale,
+                                       uint32_t *err_flag, void *stream) {
+    const hypic_status ps = check_pool(pool);
+    if (ps != HYPIC_OK) return ps;
+    if (num_requests < 0 || num_chain_slots < 0 || num_head_tokens < 0) return HYPIC_ERR_INVALID_ARG;
+    if (pool->family != HYPIC_GDN || pool->d_k != 128 || pool->d_v != 128) return HYPIC_ERR_UNSUPPORTED;
+    if (num_head_tokens >= (1LL << 27)) return HYPIC_ERR_UNSUPPORTED;
+    if (num_requests == 0) return HYPIC_OK;
+    if (!chain_offsets || !out_S || !head_offsets) return HYPIC_ERR_INVALID_ARG;
+    if (num_chain_slots > 0 && !chain_slots) return HYPIC_ERR_INVALID_ARG;
+    if (num_head_tokens == 0) {       // no head tokens at all: the plain chain
+        if (head_k || head_v || head_beta || head_log_alpha) return HYPIC_ERR_INVALID_ARG;
+        return hypic_compose_chain(pool, num_requests, chain_offsets, chain_slots, num_chain_slots, init_S,
+                                   out_S, out_log_scale, nullptr, err_flag, stream);
+    }
+    if (!head_k || !head_v || !head_beta || !head_log_alpha) return HYPIC_ERR_INVALID_ARG;
+    if ((int64_t)num_requests * pool->num_heads > 0x7fffffffLL) return HYPIC_ERR_UNSUPPORTED;
+
+    ComposeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.family = pool->family; a.H = pool->num_heads; a.dk = pool->d_k; a.dv = pool->d_v;
+    a.num_requests = num_requests; a.num_slots = pool->num_slots; a.num_chain_slots = num_chain_slots;
+    a.pool_ell = pool->log_scale; a.pool_P = pool->P; a.pool_S = pool->S;
+    a.chain_offsets = chain_offsets; a.chain_slots = chain_slots;
+    a.init_S = init_S; a.out_S = out_S; a.out_ell = out_log_scale;
+    a.err_flag = err_flag;
+    a.head_offsets = head_offsets; a.num_head_tokens = num_head_tokens;
+    a.head_k = head_k; a.head_v = head_v; a.head_beta = head_beta; a.head_la = head_log_alpha;
+    const hipError_t e = launch_compose_heads_mfma(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? HYPIC_OK : HYPIC_ERR_HIP;
 }
 

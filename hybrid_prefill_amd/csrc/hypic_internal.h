@@ -33,6 +33,11 @@ struct ComposeArgs {
     const float *init_S;
     float *out_S, *out_ell, *out_P;
     uint32_t *err_flag;
+    // per chain entry, tokens applied to the state before its record (NULL: none)
+    const int64_t *head_offsets;        // [num_chain_slots + 1]
+    const float *head_k, *head_v;       // [T][H][d_k], [T][H][d_v]
+    const float *head_beta, *head_la;   // [T][H]
+    int64_t num_head_tokens;            // T
 };
 
 struct ConvArgs {

@@ -164,6 +164,35 @@ hypic_status hypic_compose_chain(const hypic_pool *pool, int32_t num_requests,
                                  float *out_P, uint32_t *err_flag, void *stream);
 
 /*
+ * hypic_compose_chain_heads -- hypic_compose_chain where chain entry c first
+ * applies a few tokens to the state, then folds its record:
+ *       for t in [head_offsets[c], head_offsets[c+1]):
+ *           S <- alpha_t (S - beta_t k_t (k_t^T S)) + beta_t k_t v_t^T   (alpha_t = e^{log_alpha_t})
+ *       S <- e^{ell_i} (P_i S) + S_i
+ * and out_log_scale adds the tokens' log alpha.  For conv variants (besthub
+ * article, paragraph 4: the convolution state warm-up): the tokens are a reused
+ * segment's first K-1, whose keys and values the warmed conv produced
+ * (hypic_conv_kv), and the record is the segment's suffix, so the chain equals
+ * the recurrence over the concatenated request without a record per head.
+ *
+ *   head_offsets   device int64 [num_chain_slots+1], non-decreasing, inside
+ *                  [0, num_head_tokens], at most 8 tokens per entry
+ *   head_k         [T][H][d_k] fp32;  head_v [T][H][d_v] fp32
+ *   head_beta, head_log_alpha   [T][H] fp32           (T = num_head_tokens)
+ * GDN pools with d_k = d_v = 128 only (else HYPIC_ERR_UNSUPPORTED); no composed
+ * operator.  num_head_tokens = 0 (all four head pointers NULL) is the plain chain.
+ * Error behaviour as hypic_compose_chain; malformed head offsets (or more than 8
+ * tokens at an entry) set HYPIC_EFLAG_BAD_OFFSETS and NaN-fill that request.
+ */
+hypic_status hypic_compose_chain_heads(const hypic_pool *pool, int32_t num_requests,
+                                       const int64_t *chain_offsets, const int32_t *chain_slots,
+                                       int64_t num_chain_slots, const int64_t *head_offsets,
+                                       int64_t num_head_tokens, const float *head_k, const float *head_v,
+                                       const float *head_beta, const float *head_log_alpha,
+                                       const float *init_S, float *out_S, float *out_log_scale,
+                                       uint32_t *err_flag, void *stream);
+
+/*
  * hypic_conv_warmup -- convolution state warm-up at segment boundaries
  * (besthub article, paragraph 4).  A causal depthwise conv of kernel size K
  * runs before the recurrence in conv variants; a segment prefilled on its own

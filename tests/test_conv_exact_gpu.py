@@ -72,19 +72,19 @@ def test_conv_exact_reuse_equals_sequential(cfg):
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     ce.cache_segments(c, pool, np.arange(S_seg), err_flag=err)
     plan = ce.plan_reuse(c, [np.asarray(ch) for ch in CHAINS], np.arange(S_seg), S_seg)
-    out = ce.reuse(c, plan, pool, err_flag=err)
-    torch.cuda.synchronize()
-    assert int(err.item()) == 0
     say(f"[conv exact] H={H} d={dk} {x_dtype} act={act}: chains {CHAINS}")
-    worst = 0.0
-    refs = []
-    for r, ch in enumerate(CHAINS):
-        ref = _sequential(c, ch, H, dk, dv)
-        refs.append(ref)
-        for h in range(H):
-            worst = max(worst, rel_fro(np64(out[r, h]), ref[h]))
-    say(f"   composed (warmed heads + suffixes) vs sequential: max err {worst:.2e}")
-    assert worst <= tol
+    refs = [_sequential(c, ch, H, dk, dv) for ch in CHAINS]
+    paths = [False] + ([True] if ce.fused_supported(pool) else [])
+    for fused in paths:
+        out = ce.reuse(c, plan, pool, err_flag=err, fused=fused)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        worst = max(rel_fro(np64(out[r, h]), refs[r][h]) for r in range(len(CHAINS)) for h in range(H))
+        say(f"   {'fused head tokens' if fused else 'head records'} + suffixes vs sequential: max err {worst:.2e}")
+        assert worst <= tol
+    if not ce.fused_supported(pool):
+        with pytest.raises(hp.HypicError):
+            ce.reuse(c, plan, pool, fused=True)
 
     # negative control: standalone records (zero conv history at every segment start)
     pool2 = hp.Pool.allocate(hp.GDN, S_seg, H, dk, dv, device="cuda", fill=0.0)
@@ -115,3 +115,66 @@ def test_conv_kv_bad_window_flags_and_nans():
     for t, rows in ((0, [0, 1]), (2, [2, 3, 4, 5])):
         kr, vr = oracle.conv_kv(xs[rows], np64(w), None, 1, H, dk, dv)
         assert rel_fro(np64(k[t]), kr[-1]) < 1e-5 and rel_fro(np64(v[t]), vr[-1]) < 1e-5
+
+
+@pytest.mark.parametrize("R", [3, 20])
+def test_compose_chain_heads_against_oracle(R):
+    """hypic_compose_chain_heads on synthetic records and head tokens (0 to 8 per entry):
+    each entry's head tokens built into a record by the oracle, composed before the
+    entry's record; 3 requests (a 1100-entry chain crosses the LDS slot ring's refill)
+    and 20 requests; malformed head offsets (9 tokens) flag and NaN-fill that request."""
+    H, d, nslots = 2, 128, 16
+    rng = np.random.default_rng(1500 + R)
+    q, _ = np.linalg.qr(rng.standard_normal((nslots, H, d, d)))
+    pool = hp.Pool.allocate(hp.GDN, nslots, H, d, d, device="cuda", fill=0.0)
+    pool.P.copy_(torch.from_numpy(q * rng.uniform(0.9, 1.0, size=(nslots, H, 1, d))).float())
+    pool.S.copy_(torch.from_numpy(rng.standard_normal((nslots, H, d, d))).float())
+    pool.log_scale.copy_(torch.from_numpy(rng.uniform(-0.05, 0.0, size=(nslots, H))).float())
+    lens = [1100, 0, 7] if R == 3 else [int(x) for x in rng.integers(0, 12, size=R)]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    flat = rng.integers(0, nslots, size=int(offs[-1])).astype(np.int32)
+    nh = rng.integers(0, 9, size=len(flat))
+    hoffs = np.concatenate([[0], np.cumsum(nh)]).astype(np.int64)
+    T = int(hoffs[-1])
+    hk = synth.keys(T, H, d, torch.float32, 1510 + R, "cuda")
+    hv = synth.values(T, H, d, torch.float32, 1511 + R, "cuda")
+    hb = synth.write_gate(T, H, 1512 + R, "cuda")
+    hla = synth.gdn_log_decay(T, H, 1513 + R, 0.1, "cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out_ell = torch.empty((R, H), device="cuda")
+    out = hp.compose_chain_heads(pool, torch.as_tensor(offs).cuda(), torch.as_tensor(flat).cuda(),
+                                 torch.as_tensor(hoffs).cuda(), hk, hv, hb, hla, out_log_scale=out_ell,
+                                 err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    # oracle: a record per entry's head tokens, composed before the entry's record
+    k_, v_, b_, la_ = np64(hk), np64(hv), np64(hb), np64(hla)
+    hell, hP, hS = oracle.build_segments(oracle.GDN, k_, v_, la_, hoffs, beta=b_)
+    E = len(flat)
+    mp_ell = np.concatenate([hell, np64(pool.log_scale)[flat]])           # [2E + ..., H]
+    mp_P = np.concatenate([hP, np64(pool.P)[flat]])
+    mp_S = np.concatenate([hS, np64(pool.S)[flat]])
+    chain = np.empty(2 * E, dtype=np.int32)
+    chain[0::2] = np.arange(E)
+    chain[1::2] = E + np.arange(E)
+    rS, rell, _ = oracle.compose(oracle.GDN, mp_ell, mp_P, mp_S, 2 * offs, chain)
+    worst = max(rel_fro(np64(out[r, h]), rS[r, h]) for r in range(R) for h in range(H))
+    dl = float(np.max(np.abs(np64(out_ell) - rell)))
+    say(f"[compose heads] R={R} lens={lens[:6]} head tokens {T}: S err {worst:.2e}, ell err {dl:.2e}")
+    assert worst <= 1e-4 and dl <= 1e-4
+    # 9 head tokens at one entry of request 1: that request only is NaN, the flag says bad offsets
+    nh2 = nh.copy()
+    e1 = int(offs[1]) if lens[1] > 0 else int(offs[2]) if R > 2 and lens[2] > 0 else None
+    if e1 is not None:
+        nh2[e1] = 9
+        hoffs2 = np.concatenate([[0], np.cumsum(nh2)]).astype(np.int64)
+        T2 = int(hoffs2[-1])
+        err.zero_()
+        out2 = hp.compose_chain_heads(pool, torch.as_tensor(offs).cuda(), torch.as_tensor(flat).cuda(),
+                                      torch.as_tensor(hoffs2).cuda(),
+                                      *[torch.cat([x, x[:max(0, T2 - T)]]) for x in (hk, hv, hb, hla)],
+                                      err_flag=err)
+        torch.cuda.synchronize()
+        bad_r = 1 if lens[1] > 0 else 2
+        assert int(err.item()) & hp.EFLAG_BAD_OFFSETS
+        assert torch.all(torch.isnan(out2[bad_r])) and not torch.any(torch.isnan(out2[0]))
