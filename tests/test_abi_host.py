@@ -176,3 +176,24 @@ def test_conv_kv_validation(L):
     assert call(k=None) == INVALID
     assert call(src=FAKE) == INVALID                     # src_token without beta_out / la_out
     assert call(T=0) == 0
+
+
+def test_compose_chain_heads_validation(L):
+    c = L.hypic_compose_chain_heads
+    p = pool(dk=128, dv=128)
+
+    def call(pp=p, R=1, offs=FAKE, slots=FAKE, ns=1, hoffs=FAKE, T=3, hk=FAKE, hv=FAKE, hb=FAKE, hl=FAKE,
+             out=FAKE):
+        return c(ctypes.byref(pp), R, offs, slots, ns, hoffs, T, hk, hv, hb, hl, None, out, None, None, None)
+
+    # every call below fails validation before any launch
+    assert call(pp=pool(dk=64, dv=64)) == UNSUPPORTED                       # fused compose: d = 128 only
+    assert call(pp=pool(family=hp.SCALAR, dk=128, dv=128, P=False)) == UNSUPPORTED
+    assert call(T=1 << 27) == UNSUPPORTED
+    assert call(T=-1) == INVALID
+    assert call(hoffs=None) == INVALID
+    assert call(hk=None) == INVALID
+    assert call(hl=None) == INVALID
+    assert call(out=None) == INVALID
+    assert call(T=0) == INVALID                                             # no tokens, but head pointers given
+    assert call(R=0) == 0
