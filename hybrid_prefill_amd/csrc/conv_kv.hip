@@ -15,7 +15,9 @@
 // the previous segment's last raw inputs (the warm-up).
 //
 // One workgroup per output token: the conv is computed channel-parallel into
-// LDS, then one wave per head reduces the key norm and writes the head.
+// LDS (16 bytes of channels per thread and load when the channel count and the
+// pointers allow it), then one wave per head reduces the key norm and writes the
+// head.
 #include "hypic_internal.h"
 
 namespace hypic {
@@ -26,7 +28,29 @@ constexpr int NT = 256;
 template <typename OT>
 __device__ __forceinline__ OT to_out(float x) { return (OT)x; }   // bf16: round to nearest even
 
-template <typename XT, typename OT>
+// 16 bytes of raw inputs: 8 bf16 or 4 fp32 channels, as floats
+template <typename XT> struct XV;
+template <> struct XV<uint16_t> {
+    static constexpr int N = 8;
+    static __device__ __forceinline__ void load(const uint16_t *p, float *f) {
+        const uint4 r = *reinterpret_cast<const uint4 *>(p);
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+template <> struct XV<float> {
+    static constexpr int N = 4;
+    static __device__ __forceinline__ void load(const float *p, float *f) {
+        const float4 r = *reinterpret_cast<const float4 *>(p);
+        f[0] = r.x; f[1] = r.y; f[2] = r.z; f[3] = r.w;
+    }
+};
+
+template <typename XT, typename OT, bool VEC>
 __global__ __launch_bounds__(NT) void conv_kv_kernel(ConvKvArgs a) {
     extern __shared__ float y[];          // [C]
     __shared__ int bad;
@@ -65,13 +89,46 @@ __global__ __launch_bounds__(NT) void conv_kv_kernel(ConvKvArgs a) {
     int32_t rows[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) rows[j] = j < K ? a.window[(int64_t)t * K + j] : -1;
-    for (int c = th; c < C; c += NT) {
-        float acc = a.bias ? a.bias[c] : 0.0f;
+    if constexpr (VEC) {
+        // kernel size 4: a channel's taps are one 16-byte load
+        constexpr int NV = XV<XT>::N;
+        const float4 *w4 = reinterpret_cast<const float4 *>(a.weight);
+        for (int c0 = NV * th; c0 < C; c0 += NV * NT) {
+            float acc[NV];
+            float4 wv[NV];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < K && rows[j] >= 0) acc += a.weight[(int64_t)c * K + j] * load_f32(x + (int64_t)rows[j] * C + c);
-        if (a.activation == 1) acc = acc / (1.0f + expf(-acc));
-        y[c] = acc;
+            for (int i = 0; i < NV; ++i) {
+                acc[i] = a.bias ? a.bias[c0 + i] : 0.0f;
+                wv[i] = w4[c0 + i];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (rows[j] >= 0) {
+                    float xv[NV];
+                    XV<XT>::load(x + (int64_t)rows[j] * C + c0, xv);
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) {
+                        const float wj = j == 0 ? wv[i].x : j == 1 ? wv[i].y : j == 2 ? wv[i].z : wv[i].w;
+                        acc[i] += wj * xv[i];
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                float v = acc[i];
+                if (a.activation == 1) v = v / (1.0f + expf(-v));
+                y[c0 + i] = v;
+            }
+        }
+    } else {
+        for (int c = th; c < C; c += NT) {
+            float acc = a.bias ? a.bias[c] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (j < K && rows[j] >= 0) acc += a.weight[(int64_t)c * K + j] * load_f32(x + (int64_t)rows[j] * C + c);
+            if (a.activation == 1) acc = acc / (1.0f + expf(-acc));
+            y[c] = acc;
+        }
     }
     __syncthreads();
     // keys: wave w takes heads w, w + 4, ...; lane l the channels l, l + 64, ...
@@ -98,15 +155,25 @@ __global__ __launch_bounds__(NT) void conv_kv_kernel(ConvKvArgs a) {
 
 hipError_t launch_conv_kv(const ConvKvArgs &a, hipStream_t stream) {
     if (a.num_tokens <= 0) return hipSuccess;
-    const size_t lds = (size_t)a.H * (a.dk + a.dv) * sizeof(float);
+    const int C = a.H * (a.dk + a.dv);
+    const size_t lds = (size_t)C * sizeof(float);
     const dim3 grid((unsigned)a.num_tokens);
-    if (a.x_dtype == HYPIC_BF16) {
-        if (a.out_dtype == HYPIC_BF16) hipLaunchKernelGGL((conv_kv_kernel<uint16_t, __bf16>), grid, dim3(NT), lds, stream, a);
-        else hipLaunchKernelGGL((conv_kv_kernel<uint16_t, float>), grid, dim3(NT), lds, stream, a);
+    const bool bf = a.x_dtype == HYPIC_BF16;
+    const bool vec = a.ksize == 4 && C % (bf ? 8 : 4) == 0 && ((uintptr_t)a.x & 15) == 0 &&
+                     ((uintptr_t)a.weight & 15) == 0;
+#define HYPIC_CKV(XT_, OT_)                                                                        \
+    do {                                                                                           \
+        if (vec) hipLaunchKernelGGL((conv_kv_kernel<XT_, OT_, true>), grid, dim3(NT), lds, stream, a); \
+        else hipLaunchKernelGGL((conv_kv_kernel<XT_, OT_, false>), grid, dim3(NT), lds, stream, a);    \
+    } while (0)
+    if (bf) {
+        if (a.out_dtype == HYPIC_BF16) HYPIC_CKV(uint16_t, __bf16);
+        else HYPIC_CKV(uint16_t, float);
     } else {
-        if (a.out_dtype == HYPIC_BF16) hipLaunchKernelGGL((conv_kv_kernel<float, __bf16>), grid, dim3(NT), lds, stream, a);
-        else hipLaunchKernelGGL((conv_kv_kernel<float, float>), grid, dim3(NT), lds, stream, a);
+        if (a.out_dtype == HYPIC_BF16) HYPIC_CKV(float, __bf16);
+        else HYPIC_CKV(float, float);
     }
+#undef HYPIC_CKV
     return hipGetLastError();
 }
 

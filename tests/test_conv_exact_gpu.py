@@ -178,3 +178,24 @@ def test_compose_chain_heads_against_oracle(R):
         bad_r = 1 if lens[1] > 0 else 2
         assert int(err.item()) & hp.EFLAG_BAD_OFFSETS
         assert torch.all(torch.isnan(out2[bad_r])) and not torch.any(torch.isnan(out2[0]))
+
+
+@pytest.mark.parametrize("dims,dtype", [((1, 3, 2), torch.float32), ((3, 5, 3), torch.bfloat16),
+                                        ((2, 64, 64), torch.bfloat16)])
+def test_conv_kv_against_oracle(dims, dtype):
+    """conv_kv on a stream with per-token windows (the stream's own history) against the
+    oracle, on channel counts off and on the 16-byte vector width (both kernel forms)."""
+    H, dk, dv = dims
+    K, n = 4, 37
+    C = H * (dk + dv)
+    x = synth.conv_stream(n, C, dtype, 1600 + C, "cuda")
+    w = synth.conv_weights(C, K, 1601 + C, "cuda")
+    bias = torch.randn(C, device="cuda") * 0.1
+    pos = np.arange(n)[:, None] + np.arange(-K + 1, 1)[None, :]
+    win = torch.as_tensor(np.where(pos >= 0, pos, -1).astype(np.int32), device="cuda")
+    k, v = hp.conv_kv(x, win, w, H, dk, dv, bias=bias, activation=1, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kr, vr = oracle.conv_kv(np64(x), np64(w), np64(bias), 1, H, dk, dv)
+    ek, ev = rel_fro(np64(k), kr), rel_fro(np64(v), vr)
+    say(f"[conv_kv] H={H} dk={dk} dv={dv} C={C} {dtype}: k err {ek:.2e}, v err {ev:.2e}")
+    assert ek <= 1e-5 and ev <= 1e-5
