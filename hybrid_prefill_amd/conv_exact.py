@@ -33,12 +33,13 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-from . import GDN, Pool, build_segment, compose_chain, compose_chain_heads, conv_kv
+from . import GDN, SCALAR, Pool, build_segment, compose_chain, compose_chain_heads, conv_kv
 
 
 @dataclass
 class ConvCache:
-    """Raw inputs and parameters of the cached segments of one conv variant layer."""
+    """Raw inputs and parameters of the cached segments of one conv variant layer
+    (GDN, or the scalar family: both have per-token per-head beta and log alpha)."""
     x: torch.Tensor               # [rows, C] raw inputs (bf16 or fp32); segment s = rows [offsets[s], offsets[s+1])
     offsets: np.ndarray           # int64 [S+1]
     beta: torch.Tensor            # [rows, H] fp32
@@ -50,6 +51,7 @@ class ConvCache:
     d_k: int
     d_v: int
     kv_dtype: torch.dtype         # dtype of the keys and values the records are built from
+    family: int = GDN             # GDN, or SCALAR (Mamba2-style: per-token scalar decay [rows, H])
 
     @property
     def K(self) -> int:
@@ -87,7 +89,7 @@ def cache_segments(c: ConvCache, pool: Pool, slots: np.ndarray, from_token: Opti
                           err_flag=err_flag)
     offs = np.zeros(len(lens) + 1, dtype=np.int64)
     offs[1:] = np.cumsum(lens)
-    build_segment(GDN, k, v, la, torch.as_tensor(offs, device=dev), pool,
+    build_segment(c.family, k, v, la, torch.as_tensor(offs, device=dev), pool,
                   torch.as_tensor(np.asarray(slots, dtype=np.int32), device=dev), beta=b, err_flag=err_flag)
 
 
@@ -142,6 +144,7 @@ def plan_reuse(c: ConvCache, chains: List[np.ndarray], suffix_slot: np.ndarray, 
 
 
 def fused_supported(pool: Pool) -> bool:
+    """The compose with head tokens takes GDN pools with d_k = d_v = 128."""
     return pool.family == GDN and pool.d_k == 128 and pool.d_v == 128
 
 
@@ -153,6 +156,8 @@ def reuse(c: ConvCache, plan: ReusePlan, pool: Pool, out_S: Optional[torch.Tenso
     def run(name, fn):
         return timer.time(name, fn) if timer is not None else fn()
 
+    if c.family not in (GDN, SCALAR):
+        raise ValueError("conv-coupled records: GDN or scalar family")
     if fused is None:
         fused = fused_supported(pool)
     if fused:
@@ -166,7 +171,7 @@ def reuse(c: ConvCache, plan: ReusePlan, pool: Pool, out_S: Optional[torch.Tenso
     k, v, b, la = run("conv_kv", lambda: conv_kv(
         c.x, plan.head_window, c.weight, c.num_heads, c.d_k, c.d_v, bias=c.bias, activation=c.activation,
         out_dtype=c.kv_dtype, src_token=plan.head_src, beta=c.beta, log_alpha=c.log_alpha, err_flag=err_flag))
-    run("head_build", lambda: build_segment(GDN, k, v, la, plan.head_offsets, pool, plan.head_slots, beta=b,
-                                            err_flag=err_flag))
+    run("head_build", lambda: build_segment(c.family, k, v, la, plan.head_offsets, pool, plan.head_slots,
+                                            beta=b, err_flag=err_flag))
     return run("compose", lambda: compose_chain(pool, plan.chain_offsets, plan.chain_slots, out_S=out_S,
                                                 err_flag=err_flag))

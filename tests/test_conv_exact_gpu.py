@@ -35,7 +35,7 @@ LENS = [1, 2, 3, 5, 64, 130, 7, 40, 0, 3]
 CHAINS = [[0, 1, 2, 3], [4, 5, 6, 7], [5, 0, 5], [2], [7, 6, 5, 4, 3, 2, 1, 0], [8, 9, 8, 4], []]
 
 
-def _setup(H, dk, dv, x_dtype, kv_dtype, act, bias, seed, decay):
+def _setup(H, dk, dv, x_dtype, kv_dtype, act, bias, seed, decay, family=hp.GDN):
     K = 4
     C = H * (dk + dv)
     offs = synth.offsets_from_lengths(LENS)
@@ -45,7 +45,10 @@ def _setup(H, dk, dv, x_dtype, kv_dtype, act, bias, seed, decay):
     b = torch.randn(C, device="cuda") * 0.1 if bias else None
     beta = synth.write_gate(N, H, seed + 2, "cuda")
     la = synth.gdn_log_decay(N, H, seed + 3, decay, "cuda")
-    return ce.ConvCache(x, offs, beta, la, w, b, act, H, dk, dv, kv_dtype)
+    if family == hp.SCALAR:      # Mamba2-style: per-token scalar decay, beta = 1
+        beta = torch.ones_like(beta)
+        la = synth.gdn_log_decay(N, H, seed + 3, decay * 10, "cuda")
+    return ce.ConvCache(x, offs, beta, la, w, b, act, H, dk, dv, kv_dtype, family)
 
 
 def _sequential(c, chain, H, dk, dv):
@@ -57,22 +60,24 @@ def _sequential(c, chain, H, dk, dv):
     x = np64(c.x)[rows]
     k, v = oracle.conv_kv(x, np64(c.weight), None if c.bias is None else np64(c.bias), c.activation, H, dk, dv)
     b, la = np64(c.beta)[rows], np64(c.log_alpha)[rows]
-    _, _, S = oracle.build_segments(oracle.GDN, k, v, la, [0, len(rows)], beta=b, want_P=False)
+    _, _, S = oracle.build_segments(c.family, k, v, la, [0, len(rows)], beta=b, want_P=False)
     return S[0]
 
 
-@pytest.mark.parametrize("cfg", [(2, 64, 64, torch.float32, torch.float32, 1, True, 1e-4),
-                                 (4, 128, 128, torch.bfloat16, torch.bfloat16, 0, False, 2e-2)])
+@pytest.mark.parametrize("cfg", [(2, 64, 64, torch.float32, torch.float32, 1, True, 1e-4, hp.GDN),
+                                 (4, 128, 128, torch.bfloat16, torch.bfloat16, 0, False, 2e-2, hp.GDN),
+                                 (2, 64, 64, torch.float32, torch.float32, 1, False, 1e-4, hp.SCALAR),
+                                 (4, 128, 128, torch.bfloat16, torch.bfloat16, 1, True, 2e-2, hp.SCALAR)])
 def test_conv_exact_reuse_equals_sequential(cfg):
-    H, dk, dv, x_dtype, kv_dtype, act, bias, tol = cfg
-    c = _setup(H, dk, dv, x_dtype, kv_dtype, act, bias, 1300 + dk, 0.001)
+    H, dk, dv, x_dtype, kv_dtype, act, bias, tol, family = cfg
+    c = _setup(H, dk, dv, x_dtype, kv_dtype, act, bias, 1300 + dk + 7 * family, 0.001, family)
     S_seg = len(LENS)
     n_heads = sum(len(ch) for ch in CHAINS)
-    pool = hp.Pool.allocate(hp.GDN, S_seg + n_heads, H, dk, dv, device="cuda", fill=0.0)
+    pool = hp.Pool.allocate(family, S_seg + n_heads, H, dk, dv, device="cuda", fill=0.0)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     ce.cache_segments(c, pool, np.arange(S_seg), err_flag=err)
     plan = ce.plan_reuse(c, [np.asarray(ch) for ch in CHAINS], np.arange(S_seg), S_seg)
-    say(f"[conv exact] H={H} d={dk} {x_dtype} act={act}: chains {CHAINS}")
+    say(f"[conv exact] family {family} H={H} d={dk} {x_dtype} act={act}: chains {CHAINS}")
     refs = [_sequential(c, ch, H, dk, dv) for ch in CHAINS]
     paths = [False] + ([True] if ce.fused_supported(pool) else [])
     for fused in paths:
@@ -87,7 +92,7 @@ def test_conv_exact_reuse_equals_sequential(cfg):
             ce.reuse(c, plan, pool, fused=True)
 
     # negative control: standalone records (zero conv history at every segment start)
-    pool2 = hp.Pool.allocate(hp.GDN, S_seg, H, dk, dv, device="cuda", fill=0.0)
+    pool2 = hp.Pool.allocate(family, S_seg, H, dk, dv, device="cuda", fill=0.0)
     ce.cache_segments(c, pool2, np.arange(S_seg), from_token=0)
     offs = np.concatenate([[0], np.cumsum([len(ch) for ch in CHAINS])]).astype(np.int64)
     flat = np.asarray(sum(CHAINS, []), dtype=np.int32)
