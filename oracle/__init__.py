@@ -11,7 +11,8 @@ compose, don't add" and "Family comparison"):
 
 * ``build_segments`` -- per segment and head, the record ``(ell, P, S)`` of the
   recurrence ``S_t = A_t S_{t-1} + beta_t k_t v_t^T`` from ``S_0 = 0``, with
-  ``T_C = e^ell P``, token by token in fp64.
+  ``T_C = e^ell P`` (KDA, ``A_t = (I - beta k k^T) diag(alpha_t)``: ``ell = 0``,
+  ``P = T_C``), token by token in fp64.
 * ``compose`` -- ``S <- T_i S + S_i`` over a chain of pool records in prompt order.
 * ``causal_conv`` -- the full causal depthwise short convolution over a raw stream.
 * ``conv_kv`` -- a conv variant's keys and values over a raw stream: the causal
@@ -34,7 +35,7 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-SCALAR, DIAGONAL, GDN = 0, 1, 2
+SCALAR, DIAGONAL, GDN, KDA = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hypic_oracle.c")
@@ -112,12 +113,15 @@ def build_segments(family: int, k, v, log_alpha, seg_offsets, beta=None, init_S=
     if family == DIAGONAL:
         assert la.shape == (N, H, dk)
         ell = np.zeros((nseg, H, dk))
+    elif family == KDA:
+        assert la.shape == (N, H, dk)
+        ell = np.zeros((nseg, H))
     else:
         assert la.shape == (N, H)
         ell = np.zeros((nseg, H))
     if b is not None:
         assert b.shape == (N, H)
-    P = np.zeros((nseg, H, dk, dk)) if (family == GDN and want_P) else None
+    P = np.zeros((nseg, H, dk, dk)) if (family in (GDN, KDA) and want_P) else None
     S = np.zeros((nseg, H, dk, dv))
     rc = lib.oracle_build_segments(family, H, dk, dv, nseg, _ptr(offs, ctypes.c_int64),
                                    _ptr(k), _ptr(v), _ptr(b), _ptr(la), _ptr(s0),
@@ -143,7 +147,7 @@ def compose(family: int, pool_ell, pool_P, pool_S, chain_offsets, chain_slots, i
     R = offs.shape[0] - 1
     out_S = np.zeros((R, H, dk, dv))
     out_ell = np.zeros((R, H, dk)) if family == DIAGONAL else np.zeros((R, H))
-    out_P = np.zeros((R, H, dk, dk)) if (family == GDN and want_P) else None
+    out_P = np.zeros((R, H, dk, dk)) if (family in (GDN, KDA) and want_P) else None
     rc = lib.oracle_compose(family, H, dk, dv, nslots, _ptr(pe), _ptr(pP), _ptr(pS), R,
                             _ptr(offs, ctypes.c_int64), _ptr(slots, ctypes.c_int32),
                             _ptr(s0), _ptr(out_S), _ptr(out_ell), _ptr(out_P))

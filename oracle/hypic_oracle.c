@@ -30,11 +30,14 @@
  *      scalar    A_t = alpha_t I
  *      diagonal  A_t = diag(alpha_t)           (alpha_t in (0,1)^{d_k})
  *      GDN       A_t = alpha_t (I - beta_t k_t k_t^T)
+ *      KDA       A_t = (I - beta_t k_t k_t^T) diag(alpha_t)   (alpha_t in (0,1)^{d_k})
  *      T_C = A_n ... A_1,   S(C|0) = S_n,   so  S_n = T_C S_0 + S(C|0).
  *
  * A record is kept in the exactly factored form T_C = e^{ell} P with
  * ell = sum_t log alpha_t (per key channel for the diagonal family) and
  * P = prod_{t=n..1} (I - beta_t k_t k_t^T) (GDN only; P = I otherwise).
+ * KDA's per-channel gates do not commute with the projections, so its record
+ * holds T_C itself: ell = 0, P = T_C.
  * beta = NULL means beta_t = 1.
  *
  * Everything is computed token by token in fp64, exactly as the recurrence
@@ -48,7 +51,7 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_SCALAR = 0, ORACLE_DIAGONAL = 1, ORACLE_GDN = 2 };
+enum { ORACLE_SCALAR = 0, ORACLE_DIAGONAL = 1, ORACLE_GDN = 2, ORACLE_KDA = 3 };
 
 int oracle_num_threads(void)
 {
@@ -71,8 +74,8 @@ void oracle_set_num_threads(int n)
 /*
  * One head of one segment, token by token.
  *   k[t*k_ts + i], v[t*v_ts + j], beta[t*b_ts] (or NULL), la[t*la_ts (+ i)]
- * Writes ell (1 value, or d_k for the diagonal family), P (d_k*d_k, GDN only,
- * may be NULL) and S (d_k*d_v).  S0 (d_k*d_v) is the start state, NULL = 0.
+ * Writes ell (1 value, or d_k for the diagonal family), P (d_k*d_k, GDN and
+ * KDA, may be NULL) and S (d_k*d_v).  S0 (d_k*d_v) is the start state, NULL = 0.
  * work must hold d_k + d_v doubles.
  */
 static void recur_head(int family, int64_t n, int dk, int dv,
@@ -119,6 +122,29 @@ static void recur_head(int family, int64_t n, int dk, int dv,
                 for (int j = 0; j < dv; ++j)
                     S[i * dv + j] = a * (S[i * dv + j] - b * kt[i] * w[j]) + b * kt[i] * vt[j];
             ell[0] += lat;
+        } else if (family == ORACLE_KDA) {
+            /* X <- (I - b k k^T) diag(a) X for X = P and X = S, then S += b k v^T */
+            const double *lat = la + t * la_ts;
+            if (P) {
+                for (int i = 0; i < dk; ++i) {
+                    const double a = exp(lat[i]);
+                    for (int j = 0; j < dk; ++j) P[i * dk + j] *= a;
+                }
+                for (int j = 0; j < dk; ++j) u[j] = 0.0;
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dk; ++j) u[j] += kt[i] * P[i * dk + j];
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dk; ++j) P[i * dk + j] -= b * kt[i] * u[j];
+            }
+            for (int i = 0; i < dk; ++i) {
+                const double a = exp(lat[i]);
+                for (int j = 0; j < dv; ++j) S[i * dv + j] *= a;
+            }
+            for (int j = 0; j < dv; ++j) w[j] = 0.0;
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) w[j] += kt[i] * S[i * dv + j];
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) S[i * dv + j] += b * kt[i] * (vt[j] - w[j]);
         } else if (family == ORACLE_SCALAR) {
             const double lat = la[t * la_ts];
             const double a = exp(lat);
@@ -155,13 +181,14 @@ int oracle_build_segments(int family, int H, int dk, int dv,
                           const double *init_S,
                           double *ell, double *P, double *S)
 {
-    if (family < 0 || family > 2 || H <= 0 || dk <= 0 || dv <= 0 || num_segments < 0) return -1;
+    if (family < 0 || family > 3 || H <= 0 || dk <= 0 || dv <= 0 || num_segments < 0) return -1;
     if (!seg_offsets || !k || !v || !log_alpha || !ell || !S) return -1;
     for (int s = 0; s < num_segments; ++s)
         if (seg_offsets[s + 1] < seg_offsets[s] || seg_offsets[s] < 0) return -1;
 
     const int n_ell = family == ORACLE_DIAGONAL ? dk : 1;
-    const int64_t la_ts = family == ORACLE_DIAGONAL ? (int64_t)H * dk : H;
+    const int per_channel = family == ORACLE_DIAGONAL || family == ORACLE_KDA;
+    const int64_t la_ts = per_channel ? (int64_t)H * dk : H;
     const int64_t units = (int64_t)num_segments * H;
 
 #pragma omp parallel
@@ -173,8 +200,8 @@ int oracle_build_segments(int family, int H, int dk, int dv,
             const int64_t t0 = seg_offsets[s];
             const int64_t n = seg_offsets[s + 1] - t0;
             const size_t rec = (size_t)s * H + h;
-            const double *la = family == ORACLE_DIAGONAL ? log_alpha + t0 * la_ts + (int64_t)h * dk
-                                                         : log_alpha + t0 * la_ts + h;
+            const double *la = per_channel ? log_alpha + t0 * la_ts + (int64_t)h * dk
+                                           : log_alpha + t0 * la_ts + h;
             recur_head(family, n, dk, dv,
                        k + (t0 * H + h) * dk, (int64_t)H * dk,
                        v + (t0 * H + h) * dv, (int64_t)H * dv,
@@ -182,7 +209,7 @@ int oracle_build_segments(int family, int H, int dk, int dv,
                        la, la_ts,
                        init_S ? init_S + rec * dk * dv : NULL,
                        ell + rec * n_ell,
-                       (family == ORACLE_GDN && P) ? P + rec * dk * dk : NULL,
+                       ((family == ORACLE_GDN || family == ORACLE_KDA) && P) ? P + rec * dk * dk : NULL,
                        S + rec * dk * dv, work);
         }
         free(work);
@@ -192,7 +219,7 @@ int oracle_build_segments(int family, int H, int dk, int dv,
 
 /*
  * Composition of pool records in prompt order, per (request, head):
- *      S <- T_i S + S_i = e^{ell_i} (P_i S) + S_i        (GDN)
+ *      S <- T_i S + S_i = e^{ell_i} (P_i S) + S_i        (GDN; KDA with ell_i = 0)
  *      S <- e^{ell_i} S + S_i                             (scalar)
  *      S <- diag(e^{ell_i}) S + S_i                       (diagonal)
  * The composed operator is accumulated too: ell <- ell + ell_i and, for GDN
@@ -211,9 +238,10 @@ int oracle_compose(int family, int H, int dk, int dv, int64_t num_slots,
                    const double *init_S,
                    double *out_S, double *out_ell, double *out_P)
 {
-    if (family < 0 || family > 2 || H <= 0 || dk <= 0 || dv <= 0 || R < 0) return -1;
+    if (family < 0 || family > 3 || H <= 0 || dk <= 0 || dv <= 0 || R < 0) return -1;
     if (!pool_ell || !pool_S || !chain_offsets || !out_S) return -1;
-    if (family == ORACLE_GDN && !pool_P) return -1;
+    const int dense = family == ORACLE_GDN || family == ORACLE_KDA;   /* records with P */
+    if (dense && !pool_P) return -1;
     for (int r = 0; r < R; ++r) {
         if (chain_offsets[r + 1] < chain_offsets[r] || chain_offsets[r] < 0) return -1;
         for (int64_t c = chain_offsets[r]; c < chain_offsets[r + 1]; ++c)
@@ -243,7 +271,7 @@ int oracle_compose(int family, int H, int dk, int dv, int64_t num_slots,
                 const size_t rec = (size_t)chain_slots[c] * H + h;
                 const double *ell_i = pool_ell + rec * n_ell;
                 const double *S_i = pool_S + rec * dk * dv;
-                if (family == ORACLE_GDN) {
+                if (dense) {
                     const double *P_i = pool_P + rec * dk * dk;
                     const double sc = exp(ell_i[0]);
                     /* tmp = P_i S */
@@ -278,7 +306,7 @@ int oracle_compose(int family, int H, int dk, int dv, int64_t num_slots,
                 }
             }
             if (out_ell) memcpy(out_ell + orec * n_ell, ellacc, sizeof(double) * (size_t)n_ell);
-            if (out_P && family == ORACLE_GDN)
+            if (out_P && dense)
                 memcpy(out_P + orec * dk * dk, Pacc, sizeof(double) * (size_t)dk * dk);
         }
         free(tmp);

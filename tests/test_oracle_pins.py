@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import DIAGONAL, GDN, SCALAR, rel_fro
+from oracle import DIAGONAL, GDN, KDA, SCALAR, rel_fro
 
 GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -32,7 +32,7 @@ def rand_inputs(family, n, H, dk, dv, seed, decay=0.1, beta=True):
     k = z / np.linalg.norm(z, axis=-1, keepdims=True)
     v = rng.standard_normal((n, H, dv))
     b = 1.0 / (1.0 + np.exp(-rng.standard_normal((n, H)))) if beta else None
-    if family == DIAGONAL:
+    if family in (DIAGONAL, KDA):
         la = -decay * np.log1p(np.exp(rng.standard_normal((n, H, dk))))
     else:
         la = -decay * np.log1p(np.exp(rng.standard_normal((n, H))))
@@ -46,6 +46,8 @@ def dense_transition(family, k, b, la):
         return math.exp(la) * np.eye(dk)
     if family == DIAGONAL:
         return np.diag(np.exp(la))
+    if family == KDA:
+        return (np.eye(dk) - b * np.outer(k, k)) @ np.diag(np.exp(la))
     return math.exp(la) * (np.eye(dk) - b * np.outer(k, k))
 
 
@@ -64,7 +66,7 @@ def brute_force(family, k, v, b, la, S0=None):
 
 
 def record_T(family, ell, P, dk):
-    if family == GDN:
+    if family in (GDN, KDA):       # KDA: ell = 0, P = T_C
         return math.exp(ell) * P
     if family == SCALAR:
         return math.exp(ell) * np.eye(dk)
@@ -222,7 +224,7 @@ def test_plain_linear_attention_naive_add_exact():
 
 # ----------------------------------------------------------------------------- brute force
 
-@pytest.mark.parametrize("family", [SCALAR, DIAGONAL, GDN])
+@pytest.mark.parametrize("family", [SCALAR, DIAGONAL, GDN, KDA])
 def test_brute_force_dense_products(family):
     n, H, dk, dv = 37, 2, 6, 5
     k, v, b, la = rand_inputs(family, n, H, dk, dv, 10 + family, decay=0.3)
@@ -247,7 +249,7 @@ def test_empty_segment_is_identity_record():
 
 # ----------------------------------------------------------------------------- invariants
 
-@pytest.mark.parametrize("family", [SCALAR, DIAGONAL, GDN])
+@pytest.mark.parametrize("family", [SCALAR, DIAGONAL, GDN, KDA])
 def test_composition_equals_sequential(family):
     # the identity the pages fix: composed records = recurrence over the concatenation
     H, dk, dv = 2, 8, 6
@@ -260,11 +262,11 @@ def test_composition_equals_sequential(family):
     ell_seq, P_seq, S_seq = oracle.build_segments(family, k, v, la, [0, n], beta=b)
     assert rel_fro(Sc[0], S_seq[0]) < 1e-12
     np.testing.assert_allclose(ellc[0], ell_seq[0], atol=1e-12)
-    if family == GDN:
+    if family in (GDN, KDA):
         assert rel_fro(Pc[0], P_seq[0]) < 1e-12
 
 
-@pytest.mark.parametrize("family", [SCALAR, DIAGONAL, GDN])
+@pytest.mark.parametrize("family", [SCALAR, DIAGONAL, GDN, KDA])
 def test_record_maps_any_start_state(family):
     # S_n(S_0) = T_C S_0 + S(C|0) for an arbitrary start state
     n, H, dk, dv = 23, 2, 5, 4
@@ -280,7 +282,7 @@ def test_record_maps_any_start_state(family):
     assert rel_fro(Sc, S_from) < 1e-13
 
 
-@pytest.mark.parametrize("family", [SCALAR, DIAGONAL, GDN])
+@pytest.mark.parametrize("family", [SCALAR, DIAGONAL, GDN, KDA])
 def test_partition_invariance(family):
     H, dk, dv, n = 1, 6, 4, 60
     k, v, b, la = rand_inputs(family, n, H, dk, dv, 40 + family, decay=0.02)
@@ -472,3 +474,50 @@ def test_conv_kv_suffix_context_free_head_warmed():
     np.testing.assert_allclose(k[n1:n1 + K - 1], kw[K - 1:2 * (K - 1)], atol=1e-13)
     np.testing.assert_allclose(v[n1:n1 + K - 1], vw[K - 1:2 * (K - 1)], atol=1e-13)
     assert np.max(np.abs(k[n1:n1 + K - 1] - k2[:K - 1])) > 1e-2
+
+
+# ----------------------------------------------------------------------------- KDA special cases
+
+def test_kda_without_decay_is_gdn_without_decay():
+    """alpha = 1: (I - beta k k^T) diag(1) is the ungated delta rule, as GDN with log alpha = 0."""
+    n, H, dk, dv = 29, 2, 6, 5
+    k, v, b, la = rand_inputs(KDA, n, H, dk, dv, 80)
+    ell_k, P_k, S_k = oracle.build_segments(KDA, k, v, np.zeros((n, H, dk)), [0, n], beta=b)
+    ell_g, P_g, S_g = oracle.build_segments(GDN, k, v, np.zeros((n, H)), [0, n], beta=b)
+    np.testing.assert_allclose(P_k, P_g, atol=1e-14)
+    np.testing.assert_allclose(S_k, S_g, atol=1e-14)
+    assert np.all(ell_k == 0.0) and np.all(ell_g == 0.0)
+
+
+def test_kda_without_writes_is_the_product_of_gates():
+    """beta = 0: A_t = diag(alpha_t), so T_C = diag(prod_t alpha_t) and nothing is written."""
+    n, H, dk, dv = 21, 2, 5, 3
+    k, v, _, la = rand_inputs(KDA, n, H, dk, dv, 81, decay=0.2)
+    ell, P, S = oracle.build_segments(KDA, k, v, la, [0, n], beta=np.zeros((n, H)))
+    for h in range(H):
+        np.testing.assert_allclose(P[0, h], np.diag(np.exp(la[:, h].sum(axis=0))), atol=1e-14)
+    assert np.all(S == 0.0)
+
+
+def test_kda_channel_keys_closed_form():
+    """Keys along coordinate axes: each A_t is diagonal, entry i scaled by alpha_{t,i} and,
+    on the key's own axis, by (1 - beta_t); S_n = sum_t (prod_{s>t} A_s) beta_t k_t v_t^T."""
+    n, dk, dv = 17, 4, 3
+    rng = np.random.default_rng(82)
+    axes = rng.integers(0, dk, size=n)
+    k = np.zeros((n, 1, dk))
+    k[np.arange(n), 0, axes] = 1.0
+    v = rng.standard_normal((n, 1, dv))
+    b = rng.uniform(0.1, 0.9, size=(n, 1))
+    la = -0.3 * rng.uniform(0.0, 1.0, size=(n, 1, dk))
+    _, P, S = oracle.build_segments(KDA, k, v, la, [0, n], beta=b)
+    diag = np.ones(dk)
+    S_cf = np.zeros((dk, dv))
+    for t in range(n):
+        a = np.exp(la[t, 0])
+        a[axes[t]] *= 1.0 - b[t, 0]
+        diag *= a
+        S_cf = a[:, None] * S_cf
+        S_cf[axes[t]] += b[t, 0] * v[t, 0]
+    np.testing.assert_allclose(P[0, 0], np.diag(diag), atol=1e-14)
+    np.testing.assert_allclose(S[0, 0], S_cf, atol=1e-13)
