@@ -25,7 +25,7 @@ from typing import Optional
 
 import torch
 
-SCALAR, DIAGONAL, GDN = 0, 1, 2
+SCALAR, DIAGONAL, GDN, KDA = 0, 1, 2, 3
 F32, BF16 = 0, 1
 EFLAG_SLOT_OUT_OF_RANGE = 0x1
 EFLAG_BAD_OFFSETS = 0x2
@@ -144,7 +144,7 @@ class Pool:
         ls_shape = (num_slots, num_heads, d_k) if family == DIAGONAL else (num_slots, num_heads)
         mk = (lambda s: torch.full(s, fill, dtype=torch.float32, device=device)) if fill is not None \
             else (lambda s: torch.empty(s, dtype=torch.float32, device=device))
-        P = mk((num_slots, num_heads, d_k, d_k)) if family == GDN else None
+        P = mk((num_slots, num_heads, d_k, d_k)) if family in (GDN, KDA) else None
         return Pool(family, num_heads, d_k, d_v, mk(ls_shape), mk((num_slots, num_heads, d_k, d_v)), P)
 
     def _c(self) -> _Pool:
@@ -180,9 +180,9 @@ def build_segment(family: int, k: torch.Tensor, v: torch.Tensor, log_alpha: Opti
     if log_alpha is not None:
         if log_alpha.dtype != torch.float32:
             raise HypicError("log_alpha must be fp32")
-        if family == DIAGONAL:
+        if family in (DIAGONAL, KDA):
             if log_alpha.dim() != 3 or log_alpha.stride(2) != 1:
-                raise HypicError("diagonal log_alpha must be [N,H,d_k] with unit channel stride")
+                raise HypicError("per-channel log_alpha must be [N,H,d_k] with unit channel stride")
             la_st, la_sh = log_alpha.stride(0), log_alpha.stride(1)
         elif log_alpha.dim() == 1:
             la_st, la_sh = 0, log_alpha.stride(0)

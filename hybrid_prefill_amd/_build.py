@@ -14,7 +14,8 @@ LIB = os.path.join(HERE, "libhypic.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["hypic_abi.hip", "build_ref.hip", "build_mfma.hip", "build_sd_mfma.hip", "compose_ref.hip",
-           "compose_mfma.hip", "conv_warmup.hip", "conv_kv.hip"]
+           "compose_mfma.hip", "conv_warmup.hip", "conv_kv.hip",
+           "build_kda.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

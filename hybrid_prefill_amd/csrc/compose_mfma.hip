@@ -601,7 +601,8 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
 
 hipError_t launch_compose_mfma(const ComposeArgs &a, hipStream_t stream, bool *taken) {
     *taken = false;
-    if (a.family != HYPIC_GDN || a.dk != 128 || a.dv != 128) return hipSuccess;
+    // (KDA records are (ell = 0, P = T_C): the same fold)
+    if ((a.family != HYPIC_GDN && a.family != HYPIC_KDA) || a.dk != 128 || a.dv != 128) return hipSuccess;
     *taken = true;
     const int64_t units = (int64_t)a.num_requests * a.H;
     if (units <= 512) {

@@ -257,7 +257,7 @@ __host__ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 template <int DK, int DV>
 hipError_t launch_dims(const ComposeArgs &a, hipStream_t stream) {
     const int64_t units = (int64_t)a.num_requests * a.H;
-    if (a.family == HYPIC_GDN) {
+    if (a.family == HYPIC_GDN || a.family == HYPIC_KDA) {      // (KDA: ell = 0, P = T_C)
         const int nslab_S = DV / NSL;
         const int nslab = nslab_S + (a.out_P ? DK / NSL : 0);
         hipLaunchKernelGGL((compose_dense_ref_kernel<DK, DV>), dim3((unsigned)(units * nslab)), dim3(NT), 0, stream, a, nslab_S);

@@ -9,6 +9,7 @@ namespace hypic {
 hipError_t launch_build_ref(const BuildArgs &a, hipStream_t stream);
 hipError_t launch_build_mfma(const BuildArgs &a, hipStream_t stream, bool *taken);
 hipError_t launch_build_sd_mfma(const BuildArgs &a, hipStream_t stream, bool *taken);
+hipError_t launch_build_kda(const BuildArgs &a, hipStream_t stream);
 hipError_t launch_compose_ref(const ComposeArgs &a, hipStream_t stream);
 hipError_t launch_compose_mfma(const ComposeArgs &a, hipStream_t stream, bool *taken);
 hipError_t launch_compose_heads_mfma(const ComposeArgs &a, hipStream_t stream);
@@ -19,7 +20,8 @@ using namespace hypic;
 namespace {
 
 bool head_size_ok(int32_t d) { return d == 64 || d == 128; }
-bool family_ok(int32_t f) { return f == HYPIC_SCALAR || f == HYPIC_DIAGONAL || f == HYPIC_GDN; }
+bool family_ok(int32_t f) { return f == HYPIC_SCALAR || f == HYPIC_DIAGONAL || f == HYPIC_GDN || f == HYPIC_KDA; }
+bool has_P(int32_t f) { return f == HYPIC_GDN || f == HYPIC_KDA; }
 bool dtype_ok(int32_t t) { return t == HYPIC_F32 || t == HYPIC_BF16; }
 
 hypic_status check_pool(const hypic_pool *pool) {
@@ -28,7 +30,7 @@ hypic_status check_pool(const hypic_pool *pool) {
     if (pool->num_heads <= 0 || pool->num_slots < 0) return HYPIC_ERR_INVALID_ARG;
     if (!head_size_ok(pool->d_k) || !head_size_ok(pool->d_v)) return HYPIC_ERR_UNSUPPORTED;
     if (!pool->S || !pool->log_scale) return HYPIC_ERR_INVALID_ARG;
-    if ((pool->family == HYPIC_GDN) != (pool->P != nullptr)) return HYPIC_ERR_INVALID_ARG;
+    if (has_P(pool->family) != (pool->P != nullptr)) return HYPIC_ERR_INVALID_ARG;
     return HYPIC_OK;
 }
 
@@ -80,6 +82,7 @@ hypic_status hypic_build_segment(const hypic_segments *in, const hypic_pool *poo
     a.err_flag = err_flag;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (a.family == HYPIC_KDA) return launch_build_kda(a, st) == hipSuccess ? HYPIC_OK : HYPIC_ERR_HIP;
     bool taken = false;
     hipError_t e = launch_build_mfma(a, st, &taken);
     if (!taken) e = launch_build_sd_mfma(a, st, &taken);
@@ -98,7 +101,7 @@ hypic_status hypic_compose_chain(const hypic_pool *pool, int32_t num_requests,
     if (num_requests == 0) return HYPIC_OK;
     if (!chain_offsets || !out_S) return HYPIC_ERR_INVALID_ARG;
     if (num_chain_slots > 0 && !chain_slots) return HYPIC_ERR_INVALID_ARG;
-    if (out_P && pool->family != HYPIC_GDN) return HYPIC_ERR_INVALID_ARG;
+    if (out_P && !has_P(pool->family)) return HYPIC_ERR_INVALID_ARG;
     if ((int64_t)num_requests * pool->num_heads * 4 > 0x7fffffffLL) return HYPIC_ERR_UNSUPPORTED;
 
     ComposeArgs a;

@@ -10,6 +10,7 @@
  *       HYPIC_SCALAR    A_t = alpha_t I               (RetNet / Mamba2 style decay)
  *       HYPIC_DIAGONAL  A_t = diag(alpha_t)           (GLA style gates on the key channels)
  *       HYPIC_GDN       A_t = alpha_t (I - beta_t k_t k_t^T)   (gated delta rule; DeltaNet = alpha 1)
+ *       HYPIC_KDA       A_t = (I - beta_t k_t k_t^T) diag(alpha_t)   (one gate per key channel)
  *   For a segment C of n tokens its record is the cumulative transition operator
  *   T_C = A_n ... A_1 and the zero-initial terminal state S(C|0) = S_n, so that
  *   a start state S_0 maps to T_C S_0 + S(C|0).  Segments are then composed in
@@ -30,7 +31,8 @@
  * commutes with everything, so T_C = e^{ell} P with ell = sum_t log alpha_t
  * and P = prod_{t=n..1} (I - beta_t k_t k_t^T).  A pool record per head is
  *       log_scale  ell         1 float (d_k floats for HYPIC_DIAGONAL)
- *       P          d_k x d_k   fp32, row-major (HYPIC_GDN only; P = I otherwise)
+ *       P          d_k x d_k   fp32, row-major (HYPIC_GDN; for HYPIC_KDA, whose gates do not
+ *                  factor out, P = T_C itself and ell = 0; P = I otherwise)
  *       S          d_k x d_v   fp32, row-major
  * Keeping ell apart keeps T_C inside fp32 range: e^{ell} of a 2048-token
  * segment is far below the smallest fp32 normal at typical decay rates.
@@ -71,7 +73,7 @@ typedef enum {
     HYPIC_ERR_HIP = 3            /* the kernel launch failed (hipGetLastError) */
 } hypic_status;
 
-typedef enum { HYPIC_SCALAR = 0, HYPIC_DIAGONAL = 1, HYPIC_GDN = 2 } hypic_family;
+typedef enum { HYPIC_SCALAR = 0, HYPIC_DIAGONAL = 1, HYPIC_GDN = 2, HYPIC_KDA = 3 } hypic_family;
 typedef enum { HYPIC_F32 = 0, HYPIC_BF16 = 1 } hypic_dtype;
 
 #define HYPIC_EFLAG_SLOT_OUT_OF_RANGE 0x1u   /* a slot id outside [0, num_slots) */
@@ -80,7 +82,7 @@ typedef enum { HYPIC_F32 = 0, HYPIC_BF16 = 1 } hypic_dtype;
 /*
  * Segment pool: caller-owned device memory holding one record per (slot, head).
  *   log_scale  [num_slots][H] fp32, or [num_slots][H][d_k] for HYPIC_DIAGONAL
- *   P          [num_slots][H][d_k][d_k] fp32, HYPIC_GDN only (must be NULL otherwise)
+ *   P          [num_slots][H][d_k][d_k] fp32, HYPIC_GDN and HYPIC_KDA only (NULL otherwise)
  *   S          [num_slots][H][d_k][d_v] fp32
  * All three are dense and row-major.
  */
