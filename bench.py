@@ -13,13 +13,15 @@ Secondary lines (same JSON object, key "secondary"):
   rag mix        128 requests of 24-96 cached/cold GDN segments (128-1024 tokens),
                  cold builds + conv warm-up (4096 channels, kernel 4) + all chains
   conv exact     conv-coupled exact reuse: 32 requests of 24-96 cached segments,
-                 warmed head keys/values, head records, chains of 2m records
+                 warmed head keys/values applied inside the compose
+  kda            KDA family build (token-serial fp32) and 8-segment chain, H=16,
+                 d=128, bf16, 8 x 2048 tokens
 
 Inputs are resident in HBM before the timed region starts.  Kernel durations
 come from HIP events recorded on the stream the kernels are launched on.
 The cpu_baseline leg times the fp64 oracle on a bounded sample on the host.
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|sd|compose|rag|convexact] [--no-cpu]
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|sd|compose|rag|convexact|kda] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -402,6 +404,36 @@ def bench_conv_exact(args, R=32, pool_segs=512, H=32, d=128, K=4, seed=601):
             "kernels_ms": parts, "plain_chain_ms": plain_ms, "head_records_path_ms": unfused}
 
 
+def bench_kda(args, H=16, d=128, nseg=8, seg_len=2048, seed=701):
+    """KDA family (A_t = (I - beta k k^T) diag(alpha_t), per-channel gates), H=16, d=128,
+    bf16, 8 x 2048 tokens (the scalar / diagonal workload's shape): build of every
+    record (T_C, S) and the 8-segment chain.  The build is a token-serial fp32 kernel:
+    5 d_k (d_k + d_v) FLOP per token-head on the vector ALU."""
+    N = nseg * seg_len
+    k = synth.keys(N, H, d, torch.bfloat16, seed, "cuda")
+    v = synth.values(N, H, d, torch.bfloat16, seed + 1, "cuda")
+    b = synth.write_gate(N, H, seed + 2, "cuda")
+    la = synth.diagonal_log_gates(N, H, d, seed + 3, 16.0, "cuda")
+    offs = torch.as_tensor(synth.even_offsets(nseg, seg_len)).cuda()
+    slots = torch.arange(nseg, dtype=torch.int32, device="cuda")
+    chain = torch.tensor([0, nseg], dtype=torch.int64, device="cuda")
+    pool = hp.Pool.allocate(hp.KDA, nseg, H, d, d, device="cuda")
+    for _ in range(max(1, args.warmup)):
+        hp.build_segment(hp.KDA, k, v, la, offs, pool, slots, beta=b)
+    torch.cuda.synchronize()
+    b_ms, c_ms = kernel_pass((("build", lambda: hp.build_segment(hp.KDA, k, v, la, offs, pool, slots, beta=b)),
+                              ("compose", lambda: hp.compose_chain(pool, chain, slots))), max(3, args.steps // 4))
+    flops = 5.0 * d * (d + d) * N * H
+    # vector fp32 peak with packed fp32 ops off (the build flags): half of 157.3 TFLOP/s
+    peak_alu = PEAK_FP32 / 2 / 1e12
+    log(f"kda: build {b_ms:.3f} ms ({flops / (b_ms * 1e-3) / 1e12:.2f} TFLOP/s fp32 VALU), compose {c_ms:.3f} ms")
+    del pool
+    torch.cuda.empty_cache()
+    return {"workload": f"kda_build_h{H}_d{d}_{nseg}x{seg_len}", "metric": "tokens/s", "value": N / (b_ms * 1e-3),
+            "unit": "tokens/s", "ms": b_ms, "compose_ms": c_ms,
+            "roofline": roofline("alu", flops / (b_ms * 1e-3) / 1e12, peak_alu, "TFLOP/s")}
+
+
 def hbm_attainable(gib=4):
     """Context for the HBM fractions: the rate PyTorch's own device copy (read + write)
     reaches on this GPU over `gib` GiB."""
@@ -436,8 +468,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["all", "main", "sd", "compose", "rag", "convexact"], default="all",
-                    help="main: only the headline GDN step; sd / compose / rag / convexact: it plus that secondary leg")
+    ap.add_argument("--only", choices=["all", "main", "sd", "compose", "rag", "convexact", "kda"], default="all",
+                    help="main: only the headline GDN step; sd / compose / rag / convexact / kda: it plus that leg")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one untimed 1 GiB device copy (reference kernel for HBM byte counters)")
@@ -468,6 +500,8 @@ def main():
         secondary.append(bench_rag(args))
     if args.only in ("all", "convexact"):
         secondary.append(bench_conv_exact(args))
+    if args.only in ("all", "kda"):
+        secondary.append(bench_kda(args))
     attainable = hbm_attainable()
     cpu = None if args.no_cpu else cpu_baseline()
     line = {
