@@ -15,7 +15,7 @@ OBJ_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["hypic_abi.hip", "build_ref.hip", "build_mfma.hip", "build_sd_mfma.hip", "compose_ref.hip",
            "compose_mfma.hip", "conv_warmup.hip", "conv_kv.hip",
-           "build_kda.hip"]
+           "build_kda.hip", "build_kda_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -7,8 +7,8 @@
 // the record holds T_C itself (P = T_C, ell = 0), and the dense compose applies
 // it as it applies a GDN record.
 //
-// Token-serial fp32 kernel (the chunked UT form with per-channel decay inside
-// the triangular solve is not built yet).  Workgroup q of a (segment, head) keeps
+// Token-serial fp32 kernel, for the shapes other than d_k = d_v = 128 (those take
+// the chunked kernel on the matrix cores).  Workgroup q of a (segment, head) keeps
 // 64 of the d_k + d_v columns of [T | S]; four consecutive threads share a column,
 // each with d_k / 4 of its rows in registers, so a token is, per thread, a row
 // scale, a partial dot product with k (summed over the four with two shuffles)
@@ -161,6 +161,7 @@ __global__ __launch_bounds__(NT) void kda_build_kernel(KdaArgs ka) {
 
 hipError_t launch_build_kda(const BuildArgs &b, hipStream_t stream) {
     if (b.num_segments <= 0) return hipSuccess;
+    if (b.dk == 128 && b.dv == 128) return launch_build_kda_mfma(b, stream);
     KdaArgs a;
     a.b = b;
     a.nq = (b.dk + b.dv + COLS - 1) / COLS;

@@ -65,6 +65,7 @@ hipError_t launch_build(const BuildArgs &a, hipStream_t stream);
 hipError_t launch_compose(const ComposeArgs &a, hipStream_t stream);
 hipError_t launch_conv_warmup(const ConvArgs &a, hipStream_t stream);
 hipError_t launch_conv_kv(const ConvKvArgs &a, hipStream_t stream);
+hipError_t launch_build_kda_mfma(const BuildArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers
 

@@ -90,3 +90,36 @@ def test_kda_long_segments_as_given_gates():
     eC = max(rel_fro(np64(out[0, h]), S_seq[0, h]) for h in range(H))
     say(f"[kda long] S err {eS:.2e}, composed vs sequential {eC:.2e}")
     assert eS <= 2e-2 and eC <= 2e-2
+
+
+@pytest.mark.parametrize("dtype,tol", [(torch.float32, 1e-4), (torch.bfloat16, 2e-2)])
+def test_kda_strong_gates(dtype, tol):
+    """Stretches where a few key channels decay by e^-20 per token (and one token that
+    closes a channel by e^-200): at d = 128 the chunks that hold them are applied token
+    by token inside the chunked kernel (a scaled key there would leave the fp32 range),
+    the rest of each segment in chunk form; T_C, S and the composed chain against the
+    oracle."""
+    H, d = 2, 128
+    lens = [300, 97, 32, 33]
+    offs, k, v, b, la = _inputs(lens, H, d, d, dtype, 1790, 1600.0)
+    la[40:120, :, :8] = -20.0
+    la[250, 1, 100] = -200.0
+    la[330:345, 0, 5] = -12.0
+    nseg = len(lens)
+    slots = np.arange(nseg, dtype=np.int32)
+    pool = hp.Pool.allocate(hp.KDA, nseg, H, d, d, device="cuda", fill=777.0)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hp.build_segment(hp.KDA, k, v, la, torch.as_tensor(offs).cuda(), pool, torch.as_tensor(slots).cuda(),
+                     beta=b, err_flag=err)
+    out = hp.compose_chain(pool, torch.as_tensor(np.array([0, nseg], np.int64)).cuda(),
+                           torch.as_tensor(slots).cuda(), err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    kn, vn, bn, lan = np64(k), np64(v), np64(b), np64(la)
+    _, P, S = oracle.build_segments(oracle.KDA, kn, vn, lan, offs, beta=bn)
+    eT = max(rel_fro(np64(pool.P[s, h]), P[s, h]) for s in range(nseg) for h in range(H))
+    eS = max(rel_fro(np64(pool.S[s, h]), S[s, h]) for s in range(nseg) for h in range(H))
+    _, _, S_seq = oracle.build_segments(oracle.KDA, kn, vn, lan, [0, int(offs[-1])], beta=bn, want_P=False)
+    eC = max(rel_fro(np64(out[0, h]), S_seq[0, h]) for h in range(H))
+    say(f"[kda strong gates] {dtype}: T_C err {eT:.2e}, S err {eS:.2e}, composed vs sequential {eC:.2e}")
+    assert eT <= tol and eS <= tol and eC <= tol
