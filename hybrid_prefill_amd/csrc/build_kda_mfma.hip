@@ -109,28 +109,34 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
             X[r][i] = (!isS && 32 * r + 8 * (i >> 2) + 4 * hh + (i & 3) == colw) ? 1.0f : 0.0f;
 
     // Staging role: key channel ch (also the value column), tokens 16hf .. 16hf+15.
-    // The next chunk's inputs are fetched into registers while the current one runs;
-    // entries past the segment read its last token and are replaced by zeros.
+    // The next chunk's inputs are fetched into registers while the current one runs.
+    // The loads take no branch (a branch joining around a load makes the compiler
+    // wait for it there): entries past the segment read its last token, a missing
+    // log alpha or beta is read from the keys with stride 0, and the selects that
+    // replace them (zero gates and values, unit or zero beta) are applied at use.
     const int ch = th & 127, hf = th >> 7;
-    float rla[CK], rk[16], rv[16], rb = 0.0f;
+    const bool has_la = a.log_alpha != nullptr, has_b = a.beta != nullptr;
+    const float *la_p = has_la ? a.log_alpha + head * a.la_sh + ch : static_cast<const float *>(a.k);
+    const int64_t la_st = has_la ? a.la_st : 0;
+    const float *b_p = has_b ? a.beta + head * a.b_sh : static_cast<const float *>(a.k);
+    const int64_t b_st = has_b ? a.b_st : 0;
+    const XT *k_p = kp + head * a.k_sh + ch;
+    const XT *v_p = vp + head * a.v_sh + ch;
+    float rla[CK], rk[16], rv[16], rb;
     auto fetch = [&](int64_t c0) {
         const int cl = n - c0 < CK ? (int)(n - c0) : CK;
+        const int64_t base = t0 + c0;
 #pragma unroll
-        for (int t = 0; t < CK; ++t) {
-            const int64_t tok = t0 + c0 + (t < cl ? t : cl - 1);
-            rla[t] = a.log_alpha ? a.log_alpha[tok * a.la_st + head * a.la_sh + ch] : 0.0f;
-        }
+        for (int t = 0; t < CK; ++t) rla[t] = la_p[(base + (t < cl ? t : cl - 1)) * la_st];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int t = 16 * hf + u;
-            const int64_t tok = t0 + c0 + (t < cl ? t : cl - 1);
-            rk[u] = load_f32(kp + tok * a.k_st + head * a.k_sh + ch);
-            rv[u] = isS ? load_f32(vp + tok * a.v_st + head * a.v_sh + ch) : 0.0f;
+            const int64_t tok = base + (t < cl ? t : cl - 1);
+            rk[u] = load_f32(k_p + tok * a.k_st);
+            rv[u] = load_f32(v_p + tok * a.v_st);
         }
-        if (th < CK) {
-            const int64_t tok = t0 + c0 + (th < cl ? th : cl - 1);
-            rb = a.beta ? a.beta[tok * a.b_st + head * a.b_sh] : 1.0f;
-        }
+        const int tb_ = th & (CK - 1);
+        rb = b_p[(base + (tb_ < cl ? tb_ : cl - 1)) * b_st];
     };
     if (n > 0) fetch(0);
 
@@ -141,7 +147,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
             float acc = 0.0f;
 #pragma unroll
             for (int t = 0; t < CK; ++t) {
-                acc += (t < cl ? rla[t] : 0.0f) * LOG2E;
+                acc += (t < cl && has_la ? rla[t] : 0.0f) * LOG2E;
                 G[t] = acc;
             }
         }
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
                 sm.qd[t][ch] = kk * ex2(g - Gr);
                 sm.kd[t][ch] = kk * ex2(Gr - g);
                 sm.x1[t][ch] = kk * ex2(hf ? g - Gh : Gh - g);
-                sm.v[t][ch] = t < cl ? rv[u] : 0.0f;
+                sm.v[t][ch] = t < cl && isS ? rv[u] : 0.0f;
             }
             if (hf == 0) sm.gam[ch] = ex2(Gc);
         } else {
@@ -173,12 +179,12 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
             for (int u = 0; u < 16; ++u) {
                 const int t = 16 * hf + u;
                 sm.qd[t][ch] = t < cl ? rk[u] : 0.0f;
-                sm.kd[t][ch] = t < cl ? ex2(rla[t] * LOG2E) : 1.0f;
-                sm.v[t][ch] = t < cl ? rv[u] : 0.0f;
+                sm.kd[t][ch] = t < cl && has_la ? ex2(rla[t] * LOG2E) : 1.0f;
+                sm.v[t][ch] = t < cl && isS ? rv[u] : 0.0f;
             }
         }
-        if (th < CK) sm.b[th] = th < cl ? rb : 0.0f;
-        if (c0 + CK < n) fetch(c0 + CK);
+        if (th < CK) sm.b[th] = th < cl ? (has_b ? rb : 1.0f) : 0.0f;
+        fetch(c0 + CK);                     // past the last chunk: the segment's last token again, unused
         __syncthreads();
 
         if (!serial) {
