@@ -152,10 +152,15 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
             }
         }
         const float Gc = G[CK - 1], Gh = G[15], Gr = hf ? G[23] : G[7];
+        // This thread's half of the prefix (a select per token: indexing G by the
+        // runtime half would compile to a compare-and-select over all 32 registers).
+        float Gs[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) Gs[u] = hf ? G[16 + u] : G[u];
         float emax = -INFINITY;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            const float g = G[16 * hf + u];
+            const float g = Gs[u];
             emax = fmaxf(emax, fmaxf(fmaxf(g, Gc - g), fmaxf(g - Gr, Gr - g)));
             emax = fmaxf(emax, hf ? g - Gh : Gh - g);
         }
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 const int t = 16 * hf + u;
-                const float kk = t < cl ? rk[u] : 0.0f, g = G[t];
+                const float kk = t < cl ? rk[u] : 0.0f, g = Gs[u];
                 sm.kg[t][ch] = kk * ex2(g);
                 sm.kht[ch][t] = kk * ex2(Gc - g);
                 sm.qd[t][ch] = kk * ex2(g - Gr);
@@ -179,7 +184,8 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
             for (int u = 0; u < 16; ++u) {
                 const int t = 16 * hf + u;
                 sm.qd[t][ch] = t < cl ? rk[u] : 0.0f;
-                sm.kd[t][ch] = t < cl && has_la ? ex2(rla[t] * LOG2E) : 1.0f;
+                const float la_t = hf ? rla[16 + u] : rla[u];
+                sm.kd[t][ch] = t < cl && has_la ? ex2(la_t * LOG2E) : 1.0f;
                 sm.v[t][ch] = t < cl && isS ? rv[u] : 0.0f;
             }
         }
