@@ -55,7 +55,8 @@ struct KdaMfmaSmem {
     float v[CK][LP];       // v of this workgroup's columns (S workgroup)
     float kht[D][TP];      // Khat^T
     float nm[CK][TP];      // beta_t A_ts for s < t
-    float tb[CK][TP];      // T diag(beta)
+    float tw[4][CK][TP];   // per wave: T (diagonal blocks)
+    float tn[4][CK][TP];   // per wave: -T diag(beta) (upper right block zero)
     float gam[D];          // e^{g_C}
     float b[CK];
     int64_t t0, n;
@@ -138,6 +139,8 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
         const int tb_ = th & (CK - 1);
         rb = b_p[(base + (tb_ < cl ? tb_ : cl - 1)) * b_st];
     };
+    // The upper right block of every wave's -T diag(beta) stays zero.
+    for (int e = th; e < 4 * 16 * 16; e += NT) sm.tn[e >> 8][(e >> 4) & 15][16 + (e & 15)] = 0.0f;
     if (n > 0) fetch(0);
 
     for (int64_t c0 = 0; c0 < n; c0 += CK) {
@@ -219,62 +222,85 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
                 }
             }
             __syncthreads();
-            // T = (I + N)^{-1}, N = diag(beta) A strictly lower: lane j builds column j
-            // row by row; T diag(beta) goes to LDS.
-            if (w == 0 && lane < CK) {
-                const int j = lane;
-                float tc[CK];
+            // Every wave now works alone until the next chunk (no barrier):
+            // (1) W = K_g X_0 - V on its columns (contraction over state rows), which
+            //     does not need T, so the scheduler can overlap it with
+            // (2) its own copy of T = (I + N)^{-1} (N = diag(beta) A, strictly lower):
+            //     the two diagonal 16 x 16 blocks by forward substitution (lane per
+            //     column: lanes 0-15 the first block, 16-31 the second, the upper half
+            //     of the wave repeating them), then T_10 = -T_11 (N_10 T_00) on the
+            //     16x16x4 MFMA; -T diag(beta) goes to the wave's own LDS tile;
+            // (3) E = -T diag(beta) W = T diag(beta) (V - K_g X_0);
+            // (4) X_C = diag(e^{g_C}) X_0 + Khat^T E.
+            f32x16 W0, W1;
 #pragma unroll
-                for (int i = 0; i < CK; ++i) tc[i] = i == j ? 1.0f : 0.0f;
+            for (int i = 0; i < 16; ++i) {
+                W0[i] = isS ? -sm.v[8 * (i >> 2) + 4 * hh + (i & 3)][colw] : 0.0f;
+                W1[i] = 0.0f;
+            }
 #pragma unroll
-                for (int i = 1; i < CK; ++i) {
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const f32x4 kv = *reinterpret_cast<const f32x4 *>(&sm.kg[ln][32 * r + 8 * s + 4 * hh]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (r & 1) W1 = mfma32(kv[j], X[r][4 * s + j], W1);
+                        else W0 = mfma32(kv[j], X[r][4 * s + j], W0);
+                    }
+                }
+            float(*tw)[TP] = sm.tw[w];
+            float(*tn)[TP] = sm.tn[w];
+            {
+                const int c = lane & 15, blk = (lane >> 4) & 1, o = 16 * blk;
+                float tc[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) tc[i] = i == c ? 1.0f : 0.0f;
+#pragma unroll
+                for (int i = 1; i < 16; ++i) {
                     float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
                     for (int m4 = 0; m4 < i; m4 += 4) {
-                        const f32x4 nv = *reinterpret_cast<const f32x4 *>(&sm.nm[i][m4]);
+                        const f32x4 nv = *reinterpret_cast<const f32x4 *>(&sm.nm[o + i][o + m4]);
                         if (m4 + 0 < i) s0 += nv[0] * tc[m4 + 0];
                         if (m4 + 1 < i) s1 += nv[1] * tc[m4 + 1];
                         if (m4 + 2 < i) s0 += nv[2] * tc[m4 + 2];
                         if (m4 + 3 < i) s1 += nv[3] * tc[m4 + 3];
                     }
-                    if (i > j) tc[i] = -(s0 + s1);
+                    if (i > c) tc[i] = -(s0 + s1);
                 }
-                const float bj = sm.b[j];
+                const float bc = sm.b[o + c];
 #pragma unroll
-                for (int i = 0; i < CK; ++i) sm.tb[i][j] = tc[i] * bj;
+                for (int i = 0; i < 16; ++i) {
+                    tw[o + i][o + c] = tc[i];
+                    tn[o + i][o + c] = -tc[i] * bc;
+                }
             }
-            __syncthreads();
-            // M = T diag(beta) K_g (wave w: channels 32w..32w+31) and U = T diag(beta) V
-            // (wave w: its own state columns), contraction over the chunk's tokens 8s + 4hh + j.
-            f32x16 Mw, E0, E1;
+            {
+                // Y = N_10 T_00, then T_11 Y = -T_10 (contraction index 4g + j at step j).
+                const int m = lane & 15, g = lane >> 4;
+                const f32x4 na = *reinterpret_cast<const f32x4 *>(&sm.nm[16 + m][4 * g]);
+                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 16; ++i) { Mw[i] = 0.0f; E0[i] = 0.0f; E1[i] = 0.0f; }
+                for (int j = 0; j < 4; ++j) Y = mfma16(na[j], tw[4 * g + j][m], Y);
+                const f32x4 ta = *reinterpret_cast<const f32x4 *>(&tw[16 + m][16 + 4 * g]);
+                f32x4 Z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Z = mfma16(ta[j], Y[j], Z);
+                const float bm = sm.b[m];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) tn[16 + 4 * g + j][m] = Z[j] * bm;
+            }
+            const f32x16 Wt = W0 + W1;             // rows: the chunk's tokens 8(i/4) + 4hh + i%4
+            f32x16 E;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) E[i] = 0.0f;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const f32x4 ta = *reinterpret_cast<const f32x4 *>(&sm.tb[ln][8 * s + 4 * hh]);
+                const f32x4 ta = *reinterpret_cast<const f32x4 *>(&tn[ln][8 * s + 4 * hh]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int tk = 8 * s + 4 * hh + j;
-                    Mw = mfma32(ta[j], sm.kg[tk][colw], Mw);
-                    if (isS) E0 = mfma32(ta[j], sm.v[tk][colw], E0);
-                }
+                for (int j = 0; j < 4; ++j) E = mfma32(ta[j], Wt[4 * s + j], E);
             }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sm.qd[8 * (i >> 2) + 4 * hh + (i & 3)][colw] = -Mw[i];
-            __syncthreads();
-            // E = U - M X_0 on the wave's columns (contraction over state rows).
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const f32x4 ma = *reinterpret_cast<const f32x4 *>(&sm.qd[ln][32 * r + 8 * s + 4 * hh]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        if (r & 1) E1 = mfma32(ma[j], X[r][4 * s + j], E1);
-                        else E0 = mfma32(ma[j], X[r][4 * s + j], E0);
-                    }
-                }
-            const f32x16 E = E0 + E1;              // rows: the chunk's tokens 8(i/4) + 4hh + i%4
             // X_C = diag(e^{g_C}) X_0 + Khat^T E.
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
