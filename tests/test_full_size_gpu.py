@@ -13,6 +13,8 @@ the benchmark times, on sampled outputs the fp64 oracle computes one by one.
                 requests' composed states against the recurrence over their
                 concatenated tokens, sampled cold records against the oracle's
                 build, sampled boundaries against the causal conv.
+  KDA build     H=16, d=128, bf16, 8 x 2048 tokens: sampled records' S, and T_C
+                over a 256-token build of the same stream.
 """
 import numpy as np
 import pytest
@@ -193,3 +195,40 @@ def test_rag_mix_full_size():
     assert worst_c <= 1e-4
     del pool, cst, out_S
     torch.cuda.empty_cache()
+
+
+def test_kda_build_full_size():
+    """KDA family at the benchmark's KDA workload and launch (H=16, d=128, bf16, 8 x 2048
+    tokens, diagonal-family gates): sampled (segment, head) records' S against the
+    oracle's build of those tokens, and their T_C on the first 256 tokens of the same
+    stream (a separate build call: over 2048 tokens T_C falls below the fp32 range)."""
+    Hk, nseg, L, seed = 16, 8, 2048, 701
+    N = nseg * L
+    k = synth.keys(N, Hk, D, torch.bfloat16, seed, "cuda")
+    v = synth.values(N, Hk, D, torch.bfloat16, seed + 1, "cuda")
+    b = synth.write_gate(N, Hk, seed + 2, "cuda")
+    la = synth.diagonal_log_gates(N, Hk, D, seed + 3, 16.0, "cuda")
+    offs = synth.even_offsets(nseg, L)
+    pool = hp.Pool.allocate(hp.KDA, nseg, Hk, D, D, device="cuda")
+    hp.build_segment(hp.KDA, k, v, la, torch.as_tensor(offs).cuda(), pool,
+                     torch.arange(nseg, dtype=torch.int32, device="cuda"), beta=b)
+    short = np.array([0, 256], dtype=np.int64)
+    pool_s = hp.Pool.allocate(hp.KDA, 1, Hk, D, D, device="cuda")
+    hp.build_segment(hp.KDA, k, v, la, torch.as_tensor(short).cuda(), pool_s,
+                     torch.zeros(1, dtype=torch.int32, device="cuda"), beta=b)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(seed))
+    worst = 0.0
+    for s, h in zip(rng.integers(0, nseg, 3), rng.integers(0, Hk, 3)):
+        s, h = int(s), int(h)
+        a, e = int(offs[s]), int(offs[s + 1])
+        _, _, S = oracle.build_segments(oracle.KDA, np64(k[a:e, h:h + 1]), np64(v[a:e, h:h + 1]),
+                                        np64(la[a:e, h:h + 1]), [0, e - a], beta=np64(b[a:e, h:h + 1]),
+                                        want_P=False)
+        worst = max(worst, rel_fro(np64(pool.S[s, h]), S[0, 0]))
+    h = int(rng.integers(0, Hk))
+    _, P, _ = oracle.build_segments(oracle.KDA, np64(k[:256, h:h + 1]), np64(v[:256, h:h + 1]),
+                                    np64(la[:256, h:h + 1]), short, beta=np64(b[:256, h:h + 1]))
+    eT = rel_fro(np64(pool_s.P[0, h]), P[0, 0])
+    say(f"[full kda] sampled S err {worst:.2e}, T_C (256 tokens, head {h}) err {eT:.2e}")
+    assert worst <= 2e-2 and eT <= 2e-2
