@@ -158,24 +158,22 @@ def gdn_workload(H=32, dk=128, dv=128, nseg=16, seg_len=2048, seed=301):
                 H=H, dk=dk, dv=dv, nseg=nseg, seg_len=seg_len, N=nseg * seg_len)
 
 
-def gdn_step(w, timer):
+def gdn_step(w):
+    """One step of the hot path: every record of the batch built, then the chain composed."""
     st, pool = w["st"], w["pool"]
-    timer.time("build", lambda: hp.build_segment(hp.GDN, st.k, st.v, st.log_alpha, w["offs"], pool,
-                                                 w["slots"], beta=st.beta, err_flag=w["err"]))
-    timer.time("compose", lambda: hp.compose_chain(pool, w["chain_offs"], w["slots"], out_S=w["out_S"],
-                                                   err_flag=w["err"]))
+    hp.build_segment(hp.GDN, st.k, st.v, st.log_alpha, w["offs"], pool, w["slots"], beta=st.beta,
+                     err_flag=w["err"])
+    hp.compose_chain(pool, w["chain_offs"], w["slots"], out_S=w["out_S"], err_flag=w["err"])
 
 
 def bench_main(args):
     w = gdn_workload()
-    timer = KernelTimer()
     for _ in range(args.warmup):
-        gdn_step(w, timer)
+        gdn_step(w)
     torch.cuda.synchronize()
-    timer.reset()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        gdn_step(w, timer)
+        gdn_step(w)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert int(w["err"].item()) == 0
