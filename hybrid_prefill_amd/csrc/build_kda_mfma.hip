@@ -24,13 +24,23 @@
 // by more than e^-69 within seven tokens) is instead applied token by token to
 // the state, from the same staged keys, gates and values.
 //
-// Workgroup (segment, head, q): q = 0 keeps the T columns, q = 1 the S columns;
-// wave w keeps 32 of them as four 32 x 32 fp32 accumulator tiles.  Per chunk:
-// staging (thread per key channel and token half: prefix of the gates,
-// scaled keys into LDS), Gram blocks (waves 0-2, 16x16x4 fp32 MFMA), inversion
-// (wave 0, lane per column, forward substitution), M and U (every wave, its 32
-// channels of M and its 32 columns of U, 32x32x2 fp32 MFMA), then E and the
-// state update on the wave's own columns.
+// Workgroup (segment, head, q): q = 0 keeps the T columns, q = 1 the S columns.
+// Eight waves in two roles, one chunk apart, with two workgroup barriers per chunk:
+//   state waves 0-3 keep 32 columns each as four 32 x 32 fp32 accumulator tiles;
+//     phase A: W = K_g X_0 - V;
+//              wave 0 then inverts T for this chunk (the Gram came a phase earlier);
+//     phase B: E = -T diag(beta) W and X_C = diag(e^{g_C}) X_0 + Khat^T E;
+//   prep waves 4-7 work on the next chunk;
+//     phase A: staging (thread per key channel and token half: prefix of the
+//              gates, range vote, scaled key tiles into the next LDS buffer);
+//     phase B: Gram blocks (waves 4-6, 16x16x4 fp32 MFMA), then the v tile.
+// The tiles the state side reads in both phases (K_g, Khat^T, e^{g_C}, beta,
+// -T diag(beta)) are double-buffered by chunk parity; the Gram inputs and the v
+// tile (read in phase A, written in phase B) are single.  A chunk voted out of
+// range is applied token by token by the state waves, reading its raw keys and
+// gates from memory (its tiles are computed but unused).  The two roles run
+// loops of their own with the same barriers, so neither role's registers count
+// against the other's (two waves per SIMD leave 256 each).
 #include "hypic_internal.h"
 
 namespace hypic {
@@ -38,8 +48,10 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NT = 256;
+constexpr int NT = 512;                 // waves 0-3 state, 4-7 prep
 constexpr int CK = 32;                  // tokens per chunk
 constexpr int D = 128;
 constexpr int LP = 132;                 // row stride of the [CK][D] tiles (floats)
@@ -48,17 +60,18 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float EXP_LIMIT = 100.0f;     // largest base-2 exponent a scaled key may carry
 
 struct KdaMfmaSmem {
-    float kg[CK][LP];      // k_t e^{g_t}
-    float qd[CK][LP];      // diagonal blocks, query side; then -M.   Serial chunk: raw k
-    float kd[CK][LP];      // diagonal blocks, key side.              Serial chunk: e^{log alpha}
+    float kg[2][CK][LP];   // k_t e^{g_t}
+    float kht[2][D][TP];   // Khat^T
+    float tn[2][CK][TP];   // -T diag(beta) (upper right block zero)
+    float gam[2][D];       // e^{g_C}
+    float b[2][CK];
+    float qd[CK][LP];      // diagonal blocks, query side
+    float kd[CK][LP];      // diagonal blocks, key side
     float x1[CK][LP];      // off-diagonal block: key side (rows 0..15), query side (rows 16..31)
-    float v[CK][LP];       // v of this workgroup's columns (S workgroup)
-    float kht[D][TP];      // Khat^T
+    float v[CK][LP];       // v of this workgroup's columns (written in phase B for the next chunk)
     float nm[CK][TP];      // beta_t A_ts for s < t
-    float tw[4][CK][TP];   // per wave: T (diagonal blocks)
-    float tn[4][CK][TP];   // per wave: -T diag(beta) (upper right block zero)
-    float gam[D];          // e^{g_C}
-    float b[CK];
+    float tw[CK][TP];      // T, diagonal blocks (state wave 0)
+    int32_t vote[2][4];    // per prep wave: a factor of the chunk is out of range
     int64_t t0, n;
     int32_t slot, state;
 };
@@ -72,10 +85,29 @@ __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Four consecutive elements of a row through a buffer resource (the row's base in
+// scalar registers, the constant part of the offset in the instruction): the rare
+// token-by-token path then holds no per-group address registers.
+template <typename XT> __device__ __forceinline__ f32x4 bload4(__amdgpu_buffer_rsrc_t r, int off);
+template <> __device__ __forceinline__ f32x4 bload4<float>(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return f32x4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
+}
+template <> __device__ __forceinline__ f32x4 bload4<uint16_t>(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+                 __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+}
+constexpr int RSRC_WORD3 = 0x00020000;   // 32-bit data format, as for every gfx9 buffer access
+
 template <typename XT>
 __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
     __shared__ KdaMfmaSmem sm;
-    const int th = threadIdx.x, lane = th & 63, w = th >> 6;
+    const int th = threadIdx.x, lane = th & 63;
+    // wave index as a scalar: the role branches below are then scalar branches, so a
+    // wave runs only its own role's loop and barriers
+    const int w = __builtin_amdgcn_readfirstlane(th >> 6);
+    const bool prep_role = w >= 4;
     const int q = blockIdx.x & 1;
     const int head = (blockIdx.x >> 1) % a.H;
     const int seg = (blockIdx.x >> 1) / a.H;
@@ -89,173 +121,196 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
         if (st == 2 && q == 0) raise_flag(a.err_flag, HYPIC_EFLAG_BAD_OFFSETS);
         sm.t0 = o0; sm.n = o1 - o0; sm.slot = slot; sm.state = st;
     }
+    // The upper right block of both -T diag(beta) buffers stays zero.
+    for (int e = th; e < 2 * 16 * 16; e += NT) sm.tn[e >> 8][(e >> 4) & 15][16 + (e & 15)] = 0.0f;
     __syncthreads();
     const int state = sm.state;
     if (state == 1) return;
     const int64_t t0 = sm.t0;
     const int64_t n = state == 2 ? 0 : sm.n;
     const int64_t rec = (int64_t)sm.slot * a.H + head;
+    const int nch = (int)((n + CK - 1) / CK);
     const XT *kp = static_cast<const XT *>(a.k);
     const XT *vp = static_cast<const XT *>(a.v);
     const bool isS = q == 1;
+    const bool has_la = a.log_alpha != nullptr, has_b = a.beta != nullptr;
+    // A missing log alpha or beta is read from the keys with stride 0 and replaced
+    // at use (the loads take no branch: a branch joining around a load makes the
+    // compiler wait for it there).
+    const float *la_base = has_la ? a.log_alpha + head * a.la_sh : static_cast<const float *>(a.k);
+    const int64_t la_st = has_la ? a.la_st : 0;
+    const float *b_base = has_b ? a.beta + head * a.b_sh : static_cast<const float *>(a.k);
+    const int64_t b_st = has_b ? a.b_st : 0;
+    const XT *k_base = kp + head * a.k_sh;
+    const XT *v_base = vp + head * a.v_sh;
+    // token index of chunk c, position t, clamped into the segment (n > 0)
+    auto tok_of = [&](int c, int t) -> int64_t {
+        const int64_t p = (int64_t)c * CK + t;
+        return t0 + (p < n ? p : n - 1);
+    };
 
-    // MFMA role: lane (ln, hh) of wave w keeps column colw, rows 32r + 8(i/4) + 4hh + i%4.
+    // ---- state role: lane (ln, hh) of wave w keeps column colw, rows 32r + 8(i/4) + 4hh + i%4.
     const int ln = lane & 31, hh = lane >> 5;
-    const int colw = 32 * w + ln;
-    f32x16 X[4];
+    const int colw = 32 * (w & 3) + ln;
+    f32x16 X[4], Wt;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             X[r][i] = (!isS && 32 * r + 8 * (i >> 2) + 4 * hh + (i & 3) == colw) ? 1.0f : 0.0f;
 
-    // Staging role: key channel ch (also the value column), tokens 16hf .. 16hf+15.
-    // The next chunk's inputs are fetched into registers while the current one runs.
-    // The loads take no branch (a branch joining around a load makes the compiler
-    // wait for it there): entries past the segment read its last token, a missing
-    // log alpha or beta is read from the keys with stride 0, and the selects that
-    // replace them (zero gates and values, unit or zero beta) are applied at use.
-    const int ch = th & 127, hf = th >> 7;
-    const bool has_la = a.log_alpha != nullptr, has_b = a.beta != nullptr;
-    const float *la_p = has_la ? a.log_alpha + head * a.la_sh + ch : static_cast<const float *>(a.k);
-    const int64_t la_st = has_la ? a.la_st : 0;
-    const float *b_p = has_b ? a.beta + head * a.b_sh : static_cast<const float *>(a.k);
-    const int64_t b_st = has_b ? a.b_st : 0;
-    const XT *k_p = kp + head * a.k_sh + ch;
-    const XT *v_p = vp + head * a.v_sh + ch;
-    float rla[CK], rk[16], rv[16], rb;
-    auto fetch = [&](int64_t c0) {
-        const int cl = n - c0 < CK ? (int)(n - c0) : CK;
-        const int64_t base = t0 + c0;
+    // ---- prep role: key channel ch, tokens 16hf .. 16hf+15 of a chunk.
+    const int pt = th & 255, ch = pt & 127, hf = pt >> 7;
+    float rla[CK], rk[16], rv[16], sv[16], rb;
+    auto fetch = [&](int c) {
 #pragma unroll
-        for (int t = 0; t < CK; ++t) rla[t] = la_p[(base + (t < cl ? t : cl - 1)) * la_st];
+        for (int t = 0; t < CK; ++t) rla[t] = la_base[tok_of(c, t) * la_st + ch];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            const int t = 16 * hf + u;
-            const int64_t tok = base + (t < cl ? t : cl - 1);
-            rk[u] = load_f32(k_p + tok * a.k_st);
-            rv[u] = load_f32(v_p + tok * a.v_st);
+            const int64_t tok = tok_of(c, 16 * hf + u);
+            rk[u] = load_f32(k_base + tok * a.k_st + ch);
+            rv[u] = load_f32(v_base + tok * a.v_st + ch);
         }
-        const int tb_ = th & (CK - 1);
-        rb = b_p[(base + (tb_ < cl ? tb_ : cl - 1)) * b_st];
+        rb = b_base[tok_of(c, pt & (CK - 1)) * b_st];
     };
-    // The upper right block of every wave's -T diag(beta) stays zero.
-    for (int e = th; e < 4 * 16 * 16; e += NT) sm.tn[e >> 8][(e >> 4) & 15][16 + (e & 15)] = 0.0f;
-    if (n > 0) fetch(0);
-
-    for (int64_t c0 = 0; c0 < n; c0 += CK) {
-        const int cl = n - c0 < CK ? (int)(n - c0) : CK;
+    // Staging of chunk c into buffer c & 1 (and the Gram inputs), with the range vote.
+    auto stage = [&](int c) {
+        const int bf = c & 1;
+        const int64_t rem = n - (int64_t)c * CK;
+        const int cl = rem < CK ? (rem > 0 ? (int)rem : 0) : CK;
         float G[CK];
-        {
-            float acc = 0.0f;
+        float acc = 0.0f;
 #pragma unroll
-            for (int t = 0; t < CK; ++t) {
-                acc += (t < cl && has_la ? rla[t] : 0.0f) * LOG2E;
-                G[t] = acc;
-            }
+        for (int t = 0; t < CK; ++t) {
+            acc += (t < cl && has_la ? rla[t] : 0.0f) * LOG2E;
+            G[t] = acc;
         }
         const float Gc = G[CK - 1], Gh = G[15], Gr = hf ? G[23] : G[7];
-        // This thread's half of the prefix (a select per token: indexing G by the
-        // runtime half would compile to a compare-and-select over all 32 registers).
-        float Gs[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) Gs[u] = hf ? G[16 + u] : G[u];
         float emax = -INFINITY;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            const float g = Gs[u];
-            emax = fmaxf(emax, fmaxf(fmaxf(g, Gc - g), fmaxf(g - Gr, Gr - g)));
-            emax = fmaxf(emax, hf ? g - Gh : Gh - g);
+            const int t = 16 * hf + u;
+            // this thread's half of the prefix by a select per token: indexing G by the
+            // runtime half would compile to a compare-and-select over all 32 registers
+            const float g = hf ? G[16 + u] : G[u];
+            const float kk = t < cl ? rk[u] : 0.0f;
+            const float ex = hf ? g - Gh : Gh - g;
+            emax = fmaxf(emax, fmaxf(fmaxf(g, Gc - g), fmaxf(fmaxf(g - Gr, Gr - g), ex)));
+            sm.kg[bf][t][ch] = kk * ex2(g);
+            sm.kht[bf][ch][t] = kk * ex2(Gc - g);
+            sm.qd[t][ch] = kk * ex2(g - Gr);
+            sm.kd[t][ch] = kk * ex2(Gr - g);
+            sm.x1[t][ch] = kk * ex2(ex);
+            sv[u] = t < cl && isS ? rv[u] : 0.0f;   // into the v tile in phase B
         }
-        // Also the barrier after the previous chunk's last reads of the tiles.
-        const bool serial = __syncthreads_or(!(emax <= EXP_LIMIT)) != 0;
-        if (!serial) {
+        if (hf == 0) sm.gam[bf][ch] = ex2(Gc);
+        if (pt < CK) sm.b[bf][pt] = pt < cl ? (has_b ? rb : 1.0f) : 0.0f;
+        const bool out = __ballot(!(emax <= EXP_LIMIT)) != 0;
+        if (lane == 0) sm.vote[bf][w - 4] = out ? 1 : 0;
+    };
+    // Gram blocks of the staged chunk: wave 4 (0,0), wave 5 (1,1), wave 6 (1,0).
+    auto gram = [&]() {
+        const int pw = w - 4;
+        if (pw < 3) {
+            const float(*Qt)[LP] = pw == 2 ? sm.x1 : sm.qd;
+            const float(*Kt)[LP] = pw == 2 ? sm.x1 : sm.kd;
+            const int I = pw == 0 ? 0 : 1, J = pw == 1 ? 1 : 0;
+            const int m = lane & 15, g = lane >> 4;
+            f32x4 c0v = {0.f, 0.f, 0.f, 0.f}, c1v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int t = 16 * hf + u;
-                const float kk = t < cl ? rk[u] : 0.0f, g = Gs[u];
-                sm.kg[t][ch] = kk * ex2(g);
-                sm.kht[ch][t] = kk * ex2(Gc - g);
-                sm.qd[t][ch] = kk * ex2(g - Gr);
-                sm.kd[t][ch] = kk * ex2(Gr - g);
-                sm.x1[t][ch] = kk * ex2(hf ? g - Gh : Gh - g);
-                sm.v[t][ch] = t < cl && isS ? rv[u] : 0.0f;
-            }
-            if (hf == 0) sm.gam[ch] = ex2(Gc);
-        } else {
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int t = 16 * hf + u;
-                sm.qd[t][ch] = t < cl ? rk[u] : 0.0f;
-                const float la_t = hf ? rla[16 + u] : rla[u];
-                sm.kd[t][ch] = t < cl && has_la ? ex2(la_t * LOG2E) : 1.0f;
-                sm.v[t][ch] = t < cl && isS ? rv[u] : 0.0f;
-            }
-        }
-        if (th < CK) sm.b[th] = th < cl ? (has_b ? rb : 1.0f) : 0.0f;
-        fetch(c0 + CK);                     // past the last chunk: the segment's last token again, unused
-        __syncthreads();
-
-        if (!serial) {
-            // Gram blocks: wave 0 (0,0), wave 1 (1,1), wave 2 (1,0); beta_t A_ts below the diagonal.
-            if (w < 3) {
-                const float(*Qt)[LP] = w == 2 ? sm.x1 : sm.qd;
-                const float(*Kt)[LP] = w == 2 ? sm.x1 : sm.kd;
-                const int I = w == 0 ? 0 : 1, J = w == 1 ? 1 : 0;
-                const int m = lane & 15, g = lane >> 4;
-                f32x4 c0v = {0.f, 0.f, 0.f, 0.f}, c1v = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {      // contraction index 16s + 4g + j
-                    const f32x4 qa = *reinterpret_cast<const f32x4 *>(&Qt[16 * I + m][16 * s + 4 * g]);
-                    const f32x4 kb = *reinterpret_cast<const f32x4 *>(&Kt[16 * J + m][16 * s + 4 * g]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        if (s & 1) c1v = mfma16(qa[j], kb[j], c1v);
-                        else c0v = mfma16(qa[j], kb[j], c0v);
-                    }
-                }
-                const f32x4 Ab = c0v + c1v;          // rows 16I + 4g + j, column 16J + m
+            for (int s = 0; s < 8; ++s) {       // contraction index 16s + 4g + j
+                const f32x4 qa = *reinterpret_cast<const f32x4 *>(&Qt[16 * I + m][16 * s + 4 * g]);
+                const f32x4 kb = *reinterpret_cast<const f32x4 *>(&Kt[16 * J + m][16 * s + 4 * g]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int t = 16 * I + 4 * g + j, s = 16 * J + m;
-                    sm.nm[t][s] = t > s ? sm.b[t] * Ab[j] : 0.0f;
+                    if (s & 1) c1v = mfma16(qa[j], kb[j], c1v);
+                    else c0v = mfma16(qa[j], kb[j], c0v);
                 }
             }
+            return c0v + c1v;                   // rows 16I + 4g + j, column 16J + m
+        }
+        return f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto gram_store = [&](int c, f32x4 Ab) {
+        const int pw = w - 4;
+        if (pw < 3) {
+            const int I = pw == 0 ? 0 : 1, J = pw == 1 ? 1 : 0;
+            const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 16 * I + 4 * g + j, s = 16 * J + m;
+                sm.nm[t][s] = t > s ? sm.b[c & 1][t] * Ab[j] : 0.0f;
+            }
+        }
+    };
+
+    auto store_v = [&]() {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) sm.v[16 * hf + u][ch] = sv[u];
+    };
+
+    // Prologue: chunk 0 staged and its Gram formed; chunk 1's inputs in flight.
+    if (nch > 0) {
+        if (prep_role) {
+            fetch(0);
+            stage(0);
+            fetch(1);
+        }
+    }
+    __syncthreads();
+    if (nch > 0 && prep_role) {
+        gram_store(0, gram());
+        store_v();
+    }
+    __syncthreads();
+
+    // Two loops, one per role, with the same two workgroup barriers per chunk.
+    if (prep_role) {
+        for (int c = 0; c < nch; ++c) {
+            stage(c + 1);                   // phase A
+            fetch(c + 2);
             __syncthreads();
-            // Every wave now works alone until the next chunk (no barrier):
-            // (1) W = K_g X_0 - V on its columns (contraction over state rows), which
-            //     does not need T, so the scheduler can overlap it with
-            // (2) its own copy of T = (I + N)^{-1} (N = diag(beta) A, strictly lower):
-            //     the two diagonal 16 x 16 blocks by forward substitution (lane per
-            //     column: lanes 0-15 the first block, 16-31 the second, the upper half
-            //     of the wave repeating them), then T_10 = -T_11 (N_10 T_00) on the
-            //     16x16x4 MFMA; -T diag(beta) goes to the wave's own LDS tile;
-            // (3) E = -T diag(beta) W = T diag(beta) (V - K_g X_0);
-            // (4) X_C = diag(e^{g_C}) X_0 + Khat^T E.
+            gram_store(c + 1, gram());      // phase B
+            store_v();
+            __syncthreads();
+        }
+        return;
+    }
+    for (int c = 0; c < nch; ++c) {
+        const int bf = c & 1;
+        const int64_t rem = n - (int64_t)c * CK;
+        const int cl = rem < CK ? (int)rem : CK;
+        const bool serial = (sm.vote[bf][0] | sm.vote[bf][1] | sm.vote[bf][2] | sm.vote[bf][3]) != 0;
+        // ---------------- phase A
+        if (!serial) {
+            // W = K_g X_0 - V on the wave's columns (contraction over state rows)
             f32x16 W0, W1;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                W0[i] = isS ? -sm.v[8 * (i >> 2) + 4 * hh + (i & 3)][colw] : 0.0f;
+                const int t = 8 * (i >> 2) + 4 * hh + (i & 3);
+                W0[i] = isS && t < cl ? -sm.v[t][colw] : 0.0f;
                 W1[i] = 0.0f;
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const f32x4 kv = *reinterpret_cast<const f32x4 *>(&sm.kg[ln][32 * r + 8 * s + 4 * hh]);
+                    const f32x4 kv = *reinterpret_cast<const f32x4 *>(&sm.kg[bf][ln][32 * r + 8 * s + 4 * hh]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         if (r & 1) W1 = mfma32(kv[j], X[r][4 * s + j], W1);
                         else W0 = mfma32(kv[j], X[r][4 * s + j], W0);
                     }
                 }
-            float(*tw)[TP] = sm.tw[w];
-            float(*tn)[TP] = sm.tn[w];
-            {
-                const int c = lane & 15, blk = (lane >> 4) & 1, o = 16 * blk;
+            Wt = W0 + W1;
+            if (w == 0) {
+                // T = (I + N)^{-1}: the two diagonal 16 x 16 blocks by forward
+                // substitution (lane per column; the upper half of the wave repeats
+                // the lower), T_10 = -T_11 (N_10 T_00) on the 16x16x4 MFMA.
+                const int cc = lane & 15, blk = (lane >> 4) & 1, o = 16 * blk;
                 float tc[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) tc[i] = i == c ? 1.0f : 0.0f;
+                for (int i = 0; i < 16; ++i) tc[i] = i == cc ? 1.0f : 0.0f;
 #pragma unroll
                 for (int i = 1; i < 16; ++i) {
                     float s0 = 0.0f, s1 = 0.0f;
@@ -267,85 +322,98 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
                         if (m4 + 2 < i) s0 += nv[2] * tc[m4 + 2];
                         if (m4 + 3 < i) s1 += nv[3] * tc[m4 + 3];
                     }
-                    if (i > c) tc[i] = -(s0 + s1);
+                    if (i > cc) tc[i] = -(s0 + s1);
                 }
-                const float bc = sm.b[o + c];
+                const float bc = sm.b[bf][o + cc];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    tw[o + i][o + c] = tc[i];
-                    tn[o + i][o + c] = -tc[i] * bc;
+                    sm.tw[o + i][o + cc] = tc[i];
+                    sm.tn[bf][o + i][o + cc] = -tc[i] * bc;
                 }
-            }
-            {
-                // Y = N_10 T_00, then T_11 Y = -T_10 (contraction index 4g + j at step j).
                 const int m = lane & 15, g = lane >> 4;
                 const f32x4 na = *reinterpret_cast<const f32x4 *>(&sm.nm[16 + m][4 * g]);
                 f32x4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) Y = mfma16(na[j], tw[4 * g + j][m], Y);
-                const f32x4 ta = *reinterpret_cast<const f32x4 *>(&tw[16 + m][16 + 4 * g]);
+                for (int j = 0; j < 4; ++j) Y = mfma16(na[j], sm.tw[4 * g + j][m], Y);
+                const f32x4 ta = *reinterpret_cast<const f32x4 *>(&sm.tw[16 + m][16 + 4 * g]);
                 f32x4 Z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) Z = mfma16(ta[j], Y[j], Z);
-                const float bm = sm.b[m];
+                const float bm = sm.b[bf][m];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) tn[16 + 4 * g + j][m] = Z[j] * bm;
-            }
-            const f32x16 Wt = W0 + W1;             // rows: the chunk's tokens 8(i/4) + 4hh + i%4
-            f32x16 E;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) E[i] = 0.0f;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const f32x4 ta = *reinterpret_cast<const f32x4 *>(&tn[ln][8 * s + 4 * hh]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) E = mfma32(ta[j], Wt[4 * s + j], E);
-            }
-            // X_C = diag(e^{g_C}) X_0 + Khat^T E.
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const f32x4 gg = *reinterpret_cast<const f32x4 *>(&sm.gam[32 * r + 8 * s + 4 * hh]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) X[r][4 * s + j] *= gg[j];
-                }
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const f32x4 kh = *reinterpret_cast<const f32x4 *>(&sm.kht[32 * r + ln][8 * s + 4 * hh]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) X[r] = mfma32(kh[j], E[4 * s + j], X[r]);
-                }
+                for (int j = 0; j < 4; ++j) sm.tn[bf][16 + 4 * g + j][m] = Z[j] * bm;
             }
         } else {
-            // Token by token on the state: the lane pair (ln, 0), (ln, 1) holds the column.
+            // Token by token, from memory: the lane pair (ln, 0), (ln, 1) holds the column.
+            const int vk = 4 * hh * (int)sizeof(XT), vl = 16 * hh;
+#pragma unroll 1
             for (int t = 0; t < cl; ++t) {
+                const int64_t tok = t0 + (int64_t)c * CK + t;
+                const __amdgpu_buffer_rsrc_t rk_ = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(k_base + tok * a.k_st), (short)0, D * (int)sizeof(XT), RSRC_WORD3);
+                // a missing log alpha reads as zero (no records)
+                const __amdgpu_buffer_rsrc_t rl_ = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(la_base + tok * la_st), (short)0, has_la ? D * 4 : 0, RSRC_WORD3);
                 float u = 0.0f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
-                        const int row = 32 * r + 8 * s + 4 * hh;
-                        const f32x4 al = *reinterpret_cast<const f32x4 *>(&sm.kd[t][row]);
-                        const f32x4 kk = *reinterpret_cast<const f32x4 *>(&sm.qd[t][row]);
+                        const f32x4 kk = bload4<XT>(rk_, vk + (32 * r + 8 * s) * (int)sizeof(XT));
+                        const f32x4 lv = bload4<float>(rl_, vl + (32 * r + 8 * s) * 4);
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            X[r][4 * s + j] *= al[j];
+                            X[r][4 * s + j] *= ex2(lv[j] * LOG2E);
                             u += kk[j] * X[r][4 * s + j];
                         }
+                        // one group's loads at a time (hoisting them all beside the
+                        // state would overflow the register file)
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 u += __shfl_xor(u, 32);
-                const float cf = sm.b[t] * ((isS ? sm.v[t][colw] : 0.0f) - u);
+                const float bt = has_b ? a.beta[tok * a.b_st + head * a.b_sh] : 1.0f;
+                const float vt = sm.v[t][colw];
+                const float cf = bt * (vt - u);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
-                        const f32x4 kk = *reinterpret_cast<const f32x4 *>(&sm.qd[t][32 * r + 8 * s + 4 * hh]);
+                        const f32x4 kk = bload4<XT>(rk_, vk + (32 * r + 8 * s) * (int)sizeof(XT));
 #pragma unroll
                         for (int j = 0; j < 4; ++j) X[r][4 * s + j] += kk[j] * cf;
+                        __builtin_amdgcn_sched_barrier(0);
                     }
             }
         }
+        __syncthreads();
+        // ---------------- phase B
+        if (!serial) {
+            f32x16 E;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) E[i] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const f32x4 ta = *reinterpret_cast<const f32x4 *>(&sm.tn[bf][ln][8 * s + 4 * hh]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) E = mfma32(ta[j], Wt[4 * s + j], E);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const f32x4 gg = *reinterpret_cast<const f32x4 *>(&sm.gam[bf][32 * r + 8 * s + 4 * hh]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) X[r][4 * s + j] *= gg[j];
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const f32x4 kh = *reinterpret_cast<const f32x4 *>(&sm.kht[bf][32 * r + ln][8 * s + 4 * hh]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) X[r] = mfma32(kh[j], E[4 * s + j], X[r]);
+                }
+            }
+        }
+        __syncthreads();
     }
 
     const float nanv = __int_as_float(0x7fc00000);
