@@ -102,7 +102,7 @@ typedef struct hypic_pool {
  *   token t, head h:  k[t*k_stride_t + h*k_stride_h + i]   i < d_k   (kv_dtype)
  *                     v[t*v_stride_t + h*v_stride_h + j]   j < d_v   (kv_dtype)
  *                     beta[t*beta_stride_t + h*beta_stride_h]        (fp32; NULL means beta = 1)
- *                     log_alpha[t*la_stride_t + h*la_stride_h (+ i for HYPIC_DIAGONAL)]
+ *                     log_alpha[t*la_stride_t + h*la_stride_h (+ i for HYPIC_DIAGONAL, HYPIC_KDA)]
  *                                                          (fp32, log of the decay; NULL means 0)
  *   la_stride_t = 0 gives a per-head constant decay (RetNet).
  *   Segment s is tokens [seg_offsets[s], seg_offsets[s+1]) (device int64,
@@ -134,6 +134,11 @@ typedef struct hypic_segments {
  * HYPIC_EFLAG_SLOT_OUT_OF_RANGE and writes nothing for that segment; bad
  * offsets set HYPIC_EFLAG_BAD_OFFSETS and fill the segment's record with NaN.
  * NaN or Inf inputs propagate into the affected record.
+ *
+ * HYPIC_KDA at d_k = d_v = 128 runs in 32-token chunks on the fp32 matrix
+ * cores; a chunk in which some channel's gate product over seven tokens falls
+ * below about e^-69 is applied token by token instead (same result, slower).
+ * Other KDA shapes run token by token throughout.
  */
 hypic_status hypic_build_segment(const hypic_segments *in, const hypic_pool *pool,
                                  const int32_t *dst_slots, uint32_t *err_flag, void *stream);
