@@ -186,6 +186,11 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
             G[t] = acc;
         }
         const float Gc = G[CK - 1], Gh = G[15], Gr = hf ? G[23] : G[7];
+        // Two exponentials per element: the query- and key-side factors of the
+        // diagonal block, 2^{g-Gr} and 2^{Gr-g}, which the vote keeps inside
+        // [2^-100, 2^100]; the other tiles are these times per-thread constants
+        // (a constant that underflows only loses terms below 2^-26 |k|).
+        const float cg = ex2(Gr), cc = ex2(Gc - Gr), ch_ = ex2(hf ? Gr - Gh : Gh - Gr);
         float emax = -INFINITY;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
@@ -196,11 +201,12 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
             const float kk = t < cl ? rk[u] : 0.0f;
             const float ex = hf ? g - Gh : Gh - g;
             emax = fmaxf(emax, fmaxf(fmaxf(g, Gc - g), fmaxf(fmaxf(g - Gr, Gr - g), ex)));
-            sm.kg[bf][t][ch] = kk * ex2(g);
-            sm.kht[bf][ch][t] = kk * ex2(Gc - g);
-            sm.qd[t][ch] = kk * ex2(g - Gr);
-            sm.kd[t][ch] = kk * ex2(Gr - g);
-            sm.x1[t][ch] = kk * ex2(ex);
+            const float qv = kk * ex2(g - Gr), kv = kk * ex2(Gr - g);
+            sm.kg[bf][t][ch] = qv * cg;                 // k 2^{g}
+            sm.kht[bf][ch][t] = kv * cc;                // k 2^{Gc-g}
+            sm.qd[t][ch] = qv;
+            sm.kd[t][ch] = kv;
+            sm.x1[t][ch] = (hf ? qv : kv) * ch_;        // k 2^{g-Gh} (second half), k 2^{Gh-g} (first)
             sv[u] = t < cl && isS ? rv[u] : 0.0f;   // into the v tile in phase B
         }
         if (hf == 0) sm.gam[bf][ch] = ex2(Gc);
