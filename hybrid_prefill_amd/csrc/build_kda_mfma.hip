@@ -159,12 +159,13 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
         for (int i = 0; i < 16; ++i)
             X[r][i] = (!isS && 32 * r + 8 * (i >> 2) + 4 * hh + (i & 3) == colw) ? 1.0f : 0.0f;
 
-    // ---- prep role: key channel ch, tokens 16hf .. 16hf+15 of a chunk.
-    const int pt = th & 255, ch = pt & 127, hf = pt >> 7;
-    float rla[CK], rk[16], rv[16], sv[16], rb;
+    // ---- prep role: key channel ch, tokens 16hf .. 16hf+15 of a chunk; the two halves
+    // of a channel sit in lanes l and l + 32 of one wave.
+    const int pt = th & 255, ch = 32 * (pt >> 6) + (pt & 31), hf = (pt >> 5) & 1;
+    float rla[16], rk[16], rv[16], sv[16], rb;
     auto fetch = [&](int c) {
 #pragma unroll
-        for (int t = 0; t < CK; ++t) rla[t] = la_base[tok_of(c, t) * la_st + ch];
+        for (int u = 0; u < 16; ++u) rla[u] = la_base[tok_of(c, 16 * hf + u) * la_st + ch];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int64_t tok = tok_of(c, 16 * hf + u);
@@ -178,14 +179,17 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
         const int bf = c & 1;
         const int64_t rem = n - (int64_t)c * CK;
         const int cl = rem < CK ? (rem > 0 ? (int)rem : 0) : CK;
-        float G[CK];
+        // prefix over this half, then the halves' totals swapped across the wave
+        float L[16];
         float acc = 0.0f;
 #pragma unroll
-        for (int t = 0; t < CK; ++t) {
-            acc += (t < cl && has_la ? rla[t] : 0.0f) * LOG2E;
-            G[t] = acc;
+        for (int u = 0; u < 16; ++u) {
+            acc += (16 * hf + u < cl && has_la ? rla[u] : 0.0f) * LOG2E;
+            L[u] = acc;
         }
-        const float Gc = G[CK - 1], Gh = G[15], Gr = hf ? G[23] : G[7];
+        const float other = __shfl_xor(acc, 32);
+        const float off = hf ? other : 0.0f;    // the first half's total, for the second
+        const float Gc = acc + other, Gh = hf ? other : acc, Gr = off + L[7];
         // Two exponentials per element: the query- and key-side factors of the
         // diagonal block, 2^{g-Gr} and 2^{Gr-g}, which the vote keeps inside
         // [2^-100, 2^100]; the other tiles are these times per-thread constants
@@ -195,9 +199,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int t = 16 * hf + u;
-            // this thread's half of the prefix by a select per token: indexing G by the
-            // runtime half would compile to a compare-and-select over all 32 registers
-            const float g = hf ? G[16 + u] : G[u];
+            const float g = off + L[u];
             const float kk = t < cl ? rk[u] : 0.0f;
             const float ex = hf ? g - Gh : Gh - g;
             emax = fmaxf(emax, fmaxf(fmaxf(g, Gc - g), fmaxf(fmaxf(g - Gr, Gr - g), ex)));
