@@ -153,6 +153,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
     const int ln = lane & 31, hh = lane >> 5;
     const int colw = 32 * (w & 3) + ln;
     f32x16 X[4], Wt;
+    f32x4 na10 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -338,19 +339,9 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
                     sm.tw[o + i][o + cc] = tc[i];
                     sm.tn[bf][o + i][o + cc] = -tc[i] * bc;
                 }
-                const int m = lane & 15, g = lane >> 4;
-                const f32x4 na = *reinterpret_cast<const f32x4 *>(&sm.nm[16 + m][4 * g]);
-                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Y = mfma16(na[j], sm.tw[4 * g + j][m], Y);
-                const f32x4 ta = *reinterpret_cast<const f32x4 *>(&sm.tw[16 + m][16 + 4 * g]);
-                f32x4 Z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Z = mfma16(ta[j], Y[j], Z);
-                const float bm = sm.b[bf][m];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sm.tn[bf][16 + 4 * g + j][m] = Z[j] * bm;
             }
+            // N_10 for the merge in phase B (the prep waves rewrite nm meanwhile)
+            na10 = *reinterpret_cast<const f32x4 *>(&sm.nm[16 + (lane & 15)][4 * (lane >> 4)]);
         } else {
             // Token by token, from memory: the lane pair (ln, 0), (ln, 1) holds the column.
             const int vk = 4 * hh * (int)sizeof(XT), vl = 16 * hh;
@@ -396,6 +387,22 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
         __syncthreads();
         // ---------------- phase B
         if (!serial) {
+            {
+                // T_10 = -T_11 (N_10 T_00), every wave on its own (identical values into
+                // the shared tile, each wave reading back its own writes): Y = N_10 T_00,
+                // then T_11 Y = -T_10 (contraction index 4g + j at step j).
+                const int m = lane & 15, g = lane >> 4;
+                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Y = mfma16(na10[j], sm.tw[4 * g + j][m], Y);
+                const f32x4 ta = *reinterpret_cast<const f32x4 *>(&sm.tw[16 + m][16 + 4 * g]);
+                f32x4 Z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Z = mfma16(ta[j], Y[j], Z);
+                const float bm = sm.b[bf][m];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sm.tn[bf][16 + 4 * g + j][m] = Z[j] * bm;
+            }
             f32x16 E;
 #pragma unroll
             for (int i = 0; i < 16; ++i) E[i] = 0.0f;
