@@ -163,10 +163,11 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
     // ---- prep role: key channel ch, tokens 16hf .. 16hf+15 of a chunk; the two halves
     // of a channel sit in lanes l and l + 32 of one wave.
     const int pt = th & 255, ch = 32 * (pt >> 6) + (pt & 31), hf = (pt >> 5) & 1;
+    const int lch = has_la ? ch : 0;        // a missing log alpha reads the keys' first element
     float rla[16], rk[16], rv[16], sv[16], rb;
     auto fetch = [&](int c) {
 #pragma unroll
-        for (int u = 0; u < 16; ++u) rla[u] = la_base[tok_of(c, 16 * hf + u) * la_st + ch];
+        for (int u = 0; u < 16; ++u) rla[u] = la_base[tok_of(c, 16 * hf + u) * la_st + lch];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int64_t tok = tok_of(c, 16 * hf + u);

@@ -123,3 +123,29 @@ def test_kda_strong_gates(dtype, tol):
     eC = max(rel_fro(np64(out[0, h]), S_seq[0, h]) for h in range(H))
     say(f"[kda strong gates] {dtype}: T_C err {eT:.2e}, S err {eS:.2e}, composed vs sequential {eC:.2e}")
     assert eT <= tol and eS <= tol and eC <= tol
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_kda_without_gates_or_beta(d):
+    """log alpha and beta left out (NULL: no decay, beta = 1), bf16, one head, segments
+    of 1, 40 and 33 tokens: the ungated delta rule, against the oracle with zero gates
+    and unit beta."""
+    H = 1
+    lens = [1, 40, 33]
+    offs = synth.offsets_from_lengths(lens)
+    N = int(offs[-1])
+    k = synth.keys(N, H, d, torch.bfloat16, 1830 + d, "cuda")
+    v = synth.values(N, H, d, torch.bfloat16, 1831 + d, "cuda")
+    nseg = len(lens)
+    pool = hp.Pool.allocate(hp.KDA, nseg, H, d, d, device="cuda", fill=55.0)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hp.build_segment(hp.KDA, k, v, None, torch.as_tensor(offs).cuda(), pool,
+                     torch.arange(nseg, dtype=torch.int32, device="cuda"), err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    kn, vn = np64(k), np64(v)
+    _, P, S = oracle.build_segments(oracle.KDA, kn, vn, np.zeros((N, H, d)), offs)
+    eT = max(rel_fro(np64(pool.P[s, 0]), P[s, 0]) for s in range(nseg))
+    eS = max(rel_fro(np64(pool.S[s, 0]), S[s, 0]) for s in range(nseg))
+    say(f"[kda no gates] d={d}: T_C err {eT:.2e}, S err {eS:.2e}")
+    assert eT <= 2e-2 and eS <= 2e-2
