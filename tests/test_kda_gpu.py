@@ -149,3 +149,28 @@ def test_kda_without_gates_or_beta(d):
     eS = max(rel_fro(np64(pool.S[s, 0]), S[s, 0]) for s in range(nseg))
     say(f"[kda no gates] d={d}: T_C err {eT:.2e}, S err {eS:.2e}")
     assert eT <= 2e-2 and eS <= 2e-2
+
+
+def test_kda_error_paths():
+    """d = 128 (chunk kernel): a slot out of range raises its flag and leaves the pool
+    untouched, decreasing offsets raise theirs and fill that record with NaN, and the
+    valid segments of the same call still match the oracle."""
+    H, d = 2, 128
+    lens = [70, 40, 33]
+    offs, k, v, b, la = _inputs(lens, H, d, d, torch.bfloat16, 1860, 16.0)
+    bad_offs = offs.copy()
+    bad_offs[2] = bad_offs[1] - 5                 # segment 1 ends before it starts
+    pool = hp.Pool.allocate(hp.KDA, 4, H, d, d, device="cuda", fill=9.0)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    slots = torch.tensor([0, 1, 7], dtype=torch.int32, device="cuda")   # 7: out of range
+    hp.build_segment(hp.KDA, k, v, la, torch.as_tensor(bad_offs).cuda(), pool, slots, beta=b, err_flag=err)
+    torch.cuda.synchronize()
+    flags = int(err.item())
+    assert flags & hp.EFLAG_SLOT_OUT_OF_RANGE and flags & hp.EFLAG_BAD_OFFSETS
+    assert torch.isnan(pool.S[1]).all() and torch.isnan(pool.P[1]).all()
+    assert torch.all(pool.S[2:] == 9.0) and torch.all(pool.P[2:] == 9.0)
+    kn, vn, bn, lan = np64(k), np64(v), np64(b), np64(la)
+    _, P, S = oracle.build_segments(oracle.KDA, kn, vn, lan, offs[:2], beta=bn)
+    e = max(max(rel_fro(np64(pool.P[0, h]), P[0, h]), rel_fro(np64(pool.S[0, h]), S[0, h])) for h in range(H))
+    say(f"[kda errors] flags {flags:#x}, valid segment err {e:.2e}")
+    assert e <= 2e-2
