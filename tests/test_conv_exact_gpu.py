@@ -204,3 +204,44 @@ def test_conv_kv_against_oracle(dims, dtype):
     ek, ev = rel_fro(np64(k), kr), rel_fro(np64(v), vr)
     say(f"[conv_kv] H={H} dk={dk} dv={dv} C={C} {dtype}: k err {ek:.2e}, v err {ev:.2e}")
     assert ek <= 1e-5 and ev <= 1e-5
+
+
+def test_compose_chain_heads_strong_gates():
+    """hypic_compose_chain_heads with some head tokens gated by e^-50 and e^-80 (decays
+    far below the others, so an entry's head tokens all but reset the state), against
+    the oracle as above."""
+    H, d, nslots, R = 2, 128, 16, 12
+    rng = np.random.default_rng(1580)
+    q, _ = np.linalg.qr(rng.standard_normal((nslots, H, d, d)))
+    pool = hp.Pool.allocate(hp.GDN, nslots, H, d, d, device="cuda", fill=0.0)
+    pool.P.copy_(torch.from_numpy(q * rng.uniform(0.9, 1.0, size=(nslots, H, 1, d))).float())
+    pool.S.copy_(torch.from_numpy(rng.standard_normal((nslots, H, d, d))).float())
+    pool.log_scale.copy_(torch.from_numpy(rng.uniform(-0.05, 0.0, size=(nslots, H))).float())
+    lens = [int(x) for x in rng.integers(1, 12, size=R)]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    flat = rng.integers(0, nslots, size=int(offs[-1])).astype(np.int32)
+    nh = rng.integers(0, 9, size=len(flat))
+    hoffs = np.concatenate([[0], np.cumsum(nh)]).astype(np.int64)
+    T = int(hoffs[-1])
+    hk = synth.keys(T, H, d, torch.float32, 1581, "cuda")
+    hv = synth.values(T, H, d, torch.float32, 1582, "cuda")
+    hb = synth.write_gate(T, H, 1583, "cuda")
+    hla = synth.gdn_log_decay(T, H, 1584, 0.1, "cuda")
+    hla[::7] = -50.0
+    hla[3::11] = -80.0
+    out = hp.compose_chain_heads(pool, torch.as_tensor(offs).cuda(), torch.as_tensor(flat).cuda(),
+                                 torch.as_tensor(hoffs).cuda(), hk, hv, hb, hla)
+    torch.cuda.synchronize()
+    k_, v_, b_, la_ = np64(hk), np64(hv), np64(hb), np64(hla)
+    hell, hP, hS = oracle.build_segments(oracle.GDN, k_, v_, la_, hoffs, beta=b_)
+    E = len(flat)
+    mp_ell = np.concatenate([hell, np64(pool.log_scale)[flat]])
+    mp_P = np.concatenate([hP, np64(pool.P)[flat]])
+    mp_S = np.concatenate([hS, np64(pool.S)[flat]])
+    chain = np.empty(2 * E, dtype=np.int32)
+    chain[0::2] = np.arange(E)
+    chain[1::2] = E + np.arange(E)
+    rS, _, _ = oracle.compose(oracle.GDN, mp_ell, mp_P, mp_S, 2 * offs, chain)
+    worst = max(rel_fro(np64(out[r, h]), rS[r, h]) for r in range(R) for h in range(H))
+    say(f"[compose heads strong gates] head tokens {T}: S err {worst:.2e}")
+    assert worst <= 1e-4
