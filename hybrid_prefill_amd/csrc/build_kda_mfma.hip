@@ -99,6 +99,13 @@ template <> __device__ __forceinline__ f32x4 bload4<uint16_t>(__amdgpu_buffer_rs
                  __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
 }
 constexpr int RSRC_WORD3 = 0x00020000;   // 32-bit data format, as for every gfx9 buffer access
+template <typename XT> __device__ __forceinline__ float bload1(__amdgpu_buffer_rsrc_t r, int off);
+template <> __device__ __forceinline__ float bload1<float>(__amdgpu_buffer_rsrc_t r, int off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+template <> __device__ __forceinline__ float bload1<uint16_t>(__amdgpu_buffer_rsrc_t r, int off) {
+    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0) << 16);
+}
 
 template <typename XT>
 __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
@@ -163,16 +170,30 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_mfma_kernel(BuildArgs a) {
     // ---- prep role: key channel ch, tokens 16hf .. 16hf+15 of a chunk; the two halves
     // of a channel sit in lanes l and l + 32 of one wave.
     const int pt = th & 255, ch = 32 * (pt >> 6) + (pt & 31), hf = (pt >> 5) & 1;
-    const int lch = has_la ? ch : 0;        // a missing log alpha reads the keys' first element
     float rla[16], rk[16], rv[16], sv[16], rb;
+    // The chunk's rows through buffer resources: the chunk's base in scalar registers,
+    // one lane offset, and bounds that end at the segment's last row (rows past it
+    // read as zero and are masked at use), so no per-lane 64-bit address arithmetic.
     auto fetch = [&](int c) {
-#pragma unroll
-        for (int u = 0; u < 16; ++u) rla[u] = la_base[tok_of(c, 16 * hf + u) * la_st + lch];
+        const int64_t row0 = t0 + (int64_t)c * CK, rem = n - (int64_t)c * CK;
+        const int rows = rem > 0 ? (rem < CK ? (int)rem : CK) : 0;
+        const __amdgpu_buffer_rsrc_t rl_ = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(la_base + row0 * la_st), (short)0,
+            has_la && rows > 0 ? (int)(((int64_t)(rows - 1) * la_st + D) * 4) : 0, RSRC_WORD3);
+        const __amdgpu_buffer_rsrc_t rk_ = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(k_base + row0 * a.k_st), (short)0,
+            rows > 0 ? (int)(((int64_t)(rows - 1) * a.k_st + D) * (int)sizeof(XT)) : 0, RSRC_WORD3);
+        const __amdgpu_buffer_rsrc_t rv_ = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(v_base + row0 * a.v_st), (short)0,
+            rows > 0 ? (int)(((int64_t)(rows - 1) * a.v_st + D) * (int)sizeof(XT)) : 0, RSRC_WORD3);
+        const int ol = (16 * hf * (int)la_st + ch) * 4;
+        const int ok = (16 * hf * (int)a.k_st + ch) * (int)sizeof(XT);
+        const int ov = (16 * hf * (int)a.v_st + ch) * (int)sizeof(XT);
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            const int64_t tok = tok_of(c, 16 * hf + u);
-            rk[u] = load_f32(k_base + tok * a.k_st + ch);
-            rv[u] = load_f32(v_base + tok * a.v_st + ch);
+            rla[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl_, ol + u * (int)la_st * 4, 0, 0));
+            rk[u] = bload1<XT>(rk_, ok + u * (int)a.k_st * (int)sizeof(XT));
+            rv[u] = bload1<XT>(rv_, ov + u * (int)a.v_st * (int)sizeof(XT));
         }
         rb = b_base[tok_of(c, pt & (CK - 1)) * b_st];
     };
