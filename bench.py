@@ -14,8 +14,8 @@ Secondary lines (same JSON object, key "secondary"):
                  cold builds + conv warm-up (4096 channels, kernel 4) + all chains
   conv exact     conv-coupled exact reuse: 32 requests of 24-96 cached segments,
                  warmed head keys/values applied inside the compose
-  kda            KDA family build (token-serial fp32) and 8-segment chain, H=16,
-                 d=128, bf16, 8 x 2048 tokens
+  kda            KDA family build (chunked, on the fp32 matrix cores) and its
+                 8-segment chain, H=16, d=128, bf16, 8 x 2048 tokens
 
 Inputs are resident in HBM before the timed region starts.  Kernel durations
 come from HIP events recorded on the stream the kernels are launched on.

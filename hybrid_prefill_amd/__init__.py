@@ -123,6 +123,20 @@ def _device_check(*ts):
             raise HypicError("every tensor must be on the GPU")
 
 
+def _shape(name: str, t: Optional[torch.Tensor], want) -> None:
+    """The C ABI receives no sizes for most tensors, so a tensor of the wrong shape would
+    become an out-of-bounds device access: every shape is checked here, before the call."""
+    if t is not None and tuple(t.shape) != tuple(want):
+        raise HypicError(f"{name} has shape {tuple(t.shape)}, expected {tuple(want)}")
+
+
+def _flag(err_flag: Optional[torch.Tensor]) -> None:
+    """The error word is one 32-bit device word the kernels OR into."""
+    if err_flag is not None and (err_flag.dtype != torch.int32 or err_flag.numel() < 1
+                                 or not err_flag.is_contiguous()):
+        raise HypicError("err_flag must be a contiguous int32 tensor with at least one element")
+
+
 @dataclass
 class Pool:
     """Caller-owned segment pool: per (slot, head) record (log_scale, P, S), fp32."""
@@ -147,10 +161,23 @@ class Pool:
         P = mk((num_slots, num_heads, d_k, d_k)) if family in (GDN, KDA) else None
         return Pool(family, num_heads, d_k, d_v, mk(ls_shape), mk((num_slots, num_heads, d_k, d_v)), P)
 
-    def _c(self) -> _Pool:
+    def _validate(self) -> None:
+        """dtype, layout and full shape of every pool tensor (no device access)."""
         for t in (self.log_scale, self.S, self.P):
             if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
                 raise HypicError("pool tensors must be contiguous fp32")
+        n, H, dk, dv = self.S.shape[0], self.num_heads, self.d_k, self.d_v
+        _shape("pool.S", self.S, (n, H, dk, dv))
+        _shape("pool.log_scale", self.log_scale, (n, H, dk) if self.family == DIAGONAL else (n, H))
+        if self.family in (GDN, KDA):
+            if self.P is None:
+                raise HypicError("a GDN / KDA pool needs P")
+            _shape("pool.P", self.P, (n, H, dk, dk))
+        elif self.P is not None:
+            raise HypicError("only GDN / KDA pools hold P")
+
+    def _c(self) -> _Pool:
+        self._validate()
         _device_check(self.log_scale, self.S, self.P)
         return _Pool(self.family, self.num_heads, self.d_k, self.d_v, self.num_slots,
                      _ptr(self.log_scale), _ptr(self.P), _ptr(self.S))
@@ -167,7 +194,6 @@ def build_segment(family: int, k: torch.Tensor, v: torch.Tensor, log_alpha: Opti
     (diagonal), fp32, or None (no decay); beta [N,H] fp32 or None (= 1);
     seg_offsets device int64 [S+1]; dst_slots device int32 [S].
     """
-    _device_check(k, v, log_alpha, seg_offsets, dst_slots, beta, err_flag)
     if k.dtype != v.dtype:
         raise HypicError("k and v must share a dtype")
     if k.dim() != 3 or v.dim() != 3 or k.stride(2) != 1 or v.stride(2) != 1:
@@ -176,23 +202,37 @@ def build_segment(family: int, k: torch.Tensor, v: torch.Tensor, log_alpha: Opti
         raise HypicError("seg_offsets must be int64 and dst_slots int32")
     N, H, dk = k.shape
     dv = v.shape[2]
+    _shape("v", v, (N, H, dv))
+    pool._validate()
+    if (pool.family, pool.num_heads, pool.d_k, pool.d_v) != (family, H, dk, dv):
+        raise HypicError(f"pool (family {pool.family}, H={pool.num_heads}, d_k={pool.d_k}, d_v={pool.d_v}) "
+                         f"does not match the stream (family {family}, H={H}, d_k={dk}, d_v={dv})")
+    if seg_offsets.dim() != 1 or seg_offsets.numel() < 1:
+        raise HypicError("seg_offsets must be 1-D with num_segments + 1 entries")
+    _shape("dst_slots", dst_slots, (seg_offsets.numel() - 1,))
+    _flag(err_flag)
     la_st = la_sh = 0
     if log_alpha is not None:
         if log_alpha.dtype != torch.float32:
             raise HypicError("log_alpha must be fp32")
         if family in (DIAGONAL, KDA):
-            if log_alpha.dim() != 3 or log_alpha.stride(2) != 1:
+            _shape("log_alpha", log_alpha, (N, H, dk))
+            if log_alpha.stride(2) != 1:
                 raise HypicError("per-channel log_alpha must be [N,H,d_k] with unit channel stride")
             la_st, la_sh = log_alpha.stride(0), log_alpha.stride(1)
         elif log_alpha.dim() == 1:
+            _shape("log_alpha", log_alpha, (H,))
             la_st, la_sh = 0, log_alpha.stride(0)
         else:
+            _shape("log_alpha", log_alpha, (N, H))
             la_st, la_sh = log_alpha.stride(0), log_alpha.stride(1)
     b_st = b_sh = 0
     if beta is not None:
-        if beta.dtype != torch.float32 or beta.dim() != 2:
+        if beta.dtype != torch.float32:
             raise HypicError("beta must be fp32 [N,H]")
+        _shape("beta", beta, (N, H))
         b_st, b_sh = beta.stride(0), beta.stride(1)
+    _device_check(k, v, log_alpha, seg_offsets, dst_slots, beta, err_flag)
     seg = _Segments(family, H, dk, dv, seg_offsets.numel() - 1, _dtype_code(k), N,
                     _ptr(seg_offsets),
                     _ptr(k), k.stride(0), k.stride(1),
@@ -205,14 +245,27 @@ def build_segment(family: int, k: torch.Tensor, v: torch.Tensor, log_alpha: Opti
     _check(rc, "hypic_build_segment")
 
 
+def _compose_shapes(pool: Pool, R: int, init_S, out_S, out_log_scale, out_P=None) -> None:
+    H, dk, dv = pool.num_heads, pool.d_k, pool.d_v
+    _shape("init_S", init_S, (R, H, dk, dv))
+    _shape("out_S", out_S, (R, H, dk, dv))
+    _shape("out_log_scale", out_log_scale, (R, H, dk) if pool.family == DIAGONAL else (R, H))
+    if out_P is not None and pool.family not in (GDN, KDA):
+        raise HypicError("out_P needs a GDN / KDA pool")
+    if out_P is not None and out_log_scale is None:
+        raise HypicError("out_P needs out_log_scale (the composed operator is e^ell P)")
+    _shape("out_P", out_P, (R, H, dk, dk))
+
+
 def compose_chain(pool: Pool, chain_offsets: torch.Tensor, chain_slots: torch.Tensor,
                   init_S: Optional[torch.Tensor] = None, out_S: Optional[torch.Tensor] = None,
                   out_log_scale: Optional[torch.Tensor] = None, out_P: Optional[torch.Tensor] = None,
                   err_flag: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """hypic_compose_chain: S <- T_i S + S_i along each chain; returns out_S [R,H,d_k,d_v]."""
-    _device_check(chain_offsets, chain_slots, init_S, out_S, out_log_scale, out_P, err_flag)
     if chain_offsets.dtype != torch.int64 or chain_slots.dtype != torch.int32:
         raise HypicError("chain_offsets must be int64 and chain_slots int32")
+    if chain_offsets.dim() != 1 or chain_offsets.numel() < 1 or chain_slots.dim() != 1:
+        raise HypicError("chain_offsets must be 1-D [R+1] and chain_slots 1-D")
     R = chain_offsets.numel() - 1
     if out_S is None:
         out_S = torch.empty((R, pool.num_heads, pool.d_k, pool.d_v), dtype=torch.float32,
@@ -220,6 +273,10 @@ def compose_chain(pool: Pool, chain_offsets: torch.Tensor, chain_slots: torch.Te
     for t in (init_S, out_S, out_log_scale, out_P):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise HypicError("state tensors must be contiguous fp32")
+    pool._validate()
+    _compose_shapes(pool, R, init_S, out_S, out_log_scale, out_P)
+    _flag(err_flag)
+    _device_check(chain_offsets, chain_slots, init_S, out_S, out_log_scale, out_P, err_flag)
     cpool = pool._c()
     rc = lib().hypic_compose_chain(ctypes.byref(cpool), R, _ptr(chain_offsets), _ptr(chain_slots),
                                    chain_slots.numel(), _ptr(init_S), _ptr(out_S), _ptr(out_log_scale),
@@ -236,15 +293,19 @@ def compose_chain_heads(pool: Pool, chain_offsets: torch.Tensor, chain_slots: to
                         stream=None) -> torch.Tensor:
     """hypic_compose_chain_heads: each chain entry applies its head tokens, then folds its
     record; head_k [T,H,d_k], head_v [T,H,d_v], head_beta / head_log_alpha [T,H] fp32."""
-    _device_check(chain_offsets, chain_slots, head_offsets, head_k, head_v, head_beta, head_log_alpha,
-                  init_S, out_S, out_log_scale, err_flag)
     if chain_offsets.dtype != torch.int64 or chain_slots.dtype != torch.int32 or head_offsets.dtype != torch.int64:
         raise HypicError("chain_offsets / head_offsets must be int64 and chain_slots int32")
-    if head_offsets.numel() != chain_slots.numel() + 1:
-        raise HypicError("head_offsets needs one entry per chain slot plus one")
+    if chain_offsets.dim() != 1 or chain_offsets.numel() < 1 or chain_slots.dim() != 1:
+        raise HypicError("chain_offsets must be 1-D [R+1] and chain_slots 1-D")
+    _shape("head_offsets", head_offsets, (chain_slots.numel() + 1,))
     T = head_k.shape[0]
+    H, dk, dv = pool.num_heads, pool.d_k, pool.d_v
+    _shape("head_k", head_k, (T, H, dk))
+    _shape("head_v", head_v, (T, H, dv))
+    _shape("head_beta", head_beta, (T, H))
+    _shape("head_log_alpha", head_log_alpha, (T, H))
     for t_ in (head_k, head_v, head_beta, head_log_alpha):
-        if t_.dtype != torch.float32 or not t_.is_contiguous() or t_.shape[0] != T:
+        if t_.dtype != torch.float32 or not t_.is_contiguous():
             raise HypicError("head tensors must be contiguous fp32 with one row per head token")
     R = chain_offsets.numel() - 1
     if out_S is None:
@@ -252,6 +313,11 @@ def compose_chain_heads(pool: Pool, chain_offsets: torch.Tensor, chain_slots: to
     for t_ in (init_S, out_S, out_log_scale):
         if t_ is not None and (t_.dtype != torch.float32 or not t_.is_contiguous()):
             raise HypicError("state tensors must be contiguous fp32")
+    pool._validate()
+    _compose_shapes(pool, R, init_S, out_S, out_log_scale)
+    _flag(err_flag)
+    _device_check(chain_offsets, chain_slots, head_offsets, head_k, head_v, head_beta, head_log_alpha,
+                  init_S, out_S, out_log_scale, err_flag)
     cpool = pool._c()
     none = T == 0
     rc = lib().hypic_compose_chain_heads(ctypes.byref(cpool), R, _ptr(chain_offsets), _ptr(chain_slots),
@@ -270,22 +336,36 @@ def conv_warmup(tails: torch.Tensor, heads: torch.Tensor, weight: torch.Tensor,
                 num_boundaries: Optional[int] = None, out: Optional[torch.Tensor] = None,
                 err_flag: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """hypic_conv_warmup: tails/heads [rows,K-1,C] raw inputs, weight [C,K]; returns out [B,K-1,C] fp32."""
-    _device_check(tails, heads, weight, bias, tail_index, head_index, out, err_flag)
     if tails.dtype != heads.dtype or not tails.is_contiguous() or not heads.is_contiguous():
         raise HypicError("tails and heads must be contiguous and share a dtype")
+    if weight.dim() != 2:
+        raise HypicError("weight must be [C,K]")
     C, K = weight.shape
     if weight.dtype != torch.float32 or not weight.is_contiguous():
         raise HypicError("weight must be contiguous fp32 [C,K]")
-    if tails.shape[1:] != (K - 1, C) or heads.shape[1:] != (K - 1, C):
+    if tails.dim() != 3 or heads.dim() != 3 or tails.shape[1:] != (K - 1, C) or heads.shape[1:] != (K - 1, C):
         raise HypicError("tails/heads must be [rows, K-1, C]")
     for ix in (tail_index, head_index):
-        if ix is not None and ix.dtype != torch.int32:
-            raise HypicError("indices must be int32")
+        if ix is not None and (ix.dtype != torch.int32 or ix.dim() != 1 or not ix.is_contiguous()):
+            raise HypicError("indices must be contiguous 1-D int32")
     if num_boundaries is None:
         num_boundaries = tail_index.numel() if tail_index is not None else (
             head_index.numel() if head_index is not None else tails.shape[0])
+    for name, ix, table in (("tail_index", tail_index, tails), ("head_index", head_index, heads)):
+        n_have = ix.numel() if ix is not None else table.shape[0]
+        if n_have < num_boundaries:
+            raise HypicError(f"{name if ix is not None else name[:4] + 's'} covers {n_have} boundaries, "
+                             f"needs {num_boundaries}")
+    _shape("bias", bias, (C,))
+    if bias is not None and (bias.dtype != torch.float32 or not bias.is_contiguous()):
+        raise HypicError("bias must be contiguous fp32 [C]")
     if out is None:
         out = torch.empty((num_boundaries, K - 1, C), dtype=torch.float32, device=weight.device)
+    _shape("out", out, (num_boundaries, K - 1, C))
+    if out.dtype != torch.float32 or not out.is_contiguous():
+        raise HypicError("out must be contiguous fp32 [B, K-1, C]")
+    _flag(err_flag)
+    _device_check(tails, heads, weight, bias, tail_index, head_index, out, err_flag)
     rc = lib().hypic_conv_warmup(num_boundaries, C, K, _dtype_code(tails),
                                  _ptr(tails), tails.shape[0], _ptr(tail_index),
                                  _ptr(heads), heads.shape[0], _ptr(head_index),
@@ -302,7 +382,8 @@ def conv_kv(x: torch.Tensor, window: torch.Tensor, weight: torch.Tensor, num_hea
             err_flag: Optional[torch.Tensor] = None, stream=None):
     """hypic_conv_kv: x [rows, C] raw inputs, window [T, K] int32 rows (-1 = zero), weight [C, K].
     Returns (k [T, H, d_k], v [T, H, d_v]) and, with src_token, (beta [T, H], log_alpha [T, H])."""
-    _device_check(x, window, weight, bias, src_token, beta, log_alpha, err_flag)
+    if weight.dim() != 2:
+        raise HypicError("weight must be [C, K]")
     C, K = weight.shape
     if C != num_heads * (d_k + d_v):
         raise HypicError("weight must have H (d_k + d_v) channels")
@@ -316,8 +397,19 @@ def conv_kv(x: torch.Tensor, window: torch.Tensor, weight: torch.Tensor, num_hea
     for t_ in (beta, log_alpha):
         if t_ is not None and (t_.dtype != torch.float32 or not t_.is_contiguous() or t_.shape[-1] != num_heads):
             raise HypicError("beta / log_alpha must be contiguous fp32 [N, H]")
-    if src_token is not None and (src_token.dtype != torch.int32 or src_token.numel() != T):
-        raise HypicError("src_token must be int32 [T]")
+    if src_token is not None and (src_token.dtype != torch.int32 or src_token.numel() != T
+                                  or not src_token.is_contiguous()):
+        raise HypicError("src_token must be contiguous int32 [T]")
+    if beta is not None and log_alpha is not None and beta.shape != log_alpha.shape:
+        raise HypicError("beta and log_alpha must both be [N, H]")
+    for t_ in (beta, log_alpha):
+        if t_ is not None and t_.dim() != 2:
+            raise HypicError("beta / log_alpha must be contiguous fp32 [N, H]")
+    _shape("bias", bias, (C,))
+    if bias is not None and (bias.dtype != torch.float32 or not bias.is_contiguous()):
+        raise HypicError("bias must be contiguous fp32 [C]")
+    _flag(err_flag)
+    _device_check(x, window, weight, bias, src_token, beta, log_alpha, err_flag)
     dev = weight.device
     k = torch.empty((T, num_heads, d_k), dtype=out_dtype, device=dev)
     v = torch.empty((T, num_heads, d_v), dtype=out_dtype, device=dev)

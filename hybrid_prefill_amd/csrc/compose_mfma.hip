@@ -157,6 +157,7 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
     __shared__ __align__(16) float s_stage[D * D];
     __shared__ ChainStage cs;
     __shared__ int sh_bad;
+    __shared__ float sh_pmax[4];      // P mode: each wave's largest |entry| of the product
 
     const int th = threadIdx.x;
     const int w = th >> 6, l = th & 63, h = l >> 5, l32 = l & 31;
@@ -207,6 +208,7 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
     // (with head tokens the first record meets the state its head tokens made)
     const bool first_direct = !HEADS && (MODE_P || a.init_S == nullptr);
     double ell = 0.0;
+    int pexp = 0;                     // P mode: the product is 2^pexp times the state
     if (first_direct && c < c_hi) {
         const int64_t rec = (int64_t)a.chain_slots[c] * a.H + head;
         const float *src = MODE_P ? a.pool_P + rec * D * D : a.pool_S + rec * D * D;
@@ -365,6 +367,11 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
         }                                                                                        \
         if (MODE_P) {                                                                            \
             _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) st[mb] = acc[mb];                   \
+            float m_ = 0.f;                                                                      \
+            _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                     \
+                _Pragma("unroll") for (int q = 0; q < 16; ++q) m_ = fmaxf(m_, fabsf(st[mb][q])); \
+            _Pragma("unroll") for (int o_ = 32; o_ >= 1; o_ >>= 1) m_ = fmaxf(m_, __shfl_xor(m_, o_)); \
+            if (l == 0) sh_pmax[w] = m_;                                                         \
         } else {                                                                                 \
             asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   /* this wave's S_c pieces */     \
             lds_barrier();                               /* everyone's S_c pieces */            \
@@ -375,6 +382,19 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
         }                                                                                        \
         ell += (double)le;                                                                       \
         lds_barrier();       /* fragments and S_c read by all before they are replaced */       \
+        /* P mode: the product of contracting records drifts toward the fp32 subnormals;  */ \
+        /* below 2^-32 it is scaled back to [1, 2) by a power of two (exact), recorded in */ \
+        /* pexp.  Every wave takes the same decision from the same four maxima, read      */ \
+        /* before the next barrier and rewritten only after it.                           */ \
+        if (MODE_P) {                                                                            \
+            const float m_ = fmaxf(fmaxf(sh_pmax[0], sh_pmax[1]), fmaxf(sh_pmax[2], sh_pmax[3]));  \
+            if (m_ < 0x1p-32f && m_ > 0.f) {                                                     \
+                const int s_ = -ilogbf(m_);                                                      \
+                _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                 \
+                    _Pragma("unroll") for (int q = 0; q < 16; ++q) st[mb][q] = ldexpf(st[mb][q], s_); \
+                pexp -= s_;                                                                      \
+            }                                                                                    \
+        }                                                                                        \
         /* head tokens before S, so that the compiler's wait for them at the top of the   */ \
         /* next step does not also wait for S (loads complete in issue order)             */ \
         HYPIC_FETCH_H(c + 1 < c_hi ? c + 1 : c);                                                 \
@@ -401,7 +421,9 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int q = 0; q < 16; ++q) out[(int64_t)(32 * mb + acc_row(q, h)) * D + col0 + l32] = st[mb][q];
-    if (!MODE_P && a.out_ell && th == 0) a.out_ell[orec] = (float)ell;
+    // P mode runs after the state launch: its ell carries the renormalisation, so that
+    // (out_ell, out_P) stays a record of the chain, T = e^ell P
+    if (a.out_ell && th == 0) a.out_ell[orec] = (float)(ell + (double)pexp * 0.69314718055994530942);
 }
 
 // Sliced variant for few chains (the chain is sequential, so one workgroup per
@@ -425,7 +447,6 @@ struct __align__(16) PFrag {
     uint32_t lo[NFRAG * FRAG_U32];
 };
 
-template <bool MODE_P>
 __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs a) {
     __shared__ XStage xs;
     __shared__ PFrag xp;      // wave w's fragments: row block w of P_c
@@ -444,7 +465,7 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
     const int r = unit / a.H;
     const int64_t orec = (int64_t)r * a.H + head;
     const int col = 32 * sl + l32;              // this lane's state column
-    float *out = MODE_P ? a.out_P + orec * D * D : a.out_S + orec * D * D;
+    float *out = a.out_S + orec * D * D;
 
     // ---- chain validation (same rules as the reference kernel)
     if (th == 0) {
@@ -468,22 +489,22 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
     __syncthreads();
     const int bad = sh_bad;
     if (bad) {
-        if (th == 0 && !MODE_P && sl == 0)
+        if (th == 0 && sl == 0)
             raise_flag(a.err_flag, bad == 1 ? HYPIC_EFLAG_SLOT_OUT_OF_RANGE : HYPIC_EFLAG_BAD_OFFSETS);
         const float nanv = __int_as_float(0x7fc00000);
         for (int e = th; e < 32 * D; e += NT) out[(e >> 5) * D + 32 * sl + (e & 31)] = nanv;
-        if (!MODE_P && a.out_ell && th == 0 && sl == 0) a.out_ell[orec] = nanv;
+        if (a.out_ell && th == 0 && sl == 0) a.out_ell[orec] = nanv;
         return;
     }
 
     // ---- initial tile (rows 32w + acc_row, column col)
     f32x16 st;
     int64_t c = c_lo;
-    const bool first_direct = MODE_P || a.init_S == nullptr;
+    const bool first_direct = a.init_S == nullptr;
     double ell = 0.0;
     if (first_direct && c < c_hi) {
         const int64_t rec = (int64_t)a.chain_slots[c] * a.H + head;
-        const float *src = MODE_P ? a.pool_P + rec * D * D : a.pool_S + rec * D * D;
+        const float *src = a.pool_S + rec * D * D;
 #pragma unroll
         for (int q = 0; q < 16; ++q) st[q] = src[(32 * w + acc_row(q, h)) * D + col];
         ell += (double)a.pool_ell[rec];
@@ -492,8 +513,7 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int row = 32 * w + acc_row(q, h);
-            st[q] = MODE_P ? (row == col ? 1.0f : 0.0f)
-                           : (a.init_S ? a.init_S[orec * D * D + (int64_t)row * D + col] : 0.0f);
+            st[q] = a.init_S ? a.init_S[orec * D * D + (int64_t)row * D + col] : 0.0f;
         }
     }
 
@@ -516,10 +536,8 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
     } while (0)
 #define HYPIC_SFETCH(SV, CC)                                                                        \
     do {                                                                                            \
-        if (!MODE_P) {                                                                              \
-            const float *ss_ = a.pool_S + ((int64_t)chain_slot(cs, c_lo, (CC)) * a.H + head) * D * D + col; \
-            _Pragma("unroll") for (int q = 0; q < 16; ++q) SV[q] = ss_[(32 * w + acc_row(q, h)) * D]; \
-        }                                                                                           \
+        const float *ss_ = a.pool_S + ((int64_t)chain_slot(cs, c_lo, (CC)) * a.H + head) * D * D + col; \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q) SV[q] = ss_[(32 * w + acc_row(q, h)) * D];  \
     } while (0)
     // one step: publish the tile, stage P_c (and refetch its registers for step c + 2),
     // state <- e^{ell_c} P_c state + S_c
@@ -561,9 +579,7 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
             acc1_ = mfma(al_, bh_, acc1_);                                                          \
         }                                                                                           \
         acc_ += acc1_;                                                                              \
-        if (MODE_P) {                                                                               \
-            st = acc_;                                                                              \
-        } else {                                                                                    \
+        {                                                                                           \
             const float sc_ = expf(le_);                                                            \
             _Pragma("unroll") for (int q = 0; q < 16; ++q) st[q] = sc_ * acc_[q] + SV[q];           \
         }                                                                                           \
@@ -594,7 +610,7 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
 #undef HYPIC_SFETCH
 #pragma unroll
     for (int q = 0; q < 16; ++q) out[(int64_t)(32 * w + acc_row(q, h)) * D + col] = st[q];
-    if (!MODE_P && a.out_ell && th == 0 && sl == 0) a.out_ell[orec] = (float)ell;
+    if (a.out_ell && th == 0 && sl == 0) a.out_ell[orec] = (float)ell;
 }
 
 }  // namespace
@@ -608,13 +624,14 @@ hipError_t launch_compose_mfma(const ComposeArgs &a, hipStream_t stream, bool *t
     if (units <= 512) {
         // few chains: four workgroups per chain, one per 32-column slice of the state
         const dim3 grid((unsigned)((units + 7) / 8 * 8 * NSL));
-        hipLaunchKernelGGL(compose_sliced_mfma_kernel<false>, grid, dim3(NT), 0, stream, a);
-        if (a.out_P) hipLaunchKernelGGL(compose_sliced_mfma_kernel<true>, grid, dim3(NT), 0, stream, a);
-        return hipGetLastError();
+        hipLaunchKernelGGL(compose_sliced_mfma_kernel, grid, dim3(NT), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((compose_dense_mfma_kernel<false, false>), dim3((unsigned)units), dim3(NT), 0, stream, a);
     }
-    const dim3 grid((unsigned)units);
-    hipLaunchKernelGGL((compose_dense_mfma_kernel<false, false>), grid, dim3(NT), 0, stream, a);
-    if (a.out_P) hipLaunchKernelGGL((compose_dense_mfma_kernel<true, false>), grid, dim3(NT), 0, stream, a);
+    // the composed operator: one workgroup per chain, so that the whole product can be
+    // renormalised at once (it writes out_ell after the state launch)
+    if (a.out_P)
+        hipLaunchKernelGGL((compose_dense_mfma_kernel<true, false>), dim3((unsigned)units), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -9,9 +9,10 @@
 //     S <- diag(e^{ell_i}) S + S_i           (diagonal)
 // and optionally the composed operator ell <- ell + ell_i, P <- P_i P.
 //
-// GDN work split: one workgroup per (request, head, 64-column slab of S, or
-// of P when the composed P is asked for).  The slab stays in LDS across the
-// chain; P_i streams through LDS in 32-column blocks.  Scalar and diagonal
+// GDN work split: one workgroup per (request, head, 64-column slab of S).  The
+// slab stays in LDS across the chain; P_i streams through LDS in 32-column blocks.
+// The composed P runs in a launch of its own, one workgroup per (request, head)
+// holding the whole product, so that it can be renormalised as a whole.  Scalar and diagonal
 // families: 1024 state elements per workgroup, four per thread in registers (or,
 // for unaligned buffers, one workgroup per (request, head)).
 #include "hypic_internal.h"
@@ -43,21 +44,20 @@ __device__ int check_chain(const ComposeArgs &a, int r, int64_t &c_lo, int64_t &
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(NT) void compose_dense_ref_kernel(ComposeArgs a, int nslab_S) {
+__global__ __launch_bounds__(NT) void compose_dense_ref_kernel(ComposeArgs a) {
     __shared__ float St[DK][NSL + 1];
     __shared__ float Pt[DK][KB + 1];
     __shared__ int sh_bad;
 
     const int tid = threadIdx.x;
-    const int nslab = nslab_S + (a.out_P ? DK / NSL : 0);
+    constexpr int nslab = DV / NSL;
     const int slab = blockIdx.x % nslab;
     const int unit = blockIdx.x / nslab;
     const int h = unit % a.H;
     const int r = unit / a.H;
-    const bool isP = slab >= nslab_S;
-    const int c0 = (isP ? slab - nslab_S : slab) * NSL;
-    const int ldo = isP ? DK : DV;      // row length of the output matrix
-    float *out = isP ? a.out_P + ((int64_t)r * a.H + h) * DK * DK : a.out_S + ((int64_t)r * a.H + h) * DK * DV;
+    const int c0 = slab * NSL;
+    constexpr int ldo = DV;
+    float *out = a.out_S + ((int64_t)r * a.H + h) * DK * DV;
 
     int64_t lo, hi;
     const int bad = check_chain(a, r, lo, hi, &sh_bad);
@@ -72,10 +72,7 @@ __global__ __launch_bounds__(NT) void compose_dense_ref_kernel(ComposeArgs a, in
 
     for (int e = tid; e < DK * NSL; e += NT) {
         const int i = e / NSL, c = e % NSL;
-        float x;
-        if (isP) x = (i == c0 + c) ? 1.0f : 0.0f;
-        else x = a.init_S ? a.init_S[((int64_t)r * a.H + h) * DK * DV + (int64_t)i * DV + c0 + c] : 0.0f;
-        St[i][c] = x;
+        St[i][c] = a.init_S ? a.init_S[((int64_t)r * a.H + h) * DK * DV + (int64_t)i * DV + c0 + c] : 0.0f;
     }
     double ell = 0.0;
     const int tr = tid / 16, tc = tid % 16;
@@ -86,7 +83,7 @@ __global__ __launch_bounds__(NT) void compose_dense_ref_kernel(ComposeArgs a, in
         const float *Pi = a.pool_P + rec * DK * DK;
         const float le = a.pool_ell[rec];
         ell += (double)le;
-        const float sc = isP ? 1.0f : expf(le);
+        const float sc = expf(le);
         float acc[RP][4];
 #pragma unroll
         for (int p = 0; p < RP; ++p)
@@ -119,7 +116,7 @@ __global__ __launch_bounds__(NT) void compose_dense_ref_kernel(ComposeArgs a, in
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int c = tc + 16 * q;
-                St[i][c] = isP ? acc[p][q] : sc * acc[p][q] + Si[(int64_t)i * DV + c0 + c];
+                St[i][c] = sc * acc[p][q] + Si[(int64_t)i * DV + c0 + c];
             }
         }
     }
@@ -129,6 +126,95 @@ __global__ __launch_bounds__(NT) void compose_dense_ref_kernel(ComposeArgs a, in
         out[(int64_t)i * ldo + c0 + c] = St[i][c];
     }
     if (slab == 0 && a.out_ell && tid == 0) a.out_ell[(int64_t)r * a.H + h] = (float)ell;
+}
+
+// The composed operator of a GDN / KDA chain, P <- P_i P from P = I, one workgroup
+// per (request, head) holding the whole product in LDS.  A product of contracting
+// records drifts toward the fp32 subnormals (a GDN record's P shrinks by about
+// e^-4 per 2048 tokens at unit keys and beta = sigmoid(N(0,1))), so whenever the
+// largest |entry| falls below 2^-32 the product is scaled back to [1, 2) by a power
+// of two, which is exact, and the exponent goes into ell: (out_ell, out_P) stays a
+// record of the chain, T = e^ell P.  Runs after the state launch, which has raised
+// the error flag and written ell for bad chains; here only P is NaN-filled.
+template <int DK>
+__global__ __launch_bounds__(NT) void compose_P_ref_kernel(ComposeArgs a) {
+    __shared__ float Xs[DK][DK + 1];
+    __shared__ float Pt[DK][KB + 1];
+    __shared__ float red[NT / 64];
+    __shared__ int sh_bad;
+
+    const int tid = threadIdx.x;
+    const int h = blockIdx.x % a.H;
+    const int r = blockIdx.x / a.H;
+    float *out = a.out_P + ((int64_t)r * a.H + h) * DK * DK;
+    int64_t lo, hi;
+    if (check_chain(a, r, lo, hi, &sh_bad)) {
+        const float nanv = __int_as_float(0x7fc00000);
+        for (int e = tid; e < DK * DK; e += NT) out[e] = nanv;
+        return;
+    }
+    for (int e = tid; e < DK * DK; e += NT) Xs[e / DK][e % DK] = (e / DK == e % DK) ? 1.0f : 0.0f;
+    double ell = 0.0;
+    int pexp = 0;                       // the product is 2^pexp Xs
+    // thread (tr, tc) owns rows tr + 16 p and columns tc + 16 q of the product
+    constexpr int RP = DK / 16;
+    const int tr = tid / 16, tc = tid % 16;
+    for (int64_t ci = lo; ci < hi; ++ci) {
+        const int64_t rec = (int64_t)a.chain_slots[ci] * a.H + h;
+        const float *Pi = a.pool_P + rec * DK * DK;
+        ell += (double)a.pool_ell[rec];
+        float acc[RP][RP];
+#pragma unroll
+        for (int p = 0; p < RP; ++p)
+#pragma unroll
+            for (int q = 0; q < RP; ++q) acc[p][q] = 0.f;
+        for (int kb = 0; kb < DK; kb += KB) {
+            __syncthreads();
+            for (int e = tid; e < DK * KB; e += NT) {
+                const int i = e / KB, k = e % KB;
+                Pt[i][k] = Pi[(int64_t)i * DK + kb + k];
+            }
+            __syncthreads();
+            for (int k = 0; k < KB; ++k) {
+                float pv[RP], xv[RP];
+#pragma unroll
+                for (int p = 0; p < RP; ++p) pv[p] = Pt[tr + 16 * p][k];
+#pragma unroll
+                for (int q = 0; q < RP; ++q) xv[q] = Xs[kb + k][tc + 16 * q];
+#pragma unroll
+                for (int p = 0; p < RP; ++p)
+#pragma unroll
+                    for (int q = 0; q < RP; ++q) acc[p][q] += pv[p] * xv[q];
+            }
+        }
+        __syncthreads();    // every read of the old product is done
+        float m = 0.f;
+#pragma unroll
+        for (int p = 0; p < RP; ++p)
+#pragma unroll
+            for (int q = 0; q < RP; ++q) {
+                Xs[tr + 16 * p][tc + 16 * q] = acc[p][q];
+                m = fmaxf(m, fabsf(acc[p][q]));
+            }
+        for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        if ((tid & 63) == 0) red[tid >> 6] = m;
+        __syncthreads();
+        float mx = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < NT / 64; ++wv) mx = fmaxf(mx, red[wv]);
+        if (mx < 0x1p-32f && mx > 0.f) {
+            const int sft = -ilogbf(mx);
+#pragma unroll
+            for (int p = 0; p < RP; ++p)
+#pragma unroll
+                for (int q = 0; q < RP; ++q)
+                    Xs[tr + 16 * p][tc + 16 * q] = ldexpf(Xs[tr + 16 * p][tc + 16 * q], sft);
+            pexp -= sft;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < DK * DK; e += NT) out[e] = Xs[e / DK][e % DK];
+    if (a.out_ell && tid == 0) a.out_ell[(int64_t)r * a.H + h] = (float)(ell + (double)pexp * 0.69314718055994530942);
 }
 
 // Scalar / diagonal: elementwise, one workgroup per (request, head).
@@ -258,9 +344,8 @@ template <int DK, int DV>
 hipError_t launch_dims(const ComposeArgs &a, hipStream_t stream) {
     const int64_t units = (int64_t)a.num_requests * a.H;
     if (a.family == HYPIC_GDN || a.family == HYPIC_KDA) {      // (KDA: ell = 0, P = T_C)
-        const int nslab_S = DV / NSL;
-        const int nslab = nslab_S + (a.out_P ? DK / NSL : 0);
-        hipLaunchKernelGGL((compose_dense_ref_kernel<DK, DV>), dim3((unsigned)(units * nslab)), dim3(NT), 0, stream, a, nslab_S);
+        hipLaunchKernelGGL((compose_dense_ref_kernel<DK, DV>), dim3((unsigned)(units * (DV / NSL))), dim3(NT), 0, stream, a);
+        if (a.out_P) hipLaunchKernelGGL((compose_P_ref_kernel<DK>), dim3((unsigned)units), dim3(NT), 0, stream, a);
     } else if (aligned16(a.pool_S) && aligned16(a.out_S) && (!a.init_S || aligned16(a.init_S))) {
         const dim3 grid((unsigned)(units * (DK * DV / WE)));
         if (a.family == HYPIC_SCALAR)

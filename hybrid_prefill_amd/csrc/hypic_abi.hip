@@ -102,6 +102,8 @@ hypic_status hypic_compose_chain(const hypic_pool *pool, int32_t num_requests,
     if (!chain_offsets || !out_S) return HYPIC_ERR_INVALID_ARG;
     if (num_chain_slots > 0 && !chain_slots) return HYPIC_ERR_INVALID_ARG;
     if (out_P && !has_P(pool->family)) return HYPIC_ERR_INVALID_ARG;
+    // the composed operator may be renormalised into ell: both or neither
+    if (out_P && !out_log_scale) return HYPIC_ERR_INVALID_ARG;
     if ((int64_t)num_requests * pool->num_heads * 4 > 0x7fffffffLL) return HYPIC_ERR_UNSUPPORTED;
 
     ComposeArgs a;

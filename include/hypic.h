@@ -156,9 +156,20 @@ hypic_status hypic_build_segment(const hypic_segments *in, const hypic_pool *poo
  *                  yields init_S (or 0)
  *   init_S         [R][H][d_k][d_v] fp32 or NULL
  *   out_S          [R][H][d_k][d_v] fp32 (required)
- *   out_log_scale  [R][H] ([R][H][d_k] diagonal) fp32 or NULL: sum of ell_i
- *   out_P          [R][H][d_k][d_k] fp32 or NULL (GDN only): P_m ... P_1
- *   (out_log_scale, out_P, out_S) is itself a record of the concatenated chain.
+ *   out_log_scale  [R][H] ([R][H][d_k] diagonal) fp32 or NULL: sum of ell_i (plus the
+ *                  renormalisation of out_P, when that is asked for)
+ *   out_P          [R][H][d_k][d_k] fp32 or NULL (GDN, KDA): P_m ... P_1 up to a power of
+ *                  two that out_log_scale carries; needs out_log_scale (else
+ *                  HYPIC_ERR_INVALID_ARG).  A product of contracting records shrinks
+ *                  toward the fp32 subnormals (a GDN record's P by about e^-4 per 2048
+ *                  tokens at unit keys); below 2^-32 the product is scaled back by an
+ *                  exact power of two 2^s and s ln 2 is taken off out_log_scale, so
+ *                  that T = e^{out_log_scale} out_P holds throughout
+ *   (out_log_scale, out_P, out_S) is the record of the concatenated chain formed from the
+ *   chain's records: out_P is their product up to fp32 rounding (about 16 bits per
+ *   product on the matrix cores), so its error against the operator of the
+ *   concatenated tokens is the records' own error compounded over the chain, about
+ *   sqrt(m) times a record's for m records with independent rounding.
  *
  * Error behaviour: a slot id outside [0, num_slots) sets
  * HYPIC_EFLAG_SLOT_OUT_OF_RANGE, bad chain offsets set HYPIC_EFLAG_BAD_OFFSETS;

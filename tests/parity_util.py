@@ -65,3 +65,13 @@ def record_errors(family, ell_g, P_g, S_g, ell_r, P_r, S_r):
     else:
         eT = float(np.max(np.abs(np.expm1(np.asarray(ell_g, dtype=np.float64) - ell_r))))
     return eS, eT, dl
+
+
+def composed_P_errors(ell_g, P_g, ell_r, P_r):
+    """(P error, ell error) of a composed operator T = e^ell P against a reference
+    (ell_r, P_r).  The compose may move an exact power of two 2^k from P into ell
+    (renormalisation against underflow), so k = round((ell_g - ell_r) / ln 2) is taken
+    out first: P error = |2^k P_g - P_r| / |P_r|, ell error = |ell_g - ell_r - k ln 2|."""
+    d = float(ell_g) - float(ell_r)
+    k = int(round(d / math.log(2.0)))
+    return rel_fro(np.ldexp(np.asarray(P_g, dtype=np.float64), k), P_r), abs(d - k * math.log(2.0))

@@ -98,6 +98,7 @@ def test_compose_validation(L):
     assert c(ctypes.byref(p), 1, FAKE, FAKE, -2, None, FAKE, None, None, None, None) == INVALID
     ps = pool(family=hp.SCALAR, P=False)
     assert c(ctypes.byref(ps), 1, FAKE, FAKE, 1, None, FAKE, None, FAKE, None, None) == INVALID  # out_P for scalar
+    assert c(ctypes.byref(p), 1, FAKE, FAKE, 1, None, FAKE, None, FAKE, None, None) == INVALID   # out_P without ell
     pbad = pool(dk=32)
     assert c(ctypes.byref(pbad), 1, FAKE, FAKE, 1, None, FAKE, None, None, None, None) == UNSUPPORTED
     assert c(ctypes.byref(p), 0, None, None, 0, None, None, None, None, None, None) == 0
@@ -197,3 +198,128 @@ def test_compose_chain_heads_validation(L):
     assert call(out=None) == INVALID
     assert call(T=0) == INVALID                                             # no tokens, but head pointers given
     assert call(R=0) == 0
+
+
+# ----------------------------------------------------------------------------- binding shape checks
+# The C ABI receives no sizes for most tensors, so the binding checks every shape before
+# the call.  These run on CPU tensors: a wrong shape raises before the device check, a
+# right one reaches the device check (the tensors are not on the GPU).
+
+import torch  # noqa: E402
+
+
+def _raises(fn, match):
+    with pytest.raises(hp.HypicError, match=match):
+        fn()
+
+
+def test_build_segment_shape_checks():
+    N, H, d = 10, 2, 64
+    k = torch.zeros((N, H, d), dtype=torch.bfloat16)
+    v = torch.zeros((N, H, d), dtype=torch.bfloat16)
+    la = torch.zeros((N, H))
+    beta = torch.zeros((N, H))
+    offs = torch.tensor([0, 4, 10])
+    slots = torch.tensor([0, 1], dtype=torch.int32)
+    pool = hp.Pool.allocate(hp.GDN, 3, H, d, d, device="cpu")
+    ok = dict(family=hp.GDN, k=k, v=v, log_alpha=la, seg_offsets=offs, pool=pool, dst_slots=slots, beta=beta)
+
+    def call(**kw):
+        return lambda: hp.build_segment(**dict(ok, **kw))
+
+    _raises(call(), "on the GPU")                                            # shapes fine
+    _raises(call(v=torch.zeros((N, H + 1, d), dtype=torch.bfloat16)), "v has shape")
+    _raises(call(v=torch.zeros((N - 1, H, d), dtype=torch.bfloat16)), "v has shape")
+    _raises(call(log_alpha=torch.zeros((N, H, d))), "log_alpha has shape")  # 3-D gates for GDN
+    _raises(call(log_alpha=torch.zeros((N - 2, H))), "log_alpha has shape")
+    _raises(call(log_alpha=torch.zeros((H + 1,))), "log_alpha has shape")
+    _raises(call(beta=torch.zeros((N, H + 1))), "beta has shape")
+    _raises(call(dst_slots=torch.tensor([0], dtype=torch.int32)), "dst_slots has shape")
+    _raises(call(err_flag=torch.zeros(1, dtype=torch.int64)), "err_flag")
+    _raises(call(pool=hp.Pool.allocate(hp.GDN, 3, H + 1, d, d, device="cpu")), "does not match")
+    _raises(call(pool=hp.Pool.allocate(hp.SCALAR, 3, H, d, d, device="cpu")), "does not match")
+    bad = hp.Pool.allocate(hp.GDN, 3, H, d, d, device="cpu")
+    bad.P = torch.zeros((3, H, d, d + 1))
+    _raises(call(pool=bad), "pool.P has shape")
+    bad = hp.Pool.allocate(hp.GDN, 3, H, d, d, device="cpu")
+    bad.log_scale = torch.zeros((3, H, d))
+    _raises(call(pool=bad), "pool.log_scale has shape")
+    # diagonal: per-channel gates [N,H,d_k]; a diagonal pool's log_scale is [slots,H,d_k]
+    dpool = hp.Pool.allocate(hp.DIAGONAL, 3, H, d, d, device="cpu")
+    _raises(call(family=hp.DIAGONAL, pool=dpool, beta=None, log_alpha=torch.zeros((N, H, d))), "on the GPU")
+    _raises(call(family=hp.DIAGONAL, pool=dpool, beta=None, log_alpha=torch.zeros((N, H))), "log_alpha has shape")
+    dpool.log_scale = torch.zeros((3, H))
+    _raises(call(family=hp.DIAGONAL, pool=dpool, beta=None, log_alpha=torch.zeros((N, H, d))),
+            "pool.log_scale has shape")
+
+
+def test_compose_shape_checks():
+    H, d, R = 2, 64, 3
+    pool = hp.Pool.allocate(hp.GDN, 4, H, d, d, device="cpu")
+    offs = torch.tensor([0, 1, 2, 3])
+    ids = torch.tensor([0, 1, 2], dtype=torch.int32)
+    ok = dict(pool=pool, chain_offsets=offs, chain_slots=ids, out_S=torch.zeros((R, H, d, d)))
+
+    def call(**kw):
+        return lambda: hp.compose_chain(**dict(ok, **kw))
+
+    _raises(call(), "on the GPU")
+    _raises(call(out_S=torch.zeros((R - 1, H, d, d))), "out_S has shape")
+    _raises(call(init_S=torch.zeros((R, H, d, d - 1))), "init_S has shape")
+    _raises(call(out_log_scale=torch.zeros((R, H, d))), "out_log_scale has shape")
+    _raises(call(out_log_scale=torch.zeros((R, H)), out_P=torch.zeros((R, H, d, 2 * d))), "out_P has shape")
+    _raises(call(out_P=torch.zeros((R, H, d, d))), "out_P needs out_log_scale")
+    spool = hp.Pool.allocate(hp.SCALAR, 4, H, d, d, device="cpu")
+    _raises(call(pool=spool, out_P=torch.zeros((R, H, d, d))), "out_P needs")
+    dpool = hp.Pool.allocate(hp.DIAGONAL, 4, H, d, d, device="cpu")
+    _raises(call(pool=dpool, out_log_scale=torch.zeros((R, H))), "out_log_scale has shape")
+    _raises(call(pool=dpool, out_log_scale=torch.zeros((R, H, d))), "on the GPU")
+    # the fused head-token compose
+    T = 5
+    hk = dict(pool=pool, chain_offsets=offs, chain_slots=ids, head_offsets=torch.tensor([0, 2, 4, 5]),
+              head_k=torch.zeros((T, H, d)), head_v=torch.zeros((T, H, d)), head_beta=torch.zeros((T, H)),
+              head_log_alpha=torch.zeros((T, H)))
+
+    def hcall(**kw):
+        return lambda: hp.compose_chain_heads(**dict(hk, **kw))
+
+    _raises(hcall(), "on the GPU")
+    _raises(hcall(head_offsets=torch.tensor([0, 2, 5])), "head_offsets has shape")
+    _raises(hcall(head_v=torch.zeros((T, H, d + 1))), "head_v has shape")
+    _raises(hcall(head_beta=torch.zeros((T - 1, H))), "head_beta has shape")
+    _raises(hcall(head_log_alpha=torch.zeros((T, H + 1))), "head_log_alpha has shape")
+    _raises(hcall(out_S=torch.zeros((R, H, d, d + 2))), "out_S has shape")
+
+
+def test_conv_shape_checks():
+    C, K, rows = 16, 4, 5
+    tails = torch.zeros((rows, K - 1, C), dtype=torch.bfloat16)
+    heads = torch.zeros((rows, K - 1, C), dtype=torch.bfloat16)
+    w = torch.zeros((C, K))
+    ok = dict(tails=tails, heads=heads, weight=w)
+
+    def call(**kw):
+        return lambda: hp.conv_warmup(**dict(ok, **kw))
+
+    _raises(call(), "on the GPU")
+    _raises(call(bias=torch.zeros(C + 1)), "bias has shape")
+    _raises(call(out=torch.zeros((rows, K - 1, C + 1))), "out has shape")
+    _raises(call(heads=torch.zeros((rows, K, C), dtype=torch.bfloat16)), "K-1, C")
+    _raises(call(num_boundaries=rows + 1), "covers")
+    _raises(call(tail_index=torch.zeros(2, dtype=torch.int32), num_boundaries=3), "tail_index covers")
+    # conv keys and values: C = H (d_k + d_v) channels
+    H, dk, dv, T = 2, 4, 4, 3
+    Cv = H * (dk + dv)
+    kv = dict(x=torch.zeros((7, Cv), dtype=torch.bfloat16), window=torch.zeros((T, K), dtype=torch.int32),
+              weight=torch.zeros((Cv, K)), num_heads=H, d_k=dk, d_v=dv)
+
+    def kcall(**kw):
+        return lambda: hp.conv_kv(**dict(kv, **kw))
+
+    _raises(kcall(), "on the GPU")
+    _raises(kcall(weight=torch.zeros((Cv + 1, K))), "H \\(d_k \\+ d_v\\) channels")
+    _raises(kcall(window=torch.zeros((T, K + 1), dtype=torch.int32)), "window")
+    _raises(kcall(bias=torch.zeros(Cv - 1)), "bias has shape")
+    _raises(kcall(src_token=torch.zeros(T + 1, dtype=torch.int32)), "src_token")
+    _raises(kcall(src_token=torch.zeros(T, dtype=torch.int32), beta=torch.zeros((5, H)),
+                  log_alpha=torch.zeros((6, H))), "both be")
