@@ -9,6 +9,8 @@ Models", section "Core Approach"; "Cut First-Token Latency by 3.25x ...",
 paragraph 4; the podcast companion page, sections "The transition operator:
 compose, don't add" and "Family comparison"):
 
+* ``forward`` -- the same records plus every token's in-segment output
+  ``o_t = S_t^T q_t`` (the chunked prefill forward's definition).
 * ``build_segments`` -- per segment and head, the record ``(ell, P, S)`` of the
   recurrence ``S_t = A_t S_{t-1} + beta_t k_t v_t^T`` from ``S_0 = 0``, with
   ``T_C = e^ell P`` (KDA, ``A_t = (I - beta k k^T) diag(alpha_t)``: ``ell = 0``,
@@ -63,6 +65,8 @@ def _load():
                        ctypes.POINTER(ctypes.c_int32), ctypes.c_int)
     lib.oracle_build_segments.argtypes = [ci, ci, ci, ci, ci, i64, d, d, d, d, d, d, d, d]
     lib.oracle_build_segments.restype = ci
+    lib.oracle_forward.argtypes = [ci, ci, ci, ci, ci, i64, d, d, d, d, d, d, d, d, d, d]
+    lib.oracle_forward.restype = ci
     lib.oracle_compose.argtypes = [ci, ci, ci, ci, ctypes.c_int64, d, d, d, ci, i64, i32, d, d, d, d]
     lib.oracle_compose.restype = ci
     lib.oracle_causal_conv.argtypes = [ctypes.c_int64, ci, ci, d, d, d, ci, d]
@@ -129,6 +133,38 @@ def build_segments(family: int, k, v, log_alpha, seg_offsets, beta=None, init_S=
     if rc != 0:
         raise ValueError("oracle_build_segments: bad argument")
     return ell, P, S
+
+
+def forward(family: int, k, v, q, log_alpha, seg_offsets, beta=None, init_S=None, want_P: bool = True):
+    """In-segment outputs and records of a packed stream: the chunked prefill forward's
+    definition, token by token.
+
+    As build_segments, plus q [N,H,dk]: o [N,H,dv] with o[t,h] = S_t^T q_t, S_t the
+    head's state right after token t, the recurrence restarting at each segment's
+    first token from init_S[s] (or 0).  Returns (o, ell, P, S).
+    """
+    lib = _load()
+    k, v, qq, la, b, s0 = _f64(k), _f64(v), _f64(q), _f64(log_alpha), _f64(beta), _f64(init_S)
+    offs = np.ascontiguousarray(np.asarray(seg_offsets, dtype=np.int64))
+    N, H, dk = k.shape
+    dv = v.shape[2]
+    nseg = offs.shape[0] - 1
+    assert v.shape[:2] == (N, H) and qq.shape == (N, H, dk)
+    if family in (DIAGONAL, KDA):
+        assert la.shape == (N, H, dk)
+    else:
+        assert la.shape == (N, H)
+    if b is not None:
+        assert b.shape == (N, H)
+    ell = np.zeros((nseg, H, dk)) if family == DIAGONAL else np.zeros((nseg, H))
+    P = np.zeros((nseg, H, dk, dk)) if (family in (GDN, KDA) and want_P) else None
+    S = np.zeros((nseg, H, dk, dv))
+    o = np.zeros((N, H, dv))
+    rc = lib.oracle_forward(family, H, dk, dv, nseg, _ptr(offs, ctypes.c_int64), _ptr(k), _ptr(v), _ptr(qq),
+                            _ptr(b), _ptr(la), _ptr(s0), _ptr(ell), _ptr(P), _ptr(S), _ptr(o))
+    if rc != 0:
+        raise ValueError("oracle_forward: bad argument")
+    return o, ell, P, S
 
 
 def compose(family: int, pool_ell, pool_P, pool_S, chain_offsets, chain_slots, init_S=None,

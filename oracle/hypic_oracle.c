@@ -76,6 +76,10 @@ void oracle_set_num_threads(int n)
  *   k[t*k_ts + i], v[t*v_ts + j], beta[t*b_ts] (or NULL), la[t*la_ts (+ i)]
  * Writes ell (1 value, or d_k for the diagonal family), P (d_k*d_k, GDN and
  * KDA, may be NULL) and S (d_k*d_v).  S0 (d_k*d_v) is the start state, NULL = 0.
+ * With q (q[t*q_ts + i]) and o given, also the in-segment output of every token
+ * from the state right after that token's update (the readout of the recurrence
+ * that the chunked prefill forward computes):
+ *      o[t*o_ts + j] = sum_i S_t[i][j] q_t[i]      (o_t = S_t^T q_t)
  * work must hold d_k + d_v doubles.
  */
 static void recur_head(int family, int64_t n, int dk, int dv,
@@ -84,7 +88,8 @@ static void recur_head(int family, int64_t n, int dk, int dv,
                        const double *beta, int64_t b_ts,
                        const double *la, int64_t la_ts,
                        const double *S0,
-                       double *ell, double *P, double *S, double *work)
+                       double *ell, double *P, double *S, double *work,
+                       const double *q, int64_t q_ts, double *o, int64_t o_ts)
 {
     const int n_ell = family == ORACLE_DIAGONAL ? dk : 1;
     for (int i = 0; i < n_ell; ++i) ell[i] = 0.0;
@@ -161,6 +166,13 @@ static void recur_head(int family, int64_t n, int dk, int dv,
                 ell[i] += lat[i];
             }
         }
+        if (q && o) {
+            const double *qt = q + t * q_ts;
+            double *ot = o + t * o_ts;
+            for (int j = 0; j < dv; ++j) ot[j] = 0.0;
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) ot[j] += S[i * dv + j] * qt[i];
+        }
     }
 }
 
@@ -174,6 +186,13 @@ static void recur_head(int family, int64_t n, int dk, int dv,
  * NULL); S [segs][H][d_k][d_v].
  * Returns 0, or -1 on a bad argument.
  */
+int oracle_forward(int family, int H, int dk, int dv,
+                   int num_segments, const int64_t *seg_offsets,
+                   const double *k, const double *v, const double *q,
+                   const double *beta, const double *log_alpha,
+                   const double *init_S,
+                   double *ell, double *P, double *S, double *o);
+
 int oracle_build_segments(int family, int H, int dk, int dv,
                           int num_segments, const int64_t *seg_offsets,
                           const double *k, const double *v,
@@ -181,6 +200,24 @@ int oracle_build_segments(int family, int H, int dk, int dv,
                           const double *init_S,
                           double *ell, double *P, double *S)
 {
+    return oracle_forward(family, H, dk, dv, num_segments, seg_offsets, k, v, NULL, beta, log_alpha, init_S,
+                          ell, P, S, NULL);
+}
+
+/*
+ * oracle_build_segments plus the in-segment outputs: with q [N][H][d_k] and
+ * o [N][H][d_v], o[t][h] = S_t^T q_t for every token t of every segment, S_t
+ * being the head's state right after token t in a recurrence that starts at the
+ * segment's first token from init_S (or 0).  q = o = NULL: records only.
+ */
+int oracle_forward(int family, int H, int dk, int dv,
+                   int num_segments, const int64_t *seg_offsets,
+                   const double *k, const double *v, const double *q,
+                   const double *beta, const double *log_alpha,
+                   const double *init_S,
+                   double *ell, double *P, double *S, double *o)
+{
+    if ((q == NULL) != (o == NULL)) return -1;
     if (family < 0 || family > 3 || H <= 0 || dk <= 0 || dv <= 0 || num_segments < 0) return -1;
     if (!seg_offsets || !k || !v || !log_alpha || !ell || !S) return -1;
     for (int s = 0; s < num_segments; ++s)
@@ -210,7 +247,9 @@ int oracle_build_segments(int family, int H, int dk, int dv,
                        init_S ? init_S + rec * dk * dv : NULL,
                        ell + rec * n_ell,
                        ((family == ORACLE_GDN || family == ORACLE_KDA) && P) ? P + rec * dk * dk : NULL,
-                       S + rec * dk * dv, work);
+                       S + rec * dk * dv, work,
+                       q ? q + (t0 * H + h) * dk : NULL, (int64_t)H * dk,
+                       o ? o + (t0 * H + h) * dv : NULL, (int64_t)H * dv);
         }
         free(work);
     }

@@ -521,3 +521,134 @@ def test_kda_channel_keys_closed_form():
         S_cf[axes[t]] += b[t, 0] * v[t, 0]
     np.testing.assert_allclose(P[0, 0], np.diag(diag), atol=1e-14)
     np.testing.assert_allclose(S[0, 0], S_cf, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- in-segment outputs
+# o_t = S_t^T q_t from the state right after token t: the chunked prefill forward's
+# readout, with the records as side-outputs (besthub article, paragraph 7).
+
+def test_golden_gdn_two_token_outputs():
+    g = _load("gdn_two_tokens_outputs.json")
+    toks = g["tokens"]
+    k = np.array([t["k"] for t in toks])[:, None, :]
+    v = np.array([t["v"] for t in toks])[:, None, :]
+    q = np.array([t["q"] for t in toks])[:, None, :]
+    b = np.array([[t["beta"]] for t in toks])
+    la = np.log(np.array([[t["alpha"]] for t in toks]))
+    o, ell, P, S = oracle.forward(GDN, k, v, q, la, [0, 2], beta=b)
+    np.testing.assert_allclose(o[:, 0], g["expected"]["o"], atol=1e-12)
+    # the records are the build's, bit for bit
+    ell_b, P_b, S_b = oracle.build_segments(GDN, k, v, la, [0, 2], beta=b)
+    assert np.array_equal(ell, ell_b) and np.array_equal(P, P_b) and np.array_equal(S, S_b)
+
+
+@pytest.mark.parametrize("family", [SCALAR, DIAGONAL, GDN, KDA])
+def test_outputs_single_token(family):
+    """From a zero state one token writes beta k v^T, so o = beta (q . k) v."""
+    k, v, b, la = rand_inputs(family, 1, 2, 5, 3, 2101)
+    q = np.random.default_rng(2102).standard_normal((1, 2, 5))
+    o, _, _, _ = oracle.forward(family, k, v, q, la, [0, 1], beta=b)
+    for h in range(2):
+        want = b[0, h] * float(q[0, h] @ k[0, h]) * v[0, h]
+        np.testing.assert_allclose(o[0, h], want, rtol=1e-13, atol=1e-14)
+
+
+def test_outputs_gdn_orthonormal_keys_closed_form():
+    """Orthonormal keys commute through the projections, so
+    S_t = sum_{s<=t} e^{g_t - g_s} beta_s k_s v_s^T and
+    o_t = sum_{s<=t} e^{g_t - g_s} beta_s (k_s . q_t) v_s."""
+    n, d, dv = 8, 12, 5
+    rng = np.random.default_rng(2103)
+    Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    k = Q[:n][:, None, :]
+    v = rng.standard_normal((n, 1, dv))
+    q = rng.standard_normal((n, 1, d))
+    b = rng.uniform(0.1, 0.9, size=(n, 1))
+    la = -rng.uniform(0.0, 0.3, size=(n, 1))
+    o, _, _, _ = oracle.forward(GDN, k, v, q, la, [0, n], beta=b)
+    g = np.cumsum(la[:, 0])
+    for t in range(n):
+        want = sum(math.exp(g[t] - g[s]) * b[s, 0] * float(k[s, 0] @ q[t, 0]) * v[s, 0] for s in range(t + 1))
+        np.testing.assert_allclose(o[t, 0], want, rtol=1e-12, atol=1e-13)
+
+
+def test_outputs_scalar_and_diagonal_closed_forms():
+    """Scalar: o_t = sum_{s<=t} gamma^{t-s} (k_s . q_t) v_s (retention); diagonal:
+    o_t = sum_{s<=t} ((q_t * prod_{s<r<=t} alpha_r) . k_s) v_s (gated linear attention)."""
+    n, d, dv = 9, 4, 3
+    rng = np.random.default_rng(2104)
+    k, v, q = (rng.standard_normal((n, 1, d)), rng.standard_normal((n, 1, dv)), rng.standard_normal((n, 1, d)))
+    lg = math.log(0.9)
+    o, _, _, _ = oracle.forward(SCALAR, k, v, q, np.full((n, 1), lg), [0, n])
+    for t in range(n):
+        want = sum(0.9 ** (t - s) * float(k[s, 0] @ q[t, 0]) * v[s, 0] for s in range(t + 1))
+        np.testing.assert_allclose(o[t, 0], want, rtol=1e-12, atol=1e-13)
+    la = -rng.uniform(0.0, 0.5, size=(n, 1, d))
+    o, _, _, _ = oracle.forward(DIAGONAL, k, v, q, la, [0, n])
+    for t in range(n):
+        want = np.zeros(dv)
+        for s in range(t + 1):
+            decay = np.exp(la[s + 1:t + 1, 0].sum(axis=0))
+            want += float((q[t, 0] * decay) @ k[s, 0]) * v[s, 0]
+        np.testing.assert_allclose(o[t, 0], want, rtol=1e-12, atol=1e-13)
+
+
+def test_outputs_plain_linear_attention():
+    """No decay, no delta term (beta = 1 on the scalar family): causal linear
+    attention, O = tril(Q K^T) V."""
+    n, d, dv = 11, 6, 4
+    rng = np.random.default_rng(2105)
+    k, v, q = (rng.standard_normal((n, 1, d)), rng.standard_normal((n, 1, dv)), rng.standard_normal((n, 1, d)))
+    o, _, _, _ = oracle.forward(SCALAR, k, v, q, np.zeros((n, 1)), [0, n])
+    want = np.tril(q[:, 0] @ k[:, 0].T) @ v[:, 0]
+    np.testing.assert_allclose(o[:, 0], want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("family", [SCALAR, DIAGONAL, GDN, KDA])
+def test_outputs_brute_force_dense_states(family):
+    """Every token's state by dense products of the A_t matrices, read out with q_t."""
+    n, H, dk, dv = 10, 2, 4, 3
+    k, v, b, la = rand_inputs(family, n, H, dk, dv, 2106, decay=0.3)
+    q = np.random.default_rng(2107).standard_normal((n, H, dk))
+    offs = [0, 4, 4, 10]                     # an empty segment in the middle
+    o, _, _, _ = oracle.forward(family, k, v, q, la, offs, beta=b)
+    for h in range(H):
+        for s in range(3):
+            for t in range(offs[s], offs[s + 1]):
+                sl = slice(offs[s], t + 1)
+                _, St = brute_force(family, k[sl, h], v[sl, h], one_head(b, h)[sl] if b is not None else None,
+                                    la[sl, h])
+                np.testing.assert_allclose(o[t, h], St.T @ q[t, h], rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("family", [SCALAR, DIAGONAL, GDN, KDA])
+def test_outputs_from_a_start_state_compose(family):
+    """From a start state S_0 the outputs are (T_{<=t} S_0 + S_t(0))^T q_t, where
+    T_{<=t} and S_t(0) are the record of the segment's first t+1 tokens: the
+    composition law read out token by token."""
+    n, H, dk, dv = 7, 2, 4, 3
+    k, v, b, la = rand_inputs(family, n, H, dk, dv, 2108, decay=0.2)
+    rng = np.random.default_rng(2109)
+    q = rng.standard_normal((n, H, dk))
+    S0 = rng.standard_normal((1, H, dk, dv))
+    o, _, _, _ = oracle.forward(family, k, v, q, la, [0, n], beta=b, init_S=S0)
+    o0, _, _, _ = oracle.forward(family, k, v, q, la, [0, n], beta=b)
+    for t in range(n):
+        ell, P, _ = oracle.build_segments(family, k[:t + 1], v[:t + 1], la[:t + 1], [0, t + 1],
+                                          beta=None if b is None else b[:t + 1])
+        for h in range(H):
+            T = record_T(family, ell[0, h], None if P is None else P[0, h], dk)
+            want = o0[t, h] + (T @ S0[0, h]).T @ q[t, h]
+            np.testing.assert_allclose(o[t, h], want, rtol=1e-11, atol=1e-12)
+
+
+def test_outputs_last_token_reads_the_record():
+    """The last output of a segment is its zero-start record read out: o_last = S^T q_last."""
+    n, H, d = 70, 3, 6
+    k, v, b, la = rand_inputs(GDN, n, H, d, d, 2110)
+    q = np.random.default_rng(2111).standard_normal((n, H, d))
+    offs = [0, 33, 70]
+    o, _, _, S = oracle.forward(GDN, k, v, q, la, offs, beta=b)
+    for s in range(2):
+        for h in range(H):
+            np.testing.assert_allclose(o[offs[s + 1] - 1, h], S[s, h].T @ q[offs[s + 1] - 1, h], rtol=1e-13)
