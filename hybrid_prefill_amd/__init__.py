@@ -6,6 +6,8 @@ HIP stream, and allocates outputs the caller did not pass.  The names follow
 the C ABI in ``include/hypic.h``:
 
 * :func:`build_segment`  -- records ``(ell, P, S)`` of segments into pool slots
+* :func:`prefill_segment` -- the chunked prefill forward's in-segment outputs
+  ``o_t = S_t^T q_t``, with the records as optional side-outputs
 * :func:`compose_chain`  -- fold pool records along request chains
 * :func:`compose_chain_heads` -- the same with a few tokens applied to the state
   before each record (the warmed first tokens of reused conv-variant segments)
@@ -58,7 +60,7 @@ class _Segments(ctypes.Structure):
                 ("log_alpha", ctypes.c_void_p), ("la_stride_t", ctypes.c_int64), ("la_stride_h", ctypes.c_int64)]
 
 
-EXPORTED = ("hypic_build_segment", "hypic_compose_chain", "hypic_compose_chain_heads", "hypic_conv_warmup",
+EXPORTED = ("hypic_build_segment", "hypic_prefill_segment", "hypic_compose_chain", "hypic_compose_chain_heads", "hypic_conv_warmup",
             "hypic_conv_kv", "hypic_status_string", "hypic_abi_version")
 
 
@@ -74,6 +76,9 @@ def lib():
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     L.hypic_build_segment.argtypes = [ctypes.POINTER(_Segments), ctypes.POINTER(_Pool), vp, vp, vp]
     L.hypic_build_segment.restype = i32
+    L.hypic_prefill_segment.argtypes = [ctypes.POINTER(_Segments), vp, i64, i64, vp, i64, i64, i32,
+                                        ctypes.POINTER(_Pool), vp, vp, vp]
+    L.hypic_prefill_segment.restype = i32
     L.hypic_compose_chain.argtypes = [ctypes.POINTER(_Pool), i32, vp, vp, i64, vp, vp, vp, vp, vp, vp]
     L.hypic_compose_chain.restype = i32
     L.hypic_conv_warmup.argtypes = [i32, i32, i32, i32, vp, i64, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp]
@@ -183,34 +188,18 @@ class Pool:
                      _ptr(self.log_scale), _ptr(self.P), _ptr(self.S))
 
 
-def build_segment(family: int, k: torch.Tensor, v: torch.Tensor, log_alpha: Optional[torch.Tensor],
-                  seg_offsets: torch.Tensor, pool: Pool, dst_slots: torch.Tensor,
-                  beta: Optional[torch.Tensor] = None, err_flag: Optional[torch.Tensor] = None,
-                  stream=None) -> None:
-    """hypic_build_segment: records of every segment of a packed stream into pool slots.
-
-    k [N,H,d_k], v [N,H,d_v] (bf16 or fp32, unit channel stride); log_alpha
-    [N,H] (scalar, GDN), [H] broadcast per head (constant decay) or [N,H,d_k]
-    (diagonal), fp32, or None (no decay); beta [N,H] fp32 or None (= 1);
-    seg_offsets device int64 [S+1]; dst_slots device int32 [S].
-    """
+def _segments(family: int, k: torch.Tensor, v: torch.Tensor, log_alpha: Optional[torch.Tensor],
+              seg_offsets: torch.Tensor, beta: Optional[torch.Tensor]) -> _Segments:
+    """Shape and dtype checks of a packed token stream, then its C descriptor (no device access)."""
     if k.dtype != v.dtype:
         raise HypicError("k and v must share a dtype")
     if k.dim() != 3 or v.dim() != 3 or k.stride(2) != 1 or v.stride(2) != 1:
         raise HypicError("k, v must be [N,H,d] with unit channel stride")
-    if seg_offsets.dtype != torch.int64 or dst_slots.dtype != torch.int32:
-        raise HypicError("seg_offsets must be int64 and dst_slots int32")
+    if seg_offsets.dtype != torch.int64 or seg_offsets.dim() != 1 or seg_offsets.numel() < 1:
+        raise HypicError("seg_offsets must be 1-D int64 with num_segments + 1 entries")
     N, H, dk = k.shape
     dv = v.shape[2]
     _shape("v", v, (N, H, dv))
-    pool._validate()
-    if (pool.family, pool.num_heads, pool.d_k, pool.d_v) != (family, H, dk, dv):
-        raise HypicError(f"pool (family {pool.family}, H={pool.num_heads}, d_k={pool.d_k}, d_v={pool.d_v}) "
-                         f"does not match the stream (family {family}, H={H}, d_k={dk}, d_v={dv})")
-    if seg_offsets.dim() != 1 or seg_offsets.numel() < 1:
-        raise HypicError("seg_offsets must be 1-D with num_segments + 1 entries")
-    _shape("dst_slots", dst_slots, (seg_offsets.numel() - 1,))
-    _flag(err_flag)
     la_st = la_sh = 0
     if log_alpha is not None:
         if log_alpha.dtype != torch.float32:
@@ -232,17 +221,92 @@ def build_segment(family: int, k: torch.Tensor, v: torch.Tensor, log_alpha: Opti
             raise HypicError("beta must be fp32 [N,H]")
         _shape("beta", beta, (N, H))
         b_st, b_sh = beta.stride(0), beta.stride(1)
+    return _Segments(family, H, dk, dv, seg_offsets.numel() - 1, _dtype_code(k), N,
+                     _ptr(seg_offsets),
+                     _ptr(k), k.stride(0), k.stride(1),
+                     _ptr(v), v.stride(0), v.stride(1),
+                     _ptr(beta), b_st, b_sh,
+                     _ptr(log_alpha), la_st, la_sh)
+
+
+def _pool_for(pool: Pool, family: int, H: int, dk: int, dv: int, dst_slots: torch.Tensor, nseg: int) -> None:
+    pool._validate()
+    if (pool.family, pool.num_heads, pool.d_k, pool.d_v) != (family, H, dk, dv):
+        raise HypicError(f"pool (family {pool.family}, H={pool.num_heads}, d_k={pool.d_k}, d_v={pool.d_v}) "
+                         f"does not match the stream (family {family}, H={H}, d_k={dk}, d_v={dv})")
+    if dst_slots.dtype != torch.int32:
+        raise HypicError("dst_slots must be int32")
+    _shape("dst_slots", dst_slots, (nseg,))
+
+
+def build_segment(family: int, k: torch.Tensor, v: torch.Tensor, log_alpha: Optional[torch.Tensor],
+                  seg_offsets: torch.Tensor, pool: Pool, dst_slots: torch.Tensor,
+                  beta: Optional[torch.Tensor] = None, err_flag: Optional[torch.Tensor] = None,
+                  stream=None) -> None:
+    """hypic_build_segment: records of every segment of a packed stream into pool slots.
+
+    k [N,H,d_k], v [N,H,d_v] (bf16 or fp32, unit channel stride); log_alpha
+    [N,H] (scalar, GDN), [H] broadcast per head (constant decay) or [N,H,d_k]
+    (diagonal), fp32, or None (no decay); beta [N,H] fp32 or None (= 1);
+    seg_offsets device int64 [S+1]; dst_slots device int32 [S].
+    """
+    seg = _segments(family, k, v, log_alpha, seg_offsets, beta)
+    _pool_for(pool, family, seg.num_heads, seg.d_k, seg.d_v, dst_slots, seg.num_segments)
+    _flag(err_flag)
     _device_check(k, v, log_alpha, seg_offsets, dst_slots, beta, err_flag)
-    seg = _Segments(family, H, dk, dv, seg_offsets.numel() - 1, _dtype_code(k), N,
-                    _ptr(seg_offsets),
-                    _ptr(k), k.stride(0), k.stride(1),
-                    _ptr(v), v.stride(0), v.stride(1),
-                    _ptr(beta), b_st, b_sh,
-                    _ptr(log_alpha), la_st, la_sh)
     cpool = pool._c()
     rc = lib().hypic_build_segment(ctypes.byref(seg), ctypes.byref(cpool), _ptr(dst_slots),
                                    _ptr(err_flag), _stream(stream))
     _check(rc, "hypic_build_segment")
+
+
+def prefill_segment(family: int, k: torch.Tensor, v: torch.Tensor, q: Optional[torch.Tensor],
+                    log_alpha: Optional[torch.Tensor], seg_offsets: torch.Tensor,
+                    beta: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    out_dtype=torch.float32, pool: Optional[Pool] = None,
+                    dst_slots: Optional[torch.Tensor] = None, outputs: bool = True,
+                    err_flag: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
+    """hypic_prefill_segment: the chunked prefill forward of every segment (zero state
+    at each segment's first token), o_t = S_t^T q_t for every token, and with a pool
+    the records (ell, P, S) into dst_slots as build_segment writes them.
+
+    q [N,H,d_k] in k's dtype; out [N,H,d_v] fp32 or bf16 (allocated when None).
+    outputs=False: the records alone (q and out unused).  Returns out (or None).
+    """
+    seg = _segments(family, k, v, log_alpha, seg_offsets, beta)
+    N, H, dk, dv = seg.num_tokens, seg.num_heads, seg.d_k, seg.d_v
+    if pool is not None:
+        if dst_slots is None:
+            raise HypicError("a pool needs dst_slots")
+        _pool_for(pool, family, H, dk, dv, dst_slots, seg.num_segments)
+    elif not outputs:
+        raise HypicError("nothing to compute: no outputs and no pool")
+    q_st = q_sh = o_st = o_sh = 0
+    o_code = F32
+    if outputs:
+        if q is None:
+            raise HypicError("outputs need q")
+        if q.dtype != k.dtype or q.dim() != 3 or q.stride(2) != 1:
+            raise HypicError("q must be [N,H,d_k] in k's dtype with unit channel stride")
+        _shape("q", q, (N, H, dk))
+        if out is None:
+            out = torch.empty((N, H, dv), dtype=out_dtype, device=k.device)
+        if out.dim() != 3 or out.stride(2) != 1:
+            raise HypicError("out must be [N,H,d_v] with unit channel stride")
+        _shape("out", out, (N, H, dv))
+        o_code = _dtype_code(out)
+        q_st, q_sh, o_st, o_sh = q.stride(0), q.stride(1), out.stride(0), out.stride(1)
+    else:
+        q = out = None
+    _flag(err_flag)
+    _device_check(k, v, q, out, log_alpha, seg_offsets, dst_slots, beta, err_flag)
+    cpool = pool._c() if pool is not None else None
+    rc = lib().hypic_prefill_segment(ctypes.byref(seg), _ptr(q), q_st, q_sh, _ptr(out), o_st, o_sh, o_code,
+                                     None if cpool is None else ctypes.byref(cpool),
+                                     _ptr(dst_slots) if pool is not None else None, _ptr(err_flag),
+                                     _stream(stream))
+    _check(rc, "hypic_prefill_segment")
+    return out
 
 
 def _compose_shapes(pool: Pool, R: int, init_S, out_S, out_log_scale, out_P=None) -> None:

@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libhypic.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["hypic_abi.hip", "build_ref.hip", "build_mfma.hip", "build_sd_mfma.hip", "compose_ref.hip",
+SOURCES = ["hypic_abi.hip", "build_ref.hip", "build_mfma.hip", "build_fwd_mfma.hip", "build_sd_mfma.hip",
+           "compose_ref.hip",
            "compose_mfma.hip", "conv_warmup.hip", "conv_kv.hip",
            "build_kda.hip", "build_kda_mfma.hip"]
 

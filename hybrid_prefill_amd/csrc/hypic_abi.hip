@@ -90,6 +90,61 @@ hypic_status hypic_build_segment(const hypic_segments *in, const hypic_pool *poo
     return e == hipSuccess ? HYPIC_OK : HYPIC_ERR_HIP;
 }
 
+hypic_status hypic_prefill_segment(const hypic_segments *in, const void *q, int64_t q_stride_t,
+                                   int64_t q_stride_h, void *o, int64_t o_stride_t, int64_t o_stride_h,
+                                   int32_t o_dtype, const hypic_pool *pool, const int32_t *dst_slots,
+                                   uint32_t *err_flag, void *stream) {
+    if (!in) return HYPIC_ERR_INVALID_ARG;
+    if (!family_ok(in->family) || !dtype_ok(in->kv_dtype)) return HYPIC_ERR_UNSUPPORTED;
+    if (in->family != HYPIC_GDN || in->kv_dtype != HYPIC_BF16 || in->d_k != 128 || in->d_v != 128)
+        return HYPIC_ERR_UNSUPPORTED;
+    if (in->num_heads <= 0 || in->num_segments < 0 || in->num_tokens < 0) return HYPIC_ERR_INVALID_ARG;
+    if (!pool && !o) return HYPIC_ERR_INVALID_ARG;          // nothing asked for
+    if (pool) {
+        const hypic_status ps = check_pool(pool);
+        if (ps != HYPIC_OK) return ps;
+        if (pool->family != in->family || pool->num_heads != in->num_heads || pool->d_k != in->d_k ||
+            pool->d_v != in->d_v)
+            return HYPIC_ERR_INVALID_ARG;
+    }
+    if (o) {
+        if (!dtype_ok(o_dtype)) return HYPIC_ERR_UNSUPPORTED;
+        if (!q || q_stride_t < 0 || q_stride_h < 0 || o_stride_t < 0 || o_stride_h < 0) return HYPIC_ERR_INVALID_ARG;
+    }
+    if (in->num_segments == 0) return HYPIC_OK;
+    if (!in->seg_offsets || (pool && !dst_slots)) return HYPIC_ERR_INVALID_ARG;
+    if (in->num_tokens > 0 && (!in->k || !in->v)) return HYPIC_ERR_INVALID_ARG;
+    if (in->k_stride_t < 0 || in->k_stride_h < 0 || in->v_stride_t < 0 || in->v_stride_h < 0 ||
+        in->beta_stride_t < 0 || in->beta_stride_h < 0 || in->la_stride_t < 0 || in->la_stride_h < 0)
+        return HYPIC_ERR_INVALID_ARG;
+    if ((int64_t)in->num_segments * in->num_heads > 0x7fffffffLL) return HYPIC_ERR_UNSUPPORTED;
+
+    BuildArgs a;
+    memset(&a, 0, sizeof(a));
+    a.family = in->family; a.H = in->num_heads; a.dk = in->d_k; a.dv = in->d_v;
+    a.num_segments = in->num_segments; a.kv_dtype = in->kv_dtype; a.num_tokens = in->num_tokens;
+    a.seg_offsets = in->seg_offsets;
+    a.k = in->k; a.k_st = in->k_stride_t; a.k_sh = in->k_stride_h;
+    a.v = in->v; a.v_st = in->v_stride_t; a.v_sh = in->v_stride_h;
+    a.beta = in->beta; a.b_st = in->beta_stride_t; a.b_sh = in->beta_stride_h;
+    a.log_alpha = in->log_alpha; a.la_st = in->la_stride_t; a.la_sh = in->la_stride_h;
+    if (pool) {
+        a.dst_slots = dst_slots; a.num_slots = pool->num_slots;
+        a.pool_ell = pool->log_scale; a.pool_P = pool->P; a.pool_S = pool->S;
+    }
+    a.err_flag = err_flag;
+    FwdIO io;
+    memset(&io, 0, sizeof(io));
+    io.q = q; io.q_st = q_stride_t; io.q_sh = q_stride_h;
+    io.o = o; io.o_st = o_stride_t; io.o_sh = o_stride_h; io.o_bf16 = o_dtype == HYPIC_BF16;
+
+    bool taken = false;
+    const hipError_t e = launch_chunk_mfma(a, io, pool != nullptr, o != nullptr, static_cast<hipStream_t>(stream),
+                                           &taken);
+    if (!taken) return HYPIC_ERR_UNSUPPORTED;                 // unaligned rows or strides
+    return e == hipSuccess ? HYPIC_OK : HYPIC_ERR_HIP;
+}
+
 hypic_status hypic_compose_chain(const hypic_pool *pool, int32_t num_requests,
                                  const int64_t *chain_offsets, const int32_t *chain_slots,
                                  int64_t num_chain_slots,

@@ -61,7 +61,17 @@ struct ConvKvArgs {
     uint32_t *err_flag;
 };
 
+// Queries and in-segment outputs of the chunked prefill forward (device pointers,
+// strides in elements): q in the keys' dtype, o fp32 or bf16 (o_bf16).
+struct FwdIO {
+    const void *q; int64_t q_st, q_sh;
+    void *o; int64_t o_st, o_sh;
+    int32_t o_bf16;
+};
+
 hipError_t launch_build(const BuildArgs &a, hipStream_t stream);
+hipError_t launch_chunk_mfma(const BuildArgs &a, const FwdIO &io, bool records, bool outputs, hipStream_t stream,
+                             bool *taken);
 hipError_t launch_compose(const ComposeArgs &a, hipStream_t stream);
 hipError_t launch_conv_warmup(const ConvArgs &a, hipStream_t stream);
 hipError_t launch_conv_kv(const ConvKvArgs &a, hipStream_t stream);

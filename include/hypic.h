@@ -144,6 +144,36 @@ hypic_status hypic_build_segment(const hypic_segments *in, const hypic_pool *poo
                                  const int32_t *dst_slots, uint32_t *err_flag, void *stream);
 
 /*
+ * hypic_prefill_segment -- the chunked prefill forward of every segment and head of
+ * `in`, each from a zero state at the segment's first token, read out at every token:
+ *       o_t = S_t^T q_t        (S_t: the head's state right after token t's update)
+ * and, when pool is not NULL, the segment's record (ell, P, S) written to pool slot
+ * dst_slots[s] exactly as hypic_build_segment defines it.  Source: besthub article,
+ * paragraph 7 (the one-time construction of (T_C, S) next to the ordinary prefill
+ * forward) and paragraph 4 (the record); podcast page, reference 7 (the GDN
+ * recurrence whose states are read out).
+ *
+ *   q         [N][H][d_k] in kv_dtype: q[t*q_stride_t + h*q_stride_h + i]
+ *   o         [N][H][d_v] in o_dtype (HYPIC_F32 or HYPIC_BF16):
+ *             o[t*o_stride_t + h*o_stride_h + j]; written for every token of every
+ *             segment and nowhere else (segments must not overlap).  o = NULL (q
+ *             ignored): the records alone, exactly as hypic_build_segment.
+ *   pool, dst_slots   as hypic_build_segment, or NULL for the outputs alone.
+ * At least one of o and pool.  GDN with bf16 k, v and q at d_k = d_v = 128, rows
+ * 16-byte aligned and strides multiples of 8 elements; anything else returns
+ * HYPIC_ERR_UNSUPPORTED (nothing launched).
+ *
+ * Error behaviour: the flags of hypic_build_segment.  A dst slot out of range: nothing
+ * of that segment is written (neither its record nor its outputs).  Bad offsets: its
+ * record (when built) is filled with NaN and none of its outputs is written (there
+ * is no token range to write).  Every other segment is computed normally.
+ */
+hypic_status hypic_prefill_segment(const hypic_segments *in, const void *q, int64_t q_stride_t,
+                                   int64_t q_stride_h, void *o, int64_t o_stride_t, int64_t o_stride_h,
+                                   int32_t o_dtype, const hypic_pool *pool, const int32_t *dst_slots,
+                                   uint32_t *err_flag, void *stream);
+
+/*
  * hypic_compose_chain -- for every request r and head h, fold the pool records
  * chain_slots[chain_offsets[r] .. chain_offsets[r+1]) in prompt order:
  *       S <- T_i S + S_i = e^{ell_i} (P_i S) + S_i
