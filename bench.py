@@ -6,6 +6,9 @@ One step = one pass of the hot path over one batch of synthetic input:
                  (segment, head) records, then compose the 16-segment chain to
                  the request's final state.
 Secondary lines (same JSON object, key "secondary"):
+  forward        the same workload's chunked prefill forward (in-segment outputs
+                 o_t = S_t^T q_t, bf16 q and o) alone and with the records as
+                 side-outputs: the records' cost as a fraction of the forward
   compose_pool   4096-slot GDN pool (H=32, d=128, fp32 records), 64 requests each
                  composing 32 seeded slot ids -> compositions/s
   scalar/diag    RetNet-style scalar and GLA-style diagonal builds, H=16, d=128,
@@ -16,18 +19,27 @@ Secondary lines (same JSON object, key "secondary"):
                  warmed head keys/values applied inside the compose
   kda            KDA family build (chunked, on the fp32 matrix cores) and its
                  8-segment chain, H=16, d=128, bf16, 8 x 2048 tokens
+  peaks          measured peaks of this machine: a streaming read and a loop of bf16
+                 matrix-core products (libhypic_peaks.so)
 
 Inputs are resident in HBM before the timed region starts.  Kernel durations
-come from HIP events recorded on the stream the kernels are launched on.
-The cpu_baseline leg times the fp64 oracle on a bounded sample on the host.
+come from HIP events recorded on the stream the kernels are launched on, one
+event pair per launch (mean, p10, p50, p90 reported).  The cpu_baseline leg
+times the fp64 oracle on a bounded sample on the host.
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|sd|compose|rag|convexact|kda] [--no-cpu]
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--only main|forward|sd|compose|rag|convexact|kda|peaks] [--no-cpu]
+       python bench.py --summarize-traffic FETCH_CSV WRITE_CSV OUT_MD  (rocprofv3 counter CSVs -> summary)
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import ctypes
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -45,12 +57,35 @@ PEAK_HBM = 8.0e12            # B/s, MI355X published
 PEAK_BF16 = 2.5e15           # FLOP/s dense bf16 MFMA
 PEAK_FP32 = 157.3e12         # FLOP/s fp32 (matrix and vector, published)
 CHUNK = 64
-# HBM bytes per launch of the GDN build kernel, from rocprofv3 FETCH_SIZE + WRITE_SIZE
-# (scaled by the copy-kernel calibration); None until measured for the current kernel.
-# HBM bytes per launch of the GDN build on the main workload (rocprofv3 FETCH_SIZE and
-# WRITE_SIZE, each scaled by what the counter reads for a copy of known size: read
-# 604.4 MB + write 67.1 MB); None whenever the kernel changed since the counters were taken
-TRAFFIC_GDN_BUILD = 671.5e6
+CSRC = os.path.join(ROOT, "hybrid_prefill_amd", "csrc")
+# The GDN build's HBM bytes per launch come from a committed rocprofv3 counter summary
+# (FETCH_SIZE and WRITE_SIZE, scaled by what the counters read for a copy of known
+# size).  The summary records a hash of the kernel's sources; when the sources have
+# changed since, the bytes are unknown (null) until the counters are taken again.
+GDN_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gdn_build_h32_d128_16x2048_traffic.md")
+GDN_BUILD_SOURCES = ("build_mfma.hip", "gdn_mfma_common.h", "hypic_internal.h")
+
+
+def source_sha(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(profile=GDN_TRAFFIC_PROFILE, sources=GDN_BUILD_SOURCES):
+    """HBM bytes per launch from the committed counter summary, or None when it is
+    missing or the kernel's sources changed since it was taken."""
+    try:
+        text = open(profile).read()
+    except OSError:
+        return None
+    m_sha = re.search(r"kernel source sha256\[:16\]: `([0-9a-f]{16})`", text)
+    m_tot = re.search(r"HBM bytes per launch: ([0-9.]+) MB", text)
+    if not (m_sha and m_tot) or m_sha.group(1) != source_sha(sources):
+        return None
+    return float(m_tot.group(1)) * 1e6
 
 
 def log(msg):
@@ -119,25 +154,36 @@ class KernelTimer:
         self.pairs = {}
 
 
-def kernel_pass(launches, n):
-    """Mean duration of each launch in `launches` (name -> callable, idempotent): one
-    HIP-event pair around n back-to-back launches of it on the current stream, so the
-    per-launch event overhead is spread over n; a short device spin first lets the
-    host run ahead, so host time is never counted as kernel time."""
-    out = []
+def launch_stats(launches, n):
+    """Per-launch durations of each launch in `launches` (name -> callable, idempotent):
+    one HIP-event pair around every launch on the current stream, after a short device
+    spin that lets the host queue the launches ahead, so that no host time between an
+    event and its launch counts as kernel time.  Returns {name: stats}."""
+    out = {}
     for name, fn in launches:
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         if hasattr(torch.cuda, "_sleep"):
             torch.cuda._sleep(int(5e6))
-        s.record()
-        for _ in range(n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for s_, e_ in ev:
+            s_.record()
             fn()
-        e.record()
+            e_.record()
         torch.cuda.synchronize()
-        out.append(s.elapsed_time(e) / n)
-    return tuple(out)
+        out[name] = stats_ms([s_.elapsed_time(e_) for s_, e_ in ev])
+    return out
+
+
+def stats_ms(ts):
+    a = np.asarray(ts, dtype=np.float64)
+    return {"mean": float(a.mean()), "p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def kernel_pass(launches, n):
+    """Mean duration of each launch (see launch_stats)."""
+    st = launch_stats(launches, n)
+    return tuple(st[name]["mean"] for name, _ in launches)
 
 
 def roofline(bound, achieved, peak, unit, traffic=None):
@@ -178,31 +224,69 @@ def bench_main(args):
     wall = time.perf_counter() - t0
     assert int(w["err"].item()) == 0
     ms_step = wall * 1e3 / args.steps
-    # per-kernel durations: the same steps again with the launch queue filled ahead
-    # (a short device spin first), so that host time between an event and its launch
-    # never shows up as kernel time
+    # per-kernel durations: the same steps again, one event pair per launch with the
+    # launch queue filled ahead (a short device spin first)
     st_, pool_ = w["st"], w["pool"]
-    b_ms, c_ms = kernel_pass((
+    ks = launch_stats((
         ("build", lambda: hp.build_segment(hp.GDN, st_.k, st_.v, st_.log_alpha, w["offs"], pool_, w["slots"],
                                            beta=st_.beta, err_flag=w["err"])),
         ("compose", lambda: hp.compose_chain(pool_, w["chain_offs"], w["slots"], out_S=w["out_S"],
-                                             err_flag=w["err"]))), args.steps)
+                                             err_flag=w["err"]))), max(args.steps, 10))
+    b_ms, c_ms = ks["build"]["mean"], ks["compose"]["mean"]
     N, H, dk, dv, nseg = w["N"], w["H"], w["dk"], w["dv"], w["nseg"]
     flops = gdn_build_flops_per_token_head(dk, dv) * N * H
     bbytes = gdn_build_bytes(N, H, dk, dv, nseg)
     cbytes = compose_bytes([nseg], H, dk, dv)
-    log(f"main: {ms_step:.3f} ms/step wall; build {b_ms:.3f} ms, compose {c_ms:.3f} ms; "
-        f"build {flops / (b_ms * 1e-3) / 1e12:.1f} TFLOP/s, {bbytes / (b_ms * 1e-3) / 1e9:.0f} GB/s")
+    log(f"main: {ms_step:.3f} ms/step wall; build {b_ms:.3f} ms (p10 {ks['build']['p10']:.3f}, "
+        f"p90 {ks['build']['p90']:.3f}), compose {c_ms:.3f} ms; build {flops / (b_ms * 1e-3) / 1e12:.1f} TFLOP/s, "
+        f"{bbytes / (b_ms * 1e-3) / 1e9:.0f} GB/s")
     kern = {
-        "gdn_build": {"ms": b_ms, "algorithmic_flop": flops, "algorithmic_bytes": bbytes,
+        "gdn_build": {"ms": b_ms, "ms_stats": ks["build"], "algorithmic_flop": flops, "algorithmic_bytes": bbytes,
                       "tflops": flops / (b_ms * 1e-3) / 1e12, "gbps": bbytes / (b_ms * 1e-3) / 1e9,
                       "tokens_per_s": N / (b_ms * 1e-3)},
-        "gdn_compose_chain16": {"ms": c_ms, "algorithmic_bytes": cbytes, "gbps": cbytes / (c_ms * 1e-3) / 1e9,
-                                "compositions_per_s": nseg / (c_ms * 1e-3)},
+        "gdn_compose_chain16": {"ms": c_ms, "ms_stats": ks["compose"], "algorithmic_bytes": cbytes,
+                                "gbps": cbytes / (c_ms * 1e-3) / 1e9, "compositions_per_s": nseg / (c_ms * 1e-3)},
     }
-    del w
-    torch.cuda.empty_cache()
-    return ms_step, N, kern, flops, b_ms
+    return ms_step, N, kern, flops, b_ms, w
+
+
+def forward_bytes(N, H, dk, dv, nseg, o_bytes=2, records=False, kv_bytes=2):
+    """k, q, v (kv_bytes each), beta and log alpha (fp32), the outputs; plus the records."""
+    b = N * H * (kv_bytes * (2 * dk + dv) + 8 + o_bytes * dv)
+    if records:
+        b += nseg * H * 4 * (dk * dk + dk * dv + 1)
+    return b
+
+
+def bench_forward(args, w, build_ms):
+    """The main workload's chunked prefill forward (in-segment outputs, bf16 q and o)
+    alone and with the records as side-outputs; beside them the record build alone
+    (the main leg's kernel).  besthub article, paragraph 7: the records' one-time
+    construction costs a small fraction of a forward pass."""
+    st, pool = w["st"], w["pool"]
+    N, H, dk, dv, nseg = w["N"], w["H"], w["dk"], w["dv"], w["nseg"]
+    q = synth.keys(N, H, dk, torch.bfloat16, 3017, "cuda")
+    o = torch.empty((N, H, dv), dtype=torch.bfloat16, device="cuda")
+    fwd = lambda: hp.prefill_segment(hp.GDN, st.k, st.v, q, st.log_alpha, w["offs"], beta=st.beta, out=o)
+    fwd_rec = lambda: hp.prefill_segment(hp.GDN, st.k, st.v, q, st.log_alpha, w["offs"], beta=st.beta, out=o,
+                                         pool=pool, dst_slots=w["slots"])
+    for _ in range(max(1, args.warmup)):
+        fwd()
+        fwd_rec()
+    ks = launch_stats((("forward", fwd), ("forward_records", fwd_rec)), max(args.steps, 10))
+    f_ms, fr_ms = ks["forward"]["mean"], ks["forward_records"]["mean"]
+    fb = forward_bytes(N, H, dk, dv, nseg)
+    frb = forward_bytes(N, H, dk, dv, nseg, records=True)
+    log(f"forward: {f_ms:.3f} ms ({fb / (f_ms * 1e-3) / 1e9:.0f} GB/s), with records {fr_ms:.3f} ms "
+        f"(+{100 * (fr_ms / f_ms - 1):.1f} %), records alone {build_ms:.3f} ms")
+    del q, o
+    return {"workload": "gdn_prefill_forward_h32_d128_bf16_16x2048", "metric": "tokens/s",
+            "value": N / (f_ms * 1e-3), "unit": "tokens/s", "ms": f_ms, "ms_stats": ks["forward"],
+            "with_records": {"ms": fr_ms, "ms_stats": ks["forward_records"], "tokens_per_s": N / (fr_ms * 1e-3)},
+            "record_side_output_cost_frac": fr_ms / f_ms - 1.0,
+            "record_build_alone_frac": build_ms / f_ms,
+            "roofline": roofline("hbm", fb / (f_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s"),
+            "roofline_with_records": roofline("hbm", frb / (fr_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s")}
 
 
 def bench_compose_pool(args, slots=4096, H=32, d=128, R=64, m=32, seg_len=64, seed=401):
@@ -444,9 +528,21 @@ def hbm_attainable(gib=4):
     return out
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(seg_len=2048, H=32, d=128, nseg_sample=16, seed=301):
     """fp64 oracle on the host: build of nseg_sample of the main workload's 16
-    segments, all heads (the first nseg_sample segments' tokens, same seed)."""
+    segments, all heads (the first nseg_sample segments' tokens, same seed), on all
+    of the host's OpenMP threads; beside it smaller samples on one thread and a
+    compose sample (see cpu_detail)."""
     import oracle
     st = synth.gdn_stream([seg_len] * nseg_sample, H, d, d, torch.bfloat16, seed, 0.1, "cpu")
     k, v = st.k.double().numpy(), st.v.double().numpy()
@@ -455,9 +551,135 @@ def cpu_baseline(seg_len=2048, H=32, d=128, nseg_sample=16, seed=301):
     oracle.build_segments(oracle.GDN, k, v, la, st.seg_offsets, beta=b)
     dt = time.perf_counter() - t0
     toks = seg_len * nseg_sample
+    del k, v, b, la, st
     return {"value": toks / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"GDN build of {nseg_sample} x {seg_len}-token segment(s) x {H} heads, d={d}, "
-                      f"fp64 token-by-token recurrence ({dt:.1f} s wall on {oracle.num_threads()} threads)"}
+                      f"fp64 token-by-token recurrence ({dt:.1f} s wall on {oracle.num_threads()} threads)",
+            "detail": cpu_detail()}
+
+
+def cpu_detail(seed=901):
+    """Oracle samples of the other workloads: one thread (the build of the small GDN
+    workload, one 2048-token segment of the scalar and of the diagonal workload, one
+    32-record chain of the pool compose) and all threads (8 chains of the pool compose)."""
+    import oracle
+    out = {}
+    nthreads = oracle.num_threads()
+    rng = np.random.default_rng(seed)
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    def records(nslots, H, dk, dv):
+        q, _ = np.linalg.qr(rng.standard_normal((nslots, H, dk, dk)))
+        return (rng.uniform(-0.5, 0.0, size=(nslots, H)), 0.9 * q, rng.standard_normal((nslots, H, dk, dv)))
+
+    try:
+        oracle.set_num_threads(1)
+        st = synth.gdn_stream([256, 256], 1, 64, 64, torch.float32, 101, 0.1, "cpu")
+        dt = timed(lambda: oracle.build_segments(oracle.GDN, st.k.double().numpy(), st.v.double().numpy(),
+                                                 st.log_alpha.double().numpy(), st.seg_offsets,
+                                                 beta=st.beta.double().numpy()))
+        out["gdn_h1_d64_fp32_2x256_build_1thread"] = {"value": 512 / dt, "unit": "tokens/s", "s": dt}
+        N, H, D = 2048, 16, 128
+        k = synth.keys(N, H, D, torch.bfloat16, 2011, "cpu").double().numpy()
+        v = synth.values(N, H, D, torch.bfloat16, 2012, "cpu").double().numpy()
+        lg = synth.scalar_log_gamma(H, 2014, device="cpu").double().numpy()
+        dt = timed(lambda: oracle.build_segments(oracle.SCALAR, k, v, np.broadcast_to(lg, (N, H)).copy(), [0, N]))
+        out["scalar_h16_d128_1x2048_build_1thread"] = {"value": N / dt, "unit": "tokens/s", "s": dt}
+        lgd = synth.diagonal_log_gates(N, H, D, 2014, device="cpu").double().numpy()
+        dt = timed(lambda: oracle.build_segments(oracle.DIAGONAL, k, v, lgd, [0, N]))
+        out["diagonal_h16_d128_1x2048_build_1thread"] = {"value": N / dt, "unit": "tokens/s", "s": dt}
+        del k, v, lgd
+        ell, P, S = records(32, 32, 128, 128)
+        ids = np.arange(32, dtype=np.int32)
+        dt = timed(lambda: oracle.compose(oracle.GDN, ell, P, S, [0, 32], ids))
+        out["gdn_compose_h32_d128_1x32_1thread"] = {"value": 32 / dt, "unit": "compositions/s", "s": dt,
+                                                    "note": "all 32 heads per composition, as the GPU counts"}
+    finally:
+        oracle.set_num_threads(nthreads)
+    ids = rng.integers(0, 32, size=8 * 32).astype(np.int32)
+    dt = timed(lambda: oracle.compose(oracle.GDN, ell, P, S, np.arange(0, 8 * 32 + 1, 32), ids))
+    out["gdn_compose_h32_d128_8x32"] = {"value": 8 * 32 / dt, "unit": "compositions/s", "s": dt,
+                                        "threads": nthreads}
+    log("cpu detail: " + ", ".join(f"{k_} {v_['value']:.3g} {v_['unit']}" for k_, v_ in out.items()))
+    return out
+
+
+def measured_peaks():
+    """What this machine delivers: a streaming read of 4 GiB and a loop of bf16 32x32x16
+    matrix-core products on every SIMD (libhypic_peaks.so)."""
+    from hybrid_prefill_amd import _build
+    L = ctypes.CDLL(_build.PEAKS_LIB)
+    L.hypic_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    L.hypic_peak_mfma.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    buf = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1 << 20, dtype=torch.float32, device="cuda")
+    nbytes = buf.numel() * 4
+    blocks = 256 * 16
+    rd = lambda: L.hypic_peak_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(), stream)
+    iters, mblocks = 512, 256 * 4
+    mf = lambda: L.hypic_peak_mfma(iters, mblocks, sink.data_ptr(), stream)
+    for _ in range(2):
+        assert rd() == 0 and mf() == 0
+    ks = launch_stats((("read", rd), ("mfma", mf)), 8)
+    flop = iters * 4 * 32768.0 * mblocks * 4
+    out = {"read_gbps": nbytes / (ks["read"]["p50"] * 1e-3) / 1e9, "read_ms": ks["read"],
+           "bf16_mfma_tflops": flop / (ks["mfma"]["p50"] * 1e-3) / 1e12, "mfma_ms": ks["mfma"]}
+    del buf, sink
+    torch.cuda.empty_cache()
+    log(f"measured peaks: read {out['read_gbps']:.0f} GB/s, bf16 MFMA {out['bf16_mfma_tflops']:.0f} TFLOP/s")
+    return out
+
+
+def summarize_traffic(fetch_csv, write_csv, out_md, kernel="gdn_build_mfma_kernel", grid=262144,
+                      sources=GDN_BUILD_SOURCES, title="GDN build, H=32, d=128, bf16, 16 x 2048 tokens",
+                      algorithmic=None):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, with --calib-copy)
+    into the committed summary: each counter scaled by what it reads for the 1 GiB
+    device copy in the same process, per launch of `kernel` at `grid`, with the hash
+    of the kernel's sources."""
+    def per_dispatch(path, name, gsize, first=False):
+        rows = sorted((int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in csv.DictReader(open(path))
+                      if name in r["Kernel_Name"] and int(r["Grid_Size"]) == gsize)
+        if first:                    # the calibration copy is the process's first device copy
+            return rows[0][1], 1
+        vals = [v for _, v in rows]
+        return float(np.median(vals)) if vals else float("nan"), len(vals)
+
+    copy_bytes = float(1 << 30)
+    f_copy, _ = per_dispatch(fetch_csv, "__amd_rocclr_copyBuffer", 131072, first=True)
+    w_copy, _ = per_dispatch(write_csv, "__amd_rocclr_copyBuffer", 131072, first=True)
+    f_k, nf = per_dispatch(fetch_csv, kernel, grid)
+    w_k, nw = per_dispatch(write_csv, kernel, grid)
+    sf, sw = copy_bytes / (f_copy * 1024), copy_bytes / (w_copy * 1024)
+    rd, wr = f_k * 1024 * sf, w_k * 1024 * sw
+    lines = [f"# HBM traffic -- {title}", "",
+             "Two rocprofv3 passes, one counter each (FETCH_SIZE, then WRITE_SIZE), over the default-size "
+             "main leg of the benchmark with one untimed 1 GiB device copy as calibration:", "",
+             "```",
+             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch "
+             "-o fetch -- python $REPO/bench.py --only main --steps 2 --warmup 1 --no-cpu --calib-copy",
+             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write "
+             "-o write -- python $REPO/bench.py --only main --steps 2 --warmup 1 --no-cpu --calib-copy",
+             f"python $REPO/bench.py --summarize-traffic fetch_counter_collection.csv write_counter_collection.csv <this file>",
+             "```", "",
+             "| counter | copy kernel (KiB) | copy bytes (KiB) | scale | kernel per launch (KiB, median) | launches | scaled |",
+             "|---|---|---|---|---|---|---|",
+             f"| FETCH_SIZE | {f_copy:.0f} | {copy_bytes / 1024:.0f} | {sf:.3f} | {f_k:.0f} | {nf} | {rd / 1e6:.1f} MB |",
+             f"| WRITE_SIZE | {w_copy:.0f} | {copy_bytes / 1024:.0f} | {sw:.3f} | {w_k:.0f} | {nw} | {wr / 1e6:.1f} MB |",
+             "",
+             f"HBM bytes per launch: {(rd + wr) / 1e6:.1f} MB"
+             + (f" (algorithmic {algorithmic / 1e6:.1f} MB: {(rd + wr) / algorithmic:.2f}x)" if algorithmic else ""),
+             "",
+             f"kernel source sha256[:16]: `{source_sha(sources)}` ({', '.join(sources)})", ""]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
 
 
 def main():
@@ -465,12 +687,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["all", "main", "sd", "compose", "rag", "convexact", "kda"], default="all",
-                    help="main: only the headline GDN step; sd / compose / rag / convexact / kda: it plus that leg")
+    ap.add_argument("--only", choices=["all", "main", "forward", "sd", "compose", "rag", "convexact", "kda", "peaks"],
+                    default="all", help="main: only the headline GDN step; otherwise it plus that leg")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one untimed 1 GiB device copy (reference kernel for HBM byte counters)")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
+                    help="write the HBM-traffic summary of the GDN build from two rocprofv3 counter runs")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        N, H, d, nseg = 16 * 2048, 32, 128, 16
+        summarize_traffic(*args.summarize_traffic, algorithmic=gdn_build_bytes(N, H, d, d, nseg))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 (the path shards by "
               "(segment, head) with no collective, see the design notes)", file=sys.stderr)
@@ -486,9 +714,13 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    ms_step, N, kern, flops, b_ms = bench_main(args)
-    traffic = TRAFFIC_GDN_BUILD
+    ms_step, N, kern, flops, b_ms, w = bench_main(args)
+    traffic = committed_traffic()
     secondary = []
+    if args.only in ("all", "forward"):
+        secondary.append(bench_forward(args, w, b_ms))
+    del w
+    torch.cuda.empty_cache()
     if args.only in ("all", "compose"):
         secondary.append(bench_compose_pool(args))
     if args.only in ("all", "sd"):
@@ -500,7 +732,11 @@ def main():
     if args.only in ("all", "kda"):
         secondary.append(bench_kda(args))
     attainable = hbm_attainable()
+    peaks = measured_peaks() if args.only in ("all", "peaks", "main") else None
     cpu = None if args.no_cpu else cpu_baseline()
+    achieved = flops / (b_ms * 1e-3) / 1e12
+    if peaks:
+        peaks["gdn_build_frac_of_measured_mfma"] = achieved / peaks["bf16_mfma_tflops"]
     line = {
         "metric": METRIC,
         "value": N / (ms_step * 1e-3),
@@ -512,11 +748,12 @@ def main():
         "config": {"workload": "gdn_build_compose_h32_d128_bf16_16x2048",
                    "heads": 32, "d_k": 128, "d_v": 128, "segments": 16, "segment_tokens": 2048,
                    "kv_dtype": "bf16", "record_dtype": "fp32", "parallelism": "none (1 GPU)"},
-        "roofline": roofline("mfma", flops / (b_ms * 1e-3) / 1e12, PEAK_BF16 / 1e12, "TFLOP/s", traffic),
+        "roofline": roofline("mfma", achieved, PEAK_BF16 / 1e12, "TFLOP/s", traffic),
         "cpu_baseline": cpu,
         "kernels": kern,
         "secondary": secondary,
         "hbm_attainable": attainable,
+        "measured_peaks": peaks,
     }
     print(json.dumps(line), flush=True)
 
