@@ -29,7 +29,8 @@ times the fp64 oracle on a bounded sample on the host.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--only main|forward|sd|compose|rag|convexact|kda|peaks] [--no-cpu]
-       python bench.py --summarize-traffic FETCH_CSV WRITE_CSV OUT_MD  (rocprofv3 counter CSVs -> summary)
+       python bench.py --summarize-traffic FETCH_CSV WRITE_CSV OUT_DIR  (rocprofv3 counter CSVs -> summaries)
+       python bench.py --summarize-mfma CSV OUT_MD
 """
 from __future__ import annotations
 
@@ -58,12 +59,39 @@ PEAK_BF16 = 2.5e15           # FLOP/s dense bf16 MFMA
 PEAK_FP32 = 157.3e12         # FLOP/s fp32 (matrix and vector, published)
 CHUNK = 64
 CSRC = os.path.join(ROOT, "hybrid_prefill_amd", "csrc")
-# The GDN build's HBM bytes per launch come from a committed rocprofv3 counter summary
-# (FETCH_SIZE and WRITE_SIZE, scaled by what the counters read for a copy of known
-# size).  The summary records a hash of the kernel's sources; when the sources have
-# changed since, the bytes are unknown (null) until the counters are taken again.
-GDN_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gdn_build_h32_d128_16x2048_traffic.md")
-GDN_BUILD_SOURCES = ("build_mfma.hip", "gdn_mfma_common.h", "hypic_internal.h")
+# HBM bytes per launch of each timed kernel come from committed rocprofv3 counter
+# summaries (FETCH_SIZE and WRITE_SIZE, scaled by what the counters read for a device
+# copy of known size in the same process).  Each summary records a hash of the
+# kernel's sources; when they have changed since, the bytes are unknown (null) until
+# the counters are taken again.  key -> (kernel name fragment, grid in threads as the
+# counter CSV reports it (None: any), sources, workload)
+_GDN_SRC = ("build_mfma.hip", "gdn_mfma_common.h", "hypic_internal.h")
+_FWD_SRC = ("build_fwd_mfma.hip", "gdn_mfma_common.h", "hypic_internal.h")
+_CMP_SRC = ("compose_mfma.hip", "hypic_internal.h")
+_SD_SRC = ("build_sd_mfma.hip", "hypic_internal.h")
+TRAFFIC_KERNELS = {
+    "gdn_build_h32_d128_16x2048": ("gdn_build_mfma_kernel(", 262144, _GDN_SRC,
+                                   "GDN build, H=32, d=128, bf16, 16 x 2048 tokens"),
+    "gdn_compose_h32_d128_chain16": ("compose_sliced_mfma_kernel", 32768, _CMP_SRC,
+                                     "GDN compose of the 16-segment chain, H=32, d=128, fp32 records"),
+    "gdn_forward_h32_d128_16x2048": ("gdn_chunk_mfma_kernel<false, true>", 262144, _FWD_SRC,
+                                     "GDN prefill forward, outputs only, H=32, d=128, bf16, 16 x 2048 tokens"),
+    "gdn_forward_records_h32_d128_16x2048": ("gdn_chunk_mfma_kernel<true, true>", 393216, _FWD_SRC,
+                                             "GDN prefill forward with record side-outputs, H=32, d=128, bf16, "
+                                             "16 x 2048 tokens"),
+    "gdn_compose_pool4096_h32_d128_64x32": ("compose_dense_mfma_kernel<false, false>", 524288, _CMP_SRC,
+                                            "GDN compose, 4096-slot pool, 64 requests x 32 slots, H=32, d=128"),
+    "scalar_build_h16_d128_8x2048": ("sd_build_mfma_kernel<0, 2>", 131072, _SD_SRC,
+                                     "scalar-decay build, H=16, d=128, bf16, 8 x 2048 tokens"),
+    "diagonal_build_h16_d128_8x2048": ("sd_build_mfma_kernel<1, 2>", 131072, _SD_SRC,
+                                       "diagonal-gate build, H=16, d=128, bf16, 8 x 2048 tokens"),
+    "conv_warmup_rag_8305x4096_k4": ("conv_warmup_vec_kernel", None, ("conv_warmup.hip", "hypic_internal.h"),
+                                     "conv warm-up of the RAG mix, 8305 boundaries x 4096 channels, kernel 4, bf16"),
+    "gdn_build_rag_cold_2584seg": ("gdn_build_mfma_kernel(", 42336256, _GDN_SRC,
+                                   "GDN build of the RAG mix's 2584 cold segments (128-1024 tokens), H=32, d=128"),
+    "gdn_compose_rag_128req": ("compose_dense_mfma_kernel<false, false>", 1048576, _CMP_SRC,
+                               "GDN compose of the RAG mix's 128 chains (24-96 slots), H=32, d=128"),
+}
 
 
 def source_sha(names) -> str:
@@ -74,16 +102,22 @@ def source_sha(names) -> str:
     return h.hexdigest()[:16]
 
 
-def committed_traffic(profile=GDN_TRAFFIC_PROFILE, sources=GDN_BUILD_SOURCES):
+def traffic_profile(key) -> str:
+    return os.path.join(ROOT, "profiles", f"{key}_traffic.md")
+
+
+def committed_traffic(key="gdn_build_h32_d128_16x2048"):
     """HBM bytes per launch from the committed counter summary, or None when it is
     missing or the kernel's sources changed since it was taken."""
+    if key not in TRAFFIC_KERNELS:
+        return None
     try:
-        text = open(profile).read()
+        text = open(traffic_profile(key)).read()
     except OSError:
         return None
     m_sha = re.search(r"kernel source sha256\[:16\]: `([0-9a-f]{16})`", text)
     m_tot = re.search(r"HBM bytes per launch: ([0-9.]+) MB", text)
-    if not (m_sha and m_tot) or m_sha.group(1) != source_sha(sources):
+    if not (m_sha and m_tot) or m_sha.group(1) != source_sha(TRAFFIC_KERNELS[key][2]):
         return None
     return float(m_tot.group(1)) * 1e6
 
@@ -245,7 +279,8 @@ def bench_main(args):
                       "tflops": flops / (b_ms * 1e-3) / 1e12, "gbps": bbytes / (b_ms * 1e-3) / 1e9,
                       "tokens_per_s": N / (b_ms * 1e-3)},
         "gdn_compose_chain16": {"ms": c_ms, "ms_stats": ks["compose"], "algorithmic_bytes": cbytes,
-                                "gbps": cbytes / (c_ms * 1e-3) / 1e9, "compositions_per_s": nseg / (c_ms * 1e-3)},
+                                "gbps": cbytes / (c_ms * 1e-3) / 1e9, "compositions_per_s": nseg / (c_ms * 1e-3),
+                                "traffic": committed_traffic("gdn_compose_h32_d128_chain16")},
     }
     return ms_step, N, kern, flops, b_ms, w
 
@@ -285,8 +320,10 @@ def bench_forward(args, w, build_ms):
             "with_records": {"ms": fr_ms, "ms_stats": ks["forward_records"], "tokens_per_s": N / (fr_ms * 1e-3)},
             "record_side_output_cost_frac": fr_ms / f_ms - 1.0,
             "record_build_alone_frac": build_ms / f_ms,
-            "roofline": roofline("hbm", fb / (f_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s"),
-            "roofline_with_records": roofline("hbm", frb / (fr_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s")}
+            "roofline": roofline("hbm", fb / (f_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s",
+                                  committed_traffic("gdn_forward_h32_d128_16x2048")),
+            "roofline_with_records": roofline("hbm", frb / (fr_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s",
+                                               committed_traffic("gdn_forward_records_h32_d128_16x2048"))}
 
 
 def bench_compose_pool(args, slots=4096, H=32, d=128, R=64, m=32, seg_len=64, seed=401):
@@ -315,7 +352,8 @@ def bench_compose_pool(args, slots=4096, H=32, d=128, R=64, m=32, seg_len=64, se
     torch.cuda.empty_cache()
     return {"workload": f"gdn_compose_pool{slots}_h{H}_d{d}_{R}x{m}", "metric": "compositions/s",
             "value": comps / (ms * 1e-3), "unit": "compositions/s", "ms": ms,
-            "roofline": roofline("hbm", nbytes / (ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s")}
+            "roofline": roofline("hbm", nbytes / (ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s",
+                                  committed_traffic(f"gdn_compose_pool{slots}_h{H}_d{d}_{R}x{m}"))}
 
 
 def bench_sd(args, H=16, d=128, nseg=8, seg_len=2048, seed=201, copies=3):
@@ -350,13 +388,31 @@ def bench_sd(args, H=16, d=128, nseg=8, seg_len=2048, seed=201, copies=3):
         log(f"{name}: build {b_ms:.3f} ms ({nb / (b_ms * 1e-3) / 1e9:.0f} GB/s), compose {c_ms:.3f} ms")
         out.append({"workload": f"{name}_build_h{H}_d{d}_{nseg}x{seg_len}", "metric": "tokens/s",
                     "value": N / (b_ms * 1e-3), "unit": "tokens/s", "ms": b_ms, "compose_ms": c_ms,
-                    "roofline": roofline("hbm", nb / (b_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s")})
+                    "roofline": roofline("hbm", nb / (b_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s",
+                                          committed_traffic(f"{name}_build_h{H}_d{d}_{nseg}x{seg_len}"))})
         del las, pool
     return out
 
 
 def conv_bytes(B, C, K, x_bytes=2):
     return B * (2 * (K - 1) * C * x_bytes + (K - 1) * C * 4) + C * K * 4
+
+
+def rag_chains(plan, R, pool_slots):
+    """Slot chains of the RAG mix: cached positions name their pool slot, cold ones
+    a fresh slot after the pool (cold_len: {slot: tokens})."""
+    chains, cold_len, j = [], {}, 0
+    for r in range(R):
+        ch = []
+        for pos in range(plan.chain_lengths[r]):
+            if plan.is_cached[r][pos]:
+                ch.append(int(plan.cached_slot[r][pos]))
+            else:
+                cold_len[pool_slots + j] = int(plan.cold_lengths[j])
+                ch.append(pool_slots + j)
+                j += 1
+        chains.append(np.asarray(ch, dtype=np.int32))
+    return chains, cold_len
 
 
 def bench_rag(args, R=128, pool_slots=4096, H=32, d=128, C=4096, K=4, seed=501):
@@ -373,17 +429,7 @@ def bench_rag(args, R=128, pool_slots=4096, H=32, d=128, C=4096, K=4, seed=501):
         hp.build_segment(hp.GDN, st.k, st.v, st.log_alpha, torch.as_tensor(st.seg_offsets).cuda(), pool,
                          torch.arange(b0, b0 + len(lens), dtype=torch.int32, device="cuda"), beta=st.beta)
         del st
-    chains, cold_len, j = [], {}, 0
-    for r in range(R):
-        ch = []
-        for pos in range(plan.chain_lengths[r]):
-            if plan.is_cached[r][pos]:
-                ch.append(int(plan.cached_slot[r][pos]))
-            else:
-                cold_len[pool_slots + j] = int(plan.cold_lengths[j])
-                ch.append(pool_slots + j)
-                j += 1
-        chains.append(np.asarray(ch, dtype=np.int32))
+    chains, cold_len = rag_chains(plan, R, pool_slots)
     step = rag.plan_step(chains, cold_len)
     sorted_lens = sorted(cold_len.values(), reverse=True)
     cold = synth.gdn_stream(sorted_lens, H, d, d, torch.bfloat16, seed * 1000 + 999, 0.1, "cuda")
@@ -422,11 +468,13 @@ def bench_rag(args, R=128, pool_slots=4096, H=32, d=128, C=4096, K=4, seed=501):
             "compositions": step.n_compositions, "boundaries": int(step.tail_index.numel()),
             "kernels": {
                 "gdn_build": {"ms": b_ms, "roofline": roofline("mfma", bflops / (b_ms * 1e-3) / 1e12, PEAK_BF16 / 1e12,
-                                                                "TFLOP/s")},
+                                                                "TFLOP/s", committed_traffic("gdn_build_rag_cold_2584seg")),
+                              "hbm_gbps": bbytes / (b_ms * 1e-3) / 1e9},
                 "conv_warmup": {"ms": v_ms, "roofline": roofline("hbm", vbytes / (v_ms * 1e-3) / 1e9, PEAK_HBM / 1e9,
-                                                                 "GB/s")},
+                                                                 "GB/s", committed_traffic("conv_warmup_rag_8305x4096_k4"))},
                 "compose": {"ms": c_ms, "compositions_per_s": step.n_compositions / (c_ms * 1e-3),
-                            "roofline": roofline("hbm", cbytes / (c_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s")}}}
+                            "roofline": roofline("hbm", cbytes / (c_ms * 1e-3) / 1e9, PEAK_HBM / 1e9, "GB/s",
+                                                 committed_traffic("gdn_compose_rag_128req"))}}}
 
 
 def bench_conv_exact(args, R=32, pool_segs=512, H=32, d=128, K=4, seed=601):
@@ -636,47 +684,146 @@ def measured_peaks():
     return out
 
 
-def summarize_traffic(fetch_csv, write_csv, out_md, kernel="gdn_build_mfma_kernel", grid=262144,
-                      sources=GDN_BUILD_SOURCES, title="GDN build, H=32, d=128, bf16, 16 x 2048 tokens",
-                      algorithmic=None):
-    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, with --calib-copy)
-    into the committed summary: each counter scaled by what it reads for the 1 GiB
-    device copy in the same process, per launch of `kernel` at `grid`, with the hash
-    of the kernel's sources."""
-    def per_dispatch(path, name, gsize, first=False):
-        rows = sorted((int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in csv.DictReader(open(path))
-                      if name in r["Kernel_Name"] and int(r["Grid_Size"]) == gsize)
-        if first:                    # the calibration copy is the process's first device copy
-            return rows[0][1], 1
-        vals = [v for _, v in rows]
-        return float(np.median(vals)) if vals else float("nan"), len(vals)
+def algorithmic_bytes(key):
+    """Algorithmic HBM bytes per launch of a TRAFFIC_KERNELS entry (the RAG mix's
+    sizes come from its seeded plan, rebuilt on the host)."""
+    N, H, d = 16 * 2048, 32, 128
+    table = {
+        "gdn_build_h32_d128_16x2048": lambda: gdn_build_bytes(N, H, d, d, 16),
+        "gdn_compose_h32_d128_chain16": lambda: compose_bytes([16], H, d, d),
+        "gdn_forward_h32_d128_16x2048": lambda: forward_bytes(N, H, d, d, 16),
+        "gdn_forward_records_h32_d128_16x2048": lambda: forward_bytes(N, H, d, d, 16, records=True),
+        "gdn_compose_pool4096_h32_d128_64x32": lambda: compose_bytes([32] * 64, H, d, d),
+        "scalar_build_h16_d128_8x2048": lambda: sd_build_bytes(hp.SCALAR, 8 * 2048, 16, d, d, 8),
+        "diagonal_build_h16_d128_8x2048": lambda: sd_build_bytes(hp.DIAGONAL, 8 * 2048, 16, d, d, 8),
+        "conv_warmup_rag_8305x4096_k4": lambda: conv_bytes(8305, 4096, 4),
+    }
+    if key in table:
+        return table[key]()
+    if key in ("gdn_build_rag_cold_2584seg", "gdn_compose_rag_128req"):
+        from hybrid_prefill_amd import rag
+        R, pool_slots = 128, 4096
+        chains, cold_len = rag_chains(synth.rag_plan(R, pool_slots, 501), R, pool_slots)
+        step = rag.plan_step(chains, cold_len, device="cpu")
+        if key.startswith("gdn_build"):
+            return gdn_build_bytes(step.n_cold_tokens, H, d, d, len(cold_len))
+        return compose_bytes([len(c) for c in chains], H, d, d)
+    return None
+
+
+COUNTER_RUN = ("python $REPO/bench.py --steps 2 --warmup 1 --no-cpu --calib-copy")
+
+
+def summarize_traffic(fetch_csv, write_csv, out_dir):
+    """Turn two rocprofv3 --pmc runs of the benchmark (FETCH_SIZE, then WRITE_SIZE, with
+    --calib-copy) into one committed summary per timed kernel: each counter scaled by
+    what it reads for the 1 GiB device copy in the same process (the process's first
+    copy), the median over that kernel's launches at its grid, and the hash of its
+    sources."""
+    def load(path):
+        return sorted(((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"]))
+                       for r in csv.DictReader(open(path))), key=lambda t: t[0])
+
+    F, W = load(fetch_csv), load(write_csv)
+
+    def first_copy(rows):
+        return next(v for _, n, g, v in rows if "__amd_rocclr_copyBuffer" in n and g == 131072)
+
+    def per_launch(rows, frag, grid):
+        vals = [v for _, n, g, v in rows if frag in n and (grid is None or g == grid)]
+        return (float(np.median(vals)) if vals else None), len(vals)
 
     copy_bytes = float(1 << 30)
-    f_copy, _ = per_dispatch(fetch_csv, "__amd_rocclr_copyBuffer", 131072, first=True)
-    w_copy, _ = per_dispatch(write_csv, "__amd_rocclr_copyBuffer", 131072, first=True)
-    f_k, nf = per_dispatch(fetch_csv, kernel, grid)
-    w_k, nw = per_dispatch(write_csv, kernel, grid)
+    f_copy, w_copy = first_copy(F), first_copy(W)
     sf, sw = copy_bytes / (f_copy * 1024), copy_bytes / (w_copy * 1024)
-    rd, wr = f_k * 1024 * sf, w_k * 1024 * sw
-    lines = [f"# HBM traffic -- {title}", "",
-             "Two rocprofv3 passes, one counter each (FETCH_SIZE, then WRITE_SIZE), over the default-size "
-             "main leg of the benchmark with one untimed 1 GiB device copy as calibration:", "",
+    for key, (frag, grid, sources, title) in TRAFFIC_KERNELS.items():
+        f_k, nf = per_launch(F, frag, grid)
+        w_k, nw = per_launch(W, frag, grid)
+        if f_k is None or w_k is None:
+            log(f"summarize-traffic: no launches of {frag} (grid {grid}); {key} skipped")
+            continue
+        rd, wr = f_k * 1024 * sf, w_k * 1024 * sw
+        alg = algorithmic_bytes(key)
+        lines = [f"# HBM traffic -- {title}", "",
+                 "Two rocprofv3 passes over the benchmark (all legs, no CPU leg), one counter each, with one "
+                 "untimed 1 GiB device copy first as calibration:", "",
+                 "```",
+                 "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
+                 f"-d $REPO/gpurun_out/pmc_fetch -o fetch -- {COUNTER_RUN}",
+                 "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv "
+                 f"-d $REPO/gpurun_out/pmc_write -o write -- {COUNTER_RUN}",
+                 "python $REPO/bench.py --summarize-traffic $REPO/gpurun_out/pmc_fetch/fetch_counter_collection.csv "
+                 "$REPO/gpurun_out/pmc_write/write_counter_collection.csv $REPO/profiles",
+                 "```", "",
+                 f"Kernel `{frag.rstrip('(')}`" + (f", grid {grid} threads" if grid else "") + ".", "",
+                 "| counter | copy kernel (KiB) | copy bytes (KiB) | scale | kernel per launch (KiB, median) "
+                 "| launches | scaled |",
+                 "|---|---|---|---|---|---|---|",
+                 f"| FETCH_SIZE | {f_copy:.0f} | {copy_bytes / 1024:.0f} | {sf:.3f} | {f_k:.0f} | {nf} | "
+                 f"{rd / 1e6:.1f} MB |",
+                 f"| WRITE_SIZE | {w_copy:.0f} | {copy_bytes / 1024:.0f} | {sw:.3f} | {w_k:.0f} | {nw} | "
+                 f"{wr / 1e6:.1f} MB |",
+                 "",
+                 f"HBM bytes per launch: {(rd + wr) / 1e6:.1f} MB"
+                 + (f" (algorithmic {alg / 1e6:.1f} MB: {(rd + wr) / alg:.2f}x)" if alg else ""),
+                 "",
+                 f"kernel source sha256[:16]: `{source_sha(sources)}` ({', '.join(sources)})", ""]
+        with open(os.path.join(out_dir, f"{key}_traffic.md"), "w") as f:
+            f.write("\n".join(lines))
+        print(f"{key}: {(rd + wr) / 1e6:.1f} MB per launch" + (f" ({(rd + wr) / alg:.2f}x algorithmic)" if alg else ""))
+
+
+MFMA_KERNELS = {
+    "gdn_build_mfma_kernel(": (262144, "GDN build, main workload", "BF16"),
+    "gdn_chunk_mfma_kernel<false, true>": (262144, "GDN prefill forward, outputs only", "BF16"),
+    "gdn_chunk_mfma_kernel<true, true>": (393216, "GDN prefill forward with records", "BF16"),
+    "compose_sliced_mfma_kernel": (32768, "GDN compose, 16-segment chain", "BF16"),
+    "compose_dense_mfma_kernel<false, false>": (524288, "GDN compose, 4096-slot pool", "BF16"),
+    "sd_build_mfma_kernel<0, 2>": (131072, "scalar build", "BF16"),
+    "sd_build_mfma_kernel<1, 2>": (131072, "diagonal build", "BF16"),
+    "kda_chunk_mfma_kernel": (131072, "KDA build (fp32 matrix cores)", "F32"),
+}
+
+
+def summarize_mfma(csv_path, out_md):
+    """Matrix-core utilisation per kernel from one rocprofv3 --pmc run with
+    SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_BF16 and
+    SQ_INSTS_VALU_MFMA_MOPS_F32: busy fraction = busy cycles summed over the 1024
+    SIMDs / (1024 x GPU-active cycles per XCD); clock = GPU-active cycles per XCD
+    over the launch's duration; executed FLOP = MOPS x 512."""
+    disp = {}
+    for r in csv.DictReader(open(csv_path)):
+        d = disp.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
+                                               "dur": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    lines = ["# Matrix-core utilisation per kernel (bench workloads)", "",
+             "One rocprofv3 counter pass over the benchmark (all legs, no CPU leg):", "",
              "```",
-             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch "
-             "-o fetch -- python $REPO/bench.py --only main --steps 2 --warmup 1 --no-cpu --calib-copy",
-             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write "
-             "-o write -- python $REPO/bench.py --only main --steps 2 --warmup 1 --no-cpu --calib-copy",
-             f"python $REPO/bench.py --summarize-traffic fetch_counter_collection.csv write_counter_collection.csv <this file>",
+             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 --output-format csv -d $REPO/gpurun_out/pmc_mfma "
+             "-o mfma -- python $REPO/bench.py --steps 2 --warmup 1 --no-cpu",
+             "python $REPO/bench.py --summarize-mfma $REPO/gpurun_out/pmc_mfma/mfma_counter_collection.csv <this file>",
              "```", "",
-             "| counter | copy kernel (KiB) | copy bytes (KiB) | scale | kernel per launch (KiB, median) | launches | scaled |",
-             "|---|---|---|---|---|---|---|",
-             f"| FETCH_SIZE | {f_copy:.0f} | {copy_bytes / 1024:.0f} | {sf:.3f} | {f_k:.0f} | {nf} | {rd / 1e6:.1f} MB |",
-             f"| WRITE_SIZE | {w_copy:.0f} | {copy_bytes / 1024:.0f} | {sw:.3f} | {w_k:.0f} | {nw} | {wr / 1e6:.1f} MB |",
-             "",
-             f"HBM bytes per launch: {(rd + wr) / 1e6:.1f} MB"
-             + (f" (algorithmic {algorithmic / 1e6:.1f} MB: {(rd + wr) / algorithmic:.2f}x)" if algorithmic else ""),
-             "",
-             f"kernel source sha256[:16]: `{source_sha(sources)}` ({', '.join(sources)})", ""]
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs); clock = "
+             "(GRBM_GUI_ACTIVE / 8) / duration; executed TFLOP/s = MOPS x 512 / duration (counted at the "
+             "profiled launch's duration). For launches of a few tens of µs the GPU-active count also covers the "
+             "dispatch's set-up and drain, so their clock reads high.", "",
+             "| kernel | workload | grid | launches | µs (median) | clock GHz | MFMA busy | executed TFLOP/s | MOPS type |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for frag, (grid, title, ty) in MFMA_KERNELS.items():
+        ds = [d for d in disp.values() if frag in d["name"] and d["grid"] == grid and "GRBM_GUI_ACTIVE" in d]
+        if not ds:
+            continue
+        dur = float(np.median([d["dur"] for d in ds])) * 1e-9
+        grbm = float(np.median([d["GRBM_GUI_ACTIVE"] for d in ds])) / 8
+        busy = float(np.median([d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for d in ds])) / (1024 * grbm)
+        mops = float(np.median([d.get(f"SQ_INSTS_VALU_MFMA_MOPS_{ty}", 0.0) for d in ds]))
+        lines.append(f"| `{frag.rstrip('(')}` | {title} | {grid} | {len(ds)} | {dur * 1e6:.1f} | "
+                     f"{grbm / dur / 1e9:.2f} | {busy:.3f} | {mops * 512 / dur / 1e12:.1f} | {ty} |")
+    lines.append("")
+    srcs = sorted({n for v in TRAFFIC_KERNELS.values() for n in v[2]} | {"build_kda_mfma.hip"})
+    lines.append(f"sources sha256[:16]: `{source_sha(srcs)}` ({', '.join(srcs)})")
+    lines.append("")
     with open(out_md, "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
@@ -692,12 +839,16 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one untimed 1 GiB device copy (reference kernel for HBM byte counters)")
-    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
-                    help="write the HBM-traffic summary of the GDN build from two rocprofv3 counter runs")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_DIR"),
+                    help="write the HBM-traffic summaries of the timed kernels from two rocprofv3 counter runs")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("CSV", "OUT_MD"),
+                    help="write the matrix-core utilisation summary from one rocprofv3 counter run")
     args = ap.parse_args()
     if args.summarize_traffic:
-        N, H, d, nseg = 16 * 2048, 32, 128, 16
-        summarize_traffic(*args.summarize_traffic, algorithmic=gdn_build_bytes(N, H, d, d, nseg))
+        summarize_traffic(*args.summarize_traffic)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 (the path shards by "
