@@ -658,17 +658,19 @@ def cpu_detail(seed=901):
 
 
 def measured_peaks():
-    """What this machine delivers: a streaming read of 4 GiB and a loop of bf16 32x32x16
-    matrix-core products on every SIMD (libhypic_peaks.so)."""
+    """What this machine delivers: a streaming read of 4 GiB (16384 workgroups of 512
+    threads, non-temporal 16-byte loads: the best of a sweep over grid sizes, unroll
+    depths and cache policies) and a loop of bf16 32x32x16 matrix-core products on
+    every SIMD (libhypic_peaks.so)."""
     from hybrid_prefill_amd import _build
     L = ctypes.CDLL(_build.PEAKS_LIB)
     L.hypic_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     L.hypic_peak_mfma.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
-    buf = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    buf = torch.empty(1 << 30, dtype=torch.float32, device="cuda").uniform_()
     sink = torch.zeros(1 << 20, dtype=torch.float32, device="cuda")
     nbytes = buf.numel() * 4
-    blocks = 256 * 16
+    blocks = 256 * 64
     rd = lambda: L.hypic_peak_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(), stream)
     iters, mblocks = 512, 256 * 4
     mf = lambda: L.hypic_peak_mfma(iters, mblocks, sink.data_ptr(), stream)

@@ -55,7 +55,7 @@ enum { SYS_P = 0, SYS_S = 1 };
 // (A non-template helper with the LDS address space explicit: inside the kernel
 // template the LDS object's type depends on the template arguments.)
 __device__ __forceinline__ void load_lds16(const u16 *src, u16 *dst) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, kLoadNT);
 }
 
 template <bool WITH_P, bool WITH_O>

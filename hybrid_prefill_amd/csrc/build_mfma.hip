@@ -323,8 +323,8 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         const u16 *kc_ = kh + base_ * a.k_st, *vc_ = vh + base_ * a.v_st;                            \
         if (rem_ >= CH && small_st) {                                                                \
             _Pragma("unroll") for (int u_ = 0; u_ < 16; ++u_) {                                      \
-                __builtin_amdgcn_global_load_lds(kc_ + ko[u_], &sm.Km[BUF][4 * u_ * KML], 16, 0, 0);  \
-                __builtin_amdgcn_global_load_lds(vc_ + vo[u_], &sm.Vm[BUF][4 * u_ * KML], 16, 0, 0);  \
+                __builtin_amdgcn_global_load_lds(kc_ + ko[u_], &sm.Km[BUF][4 * u_ * KML], 16, 0, kLoadNT); \
+                __builtin_amdgcn_global_load_lds(vc_ + vo[u_], &sm.Vm[BUF][4 * u_ * KML], 16, 0, kLoadNT); \
             }                                                                                        \
         } else {                                                                                     \
             const int cl_ = rem_ < CH ? (int)rem_ : CH;                                              \
@@ -335,9 +335,9 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 const int t_ = 4 * u_ + r_, ts_ = t_ < cl_ ? t_ : cl_ - 1;                           \
                 const int g_ = p_ ^ (t_ & 15);                                                       \
                 __builtin_amdgcn_global_load_lds(kc_ + ts_ * a.k_st + 8 * g_,                        \
-                                                 &sm.Km[BUF][4 * u_ * KML], 16, 0, 0);               \
+                                                 &sm.Km[BUF][4 * u_ * KML], 16, 0, kLoadNT);         \
                 __builtin_amdgcn_global_load_lds(vc_ + ts_ * a.v_st + 8 * g_,                        \
-                                                 &sm.Vm[BUF][4 * u_ * KML], 16, 0, 0);               \
+                                                 &sm.Vm[BUF][4 * u_ * KML], 16, 0, kLoadNT);         \
             }                                                                                        \
         }                                                                                            \
     } while (0)

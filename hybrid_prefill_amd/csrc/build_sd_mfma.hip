@@ -97,29 +97,11 @@ __device__ __forceinline__ bf16x8 scale8(bf16x8 x, float4 f0, float4 f1) {
     return __builtin_convertvector(s, bf16x8);
 }
 
-// global_load_lds (lane i of the wave lands its bytes at dst + size * i), issued
-// through inline asm: the compiler then sees no LDS write in flight, so it puts
-// no s_waitcnt vmcnt(0) in front of every LDS read (which would wait for the
-// chunks still being prefetched); the kernel counts its own loads instead (every
-// wave issues the same number per chunk, and loads complete in issue order).
-__device__ __forceinline__ uint32_t lds_off(const void *p) {
-    return __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
-}
-__device__ __forceinline__ void gll16(const void *src, void *dst) {
-    uint32_t keep;     // m0 is the compiler's: restored after the load
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(keep)
-                 : "v"(src), "s"(lds_off(dst))
-                 : "memory");
-}
-__device__ __forceinline__ void gll4(const void *src, void *dst) {
-    uint32_t keep;     // m0 is the compiler's: restored after the load
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(keep)
-                 : "v"(src), "s"(lds_off(dst))
-                 : "memory");
-}
+// global_load_lds through inline asm (lds_dma16 / lds_dma4): the kernel counts its
+// own loads (every wave issues the same number per chunk, and loads complete in
+// issue order).
+__device__ __forceinline__ void gll16(const void *src, void *dst) { lds_dma16(src, dst); }
+__device__ __forceinline__ void gll4(const void *src, void *dst) { lds_dma4(src, dst); }
 
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");

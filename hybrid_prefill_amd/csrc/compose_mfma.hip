@@ -306,7 +306,7 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
         const int64_t frec = (int64_t)chain_slot(cs, c_lo, (CC)) * a.H + head;                \
         EL = chain_ell(cs, c_lo, (CC));                                                 \
         const float4 *fsrc = reinterpret_cast<const float4 *>(a.pool_P + frec * D * D);          \
-        _Pragma("unroll") for (int u = 0; u < 16; ++u) PF[u] = fsrc[th + NT * u];                \
+        _Pragma("unroll") for (int u = 0; u < 16; ++u) PF[u] = load_nt(fsrc + th + NT * u);     \
     } while (0)
 #define HYPIC_FETCH_S(CC)                                                                        \
     do {                                                                                         \
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
         const float4 *fss = reinterpret_cast<const float4 *>(a.pool_S + frec * D * D);           \
         _Pragma("unroll") for (int u = 0; u < 16; ++u)                                           \
             __builtin_amdgcn_global_load_lds(fss + (16 * w + u) * 64 + l,                        \
-                                             &s_stage[(16 * w + u) * 256], 16, 0, 0);               \
+                                             &s_stage[(16 * w + u) * 256], 16, 0, kLoadNT);         \
     } while (0)
     // one step: stage P_c from PF (then fetch P_{c+1} into PF), acc = P_c state,
     // state <- e^{ell_c} acc + S_c (S), or state <- acc (P)

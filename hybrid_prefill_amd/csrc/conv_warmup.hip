@@ -134,8 +134,8 @@ __global__ __launch_bounds__(NT) void conv_warmup_vec_kernel(ConvArgs a) {
         typename V::raw r[2 * K - 2];
 #pragma unroll
         for (int j = 0; j < K - 1; ++j) {
-            r[j] = *reinterpret_cast<const typename V::raw *>(tails + (ti * (K - 1) + j) * C + c0);
-            r[K - 1 + j] = *reinterpret_cast<const typename V::raw *>(heads + (hi * (K - 1) + j) * C + c0);
+            r[j] = load_nt(reinterpret_cast<const typename V::raw *>(tails + (ti * (K - 1) + j) * C + c0));
+            r[K - 1 + j] = load_nt(reinterpret_cast<const typename V::raw *>(heads + (hi * (K - 1) + j) * C + c0));
         }
         float xb[2 * K - 2][NV];
 #pragma unroll

@@ -3,8 +3,8 @@
 // kernel against the published MI355X peaks; these two kernels measure what this
 // box delivers under the same conditions, so that the fractions can also be read
 // against attainable rates:
-//   * a streaming read of a large buffer (16-byte loads, four in flight per thread,
-//     grid-stride), the attainable HBM read bandwidth;
+//   * a streaming read of a large buffer (16-byte non-temporal loads, four in flight
+//     per thread, grid-stride), the attainable HBM read bandwidth;
 //   * a loop of independent bf16 v_mfma_f32_32x32x16 products on register operands
 //     (four accumulator chains per wave, one wave per SIMD), the attainable dense
 //     bf16 matrix rate at the clock the chip holds under that load.
@@ -18,18 +18,19 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int NT = 256;
+constexpr int NT_READ = 512;
 
-__global__ __launch_bounds__(NT) void peak_read_kernel(const f32x4 *src, int64_t n4, float *sink) {
+__global__ __launch_bounds__(NT_READ) void peak_read_kernel(const f32x4 *src, int64_t n4, float *sink) {
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0, acc3 = acc0;
-    const int64_t stride = (int64_t)gridDim.x * NT;
-    int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * NT_READ;
+    int64_t i = (int64_t)blockIdx.x * NT_READ + threadIdx.x;
     for (; i + 3 * stride < n4; i += 4 * stride) {
-        acc0 += src[i];
-        acc1 += src[i + stride];
-        acc2 += src[i + 2 * stride];
-        acc3 += src[i + 3 * stride];
+        acc0 += __builtin_nontemporal_load(src + i);
+        acc1 += __builtin_nontemporal_load(src + i + stride);
+        acc2 += __builtin_nontemporal_load(src + i + 2 * stride);
+        acc3 += __builtin_nontemporal_load(src + i + 3 * stride);
     }
-    for (; i < n4; i += stride) acc0 += src[i];
+    for (; i < n4; i += stride) acc0 += __builtin_nontemporal_load(src + i);
     const f32x4 acc = acc0 + acc1 + acc2 + acc3;
     const float s = acc.x + acc.y + acc.z + acc.w;
     // a store that never happens for finite data keeps every load live
@@ -58,11 +59,11 @@ __global__ __launch_bounds__(NT) void peak_mfma_kernel(int64_t iters, float *sin
 
 extern "C" {
 
-// Streaming read of `bytes` (a multiple of 16) from `src`; sink: one float per block
-// (never written for finite data).  Returns 0, or -1 on a bad argument / launch error.
+// Streaming read of `bytes` (a multiple of 16) from `src` by `blocks` workgroups of
+// 512 threads; sink: one float per block (never written for finite data).  Returns 0, or -1 on a bad argument / launch error.
 int hypic_peak_read(const void *src, int64_t bytes, int32_t blocks, float *sink, void *stream) {
     if (!src || !sink || bytes <= 0 || (bytes & 15) || blocks <= 0) return -1;
-    hipLaunchKernelGGL(peak_read_kernel, dim3((unsigned)blocks), dim3(NT), 0, static_cast<hipStream_t>(stream),
+    hipLaunchKernelGGL(peak_read_kernel, dim3((unsigned)blocks), dim3(NT_READ), 0, static_cast<hipStream_t>(stream),
                        static_cast<const f32x4 *>(src), bytes / 16, sink);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
