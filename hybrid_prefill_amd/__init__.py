@@ -33,7 +33,9 @@ EFLAG_SLOT_OUT_OF_RANGE = 0x1
 EFLAG_BAD_OFFSETS = 0x2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhypic.so")
+# HYPIC_LIB names another build of the same library (the host-sanitized copy that the
+# sanitizer test loads); by default the in-tree libhypic.so
+LIB_PATH = os.environ.get("HYPIC_LIB") or os.path.join(_HERE, "libhypic.so")
 _lib = None
 
 

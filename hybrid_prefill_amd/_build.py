@@ -50,6 +50,39 @@ def _link(objs, out):
     os.replace(tmp, out)
 
 
+# Host-sanitized copy of the library for the CPU sanitizer test: the ABI translation
+# unit (argument validation, dispatch) is compiled with AddressSanitizer and
+# UndefinedBehaviorSanitizer on its host side only, and linked with the kernels'
+# ordinary objects.  A process loads it with clang's ASan runtime preloaded.
+SAN_LIB = os.path.join(HERE, "libhypic_san.so")
+SAN_FLAGS = ["-g", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-fsanitize=address",
+             "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    san_obj = os.path.join(OBJ_DIR, "hypic_abi_san.o")
+    cmd = [HIPCC, *FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, "hypic_abi.hip"), "-o", san_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed on hypic_abi.hip (sanitized)")
+    objs = [san_obj] + [os.path.join(OBJ_DIR, s.replace(".hip", ".o")) for s in SOURCES if s != "hypic_abi.hip"]
+    for o in objs[1:]:
+        if not os.path.exists(o):
+            raise RuntimeError(f"{o} is missing: run build() first")
+    tmp = SAN_LIB + ".tmp"
+    subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan",
+                    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                    *objs, "-o", tmp], check=True)
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print("built", SAN_LIB)
+    return SAN_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(PEAKS_SOURCES))) as ex:

@@ -41,24 +41,34 @@ SCALAR, DIAGONAL, GDN, KDA = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hypic_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_DEFAULT_LIB = os.path.join(_HERE, "liboracle.so")
+SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
+# HYPIC_ORACLE_LIB names another build of the oracle (the sanitized one, see build_library)
+_LIB_PATH = os.environ.get("HYPIC_ORACLE_LIB") or _DEFAULT_LIB
 _lib = None
 
 
-def build_library() -> str:
-    """Compile ``hypic_oracle.c`` with gcc (-O2, OpenMP) into ``oracle/liboracle.so``."""
-    tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+def build_library(sanitize: bool = False) -> str:
+    """Compile ``hypic_oracle.c`` with gcc (-O2, OpenMP) into ``oracle/liboracle.so``; with
+    sanitize, an AddressSanitizer + UndefinedBehaviorSanitizer build (abort on the first
+    report) into ``oracle/liboracle_san.so``, loaded by a process that preloads gcc's
+    libasan and libubsan."""
+    out = SAN_LIB if sanitize else _DEFAULT_LIB
+    tmp = out + ".tmp"
+    extra = ["-g", "-O1", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=undefined"] if sanitize else ["-O2"]
+    cmd = ["gcc", *extra, "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    if _LIB_PATH == _DEFAULT_LIB and (not os.path.exists(_LIB_PATH) or
+                                      os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
         build_library()
     lib = ctypes.CDLL(_LIB_PATH)
     d, i64, i32, ci = (ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
