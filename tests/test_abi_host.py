@@ -253,6 +253,37 @@ def test_build_segment_shape_checks():
             "pool.log_scale has shape")
 
 
+def test_prefill_segment_shape_checks():
+    """hypic_prefill_segment's binding: q and out against [N,H,d_k] / [N,H,d_v], q in
+    k's dtype, a pool needs dst_slots, and a call that computes nothing is refused, all
+    before any device work."""
+    N, H, d = 10, 2, 128
+    k = torch.zeros((N, H, d), dtype=torch.bfloat16)
+    v = torch.zeros((N, H, d), dtype=torch.bfloat16)
+    q = torch.zeros((N, H, d), dtype=torch.bfloat16)
+    la = torch.zeros((N, H))
+    offs = torch.tensor([0, 4, 10])
+    slots = torch.tensor([0, 1], dtype=torch.int32)
+    pool = hp.Pool.allocate(hp.GDN, 3, H, d, d, device="cpu")
+    ok = dict(family=hp.GDN, k=k, v=v, q=q, log_alpha=la, seg_offsets=offs)
+
+    def call(**kw):
+        return lambda: hp.prefill_segment(**dict(ok, **kw))
+
+    _raises(call(out=torch.zeros((N, H, d))), "on the GPU")                         # shapes fine
+    _raises(call(out=torch.zeros((N, H, d)), pool=pool, dst_slots=slots), "on the GPU")
+    _raises(call(q=torch.zeros((N, H + 1, d), dtype=torch.bfloat16)), "q has shape")
+    _raises(call(q=torch.zeros((N - 1, H, d), dtype=torch.bfloat16)), "q has shape")
+    _raises(call(q=torch.zeros((N, H, d))), "q must be")                            # fp32 q, bf16 k
+    _raises(call(q=None), "outputs need q")
+    _raises(call(out=torch.zeros((N, H, d + 1))), "out has shape")
+    _raises(call(out=torch.zeros((N, H, 2 * d))[:, :, ::2]), "unit channel stride")
+    _raises(call(pool=pool), "needs dst_slots")
+    _raises(call(pool=pool, dst_slots=torch.tensor([0], dtype=torch.int32)), "dst_slots has shape")
+    _raises(call(outputs=False), "nothing to compute")
+    _raises(call(out=torch.zeros((N, H, d)), err_flag=torch.zeros(1, dtype=torch.int64)), "err_flag")
+
+
 def test_compose_shape_checks():
     H, d, R = 2, 64, 3
     pool = hp.Pool.allocate(hp.GDN, 4, H, d, d, device="cpu")
