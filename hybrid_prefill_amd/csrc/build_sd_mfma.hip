@@ -101,6 +101,9 @@ __device__ __forceinline__ bf16x8 scale8(bf16x8 x, float4 f0, float4 f1) {
 // own loads (every wave issues the same number per chunk, and loads complete in
 // issue order).
 __device__ __forceinline__ void gll16(const void *src, void *dst) { lds_dma16(src, dst); }
+// an operand every split of the (segment, head) reads (scalar: the keys; diagonal: the
+// values): cached, so that the workgroups after the first find it in the XCD's L2
+__device__ __forceinline__ void gll16s(const void *src, void *dst) { lds_dma16_shared(src, dst); }
 __device__ __forceinline__ void gll4(const void *src, void *dst) { lds_dma4(src, dst); }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -278,6 +281,11 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     constexpr int VR = DIAG ? 4 : RPI, VG = DIAG ? 16 : GR, VW = DIAG ? D : 32 * NJB;
     auto kswz = [](int r, int g) { return DIAG ? g ^ ((r >> 1) & 7) : g ^ (r & 15); };
     auto vswz = [](int r, int g) { return DIAG ? g ^ (r & 15) : g ^ ((r >> VSH) & (GR - 1)); };
+    // the operand every split of a (segment, head) reads goes through the L2 (cached);
+    // the split's own operand and the gates are streamed (non-temporal)
+    constexpr bool SHARED_K = !DIAG && NSPLIT > 1, SHARED_V = DIAG;
+    auto gll16k = [](const void *src, void *dst) { if constexpr (SHARED_K) gll16s(src, dst); else gll16(src, dst); };
+    auto gll16v = [](const void *src, void *dst) { if constexpr (SHARED_V) gll16s(src, dst); else gll16(src, dst); };
     auto issue = [&](int64_t C, int lw, const uint32_t *ko, const uint32_t *vo, const uint32_t *go) {
         const int bi = (int)(C % NBUF);
         const int64_t base = C * CH, rem = n - base;
@@ -285,9 +293,9 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         if (rem >= CH && small_st) {
             const u16 *kc = kh + base * a.k_st, *vc = vh + base * a.v_st;
 #pragma unroll
-            for (int j = 0; j < NKI; ++j) gll16(kc + ko[j], &Bf.Km[KR * (lw + NLW * j) * KW]);
+            for (int j = 0; j < NKI; ++j) gll16k(kc + ko[j], &Bf.Km[KR * (lw + NLW * j) * KW]);
 #pragma unroll
-            for (int j = 0; j < NVI; ++j) gll16(vc + vo[j], &Bf.Vm[VR * (lw + NLW * j) * VW]);
+            for (int j = 0; j < NVI; ++j) gll16v(vc + vo[j], &Bf.Vm[VR * (lw + NLW * j) * VW]);
         } else {
             const int cl = rem < CH ? (int)rem : CH;
             int ll = l;
@@ -296,12 +304,12 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
 #pragma unroll
             for (int j = 0; j < NKI; ++j) {
                 const int u = lw + NLW * j, r = KR * u + ll / KG, rs = r < cl ? r : cl - 1;
-                gll16(kh + (base + rs) * a.k_st + 8 * kswz(r, ll % KG), &Bf.Km[KR * u * KW]);
+                gll16k(kh + (base + rs) * a.k_st + 8 * kswz(r, ll % KG), &Bf.Km[KR * u * KW]);
             }
 #pragma unroll
             for (int j = 0; j < NVI; ++j) {
                 const int u = lw + NLW * j, r = VR * u + ll / VG, rs = r < cl ? r : cl - 1;
-                gll16(vh + (base + rs) * a.v_st + 8 * vswz(r, ll % VG), &Bf.Vm[VR * u * VW]);
+                gll16v(vh + (base + rs) * a.v_st + 8 * vswz(r, ll % VG), &Bf.Vm[VR * u * VW]);
             }
         }
     };

@@ -124,6 +124,15 @@ __device__ __forceinline__ void lds_dma16(const void *src, void *dst) {
                  : "v"(src), "s"(lds_off(dst))
                  : "memory");
 }
+// the same without the non-temporal policy: for an operand that another workgroup of
+// the same XCD reads too, which should find it in the L2
+__device__ __forceinline__ void lds_dma16_shared(const void *src, void *dst) {
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep)
+                 : "v"(src), "s"(lds_off(dst))
+                 : "memory");
+}
 __device__ __forceinline__ void lds_dma4(const void *src, void *dst) {
     uint32_t keep;     // m0 is the compiler's: restored after the load
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off nt\n\ts_mov_b32 m0, %0"
