@@ -106,6 +106,11 @@ __device__ __forceinline__ void gll16(const void *src, void *dst) { lds_dma16(sr
 __device__ __forceinline__ void gll16s(const void *src, void *dst) { lds_dma16_shared(src, dst); }
 __device__ __forceinline__ void gll4(const void *src, void *dst) { lds_dma4(src, dst); }
 
+// a lane's value from another lane by a DPP control (gfx9 encoding), in registers
+template <int CTRL> __device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
@@ -425,6 +430,77 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         return G;
     };
 
+    // Diagonal family: the factors of chunk C for the workgroup key channels ch0 .. ch0 + 15,
+    // computed by compute wave w (ch0 = 16 w) one chunk ahead of their use.  Lane l takes
+    // channel ch0 + l / 4 and the tokens 16 (l % 4) .. + 15 (the channel's four lanes form
+    // a quad):
+    //   L_t (inclusive cumulative log decay of the channel), G = L_63,
+    //   fac[ci][t] = beta_t e^{G - L_t},  eg[ci] = e^G,
+    // written to the parity-C tiles; ell_acc collects the lane's log decays.  The gates
+    // were loaded by the loading waves, each of which waited for its own before the
+    // barrier that starts the chunk these factors are computed in.
+    auto factors16 = [&](int64_t C, int ch0, double &ell_acc) {
+        if constexpr (DIAG) {
+            const GateBuf &Bf = sm.gbuf[C % NBG];
+            const int64_t rem = n - C * CH;
+            const int cl = rem < CH ? (int)rem : CH;
+            const int cc = l >> 2, q4 = l & 3, ci = ch0 + cc, t0 = 16 * q4;
+            float x[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) x[j] = Bf.gate[gate_idx(t0 + j, ci)];
+            // the lane's sixteen betas, read before any factor is stored (the stores could
+            // alias them for all the compiler knows, which would serialise the reads)
+            float bt[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 b4 = *reinterpret_cast<const float4 *>(&Bf.beta[0][t0 + 4 * g]);
+                bt[4 * g] = b4.x; bt[4 * g + 1] = b4.y; bt[4 * g + 2] = b4.z; bt[4 * g + 3] = b4.w;
+            }
+            float run = 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                run += (t0 + j < cl && a.log_alpha) ? x[j] : 0.0f;
+                x[j] = run;
+            }
+            ell_acc += (double)run;
+            // over the quad, in registers: inclusive scan by lane shifts of 1 and 2, total
+            // by two pairwise exchanges
+            float incl = run;
+            {
+                const float y1 = dpp_f32<0x90>(incl);           // quad_perm [0, 0, 1, 2]
+                if (q4 >= 1) incl += y1;
+                const float y2 = dpp_f32<0x40>(incl);           // quad_perm [0, 0, 0, 1]
+                if (q4 >= 2) incl += y2;
+            }
+            float G = run + dpp_f32<0xB1>(run);                 // quad_perm [1, 0, 3, 2]
+            G += dpp_f32<0x4E>(G);                              // quad_perm [2, 3, 0, 1]
+            const float off = incl - run;
+            const int par = (int)(C & 1);
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                float f[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = t0 + 4 * gq + e;
+                    const float b = t < cl ? (a.beta ? bt[4 * gq + e] : 1.0f) : 0.0f;
+                    f[e] = b * __expf(G - (off + x[4 * gq + e]));
+                }
+                *reinterpret_cast<float4 *>(&sm.fac[par][fac_idx(ci, 4 * q4 + gq)]) = make_float4(f[0], f[1], f[2], f[3]);
+            }
+            if (q4 == 0) sm.eg[par][ci] = __expf(G);
+        }
+    };
+    // the record's ell of those channels: the sum of the channel's four lanes
+    auto write_ell16 = [&](double ell_acc, int ch0) {
+        if constexpr (DIAG) {
+            ell_acc += __shfl_xor(ell_acc, 1);
+            ell_acc += __shfl_xor(ell_acc, 2);
+            if ((l & 3) == 0)
+                a.pool_ell[((int64_t)slot * a.H + head) * D + kc0 + ch0 + (l >> 2)] =
+                    state == 2 ? __int_as_float(0x7fc00000) : (float)ell_acc;
+        }
+    };
+
     if (w >= NWC) {
         // ================= loading waves: the same barriers as the compute waves
         const int lw = w - NWC;
@@ -448,82 +524,27 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         if (!DIAG)
             for (int64_t c = 0; c < DIST && c < nc; ++c) issue(c, lw, ko, vo, go);
         if constexpr (DIAG) {
-            // The loading waves also compute every chunk's per-(token, channel) factors,
-            // one chunk ahead of the compute waves: wave lw takes channels
-            // ci = 16 lw + l % 16 of the workgroup's 64, lane quarter tq = l / 16 the tokens
-            // 16 tq .. 16 tq + 15 (only gates this wave loaded itself, so its own vmcnt
-            // wait is enough).  Per chunk C:
-            //   L_t (inclusive cumulative log decay of the channel), G = L_63,
-            //   fac[ci][t] = beta_t e^{G - L_t},  eg[ci] = e^G,
-            // written to the parity-C tiles before the barrier that starts chunk C.
-            const int cc = l & 15, tq = l >> 4, ci = 16 * lw + cc;
-            double ell_q = 0.0;                           // this lane's quarter of the channel's sum
-            auto factors = [&](int64_t C) {
-                const GateBuf &Bf = sm.gbuf[C % NBG];
-                const int64_t rem = n - C * CH;
-                const int cl = rem < CH ? (int)rem : CH;
-                float x[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) x[j] = Bf.gate[gate_idx(16 * tq + j, ci)];
-                float run = 0.f;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    run += (16 * tq + j < cl && a.log_alpha) ? x[j] : 0.0f;
-                    x[j] = run;
-                }
-                ell_q += (double)run;
-                const float q0 = __shfl(run, cc), q1 = __shfl(run, cc + 16), q2 = __shfl(run, cc + 32),
-                            q3 = __shfl(run, cc + 48);
-                const float off = (tq > 0 ? q0 : 0.f) + (tq > 1 ? q1 : 0.f) + (tq > 2 ? q2 : 0.f);
-                const float G = (q0 + q1) + (q2 + q3);
-                const int par = (int)(C & 1);
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    float f[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 16 * tq + 4 * gq + e;
-                        const float b = t < cl ? (a.beta ? Bf.beta[lw][t] : 1.0f) : 0.0f;
-                        f[e] = b * __expf(G - (off + x[4 * gq + e]));
-                    }
-                    *reinterpret_cast<float4 *>(&sm.fac[par][fac_idx(ci, 4 * tq + gq)]) =
-                        make_float4(f[0], f[1], f[2], f[3]);
-                }
-                if (tq == 0) sm.eg[par][ci] = __expf(G);
-            };
             // Issue order: "step" j >= -3 issues the gates of chunk j + 3, then the keys and
             // values of chunk j + 2 (those that exist); steps -3 .. -1 run before the loop,
-            // step c after the barrier of chunk c.  So at step c the gates of chunk c + 1
-            // (step c - 2) have two steps to land and the keys and values of chunk c + 1
-            // (step c - 1) one.  A wait names how many of this wave's loads were issued
-            // after the one it waits for.
+            // step c after the barrier of chunk c.  A wait names how many of this wave's
+            // loads were issued after the one it waits for.  Before the barrier that starts
+            // chunk c every loading wave has waited for its gates of chunk c + 1, which the
+            // compute waves turn into factors during chunk c.
             auto nG = [&](int64_t m) { return m < nc ? LPG : 0; };
             auto nKV = [&](int64_t m) { return m < nc ? LPW : 0; };
             for (int64_t j = -3; j < 0; ++j) {
                 if (j + 3 < nc) issue_g(j + 3, lw, go);
                 if (j + 2 >= 0 && j + 2 < nc) issue(j + 2, lw, ko, vo, go);
             }
-            if (nc > 0) {
-                vm_wait<2 * LPG + 3 * LPW>(nG(1) + nKV(0) + nG(2) + nKV(1));   // gates of chunk 0
-                factors(0);
-                vm_wait<2 * LPG + 3 * LPW>(nG(2) + nKV(1));                    // keys, values of chunk 0
-            }
+            vm_wait<2 * LPG + 3 * LPW>(nG(1) + nKV(0) + nG(2) + nKV(1));   // gates of chunk 0
+            lds_barrier();                                                  // ... visible to all
+            vm_wait<2 * LPG + 3 * LPW>(nG(2) + nKV(1));                    // gates 1, keys, values 0
             for (int64_t c = 0; c < nc; ++c) {
                 lds_barrier();                            // chunk c (and its factors) visible
                 if (c + 3 < nc) issue_g(c + 3, lw, go);
                 if (c + 2 < nc) issue(c + 2, lw, ko, vo, go);
-                if (c + 1 < nc) {
-                    vm_wait<2 * LPG + 3 * LPW>(nKV(c) + nG(c + 2) + nKV(c + 1) + nG(c + 3) + nKV(c + 2));
-                    factors(c + 1);                       // gates of chunk c + 1 landed
-                    vm_wait<2 * LPG + 3 * LPW>(nG(c + 3) + nKV(c + 2));   // keys, values of chunk c + 1
-                }
+                vm_wait<2 * LPG + 3 * LPW>(nG(c + 3) + nKV(c + 2));       // gates c + 2, keys, values c + 1
             }
-            // record: the channel's ell (sum of the lane quarters)
-            ell_q += __shfl_xor(ell_q, 16);
-            ell_q += __shfl_xor(ell_q, 32);
-            if (tq == 0)
-                a.pool_ell[((int64_t)slot * a.H + head) * D + kc0 + ci] =
-                    state == 2 ? __int_as_float(0x7fc00000) : (float)ell_q;
             return;
         }
         // make_table's two barriers (these waves have no tokens, and no load to wait for)
@@ -615,8 +636,11 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
             for (int64_t c = 0; c < nc; ++c) step(c, oa, oa);
         }
     } else {
-    // the loading waves computed the chunk's factors: decay, scale, multiply
+    // the chunk's factors (computed by these waves one chunk ahead): decay, scale, multiply
     const int i = 32 * (w >> 1) + l32;                // this lane's key channel (of the workgroup's 64)
+    double ell16 = 0.0;
+    lds_barrier();                                    // gates of chunk 0 visible
+    if (nc > 0) factors16(0, 16 * w, ell16);
     for (int64_t c = 0; c < nc; ++c) {
         lds_barrier();                                // chunk c and its factors visible; chunk c - 1's buffer free
         const SdBuf<DIAG, NJB> &B = sm.buf[c % NBUF];
@@ -653,7 +677,9 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb) st[jb] = mfma(ka, vb[ks][jb], st[jb]);
         }
+        if (c + 1 < nc) factors16(c + 1, 16 * w, ell16);
     }
+    write_ell16(ell16, 16 * w);
     }
     // ---- record
     const float nanv = __int_as_float(0x7fc00000);
