@@ -439,23 +439,31 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     // written to the parity-C tiles; ell_acc collects the lane's log decays.  The gates
     // were loaded by the loading waves, each of which waited for its own before the
     // barrier that starts the chunk these factors are computed in.
-    auto factors16 = [&](int64_t C, int ch0, double &ell_acc) {
+    // (in two parts: the gate and beta reads, issued before the current chunk's products
+    // so that their LDS round trip overlaps them, and the arithmetic after)
+    struct FacIn { float x[16], bt[16]; };
+    auto factors16_read = [&](int64_t C, int ch0, FacIn &fi) {
         if constexpr (DIAG) {
             const GateBuf &Bf = sm.gbuf[C % NBG];
-            const int64_t rem = n - C * CH;
-            const int cl = rem < CH ? (int)rem : CH;
             const int cc = l >> 2, q4 = l & 3, ci = ch0 + cc, t0 = 16 * q4;
-            float x[16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) x[j] = Bf.gate[gate_idx(t0 + j, ci)];
+            for (int j = 0; j < 16; ++j) fi.x[j] = Bf.gate[gate_idx(t0 + j, ci)];
             // the lane's sixteen betas, read before any factor is stored (the stores could
             // alias them for all the compiler knows, which would serialise the reads)
-            float bt[16];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const float4 b4 = *reinterpret_cast<const float4 *>(&Bf.beta[0][t0 + 4 * g]);
-                bt[4 * g] = b4.x; bt[4 * g + 1] = b4.y; bt[4 * g + 2] = b4.z; bt[4 * g + 3] = b4.w;
+                fi.bt[4 * g] = b4.x; fi.bt[4 * g + 1] = b4.y; fi.bt[4 * g + 2] = b4.z; fi.bt[4 * g + 3] = b4.w;
             }
+        }
+    };
+    auto factors16 = [&](int64_t C, int ch0, FacIn &fi, double &ell_acc) {
+        if constexpr (DIAG) {
+            const int64_t rem = n - C * CH;
+            const int cl = rem < CH ? (int)rem : CH;
+            const int cc = l >> 2, q4 = l & 3, ci = ch0 + cc, t0 = 16 * q4;
+            float *x = fi.x;
+            const float *bt = fi.bt;
             float run = 0.f;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -639,10 +647,15 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     // the chunk's factors (computed by these waves one chunk ahead): decay, scale, multiply
     const int i = 32 * (w >> 1) + l32;                // this lane's key channel (of the workgroup's 64)
     double ell16 = 0.0;
+    FacIn fi;
     lds_barrier();                                    // gates of chunk 0 visible
-    if (nc > 0) factors16(0, 16 * w, ell16);
+    if (nc > 0) {
+        factors16_read(0, 16 * w, fi);
+        factors16(0, 16 * w, fi, ell16);
+    }
     for (int64_t c = 0; c < nc; ++c) {
         lds_barrier();                                // chunk c and its factors visible; chunk c - 1's buffer free
+        if (c + 1 < nc) factors16_read(c + 1, 16 * w, fi);
         const SdBuf<DIAG, NJB> &B = sm.buf[c % NBUF];
         const int par = (int)(c & 1);
         // ---- operand reads: K^T and V^T fragments (transposing read), the factors of
@@ -677,7 +690,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb) st[jb] = mfma(ka, vb[ks][jb], st[jb]);
         }
-        if (c + 1 < nc) factors16(c + 1, 16 * w, ell16);
+        if (c + 1 < nc) factors16(c + 1, 16 * w, fi, ell16);
     }
     write_ell16(ell16, 16 * w);
     }
