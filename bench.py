@@ -31,6 +31,7 @@ usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--only main|forward|sd|compose|rag|convexact|kda|peaks] [--no-cpu]
        python bench.py --summarize-traffic FETCH_CSV WRITE_CSV OUT_DIR  (rocprofv3 counter CSVs -> summaries)
        python bench.py --summarize-mfma CSV OUT_MD
+       python bench.py --summarize-trace TRACE_CSV STATS_CSV BENCH_JSON OUT_MD
 """
 from __future__ import annotations
 
@@ -860,6 +861,133 @@ def summarize_mfma(csv_path, out_md):
     print("\n".join(lines))
 
 
+TRACE_WORKLOADS = {
+    # (kernel name as shown, x extent of the grid in threads) -> workload
+    ("compose_dense_mfma_kernel<false, false>", 262144):
+        "GDN compose, conv-exact reuse (unfused leg, and the plain chain over the suffix records)",
+    ("compose_dense_mfma_kernel<false, false>", 524288): "GDN compose, 4096-slot pool, 64 requests x 32 slots",
+    ("compose_dense_mfma_kernel<false, false>", 1048576): "GDN compose, RAG mix, 128 requests x 24-96 slots",
+    ("compose_dense_mfma_kernel<false, true>", 262144):
+        "GDN compose with warmed head tokens (conv-exact reuse, 32 requests, 5631 head tokens)",
+    ("compose_sd_wide_kernel<0, 128, 128>", 65536): "scalar compose, 8-segment chain, H=16",
+    ("compose_sd_wide_kernel<1, 128, 128>", 65536): "diagonal compose, 8-segment chain, H=16",
+    ("compose_sliced_mfma_kernel", 16384): "KDA compose, 8-segment chain, H=16 (four column slices)",
+    ("compose_sliced_mfma_kernel", 32768): "GDN compose, 16-segment chain, H=32, 4 column slices (main step)",
+    ("conv_kv_kernel", 1441536): "conv_kv, conv-exact reuse head tokens",
+    ("conv_kv_kernel", 74207488): "conv_kv, conv-exact suffix records (untimed setup)",
+    ("conv_warmup_vec_kernel<unsigned short, 4>", 512):
+        "conv warm-up, RAG mix, 8305 boundaries x 4096 channels, kernel 4",
+    ("gdn_build_mfma_kernel", 262144): "GDN build, H=32, d=128, bf16, 16 x 2048 tokens (main step)",
+    ("gdn_build_mfma_kernel", 4194304): "GDN build, RAG pool fill batches of 256 segments (untimed setup)",
+    ("gdn_build_mfma_kernel", 8388608): "GDN build, conv-exact suffix records (untimed setup)",
+    ("gdn_build_mfma_kernel", 30752768): "GDN build, conv-exact head records (unfused leg)",
+    ("gdn_build_mfma_kernel", 42336256): "GDN build, RAG mix cold segments (2584 x 32 heads)",
+    ("gdn_build_mfma_kernel", 67108864): "GDN build, 4096 x 64-token pool fill (untimed setup)",
+    ("gdn_chunk_mfma_kernel<false, true>", 262144):
+        "GDN prefill forward, outputs only, H=32, d=128, bf16, 16 x 2048 tokens",
+    ("gdn_chunk_mfma_kernel<true, true>", 393216): "GDN prefill forward with the records as side-outputs, same workload",
+    ("kda_chunk_mfma_kernel<unsigned short>", 131072):
+        "KDA build, H=16, d=128, bf16, 8 x 2048 tokens (chunk form, fp32 MFMA, two roles)",
+    ("sd_build_mfma_kernel<0, 2>", 131072): "scalar build, H=16, d=128, bf16, 8 x 2048 tokens",
+    ("sd_build_mfma_kernel<1, 2>", 131072): "diagonal build, H=16, d=128, bf16, 8 x 2048 tokens",
+    ("peak_mfma_kernel", 262144): "measured-peak bf16 MFMA loop, 1024 x 4 waves x 512 x 4 products",
+    ("peak_read_kernel", 8388608): "measured-peak streaming read of 4 GiB",
+}
+
+
+def _short_kernel_name(name):
+    """'void hypic::(anonymous namespace)::k<a, b>(hypic::Args)' -> 'k<a, b>'."""
+    n = name[5:] if name.startswith("void ") else name
+    for pre in ("hypic::(anonymous namespace)::", "(anonymous namespace)::"):
+        n = n.replace(pre, "")
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):                     # drop the parameter list at template depth 0
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    return n[:cut]
+
+
+def _trace_key(short):
+    if short.startswith("conv_kv_kernel"):
+        return "conv_kv_kernel"                    # its template arguments demangle differently by run
+    return short
+
+
+def summarize_trace(trace_csv, stats_csv, bench_json, out_md):
+    """The kernel-trace summary of the library's kernels: per (kernel, grid) launch
+    durations from rocprofv3's kernel trace, rocprofv3's own --stats table, and the
+    benchmark's HIP-event figures of an unprofiled run for comparison."""
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        short = _short_kernel_name(r["Kernel_Name"])
+        key = (_trace_key(short), int(r["Grid_Size_X"]))
+        if key not in TRACE_WORKLOADS:
+            continue
+        g = groups.setdefault(key + (short,), {"dur": [], "row": r})
+        g["dur"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    lines = ["# rocprofv3 kernel trace -- library kernels, per launch shape", "",
+             "Command (repo at $REPO on the MI355X box; the default bench run without the CPU leg):", "",
+             "```",
+             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+             "-d $REPO/gpurun_out/prof_all -o all -- python $REPO/bench.py --no-cpu",
+             "python $REPO/bench.py --summarize-trace $REPO/gpurun_out/prof_all/all_kernel_trace.csv "
+             "$REPO/gpurun_out/prof_all/all_kernel_stats.csv BENCH_JSON <this file>",
+             "```", "",
+             "Durations are per launch (End - Start of the kernel trace), grouped by kernel and grid; \"grid\" is "
+             "the x extent in threads (the conv warm-up grid is 512 x 8305, boundaries on y). The two `peak_*` "
+             "kernels are the measured-peak microbenchmarks (libhypic_peaks.so). conv_kv's template arguments "
+             "demangle garbled in the profiler.", "",
+             "| kernel | grid (threads) | wg | LDS B | VGPR | AGPR | launches | mean µs | min µs | workload |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for key in sorted(groups, key=lambda k: (k[0].startswith("peak_"), k[0], k[1])):
+        g = groups[key]
+        r, d = g["row"], g["dur"]
+        lines.append(f"| `{key[2]}` | {key[1]} | {r['Workgroup_Size_X']} | {r['LDS_Block_Size']} | {r['VGPR_Count']} | "
+                     f"{r['Accum_VGPR_Count']} | {len(d)} | {np.mean(d):.1f} | {np.min(d):.1f} | "
+                     f"{TRACE_WORKLOADS[key[:2]]} |")
+    lines += ["", "rocprofv3's own `--stats` summary (`all_kernel_stats.csv`) for the same run, all launches of a "
+              "kernel together:", "", "| kernel | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
+    for r in csv.DictReader(open(stats_csv)):
+        short = _short_kernel_name(r["Name"])
+        if not any(_trace_key(short) == k[0] for k in TRACE_WORKLOADS):
+            continue
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) * 1e-3:.1f} | "
+                     f"{float(r['MinNs']) * 1e-3:.1f} | {float(r['MaxNs']) * 1e-3:.1f} |")
+    with open(bench_json) as f:
+        b = json.loads(f.read().strip().splitlines()[-1])
+    k, sec = b["kernels"], {s["workload"]: s for s in b.get("secondary", [])}
+    gb = k["gdn_build"]["ms_stats"]
+    parts = [f"GDN build {gb['mean'] * 1e3:.0f} µs (main step; p10 {gb['p10'] * 1e3:.0f}, p90 {gb['p90'] * 1e3:.0f})",
+             f"main-step compose {k['gdn_compose_chain16']['ms'] * 1e3:.0f} µs"]
+    for name, label in (("gdn_prefill_forward_h32_d128_bf16_16x2048", "prefill forward"),
+                        ("gdn_compose_pool4096_h32_d128_64x32", "pool compose"),
+                        ("scalar_build_h16_d128_8x2048", "scalar build"),
+                        ("diagonal_build_h16_d128_8x2048", "diagonal build"),
+                        ("kda_build_h16_d128_8x2048", "KDA build")):
+        s = sec.get(name)
+        if s is None:
+            continue
+        if "with_records" in s:
+            parts.append(f"{label} {s['ms'] * 1e3:.0f} µs (outputs only) and {s['with_records']['ms'] * 1e3:.0f} µs "
+                         "(with records)")
+        else:
+            parts.append(f"{label} {s['ms'] * 1e3:.0f} µs")
+    mp = b.get("measured_peaks") or {}
+    if mp:
+        parts.append(f"streaming read of 4 GiB {mp['read_gbps'] / 1e3:.2f} TB/s, bf16 MFMA loop "
+                     f"{mp['bf16_mfma_tflops'] / 1e3:.2f} PFLOP/s")
+    lines += ["", "The bench's own HIP-event figures (mean over the timed launches) for the same kernels in the "
+              "unprofiled run of the same build:", ", ".join(parts) + ".", ""]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -874,7 +1002,12 @@ def main():
                     help="write the HBM-traffic summaries of the timed kernels from two rocprofv3 counter runs")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("CSV", "OUT_MD"),
                     help="write the matrix-core utilisation summary from one rocprofv3 counter run")
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_CSV", "STATS_CSV", "BENCH_JSON", "OUT_MD"),
+                    help="write the kernel-trace summary from one rocprofv3 kernel-trace run and a bench line")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
         return
