@@ -690,29 +690,36 @@ def cpu_detail(seed=901):
 def measured_peaks():
     """What this machine delivers: a streaming read of 4 GiB (16384 workgroups of 512
     threads, non-temporal 16-byte loads: the best of a sweep over grid sizes, unroll
-    depths and cache policies) and a loop of bf16 32x32x16 matrix-core products on
-    every SIMD (libhypic_peaks.so)."""
+    depths and cache policies), a streaming copy of 1 GiB with the same loads and
+    non-temporal stores (the rate of a kernel that writes as much as it reads), and a
+    loop of bf16 32x32x16 matrix-core products on every SIMD (libhypic_peaks.so)."""
     from hybrid_prefill_amd import _build
     L = ctypes.CDLL(_build.PEAKS_LIB)
     L.hypic_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     L.hypic_peak_mfma.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    L.hypic_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
     buf = torch.empty(1 << 30, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.zeros(1 << 20, dtype=torch.float32, device="cuda")
     nbytes = buf.numel() * 4
+    cbytes = dst.numel() * 4                      # 1 GiB read and 1 GiB written
     blocks = 256 * 64
     rd = lambda: L.hypic_peak_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(), stream)
+    cp = lambda: L.hypic_peak_copy(buf.data_ptr(), dst.data_ptr(), cbytes, blocks, stream)
     iters, mblocks = 512, 256 * 4
     mf = lambda: L.hypic_peak_mfma(iters, mblocks, sink.data_ptr(), stream)
     for _ in range(2):
-        assert rd() == 0 and mf() == 0
-    ks = launch_stats((("read", rd), ("mfma", mf)), 8)
+        assert rd() == 0 and mf() == 0 and cp() == 0
+    ks = launch_stats((("read", rd), ("copy", cp), ("mfma", mf)), 8)
     flop = iters * 4 * 32768.0 * mblocks * 4
     out = {"read_gbps": nbytes / (ks["read"]["p50"] * 1e-3) / 1e9, "read_ms": ks["read"],
+           "copy_gbps": 2 * cbytes / (ks["copy"]["p50"] * 1e-3) / 1e9, "copy_ms": ks["copy"],
            "bf16_mfma_tflops": flop / (ks["mfma"]["p50"] * 1e-3) / 1e12, "mfma_ms": ks["mfma"]}
-    del buf, sink
+    del buf, dst, sink
     torch.cuda.empty_cache()
-    log(f"measured peaks: read {out['read_gbps']:.0f} GB/s, bf16 MFMA {out['bf16_mfma_tflops']:.0f} TFLOP/s")
+    log(f"measured peaks: read {out['read_gbps']:.0f} GB/s, copy {out['copy_gbps']:.0f} GB/s (read + write), "
+        f"bf16 MFMA {out['bf16_mfma_tflops']:.0f} TFLOP/s")
     return out
 
 
@@ -892,6 +899,7 @@ TRACE_WORKLOADS = {
     ("sd_build_mfma_kernel<1, 2>", 131072): "diagonal build, H=16, d=128, bf16, 8 x 2048 tokens",
     ("peak_mfma_kernel", 262144): "measured-peak bf16 MFMA loop, 1024 x 4 waves x 512 x 4 products",
     ("peak_read_kernel", 8388608): "measured-peak streaming read of 4 GiB",
+    ("peak_copy_kernel", 8388608): "measured-peak streaming copy of 1 GiB (1 GiB read, 1 GiB written)",
 }
 
 
@@ -939,7 +947,7 @@ def summarize_trace(trace_csv, stats_csv, bench_json, out_md):
              "$REPO/gpurun_out/prof_all/all_kernel_stats.csv BENCH_JSON <this file>",
              "```", "",
              "Durations are per launch (End - Start of the kernel trace), grouped by kernel and grid; \"grid\" is "
-             "the x extent in threads (the conv warm-up grid is 512 x 8305, boundaries on y). The two `peak_*` "
+             "the x extent in threads (the conv warm-up grid is 512 x 8305, boundaries on y). The `peak_*` "
              "kernels are the measured-peak microbenchmarks (libhypic_peaks.so). conv_kv's template arguments "
              "demangle garbled in the profiler.", "",
              "| kernel | grid (threads) | wg | LDS B | VGPR | AGPR | launches | mean µs | min µs | workload |",
@@ -979,6 +987,8 @@ def summarize_trace(trace_csv, stats_csv, bench_json, out_md):
             parts.append(f"{label} {s['ms'] * 1e3:.0f} µs")
     mp = b.get("measured_peaks") or {}
     if mp:
+        if "copy_gbps" in mp:
+            parts.append(f"streaming copy of 1 GiB {mp['copy_gbps'] / 1e3:.2f} TB/s (read + write)")
         parts.append(f"streaming read of 4 GiB {mp['read_gbps'] / 1e3:.2f} TB/s, bf16 MFMA loop "
                      f"{mp['bf16_mfma_tflops'] / 1e3:.2f} PFLOP/s")
     lines += ["", "The bench's own HIP-event figures (mean over the timed launches) for the same kernels in the "

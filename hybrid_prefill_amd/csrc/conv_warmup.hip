@@ -11,12 +11,11 @@
 // From position K-1 on the window holds only the segment's own tokens, so
 // nothing else changes.
 //
-// Bandwidth-bound.  Main kernel: the boundary is the grid's y index (its table
-// indices are wave-uniform scalar loads) and each thread owns 16 bytes of
-// channels of every input row (8 bf16 or 4 fp32), so every load is one 16-byte
-// access and every output row two or one 16-byte stores, coalesced along C.
-// Channel counts or pointers that do not allow that take the one-channel-per-
-// thread kernel.
+// Bandwidth-bound.  Main kernel: the boundaries are the grid's y index (their
+// table indices are wave-uniform scalar loads) and each thread owns four channels
+// of every row, so every load is one 8- or 16-byte access and every output row one
+// 16-byte store, coalesced along C.  Channel counts or pointers that do not allow
+// that take the one-channel-per-thread kernel.
 #include "hypic_internal.h"
 
 namespace hypic {
@@ -77,84 +76,96 @@ hipError_t launch_k(const ConvArgs &a, dim3 grid, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// 16-byte vector of inputs: 8 bf16 or 4 fp32 channels
+// Four channels of one input row: 8 bytes of bf16 or 16 bytes of fp32
 template <typename XT> struct XVec;
 template <> struct XVec<uint16_t> {
-    static constexpr int N = 8;
-    typedef uint4 raw;
+    typedef uint2 raw;
     static __device__ __forceinline__ void unpack(raw r, float *f) {
-        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = __uint_as_float(w[i] << 16);
-            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
+        f[0] = __uint_as_float(r.x << 16);
+        f[1] = __uint_as_float(r.x & 0xffff0000u);
+        f[2] = __uint_as_float(r.y << 16);
+        f[3] = __uint_as_float(r.y & 0xffff0000u);
     }
 };
 template <> struct XVec<float> {
-    static constexpr int N = 4;
     typedef float4 raw;
     static __device__ __forceinline__ void unpack(raw r, float *f) { f[0] = r.x; f[1] = r.y; f[2] = r.z; f[3] = r.w; }
 };
 
+// Each thread owns four channels, so that every output row is one 16-byte store per
+// lane over a contiguous kilobyte per wave (eight bf16 channels per thread would
+// take two stores per row at a 32-byte stride, half a sector each: about 1.5x
+// slower).  A workgroup takes NB boundaries per pass and issues all their loads
+// before the first one is used.
+constexpr int CONV_NB = 2;
+
 template <typename XT, int K>
 __global__ __launch_bounds__(NT) void conv_warmup_vec_kernel(ConvArgs a) {
     typedef XVec<XT> V;
-    constexpr int NV = V::N;
     const int64_t C = a.channels;
-    const int64_t c0 = ((int64_t)blockIdx.x * NT + threadIdx.x) * NV;
+    const int64_t c0 = ((int64_t)blockIdx.x * NT + threadIdx.x) * 4;
     if (c0 >= C) return;
     const XT *tails = static_cast<const XT *>(a.tails);
     const XT *heads = static_cast<const XT *>(a.heads);
-    float w[NV][K];
+    float w[4][K];
 #pragma unroll
-    for (int i = 0; i < NV * K / 4; ++i) {
+    for (int i = 0; i < K; ++i) {
         const float4 q = *reinterpret_cast<const float4 *>(a.weight + c0 * K + 4 * i);
         const float qq[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[(4 * i + e) / K][(4 * i + e) % K] = qq[e];
     }
-    float bias[NV];
+    float bias[4];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) bias[i] = a.bias ? a.bias[c0 + i] : 0.0f;
+    for (int i = 0; i < 4; ++i) bias[i] = a.bias ? a.bias[c0 + i] : 0.0f;
     const float nanv = __int_as_float(0x7fc00000);
-    for (int64_t b = blockIdx.y; b < a.num_boundaries; b += gridDim.y) {
-        const int64_t ti = a.tail_index ? a.tail_index[b] : b;
-        const int64_t hi = a.head_index ? a.head_index[b] : b;
-        float *out = a.out + b * (K - 1) * C + c0;
-        if (ti < 0 || ti >= a.num_tails || hi < 0 || hi >= a.num_heads) {
-            if (c0 == 0) raise_flag(a.err_flag, HYPIC_EFLAG_SLOT_OUT_OF_RANGE);
+    const int64_t nb = a.num_boundaries;
+    for (int64_t b0 = (int64_t)blockIdx.y * CONV_NB; b0 < nb; b0 += (int64_t)gridDim.y * CONV_NB) {
+        typename V::raw r[CONV_NB][2 * K - 2];
+        bool ok[CONV_NB];
 #pragma unroll
-            for (int t = 0; t < K - 1; ++t)
+        for (int u = 0; u < CONV_NB; ++u) {
+            const int64_t b = b0 + u < nb ? b0 + u : nb - 1;
+            const int64_t ti = a.tail_index ? a.tail_index[b] : b;
+            const int64_t hi = a.head_index ? a.head_index[b] : b;
+            ok[u] = ti >= 0 && ti < a.num_tails && hi >= 0 && hi < a.num_heads;
+            if (ok[u]) {                            // uniform over the workgroup
 #pragma unroll
-                for (int i = 0; i < NV; i += 4)
-                    *reinterpret_cast<float4 *>(out + t * C + i) = make_float4(nanv, nanv, nanv, nanv);
-            continue;
-        }
-        typename V::raw r[2 * K - 2];
-#pragma unroll
-        for (int j = 0; j < K - 1; ++j) {
-            r[j] = load_nt(reinterpret_cast<const typename V::raw *>(tails + (ti * (K - 1) + j) * C + c0));
-            r[K - 1 + j] = load_nt(reinterpret_cast<const typename V::raw *>(heads + (hi * (K - 1) + j) * C + c0));
-        }
-        float xb[2 * K - 2][NV];
-#pragma unroll
-        for (int j = 0; j < 2 * K - 2; ++j) V::unpack(r[j], xb[j]);
-#pragma unroll
-        for (int t = 0; t < K - 1; ++t) {
-            float y[NV];
-#pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                float acc = bias[i];
-#pragma unroll
-                for (int j = 0; j < K; ++j) acc += w[i][j] * xb[t + j][i];
-                if (a.activation == 1) acc = acc / (1.0f + expf(-acc));
-                y[i] = acc;
+                for (int j = 0; j < K - 1; ++j) {
+                    r[u][j] = load_nt(reinterpret_cast<const typename V::raw *>(tails + (ti * (K - 1) + j) * C + c0));
+                    r[u][K - 1 + j] =
+                        load_nt(reinterpret_cast<const typename V::raw *>(heads + (hi * (K - 1) + j) * C + c0));
+                }
             }
+        }
 #pragma unroll
-            for (int i = 0; i < NV; i += 4)
-                __builtin_nontemporal_store((f32x4){y[i], y[i + 1], y[i + 2], y[i + 3]},
-                                            reinterpret_cast<f32x4 *>(out + t * C + i));
+        for (int u = 0; u < CONV_NB; ++u) {
+            const int64_t b = b0 + u;
+            if (b >= nb) break;
+            float *out = a.out + b * (K - 1) * C + c0;
+            if (!ok[u]) {
+                if (c0 == 0) raise_flag(a.err_flag, HYPIC_EFLAG_SLOT_OUT_OF_RANGE);
+#pragma unroll
+                for (int t = 0; t < K - 1; ++t)
+                    *reinterpret_cast<float4 *>(out + t * C) = make_float4(nanv, nanv, nanv, nanv);
+                continue;
+            }
+            float xb[2 * K - 2][4];
+#pragma unroll
+            for (int j = 0; j < 2 * K - 2; ++j) V::unpack(r[u][j], xb[j]);
+#pragma unroll
+            for (int t = 0; t < K - 1; ++t) {
+                float y[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float acc = bias[i];
+#pragma unroll
+                    for (int j = 0; j < K; ++j) acc += w[i][j] * xb[t + j][i];
+                    if (a.activation == 1) acc = acc / (1.0f + expf(-acc));
+                    y[i] = acc;
+                }
+                __builtin_nontemporal_store((f32x4){y[0], y[1], y[2], y[3]}, reinterpret_cast<f32x4 *>(out + t * C));
+            }
         }
     }
 }
@@ -179,13 +190,13 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
 hipError_t launch_conv_warmup(const ConvArgs &a, hipStream_t stream) {
     if (a.num_boundaries <= 0) return hipSuccess;
-    // vector kernel: 16 bytes of channels per thread; the weights of a thread's
-    // channels (NV * K floats) must start 16-byte aligned too
-    const int nv = a.x_dtype == HYPIC_BF16 ? 8 : 4;
-    if (a.channels % nv == 0 && aligned16(a.tails) && aligned16(a.heads) && aligned16(a.out) &&
-        aligned16(a.weight) && ((int64_t)nv * a.ksize) % 4 == 0 && (a.channels % 4 == 0)) {
-        const int64_t gx = (a.channels / nv + NT - 1) / NT;
-        const unsigned gy = (unsigned)(a.num_boundaries < 65535 ? a.num_boundaries : 65535);
+    // vector kernel: four channels per thread (8- or 16-byte loads, 16-byte stores);
+    // the weights of a thread's channels (4 K floats) start 16-byte aligned too
+    if (a.channels % 4 == 0 && aligned16(a.tails) && aligned16(a.heads) && aligned16(a.out) &&
+        aligned16(a.weight)) {
+        const int64_t gx = (a.channels / 4 + NT - 1) / NT;
+        const int64_t passes = (a.num_boundaries + CONV_NB - 1) / CONV_NB;
+        const unsigned gy = (unsigned)(passes < 65535 ? passes : 65535);
         const dim3 grid((unsigned)gx, gy);
         if (a.x_dtype == HYPIC_BF16) return launch_vec_k<uint16_t>(a, grid, stream);
         return launch_vec_k<float>(a, grid, stream);

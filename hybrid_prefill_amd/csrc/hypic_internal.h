@@ -96,8 +96,12 @@ constexpr int kLoadNT = 2;
 
 template <typename T> __device__ __forceinline__ T load_nt(const T *p) {
     typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-    static_assert(sizeof(T) == 16, "16-byte loads only");
-    return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p)));
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    static_assert(sizeof(T) == 16 || sizeof(T) == 8, "8- or 16-byte loads only");
+    if constexpr (sizeof(T) == 16)
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p)));
+    else
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p)));
 }
 
 __device__ __forceinline__ void raise_flag(uint32_t *flag, uint32_t bits) {

@@ -5,6 +5,8 @@
 // against attainable rates:
 //   * a streaming read of a large buffer (16-byte non-temporal loads, four in flight
 //     per thread, grid-stride), the attainable HBM read bandwidth;
+//   * a streaming copy (the same loads, each followed by a 16-byte non-temporal
+//     store), the attainable rate of a kernel that writes as much as it reads;
 //   * a loop of independent bf16 v_mfma_f32_32x32x16 products on register operands
 //     (four accumulator chains per wave, one wave per SIMD), the attainable dense
 //     bf16 matrix rate at the clock the chip holds under that load.
@@ -37,6 +39,22 @@ __global__ __launch_bounds__(NT_READ) void peak_read_kernel(const f32x4 *src, in
     if (s != s) sink[blockIdx.x] = s;
 }
 
+__global__ __launch_bounds__(NT_READ) void peak_copy_kernel(const f32x4 *src, f32x4 *dst, int64_t n4) {
+    const int64_t stride = (int64_t)gridDim.x * NT_READ;
+    int64_t i = (int64_t)blockIdx.x * NT_READ + threadIdx.x;
+    for (; i + 3 * stride < n4; i += 4 * stride) {
+        const f32x4 a0 = __builtin_nontemporal_load(src + i);
+        const f32x4 a1 = __builtin_nontemporal_load(src + i + stride);
+        const f32x4 a2 = __builtin_nontemporal_load(src + i + 2 * stride);
+        const f32x4 a3 = __builtin_nontemporal_load(src + i + 3 * stride);
+        __builtin_nontemporal_store(a0, dst + i);
+        __builtin_nontemporal_store(a1, dst + i + stride);
+        __builtin_nontemporal_store(a2, dst + i + 2 * stride);
+        __builtin_nontemporal_store(a3, dst + i + 3 * stride);
+    }
+    for (; i < n4; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
 __global__ __launch_bounds__(NT) void peak_mfma_kernel(int64_t iters, float *sink) {
     const float x = 1.0f + 1e-3f * (float)(threadIdx.x & 7);
     const bf16x8 a = {(__bf16)x, (__bf16)x, (__bf16)x, (__bf16)x, (__bf16)x, (__bf16)x, (__bf16)x, (__bf16)x};
@@ -65,6 +83,15 @@ int hypic_peak_read(const void *src, int64_t bytes, int32_t blocks, float *sink,
     if (!src || !sink || bytes <= 0 || (bytes & 15) || blocks <= 0) return -1;
     hipLaunchKernelGGL(peak_read_kernel, dim3((unsigned)blocks), dim3(NT_READ), 0, static_cast<hipStream_t>(stream),
                        static_cast<const f32x4 *>(src), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Streaming copy of `bytes` (a multiple of 16) from `src` to `dst` (not overlapping)
+// by `blocks` workgroups of 512 threads.  Returns 0, or -1 on a bad argument / launch error.
+int hypic_peak_copy(const void *src, void *dst, int64_t bytes, int32_t blocks, void *stream) {
+    if (!src || !dst || bytes <= 0 || (bytes & 15) || blocks <= 0) return -1;
+    hipLaunchKernelGGL(peak_copy_kernel, dim3((unsigned)blocks), dim3(NT_READ), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const f32x4 *>(src), static_cast<f32x4 *>(dst), bytes / 16);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -443,9 +443,10 @@ def test_scalar_mfma_build_error_flags():
                                                 (4, 4096, torch.bfloat16, 1, True),
                                                 (2, 96, torch.float32, 1, True),
                                                 (8, 200, torch.float32, 0, True),
-                                                # channel counts off the 16-byte vector width:
-                                                # the one-channel-per-thread kernel
                                                 (3, 100, torch.bfloat16, 0, True),
+                                                # channel counts that are not a multiple of 4:
+                                                # the one-channel-per-thread kernel
+                                                (3, 98, torch.bfloat16, 0, True),
                                                 (4, 30, torch.float32, 1, False)])
 def test_conv_warmup_equals_sequential_conv(K, C, dtype, act, bias):
     rng = np.random.default_rng(800 + K)
@@ -468,8 +469,10 @@ def test_conv_warmup_equals_sequential_conv(K, C, dtype, act, bias):
     assert worst <= 1e-4
 
 
-@pytest.mark.parametrize("C", [64, 60])
+@pytest.mark.parametrize("C", [64, 62])
 def test_conv_warmup_bad_index(C):
+    """A bad index beside good ones in the same pass of the vector kernel (C = 64) and
+    in the one-channel-per-thread kernel (C = 62): NaN rows and the flag, neighbours exact."""
     K = 4
     x = synth.conv_stream(12, C, torch.bfloat16, 810, "cuda").reshape(4, 3, C)
     w = synth.conv_weights(C, K, 811, "cuda")
