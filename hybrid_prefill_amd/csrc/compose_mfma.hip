@@ -293,12 +293,26 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
     } while (0)
 
     // ---- records in flight: P_{c+1} is fetched into registers (coalesced 16-byte
-    //      pieces q = th + 256 u) as soon as P_c has been split to bf16 hi/lo fragments
-    //      in LDS at the top of step c.  S_c goes HBM -> LDS directly (wave w's
-    //      instruction u moves pieces (16 w + u) * 64 + lane), issued at the end of step
-    //      c - 1 and waited for only at the combine of step c.  Per wave the loads issued
-    //      after S_c are exactly the 16 of P_{c+1} (the last step refetches its own P, an
-    //      L2 hit), so the combine waits for vmcnt <= 16.
+    //      pieces q = th + 256 u) once P_c has been split to bf16 hi/lo fragments in LDS
+    //      at the top of step c.  S_c goes HBM -> LDS directly (wave w's instruction u
+    //      moves pieces (16 w + u) * 64 + lane) and is waited for only at the combine of
+    //      step c.  Per wave the loads issued after S_c are exactly the 16 of P_{c+1}
+    //      (the last step refetches its own P, an L2 hit), so the combine waits for
+    //      vmcnt <= 16.
+    //      Without head tokens both are issued inside the products of step c, four
+    //      instructions per k-step (S_c in the first four k-steps, P_{c+1} in the last
+    //      four): with one wave per SIMD a batch of 16 back-to-back loads stalls the
+    //      wave's instruction stream while the memory pipe drains, whereas between
+    //      products the MFMAs already issued keep the matrix pipe busy meanwhile.  S_c
+    //      goes through inline asm there: the compiler then neither sees a pending
+    //      HBM -> LDS load (while one is, it turns every wait for a register load into
+    //      vmcnt(0), and it waits with vmcnt(0) before any read of the S stage) nor
+    //      counts it, and P_{c+1}, the last load issued, is exactly what its wait at the
+    //      top of step c + 1 covers.  The explicit vmcnt(16) and the workgroup barrier
+    //      (both with a memory clobber) order the combine's reads after the load.
+    //      With head tokens S_c is issued at the end of step c - 1 (with the builtin),
+    //      after the entry's tokens, and P_{c+1} right after the split.
+    constexpr bool SPREAD = !MODE_P && !HEADS;
     float4 pa[16];
     float ea = 0.f;               // ell of the record in pa
 #define HYPIC_FETCH_P(PF, EL, CC)                                                                \
@@ -308,6 +322,11 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
         const float4 *fsrc = reinterpret_cast<const float4 *>(a.pool_P + frec * D * D);          \
         _Pragma("unroll") for (int u = 0; u < 16; ++u) PF[u] = load_nt(fsrc + th + NT * u);     \
     } while (0)
+#define HYPIC_FETCH_P_PART(PF, FSRC, U0)                                                         \
+    _Pragma("unroll") for (int u = (U0); u < (U0) + 4; ++u) PF[u] = load_nt(FSRC + th + NT * u);
+#define HYPIC_FETCH_S_PART(FSS, U0)                                                              \
+    _Pragma("unroll") for (int u = (U0); u < (U0) + 4; ++u)                                      \
+        lds_dma16(FSS + (16 * w + u) * 64 + l, &s_stage[(16 * w + u) * 256]);
 #define HYPIC_FETCH_S(CC)                                                                        \
     do {                                                                                         \
         const int64_t frec = (int64_t)chain_slot(cs, c_lo, (CC)) * a.H + head;                \
@@ -336,7 +355,17 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
             *reinterpret_cast<u32x2 *>(&ps.lo[slot]) = u32x2{l01, l23};                          \
         }                                                                                        \
         const float le = EL;                                                                     \
-        HYPIC_FETCH_P(PF, EL, c + 1 < c_hi ? c + 1 : c);                                         \
+        const float4 *fsrc_n = nullptr, *fss_c = nullptr;                                       \
+        if constexpr (SPREAD) {                                                                  \
+            const int64_t cn_ = c + 1 < c_hi ? c + 1 : c;                                         \
+            const int64_t frn_ = (int64_t)chain_slot(cs, c_lo, cn_) * a.H + head;                 \
+            const int64_t frc_ = (int64_t)chain_slot(cs, c_lo, c) * a.H + head;                   \
+            EL = chain_ell(cs, c_lo, cn_);                                                       \
+            fsrc_n = reinterpret_cast<const float4 *>(a.pool_P + frn_ * D * D);                  \
+            fss_c = reinterpret_cast<const float4 *>(a.pool_S + frc_ * D * D);                   \
+        } else {                                                                                 \
+            HYPIC_FETCH_P(PF, EL, c + 1 < c_hi ? c + 1 : c);                                     \
+        }                                                                                        \
         HYPIC_STAGE_H();                                                                         \
         lds_barrier();                                   /* fragments (and head tokens) visible */ \
         HYPIC_APPLY_H();                                                                         \
@@ -354,6 +383,11 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
         }                                                                                        \
         _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) {                                       \
             const int cb = kb & 1, nb = cb ^ 1;                                                  \
+            if constexpr (SPREAD) {                                                              \
+                if (kb < 4) { HYPIC_FETCH_S_PART(fss_c, 4 * kb) }                                \
+                else { HYPIC_FETCH_P_PART(PF, fsrc_n, 4 * (kb - 4)) }                            \
+                __builtin_amdgcn_sched_barrier(0);    /* keep each group at its k-step */        \
+            }                                                                                    \
             if (kb + 1 < 8) {                                                                    \
                 _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) {                               \
                     const int f = (mb * 8 + kb + 1) * FRAG_U32 + lane_slot(l32, h);              \
@@ -373,6 +407,7 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
             _Pragma("unroll") for (int o_ = 32; o_ >= 1; o_ >>= 1) m_ = fmaxf(m_, __shfl_xor(m_, o_)); \
             if (l == 0) sh_pmax[w] = m_;                                                         \
         } else {                                                                                 \
+            if constexpr (SPREAD) __builtin_amdgcn_sched_barrier(0); /* products issued first */ \
             asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   /* this wave's S_c pieces */     \
             lds_barrier();                               /* everyone's S_c pieces */            \
             const float sc = expf(le);                                                           \
@@ -398,22 +433,24 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
         /* head tokens before S, so that the compiler's wait for them at the top of the   */ \
         /* next step does not also wait for S (loads complete in issue order)             */ \
         HYPIC_FETCH_H(c + 1 < c_hi ? c + 1 : c);                                                 \
-        if (!MODE_P) HYPIC_FETCH_S(c + 1 < c_hi ? c + 1 : c);  /* last step: an L2 hit */       \
+        if (!MODE_P && !SPREAD) HYPIC_FETCH_S(c + 1 < c_hi ? c + 1 : c);  /* last: an L2 hit */   \
     } while (0)
     if (c < c_hi) {
         HYPIC_FETCH_P(pa, ea, c);
         HYPIC_FETCH_H(c);
-        if (!MODE_P) HYPIC_FETCH_S(c);
+        if (!MODE_P && !SPREAD) HYPIC_FETCH_S(c);
         while (true) {
             HYPIC_STEP(pa, ea);
             if (++c >= c_hi) break;
         }
-        // the last step's S load (a refetch) lands in LDS before the workgroup ends
+        // every load (with head tokens the last step's S refetch) lands before the workgroup ends
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 #undef HYPIC_STEP
 #undef HYPIC_FETCH_P
 #undef HYPIC_FETCH_S
+#undef HYPIC_FETCH_S_PART
+#undef HYPIC_FETCH_P_PART
 #undef HYPIC_FETCH_H
 #undef HYPIC_STAGE_H
 #undef HYPIC_APPLY_H
