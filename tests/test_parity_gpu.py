@@ -174,6 +174,18 @@ def test_scalar_mixed_lengths_128_units():
                         "weak", label="scalar-mixed-128-units")
 
 
+@pytest.mark.parametrize("H,lens", [(4, [4200, 2049, 64, 4160]),                          # 16 units: 4 splits
+                                    (16, [4200, 2048, 2049, 1, 0, 4160, 130, 6200]),      # 128 units: 2 splits
+                                    (32, [4200, 2100, 64, 2049, 1, 0, 130, 2500])])       # 256 units: 1 split
+def test_scalar_segments_past_one_weight_table(H, lens):
+    """Scalar family on the matrix cores with segments longer than one 2048-token weight
+    table (the tables after the first and the state carried between them), for each
+    value split of the grid (4, 2 and 1 workgroups per (segment, head)); weak gates, so
+    the first table's tokens still count at the end of the segment."""
+    check_build_compose(hp.SCALAR, lens, H, 128, 128, torch.bfloat16, 221 + H, "weak",
+                        label=f"scalar-long-{H}x{len(lens)}")
+
+
 @pytest.mark.parametrize("variant", ["as_given", "none"])
 def test_gdn_32_heads_16x2048(variant):
     """GDN H=32, d=128, bf16, one 32768-token request in 16 x 2048 segments: all 512
