@@ -186,6 +186,15 @@ def test_scalar_segments_past_one_weight_table(H, lens):
                         label=f"scalar-long-{H}x{len(lens)}")
 
 
+@pytest.mark.parametrize("family,variant", [(hp.GDN, "as_given"), (hp.GDN, "none"), (hp.DIAGONAL, "weak")])
+def test_gdn_diagonal_segments_past_2048(family, variant):
+    """GDN and diagonal builds on the matrix cores over segments of up to 100 chunks
+    (the chunk-parity buffers, and for GDN the decay scale carried beside the state and
+    folded into it, over many cycles), composed into one chain."""
+    check_build_compose(family, [4200, 64, 6100, 1, 2049], 4, 128, 128, torch.bfloat16, 231 + family, variant,
+                        label=f"long-{family}-{variant}")
+
+
 @pytest.mark.parametrize("variant", ["as_given", "none"])
 def test_gdn_32_heads_16x2048(variant):
     """GDN H=32, d=128, bf16, one 32768-token request in 16 x 2048 segments: all 512
