@@ -27,8 +27,9 @@
 //    prefix, the Gram blocks (A11, A22 in fp32, H_21 in bf16); the inverses
 //    of the 32x32 diagonal blocks (4x4 forward substitution and fp32 merges
 //    up to 16, one 16 -> 32 merge on the MFMA), written as T diag(beta) in
-//    bf16 by each level as it finishes; prep wave 0 also loads keys and
-//    values into LDS.  Prep waves 4 and 6 turn K^T around for the update in phase b.
+//    bf16 by each level as it finishes.  Wave 4 also loads keys and values
+//    into LDS and computes the decay factors; waves 5 and 7 invert the two
+//    diagonal blocks; waves 4 and 6 turn K^T around for the update in phase b.
 // Two workgroup barriers per chunk: in phase a the state waves finish chunk
 // c - 1 (solve, update) while the prep waves compute A of chunk c; in phase b
 // the state waves form W of chunk c while the prep waves invert.
@@ -299,8 +300,8 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
     } while (0)
         if (nc > 0) HYPIC_FETCH_G(0);
         if (pw == 0) {
-            // ---- prep wave 0: loads keys and values, the decay factors, ell; inverts
-            //      block 0 of the P system.
+            // ---- wave 4: loads keys and values, the decay factors and ell in phase a;
+            //      turns K^T around for tokens 0-31 of the chunk in phase b.
             // Keys and values go straight from HBM into Km/Vm (global_load_lds): the
             // instruction for rows 4u .. 4u + 3 lands lane l's 16 bytes in row 4u + l / 16,
             // slot l % 16, so the lane loads the granule that kmo puts there.  Rows past
@@ -391,7 +392,9 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
             if (th == 256) a.pool_ell[rec] = bad ? nanv : (float)ell;
 #undef HYPIC_LOAD_KV
         } else {
-            // ---- prep waves 1-3: Gram block and A in phase a; one factor block in phase b
+            // ---- waves 5-7: a Gram block in phase a (waves 5 and 7 the diagonal blocks,
+            //      which they also start inverting; wave 6 H_21); in phase b waves 5 and 7
+            //      finish their block's inverse, wave 6 turns K^T around for tokens 32-63
             __syncthreads();                                        // prologue: chunk 0 staged
             for (int64_t i = 0; i <= nc; ++i) {
                 int thv = th;
