@@ -400,9 +400,10 @@ __global__ __launch_bounds__(ChunkThreads<WITH_P>::value, 1) void gdn_chunk_mfma
         if (nc > 0) HYPIC_FETCH_G(0);
         if (pw == 0) {
             // ---- prep wave 0: streams keys, values (one chunk ahead) and queries (at
-            //      the start of the chunk's phase a); decay factors, ell; K^T turnaround
-            //      half and Aqk blocks (0,0), (1,1) in phase b.  Rows past the segment
-            //      repeat its last row (finite; their beta is zero, their outputs unused).
+            //      the start of the chunk's phase a); decay factors, ell; in phase b K^T
+            //      turned around for tokens 0-31 and, with the records, Aqk block (0,0).
+            //      Rows past the segment repeat its last row (finite; their beta is zero,
+            //      their outputs unused).
             const u16 *kh = static_cast<const u16 *>(a.k) + t0 * a.k_st + head * a.k_sh;
             const u16 *vh = static_cast<const u16 *>(a.v) + t0 * a.v_st + head * a.v_sh;
             const u16 *qh = WITH_O ? static_cast<const u16 *>(io.q) + t0 * io.q_st + head * io.q_sh : nullptr;
@@ -481,8 +482,11 @@ __global__ __launch_bounds__(ChunkThreads<WITH_P>::value, 1) void gdn_chunk_mfma
             if (records && pl == 0) a.pool_ell[rec] = bad ? __int_as_float(0x7fc00000) : (float)ell;
 #undef HYPIC_LOAD_ROWS
         } else {
-            // ---- prep waves 1-3: Gram block and A in phase a; one factor block (waves
-            //      1, 3), or H_21 and the other K^T half (wave 2, and Aqk (1,0)), in phase b
+            // ---- prep waves 1-3: a Gram block in phase a (waves 1 and 3 the diagonal blocks,
+            //      which they also start inverting, wave 2 H_21; without the records also
+            //      Aqk blocks (0,0), (1,0), (1,1)); in phase b waves 1 and 3 finish their
+            //      block's inverse, and wave 2 turns K^T around for tokens 32-63 and, with
+            //      the records, computes Aqk blocks (1,0) and (1,1)
             __syncthreads();                                        // prologue: chunk 0 staged
             for (int64_t i = 0; i <= nc; ++i) {
                 int thv = th;
