@@ -40,11 +40,12 @@
 // and beta) go from HBM straight into LDS (global_load_lds), NBUF chunks deep, so
 // the compute waves never stall on the load queue (a single wave cannot issue a
 // chunk's loads as fast as the compute waves use it); one workgroup barrier per
-// chunk.  For the diagonal family the loading waves also compute the
-// per-(token, channel) factors and the chunk decay, once per chunk and one chunk
-// ahead, into parity-buffered LDS tiles (the compute waves of a key block would
-// otherwise both compute the same ones); their gates come in a ring of their own,
-// one chunk further ahead than the keys and values.  Tail rows past the segment
+// chunk.  For the diagonal family the loading waves also bring each chunk's gates
+// and beta, in a ring of their own one chunk further ahead than the keys and values;
+// the compute waves turn them into the per-(token, channel) factors and the chunk
+// decay one chunk ahead of use (compute wave w the workgroup's key channels
+// 16w .. 16w + 15, beside the current chunk's products), into parity-buffered LDS
+// tiles that all four compute waves then read.  Tail rows past the segment
 // repeat its last row and are masked at use (beta and log alpha of those tokens
 // read as 0).
 #include "hypic_internal.h"
@@ -148,10 +149,11 @@ struct __align__(16) SdBuf {
 // Diagonal family only (the scalar family reads its gates once per table block): a
 // chunk's gates and beta, in a ring of their own (loaded one chunk further ahead than
 // the keys and values).  Loading wave lw's share of the gates is channels
-// 16 lw .. 16 lw + 15 of the workgroup's 64 for all 64 tokens (the channels it computes
-// the factors of), in global_load_lds order: instruction j, lane l holds token
-// 16 j + l / 4, channels 16 lw + 4 (l % 4) .. + 3; every loading wave keeps its own
-// copy of beta.  So a loading wave reads only what it loaded itself.
+// 16 lw .. 16 lw + 15 of the workgroup's 64 for all 64 tokens (the channels compute
+// wave lw turns into factors), in global_load_lds order: instruction j, lane l holds
+// token 16 j + l / 4, channels 16 lw + 4 (l % 4) .. + 3.  Every loading wave loads a
+// copy of beta (so that all of them issue the same instructions and count their
+// loads alike); the compute waves read the first.
 struct __align__(16) GateBuf {
     float gate[CH * DKC];
     float beta[NLW][CH];
