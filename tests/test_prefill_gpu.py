@@ -109,6 +109,27 @@ def test_prefill_32_heads_16x2048(variant):
     assert eb <= 1e-2
 
 
+@pytest.mark.parametrize("scale", [0.1, 0.0])
+def test_prefill_segments_past_2048(scale):
+    """Segments of up to 100 chunks (the decay scale carried beside the state and folded
+    into it, over many cycles): every output and record against the oracle."""
+    H, lens = 4, [4200, 64, 6100, 1]
+    st, q, offs = _stream(lens, H, 371 + int(scale * 10), scale)
+    nseg = len(lens)
+    slots = np.arange(nseg, dtype=np.int32)
+    pool = hp.Pool.allocate(hp.GDN, nseg, H, D, D, device="cuda", fill=CANARY)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = hp.prefill_segment(hp.GDN, st.k, st.v, q, st.log_alpha, dev_i64(offs), beta=st.beta, pool=pool,
+                             dst_slots=dev_i32(slots), err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ref = _oracle(st, q, offs)
+    eo = _output_errors(out, ref[0], offs)
+    er = _record_errors(pool, slots, ref, H)
+    say(f"[prefill long] decay {scale} lens {lens}: outputs {eo:.2e}, records {max(er):.2e}")
+    assert eo <= TOL[BF] and max(er) <= TOL[BF]
+
+
 EDGE_LENS = [0, 1, 63, 64, 65, 127, 129, 200]
 
 
