@@ -241,6 +241,68 @@ def test_special_gdn_inputs():
         assert rel_fro(np64(pool.S[0, h]), ref) < 1e-4
 
 
+@pytest.mark.parametrize("family", [hp.GDN, hp.SCALAR, hp.DIAGONAL, hp.KDA])
+@pytest.mark.parametrize("layout", ["fused", "kv_offset", "gate_offset"])
+def test_build_strided_views(family, layout):
+    """k and v as head-interleaved views of one [N, H, 3, d + 8] projection buffer, beta and
+    the decay as views of wider buffers (d = 128, bf16).  'fused': every row 16-byte
+    aligned with strides in whole 16-byte units, the layout the matrix-core builds take;
+    'kv_offset': k and v rows start one element in, so none is 16-byte aligned and the
+    GDN, scalar and diagonal builds go to the generic kernel; 'gate_offset': only the
+    gate views start one element in (for the diagonal family that alone sends the build
+    to the generic kernel).  Every record is compared with the oracle on the same values."""
+    H, d = 3, 128
+    lens = [200, 0, 77, 64, 129]
+    offs = synth.offsets_from_lengths(lens)
+    N, nseg = int(offs[-1]), len(lens)
+    seed = 2300 + 10 * [hp.GDN, hp.SCALAR, hp.DIAGONAL, hp.KDA].index(family)
+    kv_sh = 1 if layout == "kv_offset" else 0
+    g_sh = 1 if layout == "gate_offset" else 0
+    proj = torch.zeros((N, H, 3, d + 8), dtype=torch.bfloat16, device="cuda")
+    k = proj[:, :, 1, kv_sh:kv_sh + d]
+    v = proj[:, :, 2, kv_sh:kv_sh + d]
+    k.copy_(synth.keys(N, H, d, torch.bfloat16, seed + 1, "cuda"))
+    v.copy_(synth.values(N, H, d, torch.bfloat16, seed + 2, "cuda"))
+    beta = None
+    if family in (hp.GDN, hp.KDA):
+        beta = torch.zeros((N, H, 3), device="cuda")[:, :, 1 + g_sh]
+        beta.copy_(synth.write_gate(N, H, seed + 3, "cuda"))
+    if family == hp.GDN:
+        la = torch.zeros((N, H, 3), device="cuda")[:, :, g_sh]
+        la.copy_(synth.gdn_log_decay(N, H, seed + 4, 0.1, "cuda"))
+    elif family == hp.SCALAR:
+        la = torch.zeros((H, 3), device="cuda")[:, 1 + g_sh]
+        la.copy_(synth.scalar_log_gamma(H, seed + 4, 0.9, 0.999, "cuda"))
+    else:
+        la = torch.zeros((N, H, d + 8), device="cuda")[:, :, g_sh:g_sh + d]
+        la.copy_(synth.diagonal_log_gates(N, H, d, seed + 4, 1600.0 if family == hp.KDA else 16.0, "cuda"))
+    assert not k.is_contiguous() and not la.is_contiguous()
+    assert beta is None or not beta.is_contiguous()
+    slots = np.arange(nseg)[::-1].copy()
+    pool = hp.Pool.allocate(family, nseg, H, d, d, device="cuda", fill=CANARY)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hp.build_segment(family, k, v, la, dev_i64(offs), pool, dev_i32(slots), beta=beta, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    kn, vn = np64(k), np64(v)
+    ell_r, P_r, S_r = oracle.build_segments(family, kn, vn, full_log_alpha(family, la, N, H), offs,
+                                            beta=None if beta is None else np64(beta))
+    g_ell, g_S = np64(pool.log_scale[slots]), np64(pool.S[slots])
+    g_P = None if pool.P is None else np64(pool.P[slots])
+    worst = [0.0, 0.0, 0.0]
+    for s in range(nseg):
+        for h in range(H):
+            if family == hp.KDA:
+                # ell = 0 and P = T_C for this family
+                e = (rel_fro(g_S[s, h], S_r[s, h]), rel_fro(g_P[s, h], P_r[s, h]), float(np.max(np.abs(g_ell[s, h]))))
+            else:
+                e = record_errors(family, g_ell[s, h], None if g_P is None else g_P[s, h], g_S[s, h],
+                                  ell_r[s, h], None if P_r is None else P_r[s, h], S_r[s, h])
+            worst = [max(a, c) for a, c in zip(worst, e)]
+    say(f"[strided {layout}] family={family}: max err S {worst[0]:.2e}  T {worst[1]:.2e}  ell {worst[2]:.2e}")
+    assert max(worst) <= TOL[torch.bfloat16]
+
+
 # ----------------------------------------------------------------------------- pool indexing / errors
 
 def _gdn_pool(num_slots=6, H=2, d=64, seed=601):
