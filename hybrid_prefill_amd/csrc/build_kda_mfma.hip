@@ -98,7 +98,6 @@ template <> __device__ __forceinline__ f32x4 bload4<uint16_t>(__amdgpu_buffer_rs
     return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
                  __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
 }
-constexpr int RSRC_WORD3 = 0x00020000;   // 32-bit data format, as for every gfx9 buffer access
 template <typename XT> __device__ __forceinline__ float bload1(__amdgpu_buffer_rsrc_t r, int off);
 template <> __device__ __forceinline__ float bload1<float>(__amdgpu_buffer_rsrc_t r, int off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));

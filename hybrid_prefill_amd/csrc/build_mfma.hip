@@ -17,12 +17,20 @@
 //     Y_1 = (T_11 diag beta_1) W_1,    Y_2 = (T_22 diag beta_2) (W_2 - H_21 Y_1),
 // so each system needs two 32x32 inverse factors and H_21 per chunk.
 //
-// Work split: one 512-thread workgroup per (segment, head), two roles.
+// Work split: 512-thread workgroups, each taking every G-th (segment, head) unit
+// (G: the grid, a multiple of the CU count; at most TMAX units per workgroup) and
+// running their chunks as one stream, so that one unit's last chunk, its record
+// write and the next unit's first chunk overlap as any two chunks do.  At set-up
+// each thread reads one unit's offsets and slot: units with an out-of-range slot
+// raise the flag, empty units and units with bad offsets get their identity or NaN
+// record written by the whole workgroup, and the rest go into an LDS table in order.
+// Every wave then walks the same chunk stream through that table.  Two roles:
 //  * State waves 0-3 each own 32 columns of P and the same 32 columns of S
 //    as eight fp32 32x32 accumulator tiles that stay in registers for the
-//    whole segment (so the four waves do identical work).  Per chunk: W = K X
+//    whole unit (so the four waves do identical work).  Per chunk: W = K X
 //    (and V - e^g . W for S), the block solve against the factors (three
-//    dependent products), and the update.
+//    dependent products), and the update; after a unit's last chunk, its record
+//    and the reset of the accumulators to (I, 0).
 //  * Prep waves 4-7 build the next chunk's factors meanwhile: the decay
 //    prefix, the Gram blocks (A11, A22 in fp32, H_21 in bf16); the inverses
 //    of the 32x32 diagonal blocks (4x4 forward substitution and fp32 merges
@@ -44,12 +52,22 @@
 // 16-byte LDS read from a plain row-major tile, at row swz(lane).
 // X . I on the MFMA moves a token-major tile into the accumulator layout
 // (one column per lane); that gives K^T and the V term of W.
+#include <atomic>
+
 #include "gdn_mfma_common.h"
 
 namespace hypic {
 namespace {
 
 constexpr int NT = 512;    // 4 state waves + 4 prep waves
+constexpr int TMAX = 512;  // units per workgroup: one per thread at set-up
+
+// A unit of the chunk stream: tokens [tok, tok + n) of head `head`, record rec = slot H + head.
+// At the back of the table, records written at set-up: tok = 0 identity, 1 NaN.
+struct UnitEnt {
+    int64_t tok, n;
+    int32_t rec, head;
+};
 
 struct __align__(16) Smem {
     static constexpr bool kWithP = true;
@@ -65,41 +83,152 @@ struct __align__(16) Smem {
     float egs[2][CH];          // -e^{g_t} sigma_c: the K X factor of W (S columns)
     float egrs[2][CH];         // e^{G - g_t} / sigma_{c+1}: the update factor (S columns)
     float rs[2];               // sigma_c e^G when the scale is folded back into the state, else 1
-    float sig_fin;             // sigma after the last chunk
-    int64_t t0, n;
-    int32_t slot, state;
+    float sig_fin[2];          // sigma after the chunk of that parity (S = sigma X at a unit's end)
+    UnitEnt units[TMAX];       // the stream's units from the front, set-up records from the back
+    int64_t wsum[8];           // set-up: per wave, chunks of its valid units
+    int32_t wcnt[8][2];        // set-up: per wave, valid units and set-up records
+    int64_t steps;             // chunks in the stream
+    int32_t nvalid, nspecial;
 };
+
+// Wave-uniform copies of values that every lane holds alike (broadcast LDS reads).
+__device__ __forceinline__ int uni32(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// A position in the chunk stream: chunk c of the nc chunks of table unit q
+// (q = nvalid past the end), with that unit's tokens [tok0, tok0 + n) and head
+// copied out of the table when the cursor enters it.
+struct Cursor {
+    int q, head;
+    int64_t c, nc, tok0, n;
+};
+
+__device__ __forceinline__ void cursor_enter(const Smem &sm, int nvalid, Cursor &r) {
+    r.c = 0;
+    if (r.q < nvalid) {
+        r.tok0 = uni64(sm.units[r.q].tok);
+        r.n = uni64(sm.units[r.q].n);
+        r.head = uni32(sm.units[r.q].head);
+        r.nc = (r.n + CH - 1) / CH;
+    } else {
+        r.tok0 = r.n = r.nc = 0;
+        r.head = 0;
+    }
+}
+
+__device__ __forceinline__ Cursor cursor_first(const Smem &sm, int nvalid) {
+    Cursor r;
+    r.q = 0;
+    cursor_enter(sm, nvalid, r);
+    return r;
+}
+
+__device__ __forceinline__ void cursor_next(const Smem &sm, int nvalid, Cursor &r) {
+    if (++r.c >= r.nc) {
+        if (r.q < nvalid) ++r.q;
+        cursor_enter(sm, nvalid, r);
+    }
+}
+
+// The tokens of the cursor's chunk: first token, rows (1..CH), head.
+struct StepDesc {
+    int64_t tok;
+    int cl, head;
+};
+
+__device__ __forceinline__ StepDesc step_desc(const Cursor &r) {
+    const int64_t rem = r.n - r.c * CH;
+    return {r.tok0 + r.c * CH, rem < CH ? (int)rem : CH, r.head};
+}
 
 __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
     __shared__ Smem sm;
 
     const int th = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(th >> 6);
-    const int head = blockIdx.x % a.H;
-    const int seg = blockIdx.x / a.H;
-
-    if (th == 0) {
-        const int64_t o0 = a.seg_offsets[seg], o1 = a.seg_offsets[seg + 1];
-        const int32_t slot = a.dst_slots[seg];
-        int st = 0;
-        if (slot < 0 || slot >= a.num_slots) st = 1;
-        else if (o0 < 0 || o1 < o0 || o1 > a.num_tokens) st = 2;
-        if (st == 1) raise_flag(a.err_flag, HYPIC_EFLAG_SLOT_OUT_OF_RANGE);
-        if (st == 2) raise_flag(a.err_flag, HYPIC_EFLAG_BAD_OFFSETS);
-        sm.t0 = o0; sm.n = o1 - o0; sm.slot = slot; sm.state = st;
-    }
-    // the upper triangles of the T diag(beta) tiles stay zero for the whole segment
-    for (int e = th; e < (int)(sizeof(sm.TB) / 16); e += NT) reinterpret_cast<u32x4 *>(&sm.TB[0][0][0][0])[e] = u32x4{};
-    __syncthreads();
-    const int state = sm.state;
-    if (state == 1) return;
-    const int64_t t0 = sm.t0;
-    const int64_t n = state == 2 ? 0 : sm.n;
-    const int64_t slot = sm.slot;
-    const int64_t nc = (n + CH - 1) / CH;
+    const int lane = th & 63;
     const float nanv = __int_as_float(0x7fc00000);
-    const bool bad = state == 2;
-    const int64_t rec = slot * a.H + head;
+
+    // ---- set-up: thread th takes unit blockIdx.x + th G (the launch keeps that count
+    //      within TMAX = NT); the valid non-empty units go into the table in order
+    {
+        const int64_t U = (int64_t)a.num_segments * a.H, G = gridDim.x;
+        const int64_t u = (int64_t)blockIdx.x + (int64_t)th * G;
+        int kind = 0;   // 0: nothing to write, 1: chunk stream, 2: identity record, 3: NaN record
+        int64_t o0 = 0, o1 = 0, rec = 0;
+        int hd = 0;
+        if (u < U) {
+            const int64_t seg = u / a.H;
+            hd = (int)(u - seg * a.H);
+            o0 = a.seg_offsets[seg];
+            o1 = a.seg_offsets[seg + 1];
+            const int64_t slot = a.dst_slots[seg];
+            if (slot < 0 || slot >= a.num_slots) {
+                raise_flag(a.err_flag, HYPIC_EFLAG_SLOT_OUT_OF_RANGE);
+            } else {
+                rec = slot * a.H + hd;
+                if (o0 < 0 || o1 < o0 || o1 > a.num_tokens) {
+                    raise_flag(a.err_flag, HYPIC_EFLAG_BAD_OFFSETS);
+                    kind = 3;
+                } else {
+                    kind = o1 > o0 ? 1 : 2;
+                }
+            }
+        }
+        const uint64_t mv = __ballot(kind == 1), ms = __ballot(kind >= 2);
+        const uint64_t below = (1ull << lane) - 1;
+        int64_t nch = kind == 1 ? (o1 - o0 + CH - 1) / CH : 0;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) nch += __shfl_xor(nch, o);
+        if (lane == 0) {
+            sm.wcnt[w][0] = __popcll(mv);
+            sm.wcnt[w][1] = __popcll(ms);
+            sm.wsum[w] = nch;
+        }
+        // the upper triangles of the T diag(beta) tiles stay zero for the whole launch
+        for (int e = th; e < (int)(sizeof(sm.TB) / 16); e += NT) reinterpret_cast<u32x4 *>(&sm.TB[0][0][0][0])[e] = u32x4{};
+        __syncthreads();
+        int pv = 0, ps = 0;
+        for (int x = 0; x < w; ++x) {
+            pv += sm.wcnt[x][0];
+            ps += sm.wcnt[x][1];
+        }
+        if (kind == 1) sm.units[pv + __popcll(mv & below)] = UnitEnt{o0, o1 - o0, (int32_t)rec, hd};
+        if (kind >= 2) sm.units[TMAX - 1 - (ps + __popcll(ms & below))] = UnitEnt{kind - 2, 0, (int32_t)rec, hd};
+        if (th == 0) {
+            int nv = 0, ns = 0;
+            int64_t stp = 0;
+            for (int x = 0; x < NT / 64; ++x) {
+                nv += sm.wcnt[x][0];
+                ns += sm.wcnt[x][1];
+                stp += sm.wsum[x];
+            }
+            sm.nvalid = nv;
+            sm.nspecial = ns;
+            sm.steps = stp;
+        }
+        __syncthreads();
+    }
+    const int nvalid = uni32(sm.nvalid);
+    const int64_t steps = uni64(sm.steps);
+    {
+        // records of empty units (I, 0, ell 0) and of units with bad offsets (NaN)
+        const int nspecial = uni32(sm.nspecial);
+        for (int s = 0; s < nspecial; ++s) {
+            const bool nanr = uni64(sm.units[TMAX - 1 - s].tok) != 0;
+            const int64_t r = uni32(sm.units[TMAX - 1 - s].rec);
+            float *P = a.pool_P + r * D * D, *S = a.pool_S + r * D * D;
+            for (int x = th; x < D * D; x += NT) {
+                P[x] = nanr ? nanv : (x / D == x % D ? 1.0f : 0.0f);
+                S[x] = nanr ? nanv : 0.0f;
+            }
+            if (th == 0) a.pool_ell[r] = nanr ? nanv : 0.0f;
+        }
+    }
 
     if (w < 4) {
         // =============================== state waves ===============================
@@ -107,18 +236,16 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         const int col = 32 * w;
         f32x16 st[2][4];                          // [column block][row block], rows swizzled
         bf16x8 wb[2][2][2];                       // W of the chunk in flight as B operands [cb][tb][half]
-        {
-            const int h = (th & 63) >> 5, l32 = th & 31;
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        st[cb][mb][r] = (cb == 0 && swz(32 * mb + acc_row(r, h)) == col + l32) ? 1.0f : 0.0f;
-        }
+        // (P, S) = (I, 0), the state before a unit's first chunk
+#define HYPIC_STATE_RESET(HH, L32)                                                                   \
+    _Pragma("unroll") for (int cb_ = 0; cb_ < 2; ++cb_)                                              \
+        _Pragma("unroll") for (int mb_ = 0; mb_ < 4; ++mb_)                                          \
+            _Pragma("unroll") for (int r_ = 0; r_ < 16; ++r_)                                        \
+                st[cb_][mb_][r_] = (cb_ == 0 && swz(32 * mb_ + acc_row(r_, (HH))) == col + (L32)) ? 1.0f : 0.0f
+        HYPIC_STATE_RESET(lane >> 5, lane & 31);
         __syncthreads();                                            // prologue: chunk 0 staged
-        for (int64_t i = 0; i <= nc; ++i) {
+        Cursor cs = cursor_first(sm, nvalid);                      // chunk i (phase b)
+        for (int64_t i = 0; i <= steps; ++i) {
             int thv = th;
             asm volatile("" : "+v"(thv));
             const int h = (thv & 63) >> 5, l32 = thv & 31;
@@ -221,40 +348,81 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 }
             }
             lds_barrier();                                          // a -> b
-            // ---- phase b: W of chunk i
-            if (i < nc) {
+            // ---- phase b: W of chunk i; the record of the unit that ended with chunk i - 1
+            //      (physical row p of a tile holds channel swz(p); S = sigma X), then the
+            //      state of the next unit
+            const bool pend = i >= 1 && cs.c == 0;
+#define HYPIC_RECORD()                                                                               \
+    do {                                                                                             \
+        const int64_t rec_ = uni32(sm.units[cs.q - 1].rec);                                          \
+        const float sfin_ = sm.sig_fin[(int)((i - 1) & 1)];                                          \
+        /* tile row swz(32 mb + acc_row(r, h)) = 8 h + 32 mb + 16 (r >> 3) + 4 ((r >> 2) & 1) + (r & 3): \
+           one lane offset for every store, the row's constant part in the scalar offset */         \
+        const int lo_ = 4 * (8 * h * D + col + l32);                                                 \
+        _Pragma("unroll") for (int cb_ = 0; cb_ < 2; ++cb_) {                                        \
+            const __amdgpu_buffer_rsrc_t rs_ = __builtin_amdgcn_make_buffer_rsrc(                    \
+                (cb_ == 0 ? a.pool_P : a.pool_S) + rec_ * D * D, (short)0, D * D * 4, RSRC_WORD3);   \
+            const float sc_ = cb_ == 0 ? 1.0f : sfin_;                                               \
+            _Pragma("unroll") for (int mb_ = 0; mb_ < 4; ++mb_)                                      \
+                _Pragma("unroll") for (int r_ = 0; r_ < 16; ++r_)                                    \
+                    __builtin_amdgcn_raw_buffer_store_b32(                                           \
+                        __float_as_uint(st[cb_][mb_][r_] * sc_), rs_, lo_,                           \
+                        4 * D * (32 * mb_ + 16 * (r_ >> 3) + 4 * ((r_ >> 2) & 1) + (r_ & 3)), 0);     \
+        }                                                                                            \
+    } while (0)
+            if (i < steps) {
                 const int b = (int)(i & 1);
                 f32x16 z[2][2];                   // [column block][token block], rows swizzled
-                // K X: A operand = Km rows (tokens) swz(32 mb + lane), B = state rows in swizzled order
-#pragma unroll
-                for (int kb = 0; kb < 8; ++kb) {
-                    bf16x8 sb[2];
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb) sb[cb] = acc_to_b(st[cb][kb >> 1], kb & 1);
-#pragma unroll
-                    for (int mb = 0; mb < 2; ++mb) {
-                        const bf16x8 km = lds8(&sm.Km[b][kmo(swz(32 * mb + l32), 2 * kb + h)]);
-#pragma unroll
-                        for (int cb = 0; cb < 2; ++cb)
-                            z[cb][mb] = mfma(km, sb[cb], kb == 0 ? f32x16{} : z[cb][mb]);
+                if (cs.c == 0) {
+                    // a unit's first chunk: the previous unit's record goes out first (its
+                    // stores drain while the products below run); with X = (I, 0), W =
+                    // (K X_P, V) is this wave's columns of K and V, turned around on the MFMA
+                    if (pend) {
+                        HYPIC_RECORD();
+                        HYPIC_STATE_RESET(h, l32);
                     }
-                }
-                {
-                    // S block: W = V - e^g . (K X): scale, then add V turned around on the MFMA
-#pragma unroll
-                    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float4 e4 = tok4(sm.egs[b], mb, q, h);
-                            z[1][mb][4 * q] *= e4.x; z[1][mb][4 * q + 1] *= e4.y;
-                            z[1][mb][4 * q + 2] *= e4.z; z[1][mb][4 * q + 3] *= e4.w;
-                        }
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
                         const bf16x8 eye = eye_b(ks, h, l32);
 #pragma unroll
+                        for (int mb = 0; mb < 2; ++mb) {
+                            const int o = kmo(swz(32 * mb + l32), 4 * w + 2 * ks + h);
+                            z[0][mb] = mfma(lds8(&sm.Km[b][o]), eye, ks == 0 ? f32x16{} : z[0][mb]);
+                            z[1][mb] = mfma(lds8(&sm.Vm[b][o]), eye, ks == 0 ? f32x16{} : z[1][mb]);
+                        }
+                    }
+                } else {
+                    // K X: A operand = Km rows (tokens) swz(32 mb + lane), B = state rows in swizzled order
+#pragma unroll
+                    for (int kb = 0; kb < 8; ++kb) {
+                        bf16x8 sb[2];
+#pragma unroll
+                        for (int cb = 0; cb < 2; ++cb) sb[cb] = acc_to_b(st[cb][kb >> 1], kb & 1);
+#pragma unroll
+                        for (int mb = 0; mb < 2; ++mb) {
+                            const bf16x8 km = lds8(&sm.Km[b][kmo(swz(32 * mb + l32), 2 * kb + h)]);
+#pragma unroll
+                            for (int cb = 0; cb < 2; ++cb)
+                                z[cb][mb] = mfma(km, sb[cb], kb == 0 ? f32x16{} : z[cb][mb]);
+                        }
+                    }
+                    {
+                        // S block: W = V - e^g . (K X): scale, then add V turned around on the MFMA
+#pragma unroll
                         for (int mb = 0; mb < 2; ++mb)
-                            z[1][mb] = mfma(lds8(&sm.Vm[b][kmo(swz(32 * mb + l32), 4 * w + 2 * ks + h)]), eye, z[1][mb]);
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const float4 e4 = tok4(sm.egs[b], mb, q, h);
+                                z[1][mb][4 * q] *= e4.x; z[1][mb][4 * q + 1] *= e4.y;
+                                z[1][mb][4 * q + 2] *= e4.z; z[1][mb][4 * q + 3] *= e4.w;
+                            }
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks) {
+                            const bf16x8 eye = eye_b(ks, h, l32);
+#pragma unroll
+                            for (int mb = 0; mb < 2; ++mb)
+                                z[1][mb] = mfma(lds8(&sm.Vm[b][kmo(swz(32 * mb + l32), 4 * w + 2 * ks + h)]), eye, z[1][mb]);
+                        }
                     }
                 }
                 // kept across the barrier as bf16 B operands: half the registers of W
@@ -264,22 +432,14 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                         for (int half = 0; half < 2; ++half) wb[cb][mb][half] = acc_to_b(z[cb][mb], half);
+            } else if (pend) {
+                HYPIC_RECORD();                                     // the last unit
             }
             __syncthreads();                                        // b -> next a
+            cursor_next(sm, nvalid, cs);
         }
-        // ---- record: physical row p of a tile holds channel swz(p); S = sigma X
-        const int h = (th & 63) >> 5, l32 = th & 31;
-        const float sfin = sm.sig_fin;
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            float *dst = (cb == 0 ? a.pool_P : a.pool_S) + rec * D * D;
-            const float sc = cb == 0 ? 1.0f : sfin;
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    dst[(int64_t)swz(32 * mb + acc_row(r, h)) * D + col + l32] = bad ? nanv : st[cb][mb][r] * sc;
-        }
+#undef HYPIC_RECORD
+#undef HYPIC_STATE_RESET
     } else {
         // =============================== prep waves ===============================
         // Their work is a chain of short dependent steps that shares each SIMD with a
@@ -288,28 +448,28 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         const int pw = w - 4;
         const int pl = th & 63;
         // every prep wave loads la and beta of a chunk itself (lane = token)
-        const float *bq = a.beta ? a.beta + (t0 + pl) * a.b_st + head * a.b_sh : nullptr;
-        const float *lq = a.log_alpha ? a.log_alpha + (t0 + pl) * a.la_st + head * a.la_sh : nullptr;
         float lar = 0.f, br = 0.f;
-#define HYPIC_FETCH_G(BASE)                                                                          \
+#define HYPIC_FETCH_G(DESC)                                                                          \
     do {                                                                                             \
-        const int64_t base_ = (BASE), rem_ = n - base_;                                              \
-        const int cl_ = rem_ < CH ? (int)rem_ : CH;                                                  \
-        br = pl < cl_ ? (bq ? bq[base_ * a.b_st] : 1.0f) : 0.0f;                                     \
-        lar = (pl < cl_ && lq) ? lq[base_ * a.la_st] : 0.0f;                                         \
+        const StepDesc d_ = (DESC);                                                                  \
+        const int64_t tk_ = d_.tok + pl;                                                             \
+        br = pl < d_.cl ? (a.beta ? a.beta[tk_ * a.b_st + d_.head * a.b_sh] : 1.0f) : 0.0f;          \
+        lar = (pl < d_.cl && a.log_alpha) ? a.log_alpha[tk_ * a.la_st + d_.head * a.la_sh] : 0.0f;   \
     } while (0)
-        if (nc > 0) HYPIC_FETCH_G(0);
+        Cursor cur = cursor_first(sm, nvalid);                     // chunk i of the stream
+        Cursor nxt = cur;                                           // chunk i + 1
+        cursor_next(sm, nvalid, nxt);
+        if (steps > 0) HYPIC_FETCH_G(step_desc(cur));
         if (pw == 0) {
             // ---- wave 4: loads keys and values, the decay factors and ell in phase a;
             //      turns K^T around for tokens 0-31 of the chunk in phase b.
             // Keys and values go straight from HBM into Km/Vm (global_load_lds): the
             // instruction for rows 4u .. 4u + 3 lands lane l's 16 bytes in row 4u + l / 16,
             // slot l % 16, so the lane loads the granule that kmo puts there.  Rows past
-            // the segment repeat its last row (finite values; their beta is zero).
-            const u16 *kh = static_cast<const u16 *>(a.k) + t0 * a.k_st + head * a.k_sh;
-            const u16 *vh = static_cast<const u16 *>(a.v) + t0 * a.v_st + head * a.v_sh;
+            // the unit repeat its last row (finite values; their beta is zero).
+            const u16 *kp = static_cast<const u16 *>(a.k), *vp = static_cast<const u16 *>(a.v);
             // full chunks (the common case): element offsets of this lane's sixteen
-            // pieces, relative to the chunk's first row, fixed for the whole segment
+            // pieces, relative to the chunk's first row, fixed for the whole launch
             const bool small_st = (int64_t)CH * (a.k_st > a.v_st ? a.k_st : a.v_st) < (1LL << 30);
             uint32_t ko[16], vo[16];
 #pragma unroll
@@ -318,17 +478,18 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 ko[u] = small_st ? (uint32_t)(t * a.k_st + 8 * g) : 0u;
                 vo[u] = small_st ? (uint32_t)(t * a.v_st + 8 * g) : 0u;
             }
-#define HYPIC_LOAD_KV(BASE, BUF)                                                                     \
+#define HYPIC_LOAD_KV(DESC, BUF)                                                                     \
     do {                                                                                             \
-        const int64_t base_ = (BASE), rem_ = n - base_;                                              \
-        const u16 *kc_ = kh + base_ * a.k_st, *vc_ = vh + base_ * a.v_st;                            \
-        if (rem_ >= CH && small_st) {                                                                \
+        const StepDesc d_ = (DESC);                                                                  \
+        const u16 *kc_ = kp + d_.tok * a.k_st + d_.head * a.k_sh;                                    \
+        const u16 *vc_ = vp + d_.tok * a.v_st + d_.head * a.v_sh;                                    \
+        if (d_.cl == CH && small_st) {                                                               \
             _Pragma("unroll") for (int u_ = 0; u_ < 16; ++u_) {                                      \
                 __builtin_amdgcn_global_load_lds(kc_ + ko[u_], &sm.Km[BUF][4 * u_ * KML], 16, 0, kLoadNT); \
                 __builtin_amdgcn_global_load_lds(vc_ + vo[u_], &sm.Vm[BUF][4 * u_ * KML], 16, 0, kLoadNT); \
             }                                                                                        \
         } else {                                                                                     \
-            const int cl_ = rem_ < CH ? (int)rem_ : CH;                                              \
+            const int cl_ = d_.cl;                                                                   \
             int l_ = pl;                                                                             \
             asm volatile("" : "+v"(l_));                                                             \
             const int r_ = l_ >> 4, p_ = l_ & 15;                                                    \
@@ -342,26 +503,26 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
             }                                                                                        \
         }                                                                                            \
     } while (0)
-            double ell = 0.0;     // this lane's tokens; summed over the wave at the end
+            double ell = 0.0;     // this lane's tokens of the unit; summed over the wave at its end
             // S = sigma X for the S columns: the decay e^G of each chunk is carried in
             // sigma and folded into X only when sigma would drop below 2^-60, so the
             // state waves do not rescale X every chunk.
             float sig = 1.0f;
-            if (pl == 0) sm.sig_fin = 1.0f;
-            if (nc > 0) {
-                HYPIC_LOAD_KV(0, 0);
+            if (steps > 0) {
+                HYPIC_LOAD_KV(step_desc(cur), 0);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
             __syncthreads();                                        // prologue: chunk 0 staged
-            for (int64_t i = 0; i <= nc; ++i) {
+            for (int64_t i = 0; i <= steps; ++i) {
                 int thv = th;
                 asm volatile("" : "+v"(thv));
                 const int l = thv & 63;
                 // ---- phase a: decay factors of chunk i; keys and values of chunk i + 1 start
-                if (i < nc) {
+                if (i < steps) {
                     const int b = (int)(i & 1);
                     const float la_i = lar, b_i = br;
-                    if (i + 1 < nc) HYPIC_LOAD_KV((i + 1) * CH, b ^ 1);     // lands during this chunk
+                    if (i + 1 < steps) HYPIC_LOAD_KV(step_desc(nxt), b ^ 1);   // lands during this chunk
+                    if (cur.c == 0) sig = 1.0f;
                     const float gv = wave_prefix_sum(la_i);
                     sm.pv[0][0][l] = gv;
                     sm.pv[0][1][l] = b_i;
@@ -373,34 +534,40 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     sm.egrs[b][l] = __expf(gt - gv) * inv;
                     if (l == 63) {
                         sm.rs[b] = fold ? sp : 1.0f;
-                        sm.sig_fin = fold ? 1.0f : sp;
+                        sm.sig_fin[b] = fold ? 1.0f : sp;
                     }
                     sig = fold ? 1.0f : sp;
                     ell += (double)la_i;
+                    if (cur.c == cur.nc - 1) {
+                        // the unit's ell
+#pragma unroll
+                        for (int o = 32; o >= 1; o >>= 1) ell += __shfl_xor(ell, o);
+                        if (l == 0) a.pool_ell[uni32(sm.units[cur.q].rec)] = (float)ell;
+                        ell = 0.0;
+                    }
                 }
                 lds_barrier();                                      // a -> b
                 // ---- phase b: keys and values of chunk i + 1 land in the other buffers;
                 //      gates of chunk i + 1 (read in phase b, so that their wait falls at
                 //      its end); factors of block 0 of the P system
-                if (i + 1 < nc) HYPIC_FETCH_G((i + 1) * CH);
-                if (i < nc) prep_kt(sm, (int)(i & 1), 0, l);
+                if (i + 1 < steps) HYPIC_FETCH_G(step_desc(nxt));
+                if (i < steps) prep_kt(sm, (int)(i & 1), 0, l);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // chunk i + 1 has landed
                 __syncthreads();                                    // b -> next a
+                cur = nxt;
+                cursor_next(sm, nvalid, nxt);
             }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) ell += __shfl_xor(ell, o);
-            if (th == 256) a.pool_ell[rec] = bad ? nanv : (float)ell;
 #undef HYPIC_LOAD_KV
         } else {
             // ---- waves 5-7: a Gram block in phase a (waves 5 and 7 the diagonal blocks,
             //      which they also start inverting; wave 6 H_21); in phase b waves 5 and 7
             //      finish their block's inverse, wave 6 turns K^T around for tokens 32-63
             __syncthreads();                                        // prologue: chunk 0 staged
-            for (int64_t i = 0; i <= nc; ++i) {
+            for (int64_t i = 0; i <= steps; ++i) {
                 int thv = th;
                 asm volatile("" : "+v"(thv));
                 const int l = thv & 63;
-                if (i < nc) {
+                if (i < steps) {
                     const int b = (int)(i & 1);
                     const float la_i = lar, b_i = br;
                     sm.pv[pw][0][l] = wave_prefix_sum(la_i);
@@ -413,10 +580,11 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     }
                 }
                 lds_barrier();                                      // a -> b
-                if (i + 1 < nc) HYPIC_FETCH_G((i + 1) * CH);        // gates of chunk i + 1
-                if (i < nc && pw != 2) prep_invert2<true>(inv_ctx(sm, (int)(i & 1), pw >> 1, pw), l);
-                if (i < nc && pw == 2) prep_kt(sm, (int)(i & 1), 1, l);
+                if (i + 1 < steps) HYPIC_FETCH_G(step_desc(nxt));   // gates of chunk i + 1
+                if (i < steps && pw != 2) prep_invert2<true>(inv_ctx(sm, (int)(i & 1), pw >> 1, pw), l);
+                if (i < steps && pw == 2) prep_kt(sm, (int)(i & 1), 1, l);
                 __syncthreads();                                    // b -> next a
+                cursor_next(sm, nvalid, nxt);
             }
         }
 #undef HYPIC_FETCH_G
@@ -425,6 +593,19 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Compute units of the current device, read once per device.
+int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 }  // namespace
 
 hipError_t launch_build_mfma(const BuildArgs &a, hipStream_t stream, bool *taken) {
@@ -432,9 +613,15 @@ hipError_t launch_build_mfma(const BuildArgs &a, hipStream_t stream, bool *taken
     if (a.family != HYPIC_GDN || a.kv_dtype != HYPIC_BF16 || a.dk != 128 || a.dv != 128) return hipSuccess;
     if (!aligned16(a.k) || !aligned16(a.v) || (a.k_st % 8) || (a.k_sh % 8) || (a.v_st % 8) || (a.v_sh % 8))
         return hipSuccess;
+    if (a.num_slots * a.H > 0x7fffffffLL) return hipSuccess;   // record index kept in 32 bits
     *taken = true;
-    const dim3 grid((unsigned)((int64_t)a.num_segments * a.H));
-    hipLaunchKernelGGL(gdn_build_mfma_kernel, grid, dim3(NT), 0, stream, a);
+    // G workgroups, a multiple of the CU count (one resident workgroup per CU), each
+    // taking at most TMAX of the U units
+    const int64_t U = (int64_t)a.num_segments * a.H;
+    const int64_t cus = cu_count();
+    int64_t G = cus * ((U + cus * TMAX - 1) / (cus * TMAX));
+    if (G > U) G = U;
+    hipLaunchKernelGGL(gdn_build_mfma_kernel, dim3((unsigned)G), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -94,6 +94,10 @@ template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t *
 // against about 6.3 TB/s without.
 constexpr int kLoadNT = 2;
 
+// Word 3 of a raw buffer resource (__builtin_amdgcn_make_buffer_rsrc): the 32-bit
+// data format, as for every gfx9 buffer access.
+constexpr int RSRC_WORD3 = 0x00020000;
+
 template <typename T> __device__ __forceinline__ T load_nt(const T *p) {
     typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));

@@ -172,6 +172,92 @@ def test_mfma_build_nan_inf_inputs_stay_in_their_record():
     assert math.isfinite(float(pool.log_scale[1, 3]))
 
 
+def _expect_special(pool, slot, kind):
+    """Record of an empty segment (identity) or of bad offsets (NaN), every head."""
+    if kind == "nan":
+        for t in (pool.S, pool.P, pool.log_scale):
+            assert torch.all(torch.isnan(t[slot]))
+    else:
+        P = pool.P[slot]
+        assert torch.all(pool.S[slot] == 0) and torch.all(pool.log_scale[slot] == 0)
+        assert torch.equal(P, torch.eye(D, device="cuda").expand_as(P))
+
+
+def test_mfma_build_unit_stream_mixed():
+    """More (segment, head) units than workgroups (40 x 32 = 1280 units, five per
+    workgroup, each running its units' chunks back to back): lengths around the chunk
+    edges, empty segments, a decreasing offset pair and an end past the stream (NaN
+    records, flag), an out-of-range slot (flag, nothing written).  Every record against
+    the oracle on its own tokens; the slots nobody writes keep their canary bytes."""
+    H = 32
+    base = [0, 1, 63, 64, 65, 127, 128, 129, 200, 300]
+    lens = [base[(7 * i) % len(base)] for i in range(40)]
+    k, v, beta, la, offs = _stream(lens, H, 1107)
+    N = int(offs[-1])
+    offs = offs.copy()
+    offs[21] = offs[20] - 10                  # segment 20: decreasing; segment 21 longer by 10
+    offs[40] = N + 5                          # segment 39: past the stream
+    nseg = 40
+    num_slots = nseg + 4
+    slots = np.random.default_rng(1107).permutation(num_slots)[:nseg].astype(np.int32)
+    slots[13] = num_slots + 3                 # out of range
+    err = _err()
+    pool = _build(k, v, beta, la, offs, slots, num_slots, err)
+    assert int(err.item()) == hp.EFLAG_BAD_OFFSETS | hp.EFLAG_SLOT_OUT_OF_RANGE
+    unused = sorted(set(range(num_slots)) - set(int(x) for x in slots))
+    for t in (pool.S, pool.P, pool.log_scale):
+        assert torch.all(t[unused] == CANARY)
+    kn, vn, bn, lan = np64(k), np64(v), np64(beta), np64(la)
+    worst, counts = 0.0, {"stream": 0, "empty": 0, "nan": 0}
+    for s in range(nseg):
+        o0, o1 = int(offs[s]), int(offs[s + 1])
+        if s == 13:
+            continue
+        if o1 < o0 or o1 > N:
+            _expect_special(pool, slots[s], "nan")
+            counts["nan"] += 1
+        elif o1 == o0:
+            _expect_special(pool, slots[s], "empty")
+            counts["empty"] += 1
+        else:
+            ref = oracle.build_segments(oracle.GDN, kn[o0:o1], vn[o0:o1], lan[o0:o1], [0, o1 - o0], beta=bn[o0:o1])
+            for h in range(H):
+                worst = max(worst, max(_check_record(pool, slots[s], ref, 0, h)))
+            counts["stream"] += 1
+    say(f"[mfma unit stream] {nseg * H} units: {counts}, max err {worst:.2e}")
+    assert counts["nan"] == 2 and counts["empty"] >= 3
+
+
+def test_mfma_build_unit_stream_full_table():
+    """4096 segments x 32 heads = 131072 units: 256 workgroups of exactly 512 units each
+    (one per set-up thread).  Lengths 0-3 and 64-65 tokens; the empty segments' records
+    checked in full, a sample of the others (among them every unit of set-up thread 511)
+    against the oracle."""
+    H, nseg = 32, 4096
+    rng = np.random.default_rng(1108)
+    lens = rng.choice([0, 1, 2, 3, 64, 65], size=nseg).tolist()
+    k, v, beta, la, offs = _stream(lens, H, 1108)
+    err = _err()
+    pool = _build(k, v, beta, la, offs, np.arange(nseg, dtype=np.int32), nseg, err)
+    assert int(err.item()) == 0
+    empty = [s for s in range(nseg) if lens[s] == 0]
+    _expect_special(pool, empty, "empty")
+    units = list(range(511 * 256, 512 * 256, 7)) + rng.choice(nseg * H, size=120, replace=False).tolist()
+    worst, n_checked = 0.0, 0
+    for u in units:
+        s, h = divmod(int(u), H)
+        o0, o1 = int(offs[s]), int(offs[s + 1])
+        if o1 == o0:
+            continue
+        ref = oracle.build_segments(oracle.GDN, np64(k[o0:o1, h:h + 1]), np64(v[o0:o1, h:h + 1]),
+                                    np64(la[o0:o1, h:h + 1]), [0, o1 - o0], beta=np64(beta[o0:o1, h:h + 1]))
+        e = record_errors(oracle.GDN, float(pool.log_scale[s, h]), np64(pool.P[s, h]), np64(pool.S[s, h]),
+                          ref[0][0, 0], ref[1][0, 0], ref[2][0, 0])
+        assert max(e) <= TOL[BF], (s, h, e)
+        worst, n_checked = max(worst, max(e)), n_checked + 1
+    say(f"[mfma unit table] {nseg * H} units, {len(empty)} empty segments, {n_checked} sampled: max err {worst:.2e}")
+
+
 # ----------------------------------------------------------------------------- compose, d = 128
 
 def _random_pool(nslots, H, seed):
