@@ -65,34 +65,83 @@ CSRC = os.path.join(ROOT, "hybrid_prefill_amd", "csrc")
 # copy of known size in the same process).  Each summary records a hash of the
 # kernel's sources; when they have changed since, the bytes are unknown (null) until
 # the counters are taken again.  key -> (kernel name fragment, grid in threads as the
-# counter CSV reports it (None: any), sources, workload)
+# counter CSV reports it (None: any), bench phase (see PHASES), sources, workload)
 _GDN_SRC = ("build_mfma.hip", "gdn_mfma_common.h", "hypic_internal.h")
 _FWD_SRC = ("build_fwd_mfma.hip", "gdn_mfma_common.h", "hypic_internal.h")
 _CMP_SRC = ("compose_mfma.hip", "hypic_internal.h")
 _SD_SRC = ("build_sd_mfma.hip", "hypic_internal.h")
 TRAFFIC_KERNELS = {
-    "gdn_build_h32_d128_16x2048": ("gdn_build_mfma_kernel(", 262144, _GDN_SRC,
+    "gdn_build_h32_d128_16x2048": ("gdn_build_mfma_kernel(", None, "main", _GDN_SRC,
                                    "GDN build, H=32, d=128, bf16, 16 x 2048 tokens"),
-    "gdn_compose_h32_d128_chain16": ("compose_sliced_mfma_kernel", 32768, _CMP_SRC,
+    "gdn_compose_h32_d128_chain16": ("compose_sliced_mfma_kernel", 32768, "main", _CMP_SRC,
                                      "GDN compose of the 16-segment chain, H=32, d=128, fp32 records"),
-    "gdn_forward_h32_d128_16x2048": ("gdn_chunk_mfma_kernel<false, true>", 262144, _FWD_SRC,
+    "gdn_forward_h32_d128_16x2048": ("gdn_chunk_mfma_kernel<false, true>", 262144, "forward", _FWD_SRC,
                                      "GDN prefill forward, outputs only, H=32, d=128, bf16, 16 x 2048 tokens"),
-    "gdn_forward_records_h32_d128_16x2048": ("gdn_chunk_mfma_kernel<true, true>", 393216, _FWD_SRC,
+    "gdn_forward_records_h32_d128_16x2048": ("gdn_chunk_mfma_kernel<true, true>", 393216, "forward", _FWD_SRC,
                                              "GDN prefill forward with record side-outputs, H=32, d=128, bf16, "
                                              "16 x 2048 tokens"),
-    "gdn_compose_pool4096_h32_d128_64x32": ("compose_dense_mfma_kernel<false, false>", 524288, _CMP_SRC,
+    "gdn_compose_pool4096_h32_d128_64x32": ("compose_dense_mfma_kernel<false, false>", 524288, "compose", _CMP_SRC,
                                             "GDN compose, 4096-slot pool, 64 requests x 32 slots, H=32, d=128"),
-    "scalar_build_h16_d128_8x2048": ("sd_build_mfma_kernel<0, 2>", 131072, _SD_SRC,
+    "scalar_build_h16_d128_8x2048": ("sd_build_mfma_kernel<0, 2>", 131072, "sd", _SD_SRC,
                                      "scalar-decay build, H=16, d=128, bf16, 8 x 2048 tokens"),
-    "diagonal_build_h16_d128_8x2048": ("sd_build_mfma_kernel<1, 2>", 131072, _SD_SRC,
+    "diagonal_build_h16_d128_8x2048": ("sd_build_mfma_kernel<1, 2>", 131072, "sd", _SD_SRC,
                                        "diagonal-gate build, H=16, d=128, bf16, 8 x 2048 tokens"),
-    "conv_warmup_rag_8305x4096_k4": ("conv_warmup_vec_kernel", None, ("conv_warmup.hip", "hypic_internal.h"),
+    "conv_warmup_rag_8305x4096_k4": ("conv_warmup_vec_kernel", None, "rag", ("conv_warmup.hip", "hypic_internal.h"),
                                      "conv warm-up of the RAG mix, 8305 boundaries x 4096 channels, kernel 4, bf16"),
-    "gdn_build_rag_cold_2584seg": ("gdn_build_mfma_kernel(", 42336256, _GDN_SRC,
+    "gdn_build_rag_cold_2584seg": ("gdn_build_mfma_kernel(", None, "rag", _GDN_SRC,
                                    "GDN build of the RAG mix's 2584 cold segments (128-1024 tokens), H=32, d=128"),
-    "gdn_compose_rag_128req": ("compose_dense_mfma_kernel<false, false>", 1048576, _CMP_SRC,
+    "gdn_compose_rag_128req": ("compose_dense_mfma_kernel<false, false>", 1048576, "rag", _CMP_SRC,
                                "GDN compose of the RAG mix's 128 chains (24-96 slots), H=32, d=128"),
 }
+
+# Bench phases.  The GDN build runs the same grid (a multiple of the CU count) for
+# every workload above a few hundred (segment, head) units, so a profile cannot tell
+# the legs apart by kernel and grid; each leg, and the untimed set-up inside a leg,
+# therefore starts with a marker launch: the streaming-copy microbenchmark over 16
+# bytes with as many 512-thread workgroups as the phase's position in PHASES (plus
+# one).  The profile summaries attribute every dispatch to the last marker before it.
+PHASES = ("main", "forward", "compose_setup", "compose", "sd", "rag_setup", "rag", "convexact_setup", "convexact",
+          "kda", "peaks")
+_PEAKS = None
+_MARK_BUF = None
+
+
+def peaks_lib():
+    """libhypic_peaks.so: the measured-peak microbenchmarks (outside the library's ABI)."""
+    global _PEAKS
+    if _PEAKS is None:
+        from hybrid_prefill_amd import _build
+        L = ctypes.CDLL(_build.PEAKS_LIB)
+        L.hypic_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+        L.hypic_peak_mfma.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        L.hypic_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                      ctypes.c_void_p]
+        _PEAKS = L
+    return _PEAKS
+
+
+def mark(phase):
+    """The marker launch of a bench phase, on the current stream."""
+    global _MARK_BUF
+    if _MARK_BUF is None:
+        _MARK_BUF = torch.zeros(8, dtype=torch.float32, device="cuda")
+    rc = peaks_lib().hypic_peak_copy(_MARK_BUF.data_ptr(), _MARK_BUF.data_ptr() + 16, 16, PHASES.index(phase) + 1,
+                                     torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, "marker launch failed"
+
+
+def dispatch_phases(rows):
+    """rows: (dispatch id, kernel name, grid in threads, ...) in any order -> {dispatch id:
+    phase or None}, markers themselves left out."""
+    phase, out = None, {}
+    for r in sorted(rows, key=lambda t: t[0]):
+        did, name, grid = r[0], r[1], r[2]
+        if "peak_copy_kernel" in name and grid % 512 == 0 and 1 <= grid // 512 <= len(PHASES):
+            phase = PHASES[grid // 512 - 1]
+            continue
+        out[did] = phase
+    return out
 
 
 def source_sha(names) -> str:
@@ -118,7 +167,7 @@ def committed_traffic(key="gdn_build_h32_d128_16x2048"):
         return None
     m_sha = re.search(r"kernel source sha256\[:16\]: `([0-9a-f]{16})`", text)
     m_tot = re.search(r"HBM bytes per launch: ([0-9.]+) MB", text)
-    if not (m_sha and m_tot) or m_sha.group(1) != source_sha(TRAFFIC_KERNELS[key][2]):
+    if not (m_sha and m_tot) or m_sha.group(1) != source_sha(TRAFFIC_KERNELS[key][3]):
         return None
     return float(m_tot.group(1)) * 1e6
 
@@ -274,6 +323,7 @@ def timed_steps(run, steps):
 
 
 def bench_main(args):
+    mark("main")
     w = gdn_workload()
     for _ in range(args.warmup):
         gdn_step(w)
@@ -328,6 +378,7 @@ def bench_forward(args, w, build_ms):
     alone and with the records as side-outputs; beside them the record build alone
     (the main leg's kernel).  besthub article, paragraph 7: the records' one-time
     construction costs a small fraction of a forward pass."""
+    mark("forward")
     st, pool = w["st"], w["pool"]
     N, H, dk, dv, nseg = w["N"], w["H"], w["dk"], w["dv"], w["nseg"]
     q = synth.keys(N, H, dk, torch.bfloat16, 3017, "cuda")
@@ -358,12 +409,14 @@ def bench_forward(args, w, build_ms):
 
 def bench_compose_pool(args, slots=4096, H=32, d=128, R=64, m=32, seg_len=64, seed=401):
     """Pool of GDN records (filled untimed by the build), R requests x m slot ids."""
+    mark("compose_setup")
     st = synth.gdn_stream([seg_len] * slots, H, d, d, torch.bfloat16, seed, 0.01, "cuda")
     pool = hp.Pool.allocate(hp.GDN, slots, H, d, d, device="cuda")
     hp.build_segment(hp.GDN, st.k, st.v, st.log_alpha, torch.as_tensor(st.seg_offsets).cuda(), pool,
                      torch.arange(slots, dtype=torch.int32, device="cuda"), beta=st.beta)
     del st
     torch.cuda.synchronize()
+    mark("compose")
     rng = np.random.Generator(np.random.PCG64(seed))
     ids = torch.as_tensor(rng.integers(0, slots, size=R * m).astype(np.int32)).cuda()
     offs = torch.arange(0, R * m + 1, m, dtype=torch.int64, device="cuda")
@@ -390,6 +443,7 @@ def bench_sd(args, H=16, d=128, nseg=8, seg_len=2048, seed=201, copies=3):
     """Scalar and diagonal builds + their 8-segment chains.  The inputs are
     rotated over `copies` seeded copies so that the timed working set exceeds
     the 256 MB Infinity Cache (one copy of k, v and the gates would fit)."""
+    mark("sd")
     out = []
     N = nseg * seg_len
     ks = [synth.keys(N, H, d, torch.bfloat16, seed * 10 + 1 + 100 * c, "cuda") for c in range(copies)]
@@ -449,6 +503,7 @@ def bench_rag(args, R=128, pool_slots=4096, H=32, d=128, C=4096, K=4, seed=501):
     """RAG-shaped step: 128 requests of 24-96 segments (128-1024 tokens), 70 %
     cache hits from a 4096-slot pool built untimed, 30 % cold segments built in
     the step, conv warm-up at every boundary, all chains composed."""
+    mark("rag_setup")
     from hybrid_prefill_amd import rag
     plan = synth.rag_plan(R, pool_slots, seed)
     n_cold = len(plan.cold_lengths)
@@ -471,6 +526,7 @@ def bench_rag(args, R=128, pool_slots=4096, H=32, d=128, C=4096, K=4, seed=501):
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     timer = KernelTimer()
     args_ = (step, pool, cold.k, cold.v, cold.beta, cold.log_alpha, tails, heads, wconv, out_S, conv_out)
+    mark("rag")
     for _ in range(max(1, args.warmup)):
         rag.prefill_step(*args_, err_flag=err)
     torch.cuda.synchronize()
@@ -515,6 +571,7 @@ def bench_conv_exact(args, R=32, pool_segs=512, H=32, d=128, K=4, seed=601):
     the head tokens applied inside the compose (hypic_compose_chain_heads); beside it
     the plain chain of the same records, and the unfused form (a record per head,
     chains of 2m records)."""
+    mark("convexact_setup")
     from hybrid_prefill_amd import conv_exact as ce
     rng = np.random.Generator(np.random.PCG64(seed))
     lens = rng.integers(128, 1025, size=pool_segs)
@@ -532,6 +589,7 @@ def bench_conv_exact(args, R=32, pool_segs=512, H=32, d=128, K=4, seed=601):
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     plain_offs = torch.as_tensor(np.concatenate([[0], np.cumsum([len(ch) for ch in chains])]).astype(np.int64)).cuda()
     plain_ids = torch.as_tensor(np.concatenate(chains)).cuda()
+    mark("convexact")
     for _ in range(max(1, args.warmup)):
         ce.reuse(c, plan, pool, out_S=out, err_flag=err)
     torch.cuda.synchronize()
@@ -570,6 +628,7 @@ def bench_kda(args, H=16, d=128, nseg=8, seg_len=2048, seed=701):
     record (T_C, S) and the 8-segment chain.  The build is the chunked kernel on the
     fp32 matrix cores; its roofline counts the definition's 5 d_k (d_k + d_v) FLOP per
     token-head against the fp32 matrix peak."""
+    mark("kda")
     N = nseg * seg_len
     k = synth.keys(N, H, d, torch.bfloat16, seed, "cuda")
     v = synth.values(N, H, d, torch.bfloat16, seed + 1, "cuda")
@@ -693,11 +752,8 @@ def measured_peaks():
     depths and cache policies), a streaming copy of 1 GiB with the same loads and
     non-temporal stores (the rate of a kernel that writes as much as it reads), and a
     loop of bf16 32x32x16 matrix-core products on every SIMD (libhypic_peaks.so)."""
-    from hybrid_prefill_amd import _build
-    L = ctypes.CDLL(_build.PEAKS_LIB)
-    L.hypic_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
-    L.hypic_peak_mfma.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
-    L.hypic_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+    mark("peaks")
+    L = peaks_lib()
     stream = torch.cuda.current_stream().cuda_stream
     buf = torch.empty(1 << 30, dtype=torch.float32, device="cuda").uniform_()
     dst = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -764,22 +820,24 @@ def summarize_traffic(fetch_csv, write_csv, out_dir):
                        for r in csv.DictReader(open(path))), key=lambda t: t[0])
 
     F, W = load(fetch_csv), load(write_csv)
+    phase_f, phase_w = dispatch_phases(F), dispatch_phases(W)
 
     def first_copy(rows):
         return next(v for _, n, g, v in rows if "__amd_rocclr_copyBuffer" in n and g == 131072)
 
-    def per_launch(rows, frag, grid):
-        vals = [v for _, n, g, v in rows if frag in n and (grid is None or g == grid)]
+    def per_launch(rows, phases, frag, grid, phase):
+        vals = [v for d, n, g, v in rows
+                if frag in n and (grid is None or g == grid) and phases.get(d, "marker") == phase]
         return (float(np.median(vals)) if vals else None), len(vals)
 
     copy_bytes = float(1 << 30)
     f_copy, w_copy = first_copy(F), first_copy(W)
     sf, sw = copy_bytes / (f_copy * 1024), copy_bytes / (w_copy * 1024)
-    for key, (frag, grid, sources, title) in TRAFFIC_KERNELS.items():
-        f_k, nf = per_launch(F, frag, grid)
-        w_k, nw = per_launch(W, frag, grid)
+    for key, (frag, grid, phase, sources, title) in TRAFFIC_KERNELS.items():
+        f_k, nf = per_launch(F, phase_f, frag, grid, phase)
+        w_k, nw = per_launch(W, phase_w, frag, grid, phase)
         if f_k is None or w_k is None:
-            log(f"summarize-traffic: no launches of {frag} (grid {grid}); {key} skipped")
+            log(f"summarize-traffic: no launches of {frag} (grid {grid}, phase {phase}); {key} skipped")
             continue
         rd, wr = f_k * 1024 * sf, w_k * 1024 * sw
         alg = algorithmic_bytes(key)
@@ -794,7 +852,8 @@ def summarize_traffic(fetch_csv, write_csv, out_dir):
                  "python $REPO/bench.py --summarize-traffic $REPO/gpurun_out/pmc_fetch/fetch_counter_collection.csv "
                  "$REPO/gpurun_out/pmc_write/write_counter_collection.csv $REPO/profiles",
                  "```", "",
-                 f"Kernel `{frag.rstrip('(')}`" + (f", grid {grid} threads" if grid else "") + ".", "",
+                 f"Kernel `{frag.rstrip('(')}`" + (f", grid {grid} threads" if grid else "")
+                 + f", launches of the bench's `{phase}` phase.", "",
                  "| counter | copy kernel (KiB) | copy bytes (KiB) | scale | kernel per launch (KiB, median) "
                  "| launches | scaled |",
                  "|---|---|---|---|---|---|---|",
@@ -812,16 +871,18 @@ def summarize_traffic(fetch_csv, write_csv, out_dir):
         print(f"{key}: {(rd + wr) / 1e6:.1f} MB per launch" + (f" ({(rd + wr) / alg:.2f}x algorithmic)" if alg else ""))
 
 
-MFMA_KERNELS = {
-    "gdn_build_mfma_kernel(": (262144, "GDN build, main workload", "BF16"),
-    "gdn_chunk_mfma_kernel<false, true>": (262144, "GDN prefill forward, outputs only", "BF16"),
-    "gdn_chunk_mfma_kernel<true, true>": (393216, "GDN prefill forward with records", "BF16"),
-    "compose_sliced_mfma_kernel": (32768, "GDN compose, 16-segment chain", "BF16"),
-    "compose_dense_mfma_kernel<false, false>": (524288, "GDN compose, 4096-slot pool", "BF16"),
-    "sd_build_mfma_kernel<0, 2>": (131072, "scalar build", "BF16"),
-    "sd_build_mfma_kernel<1, 2>": (131072, "diagonal build", "BF16"),
-    "kda_chunk_mfma_kernel": (131072, "KDA build (fp32 matrix cores)", "F32"),
-}
+MFMA_KERNELS = (
+    # (kernel name fragment, grid in threads (None: any), bench phase, workload, MOPS type)
+    ("gdn_build_mfma_kernel(", None, "main", "GDN build, main workload", "BF16"),
+    ("gdn_build_mfma_kernel(", None, "rag", "GDN build, RAG mix cold segments", "BF16"),
+    ("gdn_chunk_mfma_kernel<false, true>", 262144, "forward", "GDN prefill forward, outputs only", "BF16"),
+    ("gdn_chunk_mfma_kernel<true, true>", 393216, "forward", "GDN prefill forward with records", "BF16"),
+    ("compose_sliced_mfma_kernel", 32768, "main", "GDN compose, 16-segment chain", "BF16"),
+    ("compose_dense_mfma_kernel<false, false>", 524288, "compose", "GDN compose, 4096-slot pool", "BF16"),
+    ("sd_build_mfma_kernel<0, 2>", 131072, "sd", "scalar build", "BF16"),
+    ("sd_build_mfma_kernel<1, 2>", 131072, "sd", "diagonal build", "BF16"),
+    ("kda_chunk_mfma_kernel", 131072, "kda", "KDA build (fp32 matrix cores)", "F32"),
+)
 
 
 def summarize_mfma(csv_path, out_md):
@@ -832,9 +893,10 @@ def summarize_mfma(csv_path, out_md):
     over the launch's duration; executed FLOP = MOPS x 512."""
     disp = {}
     for r in csv.DictReader(open(csv_path)):
-        d = disp.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
-                                               "dur": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
+                                                    "dur": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
         d[r["Counter_Name"]] = float(r["Counter_Value"])
+    phases = dispatch_phases([(k, d["name"], d["grid"]) for k, d in disp.items()])
     lines = ["# Matrix-core utilisation per kernel (bench workloads)", "",
              "One rocprofv3 counter pass over the benchmark (all legs, no CPU leg):", "",
              "```",
@@ -849,10 +911,12 @@ def summarize_mfma(csv_path, out_md):
              "dispatch's set-up and drain, so their clock reads high.", "",
              "| kernel | workload | grid | launches | µs (median) | clock GHz | MFMA busy | executed TFLOP/s | MOPS type |",
              "|---|---|---|---|---|---|---|---|---|"]
-    for frag, (grid, title, ty) in MFMA_KERNELS.items():
-        ds = [d for d in disp.values() if frag in d["name"] and d["grid"] == grid and "GRBM_GUI_ACTIVE" in d]
+    for frag, grid, phase, title, ty in MFMA_KERNELS:
+        ds = [d for k, d in disp.items() if frag in d["name"] and (grid is None or d["grid"] == grid)
+              and phases.get(k, "marker") == phase and "GRBM_GUI_ACTIVE" in d]
         if not ds:
             continue
+        grid = ds[0]["grid"]
         dur = float(np.median([d["dur"] for d in ds])) * 1e-9
         grbm = float(np.median([d["GRBM_GUI_ACTIVE"] for d in ds])) / 8
         busy = float(np.median([d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for d in ds])) / (1024 * grbm)
@@ -860,7 +924,7 @@ def summarize_mfma(csv_path, out_md):
         lines.append(f"| `{frag.rstrip('(')}` | {title} | {grid} | {len(ds)} | {dur * 1e6:.1f} | "
                      f"{grbm / dur / 1e9:.2f} | {busy:.3f} | {mops * 512 / dur / 1e12:.1f} | {ty} |")
     lines.append("")
-    srcs = sorted({n for v in TRAFFIC_KERNELS.values() for n in v[2]} | {"build_kda_mfma.hip"})
+    srcs = sorted({n for v in TRAFFIC_KERNELS.values() for n in v[3]} | {"build_kda_mfma.hip"})
     lines.append(f"sources sha256[:16]: `{source_sha(srcs)}` ({', '.join(srcs)})")
     lines.append("")
     with open(out_md, "w") as f:
@@ -869,38 +933,47 @@ def summarize_mfma(csv_path, out_md):
 
 
 TRACE_WORKLOADS = {
-    # (kernel name as shown, x extent of the grid in threads) -> workload
-    ("compose_dense_mfma_kernel<false, false>", 262144):
+    # (kernel name as shown, x extent of the grid in threads (None: any), bench phase) -> workload
+    ("compose_dense_mfma_kernel<false, false>", 262144, "convexact"):
         "GDN compose, conv-exact reuse (unfused leg, and the plain chain over the suffix records)",
-    ("compose_dense_mfma_kernel<false, false>", 524288): "GDN compose, 4096-slot pool, 64 requests x 32 slots",
-    ("compose_dense_mfma_kernel<false, false>", 1048576): "GDN compose, RAG mix, 128 requests x 24-96 slots",
-    ("compose_dense_mfma_kernel<false, true>", 262144):
+    ("compose_dense_mfma_kernel<false, false>", 524288, "compose"): "GDN compose, 4096-slot pool, 64 requests x 32 slots",
+    ("compose_dense_mfma_kernel<false, false>", 1048576, "rag"): "GDN compose, RAG mix, 128 requests x 24-96 slots",
+    ("compose_dense_mfma_kernel<false, true>", 262144, "convexact"):
         "GDN compose with warmed head tokens (conv-exact reuse, 32 requests, 5631 head tokens)",
-    ("compose_sd_wide_kernel<0, 128, 128>", 65536): "scalar compose, 8-segment chain, H=16",
-    ("compose_sd_wide_kernel<1, 128, 128>", 65536): "diagonal compose, 8-segment chain, H=16",
-    ("compose_sliced_mfma_kernel", 16384): "KDA compose, 8-segment chain, H=16 (four column slices)",
-    ("compose_sliced_mfma_kernel", 32768): "GDN compose, 16-segment chain, H=32, 4 column slices (main step)",
-    ("conv_kv_kernel", 1441536): "conv_kv, conv-exact reuse head tokens",
-    ("conv_kv_kernel", 74207488): "conv_kv, conv-exact suffix records (untimed setup)",
-    ("conv_warmup_vec_kernel<unsigned short, 4>", 512):
+    ("compose_sd_wide_kernel<0, 128, 128>", 65536, "sd"): "scalar compose, 8-segment chain, H=16",
+    ("compose_sd_wide_kernel<1, 128, 128>", 65536, "sd"): "diagonal compose, 8-segment chain, H=16",
+    ("compose_sliced_mfma_kernel", 16384, "kda"): "KDA compose, 8-segment chain, H=16 (four column slices)",
+    ("compose_sliced_mfma_kernel", 32768, "main"): "GDN compose, 16-segment chain, H=32, 4 column slices (main step)",
+    ("conv_kv_kernel", None, "convexact"): "conv_kv, conv-exact reuse head tokens",
+    ("conv_kv_kernel", None, "convexact_setup"): "conv_kv, conv-exact suffix records (untimed setup)",
+    ("conv_warmup_vec_kernel<unsigned short, 4>", None, "rag"):
         "conv warm-up, RAG mix, 8305 boundaries x 4096 channels, kernel 4",
-    ("gdn_build_mfma_kernel", 262144): "GDN build, H=32, d=128, bf16, 16 x 2048 tokens (main step)",
-    ("gdn_build_mfma_kernel", 4194304): "GDN build, RAG pool fill batches of 256 segments (untimed setup)",
-    ("gdn_build_mfma_kernel", 8388608): "GDN build, conv-exact suffix records (untimed setup)",
-    ("gdn_build_mfma_kernel", 30752768): "GDN build, conv-exact head records (unfused leg)",
-    ("gdn_build_mfma_kernel", 42336256): "GDN build, RAG mix cold segments (2584 x 32 heads)",
-    ("gdn_build_mfma_kernel", 67108864): "GDN build, 4096 x 64-token pool fill (untimed setup)",
-    ("gdn_chunk_mfma_kernel<false, true>", 262144):
+    ("gdn_build_mfma_kernel", None, "main"): "GDN build, H=32, d=128, bf16, 16 x 2048 tokens (main step)",
+    ("gdn_build_mfma_kernel", None, "compose_setup"): "GDN build, 4096 x 64-token pool fill (untimed setup)",
+    ("gdn_build_mfma_kernel", None, "rag_setup"): "GDN build, RAG pool fill batches of 256 segments (untimed setup)",
+    ("gdn_build_mfma_kernel", None, "rag"): "GDN build, RAG mix cold segments (2584 x 32 heads)",
+    ("gdn_build_mfma_kernel", None, "convexact_setup"): "GDN build, conv-exact suffix records (untimed setup)",
+    ("gdn_build_mfma_kernel", None, "convexact"): "GDN build, conv-exact head records (unfused leg)",
+    ("gdn_chunk_mfma_kernel<false, true>", 262144, "forward"):
         "GDN prefill forward, outputs only, H=32, d=128, bf16, 16 x 2048 tokens",
-    ("gdn_chunk_mfma_kernel<true, true>", 393216): "GDN prefill forward with the records as side-outputs, same workload",
-    ("kda_chunk_mfma_kernel<unsigned short>", 131072):
+    ("gdn_chunk_mfma_kernel<true, true>", 393216, "forward"):
+        "GDN prefill forward with the records as side-outputs, same workload",
+    ("kda_chunk_mfma_kernel<unsigned short>", 131072, "kda"):
         "KDA build, H=16, d=128, bf16, 8 x 2048 tokens (chunk form, fp32 MFMA, two roles)",
-    ("sd_build_mfma_kernel<0, 2>", 131072): "scalar build, H=16, d=128, bf16, 8 x 2048 tokens",
-    ("sd_build_mfma_kernel<1, 2>", 131072): "diagonal build, H=16, d=128, bf16, 8 x 2048 tokens",
-    ("peak_mfma_kernel", 262144): "measured-peak bf16 MFMA loop, 1024 x 4 waves x 512 x 4 products",
-    ("peak_read_kernel", 8388608): "measured-peak streaming read of 4 GiB",
-    ("peak_copy_kernel", 8388608): "measured-peak streaming copy of 1 GiB (1 GiB read, 1 GiB written)",
+    ("sd_build_mfma_kernel<0, 2>", 131072, "sd"): "scalar build, H=16, d=128, bf16, 8 x 2048 tokens",
+    ("sd_build_mfma_kernel<1, 2>", 131072, "sd"): "diagonal build, H=16, d=128, bf16, 8 x 2048 tokens",
+    ("peak_mfma_kernel", 262144, "peaks"): "measured-peak bf16 MFMA loop, 1024 x 4 waves x 512 x 4 products",
+    ("peak_read_kernel", 8388608, "peaks"): "measured-peak streaming read of 4 GiB",
+    ("peak_copy_kernel", 8388608, "peaks"): "measured-peak streaming copy of 1 GiB (1 GiB read, 1 GiB written)",
 }
+
+
+def _trace_workload(short, grid, phase):
+    """The TRACE_WORKLOADS key of a dispatch, or None."""
+    for g in (grid, None):
+        if (short, g, phase) in TRACE_WORKLOADS:
+            return (short, g, phase)
+    return None
 
 
 def _short_kernel_name(name):
@@ -931,12 +1004,15 @@ def summarize_trace(trace_csv, stats_csv, bench_json, out_md):
     durations from rocprofv3's kernel trace, rocprofv3's own --stats table, and the
     benchmark's HIP-event figures of an unprofiled run for comparison."""
     groups = {}
-    for r in csv.DictReader(open(trace_csv)):
+    rows = list(csv.DictReader(open(trace_csv)))
+    phases = dispatch_phases([(int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size_X"])) for r in rows])
+    for r in rows:
         short = _short_kernel_name(r["Kernel_Name"])
-        key = (_trace_key(short), int(r["Grid_Size_X"]))
-        if key not in TRACE_WORKLOADS:
+        grid = int(r["Grid_Size_X"])
+        wk = _trace_workload(_trace_key(short), grid, phases.get(int(r["Dispatch_Id"]), "marker"))
+        if wk is None:
             continue
-        g = groups.setdefault(key + (short,), {"dur": [], "row": r})
+        g = groups.setdefault((wk[0], grid, wk[2], short), {"dur": [], "row": r, "wk": wk})
         g["dur"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
     lines = ["# rocprofv3 kernel trace -- library kernels, per launch shape", "",
              "Command (repo at $REPO on the MI355X box; the default bench run without the CPU leg):", "",
@@ -946,18 +1022,21 @@ def summarize_trace(trace_csv, stats_csv, bench_json, out_md):
              "python $REPO/bench.py --summarize-trace $REPO/gpurun_out/prof_all/all_kernel_trace.csv "
              "$REPO/gpurun_out/prof_all/all_kernel_stats.csv BENCH_JSON <this file>",
              "```", "",
-             "Durations are per launch (End - Start of the kernel trace), grouped by kernel and grid; \"grid\" is "
-             "the x extent in threads (the conv warm-up grid is 512 x 8305, boundaries on y). The `peak_*` "
+             "Durations are per launch (End - Start of the kernel trace), grouped by kernel, grid and bench "
+             "phase; \"grid\" is the x extent in threads (the conv warm-up grid is 512 x 8305, boundaries on y). "
+             "The GDN build runs the same grid for every workload of more than a few hundred (segment, head) "
+             "units, so launches are attributed to the bench phase whose marker launch precedes them (a "
+             "16-byte `peak_copy_kernel` with as many workgroups as the phase's number). The `peak_*` "
              "kernels are the measured-peak microbenchmarks (libhypic_peaks.so). conv_kv's template arguments "
              "demangle garbled in the profiler.", "",
-             "| kernel | grid (threads) | wg | LDS B | VGPR | AGPR | launches | mean µs | min µs | workload |",
-             "|---|---|---|---|---|---|---|---|---|---|"]
-    for key in sorted(groups, key=lambda k: (k[0].startswith("peak_"), k[0], k[1])):
+             "| kernel | grid (threads) | phase | wg | LDS B | VGPR | AGPR | launches | mean µs | min µs | workload |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for key in sorted(groups, key=lambda k: (k[0].startswith("peak_"), k[0], k[1], k[2])):
         g = groups[key]
         r, d = g["row"], g["dur"]
-        lines.append(f"| `{key[2]}` | {key[1]} | {r['Workgroup_Size_X']} | {r['LDS_Block_Size']} | {r['VGPR_Count']} | "
-                     f"{r['Accum_VGPR_Count']} | {len(d)} | {np.mean(d):.1f} | {np.min(d):.1f} | "
-                     f"{TRACE_WORKLOADS[key[:2]]} |")
+        lines.append(f"| `{key[3]}` | {key[1]} | {key[2]} | {r['Workgroup_Size_X']} | {r['LDS_Block_Size']} | "
+                     f"{r['VGPR_Count']} | {r['Accum_VGPR_Count']} | {len(d)} | {np.mean(d):.1f} | {np.min(d):.1f} | "
+                     f"{TRACE_WORKLOADS[g['wk']]} |")
     lines += ["", "rocprofv3's own `--stats` summary (`all_kernel_stats.csv`) for the same run, all launches of a "
               "kernel together:", "", "| kernel | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
     for r in csv.DictReader(open(stats_csv)):
