@@ -87,7 +87,7 @@ struct __align__(16) Smem {
     UnitEnt units[TMAX];       // the stream's units from the front, set-up records from the back
     int64_t wsum[8];           // set-up: per wave, chunks of its valid units
     int32_t wcnt[8][2];        // set-up: per wave, valid units and set-up records
-    int64_t steps;             // chunks in the stream
+    int32_t steps;             // chunks in the stream (a workgroup's units fit in memory: far below 2^31)
     int32_t nvalid, nspecial;
 };
 
@@ -100,23 +100,24 @@ __device__ __forceinline__ int64_t uni64(int64_t x) {
 }
 
 // A position in the chunk stream: chunk c of the nc chunks of table unit q
-// (q = nvalid past the end), with that unit's tokens [tok0, tok0 + n) and head
-// copied out of the table when the cursor enters it.
+// (q = nvalid past the end), with the unit's first token, the rows of its last
+// chunk and its head copied out of the table when the cursor enters it.
 struct Cursor {
-    int q, head;
-    int64_t c, nc, tok0, n;
+    int q, c, nc, last, head;
+    int64_t tok0;
 };
 
 __device__ __forceinline__ void cursor_enter(const Smem &sm, int nvalid, Cursor &r) {
     r.c = 0;
     if (r.q < nvalid) {
+        const int64_t n = uni64(sm.units[r.q].n);
         r.tok0 = uni64(sm.units[r.q].tok);
-        r.n = uni64(sm.units[r.q].n);
         r.head = uni32(sm.units[r.q].head);
-        r.nc = (r.n + CH - 1) / CH;
+        r.nc = (int)((n + CH - 1) / CH);
+        r.last = (int)(n - (int64_t)(r.nc - 1) * CH);
     } else {
-        r.tok0 = r.n = r.nc = 0;
-        r.head = 0;
+        r.tok0 = 0;
+        r.nc = r.last = r.head = 0;
     }
 }
 
@@ -141,8 +142,7 @@ struct StepDesc {
 };
 
 __device__ __forceinline__ StepDesc step_desc(const Cursor &r) {
-    const int64_t rem = r.n - r.c * CH;
-    return {r.tok0 + r.c * CH, rem < CH ? (int)rem : CH, r.head};
+    return {r.tok0 + (int64_t)r.c * CH, r.c == r.nc - 1 ? r.last : CH, r.head};
 }
 
 __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
@@ -209,12 +209,12 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
             }
             sm.nvalid = nv;
             sm.nspecial = ns;
-            sm.steps = stp;
+            sm.steps = (int32_t)stp;
         }
         __syncthreads();
     }
     const int nvalid = uni32(sm.nvalid);
-    const int64_t steps = uni64(sm.steps);
+    const int steps = uni32(sm.steps);
     {
         // records of empty units (I, 0, ell 0) and of units with bad offsets (NaN)
         const int nspecial = uni32(sm.nspecial);
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         HYPIC_STATE_RESET(lane >> 5, lane & 31);
         __syncthreads();                                            // prologue: chunk 0 staged
         Cursor cs = cursor_first(sm, nvalid);                      // chunk i (phase b)
-        for (int64_t i = 0; i <= steps; ++i) {
+        for (int i = 0; i <= steps; ++i) {
             int thv = th;
             asm volatile("" : "+v"(thv));
             const int h = (thv & 63) >> 5, l32 = thv & 31;
@@ -456,10 +456,8 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         br = pl < d_.cl ? (a.beta ? a.beta[tk_ * a.b_st + d_.head * a.b_sh] : 1.0f) : 0.0f;          \
         lar = (pl < d_.cl && a.log_alpha) ? a.log_alpha[tk_ * a.la_st + d_.head * a.la_sh] : 0.0f;   \
     } while (0)
-        Cursor cur = cursor_first(sm, nvalid);                     // chunk i of the stream
-        Cursor nxt = cur;                                           // chunk i + 1
-        cursor_next(sm, nvalid, nxt);
-        if (steps > 0) HYPIC_FETCH_G(step_desc(cur));
+        Cursor nxt = cursor_first(sm, nvalid);                     // chunk i + 1 (chunk 0 here)
+        if (steps > 0) HYPIC_FETCH_G(step_desc(nxt));
         if (pw == 0) {
             // ---- wave 4: loads keys and values, the decay factors and ell in phase a;
             //      turns K^T around for tokens 0-31 of the chunk in phase b.
@@ -509,11 +507,14 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
             // state waves do not rescale X every chunk.
             float sig = 1.0f;
             if (steps > 0) {
-                HYPIC_LOAD_KV(step_desc(cur), 0);
+                HYPIC_LOAD_KV(step_desc(nxt), 0);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
+            // chunk i: its unit, its index in the unit and the unit's chunk count
+            int cq = nxt.q, cc = nxt.c, cnc = nxt.nc;
+            cursor_next(sm, nvalid, nxt);
             __syncthreads();                                        // prologue: chunk 0 staged
-            for (int64_t i = 0; i <= steps; ++i) {
+            for (int i = 0; i <= steps; ++i) {
                 int thv = th;
                 asm volatile("" : "+v"(thv));
                 const int l = thv & 63;
@@ -522,7 +523,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     const int b = (int)(i & 1);
                     const float la_i = lar, b_i = br;
                     if (i + 1 < steps) HYPIC_LOAD_KV(step_desc(nxt), b ^ 1);   // lands during this chunk
-                    if (cur.c == 0) sig = 1.0f;
+                    if (cc == 0) sig = 1.0f;
                     const float gv = wave_prefix_sum(la_i);
                     sm.pv[0][0][l] = gv;
                     sm.pv[0][1][l] = b_i;
@@ -538,11 +539,11 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     }
                     sig = fold ? 1.0f : sp;
                     ell += (double)la_i;
-                    if (cur.c == cur.nc - 1) {
+                    if (cc == cnc - 1) {
                         // the unit's ell
 #pragma unroll
                         for (int o = 32; o >= 1; o >>= 1) ell += __shfl_xor(ell, o);
-                        if (l == 0) a.pool_ell[uni32(sm.units[cur.q].rec)] = (float)ell;
+                        if (l == 0) a.pool_ell[uni32(sm.units[cq].rec)] = (float)ell;
                         ell = 0.0;
                     }
                 }
@@ -554,7 +555,9 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 if (i < steps) prep_kt(sm, (int)(i & 1), 0, l);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // chunk i + 1 has landed
                 __syncthreads();                                    // b -> next a
-                cur = nxt;
+                cq = nxt.q;
+                cc = nxt.c;
+                cnc = nxt.nc;
                 cursor_next(sm, nvalid, nxt);
             }
 #undef HYPIC_LOAD_KV
@@ -562,8 +565,9 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
             // ---- waves 5-7: a Gram block in phase a (waves 5 and 7 the diagonal blocks,
             //      which they also start inverting; wave 6 H_21); in phase b waves 5 and 7
             //      finish their block's inverse, wave 6 turns K^T around for tokens 32-63
+            cursor_next(sm, nvalid, nxt);                           // chunk 1
             __syncthreads();                                        // prologue: chunk 0 staged
-            for (int64_t i = 0; i <= steps; ++i) {
+            for (int i = 0; i <= steps; ++i) {
                 int thv = th;
                 asm volatile("" : "+v"(thv));
                 const int l = thv & 63;
