@@ -265,7 +265,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     const int64_t t0 = sm.t0;
     const int64_t n = state == 2 ? 0 : sm.n;
     const int64_t slot = sm.slot;
-    const int64_t nc = (n + CH - 1) / CH;
+    const int nc = (int)((n + CH - 1) / CH);   // 32 bits: a segment whose keys fit in memory has far fewer chunks
 
     const u16 *kh = static_cast<const u16 *>(a.k) + t0 * a.k_st + head * a.k_sh + kc0;
     const u16 *vh = static_cast<const u16 *>(a.v) + t0 * a.v_st + head * a.v_sh + jc0;
@@ -293,9 +293,9 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     constexpr bool SHARED_K = !DIAG && NSPLIT > 1, SHARED_V = DIAG;
     auto gll16k = [](const void *src, void *dst) { if constexpr (SHARED_K) gll16s(src, dst); else gll16(src, dst); };
     auto gll16v = [](const void *src, void *dst) { if constexpr (SHARED_V) gll16s(src, dst); else gll16(src, dst); };
-    auto issue = [&](int64_t C, int lw, const uint32_t *ko, const uint32_t *vo, const uint32_t *go) {
+    auto issue = [&](int C, int lw, const uint32_t *ko, const uint32_t *vo, const uint32_t *go) {
         const int bi = (int)(C % NBUF);
-        const int64_t base = C * CH, rem = n - base;
+        const int64_t base = (int64_t)C * CH, rem = n - base;
         SdBuf<DIAG, NJB> &Bf = sm.buf[bi];
         if (rem >= CH && small_st) {
             const u16 *kc = kh + base * a.k_st, *vc = vh + base * a.v_st;
@@ -321,10 +321,10 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         }
     };
     // diagonal: chunk C's gates and beta (LPG instructions per loading wave)
-    auto issue_g = [&](int64_t C, int lw, const uint32_t *go) {
+    auto issue_g = [&](int C, int lw, const uint32_t *go) {
         if constexpr (DIAG) {
             GateBuf &Gf = sm.gbuf[C % NBG];
-            const int64_t base = C * CH, rem = n - base;
+            const int64_t base = (int64_t)C * CH, rem = n - base;
             if (rem >= CH && small_st) {
 #pragma unroll
                 for (int j = 0; j < NGI; ++j)
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     // (in two parts: the gate and beta reads, issued before the current chunk's products
     // so that their LDS round trip overlaps them, and the arithmetic after)
     struct FacIn { float x[16], bt[16]; };
-    auto factors16_read = [&](int64_t C, int ch0, FacIn &fi) {
+    auto factors16_read = [&](int C, int ch0, FacIn &fi) {
         if constexpr (DIAG) {
             const GateBuf &Bf = sm.gbuf[C % NBG];
             const int cc = l >> 2, q4 = l & 3, ci = ch0 + cc, t0 = 16 * q4;
@@ -459,9 +459,9 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
             }
         }
     };
-    auto factors16 = [&](int64_t C, int ch0, FacIn &fi, double &ell_acc) {
+    auto factors16 = [&](int C, int ch0, FacIn &fi, double &ell_acc) {
         if constexpr (DIAG) {
-            const int64_t rem = n - C * CH;
+            const int64_t rem = n - (int64_t)C * CH;
             const int cl = rem < CH ? (int)rem : CH;
             const int cc = l >> 2, q4 = l & 3, ci = ch0 + cc, t0 = 16 * q4;
             float *x = fi.x;
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         }
         go[NGI] = small_st ? (uint32_t)(l * a.b_st) : 0u;
         if (!DIAG)
-            for (int64_t c = 0; c < DIST && c < nc; ++c) issue(c, lw, ko, vo, go);
+            for (int c = 0; c < DIST && c < nc; ++c) issue(c, lw, ko, vo, go);
         if constexpr (DIAG) {
             // Issue order: "step" j >= -3 issues the gates of chunk j + 3, then the keys and
             // values of chunk j + 2 (those that exist); steps -3 .. -1 run before the loop,
@@ -540,16 +540,16 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
             // loads were issued after the one it waits for.  Before the barrier that starts
             // chunk c every loading wave has waited for its gates of chunk c + 1, which the
             // compute waves turn into factors during chunk c.
-            auto nG = [&](int64_t m) { return m < nc ? LPG : 0; };
-            auto nKV = [&](int64_t m) { return m < nc ? LPW : 0; };
-            for (int64_t j = -3; j < 0; ++j) {
+            auto nG = [&](int m) { return m < nc ? LPG : 0; };
+            auto nKV = [&](int m) { return m < nc ? LPW : 0; };
+            for (int j = -3; j < 0; ++j) {
                 if (j + 3 < nc) issue_g(j + 3, lw, go);
                 if (j + 2 >= 0 && j + 2 < nc) issue(j + 2, lw, ko, vo, go);
             }
             vm_wait<2 * LPG + 3 * LPW>(nG(1) + nKV(0) + nG(2) + nKV(1));   // gates of chunk 0
             lds_barrier();                                                  // ... visible to all
             vm_wait<2 * LPG + 3 * LPW>(nG(2) + nKV(1));                    // gates 1, keys, values 0
-            for (int64_t c = 0; c < nc; ++c) {
+            for (int c = 0; c < nc; ++c) {
                 lds_barrier();                            // chunk c (and its factors) visible
                 if (c + 3 < nc) issue_g(c + 3, lw, go);
                 if (c + 2 < nc) issue(c + 2, lw, ko, vo, go);
@@ -564,17 +564,17 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
             if (AHEAD) {
                 if (nc > 0) {
                     // chunk 0 landed: the compute waves read its operands before their loop
-                    const int64_t issued = (DIST - 1 < nc - 1 ? DIST - 1 : nc - 1);
+                    const int issued = (DIST - 1 < nc - 1 ? DIST - 1 : nc - 1);
                     wait_chunks<LPW, DIST - 1>((int)issued);
                 }
                 lds_barrier();
             }
         }
-        for (int64_t c = 0; c < nc; ++c) {
+        for (int c = 0; c < nc; ++c) {
             // chunk c + AHEAD has landed once at most the later chunks' loads remain
             {
-                const int64_t issued = c + DIST - 1 < nc - 1 ? c + DIST - 1 : nc - 1;
-                const int64_t need = c + AHEAD < nc - 1 ? c + AHEAD : nc - 1;
+                const int issued = c + DIST - 1 < nc - 1 ? c + DIST - 1 : nc - 1;
+                const int need = c + AHEAD < nc - 1 ? c + AHEAD : nc - 1;
                 wait_chunks<LPW, DIST - 1>((int)(issued - need));
             }
             lds_barrier();                            // chunk c + AHEAD visible; chunk c - 1's buffer free
@@ -596,7 +596,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         struct Ops {
             bf16x8 kr[4], vb[4][NJB];
         };
-        auto load_ops = [&](int64_t cc, Ops &o) {
+        auto load_ops = [&](int cc, Ops &o) {
             const SdBuf<DIAG, NJB> &B = sm.buf[cc % NBUF];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
@@ -607,11 +607,11 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
                                            &B.Vm[vofs[1][jb] + 16 * ks * 32 * NJB]);
             }
         };
-        auto step = [&](int64_t cc, Ops &cur, Ops &nxt) {
+        auto step = [&](int cc, Ops &cur, Ops &nxt) {
             lds_barrier();                            // chunk cc + AHEAD visible; chunk cc - 1's buffer free
             if (cc > 0 && cc % TBC == 0) {
                 // a new table block: carry the state into it (every wave is past chunk cc - 1)
-                const float eG = __expf(make_table(cc * CH));
+                const float eG = __expf(make_table((int64_t)cc * CH));
 #pragma unroll
                 for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
@@ -638,12 +638,12 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         if constexpr (AHEAD) {
             lds_barrier();                            // chunk 0 visible
             if (nc > 0) load_ops(0, oa);
-            for (int64_t c = 0; c < nc; c += 2) {
+            for (int c = 0; c < nc; c += 2) {
                 step(c, oa, ob);
                 if (c + 1 < nc) step(c + 1, ob, oa);
             }
         } else {
-            for (int64_t c = 0; c < nc; ++c) step(c, oa, oa);
+            for (int c = 0; c < nc; ++c) step(c, oa, oa);
         }
     } else {
     // the chunk's factors (computed by these waves one chunk ahead): decay, scale, multiply
@@ -655,7 +655,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         factors16_read(0, 16 * w, fi);
         factors16(0, 16 * w, fi, ell16);
     }
-    for (int64_t c = 0; c < nc; ++c) {
+    for (int c = 0; c < nc; ++c) {
         lds_barrier();                                // chunk c and its factors visible; chunk c - 1's buffer free
         if (c + 1 < nc) factors16_read(c + 1, 16 * w, fi);
         const SdBuf<DIAG, NJB> &B = sm.buf[c % NBUF];
