@@ -82,6 +82,7 @@ struct __align__(16) Smem {
     float inv_tmp[4][128];     // per prep wave: products inside the blocked inversion
     float egs[2][CH];          // -e^{g_t} sigma_c: the K X factor of W (S columns)
     float egrs[2][CH];         // e^{G - g_t} / sigma_{c+1}: the update factor (S columns)
+    float bsv[CH];             // beta_t e^{G - g_t} / sigma_{c+1} (wave 7): the S factor of block 2
     float rs[2];               // sigma_c e^G when the scale is folded back into the state, else 1
     float sig_fin[2];          // sigma after the chunk of that parity (S = sigma X at a unit's end)
     UnitEnt units[TMAX];       // the stream's units from the front, set-up records from the back
@@ -326,12 +327,6 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                     y2[cb] = mfma(f1[cb][1], u1, y2[cb]);
                 }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 e1 = tok4(sm.egrs[b], 1, q, h);
-                    y2[1][4 * q] *= e1.x; y2[1][4 * q + 1] *= e1.y;
-                    y2[1][4 * q + 2] *= e1.z; y2[1][4 * q + 3] *= e1.w;
-                }
-#pragma unroll
                 for (int cb = 0; cb < 2; ++cb) {
                     yb[2][cb] = acc_to_b(y2[cb], 0);
                     yb[3][cb] = acc_to_b(y2[cb], 1);
@@ -564,7 +559,15 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
         } else {
             // ---- waves 5-7: a Gram block in phase a (waves 5 and 7 the diagonal blocks,
             //      which they also start inverting; wave 6 H_21); in phase b waves 5 and 7
-            //      finish their block's inverse, wave 6 turns K^T around for tokens 32-63
+            //      finish their block's inverse, wave 6 turns K^T around for tokens 32-63.
+            // Wave 7 writes block 2's S factor already scaled by the update factor:
+            // e^{G - g_r} / sigma' times D T0 D^{-1} diag(beta), row r, is T0 diag(bs) with
+            // bs_c = beta_c e^{G - g_c} / sigma', because e^{G - g_r} / sigma' e^{g_r} is the
+            // same for every row; so Y_2 of the S columns comes out ready for the update, and
+            // the S factor needs no exponential per entry.  It keeps its own copy of sigma
+            // (the same recurrence, from the same gates, as wave 4's).
+            int cc = nxt.c;                                         // chunk i's index in its unit
+            float sig = 1.0f;
             cursor_next(sm, nvalid, nxt);                           // chunk 1
             __syncthreads();                                        // prologue: chunk 0 staged
             for (int i = 0; i <= steps; ++i) {
@@ -574,20 +577,32 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
                 if (i < steps) {
                     const int b = (int)(i & 1);
                     const float la_i = lar, b_i = br;
-                    sm.pv[pw][0][l] = wave_prefix_sum(la_i);
+                    const float gv = wave_prefix_sum(la_i);
+                    sm.pv[pw][0][l] = gv;
                     sm.pv[pw][1][l] = b_i;
+                    if (pw == 3) {
+                        if (cc == 0) sig = 1.0f;
+                        const float gt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 63));
+                        const float sp = sig * __expf(gt);
+                        const bool fold = sp < 0x1p-60f;
+                        const float inv = fold ? 1.0f : 1.0f / sp;
+                        sm.bsv[l] = b_i * (__expf(gt - gv) * inv);
+                        sig = fold ? 1.0f : sp;
+                    }
                     wave_lds_sync();
                     prep_gram(sm, b, pw, l);
                     if (pw != 2) {
                         wave_lds_sync();
-                        prep_invert1<true>(inv_ctx(sm, b, pw >> 1, pw), l);
+                        prep_invert1<true>(inv_ctx(sm, b, pw >> 1, pw, pw == 3 ? &sm.bsv[32] : nullptr), l);
                     }
                 }
                 lds_barrier();                                      // a -> b
                 if (i + 1 < steps) HYPIC_FETCH_G(step_desc(nxt));   // gates of chunk i + 1
-                if (i < steps && pw != 2) prep_invert2<true>(inv_ctx(sm, (int)(i & 1), pw >> 1, pw), l);
+                if (i < steps && pw != 2)
+                    prep_invert2<true>(inv_ctx(sm, (int)(i & 1), pw >> 1, pw, pw == 3 ? &sm.bsv[32] : nullptr), l);
                 if (i < steps && pw == 2) prep_kt(sm, (int)(i & 1), 1, l);
                 __syncthreads();                                    // b -> next a
+                cc = nxt.c;
                 cursor_next(sm, nvalid, nxt);
             }
         }

@@ -134,16 +134,19 @@ __device__ __forceinline__ float4 tok4(const float *v, int mb, int q, int h) {
 // Part 1 (level 0) runs in phase a right after the Gram block, part 2 (levels 1
 // and 2 and the merge) in phase b; TB is double-buffered by chunk parity, so
 // the writes may land while the state waves read the previous chunk's factors.
+// bs (optional): per-column factors of the S tile, which is then T0 diag(bs) (a row
+// scaling of the S system's solve folded into it, see the record build) instead of
+// D T0 D^{-1} diag(beta).
 struct InvCtx {
     float *M, *tmp;
     u16 *TP, *TS;
-    const float *bet, *gg;
+    const float *bet, *gg, *bs;
 };
 
 template <class SM>
-__device__ __forceinline__ InvCtx inv_ctx(SM &sm, int par, int blk, int pw) {
+__device__ __forceinline__ InvCtx inv_ctx(SM &sm, int par, int blk, int pw, const float *bs = nullptr) {
     return InvCtx{sm.Af[blk], sm.inv_tmp[pw], sm.TB[par][0][blk], sm.TB[par][SM::kS][blk], &sm.pv[pw][1][32 * blk],
-                  &sm.pv[pw][0][32 * blk]};
+                  &sm.pv[pw][0][32 * blk], bs};
 }
 
 // both factors of one T0 entry x at (r, c), r > c (WP = false: the S factor only)
@@ -151,7 +154,7 @@ template <bool WP>
 __device__ __forceinline__ void inv_put(const InvCtx &v, int r, int c, float x) {
     const float bx = x * v.bet[c];
     if (WP) v.TP[r * TBL + c] = f2bf(-bx);
-    v.TS[r * TBL + c] = f2bf(bx * __expf(v.gg[r] - v.gg[c]));
+    v.TS[r * TBL + c] = f2bf(v.bs ? x * v.bs[c] : bx * __expf(v.gg[r] - v.gg[c]));
 }
 
 // both factors of four consecutive T0 entries of row r, columns c .. c + 3
@@ -162,9 +165,16 @@ __device__ __forceinline__ void inv_put4(const InvCtx &v, int r, int c, float4 x
     const float4 g4 = *reinterpret_cast<const float4 *>(&v.gg[c]);
     const float gr = v.gg[r];
     const float b0 = x.x * b4.x, b1 = x.y * b4.y, b2 = x.z * b4.z, b3 = x.w * b4.w;
+    if (WP) *reinterpret_cast<u32x2 *>(&v.TP[r * TBL + c]) = u32x2{pack2(-b0, -b1), pack2(-b2, -b3)};
+    if (v.bs) {
+        const float4 s4 = *reinterpret_cast<const float4 *>(&v.bs[c]);
+        const float s0 = r >= c ? x.x * s4.x : 0.f, s1 = r >= c + 1 ? x.y * s4.y : 0.f;
+        const float s2 = r >= c + 2 ? x.z * s4.z : 0.f, s3 = r >= c + 3 ? x.w * s4.w : 0.f;
+        *reinterpret_cast<u32x2 *>(&v.TS[r * TBL + c]) = u32x2{pack2(s0, s1), pack2(s2, s3)};
+        return;
+    }
     const float e0 = r >= c ? __expf(gr - g4.x) : 0.f, e1 = r >= c + 1 ? __expf(gr - g4.y) : 0.f;
     const float e2 = r >= c + 2 ? __expf(gr - g4.z) : 0.f, e3 = r >= c + 3 ? __expf(gr - g4.w) : 0.f;
-    if (WP) *reinterpret_cast<u32x2 *>(&v.TP[r * TBL + c]) = u32x2{pack2(-b0, -b1), pack2(-b2, -b3)};
     *reinterpret_cast<u32x2 *>(&v.TS[r * TBL + c]) = u32x2{pack2(b0 * e0, b1 * e1), pack2(b2 * e2, b3 * e3)};
 }
 
@@ -244,7 +254,12 @@ __device__ __forceinline__ void prep_invert2(const InvCtx &v, int l) {
         const float gr = v.gg[r];
         const float b0 = -u0 * b2.x, b1 = -u1 * b2.y;
         if (WP) *reinterpret_cast<uint32_t *>(&v.TP[r * TBL + c]) = pack2(-b0, -b1);
-        *reinterpret_cast<uint32_t *>(&v.TS[r * TBL + c]) = pack2(b0 * __expf(gr - g2.x), b1 * __expf(gr - g2.y));
+        if (v.bs) {
+            const float2 s2 = *reinterpret_cast<const float2 *>(&v.bs[c]);
+            *reinterpret_cast<uint32_t *>(&v.TS[r * TBL + c]) = pack2(-u0 * s2.x, -u1 * s2.y);
+        } else {
+            *reinterpret_cast<uint32_t *>(&v.TS[r * TBL + c]) = pack2(b0 * __expf(gr - g2.x), b1 * __expf(gr - g2.y));
+        }
     }
     wave_lds_sync();
     // (2) merge to 32 on the 16x16x16 MFMA: tmp = A_10 T_00 with lane (column l%16,
