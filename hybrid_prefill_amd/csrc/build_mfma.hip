@@ -52,8 +52,6 @@
 // 16-byte LDS read from a plain row-major tile, at row swz(lane).
 // X . I on the MFMA moves a token-major tile into the accumulator layout
 // (one column per lane); that gives K^T and the V term of W.
-#include <atomic>
-
 #include "gdn_mfma_common.h"
 
 namespace hypic {
@@ -62,15 +60,9 @@ namespace {
 constexpr int NT = 512;    // 4 state waves + 4 prep waves
 constexpr int TMAX = 512;  // units per workgroup: one per thread at set-up
 
-// A unit of the chunk stream: tokens [tok, tok + n) of head `head`, record rec = slot H + head.
-// At the back of the table, records written at set-up: tok = 0 identity, 1 NaN.
-struct UnitEnt {
-    int64_t tok, n;
-    int32_t rec, head;
-};
-
 struct __align__(16) Smem {
     static constexpr bool kWithP = true;
+    static constexpr int kTmax = TMAX;
     static constexpr int kS = 1;
     u16 Km[2][CH * KML];       // keys, token-major, double-buffered by chunk parity
     u16 Vm[2][CH * KML];       // values, token-major, double-buffered by chunk parity
@@ -92,144 +84,21 @@ struct __align__(16) Smem {
     int32_t nvalid, nspecial;
 };
 
-// Wave-uniform copies of values that every lane holds alike (broadcast LDS reads).
-__device__ __forceinline__ int uni32(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ int64_t uni64(int64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
-// A position in the chunk stream: chunk c of the nc chunks of table unit q
-// (q = nvalid past the end), with the unit's first token, the rows of its last
-// chunk and its head copied out of the table when the cursor enters it.
-struct Cursor {
-    int q, c, nc, last, head;
-    int64_t tok0;
-};
-
-__device__ __forceinline__ void cursor_enter(const Smem &sm, int nvalid, Cursor &r) {
-    r.c = 0;
-    if (r.q < nvalid) {
-        const int64_t n = uni64(sm.units[r.q].n);
-        r.tok0 = uni64(sm.units[r.q].tok);
-        r.head = uni32(sm.units[r.q].head);
-        r.nc = (int)((n + CH - 1) / CH);
-        r.last = (int)(n - (int64_t)(r.nc - 1) * CH);
-    } else {
-        r.tok0 = 0;
-        r.nc = r.last = r.head = 0;
-    }
-}
-
-__device__ __forceinline__ Cursor cursor_first(const Smem &sm, int nvalid) {
-    Cursor r;
-    r.q = 0;
-    cursor_enter(sm, nvalid, r);
-    return r;
-}
-
-__device__ __forceinline__ void cursor_next(const Smem &sm, int nvalid, Cursor &r) {
-    if (++r.c >= r.nc) {
-        if (r.q < nvalid) ++r.q;
-        cursor_enter(sm, nvalid, r);
-    }
-}
-
-// The tokens of the cursor's chunk: first token, rows (1..CH), head.
-struct StepDesc {
-    int64_t tok;
-    int cl, head;
-};
-
-__device__ __forceinline__ StepDesc step_desc(const Cursor &r) {
-    return {r.tok0 + (int64_t)r.c * CH, r.c == r.nc - 1 ? r.last : CH, r.head};
-}
-
 __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
     __shared__ Smem sm;
 
     const int th = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(th >> 6);
     const int lane = th & 63;
-    const float nanv = __int_as_float(0x7fc00000);
 
-    // ---- set-up: thread th takes unit blockIdx.x + th G (the launch keeps that count
-    //      within TMAX = NT); the valid non-empty units go into the table in order
-    {
-        const int64_t U = (int64_t)a.num_segments * a.H, G = gridDim.x;
-        const int64_t u = (int64_t)blockIdx.x + (int64_t)th * G;
-        int kind = 0;   // 0: nothing to write, 1: chunk stream, 2: identity record, 3: NaN record
-        int64_t o0 = 0, o1 = 0, rec = 0;
-        int hd = 0;
-        if (u < U) {
-            const int64_t seg = u / a.H;
-            hd = (int)(u - seg * a.H);
-            o0 = a.seg_offsets[seg];
-            o1 = a.seg_offsets[seg + 1];
-            const int64_t slot = a.dst_slots[seg];
-            if (slot < 0 || slot >= a.num_slots) {
-                raise_flag(a.err_flag, HYPIC_EFLAG_SLOT_OUT_OF_RANGE);
-            } else {
-                rec = slot * a.H + hd;
-                if (o0 < 0 || o1 < o0 || o1 > a.num_tokens) {
-                    raise_flag(a.err_flag, HYPIC_EFLAG_BAD_OFFSETS);
-                    kind = 3;
-                } else {
-                    kind = o1 > o0 ? 1 : 2;
-                }
-            }
-        }
-        const uint64_t mv = __ballot(kind == 1), ms = __ballot(kind >= 2);
-        const uint64_t below = (1ull << lane) - 1;
-        int64_t nch = kind == 1 ? (o1 - o0 + CH - 1) / CH : 0;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) nch += __shfl_xor(nch, o);
-        if (lane == 0) {
-            sm.wcnt[w][0] = __popcll(mv);
-            sm.wcnt[w][1] = __popcll(ms);
-            sm.wsum[w] = nch;
-        }
-        // the upper triangles of the T diag(beta) tiles stay zero for the whole launch
-        for (int e = th; e < (int)(sizeof(sm.TB) / 16); e += NT) reinterpret_cast<u32x4 *>(&sm.TB[0][0][0][0])[e] = u32x4{};
-        __syncthreads();
-        int pv = 0, ps = 0;
-        for (int x = 0; x < w; ++x) {
-            pv += sm.wcnt[x][0];
-            ps += sm.wcnt[x][1];
-        }
-        if (kind == 1) sm.units[pv + __popcll(mv & below)] = UnitEnt{o0, o1 - o0, (int32_t)rec, hd};
-        if (kind >= 2) sm.units[TMAX - 1 - (ps + __popcll(ms & below))] = UnitEnt{kind - 2, 0, (int32_t)rec, hd};
-        if (th == 0) {
-            int nv = 0, ns = 0;
-            int64_t stp = 0;
-            for (int x = 0; x < NT / 64; ++x) {
-                nv += sm.wcnt[x][0];
-                ns += sm.wcnt[x][1];
-                stp += sm.wsum[x];
-            }
-            sm.nvalid = nv;
-            sm.nspecial = ns;
-            sm.steps = (int32_t)stp;
-        }
-        __syncthreads();
-    }
+    // ---- set-up: the workgroup's units tabled, the records of empty units and bad
+    //      offsets written (the launch keeps the unit count within TMAX = NT)
+    // the upper triangles of the T diag(beta) tiles stay zero for the whole launch
+    for (int e = th; e < (int)(sizeof(sm.TB) / 16); e += NT) reinterpret_cast<u32x4 *>(&sm.TB[0][0][0][0])[e] = u32x4{};
+    stream_setup<Smem, NT>(sm, a, true);
     const int nvalid = uni32(sm.nvalid);
     const int steps = uni32(sm.steps);
-    {
-        // records of empty units (I, 0, ell 0) and of units with bad offsets (NaN)
-        const int nspecial = uni32(sm.nspecial);
-        for (int s = 0; s < nspecial; ++s) {
-            const bool nanr = uni64(sm.units[TMAX - 1 - s].tok) != 0;
-            const int64_t r = uni32(sm.units[TMAX - 1 - s].rec);
-            float *P = a.pool_P + r * D * D, *S = a.pool_S + r * D * D;
-            for (int x = th; x < D * D; x += NT) {
-                P[x] = nanr ? nanv : (x / D == x % D ? 1.0f : 0.0f);
-                S[x] = nanr ? nanv : 0.0f;
-            }
-            if (th == 0) a.pool_ell[r] = nanr ? nanv : 0.0f;
-        }
-    }
+    stream_special_records<Smem, NT>(sm, a);
 
     if (w < 4) {
         // =============================== state waves ===============================
@@ -612,19 +481,6 @@ __global__ __launch_bounds__(NT, 1) void gdn_build_mfma_kernel(BuildArgs a) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Compute units of the current device, read once per device.
-int cu_count() {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n <= 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 }  // namespace
 
 hipError_t launch_build_mfma(const BuildArgs &a, hipStream_t stream, bool *taken) {
@@ -634,12 +490,7 @@ hipError_t launch_build_mfma(const BuildArgs &a, hipStream_t stream, bool *taken
         return hipSuccess;
     if (a.num_slots * a.H > 0x7fffffffLL) return hipSuccess;   // record index kept in 32 bits
     *taken = true;
-    // G workgroups, a multiple of the CU count (one resident workgroup per CU), each
-    // taking at most TMAX of the U units
-    const int64_t U = (int64_t)a.num_segments * a.H;
-    const int64_t cus = cu_count();
-    int64_t G = cus * ((U + cus * TMAX - 1) / (cus * TMAX));
-    if (G > U) G = U;
+    const int64_t G = stream_grid((int64_t)a.num_segments * a.H, TMAX);
     hipLaunchKernelGGL(gdn_build_mfma_kernel, dim3((unsigned)G), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }

@@ -12,6 +12,8 @@
 // in TB and H21 (the P factors are at index 0 when they exist).
 #pragma once
 
+#include <atomic>
+
 #include "hypic_internal.h"
 
 namespace hypic {
@@ -357,6 +359,184 @@ __device__ __forceinline__ void prep_gram(SM &sm, int b, int pw, int l) {
             *reinterpret_cast<float4 *>(&sm.Af[am][l32 * AFL + s4]) = make_float4(a0[0], a0[1], a0[2], a0[3]);
         }
     }
+}
+
+// ---------------------------------------------------------------- chunk streams
+// The record build and the prefill forward run several (segment, head) units per
+// workgroup, their chunks back to back as one stream.  The launch has G workgroups;
+// workgroup j takes units j, j + G, j + 2G, ... (at most SM::kTmax of them).  At
+// set-up each thread reads one unit's offsets (and slot, with records): an
+// out-of-range slot raises the flag; with records, an empty unit gets the identity
+// record and one with bad offsets the NaN record (written by the whole workgroup);
+// without records a unit with bad offsets raises the flag and writes nothing; the
+// units with tokens go into an LDS table in order.  Every wave then walks the same
+// chunk stream through the table with a cursor.  The kernel's LDS layout SM provides
+// units[SM::kTmax], wsum[waves], wcnt[waves][2], steps, nvalid and nspecial.
+
+// A unit of the stream: tokens [tok, tok + n) of head `head`, record rec = slot H + head.
+// At the back of the table, records written at set-up: tok = 0 identity, 1 NaN.
+struct UnitEnt {
+    int64_t tok, n;
+    int32_t rec, head;
+};
+
+// Wave-uniform copies of values that every lane holds alike (broadcast LDS reads).
+__device__ __forceinline__ int uni32(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// A position in the chunk stream: chunk c of the nc chunks of table unit q
+// (q = nvalid past the end), with the unit's first token, the rows of its last
+// chunk and its head copied out of the table when the cursor enters it.
+struct Cursor {
+    int q, c, nc, last, head;
+    int64_t tok0;
+};
+
+template <class SM>
+__device__ __forceinline__ void cursor_enter(const SM &sm, int nvalid, Cursor &r) {
+    r.c = 0;
+    if (r.q < nvalid) {
+        const int64_t n = uni64(sm.units[r.q].n);
+        r.tok0 = uni64(sm.units[r.q].tok);
+        r.head = uni32(sm.units[r.q].head);
+        r.nc = (int)((n + CH - 1) / CH);
+        r.last = (int)(n - (int64_t)(r.nc - 1) * CH);
+    } else {
+        r.tok0 = 0;
+        r.nc = r.last = r.head = 0;
+    }
+}
+
+template <class SM>
+__device__ __forceinline__ Cursor cursor_first(const SM &sm, int nvalid) {
+    Cursor r;
+    r.q = 0;
+    cursor_enter(sm, nvalid, r);
+    return r;
+}
+
+template <class SM>
+__device__ __forceinline__ void cursor_next(const SM &sm, int nvalid, Cursor &r) {
+    if (++r.c >= r.nc) {
+        if (r.q < nvalid) ++r.q;
+        cursor_enter(sm, nvalid, r);
+    }
+}
+
+// The tokens of the cursor's chunk: first token, rows (1..CH), head.
+struct StepDesc {
+    int64_t tok;
+    int cl, head;
+};
+
+__device__ __forceinline__ StepDesc step_desc(const Cursor &r) {
+    return {r.tok0 + (int64_t)r.c * CH, r.c == r.nc - 1 ? r.last : CH, r.head};
+}
+
+// Set-up of the stream (every thread of the workgroup, NTH of them; ends with a
+// workgroup barrier, after which the table, nvalid, nspecial and steps are visible).
+template <class SM, int NTH>
+__device__ __forceinline__ void stream_setup(SM &sm, const BuildArgs &a, bool records) {
+    static_assert(SM::kTmax <= NTH, "one unit per set-up thread");
+    const int th = threadIdx.x, lane = th & 63;
+    const int w = __builtin_amdgcn_readfirstlane(th >> 6);
+    const int64_t U = (int64_t)a.num_segments * a.H, G = gridDim.x;
+    const int64_t u = (int64_t)blockIdx.x + (int64_t)th * G;
+    int kind = 0;   // 0: nothing to write, 1: chunk stream, 2: identity record, 3: NaN record
+    int64_t o0 = 0, o1 = 0, rec = 0;
+    int hd = 0;
+    if (th < SM::kTmax && u < U) {
+        const int64_t seg = u / a.H;
+        hd = (int)(u - seg * a.H);
+        o0 = a.seg_offsets[seg];
+        o1 = a.seg_offsets[seg + 1];
+        const int64_t slot = records ? (int64_t)a.dst_slots[seg] : 0;
+        if (records && (slot < 0 || slot >= a.num_slots)) {
+            raise_flag(a.err_flag, HYPIC_EFLAG_SLOT_OUT_OF_RANGE);
+        } else {
+            rec = slot * a.H + hd;
+            if (o0 < 0 || o1 < o0 || o1 > a.num_tokens) {
+                raise_flag(a.err_flag, HYPIC_EFLAG_BAD_OFFSETS);
+                kind = records ? 3 : 0;
+            } else {
+                kind = o1 > o0 ? 1 : (records ? 2 : 0);
+            }
+        }
+    }
+    const uint64_t mv = __ballot(kind == 1), ms = __ballot(kind >= 2);
+    const uint64_t below = (1ull << lane) - 1;
+    int64_t nch = kind == 1 ? (o1 - o0 + CH - 1) / CH : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) nch += __shfl_xor(nch, o);
+    if (lane == 0) {
+        sm.wcnt[w][0] = __popcll(mv);
+        sm.wcnt[w][1] = __popcll(ms);
+        sm.wsum[w] = nch;
+    }
+    __syncthreads();
+    int pv = 0, ps = 0;
+    for (int x = 0; x < w; ++x) {
+        pv += sm.wcnt[x][0];
+        ps += sm.wcnt[x][1];
+    }
+    if (kind == 1) sm.units[pv + __popcll(mv & below)] = UnitEnt{o0, o1 - o0, (int32_t)rec, hd};
+    if (kind >= 2) sm.units[SM::kTmax - 1 - (ps + __popcll(ms & below))] = UnitEnt{kind - 2, 0, (int32_t)rec, hd};
+    if (th == 0) {
+        int nv = 0, ns = 0;
+        int64_t stp = 0;
+        for (int x = 0; x < NTH / 64; ++x) {
+            nv += sm.wcnt[x][0];
+            ns += sm.wcnt[x][1];
+            stp += sm.wsum[x];
+        }
+        sm.nvalid = nv;
+        sm.nspecial = ns;
+        sm.steps = (int32_t)stp;     // a workgroup's units fit in memory: far below 2^31 chunks
+    }
+    __syncthreads();
+}
+
+// The records written at set-up: empty units (I, 0, ell 0) and bad offsets (NaN).
+template <class SM, int NTH>
+__device__ __forceinline__ void stream_special_records(const SM &sm, const BuildArgs &a) {
+    const int th = threadIdx.x;
+    const float nanv = __int_as_float(0x7fc00000);
+    const int nspecial = uni32(sm.nspecial);
+    for (int s = 0; s < nspecial; ++s) {
+        const bool nanr = uni64(sm.units[SM::kTmax - 1 - s].tok) != 0;
+        const int64_t r = uni32(sm.units[SM::kTmax - 1 - s].rec);
+        float *P = a.pool_P + r * D * D, *S = a.pool_S + r * D * D;
+        for (int x = th; x < D * D; x += NTH) {
+            P[x] = nanr ? nanv : (x / D == x % D ? 1.0f : 0.0f);
+            S[x] = nanr ? nanv : 0.0f;
+        }
+        if (th == 0) a.pool_ell[r] = nanr ? nanv : 0.0f;
+    }
+}
+
+// Compute units of the current device, read once per device.
+inline int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// The grid of a chunk-stream launch over U units: a multiple of the CU count (one
+// resident workgroup per CU), each workgroup taking at most tmax units.
+inline int64_t stream_grid(int64_t U, int tmax) {
+    const int64_t cus = cu_count();
+    const int64_t G = cus * ((U + cus * tmax - 1) / (cus * tmax));
+    return G > U ? U : G;
 }
 
 }  // namespace
