@@ -73,7 +73,7 @@ _SD_SRC = ("build_sd_mfma.hip", "hypic_internal.h")
 TRAFFIC_KERNELS = {
     "gdn_build_h32_d128_16x2048": ("gdn_build_mfma_kernel(", None, "main", _GDN_SRC,
                                    "GDN build, H=32, d=128, bf16, 16 x 2048 tokens"),
-    "gdn_compose_h32_d128_chain16": ("compose_sliced_mfma_kernel", 32768, "main", _CMP_SRC,
+    "gdn_compose_h32_d128_chain16": ("compose_sliced_mfma_kernel", 65536, "main", _CMP_SRC,
                                      "GDN compose of the 16-segment chain, H=32, d=128, fp32 records"),
     "gdn_forward_h32_d128_16x2048": ("gdn_chunk_mfma_kernel<false, true>", 262144, "forward", _FWD_SRC,
                                      "GDN prefill forward, outputs only, H=32, d=128, bf16, 16 x 2048 tokens"),
@@ -877,7 +877,7 @@ MFMA_KERNELS = (
     ("gdn_build_mfma_kernel(", None, "rag", "GDN build, RAG mix cold segments", "BF16"),
     ("gdn_chunk_mfma_kernel<false, true>", 262144, "forward", "GDN prefill forward, outputs only", "BF16"),
     ("gdn_chunk_mfma_kernel<true, true>", 393216, "forward", "GDN prefill forward with records", "BF16"),
-    ("compose_sliced_mfma_kernel", 32768, "main", "GDN compose, 16-segment chain", "BF16"),
+    ("compose_sliced_mfma_kernel", 65536, "main", "GDN compose, 16-segment chain", "BF16"),
     ("compose_dense_mfma_kernel<false, false>", 524288, "compose", "GDN compose, 4096-slot pool", "BF16"),
     ("sd_build_mfma_kernel<0, 2>", 131072, "sd", "scalar build", "BF16"),
     ("sd_build_mfma_kernel<1, 2>", 131072, "sd", "diagonal build", "BF16"),
@@ -942,8 +942,8 @@ TRACE_WORKLOADS = {
         "GDN compose with warmed head tokens (conv-exact reuse, 32 requests, 5631 head tokens)",
     ("compose_sd_wide_kernel<0, 128, 128>", 65536, "sd"): "scalar compose, 8-segment chain, H=16",
     ("compose_sd_wide_kernel<1, 128, 128>", 65536, "sd"): "diagonal compose, 8-segment chain, H=16",
-    ("compose_sliced_mfma_kernel", 16384, "kda"): "KDA compose, 8-segment chain, H=16 (four column slices)",
-    ("compose_sliced_mfma_kernel", 32768, "main"): "GDN compose, 16-segment chain, H=32, 4 column slices (main step)",
+    ("compose_sliced_mfma_kernel", 32768, "kda"): "KDA compose, 8-segment chain, H=16 (four column slices)",
+    ("compose_sliced_mfma_kernel", 65536, "main"): "GDN compose, 16-segment chain, H=32, 4 column slices (main step)",
     ("conv_kv_kernel", None, "convexact"): "conv_kv, conv-exact reuse head tokens",
     ("conv_kv_kernel", None, "convexact_setup"): "conv_kv, conv-exact suffix records (untimed setup)",
     ("conv_warmup_vec_kernel<unsigned short, 4>", None, "rag"):

@@ -108,7 +108,7 @@ __device__ __forceinline__ float chain_ell(const ChainStage &cs, int64_t c_lo, i
     return ((lds_f32 *)cs.ell)[(c - c_lo) & (CHAIN_LDS - 1)];
 }
 // called by every thread of the workgroup at step c (the condition is uniform); the
-// entries it writes are first read CHAIN_LDS / 2 - 2 steps later, after many barriers
+// entries it writes are first read CHAIN_LDS / 2 - 3 steps later, after many barriers
 __device__ __forceinline__ void chain_refill(ChainStage &cs, const ComposeArgs &a, int64_t c_lo, int64_t c_hi,
                                              int64_t c, int head, int th, int nthreads, HeadStage *hs = nullptr) {
     const int64_t d = c - c_lo;
@@ -467,31 +467,39 @@ __global__ __launch_bounds__(NT, 1) void compose_dense_mfma_kernel(ComposeArgs a
 // (request, head) leaves most of the chip idle when there are few of them): the
 // state's columns evolve independently (column j of S only meets column j of S_i),
 // so workgroup (request, head, slice) keeps columns [32 slice, 32 slice + 32) and
-// four of them share a chain.  Wave w owns row block w of the slice (one fp32
-// 32x32 tile) and loads only rows 32w .. 32w + 31 of each P_i, straight into A
-// operand registers (split to bf16 hi/lo there: no LDS staging).  The product needs
-// every row of the slice's state as B operand, so each step the waves publish
-// their tile's hi/lo B fragments in LDS (double-buffered by step parity: one
-// workgroup barrier per step).  The next record is prefetched into registers
-// while the current product runs.
+// four of them share a chain.  Eight waves in two roles:
+//  - compute waves 0..3: wave w keeps row block w of the slice (one fp32 32x32 tile
+//    in accumulators), multiplies P_c by the slice's state and folds in S_c, then
+//    publishes its tile's hi/lo B fragments for the next step;
+//  - split waves 4..7: wave 4 + s fetches rows 32s .. 32s + 31 of each P_i two
+//    steps ahead (coalesced 16-byte pieces, two register sets) and writes them, split
+//    to bf16 hi/lo, as row block s's A fragments into the fragment area of the next
+//    step (double-buffered by step parity), while the compute waves run the products.
+// Each step has two workgroup barriers: the first finds P_c staged and the state
+// published; the compute waves then read the state's fragments into registers, and
+// the second frees the exchange area for the new state and lets the split waves
+// stage P_{c+1} (the other buffer) beside the products.
 constexpr int NSL = 4;
+constexpr int NT_SL = 512;
 struct __align__(16) XStage {
-    u32x4 f[2][8][2][64];     // [step parity][k-step][hi, lo][lane]
+    u32x4 f[8][2][64];        // [k-step][hi, lo][lane]
 };
 
-struct __align__(16) PFrag {
-    uint32_t hi[NFRAG * FRAG_U32];
-    uint32_t lo[NFRAG * FRAG_U32];
+struct __align__(16) PFrag2 {
+    uint32_t hi[2][NFRAG * FRAG_U32];     // [step parity][fragment]
+    uint32_t lo[2][NFRAG * FRAG_U32];
 };
 
-__global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs a) {
+__global__ __launch_bounds__(NT_SL, 1) void compose_sliced_mfma_kernel(ComposeArgs a) {
     __shared__ XStage xs;
-    __shared__ PFrag xp;      // wave w's fragments: row block w of P_c
+    __shared__ PFrag2 xp;
     __shared__ ChainStage cs;
     __shared__ int sh_bad;
 
     const int th = threadIdx.x;
-    const int w = th >> 6, l = th & 63, h = l >> 5, l32 = l & 31;
+    const int wid = th >> 6, l = th & 63, h = l >> 5, l32 = l & 31;
+    const bool splitter = wid >= 4;
+    const int w = wid & 3;                      // row block (of the state, or of P_i)
     // the slices of a chain sit 8 blocks apart, so they land on the same XCD (block b
     // goes to XCD b % 8) and share each P_i through its L2
     const int bx = blockIdx.x;
@@ -513,7 +521,7 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
     const int64_t c_lo = a.chain_offsets[r], c_hi = a.chain_offsets[r + 1];
     if (sh_bad == 0) {
         __syncthreads();
-        for (int64_t c = c_lo + th; c < c_hi; c += NT) {
+        for (int64_t c = c_lo + th; c < c_hi; c += NT_SL) {
             const int32_t s = a.chain_slots[c];
             const bool ok = s >= 0 && s < a.num_slots;
             if (!ok) sh_bad = 1;
@@ -529,24 +537,26 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
         if (th == 0 && sl == 0)
             raise_flag(a.err_flag, bad == 1 ? HYPIC_EFLAG_SLOT_OUT_OF_RANGE : HYPIC_EFLAG_BAD_OFFSETS);
         const float nanv = __int_as_float(0x7fc00000);
-        for (int e = th; e < 32 * D; e += NT) out[(e >> 5) * D + 32 * sl + (e & 31)] = nanv;
+        for (int e = th; e < 32 * D; e += NT_SL) out[(e >> 5) * D + 32 * sl + (e & 31)] = nanv;
         if (a.out_ell && th == 0 && sl == 0) a.out_ell[orec] = nanv;
         return;
     }
 
-    // ---- initial tile (rows 32w + acc_row, column col)
-    f32x16 st;
+    // ---- initial tile (compute waves: rows 32w + acc_row, column col)
+    f32x16 st = {};
     int64_t c = c_lo;
     const bool first_direct = a.init_S == nullptr;
     double ell = 0.0;
     if (first_direct && c < c_hi) {
-        const int64_t rec = (int64_t)a.chain_slots[c] * a.H + head;
-        const float *src = a.pool_S + rec * D * D;
+        if (!splitter) {
+            const int64_t rec = (int64_t)a.chain_slots[c] * a.H + head;
+            const float *src = a.pool_S + rec * D * D;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) st[q] = src[(32 * w + acc_row(q, h)) * D + col];
-        ell += (double)a.pool_ell[rec];
+            for (int q = 0; q < 16; ++q) st[q] = src[(32 * w + acc_row(q, h)) * D + col];
+            ell += (double)a.pool_ell[rec];
+        }
         ++c;
-    } else {
+    } else if (!splitter) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int row = 32 * w + acc_row(q, h);
@@ -554,41 +564,30 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
         }
     }
 
-    // ---- records are fetched two steps ahead into two register sets (even and odd
-    //      steps).  P_c: this wave's rows 32w .. 32w + 31 as coalesced 16-byte pieces
-    //      (piece u of lane l: row 32w + 2u + l / 32, columns 4 (l % 32) .. +3), split to
-    //      bf16 hi/lo at the top of the step and written to the wave's own fragment
-    //      area in LDS, whose A operand reads are single 16-byte loads.  S_c: this
-    //      lane's 16 tile positions.  The registers of P_c (S_c) are refilled for step
-    //      c + 2 as soon as the step has staged (added) them.
-    float4 pa[16], pb[16];
+    // compute waves: S_c's 16 tile positions of this lane, two steps ahead (two sets),
+    // and the ell of the record each set holds.  Split waves: P_i's rows 32w .. 32w + 31
+    // as 16-byte pieces (piece u of lane l: row 32w + 2u + l / 32, columns 4 (l % 32)
+    // .. +3), two register sets.
     float sa[16], sb[16];
-    float ea = 0.f, eb = 0.f;     // ell of the record each set holds
+    float ea = 0.f, eb = 0.f;
+    float4 pa[16], pb[16];
 #define HYPIC_PROW(CC) \
     (a.pool_P + ((int64_t)chain_slot(cs, c_lo, (CC)) * a.H + head) * D * D + (int64_t)(32 * w + (l >> 5)) * D + 4 * l32)
 #define HYPIC_PFETCH(PF, PROW)                                                                      \
     do {                                                                                            \
+        const float *pr_ = (PROW);                                                                  \
         _Pragma("unroll") for (int u = 0; u < 16; ++u)                                              \
-            PF[u] = *reinterpret_cast<const float4 *>((PROW) + 2 * u * D);                          \
+            PF[u] = *reinterpret_cast<const float4 *>(pr_ + 2 * u * D);                             \
     } while (0)
 #define HYPIC_SFETCH(SV, CC)                                                                        \
     do {                                                                                            \
         const float *ss_ = a.pool_S + ((int64_t)chain_slot(cs, c_lo, (CC)) * a.H + head) * D * D + col; \
         _Pragma("unroll") for (int q = 0; q < 16; ++q) SV[q] = ss_[(32 * w + acc_row(q, h)) * D];  \
     } while (0)
-    // one step: publish the tile, stage P_c (and refetch its registers for step c + 2),
-    // state <- e^{ell_c} P_c state + S_c
-#define HYPIC_STEP(PF, SV, EL, PAR)                                                                 \
+    // split wave: row block w's A fragments of a record, split to bf16 hi/lo, into
+    // fragment buffer BUF
+#define HYPIC_PSTAGE(PF, BUF)                                                                       \
     do {                                                                                            \
-        chain_refill(cs, a, c_lo, c_hi, c, head, th, NT);                                           \
-        _Pragma("unroll") for (int half = 0; half < 2; ++half) {                                    \
-            bf16x8 bh_, bl_;                                                                        \
-            acc_to_b2(st, half, bh_, bl_);                                                          \
-            xs.f[PAR][2 * w + half][0][l] = __builtin_bit_cast(u32x4, bh_);                         \
-            xs.f[PAR][2 * w + half][1][l] = __builtin_bit_cast(u32x4, bl_);                         \
-        }                                                                                           \
-        const bool more_ = c + 2 < c_hi;                                                            \
-        const float *pn_ = HYPIC_PROW(more_ ? c + 2 : c);                                           \
         _Pragma("unroll") for (int u = 0; u < 16; ++u) {                                            \
             const int li_ = 2 * u + (l >> 5), c0_ = 4 * l32;                                        \
             const int kb_ = c0_ >> 4, c16_ = c0_ & 15;                                              \
@@ -596,24 +595,44 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
             uint32_t h01_, l01_, h23_, l23_;                                                        \
             split2(PF[u].x, PF[u].y, h01_, l01_);                                                   \
             split2(PF[u].z, PF[u].w, h23_, l23_);                                                   \
-            *reinterpret_cast<u32x2 *>(&xp.hi[slot_]) = u32x2{h01_, h23_};                          \
-            *reinterpret_cast<u32x2 *>(&xp.lo[slot_]) = u32x2{l01_, l23_};                          \
-            /* unconditional (the last steps reload P_c): no phi copies */                          \
-            PF[u] = *reinterpret_cast<const float4 *>(pn_ + 2 * u * D);                             \
+            *reinterpret_cast<u32x2 *>(&xp.hi[BUF][slot_]) = u32x2{h01_, h23_};                     \
+            *reinterpret_cast<u32x2 *>(&xp.lo[BUF][slot_]) = u32x2{l01_, l23_};                     \
         }                                                                                           \
+    } while (0)
+    // compute wave: the tile's hi/lo B fragments (k-steps 2w, 2w + 1)
+#define HYPIC_PUBLISH()                                                                             \
+    do {                                                                                            \
+        _Pragma("unroll") for (int half = 0; half < 2; ++half) {                                    \
+            bf16x8 bh_, bl_;                                                                        \
+            acc_to_b2(st, half, bh_, bl_);                                                          \
+            xs.f[2 * w + half][0][l] = __builtin_bit_cast(u32x4, bh_);                              \
+            xs.f[2 * w + half][1][l] = __builtin_bit_cast(u32x4, bl_);                              \
+        }                                                                                           \
+    } while (0)
+    // compute wave, one step: state <- e^{ell_c} P_c state + S_c, then publish it
+#define HYPIC_CSTEP(SV, EL, PAR)                                                                    \
+    do {                                                                                            \
+        chain_refill(cs, a, c_lo, c_hi, c, head, th, NT_SL);                                        \
+        lds_barrier();                                                                              \
+        u32x4 bh_[8], bl_[8];                                                                       \
+        _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) {                                          \
+            bh_[kb] = xs.f[kb][0][l];                                                               \
+            bl_[kb] = xs.f[kb][1][l];                                                               \
+        }                                                                                           \
+        const bool more_ = c + 2 < c_hi;                                                            \
         const float le_ = EL;                                                                       \
-        EL = chain_ell(cs, c_lo, more_ ? c + 2 : c);          \
+        EL = chain_ell(cs, c_lo, more_ ? c + 2 : c);                                                \
         lds_barrier();                                                                              \
         f32x16 acc_ = {}, acc1_ = {};                                                               \
         _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) {                                          \
             const int f_ = (w * 8 + kb) * FRAG_U32 + lane_slot(l32, h);                             \
-            const bf16x8 ah_ = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&xp.hi[f_])); \
-            const bf16x8 al_ = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&xp.lo[f_])); \
-            const bf16x8 bh_ = __builtin_bit_cast(bf16x8, xs.f[PAR][kb][0][l]);                     \
-            const bf16x8 bl_ = __builtin_bit_cast(bf16x8, xs.f[PAR][kb][1][l]);                     \
-            acc_ = mfma(ah_, bh_, acc_);                                                            \
-            acc1_ = mfma(ah_, bl_, acc1_);                                                          \
-            acc1_ = mfma(al_, bh_, acc1_);                                                          \
+            const bf16x8 ah_ = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&xp.hi[PAR][f_])); \
+            const bf16x8 al_ = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&xp.lo[PAR][f_])); \
+            const bf16x8 b0_ = __builtin_bit_cast(bf16x8, bh_[kb]);                                 \
+            const bf16x8 b1_ = __builtin_bit_cast(bf16x8, bl_[kb]);                                 \
+            acc_ = mfma(ah_, b0_, acc_);                                                            \
+            acc1_ = mfma(ah_, b1_, acc1_);                                                          \
+            acc1_ = mfma(al_, b0_, acc1_);                                                          \
         }                                                                                           \
         acc_ += acc1_;                                                                              \
         {                                                                                           \
@@ -622,32 +641,65 @@ __global__ __launch_bounds__(NT, 1) void compose_sliced_mfma_kernel(ComposeArgs 
         }                                                                                           \
         HYPIC_SFETCH(SV, more_ ? c + 2 : c);                                                        \
         ell += (double)le_;                                                                         \
+        HYPIC_PUBLISH();                                                                            \
     } while (0)
-    if (c < c_hi) {
-        HYPIC_PFETCH(pa, HYPIC_PROW(c));
-        HYPIC_SFETCH(sa, c);
-        ea = chain_ell(cs, c_lo, c);
+    // split wave, one step: stage P_{c+1} from PN into the other buffer (on the last
+    // step PN holds a repeat of an earlier record: staged, never read), then refetch
+    // PN with P_{c+3}
+#define HYPIC_SSTEP(PN, PAR)                                                                        \
+    do {                                                                                            \
+        chain_refill(cs, a, c_lo, c_hi, c, head, th, NT_SL);                                        \
+        lds_barrier();                                                                              \
+        const float *pn_ = HYPIC_PROW(c + 3 < c_hi ? c + 3 : c);                                    \
+        lds_barrier();                                                                              \
+        HYPIC_PSTAGE(PN, (PAR) ^ 1);                                                                \
+        HYPIC_PFETCH(PN, pn_);    /* unconditional (the last steps reload P_c): no phi copies */    \
+    } while (0)
+
+    if (!splitter) {
+        HYPIC_PUBLISH();
+        if (c < c_hi) {
+            HYPIC_SFETCH(sa, c);
+            ea = chain_ell(cs, c_lo, c);
+        }
+        if (c + 1 < c_hi) {
+            HYPIC_SFETCH(sb, c + 1);
+            eb = chain_ell(cs, c_lo, c + 1);
+        }
+        // even steps use sa and fragment buffer 0, odd steps sb and buffer 1
+        while (c < c_hi) {
+            HYPIC_CSTEP(sa, ea, 0);
+            if (++c >= c_hi) break;
+            HYPIC_CSTEP(sb, eb, 1);
+            ++c;
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) out[(int64_t)(32 * w + acc_row(q, h)) * D + col] = st[q];
+        if (a.out_ell && th == 0 && sl == 0) a.out_ell[orec] = (float)ell;
+    } else {
+        // P_c staged into buffer 0, P_{c+1} in pb and P_{c+2} in pa (clamped to the
+        // chain's last record where the chain is shorter)
+        if (c < c_hi) {
+            HYPIC_PFETCH(pa, HYPIC_PROW(c));
+            HYPIC_PFETCH(pb, HYPIC_PROW(c + 1 < c_hi ? c + 1 : c));
+            HYPIC_PSTAGE(pa, 0);
+            HYPIC_PFETCH(pa, HYPIC_PROW(c + 2 < c_hi ? c + 2 : c));
+        }
+        // the same step count and barriers as the compute waves
+        while (c < c_hi) {
+            HYPIC_SSTEP(pb, 0);
+            if (++c >= c_hi) break;
+            HYPIC_SSTEP(pa, 1);
+            ++c;
+        }
     }
-    if (c + 1 < c_hi) {
-        HYPIC_PFETCH(pb, HYPIC_PROW(c + 1));
-        HYPIC_SFETCH(sb, c + 1);
-        eb = chain_ell(cs, c_lo, c + 1);
-    }
-    // even steps use pa/sa and exchange buffer 0, odd steps pb/sb and buffer 1 (the
-    // exchange is double-buffered, so one barrier per step suffices)
-    while (c < c_hi) {
-        HYPIC_STEP(pa, sa, ea, 0);
-        if (++c >= c_hi) break;
-        HYPIC_STEP(pb, sb, eb, 1);
-        ++c;
-    }
-#undef HYPIC_STEP
+#undef HYPIC_CSTEP
+#undef HYPIC_SSTEP
+#undef HYPIC_PUBLISH
+#undef HYPIC_PSTAGE
 #undef HYPIC_PFETCH
 #undef HYPIC_PROW
 #undef HYPIC_SFETCH
-#pragma unroll
-    for (int q = 0; q < 16; ++q) out[(int64_t)(32 * w + acc_row(q, h)) * D + col] = st[q];
-    if (a.out_ell && th == 0 && sl == 0) a.out_ell[orec] = (float)ell;
 }
 
 }  // namespace
@@ -661,7 +713,7 @@ hipError_t launch_compose_mfma(const ComposeArgs &a, hipStream_t stream, bool *t
     if (units <= 512) {
         // few chains: four workgroups per chain, one per 32-column slice of the state
         const dim3 grid((unsigned)((units + 7) / 8 * 8 * NSL));
-        hipLaunchKernelGGL(compose_sliced_mfma_kernel, grid, dim3(NT), 0, stream, a);
+        hipLaunchKernelGGL(compose_sliced_mfma_kernel, grid, dim3(NT_SL), 0, stream, a);
     } else {
         hipLaunchKernelGGL((compose_dense_mfma_kernel<false, false>), dim3((unsigned)units), dim3(NT), 0, stream, a);
     }
