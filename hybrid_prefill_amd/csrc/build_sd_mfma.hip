@@ -42,9 +42,10 @@
 // chunk's loads as fast as the compute waves use it); one workgroup barrier per
 // chunk.  For the diagonal family the loading waves also bring each chunk's gates
 // and beta, in a ring of their own one chunk further ahead than the keys and values;
-// the compute waves turn them into the per-(token, channel) factors and the chunk
-// decay one chunk ahead of use (compute wave w the workgroup's key channels
-// 16w .. 16w + 15, beside the current chunk's products), into parity-buffered LDS
+// four factor waves (a third role, diagonal family only: 768-thread workgroups)
+// turn them into the per-(token, channel) factors and the chunk decay one chunk
+// ahead of use (factor wave f the workgroup's key channels 16f .. 16f + 15, while
+// the compute waves run the current chunk's products), into parity-buffered LDS
 // tiles that all four compute waves then read.  Tail rows past the segment
 // repeat its last row and are masked at use (beta and log alpha of those tokens
 // read as 0).
@@ -65,7 +66,9 @@ constexpr int CH = 64;
 constexpr int D = 128;
 constexpr int NWC = 4;           // compute waves
 constexpr int NLW = 4;           // loading waves (one wave alone cannot issue loads fast enough)
+constexpr int NFW = 4;           // diagonal family: factor waves
 constexpr int NT = 64 * (NWC + NLW);
+constexpr int NT_DIAG = 64 * (NWC + NLW + NFW);
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -215,7 +218,8 @@ __device__ __forceinline__ void vm_wait(int k) {
 }
 
 template <int FAM, int NSPLIT>
-__global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) void sd_build_mfma_kernel(BuildArgs a) {
+__global__ __launch_bounds__(FAM == HYPIC_DIAGONAL ? NT_DIAG : NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1)
+void sd_build_mfma_kernel(BuildArgs a) {
     constexpr bool DIAG = FAM == HYPIC_DIAGONAL;
     constexpr int NJB = 4 / NSPLIT;                    // 32-column value blocks per workgroup
     static_assert(!DIAG || NSPLIT == 2, "the diagonal family splits the key channels in two");
@@ -433,7 +437,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     };
 
     // Diagonal family: the factors of chunk C for the workgroup key channels ch0 .. ch0 + 15,
-    // computed by compute wave w (ch0 = 16 w) one chunk ahead of their use.  Lane l takes
+    // computed by factor wave f (ch0 = 16 f) one chunk ahead of their use.  Lane l takes
     // channel ch0 + l / 4 and the tokens 16 (l % 4) .. + 15 (the channel's four lanes form
     // a quad):
     //   L_t (inclusive cumulative log decay of the channel), G = L_63,
@@ -441,8 +445,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
     // written to the parity-C tiles; ell_acc collects the lane's log decays.  The gates
     // were loaded by the loading waves, each of which waited for its own before the
     // barrier that starts the chunk these factors are computed in.
-    // (in two parts: the gate and beta reads, issued before the current chunk's products
-    // so that their LDS round trip overlaps them, and the arithmetic after)
+    // (in two parts: the gate and beta reads, all issued before the arithmetic)
     struct FacIn { float x[16], bt[16]; };
     auto factors16_read = [&](int C, int ch0, FacIn &fi) {
         if constexpr (DIAG) {
@@ -511,6 +514,31 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
         }
     };
 
+    if constexpr (DIAG) {
+        if (w >= NWC + NLW) {
+            // ================= factor waves (diagonal): during chunk c, the factors and
+            // decay of chunk c + 1 from its gates (which the loading waves waited for
+            // before the barrier that starts chunk c), into the parity-(c + 1) tiles that
+            // the compute waves last read in chunk c - 1; the same barriers as the others
+            const int fw = w - NWC - NLW;
+            double ell16 = 0.0;
+            FacIn fi;
+            lds_barrier();                            // gates of chunk 0 visible
+            if (nc > 0) {
+                factors16_read(0, 16 * fw, fi);
+                factors16(0, 16 * fw, fi, ell16);
+            }
+            for (int c = 0; c < nc; ++c) {
+                lds_barrier();                        // gates of chunk c + 1 visible; chunk c's factors published
+                if (c + 1 < nc) {
+                    factors16_read(c + 1, 16 * fw, fi);
+                    factors16(c + 1, 16 * fw, fi, ell16);
+                }
+            }
+            write_ell16(ell16, 16 * fw);
+            return;
+        }
+    }
     if (w >= NWC) {
         // ================= loading waves: the same barriers as the compute waves
         const int lw = w - NWC;
@@ -646,18 +674,11 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
             for (int c = 0; c < nc; ++c) step(c, oa, oa);
         }
     } else {
-    // the chunk's factors (computed by these waves one chunk ahead): decay, scale, multiply
+    // the chunk's factors (computed by the factor waves one chunk ahead): decay, scale, multiply
     const int i = 32 * (w >> 1) + l32;                // this lane's key channel (of the workgroup's 64)
-    double ell16 = 0.0;
-    FacIn fi;
     lds_barrier();                                    // gates of chunk 0 visible
-    if (nc > 0) {
-        factors16_read(0, 16 * w, fi);
-        factors16(0, 16 * w, fi, ell16);
-    }
     for (int c = 0; c < nc; ++c) {
         lds_barrier();                                // chunk c and its factors visible; chunk c - 1's buffer free
-        if (c + 1 < nc) factors16_read(c + 1, 16 * w, fi);
         const SdBuf<DIAG, NJB> &B = sm.buf[c % NBUF];
         const int par = (int)(c & 1);
         // ---- operand reads: K^T and V^T fragments (transposing read), the factors of
@@ -692,9 +713,7 @@ __global__ __launch_bounds__(NT, (FAM == HYPIC_SCALAR && NSPLIT == 4) ? 2 : 1) v
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb) st[jb] = mfma(ka, vb[ks][jb], st[jb]);
         }
-        if (c + 1 < nc) factors16(c + 1, 16 * w, fi, ell16);
     }
-    write_ell16(ell16, 16 * w);
     }
     // ---- record
     const float nanv = __int_as_float(0x7fc00000);
@@ -747,7 +766,8 @@ hipError_t launch_build_sd_mfma(const BuildArgs &a, hipStream_t stream, bool *ta
     const int nsplit = diag ? 2 : (units >= 256 ? 1 : units >= 128 ? 2 : 4);
     const int64_t padded = (units + 7) / 8 * 8;
     const dim3 grid((unsigned)(padded * nsplit));
-#define HYPIC_SD_LAUNCH(FAM_, NS_) hipLaunchKernelGGL((sd_build_mfma_kernel<FAM_, NS_>), grid, dim3(NT), 0, stream, a)
+#define HYPIC_SD_LAUNCH(FAM_, NS_) \
+    hipLaunchKernelGGL((sd_build_mfma_kernel<FAM_, NS_>), grid, dim3(FAM_ == HYPIC_DIAGONAL ? NT_DIAG : NT), 0, stream, a)
     if (a.family == HYPIC_SCALAR) {
         if (nsplit == 1) HYPIC_SD_LAUNCH(HYPIC_SCALAR, 1);
         else if (nsplit == 2) HYPIC_SD_LAUNCH(HYPIC_SCALAR, 2);
