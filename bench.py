@@ -84,7 +84,7 @@ TRAFFIC_KERNELS = {
                                             "GDN compose, 4096-slot pool, 64 requests x 32 slots, H=32, d=128"),
     "scalar_build_h16_d128_8x2048": ("sd_build_mfma_kernel<0, 2>", 131072, "sd", _SD_SRC,
                                      "scalar-decay build, H=16, d=128, bf16, 8 x 2048 tokens"),
-    "diagonal_build_h16_d128_8x2048": ("sd_build_mfma_kernel<1, 2>", 131072, "sd", _SD_SRC,
+    "diagonal_build_h16_d128_8x2048": ("sd_build_mfma_kernel<1, 2>", 196608, "sd", _SD_SRC,
                                        "diagonal-gate build, H=16, d=128, bf16, 8 x 2048 tokens"),
     "conv_warmup_rag_8305x4096_k4": ("conv_warmup_vec_kernel", None, "rag", ("conv_warmup.hip", "hypic_internal.h"),
                                      "conv warm-up of the RAG mix, 8305 boundaries x 4096 channels, kernel 4, bf16"),
@@ -880,7 +880,7 @@ MFMA_KERNELS = (
     ("compose_sliced_mfma_kernel", 65536, "main", "GDN compose, 16-segment chain", "BF16"),
     ("compose_dense_mfma_kernel<false, false>", 524288, "compose", "GDN compose, 4096-slot pool", "BF16"),
     ("sd_build_mfma_kernel<0, 2>", 131072, "sd", "scalar build", "BF16"),
-    ("sd_build_mfma_kernel<1, 2>", 131072, "sd", "diagonal build", "BF16"),
+    ("sd_build_mfma_kernel<1, 2>", 196608, "sd", "diagonal build", "BF16"),
     ("kda_chunk_mfma_kernel", 131072, "kda", "KDA build (fp32 matrix cores)", "F32"),
 )
 
@@ -961,7 +961,7 @@ TRACE_WORKLOADS = {
     ("kda_chunk_mfma_kernel<unsigned short>", 131072, "kda"):
         "KDA build, H=16, d=128, bf16, 8 x 2048 tokens (chunk form, fp32 MFMA, two roles)",
     ("sd_build_mfma_kernel<0, 2>", 131072, "sd"): "scalar build, H=16, d=128, bf16, 8 x 2048 tokens",
-    ("sd_build_mfma_kernel<1, 2>", 131072, "sd"): "diagonal build, H=16, d=128, bf16, 8 x 2048 tokens",
+    ("sd_build_mfma_kernel<1, 2>", 196608, "sd"): "diagonal build, H=16, d=128, bf16, 8 x 2048 tokens",
     ("peak_mfma_kernel", 262144, "peaks"): "measured-peak bf16 MFMA loop, 1024 x 4 waves x 512 x 4 products",
     ("peak_read_kernel", 8388608, "peaks"): "measured-peak streaming read of 4 GiB",
     ("peak_copy_kernel", 8388608, "peaks"): "measured-peak streaming copy of 1 GiB (1 GiB read, 1 GiB written)",
