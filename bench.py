@@ -1080,8 +1080,8 @@ def summarize_trace(trace_csv, stats_csv, bench_json, out_md):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["all", "main", "forward", "sd", "compose", "rag", "convexact", "kda", "peaks"],
                     default="all", help="main: only the headline GDN step; otherwise it plus that leg")
     ap.add_argument("--no-cpu", action="store_true")
